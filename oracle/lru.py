@@ -1,0 +1,167 @@
+"""The global LRU pool of GPU expert slots, simulated with dicts and lists.
+
+TEST INFRASTRUCTURE (oracle).  What the pages fix: the GPU keeps a
+least-recently-used cache of expert slots; an expert already cached runs in
+place and a miss is streamed over PCIe (devpik article, "Why a Huge MoE Model
+Fits on One Consumer GPU"); one LRU pool is shared by all layers (same
+section); the hybrid strategy splits each step's misses between host compute
+and streaming (same section; byteiota article, "The Bandwidth-Adaptive
+Runtime").  Finer points are this build's readings:
+
+* Keys are (layer, expert).  A call's tokens are walked in order; a *wave* is
+  the longest run of consecutive tokens whose union of selected experts has
+  at most C members.  Each wave is resolved as a set: an expert needed later
+  in the same wave is never evicted by an earlier miss.
+* Pairs P = (token, rank) in token-major order; D = distinct experts in order
+  of first appearance; hits Hs = members of D resident at the wave's start;
+  misses M = D minus Hs, in D order.
+* Hybrid: m_cpu = floor(|M| * share + 1/2) (IEEE double); the last m_cpu
+  misses go to host compute and are not inserted into the pool; the rest
+  stream.
+* Victims: free slots by ascending index, then resident slots not holding a
+  hit of this wave, by ascending last use.  The i-th streamed miss takes the
+  i-th victim.
+* Clock: one tick per pair of the wave; a touched slot's last use is the
+  clock at the wave start plus the position of its expert's last pair.
+* Prefill staging: the call streams all E experts of the layer into slots
+  (layer mod 2) * E + e; every pair is a streamed miss; residents of that half
+  are evicted; the LRU order of other slots is untouched (devpik article,
+  "Long Prompts Are the Bottleneck").
+
+Pins (tests/test_oracle_lru.py): an independent brute-force list LRU,
+hand-worked traces, the compulsory-miss, inclusion and cyclic-thrash
+properties of LRU, hits + misses = T*k.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import List, Sequence
+
+import numpy as np
+
+HIT, MISS_STREAM, MISS_CPU = 0, 1, 2
+
+
+def split_waves(sel: np.ndarray, capacity: int):
+    """Token ranges [(t0, t1)] of the waves of one call."""
+    T = sel.shape[0]
+    waves = []
+    t0 = 0
+    cur = set()
+    for t in range(T):
+        new = cur | set(int(e) for e in sel[t])
+        if len(new) > capacity:
+            waves.append((t0, t))
+            t0 = t
+            cur = set(int(e) for e in sel[t])
+        else:
+            cur = new
+    if T > 0:
+        waves.append((t0, T))
+    return waves
+
+
+def hybrid_cpu_count(m: int, share: float) -> int:
+    return int(math.floor(float(m) * float(share) + 0.5))
+
+
+class LRUPool:
+    def __init__(self, capacity: int):
+        self.C = int(capacity)
+        self.slot_of = {}  # (layer, expert) -> slot
+        self.key_of: List = [None] * self.C
+        self.last_use: List = [None] * self.C
+        self.clock = 0
+
+    def resident(self, layer: int, e: int) -> bool:
+        return (layer, e) in self.slot_of
+
+    def resolve_wave(self, layer: int, sel_wave: np.ndarray, share: float = 0.0):
+        """Resolve one wave.  sel_wave: [Tw, k] expert ids.
+
+        Returns dict with per-pair flag/slot, the streamed-miss list
+        [(expert, slot)] in D order, the CPU-miss list, D, and counters.
+        """
+        pairs = [int(e) for e in np.asarray(sel_wave).reshape(-1)]
+        P = len(pairs)
+        D = []
+        last_pos = {}
+        for p, e in enumerate(pairs):
+            if e not in last_pos:
+                D.append(e)
+            last_pos[e] = p
+        assert len(D) <= self.C
+        hits = [e for e in D if self.resident(layer, e)]
+        misses = [e for e in D if not self.resident(layer, e)]
+        m_cpu = hybrid_cpu_count(len(misses), share)
+        m_str = len(misses) - m_cpu
+        stream = misses[:m_str]
+        cpu = misses[m_str:]
+
+        protected = {self.slot_of[(layer, e)] for e in hits}
+        free = [s for s in range(self.C) if self.key_of[s] is None]
+        used = [s for s in range(self.C) if self.key_of[s] is not None and s not in protected]
+        used.sort(key=lambda s: self.last_use[s])
+        victims = free + used
+        evictions = 0
+        stream_list = []
+        for i, e in enumerate(stream):
+            s = victims[i]
+            old = self.key_of[s]
+            if old is not None:
+                del self.slot_of[old]
+                evictions += 1
+            self.key_of[s] = (layer, e)
+            self.slot_of[(layer, e)] = s
+            stream_list.append((e, s))
+        for e in hits + stream:
+            self.last_use[self.slot_of[(layer, e)]] = self.clock + last_pos[e]
+        self.clock += P
+
+        hit_set, cpu_set = set(hits), set(cpu)
+        flag = np.empty(P, np.uint8)
+        slot = np.empty(P, np.int32)
+        for p, e in enumerate(pairs):
+            if e in hit_set:
+                flag[p] = HIT
+                slot[p] = self.slot_of[(layer, e)]
+            elif e in cpu_set:
+                flag[p] = MISS_CPU
+                slot[p] = -1
+            else:
+                flag[p] = MISS_STREAM
+                slot[p] = self.slot_of[(layer, e)]
+        return dict(flag=flag, slot=slot, stream=stream_list, cpu=list(cpu), D=D,
+                    pair_hits=int((flag == HIT).sum()), expert_hits=len(hits),
+                    expert_misses=len(misses), cpu_misses=len(cpu), evictions=evictions)
+
+    def stage_layer(self, layer: int, num_experts: int, sel: np.ndarray):
+        """Prefill staging of one layer into half (layer mod 2) of slots [0, 2E)."""
+        E = num_experts
+        assert self.C >= 2 * E
+        base = (layer % 2) * E
+        evictions = 0
+        for s in range(base, base + E):
+            old = self.key_of[s]
+            if old is not None:
+                del self.slot_of[old]
+                self.key_of[s] = None
+                self.last_use[s] = None
+                evictions += 1
+        pairs = np.asarray(sel).reshape(-1)
+        flag = np.full(pairs.size, MISS_STREAM, np.uint8)
+        slot = (base + pairs).astype(np.int32)
+        D = []
+        seen = set()
+        for e in pairs:
+            if int(e) not in seen:
+                seen.add(int(e))
+                D.append(int(e))
+        return dict(flag=flag, slot=slot, stream=[(e, base + e) for e in range(E)], cpu=[], D=D,
+                    pair_hits=0, expert_hits=0, expert_misses=E, cpu_misses=0,
+                    evictions=evictions)
+
+    def snapshot(self):
+        """(key_of, last_use) copies, for comparisons with the device table."""
+        return list(self.key_of), list(self.last_use), self.clock
