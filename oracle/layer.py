@@ -90,7 +90,7 @@ class OracleLayerStack:
         slot = np.empty(T * k, np.int32)
         waves = []
         if prefill:
-            r = self.pool.stage_layer(layer, E, sel)
+            r = self.pool.stage_layer(layer, E, sel, w.num_layers)
             flag[:], slot[:] = r["flag"], r["slot"]
             waves.append(dict(t0=0, t1=T, **r))
             st = dict(pair_hits=0, expert_hits=0, expert_misses=E, cpu_misses=0,

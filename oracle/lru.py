@@ -24,9 +24,11 @@ Runtime").  Finer points are this build's readings:
 * Clock: one tick per pair of the wave; a touched slot's last use is the
   clock at the wave start plus the position of its expert's last pair.
 * Prefill staging: the call streams all E experts of the layer into slots
-  (layer mod 2) * E + e; every pair is a streamed miss; residents of that half
-  are evicted; the LRU order of other slots is untouched (devpik article,
-  "Long Prompts Are the Bottleneck").
+  (layer mod 2) * E + e; every pair is a streamed miss; since the call also
+  starts the copy of layer l+1 into the other half, residents of both halves
+  are evicted (the second only if l+1 < L); the LRU order of other slots is
+  untouched and the clock does not move (devpik article, "Long Prompts Are
+  the Bottleneck").
 
 Pins (tests/test_oracle_lru.py): an independent brute-force list LRU,
 hand-worked traces, the compulsory-miss, inclusion and cyclic-thrash
@@ -136,19 +138,26 @@ class LRUPool:
                     pair_hits=int((flag == HIT).sum()), expert_hits=len(hits),
                     expert_misses=len(misses), cpu_misses=len(cpu), evictions=evictions)
 
-    def stage_layer(self, layer: int, num_experts: int, sel: np.ndarray):
-        """Prefill staging of one layer into half (layer mod 2) of slots [0, 2E)."""
+    def stage_layer(self, layer: int, num_experts: int, sel: np.ndarray, num_layers: int):
+        """Prefill staging of one layer into half (layer mod 2) of slots [0, 2E).
+
+        The call for layer l also starts the copy of layer l+1 into the other
+        half (layer N+1 copies while layer N computes), so both halves lose
+        their LRU residents here (the second one only if l+1 < L).
+        """
         E = num_experts
         assert self.C >= 2 * E
         base = (layer % 2) * E
+        halves = [layer % 2] + ([(layer + 1) % 2] if layer + 1 < num_layers else [])
         evictions = 0
-        for s in range(base, base + E):
-            old = self.key_of[s]
-            if old is not None:
-                del self.slot_of[old]
-                self.key_of[s] = None
-                self.last_use[s] = None
-                evictions += 1
+        for h in halves:
+            for s in range(h * E, h * E + E):
+                old = self.key_of[s]
+                if old is not None:
+                    del self.slot_of[old]
+                    self.key_of[s] = None
+                    self.last_use[s] = None
+                    evictions += 1
         pairs = np.asarray(sel).reshape(-1)
         flag = np.full(pairs.size, MISS_STREAM, np.uint8)
         slot = (base + pairs).astype(np.int32)

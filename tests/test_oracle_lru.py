@@ -219,11 +219,15 @@ def test_hybrid_count_rounding():
 
 
 def test_prefill_staging_slots_and_evictions():
-    pool = LRUPool(8)
-    pool.resolve_wave(1, np.array([[2]]))  # key (1,2) -> slot 0
+    pool = LRUPool(10)
+    for e in range(6):
+        pool.resolve_wave(1, np.array([[e]]))  # keys (1,0..5) -> slots 0..5
     sel = np.array([[3, 1], [0, 3]])
-    r = pool.stage_layer(0, 4, sel)
+    r = pool.stage_layer(0, 4, sel, num_layers=2)
     assert list(r["slot"]) == [3, 1, 0, 3] and (r["flag"] == MISS_STREAM).all()
-    assert r["evictions"] == 1 and not pool.resident(1, 2)
-    r = pool.stage_layer(1, 4, sel)
+    # both halves [0,4) and [4,8) are emptied: slots 0..5 held residents
+    assert r["evictions"] == 6 and not pool.resident(1, 2)
+    r = pool.stage_layer(1, 4, sel, num_layers=2)
     assert list(r["slot"]) == [7, 5, 4, 7] and r["evictions"] == 0
+    # a decode access afterwards takes the lowest free slot
+    assert pool.resolve_wave(1, np.array([[9]]))["stream"] == [(9, 0)]
