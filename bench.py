@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Throughput of the offloaded MoE layer stack on one MI355X.
+
+Workload (default): the Qwen-35B-A3B-shaped decode layer stack -- 48 layers,
+hidden 2048, expert intermediate 768, 128 MXFP4 experts per layer, top-8,
+Zipf(1.0) popularity, one global LRU pool of 1843 slots (30% of the 6144
+experts), batch 16.  A step is one decode step through all 48 MoE layers:
+router, resolve against the pool, miss streaming from pinned host RAM,
+grouped expert FFN, combine.  Inputs are seeded and synthetic and are resident
+in HBM before the timed region starts.
+
+Prints one JSON line (see `result` below) with
+  * value = tokens per second through the whole 48-layer stack,
+  * roofline of the dominant kernel (the gate/up expert FFN), from HIP events
+    recorded by the library on the stream the kernel runs on,
+  * cpu_baseline = the CPU oracle timed on the host cores on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def measure_h2d(torch, dev, sizes=(52_224, 2_506_752, 20_054_016, 320_864_256), reps=6):
+    """Pinned host -> device copy bandwidth (GB/s) per size."""
+    out = {}
+    big = max(sizes)
+    host = torch.empty(big, dtype=torch.uint8, pin_memory=True)
+    host.fill_(1)
+    dst = torch.empty(big, dtype=torch.uint8, device=dev)
+    s = torch.cuda.current_stream()
+    for n in sizes:
+        dst[:n].copy_(host[:n], non_blocking=True)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(reps):
+            dst[:n].copy_(host[:n], non_blocking=True)
+        e1.record(s)
+        torch.cuda.synchronize()
+        out[n] = n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    return out
+
+
+def measure_hbm_copy(torch, dev, nbytes=2 << 30, reps=5):
+    a = torch.empty(nbytes // 2, dtype=torch.int16, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(3)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
+def cpu_baseline(w, batch, ncalls):
+    """The oracle as it stands, on the first `ncalls` (step 0, layer l) calls."""
+    import moe_synth as ms
+    from oracle.layer import OracleLayerStack
+
+    threads = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+
+        info = [i.get("num_threads", 1) for i in threadpool_info()]
+        threads = max(info) if info else threads
+    except Exception:
+        pass
+    st = OracleLayerStack(w)
+    xs = [ms.activations(w, l, 0, batch) for l in range(ncalls)]
+    bs = [ms.popularity_bias(w, l, 0) for l in range(ncalls)]
+    t0 = time.perf_counter()
+    for l in range(ncalls):
+        st.forward(l, xs[l], bs[l], outputs=True)
+    sec = (time.perf_counter() - t0) / ncalls
+    return {"value": batch / (sec * w.num_layers), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{ncalls} layer calls (step 0, layers 0..{ncalls - 1}) at batch {batch}, routing + LRU + "
+                      f"fp64 expert FFN + combine; {sec:.2f} s per layer call, scaled to the {w.num_layers}-layer "
+                      f"stack"}
+
+
+def run_steps(ft, torch, pool, x_all, bias_all, out, first, nsteps, L, B):
+    for s in range(first, first + nsteps):
+        for l in range(L):
+            ft.ft_moe_layer_forward(pool, l, B, x_all[s, l], bias_all[l], out, ft.FT_FWD_DECODE, None, None)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=240)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--batch", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-calls", type=int, default=6)
+    ap.add_argument("--no-extras", action="store_true", help="skip the batch 1/4 and link measurements")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import lru_expert_cache_amd as ft
+    import moe_synth as ms
+
+    ft.lib()
+    dev = torch.device("cuda", 0)
+    w = ms.workload("qwen-a3b-decode")
+    L, E, H, B = w.num_layers, w.num_experts, w.hidden, args.batch
+    nsteps = args.warmup + args.steps
+
+    t = time.perf_counter()
+    store = ms.BlobStore(w)
+    log(f"[bench] generated {store.nbytes / 1e9:.2f} GB of expert blobs in {time.perf_counter() - t:.1f} s")
+    t = time.perf_counter()
+    blobs = [store.expert(l, e) for l in range(L) for e in range(E)]
+    router = np.stack([ms.router_weight(w, l) for l in range(L)])
+    cfg = ft.make_config(L, H, w.inter, E, w.top_k, w.layer_fmt, pool_slots=w.pool_slots)
+    pool, _ = ft.ft_moe_init_pool(cfg, blobs, router)
+    del blobs, store
+    log(f"[bench] pool of {w.pool_slots} slots ready in {time.perf_counter() - t:.1f} s")
+
+    t = time.perf_counter()
+    x_host = np.empty((nsteps, L, B, H), np.uint16)
+    for s in range(nsteps):
+        for l in range(L):
+            x_host[s, l] = ms.activations(w, l, s, B)
+    x_all = torch.from_numpy(x_host.view(np.int16)).to(dev)
+    bias_all = torch.from_numpy(np.stack([ms.popularity_bias(w, l, 0) for l in range(L)])).to(dev)
+    out = torch.empty((B, H), dtype=torch.int16, device=dev)
+    del x_host
+    log(f"[bench] {nsteps} steps of activations resident on the GPU ({time.perf_counter() - t:.1f} s)")
+
+    run_steps(ft, torch, pool, x_all, bias_all, out, 0, args.warmup, L, B)
+    torch.cuda.synchronize()
+    ft.ft_moe_pool_stats(pool, reset=True)
+    ft.ft_moe_set_profiling(pool, True)
+    ft.ft_moe_profile_read(pool, reset=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run_steps(ft, torch, pool, x_all, bias_all, out, args.warmup, args.steps, L, B)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ft.ft_moe_set_profiling(pool, False)
+    prof = ft.ft_moe_profile_read(pool, reset=True)
+    st = ft.ft_moe_pool_stats(pool)
+    log(f"[bench] timed {args.steps} steps in {elapsed:.3f} s")
+
+    gu = prof["ffn_gateup"]
+    gu_avg_ms = gu["ms"] / max(gu["launches"], 1)
+    gu_gbs = gu["bytes"] / (gu["ms"] * 1e-3) / 1e9 if gu["ms"] > 0 else 0.0
+    dn = prof["ffn_down"]
+    cp = prof["copy"]
+    h2d_stream = cp["bytes"] / (cp["ms"] * 1e-3) / 1e9 if cp["ms"] > 0 else 0.0
+    pairs = st["pair_hits"] + st["pair_misses"]
+    extras = {
+        "hit_rate_pairs": st["pair_hits"] / max(pairs, 1),
+        "hit_rate_experts": st["expert_hits"] / max(st["expert_hits"] + st["expert_misses"], 1),
+        "streamed_gb_per_step": st["bytes_h2d"] / 1e9 / args.steps,
+        "min_topk_gap": st["min_topk_gap"],
+        "stage_ms_per_step": {k: v["ms"] / args.steps for k, v in prof.items()},
+        "ffn_gateup": {"launches": gu["launches"], "avg_us": gu_avg_ms * 1e3, "GBps": gu_gbs},
+        "ffn_down": {"launches": dn["launches"], "avg_us": dn["ms"] / max(dn["launches"], 1) * 1e3,
+                     "GBps": dn["bytes"] / (dn["ms"] * 1e-3) / 1e9 if dn["ms"] > 0 else 0.0},
+        "miss_stream_GBps": h2d_stream,
+    }
+    if not args.no_extras:
+        link = measure_h2d(torch, dev)
+        peak_h2d = max(link.values())
+        extras["h2d_sweep_GBps"] = {str(k): round(v, 2) for k, v in link.items()}
+        extras["miss_stream_frac_of_measured_h2d"] = h2d_stream / peak_h2d if peak_h2d else None
+        extras["hbm_copy_GBps"] = measure_hbm_copy(torch, dev)
+        for b in (1, 4):
+            xb = torch.from_numpy(np.stack([[ms.activations(w, l, 1000 + s, b) for l in range(L)]
+                                            for s in range(24)]).view(np.int16)).to(dev)
+            ob = torch.empty((b, H), dtype=torch.int16, device=dev)
+            run_steps(ft, torch, pool, xb, bias_all, ob, 0, 8, L, b)
+            torch.cuda.synchronize()
+            ta = time.perf_counter()
+            run_steps(ft, torch, pool, xb, bias_all, ob, 8, 16, L, b)
+            torch.cuda.synchronize()
+            extras[f"tokens_per_s_batch{b}"] = b * 16 / (time.perf_counter() - ta)
+    ft.ft_moe_destroy_pool(pool)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        t = time.perf_counter()
+        cpu = cpu_baseline(w, B, args.cpu_calls)
+        log(f"[bench] cpu baseline {time.perf_counter() - t:.1f} s")
+
+    value = B * args.steps / elapsed
+    result = {
+        "metric": "MoE-layer tokens/s (decode & prefill); % HBM BW / FP4 MFMA peak; hit rate",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4-weights/bf16-act/fp32-acc",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": L, "hidden": H, "expert_inter": w.inter, "experts": E,
+                   "top_k": w.top_k, "batch": B, "pool_slots": w.pool_slots, "format": "mxfp4",
+                   "zipf_alpha": w.zipf_alpha},
+        "roofline": {"kernel": "k_ffn<mxfp4, gate/up>", "bound": "hbm", "achieved": gu_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": gu_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "avg_launch_us": gu_avg_ms * 1e3},
+        "cpu_baseline": cpu,
+        "extras": extras,
+    }
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,198 @@
+/*
+ * ftmoe.h -- C ABI of the offloaded Mixture-of-Experts layer for AMD MI355X
+ * (gfx950).
+ *
+ * The layer keeps every routed expert of every layer in pinned host RAM and a
+ * least-recently-used pool of expert slots in GPU memory, one pool shared by
+ * all layers.  Per call: a router picks the top-k experts of each token; each
+ * chosen expert is looked up in the pool (a hit runs in place, a miss is
+ * streamed from host RAM over PCIe, or, in the hybrid strategy, part of the
+ * step's misses is computed on host cores); tokens are grouped by expert, run
+ * through a block-scaled 4-bit or 8-bit SwiGLU expert and combined with their
+ * routing weights.  Prefill chunks instead stream every expert of a layer,
+ * double buffered so that layer N+1 copies while layer N computes.
+ *
+ * Where the behaviour comes from (FreeToken pages, by title and section):
+ *   - offload strategy, LRU cache of expert slots, hit at GPU speed, miss over
+ *     PCIe, hybrid split of a step's misses, one global LRU pool:
+ *     devpik "FreeToken: Run Frontier MoE Models on Your Own GPU, and the RAM
+ *     It Takes", section "Why a Huge MoE Model Fits on One Consumer GPU";
+ *     byteiota "FreeToken: Run a 290B MoE Model on One Gaming GPU", sections
+ *     "VRAM Is Not the Bottleneck You Think It Is", "The Bandwidth-Adaptive
+ *     Runtime".
+ *   - prefill: all experts of a layer copied per chunk, layer N+1 copied while
+ *     N computes, a warning when the cache cannot hold the two staging layers:
+ *     devpik article, section "Long Prompts Are the Bottleneck".
+ *   - formats MXFP4, NVFP4 (an 8-bit scale per 16 weights), FP8: devpik
+ *     article, "The Real Requirement Is System RAM".
+ *   - expert-cache hit rate and cache fullness as statistics: devpik article,
+ *     "What to Watch Out For" (--moe-collect-stats); mindstudio "FreeToken
+ *     Explained", section "Is FreeToken worth using...?" (FT shell stats).
+ *
+ * Conventions: every call returns an int status (FT_OK = 0, > 0 warnings,
+ * < 0 errors) and never lets a C++ exception cross the ABI; the message of the
+ * last error of the calling thread is returned by ft_moe_last_error().
+ * "dev" pointers are HIP device addresses on the pool's device; "host"
+ * pointers are ordinary host memory.  A pool is not thread safe: drive each
+ * pool from one host thread.
+ */
+#ifndef FTMOE_H
+#define FTMOE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ft_moe_pool ft_moe_pool; /* opaque; owned by the library */
+
+enum {
+  FT_OK = 0,
+  FT_WARN_STAGING_SMALL = 1, /* init: pool cannot hold two full layers (prefill disabled) */
+  FT_E_INVALID = -1,         /* bad argument, shape or pointer */
+  FT_E_OOM_DEVICE = -2,      /* device allocation failed */
+  FT_E_OOM_PINNED = -3,      /* pinned host allocation failed */
+  FT_E_HIP = -4,             /* a HIP runtime call failed (message has details) */
+  FT_E_STATE = -5            /* call out of order (prefill layers must run 0,1,...,L-1) */
+};
+
+enum { FT_FMT_MXFP4 = 1, FT_FMT_NVFP4 = 2, FT_FMT_FP8_B128 = 3 };
+
+enum {
+  FT_FWD_DECODE = 0,         /* resolve against the LRU pool */
+  FT_FWD_PREFILL_STAGED = 1, /* stream all experts of the layer into staging half (layer % 2) */
+  FT_FWD_MODE_MASK = 0xF,
+  FT_ACT_BF16 = 0 << 4,      /* expert inputs used as given (bf16) */
+  FT_ACT_MXFP8 = 1 << 4,     /* prefill only: x and h quantised to MXFP8 (E4M3, 32-blocks) */
+  FT_ACT_MXFP4 = 2 << 4,     /* prefill only: x and h quantised to MXFP4 (E2M1, 32-blocks) */
+  FT_ACT_MASK = 0xF << 4
+};
+
+enum { FT_PAIR_HIT = 0, FT_PAIR_MISS_STREAM = 1, FT_PAIR_MISS_CPU = 2 };
+
+/* Layer geometry and pool policy.  Read only during ft_moe_init_pool. */
+typedef struct {
+  int32_t num_layers;        /* L >= 1 */
+  int32_t hidden;            /* H, multiple of 128 */
+  int32_t inter;             /* I, multiple of 128 (expert intermediate size) */
+  int32_t num_experts;       /* E per layer, 1..512 */
+  int32_t top_k;             /* k, 1..min(E, 16) */
+  int32_t has_shared_expert; /* 1: one always-resident shared expert per layer, weight 1 */
+  const int32_t *layer_fmt;  /* host [L] FT_FMT_* */
+  int64_t pool_slots;        /* > 0: number of expert slots C */
+  int64_t pool_bytes;        /* used if pool_slots == 0: C = floor(pool_bytes / largest expert size) */
+  double hybrid_cpu_share;   /* 0: pure offload; (0,1]: fraction of each wave's misses computed on host */
+  int32_t cpu_threads;       /* host threads for the hybrid worker (0 = 8) */
+  int32_t device;            /* HIP device ordinal */
+} ft_moe_config;
+
+/*
+ * Weights, in HOST memory owned by the caller and read only during init (the
+ * library copies them; the caller may free them afterwards).
+ * Canonical expert blob = [W_gate codes][W_up codes][W_down codes]
+ * [gate scales][up scales][down scales][3 x fp32 tensor scales, NVFP4 only];
+ * W_gate, W_up are [I][H], W_down is [H][I], row-major [out][in] with the
+ * block scales running along `in`; FP4 codes two per byte, even element in
+ * the low nibble; MXFP4 scales E8M0 per 32, NVFP4 scales E4M3 per 16, FP8
+ * scales little-endian fp32 per 128.  Entries of `expert` that hold the same
+ * pointer are stored once in pinned memory (they stay distinct cache keys).
+ */
+typedef struct {
+  const void *const *expert; /* [L*E] blob of (layer l, expert e) at index l*E+e */
+  const void *const *shared; /* [L] shared-expert blobs, or NULL */
+  const float *router_w;     /* [L][E][H] fp32 router weights */
+} ft_moe_weights;
+
+/* Optional per-call trace, DEVICE memory owned by the caller, T*k entries
+ * each, pair order = token-major then rank.  Any member may be NULL. */
+typedef struct {
+  int32_t *sel;  /* chosen expert of each pair (rank order: logit desc, index asc) */
+  float *w;      /* routing weight of each pair */
+  int32_t *slot; /* pool slot of the pair's expert, -1 for host-computed */
+  uint8_t *flag; /* FT_PAIR_* */
+  int32_t *row;  /* row of the pair in the expert-grouped order of its wave */
+} ft_moe_trace;
+
+typedef struct {
+  uint64_t pair_hits, pair_misses;     /* per (token, rank) pair; hit rate = hits / (hits + misses) */
+  uint64_t expert_hits, expert_misses; /* per distinct expert of a wave */
+  uint64_t cpu_misses;                 /* experts computed on host cores */
+  uint64_t evictions;                  /* resident experts displaced */
+  uint64_t bytes_h2d;                  /* streamed expert bytes + host-computed result rows */
+  uint64_t calls;                      /* forward calls */
+  int64_t slots_used, slots_total;     /* cache fullness (whole pool) */
+  double min_topk_gap;                 /* smallest logit gap between rank k and k+1 seen */
+} ft_moe_stats;
+
+/* Create a pool on cfg->device: validates the shapes, copies the expert
+ * blobs into pinned host RAM (repacked for the GPU), allocates the slot arena,
+ * the resident router weights and shared experts, and the device slot table.
+ * Returns FT_OK, FT_WARN_STAGING_SMALL (pool usable for decode only), or an
+ * error (then *out is NULL).  Env FT_MOE_FAULT=pinned_alloc forces
+ * FT_E_OOM_PINNED (for tests). */
+int ft_moe_init_pool(const ft_moe_config *cfg, const ft_moe_weights *w, ft_moe_pool **out);
+
+/* One MoE layer call on `hip_stream` (a hipStream_t, NULL = default stream).
+ * x_bf16: dev [T][H] bf16; router_bias: dev [E] fp32 added to the logits, or
+ * NULL; out_bf16: dev [T][H] bf16 (may not alias x).  flags: FT_FWD_* |
+ * FT_ACT_*.  Decode blocks the host once per wave to read the miss list and
+ * returns after the work is enqueued.  On error no slot stays assigned to an
+ * expert whose copy failed.  Env FT_MOE_FAULT=copy:<n> fails the n-th miss
+ * copy of the pool (for tests). */
+int ft_moe_layer_forward(ft_moe_pool *p, int32_t layer, int32_t num_tokens, const void *x_bf16,
+                         const float *router_bias, void *out_bf16, int32_t flags, void *hip_stream,
+                         ft_moe_trace *trace);
+
+/* Counters of one layer (or all layers for layer = -1); synchronises the
+ * pool's device.  reset != 0 zeroes the counters afterwards. */
+int ft_moe_pool_stats(ft_moe_pool *p, int32_t layer, ft_moe_stats *out, int32_t reset);
+
+/* Streamed-miss and host-miss lists of the most recent forward call, in the
+ * order the library resolved them (waves in order, each in first-appearance
+ * order).  Host arrays of capacity `cap`; counts returned even if cap is
+ * smaller. */
+int ft_moe_last_misses(const ft_moe_pool *p, int32_t *stream_expert, int32_t *stream_slot,
+                       int32_t *n_stream, int32_t *cpu_expert, int32_t *n_cpu, int32_t cap);
+
+/* Copy of the device slot table (synchronises): slot_key[C] = layer*E+expert
+ * or -1 if free, slot_last[C] = clock value of the last use, *clock.  Host
+ * arrays of pool_slots entries; NULL members are skipped. */
+int ft_moe_pool_table(ft_moe_pool *p, int32_t *slot_key, uint64_t *slot_last, uint64_t *clock,
+                      int64_t *slots);
+
+/* Set the hybrid share used by later calls (0..1). */
+int ft_moe_set_hybrid_share(ft_moe_pool *p, double share);
+
+/* Time the host expert path on `tokens` rows of one expert of `layer`
+ * (the one-time bandwidth measurement behind the hybrid share); returns
+ * expert bytes processed per second in *bytes_per_s. */
+int ft_moe_host_expert_rate(ft_moe_pool *p, int32_t layer, int32_t tokens, int32_t iters,
+                            double *bytes_per_s);
+
+/* Per-stage timing with HIP events recorded on the stream each stage runs on
+ * (the caller's stream for kernels, the pool's copy stream for miss copies),
+ * for measurement.  `bytes` accumulates the algorithmic bytes of each stage:
+ * FFN stages count the weights of the groups they run plus their activation
+ * rows read and written; the copy stage counts the expert bytes streamed. */
+enum { FT_STAGE_ROUTER = 0, FT_STAGE_TOPK, FT_STAGE_RESOLVE, FT_STAGE_FFN_GATEUP, FT_STAGE_FFN_DOWN,
+       FT_STAGE_COMBINE, FT_STAGE_COPY, FT_STAGE_COUNT };
+typedef struct {
+  double ms[FT_STAGE_COUNT];        /* summed event-measured durations */
+  double bytes[FT_STAGE_COUNT];     /* summed algorithmic bytes */
+  double flops[FT_STAGE_COUNT];     /* summed algorithmic flops (FFN stages: 2 per multiply-add) */
+  uint64_t launches[FT_STAGE_COUNT];
+} ft_moe_profile;
+
+/* enable != 0 starts recording events around every stage of later calls. */
+int ft_moe_set_profiling(ft_moe_pool *p, int32_t enable);
+/* Waits for recorded events, returns the sums; reset != 0 clears them. */
+int ft_moe_profile_read(ft_moe_pool *p, ft_moe_profile *out, int32_t reset);
+
+void ft_moe_destroy_pool(ft_moe_pool *p);
+const char *ft_moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FTMOE_H */

@@ -1,0 +1,180 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/ftmoe.h"
+
+namespace ftmoe {
+
+// ------------------------------------------------------------ limits
+constexpr int kMaxExperts = 512;  // per layer (LDS tables in the resolve kernel)
+constexpr int kMaxTopK = 16;
+constexpr int kTileRows = 16;     // rows of one weight tile (MFMA M)
+constexpr int kTileK = 128;       // K extent of one weight tile
+constexpr int kResolveThreads = 1024;
+
+// ------------------------------------------------------------ device expert layout
+// One expert in GPU memory (and in the pinned host store, which holds the same
+// bytes so a miss is one contiguous copy):
+//   [gate codes][up codes][down codes][gate scales][up scales][down scales][tensor scales]
+// each section 256-byte aligned.  A matrix W[R][K] is cut into tiles of
+// 16 rows x 128 K, stored tile-major ([R/16][K/128]).  Inside a tile, lane
+// l = 16*q + r of a 64-wide wavefront owns row r and K range [32q, 32q+32):
+//   FP4 codes: 16 bytes per lane, 1024 per tile (nibble order unchanged)
+//   FP8 codes: 32 bytes per lane, 2048 per tile
+//   MXFP4 scales: 1 byte per lane per tile ([R/16][K/128][64])
+//   NVFP4 scales: 2 bytes per lane per tile ([R/16][K/128][64][2])
+//   FP8 scales: 16 fp32 per tile, one per row ([R/16][K/128][16])
+// so that one 16-byte load per lane fetches a whole tile of FP4 codes, and
+// the lane's 8-element sub-blocks are exactly the A operand of
+// v_mfma_f32_16x16x32_bf16 (lane 16q+r holds row r, K 8j..8j+7 of sub-step j).
+struct MatLayout {
+  int64_t codes_off;
+  int64_t scales_off;
+  int32_t rows, cols;
+};
+
+struct ExpertLayout {
+  int32_t fmt = 0, hidden = 0, inter = 0;
+  MatLayout m[3];  // 0 gate [I][H], 1 up [I][H], 2 down [H][I]
+  int64_t tscale_off = 0;  // 4 fp32 (NVFP4 per-matrix scales; others 1.0)
+  int64_t bytes = 0;
+};
+
+ExpertLayout make_layout(int fmt, int hidden, int inter);
+int64_t canonical_bytes(int fmt, int hidden, int inter);
+// canonical blob -> device layout (dst has layout.bytes bytes)
+void repack_expert(const ExpertLayout& L, const uint8_t* canonical, uint8_t* dst);
+// device layout -> one row of matrix m as exact fp64 values (tensor scale applied)
+void unpack_row_f64(const ExpertLayout& L, const uint8_t* dev_blob, int m, int row, double* out);
+// device layout -> fp32 row-major matrix m (rows*cols)
+void unpack_matrix_f32(const ExpertLayout& L, const uint8_t* dev_blob, int m, float* out);
+
+// ------------------------------------------------------------ per-call device records
+struct GroupDesc {
+  uint64_t wptr;       // device address of the expert (device layout)
+  int32_t row_begin;   // first row of the group in the grouped order
+  int32_t row_count;   // rows (pairs) of the group
+  int32_t expert;      // expert index (E for the shared expert)
+  int32_t slot;        // pool slot, -1 for host-computed, -2 for the shared expert
+};
+
+// Header the resolve kernel writes into mapped pinned memory for the host.
+struct ResolveHeader {
+  int32_t t1;            // end (exclusive) of the wave that starts at t0
+  int32_t n_groups;      // distinct experts of the wave (D)
+  int32_t n_hit_list;    // groups runnable at once (hits, plus the shared expert)
+  int32_t n_stream;      // streamed-miss groups
+  int32_t n_cpu;         // host-computed groups
+  int32_t pairs;         // pairs of the wave
+  int32_t rows;          // rows incl. shared-expert rows
+  int32_t max_rows;      // largest group
+  int32_t cpu_rows;      // rows of host-computed groups
+  int32_t rows_hit_list; // rows of the groups in the hit list (incl. shared)
+  int32_t rows_stream;   // rows of the streamed-miss groups
+  int32_t pad;
+  double min_gap;        // smallest top-k gap over the wave's tokens
+  // followed by: int32 stream_expert[n], int32 stream_slot[n], int32 cpu_expert[n],
+  // int32 cpu_row_begin[n], int32 cpu_row_count[n], int32 cpu_row_tok[rows], float cpu_row_w[rows]
+};
+
+// Counters per layer in device memory.
+enum { ST_PAIR_HITS, ST_PAIR_MISSES, ST_EXPERT_HITS, ST_EXPERT_MISSES, ST_CPU_MISSES, ST_EVICTIONS,
+       ST_BYTES_H2D, ST_CALLS, ST_COUNT };
+
+// ------------------------------------------------------------ device table
+struct DevTable {
+  int32_t* key2slot;   // [L*E], -1 if not resident
+  int32_t* slot_key;   // [C], -1 if free
+  uint64_t* slot_last; // [C]
+  int32_t* lru;        // [C] slots: free ascending, then resident by last use ascending
+  int32_t* lru_tmp;    // [C]
+  int32_t* slot_mark;  // [C] stamp of the wave that hit the slot
+  uint64_t* clock;     // [1]
+  uint64_t* stats;     // [L][ST_COUNT]
+  double* min_gap;     // [L]
+};
+
+// Arguments of the resolve / permute kernel.
+struct ResolveArgs {
+  const int32_t* sel;      // [T*k]
+  const float* w;          // [T*k]
+  const double* gap;       // [T]
+  int32_t t0, T, k, E, layer, C, mode;  // mode 0 decode, 1 staged
+  int32_t stamp;
+  double share;
+  int64_t expert_bytes;    // streamed bytes of one expert of this layer
+  int32_t hidden;
+  uint64_t arena;          // device address of slot 0
+  int64_t slot_bytes;
+  uint64_t shared_ptr;     // device address of the shared expert, 0 if none
+  DevTable tab;
+  // outputs (device)
+  uint8_t* pair_flag;      // [T*k] FT_PAIR_*
+  int32_t* pair_slot;      // [T*k]
+  int32_t* pair_row;       // [T*k] row of pair (wave-relative)
+  int32_t* row_tok;        // [rows] token of row
+  float* row_w;            // [rows]
+  GroupDesc* groups;       // [max groups + 1]
+  int32_t* glist;          // [max groups + 1]: hit list, then streamed, then host
+  int32_t* dev_header;     // device copy of the header counts (for early-exit kernels)
+  // mapped pinned memory for the host (decode only), may be 0
+  uint8_t* host_rb;
+  int64_t host_rb_cap;
+};
+
+// ------------------------------------------------------------ launchers
+// router.hip
+hipError_t launch_router_logits(const uint16_t* x, const float* wr, const float* bias, double* z,
+                                int T, int H, int E, hipStream_t s);
+hipError_t launch_topk(const double* z, int T, int E, int k, int32_t* sel, float* w, double* gap,
+                       hipStream_t s);
+// resolve.hip
+hipError_t launch_resolve(const ResolveArgs& a, hipStream_t s);
+hipError_t launch_stage_table(DevTable tab, int E, int C, int layer, int num_layers, int pairs,
+                              int64_t expert_bytes, hipStream_t s);
+hipError_t launch_uncommit(DevTable tab, const int32_t* keys, const int32_t* slots, int n, int C,
+                           hipStream_t s);
+// ffn.hip
+struct FfnArgs {
+  const GroupDesc* groups;
+  const int32_t* glist;   // group indices to run
+  int32_t n_list;         // entries of glist to run (grid dimension)
+  const int32_t* n_list_dev;  // if non-null, blocks with index >= *n_list_dev exit (prefill)
+  const uint16_t* x;      // gate/up: activations [T][H] indexed by token; down: hbuf [rows][I]
+  const int32_t* row_tok; // gate/up: token of each row
+  const float* row_w;     // down: routing weight of each row
+  uint16_t* out;          // gate/up: hbuf [rows][I]; down: pbuf [rows][H]
+  int32_t hidden, inter;
+  ExpertLayout lay;
+  int32_t act_mode;       // FT_ACT_* >> 4
+};
+hipError_t launch_ffn_gateup(const FfnArgs& a, hipStream_t s);
+hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t s);
+hipError_t launch_combine(const uint16_t* pbuf, const int32_t* pair_row, int t0, int T, int k, int H,
+                          int shared_row0, uint16_t* out, hipStream_t s);
+
+// ------------------------------------------------------------ errors
+void set_error(const char* fmt, ...);
+const char* get_error();
+
+}  // namespace ftmoe
+
+#define FT_HIP_CHECK(call)                                                              \
+  do {                                                                                 \
+    hipError_t e_ = (call);                                                            \
+    if (e_ != hipSuccess) {                                                            \
+      ::ftmoe::set_error("%s failed: %s (%s:%d)", #call, hipGetErrorString(e_), __FILE__, \
+                         __LINE__);                                                    \
+      return FT_E_HIP;                                                                 \
+    }                                                                                  \
+  } while (0)

@@ -1,0 +1,388 @@
+// Grouped SwiGLU expert FFN over the rows of each expert group, and the
+// atomic-free weighted combine.
+//
+// Per group (one expert, M rows):  G = X W_g^T, U = X W_u^T (fp32 accumulate),
+// h = bf16(silu(G) * U);  Y = h W_d^T;  p = bf16(w_row * Y).
+// out[t] = bf16( sum_j p[row(t,j)] (+ p_shared[t]) ), summed in fp32 in rank
+// order.  The pages say only that experts are SwiGLU-free-form MoE experts in
+// MXFP4 / NVFP4 / FP8 (devpik article "FreeToken: Run Frontier MoE Models on
+// Your Own GPU...", "The Real Requirement Is System RAM"); the rounding points
+// are this library's reading and match the oracle's.
+//
+// gfx950 design.  The weights stream from HBM once per group; a wavefront owns
+// a 16-row tile of W and a slice of K.  One 16-byte load per lane brings a
+// whole 16x128 tile of FP4 codes in the device layout (see common.h);
+// v_cvt_scalef32_pk_bf16_fp4 turns each byte into two bf16 values already
+// multiplied by the block scale (exact: E2M1 x E8M0 and E2M1 x E4M3 fit bf16),
+// and v_mfma_f32_16x16x32_bf16 multiplies the 16x32 weight block by 32 K of
+// 16 rows of bf16 activations, which are loaded as-is (they are exactly the B
+// operand, 8 consecutive K per lane).  FP8-b128 weights convert with unit
+// scale and their fp32 block scale is applied to each 128-K partial sum.
+// Split-K slices of one row tile are summed through LDS in a fixed order.
+#include "common.h"
+
+namespace ftmoe {
+
+namespace {
+
+typedef short bf16x8 __attribute__((ext_vector_type(8)));
+typedef short bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMaxWaves = 8;  // 512 threads: up to 256 VGPRs per wave
+
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ inline float e8m0_to_f32(uint32_t b) {
+  return b == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(b << 23);
+}
+
+__device__ inline float e4m3_to_f32(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  const float mag = e == 0 ? float(m) * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (b & 0x80u) ? -mag : mag;
+}
+
+// 8 FP4 codes (one dword, element 2i in the low nibble of byte i) -> 8 bf16 x scale
+__device__ inline bf16x8 fp4x8_to_bf16(uint32_t w, float s) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3);
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+// 8 E4M3 codes (two dwords) -> 8 bf16 (exact)
+__device__ inline bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+__device__ inline bf16x8 as_bf16x8(uint4 v) {
+  bf16x8 r;
+  r[0] = short(v.x & 0xFFFF); r[1] = short(v.x >> 16);
+  r[2] = short(v.y & 0xFFFF); r[3] = short(v.y >> 16);
+  r[4] = short(v.z & 0xFFFF); r[5] = short(v.z >> 16);
+  r[6] = short(v.w & 0xFFFF); r[7] = short(v.w >> 16);
+  return r;
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (weights are read once per call: do not keep them in cache)
+__device__ inline uint4 ld_stream16(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+template <int FMT>
+struct TileRegs;
+template <>
+struct TileRegs<FT_FMT_MXFP4> {
+  uint4 c;
+  uint32_t s;  // scale byte
+};
+template <>
+struct TileRegs<FT_FMT_NVFP4> {
+  uint4 c;
+  uint32_t s;  // two scale bytes
+};
+template <>
+struct TileRegs<FT_FMT_FP8_B128> {
+  uint4 c0, c1;  // block scales are read at use (see tile_mma)
+};
+
+template <int FMT>
+__device__ inline void load_tile(TileRegs<FMT>& r, const uint8_t* __restrict__ W, const MatLayout& m, int64_t tile,
+                                 int lane) {
+  if constexpr (FMT == FT_FMT_FP8_B128) {
+    const uint8_t* p = W + m.codes_off + (tile * 64 + lane) * 32;
+    r.c0 = ld_stream16(p);
+    r.c1 = ld_stream16(p + 16);
+  } else {
+    r.c = ld_stream16(W + m.codes_off + (tile * 64 + lane) * 16);
+    if constexpr (FMT == FT_FMT_MXFP4)
+      r.s = W[m.scales_off + tile * 64 + lane];
+    else
+      r.s = *reinterpret_cast<const uint16_t*>(W + m.scales_off + (tile * 64 + lane) * 2);
+  }
+}
+
+// acc += W_tile(16 x 128) * X(128 x 16)
+// For FP8-b128, fp8_scales points at the fp32 scales of the 4 accumulator rows
+// this lane holds (rows 4q..4q+3 of the tile).
+template <int FMT>
+__device__ inline void tile_mma(const TileRegs<FMT>& r, const uint4 xv[4], floatx4& acc,
+                                const float* __restrict__ fp8_scales) {
+  if constexpr (FMT == FT_FMT_FP8_B128) {
+    floatx4 t = {0.f, 0.f, 0.f, 0.f};
+    const uint32_t w[8] = {r.c0.x, r.c0.y, r.c0.z, r.c0.w, r.c1.x, r.c1.y, r.c1.z, r.c1.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(w[2 * j], w[2 * j + 1]), as_bf16x8(xv[j]), t, 0, 0,
+                                                  0);
+    const float4 sc = *reinterpret_cast<const float4*>(fp8_scales);
+    acc[0] += sc.x * t[0];
+    acc[1] += sc.y * t[1];
+    acc[2] += sc.z * t[2];
+    acc[3] += sc.w * t[3];
+  } else {
+    const uint32_t w[4] = {r.c.x, r.c.y, r.c.z, r.c.w};
+    float s0, s1;
+    if constexpr (FMT == FT_FMT_MXFP4) {
+      s0 = s1 = e8m0_to_f32(r.s);
+    } else {
+      s0 = e4m3_to_f32(r.s & 0xFFu);
+      s1 = e4m3_to_f32(r.s >> 8);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4x8_to_bf16(w[j], j < 2 ? s0 : s1), as_bf16x8(xv[j]), acc, 0,
+                                                    0, 0);
+  }
+}
+
+// K tiles (of 128) a wavefront holds in registers
+constexpr int kpw_max(int fmt, bool gateup) { return (fmt == FT_FMT_FP8_B128 && gateup) ? 6 : 8; }
+
+// GATEUP: rows of matrices 0 (gate) and 1 (up) over K = H, epilogue SwiGLU -> hbuf.
+// else:   rows of matrix 2 (down) over K = I, epilogue routing weight -> pbuf.
+template <int FMT, bool GATEUP>
+__global__ __launch_bounds__(64 * kMaxWaves) void k_ffn(FfnArgs a, int SK, int RB, int kpw) {
+  constexpr int KPW = kpw_max(FMT, GATEUP);
+  constexpr int NM = GATEUP ? 2 : 1;
+  __shared__ floatx4 red[kMaxWaves][NM][64];
+
+  const int gi = blockIdx.y;
+  if (a.n_list_dev != nullptr && gi >= *a.n_list_dev) return;
+  const GroupDesc g = a.groups[a.glist[gi]];
+  if (g.row_count <= 0) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int rbl = w / SK, sk = w % SK;
+  const int rb = blockIdx.x * RB + rbl;
+  const uint8_t* W = reinterpret_cast<const uint8_t*>(g.wptr);
+  const MatLayout& m0 = a.lay.m[GATEUP ? 0 : 2];
+  const int K = m0.cols;
+  const int nkb = K / kTileK;
+  const int kb0 = sk * kpw;
+
+  // weights of this wave's (row tile, K slice), loaded once
+  TileRegs<FMT> tr[NM][KPW];
+#pragma unroll
+  for (int mi = 0; mi < NM; ++mi) {
+    const MatLayout& m = a.lay.m[GATEUP ? mi : 2];
+#pragma unroll
+    for (int t = 0; t < KPW; ++t)
+      if (t < kpw) load_tile<FMT>(tr[mi][t], W, m, int64_t(rb) * nkb + kb0 + t, lane);
+  }
+  float tsc[NM];
+  {
+    const float* ts = reinterpret_cast<const float*>(W + a.lay.tscale_off);
+#pragma unroll
+    for (int mi = 0; mi < NM; ++mi) tsc[mi] = FMT == FT_FMT_NVFP4 ? ts[GATEUP ? mi : 2] : 1.0f;
+  }
+
+  const int q = lane >> 4, n = lane & 15;
+  const int ntiles = (g.row_count + 15) / 16;
+  for (int nt = 0; nt < ntiles; ++nt) {
+    const int r = nt * 16 + n;
+    const bool valid = r < g.row_count;
+    const int row = g.row_begin + r;
+    int64_t xbase = 0;
+    if (valid) xbase = GATEUP ? int64_t(a.row_tok[row]) * a.hidden : int64_t(row) * a.inter;
+
+    floatx4 acc[NM];
+#pragma unroll
+    for (int mi = 0; mi < NM; ++mi) acc[mi] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < KPW; ++t) {
+      if (t < kpw) {
+        uint4 xv[4];
+        const int64_t off = xbase + int64_t(kb0 + t) * kTileK + 32 * q;
+        if (valid) {
+          const uint4* xp = reinterpret_cast<const uint4*>(a.x + off);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) xv[j] = xp[j];
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) xv[j] = make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int mi = 0; mi < NM; ++mi) {
+          const float* sp = nullptr;
+          if constexpr (FMT == FT_FMT_FP8_B128)
+            sp = reinterpret_cast<const float*>(W + a.lay.m[GATEUP ? mi : 2].scales_off) +
+                 (int64_t(rb) * nkb + kb0 + t) * 16 + 4 * q;
+          tile_mma<FMT>(tr[mi][t], xv, acc[mi], sp);
+        }
+      }
+    }
+    if (SK > 1) {
+#pragma unroll
+      for (int mi = 0; mi < NM; ++mi) red[w][mi][lane] = acc[mi];
+      __syncthreads();
+      if (sk == 0) {
+#pragma unroll
+        for (int mi = 0; mi < NM; ++mi) {
+          floatx4 s = red[w][mi][lane];
+          for (int k2 = 1; k2 < SK; ++k2) {
+            const floatx4 v = red[w + k2][mi][lane];
+            s[0] += v[0]; s[1] += v[1]; s[2] += v[2]; s[3] += v[3];
+          }
+          acc[mi] = s;
+        }
+      }
+    }
+    if (sk == 0 && valid) {
+      // lane holds output features rb*16 + 4q + i of row r
+      const int o0 = rb * 16 + 4 * q;
+      uint16_t hv[4];
+      if constexpr (GATEUP) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float gv = acc[0][i] * tsc[0];
+          const float uv = acc[1][i] * tsc[1];
+          hv[i] = f32_to_bf16_rne(gv / (1.0f + expf(-gv)) * uv);
+        }
+        uint2 pk = make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16), uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
+        *reinterpret_cast<uint2*>(a.out + int64_t(row) * a.inter + o0) = pk;
+      } else {
+        const float wr = a.row_w[row];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hv[i] = f32_to_bf16_rne(wr * (acc[0][i] * tsc[0]));
+        uint2 pk = make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16), uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
+        *reinterpret_cast<uint2*>(a.out + int64_t(row) * a.hidden + o0) = pk;
+      }
+    }
+    if (SK > 1) __syncthreads();
+  }
+}
+
+struct Split {
+  int SK, RB, kpw;
+};
+
+// K tiles per wave (kpw) and waves per row tile (SK): prefer short K slices
+// (more waves, more loads in flight), at most kMaxWaves waves per workgroup.
+Split choose_split(int K, int R, int kpwmax) {
+  const int nkb = K / kTileK, nrb = R / kTileRows;
+  Split s{0, 0, 0};
+  for (int pass = 0; pass < 2 && s.SK == 0; ++pass) {
+    const int lo = pass == 0 ? 1 : 5, hi = pass == 0 ? 4 : kpwmax;
+    for (int kpw = hi; kpw >= lo; --kpw)
+      if (nkb % kpw == 0 && nkb / kpw <= kMaxWaves) {
+        s.kpw = kpw;
+        s.SK = nkb / kpw;
+        break;
+      }
+  }
+  if (s.SK == 0) return s;
+  const int cap = s.SK > 4 ? s.SK : 4;
+  s.RB = 1;
+  for (int rb : {4, 2}) {
+    if (rb * s.SK <= cap && nrb % rb == 0) {
+      s.RB = rb;
+      break;
+    }
+  }
+  return s;
+}
+
+template <bool GATEUP>
+hipError_t launch_ffn(const FfnArgs& a, hipStream_t st) {
+  if (a.n_list <= 0) return hipSuccess;
+  const MatLayout& m = a.lay.m[GATEUP ? 0 : 2];
+  const int fmt = a.lay.fmt;
+  const Split s = choose_split(m.cols, m.rows, kpw_max(fmt, GATEUP));
+  if (s.SK == 0) return hipErrorInvalidValue;
+  const dim3 grid(m.rows / kTileRows / s.RB, a.n_list);
+  const dim3 block(64 * s.RB * s.SK);
+  switch (fmt) {
+    case FT_FMT_MXFP4:
+      hipLaunchKernelGGL((k_ffn<FT_FMT_MXFP4, GATEUP>), grid, block, 0, st, a, s.SK, s.RB, s.kpw);
+      break;
+    case FT_FMT_NVFP4:
+      hipLaunchKernelGGL((k_ffn<FT_FMT_NVFP4, GATEUP>), grid, block, 0, st, a, s.SK, s.RB, s.kpw);
+      break;
+    case FT_FMT_FP8_B128:
+      hipLaunchKernelGGL((k_ffn<FT_FMT_FP8_B128, GATEUP>), grid, block, 0, st, a, s.SK, s.RB, s.kpw);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// out[t][h..h+7] = bf16( sum_j fp32(P[row(t,j)][h..h+7]) (+ fp32(P[shared row])) )
+__global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ pbuf,
+                                                 const int32_t* __restrict__ pair_row, int t0, int k, int H,
+                                                 int shared_row0, uint16_t* __restrict__ out) {
+  const int tt = blockIdx.y;
+  const int t = t0 + tt;
+  const int h = (blockIdx.x * 256 + threadIdx.x) * 8;
+  if (h >= H) return;
+  float acc[8];
+  for (int j = 0; j < k; ++j) {
+    const int row = pair_row[int64_t(t) * k + j];
+    const uint4 v = *reinterpret_cast<const uint4*>(pbuf + int64_t(row) * H + h);
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = __uint_as_float(u[i] << 16), hi = __uint_as_float(u[i] & 0xFFFF0000u);
+      if (j == 0) {
+        acc[2 * i] = lo;
+        acc[2 * i + 1] = hi;
+      } else {
+        acc[2 * i] += lo;
+        acc[2 * i + 1] += hi;
+      }
+    }
+  }
+  if (shared_row0 >= 0) {
+    const uint4 v = *reinterpret_cast<const uint4*>(pbuf + int64_t(shared_row0 + tt) * H + h);
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += __uint_as_float(u[i] << 16);
+      acc[2 * i + 1] += __uint_as_float(u[i] & 0xFFFF0000u);
+    }
+  }
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = uint32_t(f32_to_bf16_rne(acc[2 * i])) | (uint32_t(f32_to_bf16_rne(acc[2 * i + 1])) << 16);
+  *reinterpret_cast<uint4*>(out + int64_t(t) * H + h) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+}  // namespace
+
+bool ffn_shape_ok(int fmt, int hidden, int inter) {
+  return choose_split(hidden, inter, kpw_max(fmt, true)).SK > 0 &&
+         choose_split(inter, hidden, kpw_max(fmt, false)).SK > 0;
+}
+
+hipError_t launch_ffn_gateup(const FfnArgs& a, hipStream_t s) { return launch_ffn<true>(a, s); }
+hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t s) { return launch_ffn<false>(a, s); }
+
+hipError_t launch_combine(const uint16_t* pbuf, const int32_t* pair_row, int t0, int T, int k, int H,
+                          int shared_row0, uint16_t* out, hipStream_t s) {
+  if (T <= t0) return hipSuccess;
+  const dim3 grid((H / 8 + 255) / 256, T - t0);
+  hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, s, pbuf, pair_row, t0, k, H, shared_row0, out);
+  return hipGetLastError();
+}
+
+}  // namespace ftmoe

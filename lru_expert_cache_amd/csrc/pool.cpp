@@ -1,0 +1,957 @@
+// Host runtime of the offloaded MoE layer: pool creation, the per-call
+// orchestration (router -> resolve -> miss copies -> FFN -> combine), prefill
+// double-buffered staging, the hybrid host worker, statistics.
+//
+// Pages (FreeToken, by title and section): experts in host RAM, a GPU LRU
+// cache of expert slots, misses streamed over PCIe, hybrid split of a step's
+// misses, one global pool across layers -- devpik article "FreeToken: Run
+// Frontier MoE Models on Your Own GPU, and the RAM It Takes", section "Why a
+// Huge MoE Model Fits on One Consumer GPU"; prefill copies every expert of a
+// layer per chunk, layer N+1 copied while N computes, warning when the cache
+// cannot hold the two staging layers -- same article, "Long Prompts Are the
+// Bottleneck"; pinned host memory -- same article, "The Real Requirement Is
+// System RAM".
+#include <algorithm>
+#include <chrono>
+#include <cmath>
+#include <cstdarg>
+#include <cstdlib>
+#include <functional>
+#include <map>
+#include <memory>
+#include <thread>
+
+#include "common.h"
+
+namespace ftmoe {
+
+static thread_local std::string g_err;
+
+void set_error(const char* fmt, ...) {
+  char buf[1024];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+}
+const char* get_error() { return g_err.c_str(); }
+
+bool ffn_shape_ok(int fmt, int hidden, int inter);
+
+}  // namespace ftmoe
+
+using namespace ftmoe;
+
+struct ft_moe_pool {
+  int L = 0, H = 0, I = 0, E = 0, k = 0, shared = 0, device = 0, cpu_threads = 8;
+  int64_t C = 0;
+  std::vector<int32_t> fmt;
+  ExpertLayout lay[4];
+  int64_t canon_bytes[4] = {0, 0, 0, 0};
+  int64_t slot_bytes = 0;
+  double share = 0.0;
+
+  // pinned host store (device layout), one entry per distinct (blob, format)
+  uint8_t* host_store = nullptr;
+  int64_t host_bytes = 0;
+  std::vector<int64_t> key_off;     // [L*E]
+  std::vector<uint8_t> layer_contig;
+
+  // device memory
+  uint8_t* arena = nullptr;
+  uint8_t* shared_dev = nullptr;
+  int64_t shared_stride = 0;
+  float* router_dev = nullptr;
+  DevTable tab{};
+
+  // work buffers (grow with T)
+  int cap_T = 0;
+  double* z = nullptr;
+  int32_t* sel = nullptr;
+  float* w = nullptr;
+  double* gap = nullptr;
+  uint8_t* pair_flag = nullptr;
+  int32_t* pair_slot = nullptr;
+  int32_t* pair_row = nullptr;
+  int32_t* row_tok = nullptr;
+  float* row_w = nullptr;
+  GroupDesc* groups = nullptr;
+  int32_t* glist = nullptr;
+  int32_t* dev_header = nullptr;
+  uint16_t* hbuf = nullptr;
+  uint16_t* pbuf = nullptr;
+  uint8_t* rb_host = nullptr;
+  uint8_t* rb_dev = nullptr;
+  int64_t rb_cap = 0;
+  uint16_t* x_host = nullptr;       // pinned copy of x for host-computed experts
+  uint16_t* cpu_out = nullptr;      // pinned result rows of host-computed experts
+  int32_t* fail_dev = nullptr;      // [2*E] keys and slots whose copy failed
+
+  hipStream_t copy_stream = nullptr;
+  hipEvent_t ev_resolved = nullptr, ev_copied = nullptr, ev_sync = nullptr, ev_cpu_copied = nullptr;
+  hipEvent_t ev_done[2] = {nullptr, nullptr}, ev_staged[2] = {nullptr, nullptr};
+  bool cpu_copy_pending = false;
+
+  int32_t stamp = 0;
+  int prefill_next = 0;
+  uint64_t copy_counter = 0;
+  int64_t fault_copy = -1;
+
+  std::vector<int32_t> last_se, last_ss, last_ce;
+
+  // stage timing (ft_moe_set_profiling)
+  struct ProfRec {
+    int stage;
+    hipEvent_t a, b;
+    double bytes, flops;
+  };
+  bool profiling = false;
+  std::vector<ProfRec> prof_pending;
+  std::vector<hipEvent_t> prof_free;
+  ft_moe_profile prof{};
+};
+
+namespace {
+
+struct DeviceGuard {
+  int prev = -1;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != dev) (void)hipSetDevice(dev);
+  }
+  ~DeviceGuard() {
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+template <typename T>
+int dev_alloc(T** p, int64_t n) {
+  if (hipMalloc(reinterpret_cast<void**>(p), size_t(n) * sizeof(T) + 16) != hipSuccess) {
+    *p = nullptr;
+    (void)hipGetLastError();
+    set_error("device allocation of %lld bytes failed", (long long)(n * sizeof(T)));
+    return FT_E_OOM_DEVICE;
+  }
+  return FT_OK;
+}
+
+void parallel_for(int n, int threads, const std::function<void(int, int)>& fn) {
+  threads = std::max(1, std::min(threads, n));
+  if (threads == 1) {
+    fn(0, n);
+    return;
+  }
+  std::vector<std::thread> th;
+  const int chunk = (n + threads - 1) / threads;
+  for (int t = 0; t < threads; ++t) {
+    const int b = t * chunk, e = std::min(n, b + chunk);
+    if (b >= e) break;
+    th.emplace_back(fn, b, e);
+  }
+  for (auto& x : th) x.join();
+}
+
+inline uint16_t bf16_from_double(double x) {
+  float f;
+  if (x == 0.0 || !std::isfinite(x)) {
+    f = float(x);
+  } else {
+    int e;
+    std::frexp(x, &e);
+    e = std::max(e, -125);
+    const double q = std::ldexp(1.0, e - 8);
+    f = float(std::nearbyint(x / q) * q);
+  }
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  return uint16_t(u >> 16);
+}
+
+inline double bf16_to_double(uint16_t b) {
+  const uint32_t u = uint32_t(b) << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+// Host SwiGLU expert on `rows` rows of x (bf16, [rows][H]), weights in the
+// device layout; writes p = bf16(w * y) rows.  fp64 accumulation; the same
+// rounding points as the GPU path.
+void host_expert(const ExpertLayout& L, const uint8_t* blob, const uint16_t* x, const float* wts, int rows,
+                 uint16_t* out, int threads) {
+  const int H = L.hidden, I = L.inter;
+  std::vector<double> xd(size_t(rows) * H), hd(size_t(rows) * I);
+  for (size_t i = 0; i < xd.size(); ++i) xd[i] = bf16_to_double(x[i]);
+  parallel_for(I, threads, [&](int b, int e) {
+    std::vector<double> rg(H), ru(H);
+    for (int i = b; i < e; ++i) {
+      unpack_row_f64(L, blob, 0, i, rg.data());
+      unpack_row_f64(L, blob, 1, i, ru.data());
+      for (int r = 0; r < rows; ++r) {
+        const double* xr = &xd[size_t(r) * H];
+        double g = 0.0, u = 0.0;
+        for (int h = 0; h < H; ++h) {
+          g += rg[h] * xr[h];
+          u += ru[h] * xr[h];
+        }
+        hd[size_t(r) * I + i] = bf16_to_double(bf16_from_double(g / (1.0 + std::exp(-g)) * u));
+      }
+    }
+  });
+  parallel_for(H, threads, [&](int b, int e) {
+    std::vector<double> rd(I);
+    for (int o = b; o < e; ++o) {
+      unpack_row_f64(L, blob, 2, o, rd.data());
+      for (int r = 0; r < rows; ++r) {
+        const double* hr = &hd[size_t(r) * I];
+        double y = 0.0;
+        for (int i = 0; i < I; ++i) y += rd[i] * hr[i];
+        out[size_t(r) * H + o] = bf16_from_double(double(wts[r]) * y);
+      }
+    }
+  });
+}
+
+int ensure_capacity(ft_moe_pool* p, int T) {
+  if (T <= p->cap_T) return FT_OK;
+  const int cap = std::max(T, 64);
+  hipFree(p->z); hipFree(p->sel); hipFree(p->w); hipFree(p->gap); hipFree(p->pair_flag);
+  hipFree(p->pair_slot); hipFree(p->pair_row); hipFree(p->row_tok); hipFree(p->row_w);
+  hipFree(p->hbuf); hipFree(p->pbuf);
+  if (p->rb_host) hipHostFree(p->rb_host);
+  if (p->x_host) hipHostFree(p->x_host);
+  if (p->cpu_out) hipHostFree(p->cpu_out);
+  p->rb_host = nullptr;
+  p->x_host = nullptr;
+  p->cpu_out = nullptr;
+  p->cap_T = 0;
+  const int64_t pairs = int64_t(cap) * p->k;
+  const int64_t rows = pairs + (p->shared ? cap : 0);
+  int rc;
+  if ((rc = dev_alloc(&p->z, int64_t(cap) * p->E))) return rc;
+  if ((rc = dev_alloc(&p->sel, pairs))) return rc;
+  if ((rc = dev_alloc(&p->w, pairs))) return rc;
+  if ((rc = dev_alloc(&p->gap, cap))) return rc;
+  if ((rc = dev_alloc(&p->pair_flag, pairs))) return rc;
+  if ((rc = dev_alloc(&p->pair_slot, pairs))) return rc;
+  if ((rc = dev_alloc(&p->pair_row, pairs))) return rc;
+  if ((rc = dev_alloc(&p->row_tok, rows))) return rc;
+  if ((rc = dev_alloc(&p->row_w, rows))) return rc;
+  if ((rc = dev_alloc(&p->hbuf, rows * p->I))) return rc;
+  if ((rc = dev_alloc(&p->pbuf, rows * p->H))) return rc;
+  p->rb_cap = int64_t(sizeof(ResolveHeader)) + 5 * 4 * int64_t(p->E) + 8 * pairs + 64;
+  if (hipHostMalloc(reinterpret_cast<void**>(&p->rb_host), p->rb_cap, hipHostMallocMapped | hipHostMallocCoherent) !=
+      hipSuccess) {
+    set_error("pinned readback allocation failed");
+    return FT_E_OOM_PINNED;
+  }
+  FT_HIP_CHECK(hipHostGetDevicePointer(reinterpret_cast<void**>(&p->rb_dev), p->rb_host, 0));
+  if (hipHostMalloc(reinterpret_cast<void**>(&p->x_host), size_t(cap) * p->H * 2, hipHostMallocDefault) !=
+          hipSuccess ||
+      hipHostMalloc(reinterpret_cast<void**>(&p->cpu_out), size_t(pairs) * p->H * 2, hipHostMallocDefault) !=
+          hipSuccess) {
+    set_error("pinned staging allocation failed");
+    return FT_E_OOM_PINNED;
+  }
+  p->cap_T = cap;
+  return FT_OK;
+}
+
+int fail_copies(ft_moe_pool* p, int layer, const int32_t* se, const int32_t* ss, int from, int n,
+                hipStream_t s) {
+  const std::string msg = get_error();
+  std::vector<int32_t> buf;
+  for (int i = from; i < n; ++i) buf.push_back(layer * p->E + se[i]);
+  for (int i = from; i < n; ++i) buf.push_back(ss[i]);
+  const int m = n - from;
+  if (m > 0) {
+    FT_HIP_CHECK(hipMemcpy(p->fail_dev, buf.data(), buf.size() * 4, hipMemcpyHostToDevice));
+    FT_HIP_CHECK(launch_uncommit(p->tab, p->fail_dev, p->fail_dev + m, m, int(p->C), s));
+    FT_HIP_CHECK(hipStreamSynchronize(s));
+  }
+  set_error("%s", msg.c_str());
+  return FT_E_HIP;
+}
+
+int issue_copy(ft_moe_pool* p, void* dst, const void* src, size_t bytes) {
+  ++p->copy_counter;
+  if (p->fault_copy >= 0 && int64_t(p->copy_counter) == p->fault_copy) {
+    set_error("injected failure of miss copy %llu", (unsigned long long)p->copy_counter);
+    return FT_E_HIP;
+  }
+  FT_HIP_CHECK(hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, p->copy_stream));
+  return FT_OK;
+}
+
+FfnArgs ffn_args(ft_moe_pool* p, int layer, int list_off, int n, const int32_t* n_dev) {
+  FfnArgs a{};
+  a.groups = p->groups;
+  a.glist = p->glist + list_off;
+  a.n_list = n;
+  a.n_list_dev = n_dev;
+  a.row_tok = p->row_tok;
+  a.row_w = p->row_w;
+  a.hidden = p->H;
+  a.inter = p->I;
+  a.lay = p->lay[p->fmt[layer]];
+  a.act_mode = 0;
+  return a;
+}
+
+double mat_bytes(int fmt, double rows, double cols);
+hipEvent_t prof_begin(ft_moe_pool* p, hipStream_t s);
+void prof_end(ft_moe_pool* p, int stage, hipEvent_t a, hipStream_t s, double bytes, double flops);
+
+// groups / rows: how many expert groups and rows this launch runs (for the
+// algorithmic byte and flop counts of the stage timers).
+int run_ffn(ft_moe_pool* p, int layer, const void* x, int list_off, int n, const int32_t* n_dev, hipStream_t s,
+            double groups, double rows) {
+  FfnArgs a = ffn_args(p, layer, list_off, n, n_dev);
+  const int f = p->fmt[layer];
+  const double H = p->H, I = p->I;
+  a.x = static_cast<const uint16_t*>(x);
+  a.out = p->hbuf;
+  hipEvent_t e0 = prof_begin(p, s);
+  FT_HIP_CHECK(launch_ffn_gateup(a, s));
+  prof_end(p, FT_STAGE_FFN_GATEUP, e0, s, groups * 2 * mat_bytes(f, I, H) + rows * (H + I) * 2, rows * 4 * H * I);
+  a.x = p->hbuf;
+  a.out = p->pbuf;
+  e0 = prof_begin(p, s);
+  FT_HIP_CHECK(launch_ffn_down(a, s));
+  prof_end(p, FT_STAGE_FFN_DOWN, e0, s, groups * mat_bytes(f, H, I) + rows * (I + H) * 2, rows * 2 * H * I);
+  return FT_OK;
+}
+
+ResolveArgs resolve_args(ft_moe_pool* p, int layer, int T, int t0, int mode) {
+  ResolveArgs a{};
+  a.sel = p->sel;
+  a.w = p->w;
+  a.gap = p->gap;
+  a.t0 = t0;
+  a.T = T;
+  a.k = p->k;
+  a.E = p->E;
+  a.layer = layer;
+  a.C = int(p->C);
+  a.mode = mode;
+  a.stamp = p->stamp++;
+  a.share = p->share;
+  a.expert_bytes = p->canon_bytes[p->fmt[layer]];
+  a.hidden = p->H;
+  a.arena = reinterpret_cast<uint64_t>(p->arena);
+  a.slot_bytes = p->slot_bytes;
+  a.shared_ptr = p->shared ? reinterpret_cast<uint64_t>(p->shared_dev + int64_t(layer) * p->shared_stride) : 0;
+  a.tab = p->tab;
+  a.pair_flag = p->pair_flag;
+  a.pair_slot = p->pair_slot;
+  a.pair_row = p->pair_row;
+  a.row_tok = p->row_tok;
+  a.row_w = p->row_w;
+  a.groups = p->groups;
+  a.glist = p->glist;
+  a.dev_header = p->dev_header;
+  a.host_rb = mode == 0 ? p->rb_dev : nullptr;
+  a.host_rb_cap = p->rb_cap;
+  return a;
+}
+
+// ---- stage timing
+hipEvent_t prof_event(ft_moe_pool* p) {
+  if (!p->prof_free.empty()) {
+    hipEvent_t e = p->prof_free.back();
+    p->prof_free.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+hipEvent_t prof_begin(ft_moe_pool* p, hipStream_t s) {
+  if (!p->profiling) return nullptr;
+  hipEvent_t e = prof_event(p);
+  if (e) (void)hipEventRecord(e, s);
+  return e;
+}
+
+void prof_end(ft_moe_pool* p, int stage, hipEvent_t a, hipStream_t s, double bytes, double flops = 0.0) {
+  if (!p->profiling || !a) return;
+  hipEvent_t b = prof_event(p);
+  if (!b) return;
+  (void)hipEventRecord(b, s);
+  p->prof_pending.push_back({stage, a, b, bytes, flops});
+}
+
+// Fold finished records into the sums (all of them if wait).
+void prof_drain(ft_moe_pool* p, bool wait) {
+  std::vector<ft_moe_pool::ProfRec> keep;
+  for (auto& r : p->prof_pending) {
+    if (wait)
+      (void)hipEventSynchronize(r.b);
+    else if (hipEventQuery(r.b) != hipSuccess) {
+      keep.push_back(r);
+      continue;
+    }
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) {
+      p->prof.ms[r.stage] += ms;
+      p->prof.bytes[r.stage] += r.bytes;
+      p->prof.flops[r.stage] += r.flops;
+      p->prof.launches[r.stage] += 1;
+    }
+    p->prof_free.push_back(r.a);
+    p->prof_free.push_back(r.b);
+  }
+  (void)hipGetLastError();
+  p->prof_pending.swap(keep);
+}
+
+// Algorithmic bytes of the weights of one matrix (codes + block scales).
+double mat_bytes(int fmt, double rows, double cols) {
+  const double n = rows * cols;
+  switch (fmt) {
+    case FT_FMT_MXFP4: return n / 2 + n / 32;
+    case FT_FMT_NVFP4: return n / 2 + n / 16;
+    default: return n + n / 128 * 4;
+  }
+}
+
+int copy_layer_staging(ft_moe_pool* p, int layer) {
+  const int E = p->E;
+  const int half = layer & 1;
+  uint8_t* dst = p->arena + int64_t(half) * E * p->slot_bytes;
+  const ExpertLayout& L = p->lay[p->fmt[layer]];
+  hipEvent_t e0 = prof_begin(p, p->copy_stream);
+  if (p->layer_contig[layer]) {
+    FT_HIP_CHECK(hipMemcpyAsync(dst, p->host_store + p->key_off[int64_t(layer) * E], size_t(E) * p->slot_bytes,
+                                hipMemcpyHostToDevice, p->copy_stream));
+  } else {
+    for (int e = 0; e < E; ++e)
+      FT_HIP_CHECK(hipMemcpyAsync(dst + int64_t(e) * p->slot_bytes, p->host_store + p->key_off[int64_t(layer) * E + e],
+                                  size_t(L.bytes), hipMemcpyHostToDevice, p->copy_stream));
+  }
+  prof_end(p, FT_STAGE_COPY, e0, p->copy_stream, double(E) * double(p->canon_bytes[p->fmt[layer]]), 0.0);
+  FT_HIP_CHECK(hipEventRecord(p->ev_staged[half], p->copy_stream));
+  return FT_OK;
+}
+
+int forward_prefill(ft_moe_pool* p, int layer, int T, const void* x, void* out, hipStream_t s) {
+  const int L = p->L, E = p->E;
+  if (p->C < 2 * int64_t(E)) {
+    set_error("prefill staging needs 2*E = %d slots, pool has %lld", 2 * E, (long long)p->C);
+    return FT_E_INVALID;
+  }
+  if (!(layer == 0 || layer == p->prefill_next)) {
+    set_error("prefill layer %d out of order (expected 0 or %d)", layer, p->prefill_next);
+    return FT_E_STATE;
+  }
+  // table: the staging halves lose their LRU residents
+  FT_HIP_CHECK(launch_stage_table(p->tab, E, int(p->C), layer, L, T * p->k, 0, s));
+  if (layer == 0) {
+    // first copy of the chunk: after every earlier reader of half 0 on s
+    FT_HIP_CHECK(hipEventRecord(p->ev_sync, s));
+    FT_HIP_CHECK(hipStreamWaitEvent(p->copy_stream, p->ev_sync, 0));
+    int rc = copy_layer_staging(p, 0);
+    if (rc) return rc;
+  }
+  if (layer + 1 < L) {
+    // half (layer+1)%2 was last read by layer-1 (or by earlier decode work)
+    if (layer >= 1) {
+      FT_HIP_CHECK(hipStreamWaitEvent(p->copy_stream, p->ev_done[(layer - 1) & 1], 0));
+    }
+    int rc = copy_layer_staging(p, layer + 1);
+    if (rc) return rc;
+  }
+  FT_HIP_CHECK(hipStreamWaitEvent(s, p->ev_staged[layer & 1], 0));
+  ResolveArgs ra = resolve_args(p, layer, T, 0, 1);
+  hipEvent_t er = prof_begin(p, s);
+  FT_HIP_CHECK(launch_resolve(ra, s));
+  prof_end(p, FT_STAGE_RESOLVE, er, s, 0.0, 0.0);
+  const double rows = double(T) * p->k + (p->shared ? T : 0);
+  int rc = run_ffn(p, layer, x, 0, E + 1, p->dev_header + 9, s, E + p->shared, rows);
+  if (rc) return rc;
+  hipEvent_t e0 = prof_begin(p, s);
+  FT_HIP_CHECK(launch_combine(p->pbuf, p->pair_row, 0, T, p->k, p->H, p->shared ? T * p->k : -1,
+                              static_cast<uint16_t*>(out), s));
+  prof_end(p, FT_STAGE_COMBINE, e0, s, (rows + T) * p->H * 2.0, 0.0);
+  FT_HIP_CHECK(hipEventRecord(p->ev_done[layer & 1], s));
+  p->prefill_next = layer + 1 == L ? 0 : layer + 1;
+  return FT_OK;
+}
+
+int forward_decode(ft_moe_pool* p, int layer, int T, const void* x, void* out, hipStream_t s) {
+  const int E = p->E, k = p->k;
+  const ExpertLayout& L = p->lay[p->fmt[layer]];
+  p->last_se.clear();
+  p->last_ss.clear();
+  p->last_ce.clear();
+  int t0 = 0;
+  while (t0 < T) {
+    ResolveArgs ra = resolve_args(p, layer, T, t0, 0);
+    hipEvent_t er = prof_begin(p, s);
+    FT_HIP_CHECK(launch_resolve(ra, s));
+    prof_end(p, FT_STAGE_RESOLVE, er, s, 0.0, 0.0);
+    FT_HIP_CHECK(hipEventRecord(p->ev_resolved, s));
+    FT_HIP_CHECK(hipEventSynchronize(p->ev_resolved));
+    if (p->profiling) prof_drain(p, false);
+    const ResolveHeader h = *reinterpret_cast<const ResolveHeader*>(p->rb_host);
+    const int32_t* se = reinterpret_cast<const int32_t*>(p->rb_host + sizeof(ResolveHeader));
+    const int32_t* ss = se + E;
+    const int32_t* ce = ss + E;
+    const int32_t* cb = ce + E;
+    const int32_t* cc = cb + E;
+    const int32_t* ct = cc + E;
+    const float* cw = reinterpret_cast<const float*>(ct + int64_t(T) * k);
+    if (h.t1 <= t0 || h.t1 > T) {
+      set_error("resolve returned an invalid wave end %d (t0 %d, T %d)", h.t1, t0, T);
+      return FT_E_HIP;
+    }
+    for (int i = 0; i < h.n_stream; ++i) {
+      p->last_se.push_back(se[i]);
+      p->last_ss.push_back(ss[i]);
+    }
+    for (int i = 0; i < h.n_cpu; ++i) p->last_ce.push_back(ce[i]);
+
+    // streamed misses: one contiguous copy per expert on the copy stream
+    hipEvent_t ec = h.n_stream > 0 ? prof_begin(p, p->copy_stream) : nullptr;
+    for (int i = 0; i < h.n_stream; ++i) {
+      const int64_t key = int64_t(layer) * E + se[i];
+      int rc = issue_copy(p, p->arena + int64_t(ss[i]) * p->slot_bytes, p->host_store + p->key_off[key],
+                          size_t(L.bytes));
+      if (rc) return fail_copies(p, layer, se, ss, i, h.n_stream, s);
+    }
+    if (h.n_stream > 0) {
+      prof_end(p, FT_STAGE_COPY, ec, p->copy_stream, double(h.n_stream) * double(p->canon_bytes[p->fmt[layer]]), 0.0);
+      FT_HIP_CHECK(hipEventRecord(p->ev_copied, p->copy_stream));
+    }
+
+    // host-computed misses run on CPU threads while the GPU works
+    std::thread cpu_thread;
+    std::vector<int64_t> cpu_base;
+    if (h.n_cpu > 0) {
+      if (p->cpu_copy_pending) FT_HIP_CHECK(hipEventSynchronize(p->ev_cpu_copied));
+      FT_HIP_CHECK(hipMemcpy(p->x_host, x, size_t(T) * p->H * 2, hipMemcpyDeviceToHost));
+      int64_t base = 0;
+      for (int j = 0; j < h.n_cpu; ++j) {
+        cpu_base.push_back(base);
+        base += cc[j];
+      }
+      std::vector<int32_t> toks(ct, ct + h.cpu_rows);
+      std::vector<float> wts(cw, cw + h.cpu_rows);
+      std::vector<int32_t> experts(ce, ce + h.n_cpu), counts(cc, cc + h.n_cpu);
+      cpu_thread = std::thread([p, layer, toks, wts, experts, counts, cpu_base, &L]() {
+        for (size_t j = 0; j < experts.size(); ++j) {
+          const int rows = counts[j];
+          std::vector<uint16_t> xr(size_t(rows) * p->H);
+          for (int r = 0; r < rows; ++r)
+            std::memcpy(&xr[size_t(r) * p->H], p->x_host + int64_t(toks[cpu_base[j] + r]) * p->H, size_t(p->H) * 2);
+          const uint8_t* blob = p->host_store + p->key_off[int64_t(layer) * p->E + experts[j]];
+          host_expert(L, blob, xr.data(), &wts[cpu_base[j]], rows, p->cpu_out + cpu_base[j] * p->H, p->cpu_threads);
+        }
+      });
+    }
+
+    int rc = run_ffn(p, layer, x, 0, h.n_hit_list, nullptr, s, h.n_hit_list, h.rows_hit_list);
+    if (rc == FT_OK && h.n_stream > 0) {
+      FT_HIP_CHECK(hipStreamWaitEvent(s, p->ev_copied, 0));
+      rc = run_ffn(p, layer, x, h.n_hit_list, h.n_stream, nullptr, s, h.n_stream, h.rows_stream);
+    }
+    if (cpu_thread.joinable()) cpu_thread.join();
+    if (rc) return rc;
+    if (h.n_cpu > 0) {
+      for (int j = 0; j < h.n_cpu; ++j)
+        FT_HIP_CHECK(hipMemcpyAsync(p->pbuf + int64_t(cb[j]) * p->H, p->cpu_out + cpu_base[j] * p->H,
+                                    size_t(cc[j]) * p->H * 2, hipMemcpyHostToDevice, s));
+      FT_HIP_CHECK(hipEventRecord(p->ev_cpu_copied, s));
+      p->cpu_copy_pending = true;
+    }
+    hipEvent_t eb = prof_begin(p, s);
+    FT_HIP_CHECK(launch_combine(p->pbuf, p->pair_row, t0, h.t1, k, p->H, p->shared ? h.pairs : -1,
+                                static_cast<uint16_t*>(out), s));
+    prof_end(p, FT_STAGE_COMBINE, eb, s, (double(h.rows) + (h.t1 - t0)) * p->H * 2.0, 0.0);
+    t0 = h.t1;
+  }
+  return FT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ft_moe_last_error(void) { return get_error(); }
+
+int ft_moe_init_pool(const ft_moe_config* cfg, const ft_moe_weights* wts, ft_moe_pool** out) {
+  try {
+    if (!out) {
+      set_error("out is NULL");
+      return FT_E_INVALID;
+    }
+    *out = nullptr;
+    if (!cfg || !wts || !wts->expert || !wts->router_w || !cfg->layer_fmt) {
+      set_error("NULL config, weights or layer_fmt");
+      return FT_E_INVALID;
+    }
+    const int L = cfg->num_layers, H = cfg->hidden, I = cfg->inter, E = cfg->num_experts, k = cfg->top_k;
+    if (L < 1 || H < 128 || I < 128 || H % 128 || I % 128 || H > 8192 || I > 16384) {
+      set_error("bad shape: L=%d H=%d I=%d (H, I multiples of 128, H <= 8192)", L, H, I);
+      return FT_E_INVALID;
+    }
+    if (E < 1 || E > kMaxExperts || k < 1 || k > kMaxTopK || k > E) {
+      set_error("bad experts/top_k: E=%d k=%d (E <= %d, k <= %d)", E, k, kMaxExperts, kMaxTopK);
+      return FT_E_INVALID;
+    }
+    if (cfg->hybrid_cpu_share < 0.0 || cfg->hybrid_cpu_share > 1.0) {
+      set_error("hybrid_cpu_share must be in [0,1]");
+      return FT_E_INVALID;
+    }
+    if (cfg->has_shared_expert && !wts->shared) {
+      set_error("has_shared_expert set but shared blobs are NULL");
+      return FT_E_INVALID;
+    }
+    for (int l = 0; l < L; ++l) {
+      const int f = cfg->layer_fmt[l];
+      if (f < FT_FMT_MXFP4 || f > FT_FMT_FP8_B128) {
+        set_error("layer %d: unknown format %d", l, f);
+        return FT_E_INVALID;
+      }
+      if (!ffn_shape_ok(f, H, I)) {
+        set_error("layer %d: H=%d I=%d not supported by the expert kernels", l, H, I);
+        return FT_E_INVALID;
+      }
+    }
+    for (int64_t i = 0; i < int64_t(L) * E; ++i)
+      if (!wts->expert[i]) {
+        set_error("expert blob %lld is NULL", (long long)i);
+        return FT_E_INVALID;
+      }
+    auto p = std::make_unique<ft_moe_pool>();
+    p->L = L; p->H = H; p->I = I; p->E = E; p->k = k;
+    p->shared = cfg->has_shared_expert ? 1 : 0;
+    p->device = cfg->device;
+    p->cpu_threads = cfg->cpu_threads > 0 ? cfg->cpu_threads : 8;
+    p->share = cfg->hybrid_cpu_share;
+    p->fmt.assign(cfg->layer_fmt, cfg->layer_fmt + L);
+    for (int f = 1; f <= 3; ++f) {
+      p->lay[f] = make_layout(f, H, I);
+      p->canon_bytes[f] = canonical_bytes(f, H, I);
+    }
+    for (int l = 0; l < L; ++l) p->slot_bytes = std::max(p->slot_bytes, p->lay[p->fmt[l]].bytes);
+    p->C = cfg->pool_slots > 0 ? cfg->pool_slots : (cfg->pool_bytes > 0 ? cfg->pool_bytes / p->slot_bytes : 0);
+    if (p->C < k || p->C > (int64_t(1) << 30)) {
+      set_error("pool of %lld slots cannot hold top_k = %d experts", (long long)p->C, k);
+      return FT_E_INVALID;
+    }
+    const char* fault = std::getenv("FT_MOE_FAULT");
+    if (fault && std::strncmp(fault, "copy:", 5) == 0) p->fault_copy = std::atoll(fault + 5);
+
+    // ---- pinned host store: one entry per distinct (blob pointer, format)
+    std::map<std::pair<const void*, int>, int64_t> seen;
+    p->key_off.resize(size_t(L) * E);
+    std::vector<std::pair<const void*, int>> order;
+    int64_t off = 0;
+    for (int l = 0; l < L; ++l)
+      for (int e = 0; e < E; ++e) {
+        const auto key = std::make_pair(wts->expert[int64_t(l) * E + e], p->fmt[l]);
+        auto it = seen.find(key);
+        if (it == seen.end()) {
+          seen[key] = off;
+          order.push_back(key);
+          p->key_off[int64_t(l) * E + e] = off;
+          off += p->slot_bytes;
+        } else {
+          p->key_off[int64_t(l) * E + e] = it->second;
+        }
+      }
+    p->layer_contig.assign(L, 0);
+    for (int l = 0; l < L; ++l) {
+      bool c = p->lay[p->fmt[l]].bytes == p->slot_bytes;
+      for (int e = 1; e < E && c; ++e)
+        c = p->key_off[int64_t(l) * E + e] == p->key_off[int64_t(l) * E] + int64_t(e) * p->slot_bytes;
+      p->layer_contig[l] = c;
+    }
+    p->host_bytes = off;
+    DeviceGuard dg(p->device);
+    if (fault && std::strcmp(fault, "pinned_alloc") == 0) {
+      set_error("injected pinned allocation failure (%lld bytes)", (long long)off);
+      return FT_E_OOM_PINNED;
+    }
+    if (hipHostMalloc(reinterpret_cast<void**>(&p->host_store), size_t(off), hipHostMallocDefault) != hipSuccess) {
+      (void)hipGetLastError();
+      p->host_store = nullptr;
+      set_error("pinned host allocation of %lld bytes failed", (long long)off);
+      return FT_E_OOM_PINNED;
+    }
+    {
+      const int nthr = std::max(1, std::min(16, int(std::thread::hardware_concurrency())));
+      parallel_for(int(order.size()), nthr, [&](int b, int e) {
+        for (int i = b; i < e; ++i) {
+          const auto& key = order[i];
+          repack_expert(p->lay[key.second], static_cast<const uint8_t*>(key.first), p->host_store + seen[key]);
+        }
+      });
+    }
+
+    // ---- device memory
+    int rc;
+    if ((rc = dev_alloc(&p->arena, p->C * p->slot_bytes))) {
+      ft_moe_destroy_pool(p.release());
+      return rc;
+    }
+    const int64_t rsz = int64_t(L) * E * H;
+    if ((rc = dev_alloc(&p->router_dev, rsz))) {
+      ft_moe_destroy_pool(p.release());
+      return rc;
+    }
+    FT_HIP_CHECK(hipMemcpy(p->router_dev, wts->router_w, size_t(rsz) * 4, hipMemcpyHostToDevice));
+    if (p->shared) {
+      p->shared_stride = p->slot_bytes;
+      if ((rc = dev_alloc(&p->shared_dev, int64_t(L) * p->shared_stride))) {
+        ft_moe_destroy_pool(p.release());
+        return rc;
+      }
+      std::vector<uint8_t> tmp(p->slot_bytes);
+      for (int l = 0; l < L; ++l) {
+        repack_expert(p->lay[p->fmt[l]], static_cast<const uint8_t*>(wts->shared[l]), tmp.data());
+        FT_HIP_CHECK(hipMemcpy(p->shared_dev + int64_t(l) * p->shared_stride, tmp.data(),
+                               size_t(p->lay[p->fmt[l]].bytes), hipMemcpyHostToDevice));
+      }
+    }
+    const int64_t C = p->C;
+    if ((rc = dev_alloc(&p->tab.key2slot, int64_t(L) * E)) || (rc = dev_alloc(&p->tab.slot_key, C)) ||
+        (rc = dev_alloc(&p->tab.slot_last, C)) || (rc = dev_alloc(&p->tab.lru, C)) ||
+        (rc = dev_alloc(&p->tab.lru_tmp, C)) || (rc = dev_alloc(&p->tab.slot_mark, C)) ||
+        (rc = dev_alloc(&p->tab.clock, 1)) || (rc = dev_alloc(&p->tab.stats, int64_t(L) * ST_COUNT)) ||
+        (rc = dev_alloc(&p->tab.min_gap, L)) || (rc = dev_alloc(&p->groups, E + 2)) ||
+        (rc = dev_alloc(&p->glist, E + 2)) || (rc = dev_alloc(&p->dev_header, 16)) ||
+        (rc = dev_alloc(&p->fail_dev, 2 * E + 2))) {
+      ft_moe_destroy_pool(p.release());
+      return rc;
+    }
+    FT_HIP_CHECK(hipMemset(p->tab.key2slot, 0xFF, size_t(L) * E * 4));
+    FT_HIP_CHECK(hipMemset(p->tab.slot_key, 0xFF, size_t(C) * 4));
+    FT_HIP_CHECK(hipMemset(p->tab.slot_mark, 0xFF, size_t(C) * 4));
+    FT_HIP_CHECK(hipMemset(p->tab.slot_last, 0, size_t(C) * 8));
+    FT_HIP_CHECK(hipMemset(p->tab.clock, 0, 8));
+    FT_HIP_CHECK(hipMemset(p->tab.stats, 0, size_t(L) * ST_COUNT * 8));
+    {
+      std::vector<int32_t> lru(C);
+      for (int64_t i = 0; i < C; ++i) lru[i] = int32_t(i);
+      FT_HIP_CHECK(hipMemcpy(p->tab.lru, lru.data(), size_t(C) * 4, hipMemcpyHostToDevice));
+      std::vector<double> g(L, INFINITY);
+      FT_HIP_CHECK(hipMemcpy(p->tab.min_gap, g.data(), size_t(L) * 8, hipMemcpyHostToDevice));
+    }
+    FT_HIP_CHECK(hipStreamCreateWithFlags(&p->copy_stream, hipStreamNonBlocking));
+    for (hipEvent_t* e : {&p->ev_resolved, &p->ev_copied, &p->ev_sync, &p->ev_cpu_copied, &p->ev_done[0],
+                          &p->ev_done[1], &p->ev_staged[0], &p->ev_staged[1]})
+      FT_HIP_CHECK(hipEventCreateWithFlags(e, hipEventDisableTiming));
+    FT_HIP_CHECK(hipDeviceSynchronize());
+    *out = p.release();
+    return (*out)->C < 2 * int64_t(E) ? FT_WARN_STAGING_SMALL : FT_OK;
+  } catch (const std::exception& ex) {
+    set_error("init failed: %s", ex.what());
+    return FT_E_INVALID;
+  }
+}
+
+int ft_moe_layer_forward(ft_moe_pool* p, int32_t layer, int32_t num_tokens, const void* x_bf16,
+                         const float* router_bias, void* out_bf16, int32_t flags, void* hip_stream,
+                         ft_moe_trace* trace) {
+  try {
+    if (!p || !x_bf16 || !out_bf16) {
+      set_error("NULL pool, x or out");
+      return FT_E_INVALID;
+    }
+    if (layer < 0 || layer >= p->L || num_tokens < 0) {
+      set_error("bad layer %d or token count %d", layer, num_tokens);
+      return FT_E_INVALID;
+    }
+    if ((reinterpret_cast<uintptr_t>(x_bf16) | reinterpret_cast<uintptr_t>(out_bf16)) & 15) {
+      set_error("x and out must be 16-byte aligned");
+      return FT_E_INVALID;
+    }
+    const int mode = flags & FT_FWD_MODE_MASK;
+    const int act = (flags & FT_ACT_MASK) >> 4;
+    if (mode > FT_FWD_PREFILL_STAGED || act > 2 || (flags & ~(FT_FWD_MODE_MASK | FT_ACT_MASK))) {
+      set_error("bad flags 0x%x", flags);
+      return FT_E_INVALID;
+    }
+    if (act != 0) {
+      set_error("MX activation modes are not available in this build");
+      return FT_E_INVALID;
+    }
+    if (mode == FT_FWD_DECODE && p->prefill_next != 0) {
+      set_error("decode call while prefill chunk is at layer %d", p->prefill_next);
+      return FT_E_STATE;
+    }
+    if (num_tokens == 0) return FT_OK;
+    DeviceGuard dg(p->device);
+    int rc = ensure_capacity(p, num_tokens);
+    if (rc) return rc;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    const int T = num_tokens, E = p->E, k = p->k;
+    hipEvent_t e0 = prof_begin(p, s);
+    FT_HIP_CHECK(launch_router_logits(static_cast<const uint16_t*>(x_bf16), p->router_dev + int64_t(layer) * E * p->H,
+                                      router_bias, p->z, T, p->H, E, s));
+    prof_end(p, FT_STAGE_ROUTER, e0, s, double(E) * p->H * 4 + double(T) * p->H * 2, 2.0 * T * E * p->H);
+    e0 = prof_begin(p, s);
+    FT_HIP_CHECK(launch_topk(p->z, T, E, k, p->sel, p->w, p->gap, s));
+    prof_end(p, FT_STAGE_TOPK, e0, s, double(T) * E * 8, 0.0);
+    rc = mode == FT_FWD_DECODE ? forward_decode(p, layer, T, x_bf16, out_bf16, s)
+                               : forward_prefill(p, layer, T, x_bf16, out_bf16, s);
+    if (rc) return rc;
+    if (trace) {
+      const size_t n = size_t(T) * k;
+      if (trace->sel) FT_HIP_CHECK(hipMemcpyAsync(trace->sel, p->sel, n * 4, hipMemcpyDeviceToDevice, s));
+      if (trace->w) FT_HIP_CHECK(hipMemcpyAsync(trace->w, p->w, n * 4, hipMemcpyDeviceToDevice, s));
+      if (trace->slot) FT_HIP_CHECK(hipMemcpyAsync(trace->slot, p->pair_slot, n * 4, hipMemcpyDeviceToDevice, s));
+      if (trace->flag) FT_HIP_CHECK(hipMemcpyAsync(trace->flag, p->pair_flag, n, hipMemcpyDeviceToDevice, s));
+      if (trace->row) FT_HIP_CHECK(hipMemcpyAsync(trace->row, p->pair_row, n * 4, hipMemcpyDeviceToDevice, s));
+    }
+    return FT_OK;
+  } catch (const std::exception& ex) {
+    set_error("forward failed: %s", ex.what());
+    return FT_E_INVALID;
+  }
+}
+
+int ft_moe_pool_stats(ft_moe_pool* p, int32_t layer, ft_moe_stats* out, int32_t reset) {
+  if (!p || !out || layer < -1 || layer >= p->L) {
+    set_error("bad pool, layer or output");
+    return FT_E_INVALID;
+  }
+  DeviceGuard dg(p->device);
+  FT_HIP_CHECK(hipDeviceSynchronize());
+  std::vector<uint64_t> st(size_t(p->L) * ST_COUNT);
+  std::vector<double> g(p->L);
+  std::vector<int32_t> sk(p->C);
+  FT_HIP_CHECK(hipMemcpy(st.data(), p->tab.stats, st.size() * 8, hipMemcpyDeviceToHost));
+  FT_HIP_CHECK(hipMemcpy(g.data(), p->tab.min_gap, g.size() * 8, hipMemcpyDeviceToHost));
+  FT_HIP_CHECK(hipMemcpy(sk.data(), p->tab.slot_key, sk.size() * 4, hipMemcpyDeviceToHost));
+  std::memset(out, 0, sizeof(*out));
+  out->min_topk_gap = INFINITY;
+  for (int l = 0; l < p->L; ++l) {
+    if (layer >= 0 && l != layer) continue;
+    const uint64_t* s = &st[size_t(l) * ST_COUNT];
+    out->pair_hits += s[ST_PAIR_HITS];
+    out->pair_misses += s[ST_PAIR_MISSES];
+    out->expert_hits += s[ST_EXPERT_HITS];
+    out->expert_misses += s[ST_EXPERT_MISSES];
+    out->cpu_misses += s[ST_CPU_MISSES];
+    out->evictions += s[ST_EVICTIONS];
+    out->bytes_h2d += s[ST_BYTES_H2D];
+    out->calls += s[ST_CALLS];
+    out->min_topk_gap = std::min(out->min_topk_gap, g[l]);
+  }
+  out->slots_total = p->C;
+  for (int32_t v : sk) out->slots_used += v >= 0;
+  if (reset) {
+    FT_HIP_CHECK(hipMemset(p->tab.stats, 0, st.size() * 8));
+    std::vector<double> inf(p->L, INFINITY);
+    FT_HIP_CHECK(hipMemcpy(p->tab.min_gap, inf.data(), inf.size() * 8, hipMemcpyHostToDevice));
+  }
+  return FT_OK;
+}
+
+int ft_moe_last_misses(const ft_moe_pool* p, int32_t* stream_expert, int32_t* stream_slot, int32_t* n_stream,
+                       int32_t* cpu_expert, int32_t* n_cpu, int32_t cap) {
+  if (!p) {
+    set_error("NULL pool");
+    return FT_E_INVALID;
+  }
+  if (n_stream) *n_stream = int32_t(p->last_se.size());
+  if (n_cpu) *n_cpu = int32_t(p->last_ce.size());
+  for (size_t i = 0; i < p->last_se.size() && int32_t(i) < cap; ++i) {
+    if (stream_expert) stream_expert[i] = p->last_se[i];
+    if (stream_slot) stream_slot[i] = p->last_ss[i];
+  }
+  for (size_t i = 0; i < p->last_ce.size() && int32_t(i) < cap; ++i)
+    if (cpu_expert) cpu_expert[i] = p->last_ce[i];
+  return FT_OK;
+}
+
+int ft_moe_pool_table(ft_moe_pool* p, int32_t* slot_key, uint64_t* slot_last, uint64_t* clock, int64_t* slots) {
+  if (!p) {
+    set_error("NULL pool");
+    return FT_E_INVALID;
+  }
+  DeviceGuard dg(p->device);
+  FT_HIP_CHECK(hipDeviceSynchronize());
+  if (slot_key) FT_HIP_CHECK(hipMemcpy(slot_key, p->tab.slot_key, size_t(p->C) * 4, hipMemcpyDeviceToHost));
+  if (slot_last) FT_HIP_CHECK(hipMemcpy(slot_last, p->tab.slot_last, size_t(p->C) * 8, hipMemcpyDeviceToHost));
+  if (clock) FT_HIP_CHECK(hipMemcpy(clock, p->tab.clock, 8, hipMemcpyDeviceToHost));
+  if (slots) *slots = p->C;
+  return FT_OK;
+}
+
+int ft_moe_set_hybrid_share(ft_moe_pool* p, double share) {
+  if (!p || !(share >= 0.0 && share <= 1.0)) {
+    set_error("share must be in [0,1]");
+    return FT_E_INVALID;
+  }
+  p->share = share;
+  return FT_OK;
+}
+
+int ft_moe_host_expert_rate(ft_moe_pool* p, int32_t layer, int32_t tokens, int32_t iters, double* bytes_per_s) {
+  if (!p || layer < 0 || layer >= p->L || tokens < 1 || iters < 1 || !bytes_per_s) {
+    set_error("bad arguments");
+    return FT_E_INVALID;
+  }
+  const ExpertLayout& L = p->lay[p->fmt[layer]];
+  std::vector<uint16_t> x(size_t(tokens) * p->H, 0x3F80), out(size_t(tokens) * p->H);
+  std::vector<float> w(tokens, 1.0f);
+  const uint8_t* blob = p->host_store + p->key_off[int64_t(layer) * p->E];
+  const auto t0 = std::chrono::steady_clock::now();
+  for (int i = 0; i < iters; ++i) host_expert(L, blob, x.data(), w.data(), tokens, out.data(), p->cpu_threads);
+  const double sec = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
+  *bytes_per_s = double(p->canon_bytes[p->fmt[layer]]) * iters / std::max(sec, 1e-9);
+  return FT_OK;
+}
+
+int ft_moe_set_profiling(ft_moe_pool* p, int32_t enable) {
+  if (!p) {
+    set_error("NULL pool");
+    return FT_E_INVALID;
+  }
+  p->profiling = enable != 0;
+  return FT_OK;
+}
+
+int ft_moe_profile_read(ft_moe_pool* p, ft_moe_profile* out, int32_t reset) {
+  if (!p || !out) {
+    set_error("NULL pool or output");
+    return FT_E_INVALID;
+  }
+  DeviceGuard dg(p->device);
+  prof_drain(p, true);
+  *out = p->prof;
+  if (reset) p->prof = ft_moe_profile{};
+  return FT_OK;
+}
+
+void ft_moe_destroy_pool(ft_moe_pool* p) {
+  if (!p) return;
+  DeviceGuard dg(p->device);
+  (void)hipDeviceSynchronize();
+  prof_drain(p, true);
+  for (hipEvent_t e : p->prof_free) hipEventDestroy(e);
+  hipFree(p->arena); hipFree(p->shared_dev); hipFree(p->router_dev);
+  hipFree(p->tab.key2slot); hipFree(p->tab.slot_key); hipFree(p->tab.slot_last); hipFree(p->tab.lru);
+  hipFree(p->tab.lru_tmp); hipFree(p->tab.slot_mark); hipFree(p->tab.clock); hipFree(p->tab.stats);
+  hipFree(p->tab.min_gap);
+  hipFree(p->z); hipFree(p->sel); hipFree(p->w); hipFree(p->gap); hipFree(p->pair_flag); hipFree(p->pair_slot);
+  hipFree(p->pair_row); hipFree(p->row_tok); hipFree(p->row_w); hipFree(p->groups); hipFree(p->glist);
+  hipFree(p->dev_header); hipFree(p->hbuf); hipFree(p->pbuf); hipFree(p->fail_dev);
+  if (p->rb_host) hipHostFree(p->rb_host);
+  if (p->x_host) hipHostFree(p->x_host);
+  if (p->cpu_out) hipHostFree(p->cpu_out);
+  if (p->host_store) hipHostFree(p->host_store);
+  if (p->copy_stream) hipStreamDestroy(p->copy_stream);
+  for (hipEvent_t e : {p->ev_resolved, p->ev_copied, p->ev_sync, p->ev_cpu_copied, p->ev_done[0], p->ev_done[1],
+                       p->ev_staged[0], p->ev_staged[1]})
+    if (e) hipEventDestroy(e);
+  delete p;
+}
+
+}  // extern "C"

@@ -1,0 +1,537 @@
+// Resolve one wave of a layer call against the global LRU pool of expert
+// slots, and group the wave's (token, rank) pairs by expert.
+//
+// Pages: the GPU keeps a least-recently-used cache of expert slots shared by
+// all layers; an expert already cached runs in place, a miss is streamed over
+// PCIe; the hybrid strategy splits a step's misses between host compute and
+// streaming (devpik article "FreeToken: Run Frontier MoE Models on Your Own
+// GPU...", section "Why a Huge MoE Model Fits on One Consumer GPU"); prefill
+// copies every expert of a layer per chunk (same article, "Long Prompts Are
+// the Bottleneck").  Readings where the pages are silent (also stated in the
+// oracle): a wave is the longest run of tokens whose union of experts fits the
+// pool and is resolved as a set; victims are free slots by index, then the
+// least recently used non-hit slots; one clock tick per pair.
+//
+// Device design: one 1024-thread workgroup.  The pool's recency order is kept
+// as an array `lru` of all C slots (free slots first by index, then resident
+// slots by last use), so victim selection is one prefix scan over `lru` that
+// skips this wave's hit slots, and the update is a stable compaction of the
+// untouched entries followed by the touched slots in order of their last pair.
+// Pairs are grouped in first-appearance order (D order); each pair's rank in
+// its group comes from a wavefront-ballot match of equal groups plus a
+// per-wave prefix, so rows keep pair order inside a group without atomics.
+#include "common.h"
+
+namespace ftmoe {
+
+namespace {
+
+constexpr int NT = kResolveThreads;
+constexpr int NW = NT / 64;
+
+struct ResolveSmem {
+  int first[kMaxExperts];
+  int last[kMaxExperts];
+  int dix[kMaxExperts];
+  int cnt[kMaxExperts];
+  int D[kMaxExperts];
+  int cls[kMaxExperts];
+  int dslot[kMaxExperts];
+  int mpos[kMaxExperts];
+  int off[kMaxExperts];
+  int sm[kMaxExperts];
+  int wcnt[NW][kMaxExperts];
+  int wsum[NW];
+  int scal[16];
+  double dred[NW];
+};
+
+// Exclusive prefix sum of v over the workgroup; *total gets the sum.
+__device__ int block_exscan(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wsum[wid] = x;
+  __syncthreads();
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int s = wsum[w];
+    pre += (w < wid) ? s : 0;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return pre + x - v;
+}
+
+__device__ int block_sum(int v, int* wsum) {
+  int t;
+  block_exscan(v, wsum, &t);
+  return t;
+}
+
+__device__ int block_max(int v, int* wsum) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
+  if (lane == 0) wsum[wid] = v;
+  __syncthreads();
+  int m = wsum[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) m = max(m, wsum[w]);
+  __syncthreads();
+  return m;
+}
+
+__device__ double block_min_d(double v, double* red) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmin(v, __shfl_xor(v, off, 64));
+  if (lane == 0) red[wid] = v;
+  __syncthreads();
+  double m = red[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) m = fmin(m, red[w]);
+  __syncthreads();
+  return m;
+}
+
+__global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
+  __shared__ ResolveSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int E = a.E, k = a.k, C = a.C, t0 = a.t0;
+  const bool decode = a.mode == 0;
+  const int key0 = a.layer * E;
+
+  for (int e = tid; e < E; e += NT) {
+    sm.first[e] = 0x7fffffff;
+    sm.last[e] = -1;
+    sm.dix[e] = 0;
+    sm.cnt[e] = 0;
+  }
+  __syncthreads();
+
+  // ---- 1. end of the wave: tokens while the union of experts fits C
+  if (tid == 0) sm.scal[0] = a.T;
+  if (decode && C < E && wid == 0) {
+    int count = 0, t1 = a.T;
+    for (int t = t0; t < a.T; ++t) {
+      const int e = lane < k ? a.sel[int64_t(t) * k + lane] : 0;
+      const bool isnew = lane < k && sm.dix[e] == 0;
+      const int n = __popcll(__ballot(isnew));
+      if (count + n > C) {
+        t1 = t;
+        break;
+      }
+      if (isnew) sm.dix[e] = 1;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      count += n;
+    }
+    if (lane == 0) sm.scal[0] = t1 > t0 ? t1 : t0 + 1;
+  }
+  __syncthreads();
+  const int t1 = sm.scal[0];
+  const int P = (t1 - t0) * k;
+  const int64_t pb = int64_t(t0) * k;
+  for (int e = tid; e < E; e += NT) sm.dix[e] = -1;
+
+  // ---- 2. first and last pair of each expert in the wave
+  for (int i = tid; i < P; i += NT) {
+    const int e = a.sel[pb + i];
+    atomicMin(&sm.first[e], i);
+    atomicMax(&sm.last[e], i);
+  }
+  __syncthreads();
+
+  // ---- 3. D: distinct experts in order of first appearance
+  int nD = 0;
+  for (int c0 = 0; c0 < P; c0 += NT) {
+    const int i = c0 + tid;
+    int e = 0;
+    bool f = false;
+    if (i < P) {
+      e = a.sel[pb + i];
+      f = sm.first[e] == i;
+    }
+    int tot;
+    const int pos = block_exscan(f ? 1 : 0, sm.wsum, &tot);
+    if (f) {
+      sm.D[nD + pos] = e;
+      sm.dix[e] = nD + pos;
+    }
+    nD += tot;
+  }
+  __syncthreads();
+
+  // ---- 4. hits, misses, hybrid split
+  int hit = 0;
+  if (tid < nD) {
+    const int e = sm.D[tid];
+    if (decode) {
+      const int s = a.tab.key2slot[key0 + e];
+      hit = s >= 0;
+      if (hit) {
+        sm.dslot[tid] = s;
+        a.tab.slot_mark[s] = a.stamp;
+      }
+    } else {
+      sm.dslot[tid] = (a.layer & 1) * E + e;
+    }
+  }
+  int nM;
+  const int mp = block_exscan((tid < nD && !hit) ? 1 : 0, sm.wsum, &nM);
+  // IEEE double, no contraction: floor(nM * share + 1/2)
+  const int m_cpu = decode ? int(floor(__dadd_rn(__dmul_rn(double(nM), a.share), 0.5))) : 0;
+  const int m_str = nM - m_cpu;
+  if (tid < nD) {
+    sm.mpos[tid] = hit ? -1 : mp;
+    const int c = hit ? FT_PAIR_HIT : (mp < m_str ? FT_PAIR_MISS_STREAM : FT_PAIR_MISS_CPU);
+    sm.cls[tid] = c;
+    if (c == FT_PAIR_MISS_STREAM) sm.sm[mp] = tid;
+  }
+  if (tid == 0) sm.scal[1] = 0;  // evictions
+  __syncthreads();
+
+  // ---- 5. victims: scan the recency order, skipping this wave's hit slots
+  if (decode && m_str > 0) {
+    int taken = 0;
+    for (int c0 = 0; c0 < C && taken < m_str; c0 += NT) {
+      const int i = c0 + tid;
+      int s = -1;
+      bool elig = false;
+      if (i < C) {
+        s = a.tab.lru[i];
+        elig = a.tab.slot_mark[s] != a.stamp;
+      }
+      int tot;
+      const int vp = block_exscan(elig ? 1 : 0, sm.wsum, &tot);
+      if (elig && taken + vp < m_str) {
+        const int d = sm.sm[taken + vp];
+        const int e = sm.D[d];
+        const int old = a.tab.slot_key[s];
+        if (old >= 0) {
+          a.tab.key2slot[old] = -1;
+          atomicAdd(&sm.scal[1], 1);
+        }
+        a.tab.slot_key[s] = key0 + e;
+        a.tab.key2slot[key0 + e] = s;
+        a.tab.slot_mark[s] = a.stamp;
+        sm.dslot[d] = s;
+      }
+      taken += tot;
+    }
+  }
+  __syncthreads();
+
+  // ---- 6. recency update: untouched slots keep their order, touched slots
+  // move to the recent end in order of their last pair
+  if (decode) {
+    int nkeep = 0;
+    for (int c0 = 0; c0 < C; c0 += NT) {
+      const int i = c0 + tid;
+      int s = -1;
+      bool keep = false;
+      if (i < C) {
+        s = a.tab.lru[i];
+        keep = a.tab.slot_mark[s] != a.stamp;
+      }
+      int tot;
+      const int kp = block_exscan(keep ? 1 : 0, sm.wsum, &tot);
+      if (keep) a.tab.lru_tmp[nkeep + kp] = s;
+      nkeep += tot;
+    }
+    const uint64_t clk = *a.tab.clock;
+    for (int d = tid; d < nD; d += NT) {
+      if (sm.cls[d] == FT_PAIR_MISS_CPU) continue;
+      const int mylast = sm.last[sm.D[d]];
+      int rank = 0;
+      for (int d2 = 0; d2 < nD; ++d2)
+        if (sm.cls[d2] != FT_PAIR_MISS_CPU && sm.last[sm.D[d2]] < mylast) ++rank;
+      a.tab.lru_tmp[nkeep + rank] = sm.dslot[d];
+      a.tab.slot_last[sm.dslot[d]] = clk + uint64_t(mylast);
+    }
+    __syncthreads();
+    for (int i = tid; i < C; i += NT) a.tab.lru[i] = a.tab.lru_tmp[i];
+    __syncthreads();
+    if (tid == 0) *a.tab.clock = clk + uint64_t(P);
+  }
+
+  // ---- 7. per-pair decisions
+  for (int i = tid; i < P; i += NT) {
+    const int d = sm.dix[a.sel[pb + i]];
+    const int c = sm.cls[d];
+    a.pair_flag[pb + i] = uint8_t(c);
+    a.pair_slot[pb + i] = c == FT_PAIR_MISS_CPU ? -1 : sm.dslot[d];
+  }
+
+  // ---- 8. rank of each pair inside its group (pair order), via ballot match
+  int nbits = 1;
+  while ((1 << nbits) < nD) ++nbits;
+  for (int c0 = 0; c0 < P; c0 += NT) {
+    for (int j = tid; j < NW * nD; j += NT) sm.wcnt[j / nD][j % nD] = 0;
+    __syncthreads();
+    const int i = c0 + tid;
+    const bool valid = i < P;
+    const int d = valid ? sm.dix[a.sel[pb + i]] : 0;
+    uint64_t same = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (d >> b) & 1;
+      const uint64_t bb = __ballot(valid && bit);
+      same &= bit ? bb : ~bb;
+    }
+    const int lrank = __popcll(same & ((1ull << lane) - 1ull));
+    if (valid && lrank == 0) sm.wcnt[wid][d] = __popcll(same);
+    __syncthreads();
+    for (int g = tid; g < nD; g += NT) {
+      int run = sm.cnt[g];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const int c = sm.wcnt[w][g];
+        sm.wcnt[w][g] = run;
+        run += c;
+      }
+      sm.cnt[g] = run;
+    }
+    __syncthreads();
+    if (valid) a.pair_row[pb + i] = sm.wcnt[wid][d] + lrank;
+    __syncthreads();
+  }
+
+  // ---- 9. group offsets and rows
+  {
+    int tot;
+    const int o = block_exscan(tid < nD ? sm.cnt[tid] : 0, sm.wsum, &tot);
+    if (tid < nD) sm.off[tid] = o;
+  }
+  __syncthreads();
+  for (int i = tid; i < P; i += NT) {
+    const int d = sm.dix[a.sel[pb + i]];
+    const int row = sm.off[d] + a.pair_row[pb + i];
+    a.pair_row[pb + i] = row;
+    a.row_tok[row] = t0 + i / k;
+    a.row_w[row] = a.w[pb + i];
+  }
+  const int ntok = t1 - t0;
+  const bool shared = a.shared_ptr != 0;
+  if (shared) {
+    for (int tt = tid; tt < ntok; tt += NT) {
+      a.row_tok[P + tt] = t0 + tt;
+      a.row_w[P + tt] = 1.0f;
+    }
+  }
+
+  // ---- 10. group descriptors and run lists (hits [+ shared], streamed, host)
+  int nHit;
+  const bool ishit = tid < nD && sm.cls[tid] == FT_PAIR_HIT;
+  const int hp = block_exscan(ishit ? 1 : 0, sm.wsum, &nHit);
+  const int n_hit_list = nHit + (shared ? 1 : 0);
+  if (tid < nD) {
+    const int c = sm.cls[tid];
+    GroupDesc g;
+    g.wptr = c == FT_PAIR_MISS_CPU ? 0ull : a.arena + uint64_t(sm.dslot[tid]) * uint64_t(a.slot_bytes);
+    g.row_begin = sm.off[tid];
+    g.row_count = sm.cnt[tid];
+    g.expert = sm.D[tid];
+    g.slot = c == FT_PAIR_MISS_CPU ? -1 : sm.dslot[tid];
+    a.groups[tid] = g;
+    if (c == FT_PAIR_HIT)
+      a.glist[hp] = tid;
+    else
+      a.glist[n_hit_list + sm.mpos[tid]] = tid;
+  }
+  if (tid == 0 && shared) {
+    GroupDesc g;
+    g.wptr = a.shared_ptr;
+    g.row_begin = P;
+    g.row_count = ntok;
+    g.expert = E;
+    g.slot = -2;
+    a.groups[nD] = g;
+    a.glist[nHit] = nD;
+  }
+  const int gcount = tid < nD ? sm.cnt[tid] : 0;
+  int max_rows = block_max(gcount, sm.wsum);
+  if (shared) max_rows = max(max_rows, ntok);
+  const int cpu_rows = block_sum(tid < nD && sm.cls[tid] == FT_PAIR_MISS_CPU ? sm.cnt[tid] : 0, sm.wsum);
+  const int hit_pairs = block_sum(ishit ? sm.cnt[tid] : 0, sm.wsum);
+  const int stream_rows =
+      block_sum(tid < nD && sm.cls[tid] == FT_PAIR_MISS_STREAM ? sm.cnt[tid] : 0, sm.wsum);
+  double g = __builtin_inf();
+  for (int tt = tid; tt < ntok; tt += NT) g = fmin(g, a.gap[t0 + tt]);
+  const double min_gap = block_min_d(g, sm.dred);
+  const int rows = P + (shared ? ntok : 0);
+
+  if (tid == 0) {
+    a.dev_header[0] = t1;
+    a.dev_header[1] = nD;
+    a.dev_header[2] = n_hit_list;
+    a.dev_header[3] = m_str;
+    a.dev_header[4] = m_cpu;
+    a.dev_header[5] = P;
+    a.dev_header[6] = rows;
+    a.dev_header[7] = max_rows;
+    a.dev_header[8] = cpu_rows;
+    a.dev_header[9] = nD + (shared ? 1 : 0);
+    uint64_t* st = a.tab.stats + int64_t(a.layer) * ST_COUNT;
+    if (decode) {
+      st[ST_PAIR_HITS] += uint64_t(hit_pairs);
+      st[ST_PAIR_MISSES] += uint64_t(P - hit_pairs);
+      st[ST_EXPERT_HITS] += uint64_t(nHit);
+      st[ST_EXPERT_MISSES] += uint64_t(nM);
+      st[ST_CPU_MISSES] += uint64_t(m_cpu);
+      st[ST_EVICTIONS] += uint64_t(sm.scal[1]);
+      st[ST_BYTES_H2D] += uint64_t(m_str) * uint64_t(a.expert_bytes) + uint64_t(cpu_rows) * uint64_t(a.hidden) * 2ull;
+    } else {
+      st[ST_PAIR_MISSES] += uint64_t(P);
+      st[ST_EXPERT_MISSES] += uint64_t(E);
+      st[ST_BYTES_H2D] += uint64_t(E) * uint64_t(a.expert_bytes);
+    }
+    if (t0 == 0) st[ST_CALLS] += 1;
+    a.tab.min_gap[a.layer] = fmin(a.tab.min_gap[a.layer], min_gap);
+  }
+
+  // ---- 11. host readback (decode): header, miss lists, host-computed rows
+  if (a.host_rb != nullptr) {
+    ResolveHeader* h = reinterpret_cast<ResolveHeader*>(a.host_rb);
+    int32_t* se = reinterpret_cast<int32_t*>(a.host_rb + sizeof(ResolveHeader));
+    int32_t* ss = se + E;
+    int32_t* ce = ss + E;
+    int32_t* cb = ce + E;
+    int32_t* cc = cb + E;
+    int32_t* ct = cc + E;
+    float* cw = reinterpret_cast<float*>(ct + a.T * k);
+    if (tid < nD) {
+      const int c = sm.cls[tid];
+      const int mpv = sm.mpos[tid];
+      if (c == FT_PAIR_MISS_STREAM) {
+        se[mpv] = sm.D[tid];
+        ss[mpv] = sm.dslot[tid];
+      } else if (c == FT_PAIR_MISS_CPU) {
+        ce[mpv - m_str] = sm.D[tid];
+        cb[mpv - m_str] = sm.off[tid];
+        cc[mpv - m_str] = sm.cnt[tid];
+      }
+    }
+    __syncthreads();
+    if (m_cpu > 0) {
+      // rows of host-computed groups, packed group after group
+      for (int j = 0; j < m_cpu; ++j) {
+        int base = 0;
+        for (int j2 = 0; j2 < j; ++j2) base += cc[j2];
+        for (int r = tid; r < cc[j]; r += NT) {
+          ct[base + r] = a.row_tok[cb[j] + r];
+          cw[base + r] = a.row_w[cb[j] + r];
+        }
+      }
+    }
+    if (tid == 0) {
+      h->t1 = t1;
+      h->n_groups = nD;
+      h->n_hit_list = n_hit_list;
+      h->n_stream = m_str;
+      h->n_cpu = m_cpu;
+      h->pairs = P;
+      h->rows = rows;
+      h->max_rows = max_rows;
+      h->cpu_rows = cpu_rows;
+      h->rows_hit_list = hit_pairs + (shared ? ntok : 0);
+      h->rows_stream = stream_rows;
+      h->min_gap = min_gap;
+    }
+    __threadfence_system();
+  }
+}
+
+// Free slots (prefill staging halves, or slots whose copy failed) and restore
+// the recency order invariant: free slots first by index, then residents in
+// their previous order.
+__global__ __launch_bounds__(NT) void k_free_slots(DevTable tab, int C, int lo0, int hi0, int lo1, int hi1,
+                                                   const int32_t* keys, const int32_t* slots, int n,
+                                                   uint64_t* evict_stat) {
+  __shared__ int wsum[NW];
+  __shared__ int nev;
+  const int tid = threadIdx.x;
+  if (tid == 0) nev = 0;
+  __syncthreads();
+  for (int s = tid; s < C; s += NT) {
+    const bool in = (s >= lo0 && s < hi0) || (s >= lo1 && s < hi1);
+    if (in) {
+      const int old = tab.slot_key[s];
+      if (old >= 0) {
+        tab.key2slot[old] = -1;
+        tab.slot_key[s] = -1;
+        atomicAdd(&nev, 1);
+      }
+    }
+  }
+  for (int i = tid; i < n; i += NT) {
+    const int s = slots[i];
+    if (tab.slot_key[s] == keys[i]) {
+      tab.slot_key[s] = -1;
+      tab.key2slot[keys[i]] = -1;
+    }
+  }
+  __syncthreads();
+  int nfree = 0;
+  for (int c0 = 0; c0 < C; c0 += NT) {
+    const int s = c0 + tid;
+    const bool f = s < C && tab.slot_key[s] < 0;
+    int tot;
+    const int p = block_exscan(f ? 1 : 0, wsum, &tot);
+    if (f) tab.lru_tmp[nfree + p] = s;
+    nfree += tot;
+  }
+  int nres = 0;
+  for (int c0 = 0; c0 < C; c0 += NT) {
+    const int i = c0 + tid;
+    int s = 0;
+    bool r = false;
+    if (i < C) {
+      s = tab.lru[i];
+      r = tab.slot_key[s] >= 0;
+    }
+    int tot;
+    const int p = block_exscan(r ? 1 : 0, wsum, &tot);
+    if (r) tab.lru_tmp[nfree + nres + p] = s;
+    nres += tot;
+  }
+  __syncthreads();
+  for (int i = tid; i < C; i += NT) tab.lru[i] = tab.lru_tmp[i];
+  if (tid == 0 && evict_stat) *evict_stat += uint64_t(nev);
+}
+
+}  // namespace
+
+hipError_t launch_resolve(const ResolveArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_resolve, dim3(1), dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_stage_table(DevTable tab, int E, int C, int layer, int num_layers, int pairs,
+                              int64_t expert_bytes, hipStream_t s) {
+  (void)pairs;
+  (void)expert_bytes;
+  const int h0 = layer & 1;
+  const int lo0 = h0 * E, hi0 = lo0 + E;
+  int lo1 = 0, hi1 = 0;
+  if (layer + 1 < num_layers) {
+    lo1 = ((layer + 1) & 1) * E;
+    hi1 = lo1 + E;
+  }
+  hipLaunchKernelGGL(k_free_slots, dim3(1), dim3(NT), 0, s, tab, C, lo0, hi0, lo1, hi1, nullptr, nullptr, 0,
+                     tab.stats + int64_t(layer) * ST_COUNT + ST_EVICTIONS);
+  return hipGetLastError();
+}
+
+hipError_t launch_uncommit(DevTable tab, const int32_t* keys, const int32_t* slots, int n, int C,
+                           hipStream_t s) {
+  hipLaunchKernelGGL(k_free_slots, dim3(1), dim3(NT), 0, s, tab, C, 0, 0, 0, 0, keys, slots, n, nullptr);
+  return hipGetLastError();
+}
+
+}  // namespace ftmoe

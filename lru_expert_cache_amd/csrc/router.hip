@@ -1,0 +1,244 @@
+// Router: logits z = x Wr^T + bias in fp64, then per-token top-k with
+// renormalised softmax weights.
+//
+// The pages fix only that a router sends each token to a few experts (devpik
+// article "FreeToken: Run Frontier MoE Models on Your Own GPU...", section
+// "Why a Huge MoE Model Fits on One Consumer GPU").  The exact reading used
+// here: each bf16 x fp32 product is exact in fp64 and summed in fp64, so the
+// selection (logit descending, lower expert index on ties) does not depend on
+// the summation order beyond fp64 rounding; weights are the softmax of the
+// selected logits rounded to fp32, evaluated in fp64.
+#include "common.h"
+
+namespace ftmoe {
+
+namespace {
+
+__device__ inline double bf16_to_f64(uint16_t b) {
+  return double(__uint_as_float(uint32_t(b) << 16));
+}
+
+__device__ inline double wave_sum(double v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Small batches (decode): one workgroup per expert, 256 threads stride over H
+// four elements at a time; the expert's router row stays in registers while
+// the tokens stream past.  Tokens in chunks of 8 accumulators.
+constexpr int kSmallThreads = 256;
+constexpr int kSmallMaxJ = 8;   // H <= 8 * 1024
+constexpr int kTokChunk = 8;
+
+__global__ __launch_bounds__(kSmallThreads) void k_router_logits_small(
+    const uint16_t* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
+    double* __restrict__ z, int T, int H, int E) {
+  const int e = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wid = tid >> 6;
+  __shared__ double red[kSmallThreads / 64][kTokChunk];
+  float4 wv[kSmallMaxJ];
+  const float* wrow = wr + int64_t(e) * H;
+#pragma unroll
+  for (int j = 0; j < kSmallMaxJ; ++j) {
+    const int h = 4 * tid + 1024 * j;
+    wv[j] = (h < H) ? *reinterpret_cast<const float4*>(wrow + h) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  const double b = bias ? double(bias[e]) : 0.0;
+  for (int t0 = 0; t0 < T; t0 += kTokChunk) {
+    double acc[kTokChunk];
+#pragma unroll
+    for (int c = 0; c < kTokChunk; ++c) acc[c] = 0.0;
+#pragma unroll
+    for (int c = 0; c < kTokChunk; ++c) {
+      const int t = t0 + c;
+      if (t < T) {
+        const uint16_t* xr = x + int64_t(t) * H;
+#pragma unroll
+        for (int j = 0; j < kSmallMaxJ; ++j) {
+          const int h = 4 * tid + 1024 * j;
+          if (h < H) {
+            const uint2 xv = *reinterpret_cast<const uint2*>(xr + h);
+            acc[c] = fma(bf16_to_f64(uint16_t(xv.x & 0xFFFF)), double(wv[j].x), acc[c]);
+            acc[c] = fma(bf16_to_f64(uint16_t(xv.x >> 16)), double(wv[j].y), acc[c]);
+            acc[c] = fma(bf16_to_f64(uint16_t(xv.y & 0xFFFF)), double(wv[j].z), acc[c]);
+            acc[c] = fma(bf16_to_f64(uint16_t(xv.y >> 16)), double(wv[j].w), acc[c]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kTokChunk; ++c) {
+      const double v = wave_sum(acc[c]);
+      if (lane == 0) red[wid][c] = v;
+    }
+    __syncthreads();
+    if (tid < kTokChunk && t0 + tid < T) {
+      double s = 0.0;
+#pragma unroll
+      for (int w = 0; w < kSmallThreads / 64; ++w) s += red[w][tid];
+      z[int64_t(t0 + tid) * E + e] = s + b;
+    }
+    __syncthreads();
+  }
+}
+
+// Large batches (prefill): 32 tokens x 32 experts per workgroup, each thread
+// a 2x2 register tile, K staged through LDS in chunks of 64 as fp64.
+constexpr int kTT = 32, kTE = 32, kKC = 64;
+
+__global__ __launch_bounds__(256) void k_router_logits_tiled(
+    const uint16_t* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
+    double* __restrict__ z, int T, int H, int E) {
+  __shared__ double xs[kTT][kKC + 1];
+  __shared__ double ws[kTE][kKC + 1];
+  const int tid = threadIdx.x;
+  const int tt0 = blockIdx.x * kTT, te0 = blockIdx.y * kTE;
+  const int ty = tid / 16, tx = tid % 16;  // 16 x 16 threads, 2x2 each
+  double acc[2][2] = {{0.0, 0.0}, {0.0, 0.0}};
+  for (int k0 = 0; k0 < H; k0 += kKC) {
+    // x tile: 32 x 64 bf16 = 2048 values, 8 per thread
+    {
+      const int r = tid / 8, c = (tid % 8) * 8;
+      const int t = tt0 + r;
+      if (t < T) {
+        const uint4 v = *reinterpret_cast<const uint4*>(x + int64_t(t) * H + k0 + c);
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          xs[r][c + 2 * i] = bf16_to_f64(uint16_t(u[i] & 0xFFFF));
+          xs[r][c + 2 * i + 1] = bf16_to_f64(uint16_t(u[i] >> 16));
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xs[r][c + i] = 0.0;
+      }
+    }
+    // w tile: 32 x 64 fp32, 8 per thread
+    {
+      const int r = tid / 8, c = (tid % 8) * 8;
+      const int e = te0 + r;
+      if (e < E) {
+        const float4 a = *reinterpret_cast<const float4*>(wr + int64_t(e) * H + k0 + c);
+        const float4 b = *reinterpret_cast<const float4*>(wr + int64_t(e) * H + k0 + c + 4);
+        ws[r][c + 0] = a.x; ws[r][c + 1] = a.y; ws[r][c + 2] = a.z; ws[r][c + 3] = a.w;
+        ws[r][c + 4] = b.x; ws[r][c + 5] = b.y; ws[r][c + 6] = b.z; ws[r][c + 7] = b.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ws[r][c + i] = 0.0;
+      }
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int h = 0; h < kKC; ++h) {
+      const double a0 = xs[2 * ty][h], a1 = xs[2 * ty + 1][h];
+      const double b0 = ws[2 * tx][h], b1 = ws[2 * tx + 1][h];
+      acc[0][0] = fma(a0, b0, acc[0][0]);
+      acc[0][1] = fma(a0, b1, acc[0][1]);
+      acc[1][0] = fma(a1, b0, acc[1][0]);
+      acc[1][1] = fma(a1, b1, acc[1][1]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int t = tt0 + 2 * ty + i, e = te0 + 2 * tx + j;
+      if (t < T && e < E) z[int64_t(t) * E + e] = acc[i][j] + (bias ? double(bias[e]) : 0.0);
+    }
+}
+
+// Top-k: one wavefront per token.  Each lane holds up to 8 logits; k rounds
+// of a wave-wide argmax (larger logit first, lower index on ties), then one
+// more for the gap to rank k+1.
+constexpr int kTopkWaves = 4;
+
+__device__ inline bool better(double va, int ia, double vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+__global__ __launch_bounds__(64 * kTopkWaves) void k_topk(const double* __restrict__ z, int T, int E,
+                                                          int k, int32_t* __restrict__ sel,
+                                                          float* __restrict__ w,
+                                                          double* __restrict__ gap) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kTopkWaves + (threadIdx.x >> 6);
+  if (t >= T) return;
+  constexpr int kPer = kMaxExperts / 64;
+  double v[kPer];
+  const double NEG = -__builtin_inf();
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = e < E ? z[int64_t(t) * E + e] : NEG;
+  }
+  double zsel[kMaxTopK + 1];
+  int isel[kMaxTopK + 1];
+  const int rounds = k < E ? k + 1 : k;
+  for (int r = 0; r < rounds; ++r) {
+    double bv = NEG;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E && v[i] != NEG && better(v[i], e, bv, bi)) {
+        bv = v[i];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const double ov = __shfl_xor(bv, off, 64);
+      const int oi = __shfl_xor(bi, off, 64);
+      if (better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    zsel[r] = bv;
+    isel[r] = bi;
+    if ((bi & 63) == lane) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (lane + 64 * i == bi) v[i] = NEG;
+    }
+  }
+  if (lane == 0) {
+    const double z0 = double(float(zsel[0]));
+    double ex[kMaxTopK];
+    double den = 0.0;
+    for (int j = 0; j < k; ++j) {
+      ex[j] = exp(double(float(zsel[j])) - z0);
+      den += ex[j];
+    }
+    for (int j = 0; j < k; ++j) {
+      sel[int64_t(t) * k + j] = isel[j];
+      w[int64_t(t) * k + j] = float(ex[j] / den);
+    }
+    gap[t] = k < E ? zsel[k - 1] - zsel[k] : __builtin_inf();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_router_logits(const uint16_t* x, const float* wr, const float* bias, double* z, int T,
+                                int H, int E, hipStream_t s) {
+  if (T <= 64) {
+    hipLaunchKernelGGL(k_router_logits_small, dim3(E), dim3(kSmallThreads), 0, s, x, wr, bias, z, T, H, E);
+  } else {
+    hipLaunchKernelGGL(k_router_logits_tiled, dim3((T + kTT - 1) / kTT, (E + kTE - 1) / kTE), dim3(256), 0,
+                       s, x, wr, bias, z, T, H, E);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const double* z, int T, int E, int k, int32_t* sel, float* w, double* gap,
+                       hipStream_t s) {
+  hipLaunchKernelGGL(k_topk, dim3((T + kTopkWaves - 1) / kTopkWaves), dim3(64 * kTopkWaves), 0, s, z, T, E,
+                     k, sel, w, gap);
+  return hipGetLastError();
+}
+
+}  // namespace ftmoe

@@ -77,8 +77,11 @@ class OracleLayerStack:
         return self.deq.get(("s", layer), f, lambda: ms.shared_blob(w, layer), w.hidden, w.inter)
 
     def forward(self, layer: int, x_bits: np.ndarray, bias: Optional[np.ndarray],
-                prefill: bool = False, outputs: bool = True):
-        """Run one layer call; x_bits uint16 [T,H] bf16 bit patterns."""
+                prefill: bool = False, outputs: bool = True, out_tokens=None):
+        """Run one layer call; x_bits uint16 [T,H] bf16 bit patterns.
+
+        out_tokens: compute the output only for these token indices (each
+        token's output depends only on its own row and routing)."""
         w = self.w
         T, k, E = x_bits.shape[0], w.top_k, w.num_experts
         x = formats.bf16_from_bits(x_bits)
@@ -113,7 +116,12 @@ class OracleLayerStack:
 
         res = dict(sel=sel, w=wts, flag=flag, slot=slot, waves=waves, gap=gap, stats=st, z=z)
         if outputs:
-            res["out"] = self.outputs(layer, x, sel, wts)
+            if out_tokens is None:
+                res["out"] = self.outputs(layer, x, sel, wts)
+            else:
+                tk = np.asarray(out_tokens)
+                res["out"] = self.outputs(layer, x[tk], sel[tk], wts[tk])
+                res["out_tokens"] = tk
         return res
 
     def outputs(self, layer, x, sel, wts):

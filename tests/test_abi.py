@@ -1,0 +1,64 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function the
+header declares, and rejects invalid configurations before touching a GPU."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import lru_expert_cache_amd as ft
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "ftmoe.h")).read()
+    return sorted(set(re.findall(r"\b(ft_moe_[a-z_]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert _header_functions() == sorted(ft.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ft.lib()
+    for name in _header_functions():
+        assert hasattr(L, name), name
+
+
+def test_struct_sizes_match_header_layout():
+    # int32 x6, pointer, int64 x2, double, int32 x2
+    assert ctypes.sizeof(ft.ft_moe_config) == 6 * 4 + 8 + 8 + 8 + 8 + 4 + 4
+    assert ctypes.sizeof(ft.ft_moe_stats) == 8 * 8 + 8 + 8 + 8
+    assert ctypes.sizeof(ft.ft_moe_trace) == 5 * 8
+
+
+def _cfg(**kw):
+    d = dict(num_layers=1, hidden=256, inter=128, num_experts=16, top_k=2, layer_fmt=[1], pool_slots=8)
+    d.update(kw)
+    return ft.make_config(**d)
+
+
+@pytest.mark.parametrize("kw", [dict(hidden=200), dict(inter=100), dict(num_experts=600), dict(top_k=17),
+                                dict(top_k=20, num_experts=16), dict(pool_slots=1), dict(layer_fmt=[7]),
+                                dict(hidden=16384), dict(hybrid_cpu_share=1.5)])
+def test_invalid_config_rejected_before_gpu(kw):
+    cfg = _cfg(**kw)
+    blobs = [np.zeros(16, np.uint8)] * (cfg.num_layers * cfg.num_experts)
+    rw = np.zeros((cfg.num_layers, cfg.num_experts, cfg.hidden), np.float32)
+    with pytest.raises(ft.FtError) as ei:
+        ft.ft_moe_init_pool(cfg, blobs, rw)
+    assert ei.value.code == ft.FT_E_INVALID
+    assert ft.ft_moe_last_error()
+
+
+def test_null_arguments_rejected():
+    L = ft.lib()
+    assert L.ft_moe_init_pool(None, None, None) == ft.FT_E_INVALID
+    assert L.ft_moe_layer_forward(None, 0, 1, None, None, None, 0, None, None) == ft.FT_E_INVALID
+    st = ft.ft_moe_stats()
+    assert L.ft_moe_pool_stats(None, -1, ctypes.byref(st), 0) == ft.FT_E_INVALID
+    assert L.ft_moe_set_hybrid_share(None, 0.5) == ft.FT_E_INVALID
+    L.ft_moe_destroy_pool(None)
