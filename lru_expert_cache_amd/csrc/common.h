@@ -1,6 +1,7 @@
 // Internal declarations shared by the library's translation units.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -133,13 +134,28 @@ struct ResolveArgs {
 };
 
 // ------------------------------------------------------------ launchers
+// Every launcher takes an optional pair of events (ev0, ev1).  When given, the
+// kernel is launched with hipExtLaunchKernelGGL so that the events bracket the
+// kernel's own execution (not the gap while the host enqueues it).
+struct Ev {
+  hipEvent_t a = nullptr, b = nullptr;
+};
+
+template <typename K, typename... Args>
+inline void ft_launch(K kernel, dim3 grid, dim3 block, hipStream_t s, Ev ev, Args... args) {
+  if (ev.a)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev.a, ev.b, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+}
+
 // router.hip
 hipError_t launch_router_logits(const uint16_t* x, const float* wr, const float* bias, double* z,
-                                int T, int H, int E, hipStream_t s);
+                                int T, int H, int E, hipStream_t s, Ev ev = {});
 hipError_t launch_topk(const double* z, int T, int E, int k, int32_t* sel, float* w, double* gap,
-                       hipStream_t s);
+                       hipStream_t s, Ev ev = {});
 // resolve.hip
-hipError_t launch_resolve(const ResolveArgs& a, hipStream_t s);
+hipError_t launch_resolve(const ResolveArgs& a, hipStream_t s, Ev ev = {});
 hipError_t launch_stage_table(DevTable tab, int E, int C, int layer, int num_layers, int pairs,
                               int64_t expert_bytes, hipStream_t s);
 hipError_t launch_uncommit(DevTable tab, const int32_t* keys, const int32_t* slots, int n, int C,
@@ -158,10 +174,10 @@ struct FfnArgs {
   ExpertLayout lay;
   int32_t act_mode;       // FT_ACT_* >> 4
 };
-hipError_t launch_ffn_gateup(const FfnArgs& a, hipStream_t s);
-hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t s);
+hipError_t launch_ffn_gateup(const FfnArgs& a, hipStream_t s, Ev ev = {});
+hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t s, Ev ev = {});
 hipError_t launch_combine(const uint16_t* pbuf, const int32_t* pair_row, int t0, int T, int k, int H,
-                          int shared_row0, uint16_t* out, hipStream_t s);
+                          int shared_row0, uint16_t* out, hipStream_t s, Ev ev = {});
 
 // ------------------------------------------------------------ errors
 void set_error(const char* fmt, ...);

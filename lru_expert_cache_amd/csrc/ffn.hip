@@ -13,7 +13,8 @@
 // a 16-row tile of W and a slice of K.  One 16-byte load per lane brings a
 // whole 16x128 tile of FP4 codes in the device layout (see common.h);
 // v_cvt_scalef32_pk_bf16_fp4 turns each byte into two bf16 values already
-// multiplied by the block scale (exact: E2M1 x E8M0 and E2M1 x E4M3 fit bf16),
+// multiplied by the E8M0 block scale (exact); NVFP4's E4M3 block scales are
+// not powers of two and get their mantissa factor in fp32 (still exact),
 // and v_mfma_f32_16x16x32_bf16 multiplies the 16x32 weight block by 32 K of
 // 16 rows of bf16 activations, which are loaded as-is (they are exactly the B
 // operand, 8 consecutive K per lane).  FP8-b128 weights convert with unit
@@ -55,6 +56,35 @@ __device__ inline bf16x8 fp4x8_to_bf16(uint32_t w, float s) {
   bf16x8 r;
   r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
   r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// 8 FP4 codes x an arbitrary positive fp32 scale s -> 8 bf16.  The scaled
+// converts of gfx950 take only the exponent of their scale operand (E8M0
+// semantics), so s = 2^e * f is applied in two parts: 2^e inside the convert,
+// the mantissa factor f in fp32.  For E4M3 block scales the product has at
+// most 6 significant bits, so every step is exact and the bf16 pack is a
+// truncation of exact values.
+__device__ inline bf16x8 fp4x8_to_bf16_anyscale(uint32_t w, float s) {
+  const uint32_t sb = __float_as_uint(s);
+  const float p2 = __uint_as_float(sb & 0x7F800000u);
+  const float f = __uint_as_float((sb & 0x007FFFFFu) | 0x3F800000u);
+  bf16x8 r;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    f32x2 v;
+    switch (b) {
+      case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, p2, 0); break;
+      case 1: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, p2, 1); break;
+      case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, p2, 2); break;
+      default: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, p2, 3); break;
+    }
+    const uint32_t lo = __float_as_uint(v[0] * f), hi = __float_as_uint(v[1] * f);
+    r[2 * b] = short(lo >> 16);
+    r[2 * b + 1] = short(hi >> 16);
+  }
   return r;
 }
 
@@ -148,9 +178,14 @@ __device__ inline void tile_mma(const TileRegs<FMT>& r, const uint4 xv[4], float
       s1 = e4m3_to_f32(r.s >> 8);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4x8_to_bf16(w[j], j < 2 ? s0 : s1), as_bf16x8(xv[j]), acc, 0,
-                                                    0, 0);
+    for (int j = 0; j < 4; ++j) {
+      bf16x8 av;
+      if constexpr (FMT == FT_FMT_MXFP4)
+        av = fp4x8_to_bf16(w[j], s0);
+      else
+        av = fp4x8_to_bf16_anyscale(w[j], j < 2 ? s0 : s1);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, as_bf16x8(xv[j]), acc, 0, 0, 0);
+    }
   }
 }
 
@@ -302,7 +337,7 @@ Split choose_split(int K, int R, int kpwmax) {
 }
 
 template <bool GATEUP>
-hipError_t launch_ffn(const FfnArgs& a, hipStream_t st) {
+hipError_t launch_ffn(const FfnArgs& a, hipStream_t st, Ev ev) {
   if (a.n_list <= 0) return hipSuccess;
   const MatLayout& m = a.lay.m[GATEUP ? 0 : 2];
   const int fmt = a.lay.fmt;
@@ -312,13 +347,13 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t st) {
   const dim3 block(64 * s.RB * s.SK);
   switch (fmt) {
     case FT_FMT_MXFP4:
-      hipLaunchKernelGGL((k_ffn<FT_FMT_MXFP4, GATEUP>), grid, block, 0, st, a, s.SK, s.RB, s.kpw);
+      ft_launch(k_ffn<FT_FMT_MXFP4, GATEUP>, grid, block, st, ev, a, s.SK, s.RB, s.kpw);
       break;
     case FT_FMT_NVFP4:
-      hipLaunchKernelGGL((k_ffn<FT_FMT_NVFP4, GATEUP>), grid, block, 0, st, a, s.SK, s.RB, s.kpw);
+      ft_launch(k_ffn<FT_FMT_NVFP4, GATEUP>, grid, block, st, ev, a, s.SK, s.RB, s.kpw);
       break;
     case FT_FMT_FP8_B128:
-      hipLaunchKernelGGL((k_ffn<FT_FMT_FP8_B128, GATEUP>), grid, block, 0, st, a, s.SK, s.RB, s.kpw);
+      ft_launch(k_ffn<FT_FMT_FP8_B128, GATEUP>, grid, block, st, ev, a, s.SK, s.RB, s.kpw);
       break;
     default:
       return hipErrorInvalidValue;
@@ -374,14 +409,14 @@ bool ffn_shape_ok(int fmt, int hidden, int inter) {
          choose_split(inter, hidden, kpw_max(fmt, false)).SK > 0;
 }
 
-hipError_t launch_ffn_gateup(const FfnArgs& a, hipStream_t s) { return launch_ffn<true>(a, s); }
-hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t s) { return launch_ffn<false>(a, s); }
+hipError_t launch_ffn_gateup(const FfnArgs& a, hipStream_t s, Ev ev) { return launch_ffn<true>(a, s, ev); }
+hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t s, Ev ev) { return launch_ffn<false>(a, s, ev); }
 
 hipError_t launch_combine(const uint16_t* pbuf, const int32_t* pair_row, int t0, int T, int k, int H,
-                          int shared_row0, uint16_t* out, hipStream_t s) {
+                          int shared_row0, uint16_t* out, hipStream_t s, Ev ev) {
   if (T <= t0) return hipSuccess;
   const dim3 grid((H / 8 + 255) / 256, T - t0);
-  hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, s, pbuf, pair_row, t0, k, H, shared_row0, out);
+  ft_launch(k_combine, grid, dim3(256), s, ev, pbuf, pair_row, t0, k, H, shared_row0, out);
   return hipGetLastError();
 }
 

@@ -302,6 +302,8 @@ FfnArgs ffn_args(ft_moe_pool* p, int layer, int list_off, int n, const int32_t* 
 double mat_bytes(int fmt, double rows, double cols);
 hipEvent_t prof_begin(ft_moe_pool* p, hipStream_t s);
 void prof_end(ft_moe_pool* p, int stage, hipEvent_t a, hipStream_t s, double bytes, double flops);
+Ev prof_pair(ft_moe_pool* p);
+void prof_push(ft_moe_pool* p, int stage, Ev ev, double bytes, double flops);
 
 // groups / rows: how many expert groups and rows this launch runs (for the
 // algorithmic byte and flop counts of the stage timers).
@@ -312,14 +314,14 @@ int run_ffn(ft_moe_pool* p, int layer, const void* x, int list_off, int n, const
   const double H = p->H, I = p->I;
   a.x = static_cast<const uint16_t*>(x);
   a.out = p->hbuf;
-  hipEvent_t e0 = prof_begin(p, s);
-  FT_HIP_CHECK(launch_ffn_gateup(a, s));
-  prof_end(p, FT_STAGE_FFN_GATEUP, e0, s, groups * 2 * mat_bytes(f, I, H) + rows * (H + I) * 2, rows * 4 * H * I);
+  Ev ev = prof_pair(p);
+  FT_HIP_CHECK(launch_ffn_gateup(a, s, ev));
+  prof_push(p, FT_STAGE_FFN_GATEUP, ev, groups * 2 * mat_bytes(f, I, H) + rows * (H + I) * 2, rows * 4 * H * I);
   a.x = p->hbuf;
   a.out = p->pbuf;
-  e0 = prof_begin(p, s);
-  FT_HIP_CHECK(launch_ffn_down(a, s));
-  prof_end(p, FT_STAGE_FFN_DOWN, e0, s, groups * mat_bytes(f, H, I) + rows * (I + H) * 2, rows * 2 * H * I);
+  ev = prof_pair(p);
+  FT_HIP_CHECK(launch_ffn_down(a, s, ev));
+  prof_push(p, FT_STAGE_FFN_DOWN, ev, groups * mat_bytes(f, H, I) + rows * (I + H) * 2, rows * 2 * H * I);
   return FT_OK;
 }
 
@@ -381,6 +383,20 @@ void prof_end(ft_moe_pool* p, int stage, hipEvent_t a, hipStream_t s, double byt
   if (!b) return;
   (void)hipEventRecord(b, s);
   p->prof_pending.push_back({stage, a, b, bytes, flops});
+}
+
+// Event pair for a kernel launched through ft_launch (bracketing the kernel itself).
+Ev prof_pair(ft_moe_pool* p) {
+  Ev ev;
+  if (!p->profiling) return ev;
+  ev.a = prof_event(p);
+  ev.b = prof_event(p);
+  if (!ev.a || !ev.b) ev = Ev{};
+  return ev;
+}
+
+void prof_push(ft_moe_pool* p, int stage, Ev ev, double bytes, double flops) {
+  if (ev.a) p->prof_pending.push_back({stage, ev.a, ev.b, bytes, flops});
 }
 
 // Fold finished records into the sums (all of them if wait).
@@ -446,6 +462,14 @@ int forward_prefill(ft_moe_pool* p, int layer, int T, const void* x, void* out, 
     set_error("prefill layer %d out of order (expected 0 or %d)", layer, p->prefill_next);
     return FT_E_STATE;
   }
+  // the whole layer is streamed into its staging half
+  p->last_se.resize(E);
+  p->last_ss.resize(E);
+  p->last_ce.clear();
+  for (int e = 0; e < E; ++e) {
+    p->last_se[e] = e;
+    p->last_ss[e] = (layer & 1) * E + e;
+  }
   // table: the staging halves lose their LRU residents
   FT_HIP_CHECK(launch_stage_table(p->tab, E, int(p->C), layer, L, T * p->k, 0, s));
   if (layer == 0) {
@@ -465,16 +489,16 @@ int forward_prefill(ft_moe_pool* p, int layer, int T, const void* x, void* out, 
   }
   FT_HIP_CHECK(hipStreamWaitEvent(s, p->ev_staged[layer & 1], 0));
   ResolveArgs ra = resolve_args(p, layer, T, 0, 1);
-  hipEvent_t er = prof_begin(p, s);
-  FT_HIP_CHECK(launch_resolve(ra, s));
-  prof_end(p, FT_STAGE_RESOLVE, er, s, 0.0, 0.0);
+  Ev er = prof_pair(p);
+  FT_HIP_CHECK(launch_resolve(ra, s, er));
+  prof_push(p, FT_STAGE_RESOLVE, er, 0.0, 0.0);
   const double rows = double(T) * p->k + (p->shared ? T : 0);
   int rc = run_ffn(p, layer, x, 0, E + 1, p->dev_header + 9, s, E + p->shared, rows);
   if (rc) return rc;
-  hipEvent_t e0 = prof_begin(p, s);
+  Ev ev = prof_pair(p);
   FT_HIP_CHECK(launch_combine(p->pbuf, p->pair_row, 0, T, p->k, p->H, p->shared ? T * p->k : -1,
-                              static_cast<uint16_t*>(out), s));
-  prof_end(p, FT_STAGE_COMBINE, e0, s, (rows + T) * p->H * 2.0, 0.0);
+                              static_cast<uint16_t*>(out), s, ev));
+  prof_push(p, FT_STAGE_COMBINE, ev, (rows + T) * p->H * 2.0, 0.0);
   FT_HIP_CHECK(hipEventRecord(p->ev_done[layer & 1], s));
   p->prefill_next = layer + 1 == L ? 0 : layer + 1;
   return FT_OK;
@@ -489,9 +513,9 @@ int forward_decode(ft_moe_pool* p, int layer, int T, const void* x, void* out, h
   int t0 = 0;
   while (t0 < T) {
     ResolveArgs ra = resolve_args(p, layer, T, t0, 0);
-    hipEvent_t er = prof_begin(p, s);
-    FT_HIP_CHECK(launch_resolve(ra, s));
-    prof_end(p, FT_STAGE_RESOLVE, er, s, 0.0, 0.0);
+    Ev er = prof_pair(p);
+    FT_HIP_CHECK(launch_resolve(ra, s, er));
+    prof_push(p, FT_STAGE_RESOLVE, er, 0.0, 0.0);
     FT_HIP_CHECK(hipEventRecord(p->ev_resolved, s));
     FT_HIP_CHECK(hipEventSynchronize(p->ev_resolved));
     if (p->profiling) prof_drain(p, false);
@@ -566,10 +590,10 @@ int forward_decode(ft_moe_pool* p, int layer, int T, const void* x, void* out, h
       FT_HIP_CHECK(hipEventRecord(p->ev_cpu_copied, s));
       p->cpu_copy_pending = true;
     }
-    hipEvent_t eb = prof_begin(p, s);
+    Ev eb = prof_pair(p);
     FT_HIP_CHECK(launch_combine(p->pbuf, p->pair_row, t0, h.t1, k, p->H, p->shared ? h.pairs : -1,
-                                static_cast<uint16_t*>(out), s));
-    prof_end(p, FT_STAGE_COMBINE, eb, s, (double(h.rows) + (h.t1 - t0)) * p->H * 2.0, 0.0);
+                                static_cast<uint16_t*>(out), s, eb));
+    prof_push(p, FT_STAGE_COMBINE, eb, (double(h.rows) + (h.t1 - t0)) * p->H * 2.0, 0.0);
     t0 = h.t1;
   }
   return FT_OK;
@@ -790,13 +814,13 @@ int ft_moe_layer_forward(ft_moe_pool* p, int32_t layer, int32_t num_tokens, cons
     if (rc) return rc;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     const int T = num_tokens, E = p->E, k = p->k;
-    hipEvent_t e0 = prof_begin(p, s);
+    Ev e0 = prof_pair(p);
     FT_HIP_CHECK(launch_router_logits(static_cast<const uint16_t*>(x_bf16), p->router_dev + int64_t(layer) * E * p->H,
-                                      router_bias, p->z, T, p->H, E, s));
-    prof_end(p, FT_STAGE_ROUTER, e0, s, double(E) * p->H * 4 + double(T) * p->H * 2, 2.0 * T * E * p->H);
-    e0 = prof_begin(p, s);
-    FT_HIP_CHECK(launch_topk(p->z, T, E, k, p->sel, p->w, p->gap, s));
-    prof_end(p, FT_STAGE_TOPK, e0, s, double(T) * E * 8, 0.0);
+                                      router_bias, p->z, T, p->H, E, s, e0));
+    prof_push(p, FT_STAGE_ROUTER, e0, double(E) * p->H * 4 + double(T) * p->H * 2, 2.0 * T * E * p->H);
+    e0 = prof_pair(p);
+    FT_HIP_CHECK(launch_topk(p->z, T, E, k, p->sel, p->w, p->gap, s, e0));
+    prof_push(p, FT_STAGE_TOPK, e0, double(T) * E * 8, 0.0);
     rc = mode == FT_FWD_DECODE ? forward_decode(p, layer, T, x_bf16, out_bf16, s)
                                : forward_prefill(p, layer, T, x_bf16, out_bf16, s);
     if (rc) return rc;

@@ -507,8 +507,8 @@ __global__ __launch_bounds__(NT) void k_free_slots(DevTable tab, int C, int lo0,
 
 }  // namespace
 
-hipError_t launch_resolve(const ResolveArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_resolve, dim3(1), dim3(NT), 0, s, a);
+hipError_t launch_resolve(const ResolveArgs& a, hipStream_t s, Ev ev) {
+  ft_launch(k_resolve, dim3(1), dim3(NT), s, ev, a);
   return hipGetLastError();
 }
 

@@ -224,20 +224,20 @@ __global__ __launch_bounds__(64 * kTopkWaves) void k_topk(const double* __restri
 }  // namespace
 
 hipError_t launch_router_logits(const uint16_t* x, const float* wr, const float* bias, double* z, int T,
-                                int H, int E, hipStream_t s) {
+                                int H, int E, hipStream_t s, Ev ev) {
   if (T <= 64) {
-    hipLaunchKernelGGL(k_router_logits_small, dim3(E), dim3(kSmallThreads), 0, s, x, wr, bias, z, T, H, E);
+    ft_launch(k_router_logits_small, dim3(E), dim3(kSmallThreads), s, ev, x, wr, bias, z, T, H, E);
   } else {
-    hipLaunchKernelGGL(k_router_logits_tiled, dim3((T + kTT - 1) / kTT, (E + kTE - 1) / kTE), dim3(256), 0,
-                       s, x, wr, bias, z, T, H, E);
+    ft_launch(k_router_logits_tiled, dim3((T + kTT - 1) / kTT, (E + kTE - 1) / kTE), dim3(256), s, ev, x, wr,
+              bias, z, T, H, E);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_topk(const double* z, int T, int E, int k, int32_t* sel, float* w, double* gap,
-                       hipStream_t s) {
-  hipLaunchKernelGGL(k_topk, dim3((T + kTopkWaves - 1) / kTopkWaves), dim3(64 * kTopkWaves), 0, s, z, T, E,
-                     k, sel, w, gap);
+                       hipStream_t s, Ev ev) {
+  ft_launch(k_topk, dim3((T + kTopkWaves - 1) / kTopkWaves), dim3(64 * kTopkWaves), s, ev, z, T, E, k, sel, w,
+            gap);
   return hipGetLastError();
 }
 

@@ -33,7 +33,8 @@ _ELEM = {ACT_MXFP8: "e4m3", ACT_MXFP4: "e2m1"}
 
 
 def silu(g: np.ndarray) -> np.ndarray:
-    return g / (1.0 + np.exp(-g))
+    with np.errstate(over="ignore"):  # exp(-g) = inf for g << 0 gives silu = -0
+        return g / (1.0 + np.exp(-g))
 
 
 def act_quant(v: np.ndarray, act_mode: int) -> np.ndarray:

@@ -62,3 +62,13 @@ def test_null_arguments_rejected():
     assert L.ft_moe_pool_stats(None, -1, ctypes.byref(st), 0) == ft.FT_E_INVALID
     assert L.ft_moe_set_hybrid_share(None, 0.5) == ft.FT_E_INVALID
     L.ft_moe_destroy_pool(None)
+
+
+def test_pinned_allocation_failure_is_reported(monkeypatch):
+    monkeypatch.setenv("FT_MOE_FAULT", "pinned_alloc")
+    cfg = _cfg()
+    blobs = [np.zeros(52_224, np.uint8)] * 16
+    rw = np.zeros((1, 16, 256), np.float32)
+    with pytest.raises(ft.FtError) as ei:
+        ft.ft_moe_init_pool(cfg, blobs, rw)
+    assert ei.value.code == ft.FT_E_OOM_PINNED

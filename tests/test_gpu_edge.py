@@ -1,0 +1,154 @@
+"""GPU parity on small synthetic layers that cover the edge cases: every
+format, ragged token counts, odd expert counts, k = 1, waves, the all-resident
+("fused") pool, the shared expert, hybrid shares 0 < s < 1 and s = 1, prefill
+staging followed by decode, and the error paths forced from the host."""
+
+import os
+
+import numpy as np
+import pytest
+
+import moe_synth as ms
+from oracle.layer import OracleLayerStack
+
+pytestmark = pytest.mark.gpu
+
+MX, NV, F8 = ms.FMT_MXFP4, ms.FMT_NVFP4, ms.FMT_FP8_B128
+
+
+def _small(cfg_id, L, H, I, E, k, fmts, C, shared=False, alpha=1.0, n_blobs=None):
+    return ms.Workload(cfg_id, f"small-{cfg_id}", L, H, I, E, k, tuple(fmts), C, (8,), 4, "decode", alpha, None,
+                       shared, False, n_blobs)
+
+
+CASES = {
+    "nvfp4-plain": (_small(107, 1, 256, 128, 8, 2, [NV], 16), [(4, 0)], 0.0),
+    "mxfp4-shared": (_small(108, 1, 256, 128, 8, 2, [MX], 16, shared=True), [(4, 0)], 0.0),
+    "fp8-waves": (_small(100, 2, 256, 128, 8, 2, [F8, F8], 6), [(8, 0), (3, 1), (8, 2)], 0.0),
+    "nvfp4-shared-fused": (_small(101, 2, 384, 256, 12, 3, [NV, NV], 40, shared=True), [(5, 0), (7, 1), (1, 2)], 0.0),
+    "mixed-hybrid": (_small(102, 3, 256, 384, 10, 2, [MX, F8, NV], 12), [(5, 0), (9, 1), (2, 2)], 0.5),
+    "all-host": (_small(103, 2, 256, 128, 9, 2, [MX, F8], 9), [(4, 0), (4, 1)], 1.0),
+    "k1-odd-E": (_small(104, 2, 128, 128, 5, 1, [MX, MX], 3, alpha=None), [(17, 0), (1, 1), (33, 2)], 0.0),
+    "wide-k": (_small(105, 1, 512, 256, 40, 16, [MX], 48), [(3, 0), (11, 1)], 0.0),
+    "aliased-blobs": (_small(106, 4, 256, 128, 8, 2, [MX, NV, MX, F8], 10, n_blobs=5), [(6, 0), (6, 1)], 0.0),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_small_case(name):
+    from tests.moe_case import GpuLayerStack, compare_call, compare_table
+    import lru_expert_cache_amd as ft
+
+    w, calls, share = CASES[name]
+    g = GpuLayerStack(w, share=share)
+    o = OracleLayerStack(w, pool_slots=g.C, share=share)
+    try:
+        for T, s in calls:
+            for l in range(w.num_layers):
+                x = ms.activations(w, l, s, T)
+                b = ms.popularity_bias(w, l, 0)
+                gr = g.forward(l, x, g.bias(l, s))
+                orr = o.forward(l, x, b)
+                compare_call(gr, orr, w.top_k)
+        compare_table(g, o)
+        st = ft.ft_moe_pool_stats(g.pool)
+        for key in ("pair_hits", "pair_misses", "expert_hits", "expert_misses", "cpu_misses", "evictions",
+                    "bytes_h2d", "calls"):
+            assert st[key] == o.stats[key], (key, st[key], o.stats[key])
+        if name == "nvfp4-shared-fused":
+            assert st["evictions"] == 0
+        if name == "all-host":
+            assert st["pair_hits"] == 0 and st["slots_used"] == 0
+    finally:
+        g.close()
+
+
+def test_prefill_then_decode_small():
+    from tests.moe_case import GpuLayerStack, compare_call, compare_table
+
+    w = _small(110, 3, 256, 128, 8, 2, [MX, F8, NV], 20)
+    g = GpuLayerStack(w)
+    o = OracleLayerStack(w, pool_slots=g.C)
+    try:
+        for s in range(2):  # decode, then a prefill chunk, then decode again
+            for l in range(3):
+                x = ms.activations(w, l, s, 6)
+                compare_call(g.forward(l, x, g.bias(l, s)), o.forward(l, x, ms.popularity_bias(w, l, 0)), 2)
+            for l in range(3):
+                x = ms.activations(w, l, 100 + s, 45)
+                compare_call(g.forward(l, x, g.bias(l, 0), prefill=True),
+                             o.forward(l, x, ms.popularity_bias(w, l, 0), prefill=True), 2)
+        compare_table(g, o)
+    finally:
+        g.close()
+
+
+def test_state_errors_and_staging_warning():
+    import torch
+    from tests.moe_case import GpuLayerStack
+    import lru_expert_cache_amd as ft
+
+    w = _small(111, 3, 256, 128, 8, 2, [MX, MX, MX], 20)
+    g = GpuLayerStack(w)
+    try:
+        x = torch.zeros((4, 256), dtype=torch.int16, device="cuda")
+        out = torch.empty_like(x)
+        with pytest.raises(ft.FtError) as ei:
+            ft.ft_moe_layer_forward(g.pool, 1, 4, x, None, out, ft.FT_FWD_PREFILL_STAGED)
+        assert ei.value.code == ft.FT_E_STATE
+        ft.ft_moe_layer_forward(g.pool, 0, 4, x, None, out, ft.FT_FWD_PREFILL_STAGED)
+        with pytest.raises(ft.FtError) as ei:
+            ft.ft_moe_layer_forward(g.pool, 0, 4, x, None, out, ft.FT_FWD_DECODE)
+        assert ei.value.code == ft.FT_E_STATE
+        ft.ft_moe_layer_forward(g.pool, 1, 4, x, None, out, ft.FT_FWD_PREFILL_STAGED)
+        ft.ft_moe_layer_forward(g.pool, 2, 4, x, None, out, ft.FT_FWD_PREFILL_STAGED)
+        ft.ft_moe_layer_forward(g.pool, 0, 4, x, None, out, ft.FT_FWD_DECODE)
+        with pytest.raises(ft.FtError) as ei:
+            ft.ft_moe_layer_forward(g.pool, 0, 4, x, None, out, ft.FT_FWD_DECODE | ft.FT_ACT_MXFP4)
+        assert ei.value.code == ft.FT_E_INVALID
+        torch.cuda.synchronize()
+    finally:
+        g.close()
+    small = _small(112, 2, 256, 128, 8, 2, [MX, MX], 10)
+    g = GpuLayerStack(small)
+    try:
+        assert g.init_rc == ft.FT_WARN_STAGING_SMALL
+        x = torch.zeros((4, 256), dtype=torch.int16, device="cuda")
+        with pytest.raises(ft.FtError) as ei:
+            ft.ft_moe_layer_forward(g.pool, 0, 4, x, None, torch.empty_like(x), ft.FT_FWD_PREFILL_STAGED)
+        assert ei.value.code == ft.FT_E_INVALID
+    finally:
+        g.close()
+
+
+def test_failed_copy_leaves_key_non_resident(monkeypatch):
+    import torch
+    from tests.moe_case import GpuLayerStack
+    import lru_expert_cache_amd as ft
+
+    w = _small(113, 2, 256, 128, 8, 2, [MX, MX], 16)
+    monkeypatch.setenv("FT_MOE_FAULT", "copy:3")
+    g = GpuLayerStack(w)
+    monkeypatch.delenv("FT_MOE_FAULT")
+    try:
+        x = torch.from_numpy(ms.activations(w, 0, 0, 4).view(np.int16)).cuda()
+        out = torch.empty_like(x)
+        with pytest.raises(ft.FtError) as ei:
+            ft.ft_moe_layer_forward(g.pool, 0, 4, x, None, out, ft.FT_FWD_DECODE)
+        assert ei.value.code == ft.FT_E_HIP and "injected" in str(ei.value)
+        stream, _ = ft.ft_moe_last_misses(g.pool)
+        assert len(stream) >= 3
+        key, _, _ = ft.ft_moe_pool_table(g.pool, 16)
+        ok = {e for e, s in stream[:2]}
+        failed = {e for e, s in stream[2:]}
+        resident = {int(k) for k in key if k >= 0}
+        assert ok <= resident and not (failed & resident)
+        assert (key >= 0).sum() == 2
+        # the pool keeps working: the failed experts miss again and are fetched
+        ft.ft_moe_layer_forward(g.pool, 0, 4, x, None, out, ft.FT_FWD_DECODE)
+        torch.cuda.synchronize()
+        key, _, _ = ft.ft_moe_pool_table(g.pool, 16)
+        assert failed <= {int(k) for k in key if k >= 0}
+        assert torch.isfinite(out.view(torch.bfloat16).float()).all()
+    finally:
+        g.close()
