@@ -184,8 +184,9 @@ typedef struct {
   uint64_t launches[FT_STAGE_COUNT];
 } ft_moe_profile;
 
-/* enable != 0 starts recording events around every stage of later calls. */
-int ft_moe_set_profiling(ft_moe_pool *p, int32_t enable);
+/* stage_mask: bit FT_STAGE_x set = record events around that stage in later
+ * calls (0 = off, (1 << FT_STAGE_COUNT) - 1 = all). */
+int ft_moe_set_profiling(ft_moe_pool *p, int32_t stage_mask);
 /* Waits for recorded events, returns the sums; reset != 0 clears them. */
 int ft_moe_profile_read(ft_moe_pool *p, ft_moe_profile *out, int32_t reset);
 

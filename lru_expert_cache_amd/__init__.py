@@ -227,8 +227,15 @@ def ft_moe_host_expert_rate(pool, layer: int, tokens: int, iters: int = 1) -> fl
     return r.value
 
 
-def ft_moe_set_profiling(pool, enable: bool = True):
-    _check(lib().ft_moe_set_profiling(pool, int(bool(enable))))
+def ft_moe_set_profiling(pool, stages=None):
+    """stages: None = all stages, [] = off, else a list of names from FT_STAGES."""
+    if stages is None:
+        mask = (1 << len(FT_STAGES)) - 1
+    else:
+        mask = 0
+        for st in stages:
+            mask |= 1 << FT_STAGES.index(st)
+    _check(lib().ft_moe_set_profiling(pool, int(mask)))
 
 
 def ft_moe_profile_read(pool, reset: bool = False) -> dict:

@@ -84,6 +84,8 @@ struct ResolveHeader {
   int32_t rows_stream;   // rows of the streamed-miss groups
   int32_t pad;
   double min_gap;        // smallest top-k gap over the wave's tokens
+  uint32_t seq;          // written last: the stamp of the wave (the host waits for it)
+  uint32_t pad2;
   // followed by: int32 stream_expert[n], int32 stream_slot[n], int32 cpu_expert[n],
   // int32 cpu_row_begin[n], int32 cpu_row_count[n], int32 cpu_row_tok[rows], float cpu_row_w[rows]
 };
@@ -107,9 +109,11 @@ struct DevTable {
 
 // Arguments of the resolve / permute kernel.
 struct ResolveArgs {
-  const int32_t* sel;      // [T*k]
-  const float* w;          // [T*k]
-  const double* gap;       // [T]
+  const double* z;         // [T][E] router logits (read when do_topk)
+  int32_t do_topk;         // 1: compute sel / w / gap of all T tokens first
+  int32_t* sel;            // [T*k]
+  float* w;                // [T*k]
+  double* gap;             // [T]
   int32_t t0, T, k, E, layer, C, mode;  // mode 0 decode, 1 staged
   int32_t stamp;
   double share;

@@ -194,9 +194,9 @@ constexpr int kpw_max(int fmt, bool gateup) { return (fmt == FT_FMT_FP8_B128 && 
 
 // GATEUP: rows of matrices 0 (gate) and 1 (up) over K = H, epilogue SwiGLU -> hbuf.
 // else:   rows of matrix 2 (down) over K = I, epilogue routing weight -> pbuf.
-template <int FMT, bool GATEUP>
-__global__ __launch_bounds__(64 * kMaxWaves) void k_ffn(FfnArgs a, int SK, int RB, int kpw) {
-  constexpr int KPW = kpw_max(FMT, GATEUP);
+template <int FMT, bool GATEUP, int KPW>
+__global__ __launch_bounds__(64 * kMaxWaves) void k_ffn(FfnArgs a, int SK, int RB) {
+  constexpr int kpw = KPW;
   constexpr int NM = GATEUP ? 2 : 1;
   __shared__ floatx4 red[kMaxWaves][NM][64];
 
@@ -336,6 +336,25 @@ Split choose_split(int K, int R, int kpwmax) {
   return s;
 }
 
+template <int FMT, bool GATEUP>
+hipError_t launch_fmt(const FfnArgs& a, const Split& s, dim3 grid, dim3 block, hipStream_t st, Ev ev) {
+  switch (s.kpw) {
+#define FT_KPW_CASE(N)                                                                   \
+  case N:                                                                                \
+    if constexpr (N <= kpw_max(FMT, GATEUP)) {                                           \
+      ft_launch(k_ffn<FMT, GATEUP, N>, grid, block, st, ev, a, s.SK, s.RB);              \
+      return hipGetLastError();                                                          \
+    }                                                                                    \
+    break;
+    FT_KPW_CASE(1) FT_KPW_CASE(2) FT_KPW_CASE(3) FT_KPW_CASE(4)
+    FT_KPW_CASE(5) FT_KPW_CASE(6) FT_KPW_CASE(7) FT_KPW_CASE(8)
+#undef FT_KPW_CASE
+    default:
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
 template <bool GATEUP>
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t st, Ev ev) {
   if (a.n_list <= 0) return hipSuccess;
@@ -346,19 +365,11 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t st, Ev ev) {
   const dim3 grid(m.rows / kTileRows / s.RB, a.n_list);
   const dim3 block(64 * s.RB * s.SK);
   switch (fmt) {
-    case FT_FMT_MXFP4:
-      ft_launch(k_ffn<FT_FMT_MXFP4, GATEUP>, grid, block, st, ev, a, s.SK, s.RB, s.kpw);
-      break;
-    case FT_FMT_NVFP4:
-      ft_launch(k_ffn<FT_FMT_NVFP4, GATEUP>, grid, block, st, ev, a, s.SK, s.RB, s.kpw);
-      break;
-    case FT_FMT_FP8_B128:
-      ft_launch(k_ffn<FT_FMT_FP8_B128, GATEUP>, grid, block, st, ev, a, s.SK, s.RB, s.kpw);
-      break;
-    default:
-      return hipErrorInvalidValue;
+    case FT_FMT_MXFP4: return launch_fmt<FT_FMT_MXFP4, GATEUP>(a, s, grid, block, st, ev);
+    case FT_FMT_NVFP4: return launch_fmt<FT_FMT_NVFP4, GATEUP>(a, s, grid, block, st, ev);
+    case FT_FMT_FP8_B128: return launch_fmt<FT_FMT_FP8_B128, GATEUP>(a, s, grid, block, st, ev);
+    default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 // out[t][h..h+7] = bf16( sum_j fp32(P[row(t,j)][h..h+7]) (+ fp32(P[shared row])) )

@@ -88,8 +88,10 @@ struct ft_moe_pool {
   uint16_t* cpu_out = nullptr;      // pinned result rows of host-computed experts
   int32_t* fail_dev = nullptr;      // [2*E] keys and slots whose copy failed
 
-  hipStream_t copy_stream = nullptr;
-  hipEvent_t ev_resolved = nullptr, ev_copied = nullptr, ev_sync = nullptr, ev_cpu_copied = nullptr;
+  hipStream_t copy_stream = nullptr;     // prefill staging, and miss copies (even)
+  hipStream_t copy_stream2 = nullptr;    // miss copies (odd): two DMA queues overlap per-copy setup
+  hipEvent_t ev_resolved = nullptr, ev_copied = nullptr, ev_copied2 = nullptr, ev_sync = nullptr,
+             ev_cpu_copied = nullptr;
   hipEvent_t ev_done[2] = {nullptr, nullptr}, ev_staged[2] = {nullptr, nullptr};
   bool cpu_copy_pending = false;
 
@@ -106,7 +108,7 @@ struct ft_moe_pool {
     hipEvent_t a, b;
     double bytes, flops;
   };
-  bool profiling = false;
+  int32_t prof_mask = 0;  // bit i: time stage i
   std::vector<ProfRec> prof_pending;
   std::vector<hipEvent_t> prof_free;
   ft_moe_profile prof{};
@@ -274,13 +276,13 @@ int fail_copies(ft_moe_pool* p, int layer, const int32_t* se, const int32_t* ss,
   return FT_E_HIP;
 }
 
-int issue_copy(ft_moe_pool* p, void* dst, const void* src, size_t bytes) {
+int issue_copy(ft_moe_pool* p, void* dst, const void* src, size_t bytes, hipStream_t cs) {
   ++p->copy_counter;
   if (p->fault_copy >= 0 && int64_t(p->copy_counter) == p->fault_copy) {
     set_error("injected failure of miss copy %llu", (unsigned long long)p->copy_counter);
     return FT_E_HIP;
   }
-  FT_HIP_CHECK(hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, p->copy_stream));
+  FT_HIP_CHECK(hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, cs));
   return FT_OK;
 }
 
@@ -302,7 +304,7 @@ FfnArgs ffn_args(ft_moe_pool* p, int layer, int list_off, int n, const int32_t* 
 double mat_bytes(int fmt, double rows, double cols);
 hipEvent_t prof_begin(ft_moe_pool* p, hipStream_t s);
 void prof_end(ft_moe_pool* p, int stage, hipEvent_t a, hipStream_t s, double bytes, double flops);
-Ev prof_pair(ft_moe_pool* p);
+Ev prof_pair(ft_moe_pool* p, hipStream_t s, int stage);
 void prof_push(ft_moe_pool* p, int stage, Ev ev, double bytes, double flops);
 
 // groups / rows: how many expert groups and rows this launch runs (for the
@@ -314,12 +316,12 @@ int run_ffn(ft_moe_pool* p, int layer, const void* x, int list_off, int n, const
   const double H = p->H, I = p->I;
   a.x = static_cast<const uint16_t*>(x);
   a.out = p->hbuf;
-  Ev ev = prof_pair(p);
+  Ev ev = prof_pair(p, s, FT_STAGE_FFN_GATEUP);
   FT_HIP_CHECK(launch_ffn_gateup(a, s, ev));
   prof_push(p, FT_STAGE_FFN_GATEUP, ev, groups * 2 * mat_bytes(f, I, H) + rows * (H + I) * 2, rows * 4 * H * I);
   a.x = p->hbuf;
   a.out = p->pbuf;
-  ev = prof_pair(p);
+  ev = prof_pair(p, s, FT_STAGE_FFN_DOWN);
   FT_HIP_CHECK(launch_ffn_down(a, s, ev));
   prof_push(p, FT_STAGE_FFN_DOWN, ev, groups * mat_bytes(f, H, I) + rows * (I + H) * 2, rows * 2 * H * I);
   return FT_OK;
@@ -327,6 +329,8 @@ int run_ffn(ft_moe_pool* p, int layer, const void* x, int list_off, int n, const
 
 ResolveArgs resolve_args(ft_moe_pool* p, int layer, int T, int t0, int mode) {
   ResolveArgs a{};
+  a.z = p->z;
+  a.do_topk = (mode == 0 && t0 == 0) ? 1 : 0;
   a.sel = p->sel;
   a.w = p->w;
   a.gap = p->gap;
@@ -371,14 +375,14 @@ hipEvent_t prof_event(ft_moe_pool* p) {
 }
 
 hipEvent_t prof_begin(ft_moe_pool* p, hipStream_t s) {
-  if (!p->profiling) return nullptr;
+  if (!(p->prof_mask & (1 << FT_STAGE_COPY))) return nullptr;
   hipEvent_t e = prof_event(p);
   if (e) (void)hipEventRecord(e, s);
   return e;
 }
 
 void prof_end(ft_moe_pool* p, int stage, hipEvent_t a, hipStream_t s, double bytes, double flops = 0.0) {
-  if (!p->profiling || !a) return;
+  if (!a) return;
   hipEvent_t b = prof_event(p);
   if (!b) return;
   (void)hipEventRecord(b, s);
@@ -386,9 +390,10 @@ void prof_end(ft_moe_pool* p, int stage, hipEvent_t a, hipStream_t s, double byt
 }
 
 // Event pair for a kernel launched through ft_launch (bracketing the kernel itself).
-Ev prof_pair(ft_moe_pool* p) {
+Ev prof_pair(ft_moe_pool* p, hipStream_t s, int stage) {
+  (void)s;
   Ev ev;
-  if (!p->profiling) return ev;
+  if (!(p->prof_mask & (1 << stage))) return ev;
   ev.a = prof_event(p);
   ev.b = prof_event(p);
   if (!ev.a || !ev.b) ev = Ev{};
@@ -489,13 +494,13 @@ int forward_prefill(ft_moe_pool* p, int layer, int T, const void* x, void* out, 
   }
   FT_HIP_CHECK(hipStreamWaitEvent(s, p->ev_staged[layer & 1], 0));
   ResolveArgs ra = resolve_args(p, layer, T, 0, 1);
-  Ev er = prof_pair(p);
+  Ev er = prof_pair(p, s, FT_STAGE_RESOLVE);
   FT_HIP_CHECK(launch_resolve(ra, s, er));
   prof_push(p, FT_STAGE_RESOLVE, er, 0.0, 0.0);
   const double rows = double(T) * p->k + (p->shared ? T : 0);
   int rc = run_ffn(p, layer, x, 0, E + 1, p->dev_header + 9, s, E + p->shared, rows);
   if (rc) return rc;
-  Ev ev = prof_pair(p);
+  Ev ev = prof_pair(p, s, FT_STAGE_COMBINE);
   FT_HIP_CHECK(launch_combine(p->pbuf, p->pair_row, 0, T, p->k, p->H, p->shared ? T * p->k : -1,
                               static_cast<uint16_t*>(out), s, ev));
   prof_push(p, FT_STAGE_COMBINE, ev, (rows + T) * p->H * 2.0, 0.0);
@@ -513,12 +518,37 @@ int forward_decode(ft_moe_pool* p, int layer, int T, const void* x, void* out, h
   int t0 = 0;
   while (t0 < T) {
     ResolveArgs ra = resolve_args(p, layer, T, t0, 0);
-    Ev er = prof_pair(p);
+    volatile uint32_t* seq = &reinterpret_cast<ResolveHeader*>(p->rb_host)->seq;
+    *seq = uint32_t(ra.stamp) ^ 0x80000000u;
+    Ev er = prof_pair(p, s, FT_STAGE_RESOLVE);
     FT_HIP_CHECK(launch_resolve(ra, s, er));
     prof_push(p, FT_STAGE_RESOLVE, er, 0.0, 0.0);
     FT_HIP_CHECK(hipEventRecord(p->ev_resolved, s));
-    FT_HIP_CHECK(hipEventSynchronize(p->ev_resolved));
-    if (p->profiling) prof_drain(p, false);
+    // The kernel publishes the wave's stamp in mapped memory after its other
+    // writes; spinning on it returns sooner than an event wait.  A stream
+    // error (or a very long wait) falls back to the event, which reports it.
+    {
+      const auto t_start = std::chrono::steady_clock::now();
+      uint32_t n = 0;
+      while (*seq != uint32_t(ra.stamp)) {
+        __builtin_ia32_pause();
+        if ((++n & 0xFFF) == 0) {
+          const hipError_t q = hipEventQuery(p->ev_resolved);
+          if (q != hipErrorNotReady && *seq != uint32_t(ra.stamp)) {
+            FT_HIP_CHECK(hipEventSynchronize(p->ev_resolved));
+            if (*seq != uint32_t(ra.stamp)) {
+              set_error("resolve finished without publishing its results");
+              return FT_E_HIP;
+            }
+          }
+          if (std::chrono::steady_clock::now() - t_start > std::chrono::seconds(30)) {
+            FT_HIP_CHECK(hipEventSynchronize(p->ev_resolved));
+          }
+        }
+      }
+      std::atomic_thread_fence(std::memory_order_acquire);
+    }
+    if (p->prof_mask) prof_drain(p, false);
     const ResolveHeader h = *reinterpret_cast<const ResolveHeader*>(p->rb_host);
     const int32_t* se = reinterpret_cast<const int32_t*>(p->rb_host + sizeof(ResolveHeader));
     const int32_t* ss = se + E;
@@ -537,15 +567,26 @@ int forward_decode(ft_moe_pool* p, int layer, int T, const void* x, void* out, h
     }
     for (int i = 0; i < h.n_cpu; ++i) p->last_ce.push_back(ce[i]);
 
-    // streamed misses: one contiguous copy per expert on the copy stream
+    // streamed misses: one contiguous copy per expert, alternating between two
+    // copy streams.  Everything earlier on s (the readers of the victim slots)
+    // has finished: the resolve kernel that published this list ran after it.
     hipEvent_t ec = h.n_stream > 0 ? prof_begin(p, p->copy_stream) : nullptr;
+    if (ec && h.n_stream > 1) FT_HIP_CHECK(hipStreamWaitEvent(p->copy_stream2, ec, 0));
     for (int i = 0; i < h.n_stream; ++i) {
       const int64_t key = int64_t(layer) * E + se[i];
       int rc = issue_copy(p, p->arena + int64_t(ss[i]) * p->slot_bytes, p->host_store + p->key_off[key],
-                          size_t(L.bytes));
-      if (rc) return fail_copies(p, layer, se, ss, i, h.n_stream, s);
+                          size_t(L.bytes), (i & 1) ? p->copy_stream2 : p->copy_stream);
+      if (rc) {
+        (void)hipStreamSynchronize(p->copy_stream);
+        (void)hipStreamSynchronize(p->copy_stream2);
+        return fail_copies(p, layer, se, ss, i, h.n_stream, s);
+      }
     }
     if (h.n_stream > 0) {
+      if (h.n_stream > 1) {
+        FT_HIP_CHECK(hipEventRecord(p->ev_copied2, p->copy_stream2));
+        FT_HIP_CHECK(hipStreamWaitEvent(p->copy_stream, p->ev_copied2, 0));
+      }
       prof_end(p, FT_STAGE_COPY, ec, p->copy_stream, double(h.n_stream) * double(p->canon_bytes[p->fmt[layer]]), 0.0);
       FT_HIP_CHECK(hipEventRecord(p->ev_copied, p->copy_stream));
     }
@@ -590,7 +631,7 @@ int forward_decode(ft_moe_pool* p, int layer, int T, const void* x, void* out, h
       FT_HIP_CHECK(hipEventRecord(p->ev_cpu_copied, s));
       p->cpu_copy_pending = true;
     }
-    Ev eb = prof_pair(p);
+    Ev eb = prof_pair(p, s, FT_STAGE_COMBINE);
     FT_HIP_CHECK(launch_combine(p->pbuf, p->pair_row, t0, h.t1, k, p->H, p->shared ? h.pairs : -1,
                                 static_cast<uint16_t*>(out), s, eb));
     prof_push(p, FT_STAGE_COMBINE, eb, (double(h.rows) + (h.t1 - t0)) * p->H * 2.0, 0.0);
@@ -766,7 +807,8 @@ int ft_moe_init_pool(const ft_moe_config* cfg, const ft_moe_weights* wts, ft_moe
       FT_HIP_CHECK(hipMemcpy(p->tab.min_gap, g.data(), size_t(L) * 8, hipMemcpyHostToDevice));
     }
     FT_HIP_CHECK(hipStreamCreateWithFlags(&p->copy_stream, hipStreamNonBlocking));
-    for (hipEvent_t* e : {&p->ev_resolved, &p->ev_copied, &p->ev_sync, &p->ev_cpu_copied, &p->ev_done[0],
+    FT_HIP_CHECK(hipStreamCreateWithFlags(&p->copy_stream2, hipStreamNonBlocking));
+    for (hipEvent_t* e : {&p->ev_resolved, &p->ev_copied, &p->ev_copied2, &p->ev_sync, &p->ev_cpu_copied, &p->ev_done[0],
                           &p->ev_done[1], &p->ev_staged[0], &p->ev_staged[1]})
       FT_HIP_CHECK(hipEventCreateWithFlags(e, hipEventDisableTiming));
     FT_HIP_CHECK(hipDeviceSynchronize());
@@ -814,13 +856,16 @@ int ft_moe_layer_forward(ft_moe_pool* p, int32_t layer, int32_t num_tokens, cons
     if (rc) return rc;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     const int T = num_tokens, E = p->E, k = p->k;
-    Ev e0 = prof_pair(p);
+    Ev e0 = prof_pair(p, s, FT_STAGE_ROUTER);
     FT_HIP_CHECK(launch_router_logits(static_cast<const uint16_t*>(x_bf16), p->router_dev + int64_t(layer) * E * p->H,
                                       router_bias, p->z, T, p->H, E, s, e0));
     prof_push(p, FT_STAGE_ROUTER, e0, double(E) * p->H * 4 + double(T) * p->H * 2, 2.0 * T * E * p->H);
-    e0 = prof_pair(p);
-    FT_HIP_CHECK(launch_topk(p->z, T, E, k, p->sel, p->w, p->gap, s, e0));
-    prof_push(p, FT_STAGE_TOPK, e0, double(T) * E * 8, 0.0);
+    if (mode == FT_FWD_PREFILL_STAGED) {
+      // decode folds the top-k into its resolve kernel
+      e0 = prof_pair(p, s, FT_STAGE_TOPK);
+      FT_HIP_CHECK(launch_topk(p->z, T, E, k, p->sel, p->w, p->gap, s, e0));
+      prof_push(p, FT_STAGE_TOPK, e0, double(T) * E * 8, 0.0);
+    }
     rc = mode == FT_FWD_DECODE ? forward_decode(p, layer, T, x_bf16, out_bf16, s)
                                : forward_prefill(p, layer, T, x_bf16, out_bf16, s);
     if (rc) return rc;
@@ -933,12 +978,12 @@ int ft_moe_host_expert_rate(ft_moe_pool* p, int32_t layer, int32_t tokens, int32
   return FT_OK;
 }
 
-int ft_moe_set_profiling(ft_moe_pool* p, int32_t enable) {
+int ft_moe_set_profiling(ft_moe_pool* p, int32_t stage_mask) {
   if (!p) {
     set_error("NULL pool");
     return FT_E_INVALID;
   }
-  p->profiling = enable != 0;
+  p->prof_mask = stage_mask & ((1 << FT_STAGE_COUNT) - 1);
   return FT_OK;
 }
 
@@ -972,7 +1017,8 @@ void ft_moe_destroy_pool(ft_moe_pool* p) {
   if (p->cpu_out) hipHostFree(p->cpu_out);
   if (p->host_store) hipHostFree(p->host_store);
   if (p->copy_stream) hipStreamDestroy(p->copy_stream);
-  for (hipEvent_t e : {p->ev_resolved, p->ev_copied, p->ev_sync, p->ev_cpu_copied, p->ev_done[0], p->ev_done[1],
+  if (p->copy_stream2) hipStreamDestroy(p->copy_stream2);
+  for (hipEvent_t e : {p->ev_resolved, p->ev_copied, p->ev_copied2, p->ev_sync, p->ev_cpu_copied, p->ev_done[0], p->ev_done[1],
                        p->ev_staged[0], p->ev_staged[1]})
     if (e) hipEventDestroy(e);
   delete p;

@@ -21,6 +21,7 @@
 // its group comes from a wavefront-ballot match of equal groups plus a
 // per-wave prefix, so rows keep pair order inside a group without atomics.
 #include "common.h"
+#include "topk.h"
 
 namespace ftmoe {
 
@@ -107,6 +108,14 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
   const int E = a.E, k = a.k, C = a.C, t0 = a.t0;
   const bool decode = a.mode == 0;
   const int key0 = a.layer * E;
+
+  // ---- 0. top-k of every token of the call (first wave of a decode call)
+  if (a.do_topk) {
+    for (int t = wid; t < a.T; t += NW)
+      wave_topk(a.z + int64_t(t) * E, E, k, a.sel + int64_t(t) * k, a.w + int64_t(t) * k, a.gap + t);
+    __threadfence_block();
+    __syncthreads();
+  }
 
   for (int e = tid; e < E; e += NT) {
     sm.first[e] = 0x7fffffff;
@@ -444,6 +453,10 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
       h->min_gap = min_gap;
     }
     __threadfence_system();
+    __syncthreads();
+    if (tid == 0) {
+      __hip_atomic_store(&h->seq, uint32_t(a.stamp), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
   }
 }
 

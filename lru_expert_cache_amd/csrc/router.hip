@@ -9,6 +9,7 @@
 // the summation order beyond fp64 rounding; weights are the softmax of the
 // selected logits rounded to fp32, evaluated in fp64.
 #include "common.h"
+#include "topk.h"
 
 namespace ftmoe {
 
@@ -150,75 +151,19 @@ __global__ __launch_bounds__(256) void k_router_logits_tiled(
     }
 }
 
-// Top-k: one wavefront per token.  Each lane holds up to 8 logits; k rounds
-// of a wave-wide argmax (larger logit first, lower index on ties), then one
-// more for the gap to rank k+1.
-constexpr int kTopkWaves = 4;
+}  // namespace
 
-__device__ inline bool better(double va, int ia, double vb, int ib) {
-  return va > vb || (va == vb && ia < ib);
-}
+namespace {
+
+constexpr int kTopkWaves = 4;
 
 __global__ __launch_bounds__(64 * kTopkWaves) void k_topk(const double* __restrict__ z, int T, int E,
                                                           int k, int32_t* __restrict__ sel,
                                                           float* __restrict__ w,
                                                           double* __restrict__ gap) {
-  const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * kTopkWaves + (threadIdx.x >> 6);
   if (t >= T) return;
-  constexpr int kPer = kMaxExperts / 64;
-  double v[kPer];
-  const double NEG = -__builtin_inf();
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int e = lane + 64 * i;
-    v[i] = e < E ? z[int64_t(t) * E + e] : NEG;
-  }
-  double zsel[kMaxTopK + 1];
-  int isel[kMaxTopK + 1];
-  const int rounds = k < E ? k + 1 : k;
-  for (int r = 0; r < rounds; ++r) {
-    double bv = NEG;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E && v[i] != NEG && better(v[i], e, bv, bi)) {
-        bv = v[i];
-        bi = e;
-      }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const double ov = __shfl_xor(bv, off, 64);
-      const int oi = __shfl_xor(bi, off, 64);
-      if (better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    zsel[r] = bv;
-    isel[r] = bi;
-    if ((bi & 63) == lane) {
-#pragma unroll
-      for (int i = 0; i < kPer; ++i)
-        if (lane + 64 * i == bi) v[i] = NEG;
-    }
-  }
-  if (lane == 0) {
-    const double z0 = double(float(zsel[0]));
-    double ex[kMaxTopK];
-    double den = 0.0;
-    for (int j = 0; j < k; ++j) {
-      ex[j] = exp(double(float(zsel[j])) - z0);
-      den += ex[j];
-    }
-    for (int j = 0; j < k; ++j) {
-      sel[int64_t(t) * k + j] = isel[j];
-      w[int64_t(t) * k + j] = float(ex[j] / den);
-    }
-    gap[t] = k < E ? zsel[k - 1] - zsel[k] : __builtin_inf();
-  }
+  wave_topk(z + int64_t(t) * E, E, k, sel + int64_t(t) * k, w + int64_t(t) * k, gap + t);
 }
 
 }  // namespace
