@@ -80,7 +80,7 @@ typedef struct {
   int32_t top_k;             /* k, 1..min(E, 16) */
   int32_t has_shared_expert; /* 1: one always-resident shared expert per layer, weight 1 */
   const int32_t *layer_fmt;  /* host [L] FT_FMT_* */
-  int64_t pool_slots;        /* > 0: number of expert slots C */
+  int64_t pool_slots;        /* > 0: number of expert slots C (top_k <= C <= 65536) */
   int64_t pool_bytes;        /* used if pool_slots == 0: C = floor(pool_bytes / largest expert size) */
   double hybrid_cpu_share;   /* 0: pure offload; (0,1]: fraction of each wave's misses computed on host */
   int32_t cpu_threads;       /* host threads for the hybrid worker (0 = 8) */

@@ -22,6 +22,7 @@ constexpr int kMaxTopK = 16;
 constexpr int kTileRows = 16;     // rows of one weight tile (MFMA M)
 constexpr int kTileK = 128;       // K extent of one weight tile
 constexpr int kResolveThreads = 1024;
+constexpr int kMaxSlots = 65536;  // pool slots (LDS bitmap of protected slots in resolve)
 
 // ------------------------------------------------------------ device expert layout
 // One expert in GPU memory (and in the pinned host store, which holds the same
@@ -99,9 +100,8 @@ struct DevTable {
   int32_t* key2slot;   // [L*E], -1 if not resident
   int32_t* slot_key;   // [C], -1 if free
   uint64_t* slot_last; // [C]
-  int32_t* lru;        // [C] slots: free ascending, then resident by last use ascending
-  int32_t* lru_tmp;    // [C]
-  int32_t* slot_mark;  // [C] stamp of the wave that hit the slot
+  int32_t* lru[2];     // [C] each; lru[*lru_cur] = slots: free ascending, then resident by last use
+  int32_t* lru_cur;    // [1] which of the two recency buffers is current
   uint64_t* clock;     // [1]
   uint64_t* stats;     // [L][ST_COUNT]
   double* min_gap;     // [L]

@@ -88,10 +88,15 @@ struct ft_moe_pool {
   uint16_t* cpu_out = nullptr;      // pinned result rows of host-computed experts
   int32_t* fail_dev = nullptr;      // [2*E] keys and slots whose copy failed
 
-  hipStream_t copy_stream = nullptr;     // prefill staging, and miss copies (even)
-  hipStream_t copy_stream2 = nullptr;    // miss copies (odd): two DMA queues overlap per-copy setup
-  hipEvent_t ev_resolved = nullptr, ev_copied = nullptr, ev_copied2 = nullptr, ev_sync = nullptr,
-             ev_cpu_copied = nullptr;
+  // Miss copies rotate over n_copy streams (several DMA queues overlap the
+  // per-copy setup of one copy with the transfer of another); copy[0] also
+  // carries the prefill staging copies.
+  static constexpr int kMaxCopyStreams = 4;
+  int n_copy = 2;
+  hipStream_t copy[kMaxCopyStreams] = {nullptr, nullptr, nullptr, nullptr};
+  hipEvent_t ev_copy_done[kMaxCopyStreams] = {nullptr, nullptr, nullptr, nullptr};
+  hipStream_t copy_stream = nullptr;  // == copy[0]
+  hipEvent_t ev_resolved = nullptr, ev_copied = nullptr, ev_sync = nullptr, ev_cpu_copied = nullptr;
   hipEvent_t ev_done[2] = {nullptr, nullptr}, ev_staged[2] = {nullptr, nullptr};
   bool cpu_copy_pending = false;
 
@@ -567,28 +572,29 @@ int forward_decode(ft_moe_pool* p, int layer, int T, const void* x, void* out, h
     }
     for (int i = 0; i < h.n_cpu; ++i) p->last_ce.push_back(ce[i]);
 
-    // streamed misses: one contiguous copy per expert, alternating between two
-    // copy streams.  Everything earlier on s (the readers of the victim slots)
-    // has finished: the resolve kernel that published this list ran after it.
-    hipEvent_t ec = h.n_stream > 0 ? prof_begin(p, p->copy_stream) : nullptr;
-    if (ec && h.n_stream > 1) FT_HIP_CHECK(hipStreamWaitEvent(p->copy_stream2, ec, 0));
+    // streamed misses: one contiguous copy per expert, rotating over the copy
+    // streams.  Everything earlier on s (the readers of the victim slots) has
+    // finished: the resolve kernel that published this list ran after it.
+    const int ncs = std::min(p->n_copy, std::max(h.n_stream, 1));
+    hipEvent_t ec = h.n_stream > 0 ? prof_begin(p, p->copy[0]) : nullptr;
+    if (ec)
+      for (int c = 1; c < ncs; ++c) FT_HIP_CHECK(hipStreamWaitEvent(p->copy[c], ec, 0));
     for (int i = 0; i < h.n_stream; ++i) {
       const int64_t key = int64_t(layer) * E + se[i];
       int rc = issue_copy(p, p->arena + int64_t(ss[i]) * p->slot_bytes, p->host_store + p->key_off[key],
-                          size_t(L.bytes), (i & 1) ? p->copy_stream2 : p->copy_stream);
+                          size_t(L.bytes), p->copy[i % ncs]);
       if (rc) {
-        (void)hipStreamSynchronize(p->copy_stream);
-        (void)hipStreamSynchronize(p->copy_stream2);
+        for (int c = 0; c < ncs; ++c) (void)hipStreamSynchronize(p->copy[c]);
         return fail_copies(p, layer, se, ss, i, h.n_stream, s);
       }
     }
     if (h.n_stream > 0) {
-      if (h.n_stream > 1) {
-        FT_HIP_CHECK(hipEventRecord(p->ev_copied2, p->copy_stream2));
-        FT_HIP_CHECK(hipStreamWaitEvent(p->copy_stream, p->ev_copied2, 0));
+      for (int c = 1; c < ncs; ++c) {
+        FT_HIP_CHECK(hipEventRecord(p->ev_copy_done[c], p->copy[c]));
+        FT_HIP_CHECK(hipStreamWaitEvent(p->copy[0], p->ev_copy_done[c], 0));
       }
-      prof_end(p, FT_STAGE_COPY, ec, p->copy_stream, double(h.n_stream) * double(p->canon_bytes[p->fmt[layer]]), 0.0);
-      FT_HIP_CHECK(hipEventRecord(p->ev_copied, p->copy_stream));
+      prof_end(p, FT_STAGE_COPY, ec, p->copy[0], double(h.n_stream) * double(p->canon_bytes[p->fmt[layer]]), 0.0);
+      FT_HIP_CHECK(hipEventRecord(p->ev_copied, p->copy[0]));
     }
 
     // host-computed misses run on CPU threads while the GPU works
@@ -703,8 +709,8 @@ int ft_moe_init_pool(const ft_moe_config* cfg, const ft_moe_weights* wts, ft_moe
     }
     for (int l = 0; l < L; ++l) p->slot_bytes = std::max(p->slot_bytes, p->lay[p->fmt[l]].bytes);
     p->C = cfg->pool_slots > 0 ? cfg->pool_slots : (cfg->pool_bytes > 0 ? cfg->pool_bytes / p->slot_bytes : 0);
-    if (p->C < k || p->C > (int64_t(1) << 30)) {
-      set_error("pool of %lld slots cannot hold top_k = %d experts", (long long)p->C, k);
+    if (p->C < k || p->C > kMaxSlots) {
+      set_error("pool of %lld slots: need top_k = %d <= slots <= %d", (long long)p->C, k, kMaxSlots);
       return FT_E_INVALID;
     }
     const char* fault = std::getenv("FT_MOE_FAULT");
@@ -784,8 +790,8 @@ int ft_moe_init_pool(const ft_moe_config* cfg, const ft_moe_weights* wts, ft_moe
     }
     const int64_t C = p->C;
     if ((rc = dev_alloc(&p->tab.key2slot, int64_t(L) * E)) || (rc = dev_alloc(&p->tab.slot_key, C)) ||
-        (rc = dev_alloc(&p->tab.slot_last, C)) || (rc = dev_alloc(&p->tab.lru, C)) ||
-        (rc = dev_alloc(&p->tab.lru_tmp, C)) || (rc = dev_alloc(&p->tab.slot_mark, C)) ||
+        (rc = dev_alloc(&p->tab.slot_last, C)) || (rc = dev_alloc(&p->tab.lru[0], C)) ||
+        (rc = dev_alloc(&p->tab.lru[1], C)) || (rc = dev_alloc(&p->tab.lru_cur, 1)) ||
         (rc = dev_alloc(&p->tab.clock, 1)) || (rc = dev_alloc(&p->tab.stats, int64_t(L) * ST_COUNT)) ||
         (rc = dev_alloc(&p->tab.min_gap, L)) || (rc = dev_alloc(&p->groups, E + 2)) ||
         (rc = dev_alloc(&p->glist, E + 2)) || (rc = dev_alloc(&p->dev_header, 16)) ||
@@ -795,20 +801,25 @@ int ft_moe_init_pool(const ft_moe_config* cfg, const ft_moe_weights* wts, ft_moe
     }
     FT_HIP_CHECK(hipMemset(p->tab.key2slot, 0xFF, size_t(L) * E * 4));
     FT_HIP_CHECK(hipMemset(p->tab.slot_key, 0xFF, size_t(C) * 4));
-    FT_HIP_CHECK(hipMemset(p->tab.slot_mark, 0xFF, size_t(C) * 4));
+    FT_HIP_CHECK(hipMemset(p->tab.lru_cur, 0, 4));
     FT_HIP_CHECK(hipMemset(p->tab.slot_last, 0, size_t(C) * 8));
     FT_HIP_CHECK(hipMemset(p->tab.clock, 0, 8));
     FT_HIP_CHECK(hipMemset(p->tab.stats, 0, size_t(L) * ST_COUNT * 8));
     {
       std::vector<int32_t> lru(C);
       for (int64_t i = 0; i < C; ++i) lru[i] = int32_t(i);
-      FT_HIP_CHECK(hipMemcpy(p->tab.lru, lru.data(), size_t(C) * 4, hipMemcpyHostToDevice));
+      FT_HIP_CHECK(hipMemcpy(p->tab.lru[0], lru.data(), size_t(C) * 4, hipMemcpyHostToDevice));
       std::vector<double> g(L, INFINITY);
       FT_HIP_CHECK(hipMemcpy(p->tab.min_gap, g.data(), size_t(L) * 8, hipMemcpyHostToDevice));
     }
-    FT_HIP_CHECK(hipStreamCreateWithFlags(&p->copy_stream, hipStreamNonBlocking));
-    FT_HIP_CHECK(hipStreamCreateWithFlags(&p->copy_stream2, hipStreamNonBlocking));
-    for (hipEvent_t* e : {&p->ev_resolved, &p->ev_copied, &p->ev_copied2, &p->ev_sync, &p->ev_cpu_copied, &p->ev_done[0],
+    if (const char* cs = std::getenv("FT_MOE_COPY_STREAMS"))
+      p->n_copy = std::max(1, std::min(ft_moe_pool::kMaxCopyStreams, std::atoi(cs)));
+    for (int c = 0; c < p->n_copy; ++c) {
+      FT_HIP_CHECK(hipStreamCreateWithFlags(&p->copy[c], hipStreamNonBlocking));
+      FT_HIP_CHECK(hipEventCreateWithFlags(&p->ev_copy_done[c], hipEventDisableTiming));
+    }
+    p->copy_stream = p->copy[0];
+    for (hipEvent_t* e : {&p->ev_resolved, &p->ev_copied, &p->ev_sync, &p->ev_cpu_copied, &p->ev_done[0],
                           &p->ev_done[1], &p->ev_staged[0], &p->ev_staged[1]})
       FT_HIP_CHECK(hipEventCreateWithFlags(e, hipEventDisableTiming));
     FT_HIP_CHECK(hipDeviceSynchronize());
@@ -1006,8 +1017,8 @@ void ft_moe_destroy_pool(ft_moe_pool* p) {
   prof_drain(p, true);
   for (hipEvent_t e : p->prof_free) hipEventDestroy(e);
   hipFree(p->arena); hipFree(p->shared_dev); hipFree(p->router_dev);
-  hipFree(p->tab.key2slot); hipFree(p->tab.slot_key); hipFree(p->tab.slot_last); hipFree(p->tab.lru);
-  hipFree(p->tab.lru_tmp); hipFree(p->tab.slot_mark); hipFree(p->tab.clock); hipFree(p->tab.stats);
+  hipFree(p->tab.key2slot); hipFree(p->tab.slot_key); hipFree(p->tab.slot_last); hipFree(p->tab.lru[0]);
+  hipFree(p->tab.lru[1]); hipFree(p->tab.lru_cur); hipFree(p->tab.clock); hipFree(p->tab.stats);
   hipFree(p->tab.min_gap);
   hipFree(p->z); hipFree(p->sel); hipFree(p->w); hipFree(p->gap); hipFree(p->pair_flag); hipFree(p->pair_slot);
   hipFree(p->pair_row); hipFree(p->row_tok); hipFree(p->row_w); hipFree(p->groups); hipFree(p->glist);
@@ -1016,9 +1027,11 @@ void ft_moe_destroy_pool(ft_moe_pool* p) {
   if (p->x_host) hipHostFree(p->x_host);
   if (p->cpu_out) hipHostFree(p->cpu_out);
   if (p->host_store) hipHostFree(p->host_store);
-  if (p->copy_stream) hipStreamDestroy(p->copy_stream);
-  if (p->copy_stream2) hipStreamDestroy(p->copy_stream2);
-  for (hipEvent_t e : {p->ev_resolved, p->ev_copied, p->ev_copied2, p->ev_sync, p->ev_cpu_copied, p->ev_done[0], p->ev_done[1],
+  for (int c = 0; c < ft_moe_pool::kMaxCopyStreams; ++c) {
+    if (p->copy[c]) hipStreamDestroy(p->copy[c]);
+    if (p->ev_copy_done[c]) hipEventDestroy(p->ev_copy_done[c]);
+  }
+  for (hipEvent_t e : {p->ev_resolved, p->ev_copied, p->ev_sync, p->ev_cpu_copied, p->ev_done[0], p->ev_done[1],
                        p->ev_staged[0], p->ev_staged[1]})
     if (e) hipEventDestroy(e);
   delete p;

@@ -44,6 +44,8 @@ struct ResolveSmem {
   int wcnt[NW][kMaxExperts];
   int wsum[NW];
   int scal[16];
+  uint32_t prot[kMaxSlots / 32];  // slots hit by this wave (not evictable)
+  int ired[4 * NW];
   double dred[NW];
 };
 
@@ -70,36 +72,42 @@ __device__ int block_exscan(int v, int* wsum, int* total) {
   return pre + x - v;
 }
 
-__device__ int block_sum(int v, int* wsum) {
-  int t;
-  block_exscan(v, wsum, &t);
-  return t;
-}
+// One pass for the call's closing counters: three sums, a max and an fp64 min.
+struct Closing {
+  int cpu_rows, hit_pairs, stream_rows, max_rows;
+  double min_gap;
+};
 
-__device__ int block_max(int v, int* wsum) {
+__device__ Closing block_closing(int cpu_rows, int hit_pairs, int stream_rows, int max_rows, double gap, int* ired,
+                                 double* dred) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
-  if (lane == 0) wsum[wid] = v;
+  for (int off = 32; off >= 1; off >>= 1) {
+    cpu_rows += __shfl_xor(cpu_rows, off, 64);
+    hit_pairs += __shfl_xor(hit_pairs, off, 64);
+    stream_rows += __shfl_xor(stream_rows, off, 64);
+    max_rows = max(max_rows, __shfl_xor(max_rows, off, 64));
+    gap = fmin(gap, __shfl_xor(gap, off, 64));
+  }
+  if (lane == 0) {
+    ired[4 * wid + 0] = cpu_rows;
+    ired[4 * wid + 1] = hit_pairs;
+    ired[4 * wid + 2] = stream_rows;
+    ired[4 * wid + 3] = max_rows;
+    dred[wid] = gap;
+  }
   __syncthreads();
-  int m = wsum[0];
+  Closing c{0, 0, 0, 0, __builtin_inf()};
 #pragma unroll
-  for (int w = 1; w < NW; ++w) m = max(m, wsum[w]);
+  for (int w = 0; w < NW; ++w) {
+    c.cpu_rows += ired[4 * w + 0];
+    c.hit_pairs += ired[4 * w + 1];
+    c.stream_rows += ired[4 * w + 2];
+    c.max_rows = max(c.max_rows, ired[4 * w + 3]);
+    c.min_gap = fmin(c.min_gap, dred[w]);
+  }
   __syncthreads();
-  return m;
-}
-
-__device__ double block_min_d(double v, double* red) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmin(v, __shfl_xor(v, off, 64));
-  if (lane == 0) red[wid] = v;
-  __syncthreads();
-  double m = red[0];
-#pragma unroll
-  for (int w = 1; w < NW; ++w) m = fmin(m, red[w]);
-  __syncthreads();
-  return m;
+  return c;
 }
 
 __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
@@ -178,6 +186,10 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
   __syncthreads();
 
   // ---- 4. hits, misses, hybrid split
+  if (decode) {
+    for (int i = tid; i < (C + 31) / 32; i += NT) sm.prot[i] = 0u;
+    __syncthreads();
+  }
   int hit = 0;
   if (tid < nD) {
     const int e = sm.D[tid];
@@ -186,7 +198,7 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
       hit = s >= 0;
       if (hit) {
         sm.dslot[tid] = s;
-        a.tab.slot_mark[s] = a.stamp;
+        atomicOr(&sm.prot[s >> 5], 1u << (s & 31));
       }
     } else {
       sm.dslot[tid] = (a.layer & 1) * E + e;
@@ -206,54 +218,46 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
   if (tid == 0) sm.scal[1] = 0;  // evictions
   __syncthreads();
 
-  // ---- 5. victims: scan the recency order, skipping this wave's hit slots
-  if (decode && m_str > 0) {
-    int taken = 0;
-    for (int c0 = 0; c0 < C && taken < m_str; c0 += NT) {
-      const int i = c0 + tid;
-      int s = -1;
-      bool elig = false;
-      if (i < C) {
-        s = a.tab.lru[i];
-        elig = a.tab.slot_mark[s] != a.stamp;
-      }
-      int tot;
-      const int vp = block_exscan(elig ? 1 : 0, sm.wsum, &tot);
-      if (elig && taken + vp < m_str) {
-        const int d = sm.sm[taken + vp];
-        const int e = sm.D[d];
-        const int old = a.tab.slot_key[s];
-        if (old >= 0) {
-          a.tab.key2slot[old] = -1;
-          atomicAdd(&sm.scal[1], 1);
-        }
-        a.tab.slot_key[s] = key0 + e;
-        a.tab.key2slot[key0 + e] = s;
-        a.tab.slot_mark[s] = a.stamp;
-        sm.dslot[d] = s;
-      }
-      taken += tot;
-    }
-  }
-  __syncthreads();
-
-  // ---- 6. recency update: untouched slots keep their order, touched slots
-  // move to the recent end in order of their last pair
+  // ---- 5. victims and recency update in one pass over the recency order.
+  // An entry is eligible unless it holds a hit of this wave; the first m_str
+  // eligible entries are the victims, the other eligible entries keep their
+  // order, and the touched slots (hits and streamed misses) follow in order of
+  // their expert's last pair.  The new order goes to the other buffer.
   if (decode) {
-    int nkeep = 0;
+    const int cur = *a.tab.lru_cur;
+    const int32_t* lru_in = a.tab.lru[cur];
+    int32_t* lru_out = a.tab.lru[cur ^ 1];
+    int neli = 0;
     for (int c0 = 0; c0 < C; c0 += NT) {
       const int i = c0 + tid;
-      int s = -1;
-      bool keep = false;
+      int s = 0;
+      bool elig = false;
       if (i < C) {
-        s = a.tab.lru[i];
-        keep = a.tab.slot_mark[s] != a.stamp;
+        s = lru_in[i];
+        elig = !((sm.prot[s >> 5] >> (s & 31)) & 1u);
       }
       int tot;
-      const int kp = block_exscan(keep ? 1 : 0, sm.wsum, &tot);
-      if (keep) a.tab.lru_tmp[nkeep + kp] = s;
-      nkeep += tot;
+      const int vp = neli + block_exscan(elig ? 1 : 0, sm.wsum, &tot);
+      if (elig) {
+        if (vp < m_str) {
+          const int d = sm.sm[vp];
+          const int e = sm.D[d];
+          const int old = a.tab.slot_key[s];
+          if (old >= 0) {
+            a.tab.key2slot[old] = -1;
+            atomicAdd(&sm.scal[1], 1);
+          }
+          a.tab.slot_key[s] = key0 + e;
+          a.tab.key2slot[key0 + e] = s;
+          sm.dslot[d] = s;
+        } else {
+          lru_out[vp - m_str] = s;
+        }
+      }
+      neli += tot;
     }
+    __syncthreads();
+    const int nkeep = neli - m_str;
     const uint64_t clk = *a.tab.clock;
     for (int d = tid; d < nD; d += NT) {
       if (sm.cls[d] == FT_PAIR_MISS_CPU) continue;
@@ -261,13 +265,14 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
       int rank = 0;
       for (int d2 = 0; d2 < nD; ++d2)
         if (sm.cls[d2] != FT_PAIR_MISS_CPU && sm.last[sm.D[d2]] < mylast) ++rank;
-      a.tab.lru_tmp[nkeep + rank] = sm.dslot[d];
+      lru_out[nkeep + rank] = sm.dslot[d];
       a.tab.slot_last[sm.dslot[d]] = clk + uint64_t(mylast);
     }
     __syncthreads();
-    for (int i = tid; i < C; i += NT) a.tab.lru[i] = a.tab.lru_tmp[i];
-    __syncthreads();
-    if (tid == 0) *a.tab.clock = clk + uint64_t(P);
+    if (tid == 0) {
+      *a.tab.clock = clk + uint64_t(P);
+      *a.tab.lru_cur = cur ^ 1;
+    }
   }
 
   // ---- 7. per-pair decisions
@@ -363,16 +368,16 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
     a.groups[nD] = g;
     a.glist[nHit] = nD;
   }
-  const int gcount = tid < nD ? sm.cnt[tid] : 0;
-  int max_rows = block_max(gcount, sm.wsum);
-  if (shared) max_rows = max(max_rows, ntok);
-  const int cpu_rows = block_sum(tid < nD && sm.cls[tid] == FT_PAIR_MISS_CPU ? sm.cnt[tid] : 0, sm.wsum);
-  const int hit_pairs = block_sum(ishit ? sm.cnt[tid] : 0, sm.wsum);
-  const int stream_rows =
-      block_sum(tid < nD && sm.cls[tid] == FT_PAIR_MISS_STREAM ? sm.cnt[tid] : 0, sm.wsum);
   double g = __builtin_inf();
   for (int tt = tid; tt < ntok; tt += NT) g = fmin(g, a.gap[t0 + tt]);
-  const double min_gap = block_min_d(g, sm.dred);
+  const bool live_d = tid < nD;
+  const int cls_d = live_d ? sm.cls[tid] : -1;
+  const int cnt_d = live_d ? sm.cnt[tid] : 0;
+  const Closing cl = block_closing(cls_d == FT_PAIR_MISS_CPU ? cnt_d : 0, cls_d == FT_PAIR_HIT ? cnt_d : 0,
+                                   cls_d == FT_PAIR_MISS_STREAM ? cnt_d : 0, cnt_d, g, sm.ired, sm.dred);
+  const int max_rows = shared ? max(cl.max_rows, ntok) : cl.max_rows;
+  const int cpu_rows = cl.cpu_rows, hit_pairs = cl.hit_pairs, stream_rows = cl.stream_rows;
+  const double min_gap = cl.min_gap;
   const int rows = P + (shared ? ntok : 0);
 
   if (tid == 0) {
@@ -490,13 +495,16 @@ __global__ __launch_bounds__(NT) void k_free_slots(DevTable tab, int C, int lo0,
     }
   }
   __syncthreads();
+  const int cur = *tab.lru_cur;
+  const int32_t* lru_in = tab.lru[cur];
+  int32_t* lru_out = tab.lru[cur ^ 1];
   int nfree = 0;
   for (int c0 = 0; c0 < C; c0 += NT) {
     const int s = c0 + tid;
     const bool f = s < C && tab.slot_key[s] < 0;
     int tot;
     const int p = block_exscan(f ? 1 : 0, wsum, &tot);
-    if (f) tab.lru_tmp[nfree + p] = s;
+    if (f) lru_out[nfree + p] = s;
     nfree += tot;
   }
   int nres = 0;
@@ -505,17 +513,19 @@ __global__ __launch_bounds__(NT) void k_free_slots(DevTable tab, int C, int lo0,
     int s = 0;
     bool r = false;
     if (i < C) {
-      s = tab.lru[i];
+      s = lru_in[i];
       r = tab.slot_key[s] >= 0;
     }
     int tot;
     const int p = block_exscan(r ? 1 : 0, wsum, &tot);
-    if (r) tab.lru_tmp[nfree + nres + p] = s;
+    if (r) lru_out[nfree + nres + p] = s;
     nres += tot;
   }
   __syncthreads();
-  for (int i = tid; i < C; i += NT) tab.lru[i] = tab.lru_tmp[i];
-  if (tid == 0 && evict_stat) *evict_stat += uint64_t(nev);
+  if (tid == 0) {
+    *tab.lru_cur = cur ^ 1;
+    if (evict_stat) *evict_stat += uint64_t(nev);
+  }
 }
 
 }  // namespace

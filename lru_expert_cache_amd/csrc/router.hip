@@ -19,19 +19,15 @@ __device__ inline double bf16_to_f64(uint16_t b) {
   return double(__uint_as_float(uint32_t(b) << 16));
 }
 
-__device__ inline double wave_sum(double v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
-// Small batches (decode): one workgroup per expert, 256 threads stride over H
-// four elements at a time; the expert's router row stays in registers while
-// the tokens stream past.  Tokens in chunks of 8 accumulators.
+// Small batches (decode): one workgroup per expert; its 256 threads stride
+// over H four elements at a time (coalesced loads), the expert's router row
+// stays in registers while up to 16 tokens stream past.  The per-token sums
+// are reduced with a butterfly whose steps are interleaved across the tokens
+// of the chunk (independent shuffles overlap), then across the 4 waves in LDS.
 constexpr int kSmallThreads = 256;
 constexpr int kSmallMaxJ = 8;   // H <= 8 * 1024
-constexpr int kTokChunk = 8;
 
+template <int kTokChunk>
 __global__ __launch_bounds__(kSmallThreads) void k_router_logits_small(
     const uint16_t* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
     double* __restrict__ z, int T, int H, int E) {
@@ -48,31 +44,42 @@ __global__ __launch_bounds__(kSmallThreads) void k_router_logits_small(
   }
   const double b = bias ? double(bias[e]) : 0.0;
   for (int t0 = 0; t0 < T; t0 += kTokChunk) {
-    double acc[kTokChunk];
-#pragma unroll
-    for (int c = 0; c < kTokChunk; ++c) acc[c] = 0.0;
+    // all loads of the chunk first (clamped rows, so they can be hoisted), then the math
+    uint2 xv[kTokChunk][2];
 #pragma unroll
     for (int c = 0; c < kTokChunk; ++c) {
-      const int t = t0 + c;
-      if (t < T) {
-        const uint16_t* xr = x + int64_t(t) * H;
+      const uint16_t* xr = x + int64_t(min(t0 + c, T - 1)) * H;
 #pragma unroll
-        for (int j = 0; j < kSmallMaxJ; ++j) {
-          const int h = 4 * tid + 1024 * j;
-          if (h < H) {
-            const uint2 xv = *reinterpret_cast<const uint2*>(xr + h);
-            acc[c] = fma(bf16_to_f64(uint16_t(xv.x & 0xFFFF)), double(wv[j].x), acc[c]);
-            acc[c] = fma(bf16_to_f64(uint16_t(xv.x >> 16)), double(wv[j].y), acc[c]);
-            acc[c] = fma(bf16_to_f64(uint16_t(xv.y & 0xFFFF)), double(wv[j].z), acc[c]);
-            acc[c] = fma(bf16_to_f64(uint16_t(xv.y >> 16)), double(wv[j].w), acc[c]);
-          }
+      for (int j = 0; j < 2; ++j) {
+        const int h = 4 * tid + 1024 * j;
+        xv[c][j] = (h < H) ? *reinterpret_cast<const uint2*>(xr + h) : make_uint2(0, 0);
+      }
+    }
+    double acc[kTokChunk];
+#pragma unroll
+    for (int c = 0; c < kTokChunk; ++c) {
+      acc[c] = 0.0;
+      const uint16_t* xr = x + int64_t(min(t0 + c, T - 1)) * H;
+#pragma unroll
+      for (int j = 0; j < kSmallMaxJ; ++j) {
+        const int h = 4 * tid + 1024 * j;
+        if (h < H && t0 + c < T) {
+          const uint2 v = j < 2 ? xv[c][j] : *reinterpret_cast<const uint2*>(xr + h);
+          acc[c] = fma(bf16_to_f64(uint16_t(v.x & 0xFFFF)), double(wv[j].x), acc[c]);
+          acc[c] = fma(bf16_to_f64(uint16_t(v.x >> 16)), double(wv[j].y), acc[c]);
+          acc[c] = fma(bf16_to_f64(uint16_t(v.y & 0xFFFF)), double(wv[j].z), acc[c]);
+          acc[c] = fma(bf16_to_f64(uint16_t(v.y >> 16)), double(wv[j].w), acc[c]);
         }
       }
     }
 #pragma unroll
-    for (int c = 0; c < kTokChunk; ++c) {
-      const double v = wave_sum(acc[c]);
-      if (lane == 0) red[wid][c] = v;
+    for (int off = 32; off >= 1; off >>= 1) {
+#pragma unroll
+      for (int c = 0; c < kTokChunk; ++c) acc[c] += __shfl_xor(acc[c], off, 64);
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int c = 0; c < kTokChunk; ++c) red[wid][c] = acc[c];
     }
     __syncthreads();
     if (tid < kTokChunk && t0 + tid < T) {
@@ -171,7 +178,10 @@ __global__ __launch_bounds__(64 * kTopkWaves) void k_topk(const double* __restri
 hipError_t launch_router_logits(const uint16_t* x, const float* wr, const float* bias, double* z, int T,
                                 int H, int E, hipStream_t s, Ev ev) {
   if (T <= 64) {
-    ft_launch(k_router_logits_small, dim3(E), dim3(kSmallThreads), s, ev, x, wr, bias, z, T, H, E);
+    if (T <= 4)
+      ft_launch(k_router_logits_small<4>, dim3(E), dim3(kSmallThreads), s, ev, x, wr, bias, z, T, H, E);
+    else
+      ft_launch(k_router_logits_small<16>, dim3(E), dim3(kSmallThreads), s, ev, x, wr, bias, z, T, H, E);
   } else {
     ft_launch(k_router_logits_tiled, dim3((T + kTT - 1) / kTT, (E + kTE - 1) / kTE), dim3(256), s, ev, x, wr,
               bias, z, T, H, E);

@@ -12,75 +12,98 @@
 
 namespace ftmoe {
 
-// Top-k of one token by one wavefront: each lane holds up to 8 logits; k
-// rounds of a wave-wide argmax (larger logit first, lower index on ties), then
-// one more for the gap to rank k+1.  Lane 0 writes sel[0..k), w[0..k), *gap.
-__device__ inline void wave_topk(const double* __restrict__ zrow, int E, int k, int32_t* __restrict__ sel,
-                          float* __restrict__ w, double* __restrict__ gap) {
+// Top-k of one token by one wavefront: k+1 rounds of a wave-wide argmax
+// (larger logit first, lower expert index on ties).  Each lane keeps the best
+// of its own logits (experts lane, lane+64, ...); a round reduces the 64 lane
+// bests with DPP row permutations (quad xor 1, quad xor 2, half-row mirror,
+// row mirror: every lane ends with the best of its row of 16) and four
+// readlanes across the rows, then only the winning lane refreshes its best.
+// No LDS round trips and no divergent branches in the reduction.
+template <int CTRL>
+__device__ __attribute__((always_inline)) inline void dpp_best(double& v, int& i) {
+  const uint64_t b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(int(uint32_t(b)), int(uint32_t(b)), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(int(uint32_t(b >> 32)), int(uint32_t(b >> 32)), CTRL, 0xF, 0xF, false);
+  const int oi = __builtin_amdgcn_update_dpp(i, i, CTRL, 0xF, 0xF, false);
+  const double ov = __longlong_as_double((int64_t(uint32_t(hi)) << 32) | uint32_t(lo));
+  const bool take = (ov > v) | ((ov == v) & (oi < i));
+  v = take ? ov : v;
+  i = take ? oi : i;
+}
+
+__device__ __attribute__((always_inline)) inline double readlane_f64(double v, int src) {
+  const uint64_t b = __double_as_longlong(v);
+  const uint32_t lo = __builtin_amdgcn_readlane(uint32_t(b), src);
+  const uint32_t hi = __builtin_amdgcn_readlane(uint32_t(b >> 32), src);
+  return __longlong_as_double((int64_t(hi) << 32) | lo);
+}
+
+__device__ __attribute__((always_inline)) inline void wave_topk(const double* __restrict__ zrow, int E, int k,
+                                                                int32_t* __restrict__ sel, float* __restrict__ w,
+                                                                double* __restrict__ gap) {
   const int lane = threadIdx.x & 63;
   constexpr int kPer = kMaxExperts / 64;
   const double NEG = -__builtin_inf();
   double v[kPer];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int e = lane + 64 * i;
-    v[i] = e < E ? zrow[e] : NEG;
+  for (int j = 0; j < kPer; ++j) {
+    const int e = lane + 64 * j;
+    const double x = e < E ? zrow[e] : NEG;
+    v[j] = x == 0.0 ? 0.0 : x;  // -0 and +0 compare equal; keep one spelling
   }
-  double zsel[kMaxTopK + 1];
-  int isel[kMaxTopK + 1];
-  double zk1 = 0.0, zk = 0.0;
+  // this lane's best (value, expert)
+  double bv = NEG;
+  int bi = 0x7fffffff;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = lane + 64 * j;
+    const bool take = (v[j] > bv) | ((v[j] == bv) & (e < bi));
+    bv = take ? v[j] : bv;
+    bi = take ? e : bi;
+  }
   const int rounds = k < E ? k + 1 : k;
+  double myz = 0.0, zk1 = 0.0, zk = 0.0;
+  for (int r = 0; r < rounds; ++r) {
+    double rv = bv;
+    int ri = bi;
+    dpp_best<0xB1>(rv, ri);   // quad_perm [1,0,3,2]
+    dpp_best<0x4E>(rv, ri);   // quad_perm [2,3,0,1]
+    dpp_best<0x141>(rv, ri);  // row_half_mirror
+    dpp_best<0x140>(rv, ri);  // row_mirror
+    double wv = readlane_f64(rv, 0);
+    int wi = __builtin_amdgcn_readlane(ri, 0);
 #pragma unroll
-  for (int r = 0; r < kMaxTopK + 1; ++r) {
-    if (r < rounds) {
-      double bv = NEG;
-      int bi = 0x7fffffff;
+    for (int row = 1; row < 4; ++row) {
+      const double ov = readlane_f64(rv, 16 * row);
+      const int oi = __builtin_amdgcn_readlane(ri, 16 * row);
+      const bool take = (ov > wv) | ((ov == wv) & (oi < wi));
+      wv = take ? ov : wv;
+      wi = take ? oi : wi;
+    }
+    if (r < k && lane == 0) sel[r] = wi;
+    if (lane == r) myz = wv;
+    if (r == k - 1) zk1 = wv;
+    if (r == k) zk = wv;
+    if ((wi & 63) == lane) {  // the winner drops the taken logit and refreshes its best
+      bv = NEG;
+      bi = 0x7fffffff;
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const int e = lane + 64 * i;
-        if (e < E && v[i] != NEG && (v[i] > bv || (v[i] == bv && e < bi))) {
-          bv = v[i];
-          bi = e;
-        }
+      for (int j = 0; j < kPer; ++j) {
+        const int e = lane + 64 * j;
+        if (e == wi) v[j] = NEG;
+        const bool take = (v[j] > bv) | ((v[j] == bv) & (e < bi));
+        bv = take ? v[j] : bv;
+        bi = take ? e : bi;
       }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const double ov = __shfl_xor(bv, off, 64);
-        const int oi = __shfl_xor(bi, off, 64);
-        if (ov > bv || (ov == bv && oi < bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      zsel[r] = bv;
-      isel[r] = bi;
-      if (r == k - 1) zk1 = bv;
-      if (r == k) zk = bv;
-#pragma unroll
-      for (int i = 0; i < kPer; ++i)
-        if (lane + 64 * i == bi) v[i] = NEG;
     }
   }
-  if (lane == 0) {
-    const double z0 = double(float(zsel[0]));
-    double ex[kMaxTopK];
-    double den = 0.0;
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-      if (j < k) {
-        ex[j] = exp(double(float(zsel[j])) - z0);
-        den += ex[j];
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-      if (j < k) {
-        sel[j] = isel[j];
-        w[j] = float(ex[j] / den);
-      }
-    }
-    *gap = k < E ? zk1 - zk : __builtin_inf();
-  }
+  // weights: lane j < k holds the logit of rank j
+  const double f0 = double(float(readlane_f64(myz, 0)));
+  const double ex = lane < k ? exp(double(float(myz)) - f0) : 0.0;
+  double den = 0.0;
+  for (int j = 0; j < k; ++j) den += readlane_f64(ex, j);
+  if (lane < k) w[lane] = float(ex / den);
+  if (lane == 0) *gap = k < E ? zk1 - zk : __builtin_inf();
 }
 
 }  // namespace ftmoe
