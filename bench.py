@@ -69,6 +69,24 @@ def measure_hbm_copy(torch, dev, nbytes=2 << 30, reps=5):
     return 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
+def measured_traffic():
+    """HBM bytes per launch of the gate/up FFN kernel from the committed rocprofv3
+    counter summary, or None when ffn.hip has changed since it was taken."""
+    import hashlib
+
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, "profiles", "ffn_gateup_qwen_a3b_decode_b16_hbm_traffic.md")
+    src = os.path.join(root, "lru_expert_cache_amd", "csrc", "ffn.hip")
+    try:
+        kv = dict(l.strip().split("=", 1) for l in open(path) if "=" in l and not l.startswith(" "))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if kv.get("ffn_source_sha256") != sha:
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(w, batch, ncalls):
     """The oracle as it stands, on the first `ncalls` (step 0, layer l) calls."""
     import moe_synth as ms
@@ -110,6 +128,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-calls", type=int, default=6)
     ap.add_argument("--no-extras", action="store_true", help="skip the batch 1/4 and link measurements")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
@@ -208,6 +228,13 @@ def main():
             torch.cuda.synchronize()
             extras[f"tokens_per_s_batch{b}"] = b * 16 / (time.perf_counter() - ta)
     ft.ft_moe_destroy_pool(pool)
+    if args.calibrate_copy:
+        a = torch.empty(128 << 20, dtype=torch.int16, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        extras["calibration_copy_bytes"] = a.numel() * 2
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -233,7 +260,8 @@ def main():
                    "top_k": w.top_k, "batch": B, "pool_slots": w.pool_slots, "format": "mxfp4",
                    "zipf_alpha": w.zipf_alpha},
         "roofline": {"kernel": "k_ffn<mxfp4, gate/up>", "bound": "hbm", "achieved": gu_gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": gu_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": gu_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(),
+                     "algorithmic_bytes_per_launch": gu["bytes"] / max(gu["launches"], 1),
                      "avg_launch_us": gu_avg_ms * 1e3},
         "cpu_baseline": cpu,
         "extras": extras,
