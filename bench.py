@@ -113,6 +113,36 @@ def cpu_baseline(w, batch, ncalls):
                       f"stack"}
 
 
+def measure_prefill(ft, torch, ms, pool, dev):
+    """One 4096-token chunk through the 48 staged layers (Qwen-A3B prefill shape)."""
+    w = ms.workload("qwen-a3b-prefill-4096")
+    T, L = w.batches[0], w.num_layers
+    xs = torch.from_numpy(np.stack([ms.activations(w, l, 0, T) for l in range(L)]).view(np.int16)).to(dev)
+    bias = torch.from_numpy(np.stack([ms.popularity_bias(w, l, 0) for l in range(L)])).to(dev)
+    out = torch.empty((T, w.hidden), dtype=torch.int16, device=dev)
+    flags = ft.FT_FWD_PREFILL_STAGED
+    for l in range(L):  # warm
+        ft.ft_moe_layer_forward(pool, l, T, xs[l], bias[l], out, flags, None, None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for l in range(L):
+        ft.ft_moe_layer_forward(pool, l, T, xs[l], bias[l], out, flags, None, None)
+    torch.cuda.synchronize()
+    sec = time.perf_counter() - t0
+    ft.ft_moe_set_profiling(pool, None)
+    ft.ft_moe_profile_read(pool, reset=True)
+    for l in range(L):
+        ft.ft_moe_layer_forward(pool, l, T, xs[l], bias[l], out, flags, None, None)
+    ft.ft_moe_set_profiling(pool, [])
+    pr = ft.ft_moe_profile_read(pool, reset=True)
+    gemm_ms = pr["ffn_gateup"]["ms"] + pr["ffn_down"]["ms"]
+    flops = pr["ffn_gateup"]["flops"] + pr["ffn_down"]["flops"]
+    return {"chunk_tokens": T, "layers": L, "chunk_s": sec, "tokens_per_s": T / sec,
+            "copy_GBps": pr["copy"]["bytes"] / (pr["copy"]["ms"] * 1e-3) / 1e9 if pr["copy"]["ms"] else None,
+            "ffn_ms_per_layer": gemm_ms / L, "ffn_TFLOPs": flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms else None,
+            "stage_ms_per_layer": {k: v["ms"] / L for k, v in pr.items()}}
+
+
 def run_steps(ft, torch, pool, x_all, bias_all, out, first, nsteps, L, B):
     for s in range(first, first + nsteps):
         for l in range(L):
@@ -155,6 +185,11 @@ def main():
     router = np.stack([ms.router_weight(w, l) for l in range(L)])
     cfg = ft.make_config(L, H, w.inter, E, w.top_k, w.layer_fmt, pool_slots=w.pool_slots)
     pool, _ = ft.ft_moe_init_pool(cfg, blobs, router)
+    prefill_pool = None
+    if not args.no_extras:
+        wp = ms.workload("qwen-a3b-prefill-4096")
+        cfgp = ft.make_config(L, H, w.inter, E, w.top_k, wp.layer_fmt, pool_slots=wp.pool_slots)
+        prefill_pool, _ = ft.ft_moe_init_pool(cfgp, blobs, router)
     del blobs, store
     log(f"[bench] pool of {w.pool_slots} slots ready in {time.perf_counter() - t:.1f} s")
 
@@ -228,6 +263,9 @@ def main():
             torch.cuda.synchronize()
             extras[f"tokens_per_s_batch{b}"] = b * 16 / (time.perf_counter() - ta)
     ft.ft_moe_destroy_pool(pool)
+    if prefill_pool is not None:
+        extras["prefill"] = measure_prefill(ft, torch, ms, prefill_pool, dev)
+        ft.ft_moe_destroy_pool(prefill_pool)
     if args.calibrate_copy:
         a = torch.empty(128 << 20, dtype=torch.int16, device=dev).fill_(1)
         b = torch.empty_like(a)

@@ -64,8 +64,12 @@ enum {
   FT_FWD_PREFILL_STAGED = 1, /* stream all experts of the layer into staging half (layer % 2) */
   FT_FWD_MODE_MASK = 0xF,
   FT_ACT_BF16 = 0 << 4,      /* expert inputs used as given (bf16) */
-  FT_ACT_MXFP8 = 1 << 4,     /* prefill only: x and h quantised to MXFP8 (E4M3, 32-blocks) */
-  FT_ACT_MXFP4 = 2 << 4,     /* prefill only: x and h quantised to MXFP4 (E2M1, 32-blocks) */
+  /* MX activation modes: prefill calls on MXFP4-weight layers only (else
+   * FT_E_INVALID).  x and h are quantised per 32-element block as the OCP MX
+   * v1.0 conversion defines (power-of-two scale from the block's amax,
+   * nearest-even, saturating) and both products run on the block-scaled MFMA. */
+  FT_ACT_MXFP8 = 1 << 4,     /* x and h as MXFP8 (E4M3) */
+  FT_ACT_MXFP4 = 2 << 4,     /* x and h as MXFP4 (E2M1) */
   FT_ACT_MASK = 0xF << 4
 };
 

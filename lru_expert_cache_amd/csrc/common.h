@@ -132,6 +132,8 @@ struct ResolveArgs {
   GroupDesc* groups;       // [max groups + 1]
   int32_t* glist;          // [max groups + 1]: hit list, then streamed, then host
   int32_t* dev_header;     // device copy of the header counts (for early-exit kernels)
+  int32_t* tiles;          // prefill: (group, 64-row tile) pairs for the MX GEMM, or null
+  int32_t tile_rows;       // rows per tile
   // mapped pinned memory for the host (decode only), may be 0
   uint8_t* host_rb;
   int64_t host_rb_cap;
@@ -182,6 +184,27 @@ hipError_t launch_ffn_gateup(const FfnArgs& a, hipStream_t s, Ev ev = {});
 hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t s, Ev ev = {});
 hipError_t launch_combine(const uint16_t* pbuf, const int32_t* pair_row, int t0, int T, int k, int H,
                           int shared_row0, uint16_t* out, hipStream_t s, Ev ev = {});
+bool ffn_shape_ok(int fmt, int hidden, int inter);
+
+// mxq.hip: bf16 rows [rows][K] -> MX codes (FP4 [rows][K/2] or FP8 [rows][K]) + E8M0 scales [rows][K/32]
+hipError_t launch_mx_quant(const uint16_t* in, int rows, int K, bool fp4, uint8_t* codes, uint8_t* scales,
+                           hipStream_t s);
+// gemm_mx.hip: grouped prefill GEMM on the block-scaled MFMA (MXFP4 weights, MX activations)
+struct MxGemmArgs {
+  const GroupDesc* groups;
+  const int32_t* tiles;       // (group, tile) pairs
+  const int32_t* n_tiles_dev; // number of valid pairs
+  int32_t max_tiles;          // grid bound
+  const uint8_t* act_codes;   // gate/up: quantised x [T][.] by token; down: quantised h [rows][.]
+  const uint8_t* act_scales;
+  const int32_t* row_tok;     // gate/up: token of each row
+  const float* row_w;         // down: routing weight of each row
+  uint16_t* out;              // gate/up: h [rows][I]; down: p [rows][H]
+  int32_t hidden, inter;
+  ExpertLayout lay;
+};
+int mx_gemm_rows_per_tile();
+hipError_t launch_mx_gemm(const MxGemmArgs& a, bool gateup, bool act_fp4, hipStream_t s, Ev ev = {});
 
 // ------------------------------------------------------------ errors
 void set_error(const char* fmt, ...);

@@ -87,6 +87,13 @@ struct ft_moe_pool {
   uint16_t* x_host = nullptr;       // pinned copy of x for host-computed experts
   uint16_t* cpu_out = nullptr;      // pinned result rows of host-computed experts
   int32_t* fail_dev = nullptr;      // [2*E] keys and slots whose copy failed
+  // prefill MX activation modes
+  uint8_t* xq_codes = nullptr;      // [cap][H] (FP8) or [cap][H/2] (FP4)
+  uint8_t* xq_scales = nullptr;     // [cap][H/32]
+  uint8_t* hq_codes = nullptr;      // [rows][I] or [rows][I/2]
+  uint8_t* hq_scales = nullptr;     // [rows][I/32]
+  int32_t* tiles = nullptr;         // [2 * max_tiles]
+  int32_t max_tiles = 0;
 
   // Miss copies rotate over n_copy streams (several DMA queues overlap the
   // per-copy setup of one copy with the transfer of another); copy[0] also
@@ -226,6 +233,7 @@ int ensure_capacity(ft_moe_pool* p, int T) {
   hipFree(p->z); hipFree(p->sel); hipFree(p->w); hipFree(p->gap); hipFree(p->pair_flag);
   hipFree(p->pair_slot); hipFree(p->pair_row); hipFree(p->row_tok); hipFree(p->row_w);
   hipFree(p->hbuf); hipFree(p->pbuf);
+  hipFree(p->xq_codes); hipFree(p->xq_scales); hipFree(p->hq_codes); hipFree(p->hq_scales); hipFree(p->tiles);
   if (p->rb_host) hipHostFree(p->rb_host);
   if (p->x_host) hipHostFree(p->x_host);
   if (p->cpu_out) hipHostFree(p->cpu_out);
@@ -247,6 +255,13 @@ int ensure_capacity(ft_moe_pool* p, int T) {
   if ((rc = dev_alloc(&p->row_w, rows))) return rc;
   if ((rc = dev_alloc(&p->hbuf, rows * p->I))) return rc;
   if ((rc = dev_alloc(&p->pbuf, rows * p->H))) return rc;
+  const int tr = mx_gemm_rows_per_tile();
+  p->max_tiles = int32_t((pairs + tr - 1) / tr + p->E + (cap + tr - 1) / tr + 2);
+  if ((rc = dev_alloc(&p->xq_codes, int64_t(cap) * p->H))) return rc;
+  if ((rc = dev_alloc(&p->xq_scales, int64_t(cap) * p->H / 32))) return rc;
+  if ((rc = dev_alloc(&p->hq_codes, rows * p->I))) return rc;
+  if ((rc = dev_alloc(&p->hq_scales, rows * p->I / 32))) return rc;
+  if ((rc = dev_alloc(&p->tiles, 2 * int64_t(p->max_tiles)))) return rc;
   p->rb_cap = int64_t(sizeof(ResolveHeader)) + 5 * 4 * int64_t(p->E) + 8 * pairs + 64;
   if (hipHostMalloc(reinterpret_cast<void**>(&p->rb_host), p->rb_cap, hipHostMallocMapped | hipHostMallocCoherent) !=
       hipSuccess) {
@@ -364,6 +379,8 @@ ResolveArgs resolve_args(ft_moe_pool* p, int layer, int T, int t0, int mode) {
   a.dev_header = p->dev_header;
   a.host_rb = mode == 0 ? p->rb_dev : nullptr;
   a.host_rb_cap = p->rb_cap;
+  a.tiles = mode == 1 ? p->tiles : nullptr;
+  a.tile_rows = mx_gemm_rows_per_tile();
   return a;
 }
 
@@ -462,8 +479,44 @@ int copy_layer_staging(ft_moe_pool* p, int layer) {
   return FT_OK;
 }
 
-int forward_prefill(ft_moe_pool* p, int layer, int T, const void* x, void* out, hipStream_t s) {
+int run_mx_ffn(ft_moe_pool* p, int layer, const void* x, int T, bool fp4, hipStream_t s) {
+  const int rows = T * p->k + (p->shared ? T : 0);
+  const double H = p->H, I = p->I;
+  FT_HIP_CHECK(launch_mx_quant(static_cast<const uint16_t*>(x), T, p->H, fp4, p->xq_codes, p->xq_scales, s));
+  MxGemmArgs a{};
+  a.groups = p->groups;
+  a.tiles = p->tiles;
+  a.n_tiles_dev = p->dev_header + 10;
+  a.max_tiles = p->max_tiles;
+  a.act_codes = p->xq_codes;
+  a.act_scales = p->xq_scales;
+  a.row_tok = p->row_tok;
+  a.row_w = p->row_w;
+  a.out = p->hbuf;
+  a.hidden = p->H;
+  a.inter = p->I;
+  a.lay = p->lay[p->fmt[layer]];
+  Ev ev = prof_pair(p, s, FT_STAGE_FFN_GATEUP);
+  FT_HIP_CHECK(launch_mx_gemm(a, true, fp4, s, ev));
+  prof_push(p, FT_STAGE_FFN_GATEUP, ev, (p->E + p->shared) * 2 * mat_bytes(FT_FMT_MXFP4, I, H) + rows * I * 2.0 +
+            T * H * (fp4 ? 0.5 + 1.0 / 32 : 1.0 + 1.0 / 32), rows * 4 * H * I);
+  FT_HIP_CHECK(launch_mx_quant(p->hbuf, rows, p->I, fp4, p->hq_codes, p->hq_scales, s));
+  a.act_codes = p->hq_codes;
+  a.act_scales = p->hq_scales;
+  a.out = p->pbuf;
+  ev = prof_pair(p, s, FT_STAGE_FFN_DOWN);
+  FT_HIP_CHECK(launch_mx_gemm(a, false, fp4, s, ev));
+  prof_push(p, FT_STAGE_FFN_DOWN, ev, (p->E + p->shared) * mat_bytes(FT_FMT_MXFP4, H, I) + rows * H * 2.0 +
+            rows * I * (fp4 ? 0.5 + 1.0 / 32 : 1.0 + 1.0 / 32), rows * 2 * H * I);
+  return FT_OK;
+}
+
+int forward_prefill(ft_moe_pool* p, int layer, int T, const void* x, void* out, hipStream_t s, int act) {
   const int L = p->L, E = p->E;
+  if (act != 0 && p->fmt[layer] != FT_FMT_MXFP4) {
+    set_error("MX activation modes need MXFP4 expert weights (layer %d)", layer);
+    return FT_E_INVALID;
+  }
   if (p->C < 2 * int64_t(E)) {
     set_error("prefill staging needs 2*E = %d slots, pool has %lld", 2 * E, (long long)p->C);
     return FT_E_INVALID;
@@ -503,7 +556,8 @@ int forward_prefill(ft_moe_pool* p, int layer, int T, const void* x, void* out, 
   FT_HIP_CHECK(launch_resolve(ra, s, er));
   prof_push(p, FT_STAGE_RESOLVE, er, 0.0, 0.0);
   const double rows = double(T) * p->k + (p->shared ? T : 0);
-  int rc = run_ffn(p, layer, x, 0, E + 1, p->dev_header + 9, s, E + p->shared, rows);
+  int rc = act != 0 ? run_mx_ffn(p, layer, x, T, act == (FT_ACT_MXFP4 >> 4), s)
+                    : run_ffn(p, layer, x, 0, E + 1, p->dev_header + 9, s, E + p->shared, rows);
   if (rc) return rc;
   Ev ev = prof_pair(p, s, FT_STAGE_COMBINE);
   FT_HIP_CHECK(launch_combine(p->pbuf, p->pair_row, 0, T, p->k, p->H, p->shared ? T * p->k : -1,
@@ -853,8 +907,8 @@ int ft_moe_layer_forward(ft_moe_pool* p, int32_t layer, int32_t num_tokens, cons
       set_error("bad flags 0x%x", flags);
       return FT_E_INVALID;
     }
-    if (act != 0) {
-      set_error("MX activation modes are not available in this build");
+    if (act != 0 && mode == FT_FWD_DECODE) {
+      set_error("MX activation modes apply to prefill calls only");
       return FT_E_INVALID;
     }
     if (mode == FT_FWD_DECODE && p->prefill_next != 0) {
@@ -878,7 +932,7 @@ int ft_moe_layer_forward(ft_moe_pool* p, int32_t layer, int32_t num_tokens, cons
       prof_push(p, FT_STAGE_TOPK, e0, double(T) * E * 8, 0.0);
     }
     rc = mode == FT_FWD_DECODE ? forward_decode(p, layer, T, x_bf16, out_bf16, s)
-                               : forward_prefill(p, layer, T, x_bf16, out_bf16, s);
+                               : forward_prefill(p, layer, T, x_bf16, out_bf16, s, act);
     if (rc) return rc;
     if (trace) {
       const size_t n = size_t(T) * k;

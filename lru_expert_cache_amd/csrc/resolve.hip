@@ -380,6 +380,29 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
   const double min_gap = cl.min_gap;
   const int rows = P + (shared ? ntok : 0);
 
+  // prefill: the (group, row tile) work list of the MX GEMM
+  if (a.tiles != nullptr) {
+    const int tr = a.tile_rows;
+    const int nt = live_d ? (cnt_d + tr - 1) / tr : 0;
+    int ntot;
+    const int base = block_exscan(nt, sm.wsum, &ntot);
+    for (int j = 0; j < nt; ++j) {
+      a.tiles[2 * (base + j)] = tid;
+      a.tiles[2 * (base + j) + 1] = j;
+    }
+    if (tid == 0) {
+      int tot = ntot;
+      if (shared) {
+        for (int j = 0; j < (ntok + tr - 1) / tr; ++j) {
+          a.tiles[2 * tot] = nD;
+          a.tiles[2 * tot + 1] = j;
+          ++tot;
+        }
+      }
+      a.dev_header[10] = tot;
+    }
+  }
+
   if (tid == 0) {
     a.dev_header[0] = t1;
     a.dev_header[1] = nD;

@@ -152,3 +152,41 @@ def test_failed_copy_leaves_key_non_resident(monkeypatch):
         assert torch.isfinite(out.view(torch.bfloat16).float()).all()
     finally:
         g.close()
+
+
+def _act_case(shared, act_mode):
+    from tests.moe_case import GpuLayerStack, rel_l2
+    from oracle import ffn as OFFN, formats as OF
+    import lru_expert_cache_amd as ft
+
+    w = _small(120 + int(shared), 3, 256, 256, 8, 2, [MX, MX, MX], 16, shared=shared)
+    g = GpuLayerStack(w)
+    o = OracleLayerStack(w, pool_slots=g.C, act_mode=act_mode)
+    flag = ft.FT_ACT_MXFP4 if act_mode == OFFN.ACT_MXFP4 else ft.FT_ACT_MXFP8
+    rels = []
+    try:
+        for l in range(3):
+            x = ms.activations(w, l, 7, 100)  # 100 tokens: ragged against 64-row tiles
+            gr = g.forward(l, x, g.bias(l, 0), prefill=True, act=flag)
+            orr = o.forward(l, x, ms.popularity_bias(w, l, 0), prefill=True)
+            from tests.moe_case import compare_call
+            compare_call(gr, orr, w.top_k, check_out=False)
+            got = OF.bf16_from_bits(gr["out_bits"])
+            rels.append(rel_l2(got, orr["out"]))
+        return rels
+    finally:
+        g.close()
+
+
+@pytest.mark.parametrize("shared", [False, True])
+@pytest.mark.parametrize("act", ["mxfp8", "mxfp4"])
+def test_prefill_mx_activation_modes_small(shared, act):
+    from oracle import ffn as OFFN
+
+    mode = OFFN.ACT_MXFP4 if act == "mxfp4" else OFFN.ACT_MXFP8
+    rels = _act_case(shared, mode)
+    print(act, "shared" if shared else "", "rel-L2", rels)
+    # x is quantised identically on both sides; h may land on the other side of
+    # an element rounding boundary when its last bf16 bit differs (fp32 MFMA
+    # accumulation vs fp64), which moves single elements by one grid step
+    assert max(rels) <= (2e-3 if act == "mxfp8" else 6e-3)
