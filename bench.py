@@ -114,33 +114,47 @@ def cpu_baseline(w, batch, ncalls):
 
 
 def measure_prefill(ft, torch, ms, pool, dev):
-    """One 4096-token chunk through the 48 staged layers (Qwen-A3B prefill shape)."""
+    """One 4096-token chunk through the 48 staged layers (Qwen-A3B prefill
+    shape), with bf16 expert inputs and with x and h MX-quantised (MXFP8,
+    MXFP4).  The MX GEMM rate is priced against the MFMA peak of its narrower
+    operand rate: FP8 (5.0 PFLOP/s) when either operand is FP8, FP4 (10.1)."""
     w = ms.workload("qwen-a3b-prefill-4096")
     T, L = w.batches[0], w.num_layers
     xs = torch.from_numpy(np.stack([ms.activations(w, l, 0, T) for l in range(L)]).view(np.int16)).to(dev)
     bias = torch.from_numpy(np.stack([ms.popularity_bias(w, l, 0) for l in range(L)])).to(dev)
     out = torch.empty((T, w.hidden), dtype=torch.int16, device=dev)
-    flags = ft.FT_FWD_PREFILL_STAGED
-    for l in range(L):  # warm
-        ft.ft_moe_layer_forward(pool, l, T, xs[l], bias[l], out, flags, None, None)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for l in range(L):
-        ft.ft_moe_layer_forward(pool, l, T, xs[l], bias[l], out, flags, None, None)
-    torch.cuda.synchronize()
-    sec = time.perf_counter() - t0
-    ft.ft_moe_set_profiling(pool, None)
-    ft.ft_moe_profile_read(pool, reset=True)
-    for l in range(L):
-        ft.ft_moe_layer_forward(pool, l, T, xs[l], bias[l], out, flags, None, None)
-    ft.ft_moe_set_profiling(pool, [])
-    pr = ft.ft_moe_profile_read(pool, reset=True)
-    gemm_ms = pr["ffn_gateup"]["ms"] + pr["ffn_down"]["ms"]
-    flops = pr["ffn_gateup"]["flops"] + pr["ffn_down"]["flops"]
-    return {"chunk_tokens": T, "layers": L, "chunk_s": sec, "tokens_per_s": T / sec,
-            "copy_GBps": pr["copy"]["bytes"] / (pr["copy"]["ms"] * 1e-3) / 1e9 if pr["copy"]["ms"] else None,
-            "ffn_ms_per_layer": gemm_ms / L, "ffn_TFLOPs": flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms else None,
-            "stage_ms_per_layer": {k: v["ms"] / L for k, v in pr.items()}}
+    res = {"chunk_tokens": T, "layers": L}
+    for name, act, peak in (("bf16", ft.FT_ACT_BF16, None), ("mxfp8", ft.FT_ACT_MXFP8, 5.0e15),
+                            ("mxfp4", ft.FT_ACT_MXFP4, 10.1e15)):
+        flags = ft.FT_FWD_PREFILL_STAGED | act
+        for l in range(L):  # warm
+            ft.ft_moe_layer_forward(pool, l, T, xs[l], bias[l], out, flags, None, None)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for l in range(L):
+            ft.ft_moe_layer_forward(pool, l, T, xs[l], bias[l], out, flags, None, None)
+        torch.cuda.synchronize()
+        sec = time.perf_counter() - t0
+        ft.ft_moe_set_profiling(pool, None)
+        ft.ft_moe_profile_read(pool, reset=True)
+        for l in range(L):
+            ft.ft_moe_layer_forward(pool, l, T, xs[l], bias[l], out, flags, None, None)
+        ft.ft_moe_set_profiling(pool, [])
+        pr = ft.ft_moe_profile_read(pool, reset=True)
+        gemm_ms = pr["ffn_gateup"]["ms"] + pr["ffn_down"]["ms"]
+        flops = pr["ffn_gateup"]["flops"] + pr["ffn_down"]["flops"]
+        tf = flops / (gemm_ms * 1e-3) if gemm_ms else None
+        r = {"chunk_s": sec, "tokens_per_s": T / sec,
+             "copy_GBps": pr["copy"]["bytes"] / (pr["copy"]["ms"] * 1e-3) / 1e9 if pr["copy"]["ms"] else None,
+             "ffn_ms_per_layer": gemm_ms / L, "ffn_TFLOPs": tf / 1e12 if tf else None,
+             "stage_ms_per_layer": {k: v["ms"] / L for k, v in pr.items()}}
+        if peak and tf:
+            r["ffn_peak_TFLOPs"] = peak / 1e12
+            r["ffn_frac_of_peak"] = tf / peak
+        res[name] = r
+        log(f"[bench] prefill {name}: {T / sec:.0f} tokens/s, FFN {gemm_ms / L:.3f} ms/layer"
+            + (f" at {tf / 1e12:.0f} TFLOP/s" if tf else ""))
+    return res
 
 
 def run_steps(ft, torch, pool, x_all, bias_all, out, first, nsteps, L, B):

@@ -163,3 +163,38 @@ def test_qwen_a3b_prefill_4096(qwen_store):
         print("rel-L2", rels)
     finally:
         g.close()
+
+
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("act", ["mxfp8", "mxfp4"])
+def test_qwen_a3b_prefill_4096_mx_activations(qwen_store, act):
+    """Full 4096-token chunk through all 48 staged layers with x and h
+    MX-quantised: decisions exact on every layer, outputs on sampled tokens."""
+    w = ms.workload("qwen-a3b-prefill-4096")
+    from tests.moe_case import GpuLayerStack, compare_call
+    from oracle import ffn as OFFN
+    import lru_expert_cache_amd as ft
+
+    mode = OFFN.ACT_MXFP4 if act == "mxfp4" else OFFN.ACT_MXFP8
+    flag = ft.FT_ACT_MXFP4 if act == "mxfp4" else ft.FT_ACT_MXFP8
+    g = GpuLayerStack(w, store=qwen_store)
+    o = OracleLayerStack(w, pool_slots=g.C, blob_fn=lambda l, e: qwen_store.expert(l, e), dequant_items=130,
+                         act_mode=mode)
+    T = 4096
+    rng = np.random.default_rng(1)
+    try:
+        rels = []
+        for l in range(w.num_layers):
+            x = ms.activations(w, l, 0, T)
+            b = ms.popularity_bias(w, l, 0)
+            want = l in (0, 47)
+            toks = np.sort(rng.choice(T, 16, replace=False)) if want else None
+            gr = g.forward(l, x, g.bias(l, 0), prefill=True, act=flag)
+            orr = o.forward(l, x, b, prefill=True, outputs=want, out_tokens=toks)
+            r = compare_call(gr, orr, w.top_k, check_out=want, tol=2e-3 if act == "mxfp8" else 6e-3)
+            if r is not None:
+                rels.append(r)
+        print(act, "rel-L2", rels)
+        assert len(rels) == 2
+    finally:
+        g.close()
