@@ -137,6 +137,12 @@ struct ResolveArgs {
   // mapped pinned memory for the host (decode only), may be 0
   uint8_t* host_rb;
   int64_t host_rb_cap;
+  // stage-timing counters for calls whose group and row counts the host never
+  // reads (device-driven decode): per timed stage (0 gate/up, 1 down, 2 copy)
+  // and weight format, {expert groups, rows} are added.  Null = off.
+  uint64_t* prof_cnt;      // [3][4][2]
+  int32_t prof_stages;     // bit i: stage i above is timed in this call
+  int32_t fmt;             // weight format of the layer
 };
 
 // ------------------------------------------------------------ launchers
@@ -170,8 +176,9 @@ hipError_t launch_uncommit(DevTable tab, const int32_t* keys, const int32_t* slo
 struct FfnArgs {
   const GroupDesc* groups;
   const int32_t* glist;   // group indices to run
-  int32_t n_list;         // entries of glist to run (grid dimension)
-  const int32_t* n_list_dev;  // if non-null, blocks with index >= *n_list_dev exit (prefill)
+  int32_t n_list;         // entries of glist to run, or (with n_list_dev) an upper bound for the grid
+  const int32_t* n_list_dev;    // if non-null: the number of entries, read on the device
+  const int32_t* list_off_dev;  // if non-null: glist entries start at glist[*list_off_dev]
   const uint16_t* x;      // gate/up: activations [T][H] indexed by token; down: hbuf [rows][I]
   const int32_t* row_tok; // gate/up: token of each row
   const float* row_w;     // down: routing weight of each row
@@ -185,6 +192,21 @@ hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t s, Ev ev = {});
 hipError_t launch_combine(const uint16_t* pbuf, const int32_t* pair_row, int t0, int T, int k, int H,
                           int shared_row0, uint16_t* out, hipStream_t s, Ev ev = {});
 bool ffn_shape_ok(int fmt, int hidden, int inter);
+
+// copy.hip: streamed misses copied by the GPU from the pinned host store.
+// The list is the one the resolve kernel left in device memory: entries
+// glist[hdr[2] .. hdr[2] + hdr[3]) are the streamed-miss groups, whose
+// GroupDesc holds the destination slot address and the expert.
+struct MissCopyArgs {
+  const uint8_t* host;        // device-visible address of the pinned host store
+  const int64_t* key_off;     // [L*E] offset of each key's blob in the store
+  const int32_t* dev_header;  // resolve's counts
+  const int32_t* glist;
+  const GroupDesc* groups;
+  int32_t layer, E;
+  int64_t bytes;              // bytes per expert of this layer (multiple of 16)
+};
+hipError_t launch_miss_copy(const MissCopyArgs& a, int workgroups, hipStream_t s, Ev ev = {});
 
 // mxq.hip: bf16 rows [rows][K] -> MX codes (FP4 [rows][K/2] or FP8 [rows][K]) + E8M0 scales [rows][K/32]
 hipError_t launch_mx_quant(const uint16_t* in, int rows, int K, bool fp4, uint8_t* codes, uint8_t* scales,

@@ -20,6 +20,8 @@
 // operand, 8 consecutive K per lane).  FP8-b128 weights convert with unit
 // scale and their fp32 block scale is applied to each 128-K partial sum.
 // Split-K slices of one row tile are summed through LDS in a fixed order.
+#include <algorithm>
+
 #include "common.h"
 
 namespace ftmoe {
@@ -31,6 +33,7 @@ typedef short bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxWaves = 8;  // 512 threads: up to 256 VGPRs per wave
+constexpr int64_t kFfnMaxGrid = 2048;  // 8 workgroups on each of the 256 CUs
 
 __device__ inline uint16_t f32_to_bf16_rne(float f) {
   const uint32_t u = __float_as_uint(f);
@@ -200,110 +203,116 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_ffn(FfnArgs a, int SK, int R
   constexpr int NM = GATEUP ? 2 : 1;
   __shared__ floatx4 red[kMaxWaves][NM][64];
 
-  const int gi = blockIdx.y;
-  if (a.n_list_dev != nullptr && gi >= *a.n_list_dev) return;
-  const GroupDesc g = a.groups[a.glist[gi]];
-  if (g.row_count <= 0) return;
-
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int rbl = w / SK, sk = w % SK;
-  const int rb = blockIdx.x * RB + rbl;
-  const uint8_t* W = reinterpret_cast<const uint8_t*>(g.wptr);
   const MatLayout& m0 = a.lay.m[GATEUP ? 0 : 2];
   const int K = m0.cols;
   const int nkb = K / kTileK;
   const int kb0 = sk * kpw;
+  const int nrbb = m0.rows / kTileRows / RB;  // row blocks of one group
+  const int n_list = a.n_list_dev != nullptr ? *a.n_list_dev : a.n_list;
+  const int list_off = a.list_off_dev != nullptr ? *a.list_off_dev : 0;
+  const int n_items = n_list * nrbb;
 
-  // weights of this wave's (row tile, K slice), loaded once
-  TileRegs<FMT> tr[NM][KPW];
-#pragma unroll
-  for (int mi = 0; mi < NM; ++mi) {
-    const MatLayout& m = a.lay.m[GATEUP ? mi : 2];
-#pragma unroll
-    for (int t = 0; t < KPW; ++t)
-      if (t < kpw) load_tile<FMT>(tr[mi][t], W, m, int64_t(rb) * nkb + kb0 + t, lane);
-  }
-  float tsc[NM];
-  {
-    const float* ts = reinterpret_cast<const float*>(W + a.lay.tscale_off);
-#pragma unroll
-    for (int mi = 0; mi < NM; ++mi) tsc[mi] = FMT == FT_FMT_NVFP4 ? ts[GATEUP ? mi : 2] : 1.0f;
-  }
+  // items (group, row block), group-major, strided over the grid
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int gi = item / nrbb;
+    const GroupDesc g = a.groups[a.glist[list_off + gi]];
+    if (g.row_count <= 0) continue;  // uniform over the workgroup
+    const int rb = (item - gi * nrbb) * RB + rbl;
+    const uint8_t* W = reinterpret_cast<const uint8_t*>(g.wptr);
 
-  const int q = lane >> 4, n = lane & 15;
-  const int ntiles = (g.row_count + 15) / 16;
-  for (int nt = 0; nt < ntiles; ++nt) {
-    const int r = nt * 16 + n;
-    const bool valid = r < g.row_count;
-    const int row = g.row_begin + r;
-    int64_t xbase = 0;
-    if (valid) xbase = GATEUP ? int64_t(a.row_tok[row]) * a.hidden : int64_t(row) * a.inter;
-
-    floatx4 acc[NM];
+    // weights of this wave's (row tile, K slice), loaded once
+    TileRegs<FMT> tr[NM][KPW];
 #pragma unroll
-    for (int mi = 0; mi < NM; ++mi) acc[mi] = {0.f, 0.f, 0.f, 0.f};
+    for (int mi = 0; mi < NM; ++mi) {
+      const MatLayout& m = a.lay.m[GATEUP ? mi : 2];
 #pragma unroll
-    for (int t = 0; t < KPW; ++t) {
-      if (t < kpw) {
-        uint4 xv[4];
-        const int64_t off = xbase + int64_t(kb0 + t) * kTileK + 32 * q;
-        if (valid) {
-          const uint4* xp = reinterpret_cast<const uint4*>(a.x + off);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) xv[j] = xp[j];
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) xv[j] = make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int mi = 0; mi < NM; ++mi) {
-          const float* sp = nullptr;
-          if constexpr (FMT == FT_FMT_FP8_B128)
-            sp = reinterpret_cast<const float*>(W + a.lay.m[GATEUP ? mi : 2].scales_off) +
-                 (int64_t(rb) * nkb + kb0 + t) * 16 + 4 * q;
-          tile_mma<FMT>(tr[mi][t], xv, acc[mi], sp);
-        }
-      }
+      for (int t = 0; t < KPW; ++t)
+        if (t < kpw) load_tile<FMT>(tr[mi][t], W, m, int64_t(rb) * nkb + kb0 + t, lane);
     }
-    if (SK > 1) {
+    float tsc[NM];
+    {
+      const float* ts = reinterpret_cast<const float*>(W + a.lay.tscale_off);
 #pragma unroll
-      for (int mi = 0; mi < NM; ++mi) red[w][mi][lane] = acc[mi];
-      __syncthreads();
-      if (sk == 0) {
+      for (int mi = 0; mi < NM; ++mi) tsc[mi] = FMT == FT_FMT_NVFP4 ? ts[GATEUP ? mi : 2] : 1.0f;
+    }
+
+    const int q = lane >> 4, n = lane & 15;
+    const int ntiles = (g.row_count + 15) / 16;
+    for (int nt = 0; nt < ntiles; ++nt) {
+      const int r = nt * 16 + n;
+      const bool valid = r < g.row_count;
+      const int row = g.row_begin + r;
+      int64_t xbase = 0;
+      if (valid) xbase = GATEUP ? int64_t(a.row_tok[row]) * a.hidden : int64_t(row) * a.inter;
+
+      floatx4 acc[NM];
 #pragma unroll
-        for (int mi = 0; mi < NM; ++mi) {
-          floatx4 s = red[w][mi][lane];
-          for (int k2 = 1; k2 < SK; ++k2) {
-            const floatx4 v = red[w + k2][mi][lane];
-            s[0] += v[0]; s[1] += v[1]; s[2] += v[2]; s[3] += v[3];
+      for (int mi = 0; mi < NM; ++mi) acc[mi] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < KPW; ++t) {
+        if (t < kpw) {
+          uint4 xv[4];
+          const int64_t off = xbase + int64_t(kb0 + t) * kTileK + 32 * q;
+          if (valid) {
+            const uint4* xp = reinterpret_cast<const uint4*>(a.x + off);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) xv[j] = xp[j];
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) xv[j] = make_uint4(0, 0, 0, 0);
           }
-          acc[mi] = s;
+#pragma unroll
+          for (int mi = 0; mi < NM; ++mi) {
+            const float* sp = nullptr;
+            if constexpr (FMT == FT_FMT_FP8_B128)
+              sp = reinterpret_cast<const float*>(W + a.lay.m[GATEUP ? mi : 2].scales_off) +
+                   (int64_t(rb) * nkb + kb0 + t) * 16 + 4 * q;
+            tile_mma<FMT>(tr[mi][t], xv, acc[mi], sp);
+          }
         }
       }
-    }
-    if (sk == 0 && valid) {
-      // lane holds output features rb*16 + 4q + i of row r
-      const int o0 = rb * 16 + 4 * q;
-      uint16_t hv[4];
-      if constexpr (GATEUP) {
+      if (SK > 1) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float gv = acc[0][i] * tsc[0];
-          const float uv = acc[1][i] * tsc[1];
-          hv[i] = f32_to_bf16_rne(gv / (1.0f + expf(-gv)) * uv);
+        for (int mi = 0; mi < NM; ++mi) red[w][mi][lane] = acc[mi];
+        __syncthreads();
+        if (sk == 0) {
+#pragma unroll
+          for (int mi = 0; mi < NM; ++mi) {
+            floatx4 s = red[w][mi][lane];
+            for (int k2 = 1; k2 < SK; ++k2) {
+              const floatx4 v = red[w + k2][mi][lane];
+              s[0] += v[0]; s[1] += v[1]; s[2] += v[2]; s[3] += v[3];
+            }
+            acc[mi] = s;
+          }
         }
-        uint2 pk = make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16), uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
-        *reinterpret_cast<uint2*>(a.out + int64_t(row) * a.inter + o0) = pk;
-      } else {
-        const float wr = a.row_w[row];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) hv[i] = f32_to_bf16_rne(wr * (acc[0][i] * tsc[0]));
-        uint2 pk = make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16), uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
-        *reinterpret_cast<uint2*>(a.out + int64_t(row) * a.hidden + o0) = pk;
       }
+      if (sk == 0 && valid) {
+        // lane holds output features rb*16 + 4q + i of row r
+        const int o0 = rb * 16 + 4 * q;
+        uint16_t hv[4];
+        if constexpr (GATEUP) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float gv = acc[0][i] * tsc[0];
+            const float uv = acc[1][i] * tsc[1];
+            hv[i] = f32_to_bf16_rne(gv / (1.0f + expf(-gv)) * uv);
+          }
+          uint2 pk = make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16), uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
+          *reinterpret_cast<uint2*>(a.out + int64_t(row) * a.inter + o0) = pk;
+        } else {
+          const float wr = a.row_w[row];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) hv[i] = f32_to_bf16_rne(wr * (acc[0][i] * tsc[0]));
+          uint2 pk = make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16), uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
+          *reinterpret_cast<uint2*>(a.out + int64_t(row) * a.hidden + o0) = pk;
+        }
+      }
+      if (SK > 1) __syncthreads();
     }
-    if (SK > 1) __syncthreads();
-  }
+  }  // items
 }
 
 struct Split {
@@ -362,7 +371,10 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t st, Ev ev) {
   const int fmt = a.lay.fmt;
   const Split s = choose_split(m.cols, m.rows, kpw_max(fmt, GATEUP));
   if (s.SK == 0) return hipErrorInvalidValue;
-  const dim3 grid(m.rows / kTileRows / s.RB, a.n_list);
+  // one workgroup per item up to a chip's worth of resident workgroups; the
+  // kernel strides over the rest (and over the unused tail of a bound)
+  const int64_t items = int64_t(a.n_list) * (m.rows / kTileRows / s.RB);
+  const dim3 grid(unsigned(std::min<int64_t>(items, kFfnMaxGrid)));
   const dim3 block(64 * s.RB * s.SK);
   switch (fmt) {
     case FT_FMT_MXFP4: return launch_fmt<FT_FMT_MXFP4, GATEUP>(a, s, grid, block, st, ev);

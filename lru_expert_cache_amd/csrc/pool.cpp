@@ -54,9 +54,17 @@ struct ft_moe_pool {
 
   // pinned host store (device layout), one entry per distinct (blob, format)
   uint8_t* host_store = nullptr;
+  const uint8_t* host_store_dev = nullptr;  // its device-visible address
   int64_t host_bytes = 0;
   std::vector<int64_t> key_off;     // [L*E]
+  int64_t* key_off_dev = nullptr;   // [L*E] device copy (device-driven miss copies)
   std::vector<uint8_t> layer_contig;
+
+  // Decode runs device-driven (the GPU copies its own misses; the host never
+  // waits) unless the call needs the host: hybrid split, several waves, or
+  // FT_MOE_DECODE_PATH=host / injected copy failures.
+  bool dev_decode = true;
+  int copy_wgs = 64;                // workgroups of the miss-copy kernel
 
   // device memory
   uint8_t* arena = nullptr;
@@ -112,7 +120,15 @@ struct ft_moe_pool {
   uint64_t copy_counter = 0;
   int64_t fault_copy = -1;
 
-  std::vector<int32_t> last_se, last_ss, last_ce;
+  // miss lists of the latest call; after a device-driven call they are read
+  // from the resolve kernel's mapped readback when first asked for
+  mutable std::vector<int32_t> last_se, last_ss, last_ce;
+  mutable bool last_pending = false;
+
+  // calls on different streams are ordered through this event
+  hipEvent_t ev_call_done = nullptr;
+  hipStream_t last_stream = nullptr;
+  bool any_call = false;
 
   // stage timing (ft_moe_set_profiling)
   struct ProfRec {
@@ -124,6 +140,10 @@ struct ft_moe_pool {
   std::vector<ProfRec> prof_pending;
   std::vector<hipEvent_t> prof_free;
   ft_moe_profile prof{};
+  // device-driven calls: groups and rows behind the timed FFN and copy
+  // stages are counted on the device (ResolveArgs::prof_cnt)
+  uint64_t* prof_cnt_dev = nullptr;  // [3][4][2]
+  uint64_t prof_cnt_seen[24] = {};
 };
 
 namespace {
@@ -230,6 +250,7 @@ void host_expert(const ExpertLayout& L, const uint8_t* blob, const uint16_t* x, 
 int ensure_capacity(ft_moe_pool* p, int T) {
   if (T <= p->cap_T) return FT_OK;
   const int cap = std::max(T, 64);
+  FT_HIP_CHECK(hipDeviceSynchronize());  // earlier calls may still use the old buffers
   hipFree(p->z); hipFree(p->sel); hipFree(p->w); hipFree(p->gap); hipFree(p->pair_flag);
   hipFree(p->pair_slot); hipFree(p->pair_row); hipFree(p->row_tok); hipFree(p->row_w);
   hipFree(p->hbuf); hipFree(p->pbuf);
@@ -306,12 +327,13 @@ int issue_copy(ft_moe_pool* p, void* dst, const void* src, size_t bytes, hipStre
   return FT_OK;
 }
 
-FfnArgs ffn_args(ft_moe_pool* p, int layer, int list_off, int n, const int32_t* n_dev) {
+FfnArgs ffn_args(ft_moe_pool* p, int layer, int list_off, int n, const int32_t* n_dev, const int32_t* off_dev) {
   FfnArgs a{};
   a.groups = p->groups;
   a.glist = p->glist + list_off;
   a.n_list = n;
   a.n_list_dev = n_dev;
+  a.list_off_dev = off_dev;
   a.row_tok = p->row_tok;
   a.row_w = p->row_w;
   a.hidden = p->H;
@@ -328,10 +350,11 @@ Ev prof_pair(ft_moe_pool* p, hipStream_t s, int stage);
 void prof_push(ft_moe_pool* p, int stage, Ev ev, double bytes, double flops);
 
 // groups / rows: how many expert groups and rows this launch runs (for the
-// algorithmic byte and flop counts of the stage timers).
+// algorithmic byte and flop counts of the stage timers; 0 when the device
+// counts them).  off_dev: glist offset read on the device, or null.
 int run_ffn(ft_moe_pool* p, int layer, const void* x, int list_off, int n, const int32_t* n_dev, hipStream_t s,
-            double groups, double rows) {
-  FfnArgs a = ffn_args(p, layer, list_off, n, n_dev);
+            double groups, double rows, const int32_t* off_dev = nullptr) {
+  FfnArgs a = ffn_args(p, layer, list_off, n, n_dev, off_dev);
   const int f = p->fmt[layer];
   const double H = p->H, I = p->I;
   a.x = static_cast<const uint16_t*>(x);
@@ -526,6 +549,7 @@ int forward_prefill(ft_moe_pool* p, int layer, int T, const void* x, void* out, 
     return FT_E_STATE;
   }
   // the whole layer is streamed into its staging half
+  p->last_pending = false;
   p->last_se.resize(E);
   p->last_ss.resize(E);
   p->last_ce.clear();
@@ -568,12 +592,77 @@ int forward_prefill(ft_moe_pool* p, int layer, int T, const void* x, void* out, 
   return FT_OK;
 }
 
+// Decode with device-driven misses (one wave: T*k <= C), enqueued on s with
+// no host wait: resolve -> miss copy -> FFN of every group -> combine.  The
+// copy overwrites victim slots only, and every earlier reader of those slots
+// precedes the resolve kernel on s.  Everything stays on one stream: waits
+// across queues cost more than the FFN of the hits that could overlap the
+// copy, and an FFN sharing CUs with the copy's PCIe loads is starved.
+int forward_decode_dev(ft_moe_pool* p, int layer, int T, const void* x, void* out, hipStream_t s) {
+  const int E = p->E, k = p->k;
+  const int f = p->fmt[layer];
+  if (p->prof_mask) prof_drain(p, false);
+  ResolveArgs ra = resolve_args(p, layer, T, 0, 0);
+  const int bits = ((p->prof_mask >> FT_STAGE_FFN_GATEUP) & 1) | (((p->prof_mask >> FT_STAGE_FFN_DOWN) & 1) << 1) |
+                   (((p->prof_mask >> FT_STAGE_COPY) & 1) << 2);
+  if (bits) {
+    ra.prof_cnt = p->prof_cnt_dev;
+    ra.prof_stages = bits;
+    ra.fmt = f;
+  }
+  Ev er = prof_pair(p, s, FT_STAGE_RESOLVE);
+  FT_HIP_CHECK(launch_resolve(ra, s, er));
+  prof_push(p, FT_STAGE_RESOLVE, er, 0.0, 0.0);
+
+  MissCopyArgs ca{};
+  ca.host = p->host_store_dev;
+  ca.key_off = p->key_off_dev;
+  ca.dev_header = p->dev_header;
+  ca.glist = p->glist;
+  ca.groups = p->groups;
+  ca.layer = layer;
+  ca.E = E;
+  ca.bytes = p->lay[f].bytes;
+  Ev ec = prof_pair(p, s, FT_STAGE_COPY);
+  FT_HIP_CHECK(launch_miss_copy(ca, p->copy_wgs, s, ec));
+  prof_push(p, FT_STAGE_COPY, ec, 0.0, 0.0);
+
+  // all groups (hit list, then streamed misses; no host-computed ones here)
+  const int pairs = T * k;
+  const int bound = std::min(pairs, E) + p->shared;
+  int rc = run_ffn(p, layer, x, 0, bound, p->dev_header + 9, s, 0.0, 0.0);
+  if (rc) return rc;
+  const int rows = pairs + (p->shared ? T : 0);
+  Ev eb = prof_pair(p, s, FT_STAGE_COMBINE);
+  FT_HIP_CHECK(launch_combine(p->pbuf, p->pair_row, 0, T, k, p->H, p->shared ? pairs : -1,
+                              static_cast<uint16_t*>(out), s, eb));
+  prof_push(p, FT_STAGE_COMBINE, eb, (double(rows) + T) * p->H * 2.0, 0.0);
+  p->last_pending = true;
+  return FT_OK;
+}
+
+// Miss lists of the latest device-driven call, from the resolve kernel's
+// mapped readback (waits for the stream of that call).
+int read_pending_misses(const ft_moe_pool* p) {
+  if (!p->last_pending) return FT_OK;
+  FT_HIP_CHECK(hipStreamSynchronize(p->last_stream));
+  const ResolveHeader h = *reinterpret_cast<const ResolveHeader*>(p->rb_host);
+  const int32_t* se = reinterpret_cast<const int32_t*>(p->rb_host + sizeof(ResolveHeader));
+  const int32_t* ss = se + p->E;
+  p->last_se.assign(se, se + h.n_stream);
+  p->last_ss.assign(ss, ss + h.n_stream);
+  p->last_ce.clear();
+  p->last_pending = false;
+  return FT_OK;
+}
+
 int forward_decode(ft_moe_pool* p, int layer, int T, const void* x, void* out, hipStream_t s) {
   const int E = p->E, k = p->k;
   const ExpertLayout& L = p->lay[p->fmt[layer]];
   p->last_se.clear();
   p->last_ss.clear();
   p->last_ce.clear();
+  p->last_pending = false;
   int t0 = 0;
   while (t0 < T) {
     ResolveArgs ra = resolve_args(p, layer, T, t0, 0);
@@ -808,6 +897,16 @@ int ft_moe_init_pool(const ft_moe_config* cfg, const ft_moe_weights* wts, ft_moe
       return FT_E_OOM_PINNED;
     }
     {
+      void* hd = nullptr;
+      if (hipHostGetDevicePointer(&hd, p->host_store, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        ft_moe_destroy_pool(p.release());
+        set_error("pinned host store is not mapped for the device");
+        return FT_E_HIP;
+      }
+      p->host_store_dev = static_cast<const uint8_t*>(hd);
+    }
+    {
       const int nthr = std::max(1, std::min(16, int(std::thread::hardware_concurrency())));
       parallel_for(int(order.size()), nthr, [&](int b, int e) {
         for (int i = b; i < e; ++i) {
@@ -849,7 +948,8 @@ int ft_moe_init_pool(const ft_moe_config* cfg, const ft_moe_weights* wts, ft_moe
         (rc = dev_alloc(&p->tab.clock, 1)) || (rc = dev_alloc(&p->tab.stats, int64_t(L) * ST_COUNT)) ||
         (rc = dev_alloc(&p->tab.min_gap, L)) || (rc = dev_alloc(&p->groups, E + 2)) ||
         (rc = dev_alloc(&p->glist, E + 2)) || (rc = dev_alloc(&p->dev_header, 16)) ||
-        (rc = dev_alloc(&p->fail_dev, 2 * E + 2))) {
+        (rc = dev_alloc(&p->fail_dev, 2 * E + 2)) || (rc = dev_alloc(&p->key_off_dev, int64_t(L) * E)) ||
+        (rc = dev_alloc(&p->prof_cnt_dev, 24))) {
       ft_moe_destroy_pool(p.release());
       return rc;
     }
@@ -859,6 +959,13 @@ int ft_moe_init_pool(const ft_moe_config* cfg, const ft_moe_weights* wts, ft_moe
     FT_HIP_CHECK(hipMemset(p->tab.slot_last, 0, size_t(C) * 8));
     FT_HIP_CHECK(hipMemset(p->tab.clock, 0, 8));
     FT_HIP_CHECK(hipMemset(p->tab.stats, 0, size_t(L) * ST_COUNT * 8));
+    FT_HIP_CHECK(hipMemset(p->prof_cnt_dev, 0, 24 * 8));
+    FT_HIP_CHECK(hipMemcpy(p->key_off_dev, p->key_off.data(), p->key_off.size() * 8, hipMemcpyHostToDevice));
+    for (int f = 1; f <= 3; ++f)
+      if (p->lay[f].bytes % 16) p->dev_decode = false;
+    if (const char* dp = std::getenv("FT_MOE_DECODE_PATH")) p->dev_decode = p->dev_decode && std::strcmp(dp, "host");
+    if (p->fault_copy >= 0) p->dev_decode = false;  // injected copy failures exist on the host path only
+    if (const char* cw = std::getenv("FT_MOE_COPY_WGS")) p->copy_wgs = std::max(1, std::min(1024, std::atoi(cw)));
     {
       std::vector<int32_t> lru(C);
       for (int64_t i = 0; i < C; ++i) lru[i] = int32_t(i);
@@ -874,7 +981,7 @@ int ft_moe_init_pool(const ft_moe_config* cfg, const ft_moe_weights* wts, ft_moe
     }
     p->copy_stream = p->copy[0];
     for (hipEvent_t* e : {&p->ev_resolved, &p->ev_copied, &p->ev_sync, &p->ev_cpu_copied, &p->ev_done[0],
-                          &p->ev_done[1], &p->ev_staged[0], &p->ev_staged[1]})
+                          &p->ev_done[1], &p->ev_staged[0], &p->ev_staged[1], &p->ev_call_done})
       FT_HIP_CHECK(hipEventCreateWithFlags(e, hipEventDisableTiming));
     FT_HIP_CHECK(hipDeviceSynchronize());
     *out = p.release();
@@ -921,6 +1028,11 @@ int ft_moe_layer_forward(ft_moe_pool* p, int32_t layer, int32_t num_tokens, cons
     if (rc) return rc;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     const int T = num_tokens, E = p->E, k = p->k;
+    if (p->any_call && s != p->last_stream) {
+      // a call on another stream: order it after everything enqueued so far
+      FT_HIP_CHECK(hipEventRecord(p->ev_call_done, p->last_stream));
+      FT_HIP_CHECK(hipStreamWaitEvent(s, p->ev_call_done, 0));
+    }
     Ev e0 = prof_pair(p, s, FT_STAGE_ROUTER);
     FT_HIP_CHECK(launch_router_logits(static_cast<const uint16_t*>(x_bf16), p->router_dev + int64_t(layer) * E * p->H,
                                       router_bias, p->z, T, p->H, E, s, e0));
@@ -931,9 +1043,15 @@ int ft_moe_layer_forward(ft_moe_pool* p, int32_t layer, int32_t num_tokens, cons
       FT_HIP_CHECK(launch_topk(p->z, T, E, k, p->sel, p->w, p->gap, s, e0));
       prof_push(p, FT_STAGE_TOPK, e0, double(T) * E * 8, 0.0);
     }
-    rc = mode == FT_FWD_DECODE ? forward_decode(p, layer, T, x_bf16, out_bf16, s)
-                               : forward_prefill(p, layer, T, x_bf16, out_bf16, s, act);
+    if (mode == FT_FWD_DECODE) {
+      const bool dev = p->dev_decode && p->share == 0.0 && int64_t(T) * k <= p->C;
+      rc = dev ? forward_decode_dev(p, layer, T, x_bf16, out_bf16, s) : forward_decode(p, layer, T, x_bf16, out_bf16, s);
+    } else {
+      rc = forward_prefill(p, layer, T, x_bf16, out_bf16, s, act);
+    }
     if (rc) return rc;
+    p->last_stream = s;
+    p->any_call = true;
     if (trace) {
       const size_t n = size_t(T) * k;
       if (trace->sel) FT_HIP_CHECK(hipMemcpyAsync(trace->sel, p->sel, n * 4, hipMemcpyDeviceToDevice, s));
@@ -992,6 +1110,11 @@ int ft_moe_last_misses(const ft_moe_pool* p, int32_t* stream_expert, int32_t* st
   if (!p) {
     set_error("NULL pool");
     return FT_E_INVALID;
+  }
+  {
+    DeviceGuard dg(p->device);
+    const int rc = read_pending_misses(p);
+    if (rc) return rc;
   }
   if (n_stream) *n_stream = int32_t(p->last_se.size());
   if (n_cpu) *n_cpu = int32_t(p->last_ce.size());
@@ -1059,6 +1182,27 @@ int ft_moe_profile_read(ft_moe_pool* p, ft_moe_profile* out, int32_t reset) {
   }
   DeviceGuard dg(p->device);
   prof_drain(p, true);
+  {
+    // work of device-driven calls, counted by their resolve kernels
+    uint64_t cnt[24];
+    FT_HIP_CHECK(hipDeviceSynchronize());
+    FT_HIP_CHECK(hipMemcpy(cnt, p->prof_cnt_dev, sizeof(cnt), hipMemcpyDeviceToHost));
+    const double H = p->H, I = p->I;
+    for (int f = 1; f <= 3; ++f) {
+      double d[3][2];
+      for (int st = 0; st < 3; ++st)
+        for (int j = 0; j < 2; ++j) {
+          const int i = (st * 4 + f) * 2 + j;
+          d[st][j] = double(cnt[i] - p->prof_cnt_seen[i]);
+          p->prof_cnt_seen[i] = cnt[i];
+        }
+      p->prof.bytes[FT_STAGE_FFN_GATEUP] += d[0][0] * 2 * mat_bytes(f, I, H) + d[0][1] * (H + I) * 2;
+      p->prof.flops[FT_STAGE_FFN_GATEUP] += d[0][1] * 4 * H * I;
+      p->prof.bytes[FT_STAGE_FFN_DOWN] += d[1][0] * mat_bytes(f, H, I) + d[1][1] * (I + H) * 2;
+      p->prof.flops[FT_STAGE_FFN_DOWN] += d[1][1] * 2 * H * I;
+      p->prof.bytes[FT_STAGE_COPY] += d[2][0] * double(p->canon_bytes[f]);
+    }
+  }
   *out = p->prof;
   if (reset) p->prof = ft_moe_profile{};
   return FT_OK;
@@ -1077,6 +1221,7 @@ void ft_moe_destroy_pool(ft_moe_pool* p) {
   hipFree(p->z); hipFree(p->sel); hipFree(p->w); hipFree(p->gap); hipFree(p->pair_flag); hipFree(p->pair_slot);
   hipFree(p->pair_row); hipFree(p->row_tok); hipFree(p->row_w); hipFree(p->groups); hipFree(p->glist);
   hipFree(p->dev_header); hipFree(p->hbuf); hipFree(p->pbuf); hipFree(p->fail_dev);
+  hipFree(p->key_off_dev); hipFree(p->prof_cnt_dev);
   if (p->rb_host) hipHostFree(p->rb_host);
   if (p->x_host) hipHostFree(p->x_host);
   if (p->cpu_out) hipHostFree(p->cpu_out);
@@ -1086,7 +1231,7 @@ void ft_moe_destroy_pool(ft_moe_pool* p) {
     if (p->ev_copy_done[c]) hipEventDestroy(p->ev_copy_done[c]);
   }
   for (hipEvent_t e : {p->ev_resolved, p->ev_copied, p->ev_sync, p->ev_cpu_copied, p->ev_done[0], p->ev_done[1],
-                       p->ev_staged[0], p->ev_staged[1]})
+                       p->ev_staged[0], p->ev_staged[1], p->ev_call_done})
     if (e) hipEventDestroy(e);
   delete p;
 }

@@ -430,6 +430,18 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
     }
     if (t0 == 0) st[ST_CALLS] += 1;
     a.tab.min_gap[a.layer] = fmin(a.tab.min_gap[a.layer], min_gap);
+    if (a.prof_cnt != nullptr) {
+      // groups and rows behind the timed stages of this call (both FFN
+      // launches: hit list and streamed misses; the copy: streamed misses)
+      const uint64_t g_all = uint64_t(n_hit_list + m_str);
+      const uint64_t r_all = uint64_t(hit_pairs + (shared ? ntok : 0) + stream_rows);
+      for (int st2 = 0; st2 < 3; ++st2) {
+        if (!((a.prof_stages >> st2) & 1)) continue;
+        uint64_t* c = a.prof_cnt + (st2 * 4 + a.fmt) * 2;
+        c[0] += st2 == 2 ? uint64_t(m_str) : g_all;
+        c[1] += st2 == 2 ? 0ull : r_all;
+      }
+    }
   }
 
   // ---- 11. host readback (decode): header, miss lists, host-computed rows

@@ -192,3 +192,56 @@ def test_prefill_mx_activation_modes_small(shared, act):
     # each block with fewer bits than fp32), which moves single elements by one
     # grid step
     assert max(rels) <= (2e-3 if act == "mxfp8" else 6e-3)
+
+
+def test_device_driven_and_host_driven_decode_agree():
+    """Decode calls that fit one wave run device-driven (the GPU copies its own
+    misses and the host never waits); FT_MOE_DECODE_PATH=host forces the
+    host-driven path.  Both must give the oracle's decisions and bit-identical
+    outputs, tables and counters.  The device-driven pool is driven
+    asynchronously across three streams with no host wait between calls."""
+    import torch
+
+    from tests.moe_case import GpuLayerStack, compare_call, compare_table
+    import lru_expert_cache_amd as ft
+
+    w = _small(111, 3, 256, 256, 12, 3, [MX, F8, NV], 20, shared=True, alpha=None)  # uniform: evicts
+    os.environ["FT_MOE_DECODE_PATH"] = "host"
+    try:
+        gh = GpuLayerStack(w)
+    finally:
+        del os.environ["FT_MOE_DECODE_PATH"]
+    gd = GpuLayerStack(w)
+    o = OracleLayerStack(w, pool_slots=gh.C)
+    dev = gd.dev
+    streams = [None, torch.cuda.Stream(dev), torch.cuda.Stream(dev)]
+    try:
+        calls = [(6, 0), (1, 1), (5, 2), (2, 3), (6, 4), (3, 5)]
+        pending = []
+        for i, (T, s) in enumerate(calls):
+            for l in range(w.num_layers):
+                x_bits = ms.activations(w, l, s, T)
+                hr = gh.forward(l, x_bits, gh.bias(l, s))
+                compare_call(hr, o.forward(l, x_bits, ms.popularity_bias(w, l, 0)), w.top_k)
+                x = torch.from_numpy(x_bits.view(np.int16)).to(dev)
+                out = torch.empty_like(x)
+                sel = torch.empty(T * w.top_k, dtype=torch.int32, device=dev)
+                slot = torch.empty_like(sel)
+                st = streams[(i * w.num_layers + l) % 3]
+                bias = gd.bias(l, s)
+                ft.ft_moe_layer_forward(gd.pool, l, T, x, bias, out, ft.FT_FWD_DECODE, st,
+                                        {"sel": sel, "slot": slot})
+                pending.append((hr, out, sel, slot, (x, bias)))  # inputs stay alive until the sync
+        torch.cuda.synchronize()
+        for hr, out, sel, slot, _ in pending:
+            assert np.array_equal(out.cpu().numpy().view(np.uint16), hr["out_bits"])
+            assert np.array_equal(sel.cpu().numpy().reshape(hr["sel"].shape), hr["sel"])
+            assert np.array_equal(slot.cpu().numpy(), hr["slot"])
+        assert ft.ft_moe_last_misses(gd.pool) == ft.ft_moe_last_misses(gh.pool)
+        compare_table(gd, o)
+        sh, sd = ft.ft_moe_pool_stats(gh.pool), ft.ft_moe_pool_stats(gd.pool)
+        assert sh == sd, (sh, sd)
+        assert sd["evictions"] > 0 and sd["pair_hits"] > 0
+    finally:
+        gh.close()
+        gd.close()
