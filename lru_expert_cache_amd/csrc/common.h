@@ -143,6 +143,7 @@ struct ResolveArgs {
   uint64_t* prof_cnt;      // [3][4][2]
   int32_t prof_stages;     // bit i: stage i above is timed in this call
   int32_t fmt;             // weight format of the layer
+  int32_t host_wait;       // 1: the host spins on the readback stamp (publish it system-wide)
 };
 
 // ------------------------------------------------------------ launchers
@@ -186,6 +187,8 @@ struct FfnArgs {
   int32_t hidden, inter;
   ExpertLayout lay;
   int32_t act_mode;       // FT_ACT_* >> 4
+  int32_t max_rows;       // bound on the rows of any group (a decode call's token count),
+                          // selects the decode kernels; 0 = unknown
 };
 hipError_t launch_ffn_gateup(const FfnArgs& a, hipStream_t s, Ev ev = {});
 hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t s, Ev ev = {});

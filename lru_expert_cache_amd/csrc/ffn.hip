@@ -21,6 +21,8 @@
 // scale and their fp32 block scale is applied to each 128-K partial sum.
 // Split-K slices of one row tile are summed through LDS in a fixed order.
 #include <algorithm>
+#include <cstring>
+#include <utility>
 
 #include "common.h"
 
@@ -188,6 +190,196 @@ __device__ inline void tile_mma(const TileRegs<FMT>& r, const uint4 xv[4], float
       else
         av = fp4x8_to_bf16_anyscale(w[j], j < 2 ? s0 : s1);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, as_bf16x8(xv[j]), acc, 0, 0, 0);
+    }
+  }
+}
+
+
+// tile_mma with the FP8-b128 row scales of the lane's four accumulator rows
+// already in registers
+template <int FMT>
+__device__ inline void tile_mma_sc(const TileRegs<FMT>& r, const uint4 xv[4], floatx4& acc, float4 sc) {
+  static_assert(FMT == FT_FMT_FP8_B128, "FP8-b128 only");
+  floatx4 t = {0.f, 0.f, 0.f, 0.f};
+  const uint32_t w[8] = {r.c0.x, r.c0.y, r.c0.z, r.c0.w, r.c1.x, r.c1.y, r.c1.z, r.c1.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(w[2 * j], w[2 * j + 1]), as_bf16x8(xv[j]), t, 0, 0, 0);
+  acc[0] += sc.x * t[0];
+  acc[1] += sc.y * t[1];
+  acc[2] += sc.z * t[2];
+  acc[3] += sc.w * t[3];
+}
+
+// ---------------------------------------------------------------------------
+// Decode-sized calls (few rows per expert): a workgroup of four waves owns 64
+// output features (four 16-row weight tiles, one per wave) of one expert and
+// walks the full K in lockstep.  Each wave streams its weight tiles through a
+// ring of D register stages; the 16 x 128 activation tile of each K step is
+// loaded by the whole workgroup (one 16-byte piece per thread, queued with the
+// weights D steps ahead) and handed to the MFMA B operand through a double-
+// buffered LDS tile, XOR-swizzled so that both the writes and the b128 reads
+// are free of bank conflicts.  Loads complete in issue order, so the loads of
+// a step that are not streamed (tokens, routing weights, tensor scales) are
+// made when an item starts, before its first prefetch; a prefetch past the end
+// reads one shared line instead of branching.  Groups with more than 16 rows
+// stream their weights once per 16 rows (decode calls have few such rows).
+// f(integral_constant<0>) ... f(integral_constant<N-1>): ring slots indexed at compile time
+template <typename F, int... I>
+__device__ __attribute__((always_inline)) inline void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __attribute__((always_inline)) inline void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+constexpr int kStreamWaves = 4;     // 16-row weight tiles per workgroup
+constexpr int kStreamMaxChunks = 2; // row chunks of 16 a group may have (max_rows <= 32)
+
+template <int FMT>
+__device__ inline void load_tile_sel(TileRegs<FMT>& r, const uint8_t* __restrict__ W, const MatLayout& m,
+                                     int64_t tile, int lane, bool live, const uint8_t* dummy) {
+  if constexpr (FMT == FT_FMT_FP8_B128) {
+    const uint8_t* p = live ? W + m.codes_off + (tile * 64 + lane) * 32 : dummy;
+    r.c0 = ld_stream16(p);
+    r.c1 = ld_stream16(p + 16);
+  } else {
+    r.c = ld_stream16(live ? W + m.codes_off + (tile * 64 + lane) * 16 : dummy);
+    if constexpr (FMT == FT_FMT_MXFP4)
+      r.s = *(live ? W + m.scales_off + tile * 64 + lane : dummy);
+    else
+      r.s = *reinterpret_cast<const uint16_t*>(live ? W + m.scales_off + (tile * 64 + lane) * 2 : dummy);
+  }
+}
+
+template <int FMT, bool GATEUP, int D>
+__global__ __launch_bounds__(64 * kStreamWaves) void k_ffn_stream(FfnArgs a) {
+  constexpr int NM = GATEUP ? 2 : 1;
+  constexpr bool F8 = FMT == FT_FMT_FP8_B128;
+  __shared__ uint4 xs[2][256];  // activation tile: 16 rows x 128 K bf16, swizzled
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int q = lane >> 4, n = lane & 15;
+  const MatLayout& m0 = a.lay.m[GATEUP ? 0 : 2];
+  const int nkb = m0.cols / kTileK;
+  const int nfb = m0.rows / (kTileRows * kStreamWaves);  // feature blocks of one group
+  const int n_list = a.n_list_dev != nullptr ? *a.n_list_dev : a.n_list;
+  const int list_off = a.list_off_dev != nullptr ? *a.list_off_dev : 0;
+  const int n_items = n_list * nfb;
+  const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.groups);
+  // this thread's piece of the activation tile: row xr, 8 K values at chunk xc
+  const int xr = tid >> 4, xc = tid & 15;
+  const int xslot = xr * 16 + (xc ^ xr);
+  int par = 0;  // LDS buffer parity, kept across items
+
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int gi = item / nfb;
+    const GroupDesc g = a.groups[a.glist[list_off + gi]];
+    if (g.row_count <= 0 || g.wptr == 0) continue;  // uniform over the workgroup
+    const int rb = (item - gi * nfb) * kStreamWaves + w;  // this wave's 16-row weight tile
+    const uint8_t* W = reinterpret_cast<const uint8_t*>(g.wptr);
+    const int nrc = min((g.row_count + 15) >> 4, kStreamMaxChunks);
+    const int nsteps = nrc * nkb;
+
+    // per-item reads, made before the stream starts
+    const uint16_t* xrow[kStreamMaxChunks];
+    float wr[kStreamMaxChunks];
+#pragma unroll
+    for (int c = 0; c < kStreamMaxChunks; ++c) {
+      const int r = c * 16 + xr;
+      const bool ok = c < nrc && r < g.row_count;
+      const int row = g.row_begin + (ok ? r : 0);
+      xrow[c] = GATEUP ? a.x + int64_t(a.row_tok[row]) * a.hidden : a.x + int64_t(row) * a.inter;
+      const int re = c * 16 + n;  // epilogue row of this lane
+      wr[c] = GATEUP ? 0.0f : a.row_w[g.row_begin + (c < nrc && re < g.row_count ? re : 0)];
+    }
+    float tsc[NM];
+#pragma unroll
+    for (int mi = 0; mi < NM; ++mi)
+      tsc[mi] = FMT == FT_FMT_NVFP4 ? reinterpret_cast<const float*>(W + a.lay.tscale_off)[GATEUP ? mi : 2] : 1.0f;
+
+    // the ring: weights and the activation piece of steps s .. s+D-1
+    TileRegs<FMT> wring[D][NM];
+    float4 sring[D][NM];
+    u32x4 xring[D];
+    auto fetch = [&](int slot_s, auto uc) {
+      constexpr int u = decltype(uc)::value;
+      const bool live = slot_s < nsteps;
+      const int c = live ? slot_s / nkb : 0;
+      const int t = live ? slot_s - c * nkb : 0;
+      const int64_t tile = int64_t(rb) * nkb + t;
+#pragma unroll
+      for (int mi = 0; mi < NM; ++mi) {
+        const MatLayout& m = a.lay.m[GATEUP ? mi : 2];
+        load_tile_sel<FMT>(wring[u][mi], W, m, tile, lane, live, dummy);
+        if constexpr (F8)
+          sring[u][mi] = *reinterpret_cast<const float4*>(
+              live ? W + m.scales_off + (tile * 16 + 4 * q) * 4 : dummy);
+      }
+      const uint16_t* xp = c == 0 ? xrow[0] : xrow[kStreamMaxChunks - 1];
+      xring[u] = *reinterpret_cast<const u32x4*>(live ? xp + t * kTileK + xc * 8 : a.x);
+    };
+    static_for<D>([&](auto uc) { fetch(decltype(uc)::value, uc); });
+
+    floatx4 acc[NM];
+#pragma unroll
+    for (int mi = 0; mi < NM; ++mi) acc[mi] = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < nsteps; s0 += D) {
+      static_for<D>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        const int s = s0 + u;
+        // activation tile of step s -> LDS, then the operands of this wave
+        xs[par][xslot] = make_uint4(xring[u][0], xring[u][1], xring[u][2], xring[u][3]);
+        __syncthreads();
+        uint4 bx[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bx[j] = xs[par][n * 16 + ((4 * q + j) ^ n)];
+        par ^= 1;
+        TileRegs<FMT> wt[NM];
+        float4 st[NM];
+#pragma unroll
+        for (int mi = 0; mi < NM; ++mi) {
+          wt[mi] = wring[u][mi];
+          st[mi] = sring[u][mi];
+        }
+        fetch(s + D, uc);  // refill the slot just consumed
+#pragma unroll
+        for (int mi = 0; mi < NM; ++mi) {
+          if constexpr (F8)
+            tile_mma_sc<FMT>(wt[mi], bx, acc[mi], st[mi]);
+          else
+            tile_mma<FMT>(wt[mi], bx, acc[mi], nullptr);
+        }
+        const int t = s % nkb;
+        if (t == nkb - 1) {  // end of a row chunk: epilogue, lane holds features rb*16+4q+i of row c*16+n
+          const int c = s / nkb;
+          const int r = c * 16 + n;
+          if (r < g.row_count) {
+            const int row = g.row_begin + r;
+            const int o0 = rb * 16 + 4 * q;
+            uint16_t hv[4];
+            if constexpr (GATEUP) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float gv = acc[0][i] * tsc[0];
+                const float uv = acc[1][i] * tsc[1];
+                hv[i] = f32_to_bf16_rne(gv / (1.0f + expf(-gv)) * uv);
+              }
+              *reinterpret_cast<uint2*>(a.out + int64_t(row) * a.inter + o0) =
+                  make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16), uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
+            } else {
+              const float wrow = c == 0 ? wr[0] : wr[kStreamMaxChunks - 1];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) hv[i] = f32_to_bf16_rne(wrow * (acc[0][i] * tsc[0]));
+              *reinterpret_cast<uint2*>(a.out + int64_t(row) * a.hidden + o0) =
+                  make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16), uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
+            }
+          }
+#pragma unroll
+          for (int mi = 0; mi < NM; ++mi) acc[mi] = {0.f, 0.f, 0.f, 0.f};
+        }
+      });
     }
   }
 }
@@ -364,9 +556,278 @@ hipError_t launch_fmt(const FfnArgs& a, const Split& s, dim3 grid, dim3 block, h
   return hipErrorInvalidValue;
 }
 
+// resident workgroups per CU of a kernel (for persistent grids), computed once
+template <typename Kern>
+int64_t resident_grid(Kern k, int block) {
+  int dev = 0, cus = 0, per_cu = 0;
+  (void)hipGetDevice(&dev);
+  (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, block, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+  return int64_t(per_cu) * std::max(cus, 1);
+}
+
+template <int FMT, bool GATEUP, int D>
+hipError_t launch_stream_d(const FfnArgs& a, hipStream_t st, Ev ev) {
+  static const int64_t cap = resident_grid(k_ffn_stream<FMT, GATEUP, D>, 64 * kStreamWaves);
+  const MatLayout& m = a.lay.m[GATEUP ? 0 : 2];
+  const int64_t items = int64_t(a.n_list) * (m.rows / (kTileRows * kStreamWaves));
+  ft_launch(k_ffn_stream<FMT, GATEUP, D>, dim3(unsigned(std::min(items, cap))), dim3(64 * kStreamWaves), st, ev, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Split-K decode kernel with an item ring: a persistent workgroup of SK waves
+// owns one 16-row weight tile per item (item = expert group x row tile) and
+// splits its K over the waves (each wave KPW tiles of 128), like k_ffn; the
+// registers of one item's slice (weights plus the lane's 64 bytes of
+// activations per K tile) form a ring whose slot t is refilled with the next
+// item's tile t as soon as tile t has been multiplied, so the next item
+// streams in while the current one finishes, its partial sums meet in LDS and
+// its epilogue runs.  Per-item reads the ring depends on (the tokens of the
+// rows, routing weights) are made one item earlier, so that waiting for them
+// never waits for the ring.  Invalid activation rows read one shared line and
+// only feed output columns that are not written.  Every group has at most 16
+// rows (calls of up to 16 tokens).
+template <int FMT, bool GATEUP, int KPW>
+__global__ __launch_bounds__(64 * kMaxWaves) void k_ffn_ring(FfnArgs a, int SK) {
+  constexpr int NM = GATEUP ? 2 : 1;
+  constexpr bool F8 = FMT == FT_FMT_FP8_B128;
+  __shared__ floatx4 red[kMaxWaves][NM][64];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int q = lane >> 4, n = lane & 15;
+  const int sk = w;  // one row tile per workgroup: wave = K slice
+  const MatLayout& m0 = a.lay.m[GATEUP ? 0 : 2];
+  const int nkb = m0.cols / kTileK;
+  const int kb0 = sk * KPW;
+  const int nrb = m0.rows / kTileRows;
+  const int n_list = a.n_list_dev != nullptr ? *a.n_list_dev : a.n_list;
+  const int list_off = a.list_off_dev != nullptr ? *a.list_off_dev : 0;
+  const int n_items = n_list * nrb;
+  if (int(blockIdx.x) >= n_items) return;
+  const int G = int(gridDim.x);
+  const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.groups);
+
+  struct Item {
+    uint64_t wptr;
+    int row_begin, row_count, rb;
+  };
+  auto desc = [&](int item) -> Item {
+    const bool ok = item < n_items;
+    const int it = ok ? item : n_items - 1;
+    const int gi = it / nrb;
+    const GroupDesc g = a.groups[a.glist[list_off + gi]];
+    Item r;
+    r.wptr = g.wptr;
+    r.row_begin = g.row_begin;
+    r.row_count = ok && g.wptr != 0 ? g.row_count : 0;
+    r.rb = it - gi * nrb;
+    return r;
+  };
+  // activation row (GATEUP: by token) of this lane for rows 0..15 of an item;
+  // null for a row the group does not have
+  auto row_src = [&](const Item& d, int rc) -> const uint16_t* {
+    const int r = rc * 16 + n;
+    if (r >= d.row_count) return nullptr;
+    const int row = d.row_begin + r;
+    return GATEUP ? a.x + int64_t(a.row_tok[row]) * a.hidden : a.x + int64_t(row) * a.inter;
+  };
+
+  TileRegs<FMT> wring[KPW][NM];
+  float4 sring[KPW][NM];
+  u32x4 xring[KPW][4];
+  auto fetch = [&](const Item& d, const uint16_t* xsrc, auto tc) {
+    constexpr int t = decltype(tc)::value;
+    const bool live = d.row_count > 0;
+    const uint8_t* W = reinterpret_cast<const uint8_t*>(d.wptr);
+    const int64_t tile = int64_t(d.rb) * nkb + kb0 + t;
+#pragma unroll
+    for (int mi = 0; mi < NM; ++mi) {
+      const MatLayout& m = a.lay.m[GATEUP ? mi : 2];
+      load_tile_sel<FMT>(wring[t][mi], W, m, tile, lane, live, dummy);
+      if constexpr (F8)
+        sring[t][mi] = *reinterpret_cast<const float4*>(live ? W + m.scales_off + (tile * 16 + 4 * q) * 4 : dummy);
+    }
+    // a missing row reads one shared line (its output column is not written)
+    const u32x4* xp = reinterpret_cast<const u32x4*>(xsrc ? xsrc + (kb0 + t) * kTileK + 32 * q : a.x);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xring[t][j] = xp[xsrc ? j : 0];
+  };
+  auto mma = [&](auto tc, floatx4 (&acc)[NM]) {
+    constexpr int t = decltype(tc)::value;
+    uint4 xv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xv[j] = make_uint4(xring[t][j][0], xring[t][j][1], xring[t][j][2], xring[t][j][3]);
+#pragma unroll
+    for (int mi = 0; mi < NM; ++mi) {
+      if constexpr (F8)
+        tile_mma_sc<FMT>(wring[t][mi], xv, acc[mi], sring[t][mi]);
+      else
+        tile_mma<FMT>(wring[t][mi], xv, acc[mi], nullptr);
+    }
+  };
+  // partial sums of the SK waves meet in LDS; wave 0 writes rows rc*16 + n
+  auto finish = [&](const Item& d, int rc, floatx4 (&acc)[NM], const float (&tsc)[NM], float wr) {
+    if (SK > 1) {
+#pragma unroll
+      for (int mi = 0; mi < NM; ++mi) red[w][mi][lane] = acc[mi];
+      __syncthreads();
+      if (sk == 0) {
+#pragma unroll
+        for (int mi = 0; mi < NM; ++mi) {
+          floatx4 s = red[0][mi][lane];
+          for (int k2 = 1; k2 < SK; ++k2) {
+            const floatx4 v = red[k2][mi][lane];
+            s[0] += v[0]; s[1] += v[1]; s[2] += v[2]; s[3] += v[3];
+          }
+          acc[mi] = s;
+        }
+      }
+    }
+    const int r = rc * 16 + n;
+    if (sk == 0 && r < d.row_count) {
+      const int row = d.row_begin + r;
+      const int o0 = d.rb * 16 + 4 * q;
+      uint16_t hv[4];
+      if constexpr (GATEUP) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float gv = acc[0][i] * tsc[0];
+          const float uv = acc[1][i] * tsc[1];
+          hv[i] = f32_to_bf16_rne(gv / (1.0f + expf(-gv)) * uv);
+        }
+        *reinterpret_cast<uint2*>(a.out + int64_t(row) * a.inter + o0) =
+            make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16), uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hv[i] = f32_to_bf16_rne(wr * (acc[0][i] * tsc[0]));
+        *reinterpret_cast<uint2*>(a.out + int64_t(row) * a.hidden + o0) =
+            make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16), uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
+      }
+    }
+    if (SK > 1) __syncthreads();
+  };
+  auto row_weight = [&](const Item& d, int rc) -> float {
+    const int r = rc * 16 + n;
+    return GATEUP ? 0.0f : a.row_w[d.row_begin + (r < d.row_count ? r : 0)];
+  };
+
+  // prologue: the first item in the ring, the row data of the second
+  int item = blockIdx.x;
+  Item cur = desc(item);
+  const uint16_t* xs_cur = row_src(cur, 0);
+  float wr_cur = row_weight(cur, 0);
+  static_for<KPW>([&](auto tc) { fetch(cur, xs_cur, tc); });
+  Item nxt = desc(item + G);
+  const uint16_t* xs_nxt = row_src(nxt, 0);
+  float wr_nxt = row_weight(nxt, 0);
+
+  for (;;) {
+    // row data of the item after next, ahead of this item's refills
+    const Item nn = desc(item + 2 * G);
+    const uint16_t* xs_nn = row_src(nn, 0);
+    const float wr_nn = row_weight(nn, 0);
+    float tsc[NM];
+#pragma unroll
+    for (int mi = 0; mi < NM; ++mi)
+      tsc[mi] = FMT == FT_FMT_NVFP4 && cur.row_count > 0
+                    ? reinterpret_cast<const float*>(cur.wptr + a.lay.tscale_off)[GATEUP ? mi : 2]
+                    : 1.0f;
+    floatx4 acc[NM];
+#pragma unroll
+    for (int mi = 0; mi < NM; ++mi) acc[mi] = {0.f, 0.f, 0.f, 0.f};
+    static_for<KPW>([&](auto tc) {
+      mma(tc, acc);
+      fetch(nxt, xs_nxt, tc);  // the slot just used takes the next item's tile
+    });
+    if (cur.row_count > 0) {
+      finish(cur, 0, acc, tsc, wr_cur);
+    }
+    item += G;
+    if (item >= n_items) break;
+    cur = nxt;
+    xs_cur = xs_nxt;
+    wr_cur = wr_nxt;
+    nxt = nn;
+    xs_nxt = xs_nn;
+    wr_nxt = wr_nn;
+  }
+}
+
+#ifndef FT_STREAM_MAXD
+#define FT_STREAM_MAXD 4
+#endif
+// Ring depth: the deepest (up to 4: deeper rings cost occupancy and measured
+// slower) that divides the K steps and keeps the weight ring within 80
+// registers.
+template <int FMT, bool GATEUP>
+hipError_t launch_stream(const FfnArgs& a, hipStream_t st, Ev ev) {
+  const int nkb = a.lay.m[GATEUP ? 0 : 2].cols / kTileK;
+  constexpr int regs = (GATEUP ? 2 : 1) * (FMT == FT_FMT_FP8_B128 ? 12 : 5);  // per ring slot
+  constexpr int dmax = std::min(FT_STREAM_MAXD, 80 / regs);
+  if (dmax >= 8 && nkb % 8 == 0) return launch_stream_d<FMT, GATEUP, (dmax >= 8 ? 8 : 1)>(a, st, ev);
+  if (dmax >= 6 && nkb % 6 == 0) return launch_stream_d<FMT, GATEUP, (dmax >= 6 ? 6 : 1)>(a, st, ev);
+  if (dmax >= 4 && nkb % 4 == 0) return launch_stream_d<FMT, GATEUP, (dmax >= 4 ? 4 : 1)>(a, st, ev);
+  if (dmax >= 3 && nkb % 3 == 0) return launch_stream_d<FMT, GATEUP, (dmax >= 3 ? 3 : 1)>(a, st, ev);
+  if (dmax >= 2 && nkb % 2 == 0) return launch_stream_d<FMT, GATEUP, 2>(a, st, ev);
+  return launch_stream_d<FMT, GATEUP, 1>(a, st, ev);
+}
+
+// Ring kernel split: the most K tiles per wave (at most 4) that divide K with
+// at most kMaxWaves waves and keep one item's slice within 112 registers.
+template <int FMT, bool GATEUP>
+int ring_kpw(int nkb) {
+  constexpr int slot = (GATEUP ? 2 : 1) * (FMT == FT_FMT_FP8_B128 ? 12 : 5) + 16;
+  for (int kpw = 4; kpw >= 1; --kpw)
+    if (nkb % kpw == 0 && nkb / kpw <= kMaxWaves && kpw * slot <= 112) return kpw;
+  return 0;
+}
+
+template <int FMT, bool GATEUP, int KPW>
+hipError_t launch_ring_k(const FfnArgs& a, int SK, hipStream_t st, Ev ev) {
+  static int64_t cap[kMaxWaves + 1] = {};
+  if (!cap[SK]) cap[SK] = resident_grid(k_ffn_ring<FMT, GATEUP, KPW>, 64 * SK);
+  const int64_t items = int64_t(a.n_list) * (a.lay.m[GATEUP ? 0 : 2].rows / kTileRows);
+  ft_launch(k_ffn_ring<FMT, GATEUP, KPW>, dim3(unsigned(std::min(items, cap[SK]))), dim3(64 * SK), st, ev, a, SK);
+  return hipGetLastError();
+}
+
+template <int FMT, bool GATEUP>
+hipError_t launch_small(const FfnArgs& a, hipStream_t st, Ev ev) {
+  const int nkb = a.lay.m[GATEUP ? 0 : 2].cols / kTileK;
+  // gate/up: the item ring; down (short K, tiny items): the K-streaming kernel
+  int kpw = GATEUP && a.max_rows > 0 && a.max_rows <= kTileRows ? ring_kpw<FMT, GATEUP>(nkb) : 0;
+#ifdef FT_FFN_KERNEL_ENV
+  if (const char* e = getenv("FFN_KERNEL"))
+    if (!strcmp(e, "stream")) kpw = 0;
+#endif
+  switch (kpw) {
+    case 4: return launch_ring_k<FMT, GATEUP, 4>(a, nkb / 4, st, ev);
+    case 3: return launch_ring_k<FMT, GATEUP, 3>(a, nkb / 3, st, ev);
+    case 2: return launch_ring_k<FMT, GATEUP, 2>(a, nkb / 2, st, ev);
+    case 1: return launch_ring_k<FMT, GATEUP, 1>(a, nkb, st, ev);
+    default: break;
+  }
+  if (a.lay.m[GATEUP ? 0 : 2].rows % (kTileRows * kStreamWaves)) return hipErrorInvalidValue;
+  return launch_stream<FMT, GATEUP>(a, st, ev);
+}
+
 template <bool GATEUP>
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t st, Ev ev) {
   if (a.n_list <= 0) return hipSuccess;
+  bool small = a.max_rows > 0 && a.max_rows <= 2 * kTileRows;
+#ifdef FT_FFN_KERNEL_ENV
+  if (const char* e = getenv("FFN_KERNEL"))
+    if (!strcmp(e, "grid")) small = false;
+#endif
+  if (small) {
+    switch (a.lay.fmt) {
+      case FT_FMT_MXFP4: return launch_small<FT_FMT_MXFP4, GATEUP>(a, st, ev);
+      case FT_FMT_NVFP4: return launch_small<FT_FMT_NVFP4, GATEUP>(a, st, ev);
+      case FT_FMT_FP8_B128: return launch_small<FT_FMT_FP8_B128, GATEUP>(a, st, ev);
+      default: return hipErrorInvalidValue;
+    }
+  }
   const MatLayout& m = a.lay.m[GATEUP ? 0 : 2];
   const int fmt = a.lay.fmt;
   const Split s = choose_split(m.cols, m.rows, kpw_max(fmt, GATEUP));

@@ -65,6 +65,9 @@ struct ft_moe_pool {
   // FT_MOE_DECODE_PATH=host / injected copy failures.
   bool dev_decode = true;
   int copy_wgs = 64;                // workgroups of the miss-copy kernel
+  // decode calls of up to 32 tokens use the K-streaming FFN kernel unless
+  // FT_MOE_FFN=grid (the split-K kernel every other call uses)
+  bool ffn_stream = true;
 
   // device memory
   uint8_t* arena = nullptr;
@@ -353,8 +356,9 @@ void prof_push(ft_moe_pool* p, int stage, Ev ev, double bytes, double flops);
 // algorithmic byte and flop counts of the stage timers; 0 when the device
 // counts them).  off_dev: glist offset read on the device, or null.
 int run_ffn(ft_moe_pool* p, int layer, const void* x, int list_off, int n, const int32_t* n_dev, hipStream_t s,
-            double groups, double rows, const int32_t* off_dev = nullptr) {
+            double groups, double rows, const int32_t* off_dev = nullptr, int max_group_rows = 1 << 30) {
   FfnArgs a = ffn_args(p, layer, list_off, n, n_dev, off_dev);
+  a.max_rows = p->ffn_stream && max_group_rows <= 32 ? max_group_rows : 0;
   const int f = p->fmt[layer];
   const double H = p->H, I = p->I;
   a.x = static_cast<const uint16_t*>(x);
@@ -402,6 +406,7 @@ ResolveArgs resolve_args(ft_moe_pool* p, int layer, int T, int t0, int mode) {
   a.dev_header = p->dev_header;
   a.host_rb = mode == 0 ? p->rb_dev : nullptr;
   a.host_rb_cap = p->rb_cap;
+  a.host_wait = mode == 0 ? 1 : 0;
   a.tiles = mode == 1 ? p->tiles : nullptr;
   a.tile_rows = mx_gemm_rows_per_tile();
   return a;
@@ -603,6 +608,7 @@ int forward_decode_dev(ft_moe_pool* p, int layer, int T, const void* x, void* ou
   const int f = p->fmt[layer];
   if (p->prof_mask) prof_drain(p, false);
   ResolveArgs ra = resolve_args(p, layer, T, 0, 0);
+  ra.host_wait = 0;  // nobody spins: the readback is read after a stream sync
   const int bits = ((p->prof_mask >> FT_STAGE_FFN_GATEUP) & 1) | (((p->prof_mask >> FT_STAGE_FFN_DOWN) & 1) << 1) |
                    (((p->prof_mask >> FT_STAGE_COPY) & 1) << 2);
   if (bits) {
@@ -630,7 +636,8 @@ int forward_decode_dev(ft_moe_pool* p, int layer, int T, const void* x, void* ou
   // all groups (hit list, then streamed misses; no host-computed ones here)
   const int pairs = T * k;
   const int bound = std::min(pairs, E) + p->shared;
-  int rc = run_ffn(p, layer, x, 0, bound, p->dev_header + 9, s, 0.0, 0.0);
+  // a group has at most one row per token
+  int rc = run_ffn(p, layer, x, 0, bound, p->dev_header + 9, s, 0.0, 0.0, nullptr, T);
   if (rc) return rc;
   const int rows = pairs + (p->shared ? T : 0);
   Ev eb = prof_pair(p, s, FT_STAGE_COMBINE);
@@ -766,10 +773,10 @@ int forward_decode(ft_moe_pool* p, int layer, int T, const void* x, void* out, h
       });
     }
 
-    int rc = run_ffn(p, layer, x, 0, h.n_hit_list, nullptr, s, h.n_hit_list, h.rows_hit_list);
+    int rc = run_ffn(p, layer, x, 0, h.n_hit_list, nullptr, s, h.n_hit_list, h.rows_hit_list, nullptr, T);
     if (rc == FT_OK && h.n_stream > 0) {
       FT_HIP_CHECK(hipStreamWaitEvent(s, p->ev_copied, 0));
-      rc = run_ffn(p, layer, x, h.n_hit_list, h.n_stream, nullptr, s, h.n_stream, h.rows_stream);
+      rc = run_ffn(p, layer, x, h.n_hit_list, h.n_stream, nullptr, s, h.n_stream, h.rows_stream, nullptr, T);
     }
     if (cpu_thread.joinable()) cpu_thread.join();
     if (rc) return rc;
@@ -965,6 +972,7 @@ int ft_moe_init_pool(const ft_moe_config* cfg, const ft_moe_weights* wts, ft_moe
       if (p->lay[f].bytes % 16) p->dev_decode = false;
     if (const char* dp = std::getenv("FT_MOE_DECODE_PATH")) p->dev_decode = p->dev_decode && std::strcmp(dp, "host");
     if (p->fault_copy >= 0) p->dev_decode = false;  // injected copy failures exist on the host path only
+    if (const char* fk = std::getenv("FT_MOE_FFN")) p->ffn_stream = std::strcmp(fk, "grid") != 0;
     if (const char* cw = std::getenv("FT_MOE_COPY_WGS")) p->copy_wgs = std::max(1, std::min(1024, std::atoi(cw)));
     {
       std::vector<int32_t> lru(C);

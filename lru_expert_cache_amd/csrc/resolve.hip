@@ -29,6 +29,8 @@ namespace {
 
 constexpr int NT = kResolveThreads;
 constexpr int NW = NT / 64;
+constexpr int kLdsPairs = 2048;  // pairs of a wave kept in LDS (decode calls with T*k up to this)
+constexpr int kPf = 4;           // recency-order entries per thread read at kernel start (C <= 4096)
 
 struct ResolveSmem {
   int first[kMaxExperts];
@@ -47,6 +49,14 @@ struct ResolveSmem {
   uint32_t prot[kMaxSlots / 32];  // slots hit by this wave (not evictable)
   int ired[4 * NW];
   double dred[NW];
+  int k2s[kMaxExperts];           // key -> slot of this layer's experts, read at start
+  // the wave's pairs mirrored in LDS when P <= kLdsPairs (decode calls)
+  int32_t psel[kLdsPairs];
+  float pw[kLdsPairs];
+  int32_t prow[kLdsPairs];
+  double pgap[kLdsPairs];
+  uint32_t lastbits[kLdsPairs / 32];  // positions of the touched experts' last pairs
+  int lastpre[kLdsPairs / 32];
 };
 
 // Exclusive prefix sum of v over the workgroup; *total gets the sum.
@@ -117,14 +127,56 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
   const bool decode = a.mode == 0;
   const int key0 = a.layer * E;
 
-  // ---- 0. top-k of every token of the call (first wave of a decode call)
-  if (a.do_topk) {
-    for (int t = wid; t < a.T; t += NW)
-      wave_topk(a.z + int64_t(t) * E, E, k, a.sel + int64_t(t) * k, a.w + int64_t(t) * k, a.gap + t);
-    __threadfence_block();
-    __syncthreads();
+  // ---- prologue: every global read that does not depend on this call's
+  // routing is issued first, so that its latency overlaps the top-k: the
+  // recency order and the keys held by its first slots, this layer's
+  // key -> slot entries, the clock and the counters.
+  int cur = 0;
+  uint64_t clk = 0;
+  int k2s = -1;
+  if (decode) {
+    cur = *a.tab.lru_cur;
+    clk = *a.tab.clock;
+    if (tid < E) k2s = a.tab.key2slot[key0 + tid];
+  }
+  uint64_t* st = a.tab.stats + int64_t(a.layer) * ST_COUNT;
+  uint64_t st0[ST_COUNT];
+  double gap0 = 0.0;
+  uint64_t pc0[3][2] = {{0, 0}, {0, 0}, {0, 0}};
+  if (tid == 0) {
+#pragma unroll
+    for (int i = 0; i < ST_COUNT; ++i) st0[i] = st[i];
+    gap0 = a.tab.min_gap[a.layer];
+    if (a.prof_cnt != nullptr)
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        pc0[i][0] = a.prof_cnt[(i * 4 + a.fmt) * 2];
+        pc0[i][1] = a.prof_cnt[(i * 4 + a.fmt) * 2 + 1];
+      }
+  }
+  const int32_t* lru_in = a.tab.lru[cur];
+  int pf_s[kPf], pf_key[kPf];
+#pragma unroll
+  for (int j = 0; j < kPf; ++j) {
+    const int i = j * NT + tid;
+    pf_s[j] = (decode && i < C) ? lru_in[i] : 0;
   }
 
+  // ---- 0. top-k of every token of the call (first wave of a decode call)
+  const bool mirror = a.do_topk && int64_t(a.T) * k <= kLdsPairs;
+  if (a.do_topk) {
+    for (int t = wid; t < a.T; t += NW)
+      wave_topk(a.z + int64_t(t) * E, E, k, a.sel + int64_t(t) * k, a.w + int64_t(t) * k, a.gap + t,
+                mirror ? sm.psel + t * k : nullptr, mirror ? sm.pw + t * k : nullptr, mirror ? sm.pgap + t : nullptr);
+    __threadfence_block();
+  }
+  // keys of the prefetched recency entries (the old key of a victim slot)
+#pragma unroll
+  for (int j = 0; j < kPf; ++j) {
+    const int i = j * NT + tid;
+    pf_key[j] = (decode && i < C) ? a.tab.slot_key[pf_s[j]] : -1;
+  }
+  if (decode && tid < E) sm.k2s[tid] = k2s;
   for (int e = tid; e < E; e += NT) {
     sm.first[e] = 0x7fffffff;
     sm.last[e] = -1;
@@ -138,7 +190,7 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
   if (decode && C < E && wid == 0) {
     int count = 0, t1 = a.T;
     for (int t = t0; t < a.T; ++t) {
-      const int e = lane < k ? a.sel[int64_t(t) * k + lane] : 0;
+      const int e = lane < k ? (mirror ? sm.psel[t * k + lane] : a.sel[int64_t(t) * k + lane]) : 0;
       const bool isnew = lane < k && sm.dix[e] == 0;
       const int n = __popcll(__ballot(isnew));
       if (count + n > C) {
@@ -154,12 +206,25 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
   __syncthreads();
   const int t1 = sm.scal[0];
   const int P = (t1 - t0) * k;
+  const int ntok = t1 - t0;
   const int64_t pb = int64_t(t0) * k;
   for (int e = tid; e < E; e += NT) sm.dix[e] = -1;
 
+  // pairs of this wave in LDS: already there from the top-k, else one copy
+  const bool lp = P <= kLdsPairs;
+  if (lp && !mirror) {
+    for (int i = tid; i < P; i += NT) {
+      sm.psel[i] = a.sel[pb + i];
+      sm.pw[i] = a.w[pb + i];
+    }
+    for (int tt = tid; tt < ntok; tt += NT) sm.pgap[tt] = a.gap[t0 + tt];
+    __syncthreads();
+  }
+  auto SEL = [&](int i) -> int { return lp ? sm.psel[i] : a.sel[pb + i]; };
+
   // ---- 2. first and last pair of each expert in the wave
   for (int i = tid; i < P; i += NT) {
-    const int e = a.sel[pb + i];
+    const int e = SEL(i);
     atomicMin(&sm.first[e], i);
     atomicMax(&sm.last[e], i);
   }
@@ -172,7 +237,7 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
     int e = 0;
     bool f = false;
     if (i < P) {
-      e = a.sel[pb + i];
+      e = SEL(i);
       f = sm.first[e] == i;
     }
     int tot;
@@ -194,7 +259,7 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
   if (tid < nD) {
     const int e = sm.D[tid];
     if (decode) {
-      const int s = a.tab.key2slot[key0 + e];
+      const int s = sm.k2s[e];
       hit = s >= 0;
       if (hit) {
         sm.dslot[tid] = s;
@@ -224,25 +289,17 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
   // order, and the touched slots (hits and streamed misses) follow in order of
   // their expert's last pair.  The new order goes to the other buffer.
   if (decode) {
-    const int cur = *a.tab.lru_cur;
-    const int32_t* lru_in = a.tab.lru[cur];
     int32_t* lru_out = a.tab.lru[cur ^ 1];
     int neli = 0;
-    for (int c0 = 0; c0 < C; c0 += NT) {
-      const int i = c0 + tid;
-      int s = 0;
-      bool elig = false;
-      if (i < C) {
-        s = lru_in[i];
-        elig = !((sm.prot[s >> 5] >> (s & 31)) & 1u);
-      }
+    auto take = [&](bool valid, int s, int oldk, bool have_old) {
+      const bool elig = valid && !((sm.prot[s >> 5] >> (s & 31)) & 1u);
       int tot;
       const int vp = neli + block_exscan(elig ? 1 : 0, sm.wsum, &tot);
       if (elig) {
         if (vp < m_str) {
           const int d = sm.sm[vp];
           const int e = sm.D[d];
-          const int old = a.tab.slot_key[s];
+          const int old = have_old ? oldk : a.tab.slot_key[s];
           if (old >= 0) {
             a.tab.key2slot[old] = -1;
             atomicAdd(&sm.scal[1], 1);
@@ -255,29 +312,64 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
         }
       }
       neli += tot;
+    };
+#pragma unroll
+    for (int j = 0; j < kPf; ++j)
+      if (j * NT < C) take(j * NT + tid < C, pf_s[j], pf_key[j], true);
+    for (int c0 = kPf * NT; c0 < C; c0 += NT) {
+      const int i = c0 + tid;
+      take(i < C, i < C ? lru_in[i] : 0, 0, false);
     }
     __syncthreads();
     const int nkeep = neli - m_str;
-    const uint64_t clk = *a.tab.clock;
-    for (int d = tid; d < nD; d += NT) {
-      if (sm.cls[d] == FT_PAIR_MISS_CPU) continue;
-      const int mylast = sm.last[sm.D[d]];
-      int rank = 0;
-      for (int d2 = 0; d2 < nD; ++d2)
-        if (sm.cls[d2] != FT_PAIR_MISS_CPU && sm.last[sm.D[d2]] < mylast) ++rank;
-      lru_out[nkeep + rank] = sm.dslot[d];
-      a.tab.slot_last[sm.dslot[d]] = clk + uint64_t(mylast);
+    // rank of a touched slot = touched experts whose last pair comes earlier
+    if (lp) {
+      const int nwords = (P + 31) / 32;  // <= 64
+      if (tid < nwords) sm.lastbits[tid] = 0u;
+      __syncthreads();
+      if (tid < nD && sm.cls[tid] != FT_PAIR_MISS_CPU) {
+        const int ml = sm.last[sm.D[tid]];
+        atomicOr(&sm.lastbits[ml >> 5], 1u << (ml & 31));
+      }
+      __syncthreads();
+      if (wid == 0) {
+        const int pc = lane < nwords ? __popc(sm.lastbits[lane]) : 0;
+        int x = pc;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int y = __shfl_up(x, off, 64);
+          if (lane >= off) x += y;
+        }
+        if (lane < nwords) sm.lastpre[lane] = x - pc;
+      }
+      __syncthreads();
+      if (tid < nD && sm.cls[tid] != FT_PAIR_MISS_CPU) {
+        const int ml = sm.last[sm.D[tid]];
+        const int rank = sm.lastpre[ml >> 5] + __popc(sm.lastbits[ml >> 5] & ((1u << (ml & 31)) - 1u));
+        lru_out[nkeep + rank] = sm.dslot[tid];
+        a.tab.slot_last[sm.dslot[tid]] = clk + uint64_t(ml);
+      }
+    } else {
+      for (int d = tid; d < nD; d += NT) {
+        if (sm.cls[d] == FT_PAIR_MISS_CPU) continue;
+        const int mylast = sm.last[sm.D[d]];
+        int rank = 0;
+        for (int d2 = 0; d2 < nD; ++d2)
+          if (sm.cls[d2] != FT_PAIR_MISS_CPU && sm.last[sm.D[d2]] < mylast) ++rank;
+        lru_out[nkeep + rank] = sm.dslot[d];
+        a.tab.slot_last[sm.dslot[d]] = clk + uint64_t(mylast);
+      }
     }
-    __syncthreads();
     if (tid == 0) {
       *a.tab.clock = clk + uint64_t(P);
       *a.tab.lru_cur = cur ^ 1;
     }
+    __syncthreads();
   }
 
   // ---- 7. per-pair decisions
   for (int i = tid; i < P; i += NT) {
-    const int d = sm.dix[a.sel[pb + i]];
+    const int d = sm.dix[SEL(i)];
     const int c = sm.cls[d];
     a.pair_flag[pb + i] = uint8_t(c);
     a.pair_slot[pb + i] = c == FT_PAIR_MISS_CPU ? -1 : sm.dslot[d];
@@ -291,7 +383,7 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
     __syncthreads();
     const int i = c0 + tid;
     const bool valid = i < P;
-    const int d = valid ? sm.dix[a.sel[pb + i]] : 0;
+    const int d = valid ? sm.dix[SEL(i)] : 0;
     uint64_t same = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
       const bool bit = (d >> b) & 1;
@@ -312,7 +404,12 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
       sm.cnt[g] = run;
     }
     __syncthreads();
-    if (valid) a.pair_row[pb + i] = sm.wcnt[wid][d] + lrank;
+    if (valid) {
+      if (lp)
+        sm.prow[i] = sm.wcnt[wid][d] + lrank;
+      else
+        a.pair_row[pb + i] = sm.wcnt[wid][d] + lrank;
+    }
     __syncthreads();
   }
 
@@ -324,13 +421,12 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
   }
   __syncthreads();
   for (int i = tid; i < P; i += NT) {
-    const int d = sm.dix[a.sel[pb + i]];
-    const int row = sm.off[d] + a.pair_row[pb + i];
+    const int d = sm.dix[SEL(i)];
+    const int row = sm.off[d] + (lp ? sm.prow[i] : a.pair_row[pb + i]);
     a.pair_row[pb + i] = row;
     a.row_tok[row] = t0 + i / k;
-    a.row_w[row] = a.w[pb + i];
+    a.row_w[row] = lp ? sm.pw[i] : a.w[pb + i];
   }
-  const int ntok = t1 - t0;
   const bool shared = a.shared_ptr != 0;
   if (shared) {
     for (int tt = tid; tt < ntok; tt += NT) {
@@ -369,7 +465,7 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
     a.glist[nHit] = nD;
   }
   double g = __builtin_inf();
-  for (int tt = tid; tt < ntok; tt += NT) g = fmin(g, a.gap[t0 + tt]);
+  for (int tt = tid; tt < ntok; tt += NT) g = fmin(g, lp ? sm.pgap[tt] : a.gap[t0 + tt]);
   const bool live_d = tid < nD;
   const int cls_d = live_d ? sm.cls[tid] : -1;
   const int cnt_d = live_d ? sm.cnt[tid] : 0;
@@ -414,32 +510,36 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
     a.dev_header[7] = max_rows;
     a.dev_header[8] = cpu_rows;
     a.dev_header[9] = nD + (shared ? 1 : 0);
-    uint64_t* st = a.tab.stats + int64_t(a.layer) * ST_COUNT;
+    // counters: values read in the prologue plus this call's share
+    uint64_t d[ST_COUNT] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (decode) {
-      st[ST_PAIR_HITS] += uint64_t(hit_pairs);
-      st[ST_PAIR_MISSES] += uint64_t(P - hit_pairs);
-      st[ST_EXPERT_HITS] += uint64_t(nHit);
-      st[ST_EXPERT_MISSES] += uint64_t(nM);
-      st[ST_CPU_MISSES] += uint64_t(m_cpu);
-      st[ST_EVICTIONS] += uint64_t(sm.scal[1]);
-      st[ST_BYTES_H2D] += uint64_t(m_str) * uint64_t(a.expert_bytes) + uint64_t(cpu_rows) * uint64_t(a.hidden) * 2ull;
+      d[ST_PAIR_HITS] = uint64_t(hit_pairs);
+      d[ST_PAIR_MISSES] = uint64_t(P - hit_pairs);
+      d[ST_EXPERT_HITS] = uint64_t(nHit);
+      d[ST_EXPERT_MISSES] = uint64_t(nM);
+      d[ST_CPU_MISSES] = uint64_t(m_cpu);
+      d[ST_EVICTIONS] = uint64_t(sm.scal[1]);
+      d[ST_BYTES_H2D] = uint64_t(m_str) * uint64_t(a.expert_bytes) + uint64_t(cpu_rows) * uint64_t(a.hidden) * 2ull;
     } else {
-      st[ST_PAIR_MISSES] += uint64_t(P);
-      st[ST_EXPERT_MISSES] += uint64_t(E);
-      st[ST_BYTES_H2D] += uint64_t(E) * uint64_t(a.expert_bytes);
+      d[ST_PAIR_MISSES] = uint64_t(P);
+      d[ST_EXPERT_MISSES] = uint64_t(E);
+      d[ST_BYTES_H2D] = uint64_t(E) * uint64_t(a.expert_bytes);
     }
-    if (t0 == 0) st[ST_CALLS] += 1;
-    a.tab.min_gap[a.layer] = fmin(a.tab.min_gap[a.layer], min_gap);
+    d[ST_CALLS] = t0 == 0 ? 1ull : 0ull;
+#pragma unroll
+    for (int i = 0; i < ST_COUNT; ++i) st[i] = st0[i] + d[i];
+    a.tab.min_gap[a.layer] = fmin(gap0, min_gap);
     if (a.prof_cnt != nullptr) {
-      // groups and rows behind the timed stages of this call (both FFN
-      // launches: hit list and streamed misses; the copy: streamed misses)
+      // groups and rows behind the timed stages of this call (the FFN over
+      // the hit list and the streamed misses; the copy of the streamed misses)
       const uint64_t g_all = uint64_t(n_hit_list + m_str);
       const uint64_t r_all = uint64_t(hit_pairs + (shared ? ntok : 0) + stream_rows);
+#pragma unroll
       for (int st2 = 0; st2 < 3; ++st2) {
         if (!((a.prof_stages >> st2) & 1)) continue;
         uint64_t* c = a.prof_cnt + (st2 * 4 + a.fmt) * 2;
-        c[0] += st2 == 2 ? uint64_t(m_str) : g_all;
-        c[1] += st2 == 2 ? 0ull : r_all;
+        c[0] = pc0[st2][0] + (st2 == 2 ? uint64_t(m_str) : g_all);
+        c[1] = pc0[st2][1] + (st2 == 2 ? 0ull : r_all);
       }
     }
   }
@@ -466,8 +566,8 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
         cc[mpv - m_str] = sm.cnt[tid];
       }
     }
-    __syncthreads();
     if (m_cpu > 0) {
+      __syncthreads();
       // rows of host-computed groups, packed group after group
       for (int j = 0; j < m_cpu; ++j) {
         int base = 0;
@@ -492,10 +592,11 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
       h->rows_stream = stream_rows;
       h->min_gap = min_gap;
     }
-    __threadfence_system();
-    __syncthreads();
-    if (tid == 0) {
-      __hip_atomic_store(&h->seq, uint32_t(a.stamp), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+    if (a.host_wait) {
+      // the host spins on the stamp: publish everything above first
+      __threadfence_system();
+      __syncthreads();
+      if (tid == 0) __hip_atomic_store(&h->seq, uint32_t(a.stamp), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
     }
   }
 }

@@ -38,9 +38,11 @@ __device__ __attribute__((always_inline)) inline double readlane_f64(double v, i
   return __longlong_as_double((int64_t(hi) << 32) | lo);
 }
 
+// sel2 / w2 / gap2: optional second copy of the results (an LDS mirror), or null.
 __device__ __attribute__((always_inline)) inline void wave_topk(const double* __restrict__ zrow, int E, int k,
                                                                 int32_t* __restrict__ sel, float* __restrict__ w,
-                                                                double* __restrict__ gap) {
+                                                                double* __restrict__ gap, int32_t* sel2 = nullptr,
+                                                                float* w2 = nullptr, double* gap2 = nullptr) {
   const int lane = threadIdx.x & 63;
   constexpr int kPer = kMaxExperts / 64;
   const double NEG = -__builtin_inf();
@@ -80,7 +82,10 @@ __device__ __attribute__((always_inline)) inline void wave_topk(const double* __
       wv = take ? ov : wv;
       wi = take ? oi : wi;
     }
-    if (r < k && lane == 0) sel[r] = wi;
+    if (r < k && lane == 0) {
+      sel[r] = wi;
+      if (sel2) sel2[r] = wi;
+    }
     if (lane == r) myz = wv;
     if (r == k - 1) zk1 = wv;
     if (r == k) zk = wv;
@@ -102,8 +107,14 @@ __device__ __attribute__((always_inline)) inline void wave_topk(const double* __
   const double ex = lane < k ? exp(double(float(myz)) - f0) : 0.0;
   double den = 0.0;
   for (int j = 0; j < k; ++j) den += readlane_f64(ex, j);
-  if (lane < k) w[lane] = float(ex / den);
-  if (lane == 0) *gap = k < E ? zk1 - zk : __builtin_inf();
+  if (lane < k) {
+    w[lane] = float(ex / den);
+    if (w2) w2[lane] = float(ex / den);
+  }
+  if (lane == 0) {
+    *gap = k < E ? zk1 - zk : __builtin_inf();
+    if (gap2) *gap2 = k < E ? zk1 - zk : __builtin_inf();
+  }
 }
 
 }  // namespace ftmoe
