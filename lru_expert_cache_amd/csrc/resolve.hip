@@ -44,7 +44,7 @@ struct ResolveSmem {
   int off[kMaxExperts];
   int sm[kMaxExperts];
   int wcnt[NW][kMaxExperts];
-  int wsum[NW];
+  int wbuf[2][NW];
   int scal[16];
   uint32_t prot[kMaxSlots / 32];  // slots hit by this wave (not evictable)
   int ired[4 * NW];
@@ -59,30 +59,121 @@ struct ResolveSmem {
   int lastpre[kLdsPairs / 32];
 };
 
-// Exclusive prefix sum of v over the workgroup; *total gets the sum.
-__device__ int block_exscan(int v, int* wsum, int* total) {
+// ---- workgroup scans and reductions without LDS round trips inside a wave:
+// DPP row operations plus readlanes across the four rows of 16 lanes.  The
+// per-wave totals meet in LDS; two alternating buffers let a scan skip the
+// barrier that would otherwise protect the buffer from the next scan.
+template <int CTRL>
+__device__ __attribute__((always_inline)) inline int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+// inclusive prefix sum over the wavefront
+__device__ __attribute__((always_inline)) inline int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & 63;
+  x += dpp_i<0x111>(x);  // row_shr:1
+  x += dpp_i<0x112>(x);  // row_shr:2
+  x += dpp_i<0x114>(x);  // row_shr:4
+  x += dpp_i<0x118>(x);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
+            r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = lane >> 4;
+  return x + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+
+// every lane of a row of 16 gets the row's sum / max (butterfly inside the row)
+__device__ __attribute__((always_inline)) inline int row_sum(int x) {
+  x += dpp_i<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_i<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_i<0x141>(x);  // row_half_mirror
+  x += dpp_i<0x140>(x);  // row_mirror
+  return x;
+}
+__device__ __attribute__((always_inline)) inline int row_max(int x) {
+  x = max(x, dpp_i<0xB1>(x));
+  x = max(x, dpp_i<0x4E>(x));
+  x = max(x, dpp_i<0x141>(x));
+  x = max(x, dpp_i<0x140>(x));
+  return x;
+}
+template <int CTRL>
+__device__ __attribute__((always_inline)) inline double dpp_d(double v) {
+  const uint64_t b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(int(uint32_t(b)), int(uint32_t(b)), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(int(uint32_t(b >> 32)), int(uint32_t(b >> 32)), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((int64_t(uint32_t(hi)) << 32) | uint32_t(lo));
+}
+__device__ __attribute__((always_inline)) inline double row_min(double x) {
+  x = fmin(x, dpp_d<0xB1>(x));
+  x = fmin(x, dpp_d<0x4E>(x));
+  x = fmin(x, dpp_d<0x141>(x));
+  x = fmin(x, dpp_d<0x140>(x));
+  return x;
+}
+__device__ __attribute__((always_inline)) inline int wave_sum(int x) {
+  x = row_sum(x);
+  return __builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16) + __builtin_amdgcn_readlane(x, 32) +
+         __builtin_amdgcn_readlane(x, 48);
+}
+__device__ __attribute__((always_inline)) inline int wave_max(int x) {
+  x = row_max(x);
+  return max(max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+             max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
+}
+__device__ __attribute__((always_inline)) inline double readlane_d(double v, int src) {
+  const uint64_t b = __double_as_longlong(v);
+  const uint32_t lo = __builtin_amdgcn_readlane(uint32_t(b), src);
+  const uint32_t hi = __builtin_amdgcn_readlane(uint32_t(b >> 32), src);
+  return __longlong_as_double((int64_t(hi) << 32) | lo);
+}
+__device__ __attribute__((always_inline)) inline double wave_min(double x) {
+  x = row_min(x);
+  return fmin(fmin(readlane_d(x, 0), readlane_d(x, 16)), fmin(readlane_d(x, 32), readlane_d(x, 48)));
+}
+
+// Wave totals of the block scans, in two alternating buffers.
+// Exclusive prefix sum of v over the workgroup; *total gets the sum.  par
+// (uniform, per thread) selects the buffer and flips.
+__device__ __attribute__((always_inline)) inline int block_exscan(int v, int (&wbuf)[2][NW], int& par,
+                                                                  int* total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  if (lane == 63) wsum[wid] = x;
+  const int incl = wave_incl_scan(v);
+  if (lane == 63) wbuf[par][wid] = incl;
   __syncthreads();
   int pre = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
-    const int s = wsum[w];
+    const int s = wbuf[par][w];
     pre += (w < wid) ? s : 0;
     tot += s;
   }
-  __syncthreads();
+  par ^= 1;
   *total = tot;
-  return pre + x - v;
+  return pre + incl - v;
 }
 
-// One pass for the call's closing counters: three sums, a max and an fp64 min.
+// Exclusive count of set flags over the workgroup (ballot within the wave).
+__device__ __attribute__((always_inline)) inline int block_excount(bool f, int (&wbuf)[2][NW], int& par,
+                                                                   int* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const uint64_t m = __ballot(f);
+  const int below = __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
+  if (lane == 0) wbuf[par][wid] = __popcll(m);
+  __syncthreads();
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int s = wbuf[par][w];
+    pre += (w < wid) ? s : 0;
+    tot += s;
+  }
+  par ^= 1;
+  *total = tot;
+  return pre + below;
+}
+
+// One pass for the call's closing counters: three sums, a max and an fp64 min
+// (one barrier; its buffers are used once per kernel).
 struct Closing {
   int cpu_rows, hit_pairs, stream_rows, max_rows;
   double min_gap;
@@ -91,14 +182,11 @@ struct Closing {
 __device__ Closing block_closing(int cpu_rows, int hit_pairs, int stream_rows, int max_rows, double gap, int* ired,
                                  double* dred) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    cpu_rows += __shfl_xor(cpu_rows, off, 64);
-    hit_pairs += __shfl_xor(hit_pairs, off, 64);
-    stream_rows += __shfl_xor(stream_rows, off, 64);
-    max_rows = max(max_rows, __shfl_xor(max_rows, off, 64));
-    gap = fmin(gap, __shfl_xor(gap, off, 64));
-  }
+  cpu_rows = wave_sum(cpu_rows);
+  hit_pairs = wave_sum(hit_pairs);
+  stream_rows = wave_sum(stream_rows);
+  max_rows = wave_max(max_rows);
+  gap = wave_min(gap);
   if (lane == 0) {
     ired[4 * wid + 0] = cpu_rows;
     ired[4 * wid + 1] = hit_pairs;
@@ -116,7 +204,6 @@ __device__ Closing block_closing(int cpu_rows, int hit_pairs, int stream_rows, i
     c.max_rows = max(c.max_rows, ired[4 * w + 3]);
     c.min_gap = fmin(c.min_gap, dred[w]);
   }
-  __syncthreads();
   return c;
 }
 
@@ -124,6 +211,7 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
   __shared__ ResolveSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int E = a.E, k = a.k, C = a.C, t0 = a.t0;
+  int par = 0;  // scan buffer parity
   const bool decode = a.mode == 0;
   const int key0 = a.layer * E;
 
@@ -155,11 +243,19 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
       }
   }
   const int32_t* lru_in = a.tab.lru[cur];
+  // both recency buffers, so that these loads need not wait for lru_cur
   int pf_s[kPf], pf_key[kPf];
+  {
+    int pf0[kPf], pf1[kPf];
 #pragma unroll
-  for (int j = 0; j < kPf; ++j) {
-    const int i = j * NT + tid;
-    pf_s[j] = (decode && i < C) ? lru_in[i] : 0;
+    for (int j = 0; j < kPf; ++j) {
+      const int i = j * NT + tid;
+      const bool ok = decode && i < C;
+      pf0[j] = ok ? a.tab.lru[0][i] : 0;
+      pf1[j] = ok ? a.tab.lru[1][i] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kPf; ++j) pf_s[j] = cur ? pf1[j] : pf0[j];
   }
 
   // ---- 0. top-k of every token of the call (first wave of a decode call)
@@ -168,7 +264,8 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
     for (int t = wid; t < a.T; t += NW)
       wave_topk(a.z + int64_t(t) * E, E, k, a.sel + int64_t(t) * k, a.w + int64_t(t) * k, a.gap + t,
                 mirror ? sm.psel + t * k : nullptr, mirror ? sm.pw + t * k : nullptr, mirror ? sm.pgap + t : nullptr);
-    __threadfence_block();
+    // later phases read the global copies only without the LDS mirror
+    if (!mirror) __threadfence_block();
   }
   // keys of the prefetched recency entries (the old key of a victim slot)
 #pragma unroll
@@ -241,7 +338,7 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
       f = sm.first[e] == i;
     }
     int tot;
-    const int pos = block_exscan(f ? 1 : 0, sm.wsum, &tot);
+    const int pos = block_excount(f, sm.wbuf, par, &tot);
     if (f) {
       sm.D[nD + pos] = e;
       sm.dix[e] = nD + pos;
@@ -270,7 +367,7 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
     }
   }
   int nM;
-  const int mp = block_exscan((tid < nD && !hit) ? 1 : 0, sm.wsum, &nM);
+  const int mp = block_excount(tid < nD && !hit, sm.wbuf, par, &nM);
   // IEEE double, no contraction: floor(nM * share + 1/2)
   const int m_cpu = decode ? int(floor(__dadd_rn(__dmul_rn(double(nM), a.share), 0.5))) : 0;
   const int m_str = nM - m_cpu;
@@ -294,7 +391,7 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
     auto take = [&](bool valid, int s, int oldk, bool have_old) {
       const bool elig = valid && !((sm.prot[s >> 5] >> (s & 31)) & 1u);
       int tot;
-      const int vp = neli + block_exscan(elig ? 1 : 0, sm.wsum, &tot);
+      const int vp = neli + block_excount(elig, sm.wbuf, par, &tot);
       if (elig) {
         if (vp < m_str) {
           const int d = sm.sm[vp];
@@ -416,7 +513,7 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
   // ---- 9. group offsets and rows
   {
     int tot;
-    const int o = block_exscan(tid < nD ? sm.cnt[tid] : 0, sm.wsum, &tot);
+    const int o = block_exscan(tid < nD ? sm.cnt[tid] : 0, sm.wbuf, par, &tot);
     if (tid < nD) sm.off[tid] = o;
   }
   __syncthreads();
@@ -438,7 +535,7 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
   // ---- 10. group descriptors and run lists (hits [+ shared], streamed, host)
   int nHit;
   const bool ishit = tid < nD && sm.cls[tid] == FT_PAIR_HIT;
-  const int hp = block_exscan(ishit ? 1 : 0, sm.wsum, &nHit);
+  const int hp = block_excount(ishit, sm.wbuf, par, &nHit);
   const int n_hit_list = nHit + (shared ? 1 : 0);
   if (tid < nD) {
     const int c = sm.cls[tid];
@@ -481,7 +578,7 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
     const int tr = a.tile_rows;
     const int nt = live_d ? (cnt_d + tr - 1) / tr : 0;
     int ntot;
-    const int base = block_exscan(nt, sm.wsum, &ntot);
+    const int base = block_exscan(nt, sm.wbuf, par, &ntot);
     for (int j = 0; j < nt; ++j) {
       a.tiles[2 * (base + j)] = tid;
       a.tiles[2 * (base + j) + 1] = j;
@@ -607,8 +704,9 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
 __global__ __launch_bounds__(NT) void k_free_slots(DevTable tab, int C, int lo0, int hi0, int lo1, int hi1,
                                                    const int32_t* keys, const int32_t* slots, int n,
                                                    uint64_t* evict_stat) {
-  __shared__ int wsum[NW];
+  __shared__ int wbuf[2][NW];
   __shared__ int nev;
+  int par = 0;
   const int tid = threadIdx.x;
   if (tid == 0) nev = 0;
   __syncthreads();
@@ -639,7 +737,7 @@ __global__ __launch_bounds__(NT) void k_free_slots(DevTable tab, int C, int lo0,
     const int s = c0 + tid;
     const bool f = s < C && tab.slot_key[s] < 0;
     int tot;
-    const int p = block_exscan(f ? 1 : 0, wsum, &tot);
+    const int p = block_excount(f, wbuf, par, &tot);
     if (f) lru_out[nfree + p] = s;
     nfree += tot;
   }
@@ -653,7 +751,7 @@ __global__ __launch_bounds__(NT) void k_free_slots(DevTable tab, int C, int lo0,
       r = tab.slot_key[s] >= 0;
     }
     int tot;
-    const int p = block_exscan(r ? 1 : 0, wsum, &tot);
+    const int p = block_excount(r, wbuf, par, &tot);
     if (r) lru_out[nfree + nres + p] = s;
     nres += tot;
   }

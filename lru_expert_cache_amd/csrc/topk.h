@@ -16,15 +16,17 @@ namespace ftmoe {
 // (larger logit first, lower expert index on ties).  Each lane keeps the best
 // of its own logits (experts lane, lane+64, ...); a round reduces the 64 lane
 // bests with DPP row permutations (quad xor 1, quad xor 2, half-row mirror,
-// row mirror: every lane ends with the best of its row of 16) and four
-// readlanes across the rows, then only the winning lane refreshes its best.
+// row mirror: every lane ends with the best of its row of 16) and the two row
+// broadcasts (lane 15 of rows 0 and 2 into rows 1 and 3, then lane 31 into
+// rows 2 and 3), reads lane 63, and only the winning lane refreshes its best.
 // No LDS round trips and no divergent branches in the reduction.
-template <int CTRL>
+// ROWS: rows of 16 lanes that take part (the others see their own value).
+template <int CTRL, int ROWS = 0xF>
 __device__ __attribute__((always_inline)) inline void dpp_best(double& v, int& i) {
   const uint64_t b = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_update_dpp(int(uint32_t(b)), int(uint32_t(b)), CTRL, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(int(uint32_t(b >> 32)), int(uint32_t(b >> 32)), CTRL, 0xF, 0xF, false);
-  const int oi = __builtin_amdgcn_update_dpp(i, i, CTRL, 0xF, 0xF, false);
+  const int lo = __builtin_amdgcn_update_dpp(int(uint32_t(b)), int(uint32_t(b)), CTRL, ROWS, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(int(uint32_t(b >> 32)), int(uint32_t(b >> 32)), CTRL, ROWS, 0xF, false);
+  const int oi = __builtin_amdgcn_update_dpp(i, i, CTRL, ROWS, 0xF, false);
   const double ov = __longlong_as_double((int64_t(uint32_t(hi)) << 32) | uint32_t(lo));
   const bool take = (ov > v) | ((ov == v) & (oi < i));
   v = take ? ov : v;
@@ -38,13 +40,14 @@ __device__ __attribute__((always_inline)) inline double readlane_f64(double v, i
   return __longlong_as_double((int64_t(hi) << 32) | lo);
 }
 
+// kPer: logits per lane (E <= 64 * kPer).
 // sel2 / w2 / gap2: optional second copy of the results (an LDS mirror), or null.
-__device__ __attribute__((always_inline)) inline void wave_topk(const double* __restrict__ zrow, int E, int k,
-                                                                int32_t* __restrict__ sel, float* __restrict__ w,
-                                                                double* __restrict__ gap, int32_t* sel2 = nullptr,
-                                                                float* w2 = nullptr, double* gap2 = nullptr) {
+template <int kPer>
+__device__ __attribute__((always_inline)) inline void wave_topk_n(const double* __restrict__ zrow, int E, int k,
+                                                                  int32_t* __restrict__ sel, float* __restrict__ w,
+                                                                  double* __restrict__ gap, int32_t* sel2,
+                                                                  float* w2, double* gap2) {
   const int lane = threadIdx.x & 63;
-  constexpr int kPer = kMaxExperts / 64;
   const double NEG = -__builtin_inf();
   double v[kPer];
 #pragma unroll
@@ -68,20 +71,14 @@ __device__ __attribute__((always_inline)) inline void wave_topk(const double* __
   for (int r = 0; r < rounds; ++r) {
     double rv = bv;
     int ri = bi;
-    dpp_best<0xB1>(rv, ri);   // quad_perm [1,0,3,2]
-    dpp_best<0x4E>(rv, ri);   // quad_perm [2,3,0,1]
-    dpp_best<0x141>(rv, ri);  // row_half_mirror
-    dpp_best<0x140>(rv, ri);  // row_mirror
-    double wv = readlane_f64(rv, 0);
-    int wi = __builtin_amdgcn_readlane(ri, 0);
-#pragma unroll
-    for (int row = 1; row < 4; ++row) {
-      const double ov = readlane_f64(rv, 16 * row);
-      const int oi = __builtin_amdgcn_readlane(ri, 16 * row);
-      const bool take = (ov > wv) | ((ov == wv) & (oi < wi));
-      wv = take ? ov : wv;
-      wi = take ? oi : wi;
-    }
+    dpp_best<0xB1>(rv, ri);        // quad_perm [1,0,3,2]
+    dpp_best<0x4E>(rv, ri);        // quad_perm [2,3,0,1]
+    dpp_best<0x141>(rv, ri);       // row_half_mirror
+    dpp_best<0x140>(rv, ri);       // row_mirror: every lane holds its row's best
+    dpp_best<0x142, 0xA>(rv, ri);  // row_bcast:15 into rows 1 and 3
+    dpp_best<0x143, 0xC>(rv, ri);  // row_bcast:31 into rows 2 and 3: lane 63 holds the best
+    const double wv = readlane_f64(rv, 63);
+    const int wi = __builtin_amdgcn_readlane(ri, 63);
     if (r < k && lane == 0) {
       sel[r] = wi;
       if (sel2) sel2[r] = wi;
@@ -115,6 +112,19 @@ __device__ __attribute__((always_inline)) inline void wave_topk(const double* __
     *gap = k < E ? zk1 - zk : __builtin_inf();
     if (gap2) *gap2 = k < E ? zk1 - zk : __builtin_inf();
   }
+}
+
+__device__ __attribute__((always_inline)) inline void wave_topk(const double* __restrict__ zrow, int E, int k,
+                                                                int32_t* __restrict__ sel, float* __restrict__ w,
+                                                                double* __restrict__ gap, int32_t* sel2 = nullptr,
+                                                                float* w2 = nullptr, double* gap2 = nullptr) {
+  static_assert(kMaxExperts <= 512, "at most 8 logits per lane");
+  if (E <= 128)
+    wave_topk_n<2>(zrow, E, k, sel, w, gap, sel2, w2, gap2);
+  else if (E <= 256)
+    wave_topk_n<4>(zrow, E, k, sel, w, gap, sel2, w2, gap2);
+  else
+    wave_topk_n<8>(zrow, E, k, sel, w, gap, sel2, w2, gap2);
 }
 
 }  // namespace ftmoe
