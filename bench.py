@@ -319,7 +319,7 @@ def main():
         "config": {"workload": w.name, "layers": L, "hidden": H, "expert_inter": w.inter, "experts": E,
                    "top_k": w.top_k, "batch": B, "pool_slots": w.pool_slots, "format": "mxfp4",
                    "zipf_alpha": w.zipf_alpha},
-        "roofline": {"kernel": "k_ffn<mxfp4, gate/up>", "bound": "hbm", "achieved": gu_gbs, "peak": HBM_PEAK_GBS,
+        "roofline": {"kernel": "k_ffn_ring<mxfp4, gate/up, 4>", "bound": "hbm", "achieved": gu_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": gu_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "algorithmic_bytes_per_launch": gu["bytes"] / max(gu["launches"], 1),
                      "avg_launch_us": gu_avg_ms * 1e3},
