@@ -157,27 +157,52 @@ def measure_prefill(ft, torch, ms, pool, dev):
     return res
 
 
-def run_steps(ft, torch, pool, x_all, bias_all, out, first, nsteps, L, B, sample_gateup=False):
-    """Decode steps.  sample_gateup: time the gate/up launch of one layer per
-    step (rotating over the layers) with HIP events; an event between two
-    kernels costs a few microseconds of queue time, so timing every launch
-    would slow the step it measures."""
+def run_steps(ft, torch, pool, x_all, bias_of, out, first, nsteps, L, B, sample_gateup=False):
+    """Decode steps (x_all[s] is step s's input).  bias_of(s, l): the router
+    bias of layer l at step s (popularity phases), or None.  sample_gateup:
+    time the gate/up launch of one layer per step (rotating over the layers)
+    with HIP events; an event between two kernels costs a few microseconds of
+    queue time, so timing every launch would slow the step it measures."""
     for s in range(first, first + nsteps):
         lp = (s * 7) % L if sample_gateup else -1
         for l in range(L):
             if l == lp:
                 ft.ft_moe_set_profiling(pool, ["ffn_gateup"])
-            ft.ft_moe_layer_forward(pool, l, B, x_all[s, l], bias_all[l], out, ft.FT_FWD_DECODE, None, None)
+            ft.ft_moe_layer_forward(pool, l, B, x_all[s, l], bias_of(s, l), out, ft.FT_FWD_DECODE, None, None)
             if l == lp:
                 ft.ft_moe_set_profiling(pool, [])
+
+
+def ffn_kernel_label(w, B):
+    """The decode FFN kernel of the gate/up launch at this batch, by the
+    library's rule: at most 16 tokens and a K split of at most 4 tiles per wave
+    over at most 8 waves within the register budget -> k_ffn_ring; at most 64
+    tokens -> k_ffn_stream; else the split-K k_ffn."""
+    names = {1: "mxfp4", 2: "nvfp4", 3: "fp8"}
+    fmts = sorted({names[f] for f in w.layer_fmt})
+    nkb = w.hidden // 128
+
+    def ring_fits(f):
+        slot = 2 * (12 if f == "fp8" else 5) + 16
+        return any(nkb % k == 0 and nkb // k <= 8 and k * slot <= 112 for k in (4, 3, 2, 1))
+
+    if B <= 16 and all(ring_fits(f) for f in fmts):
+        kern = "k_ffn_ring"
+    elif B <= 64:
+        kern = "k_ffn_stream"
+    else:
+        kern = "k_ffn"
+    return f"{kern}<{'|'.join(fmts)}, gate/up>"
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=240)
-    ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--batch", type=int, default=16)
+    ap.add_argument("--workload", default="qwen-a3b-decode",
+                    help="decode workload: qwen-a3b-decode (default), deepseek-v4-flash-decode, glm-5.2-mixed-decode")
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 240; 8 for the other workloads)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 16; 2 for the other workloads)")
+    ap.add_argument("--batch", type=int, default=None, help="tokens per call (default: the workload's largest)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-calls", type=int, default=6)
     ap.add_argument("--no-extras", action="store_true", help="skip the batch 1/4 and link measurements")
@@ -196,8 +221,19 @@ def main():
 
     ft.lib()
     dev = torch.device("cuda", 0)
-    w = ms.workload("qwen-a3b-decode")
-    L, E, H, B = w.num_layers, w.num_experts, w.hidden, args.batch
+    w = ms.workload(args.workload)
+    if w.mode != "decode":
+        print(f"bench.py times decode workloads; {w.name} is a {w.mode} workload (its chunk is timed as an extra)",
+              file=sys.stderr)
+        sys.exit(2)
+    headline = w.name == "qwen-a3b-decode"
+    if args.steps is None:
+        args.steps = 240 if headline else 8
+    if args.warmup is None:
+        args.warmup = 16 if headline else 2
+    if not headline:
+        args.no_extras = True  # the batch sweep, link and prefill extras belong to the default workload
+    L, E, H, B = w.num_layers, w.num_experts, w.hidden, args.batch or w.batches[-1]
     nsteps = args.warmup + args.steps
 
     t = time.perf_counter()
@@ -206,15 +242,25 @@ def main():
     t = time.perf_counter()
     blobs = [store.expert(l, e) for l in range(L) for e in range(E)]
     router = np.stack([ms.router_weight(w, l) for l in range(L)])
-    cfg = ft.make_config(L, H, w.inter, E, w.top_k, w.layer_fmt, pool_slots=w.pool_slots)
-    pool, _ = ft.ft_moe_init_pool(cfg, blobs, router)
+    shared = [store.shared(l) for l in range(L)] if w.shared_expert else None
+    cfg = ft.make_config(L, H, w.inter, E, w.top_k, w.layer_fmt, pool_slots=w.pool_slots, shared=w.shared_expert)
+    pool, _ = ft.ft_moe_init_pool(cfg, blobs, router, shared)
     prefill_pool = None
     if not args.no_extras:
         wp = ms.workload("qwen-a3b-prefill-4096")
         cfgp = ft.make_config(L, H, w.inter, E, w.top_k, wp.layer_fmt, pool_slots=wp.pool_slots)
         prefill_pool, _ = ft.ft_moe_init_pool(cfgp, blobs, router)
-    del blobs, store
+    del blobs, store, shared
     log(f"[bench] pool of {w.pool_slots} slots ready in {time.perf_counter() - t:.1f} s")
+    share = 0.0
+    if w.hybrid:
+        # the one-time measurement behind the split: host expert rate vs pinned H2D rate
+        eb = ms.expert_bytes(w.layer_fmt[0], H, w.inter)
+        cpu_bps = ft.ft_moe_host_expert_rate(pool, 0, max(1, B * w.top_k // 64), 1)
+        link = measure_h2d(torch, dev, sizes=(eb,), reps=4)[eb] * 1e9
+        share = cpu_bps / (cpu_bps + link)
+        ft.ft_moe_set_hybrid_share(pool, share)
+        log(f"[bench] hybrid share {share:.4f} (host {cpu_bps / 1e9:.2f} GB/s, link {link / 1e9:.1f} GB/s)")
 
     t = time.perf_counter()
     x_host = np.empty((nsteps, L, B, H), np.uint16)
@@ -222,12 +268,20 @@ def main():
         for l in range(L):
             x_host[s, l] = ms.activations(w, l, s, B)
     x_all = torch.from_numpy(x_host.view(np.int16)).to(dev)
-    bias_all = torch.from_numpy(np.stack([ms.popularity_bias(w, l, 0) for l in range(L)])).to(dev)
+    phases = sorted({w.phase(s) for s in range(nsteps)})
+    biases = {}
+    if w.zipf_alpha is not None:
+        for ph in phases:
+            biases[ph] = torch.from_numpy(np.stack([ms.popularity_bias(w, l, ph) for l in range(L)])).to(dev)
+
+    def bias_of(s, l):
+        return biases[w.phase(s)][l] if biases else None
+
     out = torch.empty((B, H), dtype=torch.int16, device=dev)
     del x_host
     log(f"[bench] {nsteps} steps of activations resident on the GPU ({time.perf_counter() - t:.1f} s)")
 
-    run_steps(ft, torch, pool, x_all, bias_all, out, 0, args.warmup, L, B)
+    run_steps(ft, torch, pool, x_all, bias_of, out, 0, args.warmup, L, B)
     torch.cuda.synchronize()
     ft.ft_moe_pool_stats(pool, reset=True)
     # timed region: events bracket the dominant kernel (gate/up FFN) and the
@@ -235,7 +289,7 @@ def main():
     ft.ft_moe_profile_read(pool, reset=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    run_steps(ft, torch, pool, x_all, bias_all, out, args.warmup, args.steps, L, B, sample_gateup=True)
+    run_steps(ft, torch, pool, x_all, bias_of, out, args.warmup, args.steps, L, B, sample_gateup=True)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ft.ft_moe_set_profiling(pool, [])
@@ -245,7 +299,7 @@ def main():
     # a short extra pass with every stage timed, for the per-stage breakdown
     nb = min(8, args.steps)
     ft.ft_moe_set_profiling(pool, None)
-    run_steps(ft, torch, pool, x_all, bias_all, out, args.warmup, nb, L, B)
+    run_steps(ft, torch, pool, x_all, bias_of, out, args.warmup, nb, L, B)
     ft.ft_moe_set_profiling(pool, [])
     stages = ft.ft_moe_profile_read(pool, reset=True)
 
@@ -278,10 +332,10 @@ def main():
             xb = torch.from_numpy(np.stack([[ms.activations(w, l, 1000 + s, b) for l in range(L)]
                                             for s in range(24)]).view(np.int16)).to(dev)
             ob = torch.empty((b, H), dtype=torch.int16, device=dev)
-            run_steps(ft, torch, pool, xb, bias_all, ob, 0, 8, L, b)
+            run_steps(ft, torch, pool, xb, bias_of, ob, 0, 8, L, b)
             torch.cuda.synchronize()
             ta = time.perf_counter()
-            run_steps(ft, torch, pool, xb, bias_all, ob, 8, 16, L, b)
+            run_steps(ft, torch, pool, xb, bias_of, ob, 8, 16, L, b)
             torch.cuda.synchronize()
             extras[f"tokens_per_s_batch{b}"] = b * 16 / (time.perf_counter() - ta)
     ft.ft_moe_destroy_pool(pool)
@@ -297,7 +351,7 @@ def main():
         extras["calibration_copy_bytes"] = a.numel() * 2
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and headline:
         t = time.perf_counter()
         cpu = cpu_baseline(w, B, args.cpu_calls)
         log(f"[bench] cpu baseline {time.perf_counter() - t:.1f} s")
@@ -314,13 +368,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4-weights/bf16-act/fp32-acc",
+        "dtype": "|".join(sorted({ {1: "mxfp4", 2: "nvfp4", 3: "fp8"}[f] for f in w.layer_fmt})) + "-weights/bf16-act/fp32-acc",
         "data": "synthetic",
         "config": {"workload": w.name, "layers": L, "hidden": H, "expert_inter": w.inter, "experts": E,
-                   "top_k": w.top_k, "batch": B, "pool_slots": w.pool_slots, "format": "mxfp4",
-                   "zipf_alpha": w.zipf_alpha},
-        "roofline": {"kernel": "k_ffn_ring<mxfp4, gate/up, 4>", "bound": "hbm", "achieved": gu_gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": gu_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(),
+                   "top_k": w.top_k, "batch": B, "pool_slots": w.pool_slots,
+                   "format": "|".join(sorted({ {1: "mxfp4", 2: "nvfp4", 3: "fp8-b128"}[f] for f in w.layer_fmt})),
+                   "zipf_alpha": w.zipf_alpha, "shared_expert": w.shared_expert, "hybrid_share": share,
+                   "host_blob_aliasing": w.n_blobs},
+        "roofline": {"kernel": ffn_kernel_label(w, B), "bound": "hbm", "achieved": gu_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": gu_gbs / HBM_PEAK_GBS, "traffic": measured_traffic() if headline else None,
                      "algorithmic_bytes_per_launch": gu["bytes"] / max(gu["launches"], 1),
                      "avg_launch_us": gu_avg_ms * 1e3},
         "cpu_baseline": cpu,

@@ -187,8 +187,8 @@ struct FfnArgs {
   int32_t hidden, inter;
   ExpertLayout lay;
   int32_t act_mode;       // FT_ACT_* >> 4
-  int32_t max_rows;       // bound on the rows of any group (a decode call's token count),
-                          // selects the decode kernels; 0 = unknown
+  int32_t max_rows;       // bound on the rows of any group (a decode call's token count):
+                          // <= 16 ring (gate/up), <= 64 streaming kernel; 0 = unknown
 };
 hipError_t launch_ffn_gateup(const FfnArgs& a, hipStream_t s, Ev ev = {});
 hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t s, Ev ev = {});

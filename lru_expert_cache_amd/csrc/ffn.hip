@@ -223,7 +223,8 @@ __device__ inline void tile_mma_sc(const TileRegs<FMT>& r, const uint4 xv[4], fl
 // a step that are not streamed (tokens, routing weights, tensor scales) are
 // made when an item starts, before its first prefetch; a prefetch past the end
 // reads one shared line instead of branching.  Groups with more than 16 rows
-// stream their weights once per 16 rows (decode calls have few such rows).
+// (at most 64) stream their weights once per 16 rows (decode calls have few
+// such rows).
 // f(integral_constant<0>) ... f(integral_constant<N-1>): ring slots indexed at compile time
 template <typename F, int... I>
 __device__ __attribute__((always_inline)) inline void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
@@ -234,8 +235,10 @@ __device__ __attribute__((always_inline)) inline void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+typedef long long i64x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kStreamWaves = 4;     // 16-row weight tiles per workgroup
-constexpr int kStreamMaxChunks = 2; // row chunks of 16 a group may have (max_rows <= 32)
+constexpr int kStreamMaxChunks = 4; // row chunks of 16 a group may have (max_rows <= 64)
 
 template <int FMT>
 __device__ inline void load_tile_sel(TileRegs<FMT>& r, const uint8_t* __restrict__ W, const MatLayout& m,
@@ -282,15 +285,17 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_ffn_stream(FfnArgs a) {
     const int nrc = min((g.row_count + 15) >> 4, kStreamMaxChunks);
     const int nsteps = nrc * nkb;
 
-    // per-item reads, made before the stream starts
-    const uint16_t* xrow[kStreamMaxChunks];
-    float wr[kStreamMaxChunks];
+    // per-item reads, made before the stream starts: per row chunk, this
+    // thread's activation row (element offset from x) and, for down, the
+    // routing weight of the lane's epilogue row (vectors: indexed in registers)
+    i64x4 xoff;
+    f32x4 wr;
 #pragma unroll
     for (int c = 0; c < kStreamMaxChunks; ++c) {
       const int r = c * 16 + xr;
       const bool ok = c < nrc && r < g.row_count;
       const int row = g.row_begin + (ok ? r : 0);
-      xrow[c] = GATEUP ? a.x + int64_t(a.row_tok[row]) * a.hidden : a.x + int64_t(row) * a.inter;
+      xoff[c] = GATEUP ? int64_t(a.row_tok[row]) * a.hidden : int64_t(row) * a.inter;
       const int re = c * 16 + n;  // epilogue row of this lane
       wr[c] = GATEUP ? 0.0f : a.row_w[g.row_begin + (c < nrc && re < g.row_count ? re : 0)];
     }
@@ -317,7 +322,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_ffn_stream(FfnArgs a) {
           sring[u][mi] = *reinterpret_cast<const float4*>(
               live ? W + m.scales_off + (tile * 16 + 4 * q) * 4 : dummy);
       }
-      const uint16_t* xp = c == 0 ? xrow[0] : xrow[kStreamMaxChunks - 1];
+      const uint16_t* xp = a.x + xoff[c];
       xring[u] = *reinterpret_cast<const u32x4*>(live ? xp + t * kTileK + xc * 8 : a.x);
     };
     static_for<D>([&](auto uc) { fetch(decltype(uc)::value, uc); });
@@ -369,7 +374,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_ffn_stream(FfnArgs a) {
               *reinterpret_cast<uint2*>(a.out + int64_t(row) * a.inter + o0) =
                   make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16), uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
             } else {
-              const float wrow = c == 0 ? wr[0] : wr[kStreamMaxChunks - 1];
+              const float wrow = wr[c];
 #pragma unroll
               for (int i = 0; i < 4; ++i) hv[i] = f32_to_bf16_rne(wrow * (acc[0][i] * tsc[0]));
               *reinterpret_cast<uint2*>(a.out + int64_t(row) * a.hidden + o0) =
@@ -815,7 +820,7 @@ hipError_t launch_small(const FfnArgs& a, hipStream_t st, Ev ev) {
 template <bool GATEUP>
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t st, Ev ev) {
   if (a.n_list <= 0) return hipSuccess;
-  bool small = a.max_rows > 0 && a.max_rows <= 2 * kTileRows;
+  bool small = a.max_rows > 0 && a.max_rows <= kStreamMaxChunks * kTileRows;
 #ifdef FT_FFN_KERNEL_ENV
   if (const char* e = getenv("FFN_KERNEL"))
     if (!strcmp(e, "grid")) small = false;

@@ -357,8 +357,11 @@ void prof_push(ft_moe_pool* p, int stage, Ev ev, double bytes, double flops);
 // counts them).  off_dev: glist offset read on the device, or null.
 int run_ffn(ft_moe_pool* p, int layer, const void* x, int list_off, int n, const int32_t* n_dev, hipStream_t s,
             double groups, double rows, const int32_t* off_dev = nullptr, int max_group_rows = 1 << 30) {
+  // nothing to run (a count known on the host): no launch, and no timing record
+  // (its recycled events would still hold an earlier launch's timestamps)
+  if (n_dev == nullptr && n <= 0) return FT_OK;
   FfnArgs a = ffn_args(p, layer, list_off, n, n_dev, off_dev);
-  a.max_rows = p->ffn_stream && max_group_rows <= 32 ? max_group_rows : 0;
+  a.max_rows = p->ffn_stream && max_group_rows <= 64 ? max_group_rows : 0;
   const int f = p->fmt[layer];
   const double H = p->H, I = p->I;
   a.x = static_cast<const uint16_t*>(x);
