@@ -157,6 +157,32 @@ def measure_prefill(ft, torch, ms, pool, dev):
     return res
 
 
+def measure_graph(ft, torch, pool, x_all, bias_of, L, B, first, nrep, dev):
+    """Tokens/s of a whole decode step (L layer calls) captured once into a
+    HIP graph and replayed; each replay's inputs are copied into the captured
+    input buffers first (that copy is inside the timing)."""
+    H = x_all.shape[-1]
+    ft.ft_moe_reserve(pool, B)
+    xin = torch.empty((L, B, H), dtype=torch.int16, device=dev)
+    outs = torch.empty((L, B, H), dtype=torch.int16, device=dev)
+    side = torch.cuda.Stream(dev)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for l in range(L):
+            ft.ft_moe_layer_forward(pool, l, B, xin[l], bias_of(first, l), outs[l], ft.FT_FWD_DECODE, side, None)
+    for s in range(first, first + 2):  # warm replays
+        xin.copy_(x_all[s])
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(first + 2, first + 2 + nrep):
+        xin.copy_(x_all[s])
+        g.replay()
+    torch.cuda.synchronize()
+    return B * nrep / (time.perf_counter() - t0)
+
+
 def run_steps(ft, torch, pool, x_all, bias_of, out, first, nsteps, L, B, sample_gateup=False):
     """Decode steps (x_all[s] is step s's input).  bias_of(s, l): the router
     bias of layer l at step s (popularity phases), or None.  sample_gateup:
@@ -338,6 +364,9 @@ def main():
             run_steps(ft, torch, pool, xb, bias_of, ob, 8, 16, L, b)
             torch.cuda.synchronize()
             extras[f"tokens_per_s_batch{b}"] = b * 16 / (time.perf_counter() - ta)
+            if b == 1:
+                extras["graph_tokens_per_s_batch1"] = measure_graph(ft, torch, pool, xb, bias_of, L, 1, 0, 16, dev)
+        extras["graph_tokens_per_s_batch16"] = measure_graph(ft, torch, pool, x_all, bias_of, L, B, 0, 16, dev)
     ft.ft_moe_destroy_pool(pool)
     if prefill_pool is not None:
         extras["prefill"] = measure_prefill(ft, torch, ms, prefill_pool, dev)

@@ -165,6 +165,24 @@ int ft_moe_last_misses(const ft_moe_pool *p, int32_t *stream_expert, int32_t *st
 int ft_moe_pool_table(ft_moe_pool *p, int32_t *slot_key, uint64_t *slot_last, uint64_t *clock,
                       int64_t *slots);
 
+/* Grow the per-call work buffers for calls of up to max_tokens tokens now
+ * (synchronises the device when it grows them; a call that needs no growth
+ * allocates nothing; the buffers hold at least 64 tokens).  Needed before
+ * capturing calls into a HIP graph.
+ *
+ * Graph capture (the pages list graph-compatible execution among the
+ * runtime's mechanisms: dev.to "FreeToken uses bandwidth-adaptive CPU-GPU
+ * co-execution on your desktop", section "What the project says it does").
+ * ft_moe_layer_forward may be called on a stream that is capturing when the
+ * call is a device-driven decode call (FT_FWD_DECODE, no hybrid share, T*top_k
+ * <= pool slots, FT_MOE_DECODE_PATH not "host") that fits the buffers
+ * already reserved; every other call returns FT_E_INVALID while capturing.  Captured
+ * calls take no host decision: a replay resolves its experts against the slot
+ * table as it stands when the replay runs, copies its own misses, and updates
+ * table and counters like an eager call.  Stage timing is skipped while
+ * capturing, and ft_moe_last_misses reports the most recent eager call. */
+int ft_moe_reserve(ft_moe_pool *p, int32_t max_tokens);
+
 /* Set the hybrid share used by later calls (0..1). */
 int ft_moe_set_hybrid_share(ft_moe_pool *p, double share);
 

@@ -1035,11 +1035,27 @@ int ft_moe_layer_forward(ft_moe_pool* p, int32_t layer, int32_t num_tokens, cons
     }
     if (num_tokens == 0) return FT_OK;
     DeviceGuard dg(p->device);
-    int rc = ensure_capacity(p, num_tokens);
-    if (rc) return rc;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     const int T = num_tokens, E = p->E, k = p->k;
-    if (p->any_call && s != p->last_stream) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    FT_HIP_CHECK(hipStreamIsCapturing(s, &cap));
+    const bool capturing = cap != hipStreamCaptureStatusNone;
+    const bool dev_path = mode == FT_FWD_DECODE && p->dev_decode && p->share == 0.0 && int64_t(T) * k <= p->C;
+    if (capturing && (!dev_path || T > p->cap_T)) {
+      set_error("a captured call must be a device-driven decode call of at most the reserved %d tokens "
+                "(T=%d, mode %d)", p->cap_T, T, mode);
+      return FT_E_INVALID;
+    }
+    int rc = ensure_capacity(p, num_tokens);
+    if (rc) return rc;
+    const int32_t prof_saved = p->prof_mask;
+    if (capturing) p->prof_mask = 0;  // no event records inside a graph
+    struct Restore {
+      ft_moe_pool* p;
+      int32_t m;
+      ~Restore() { p->prof_mask = m; }
+    } restore{p, prof_saved};
+    if (p->any_call && s != p->last_stream && !capturing) {
       // a call on another stream: order it after everything enqueued so far
       FT_HIP_CHECK(hipEventRecord(p->ev_call_done, p->last_stream));
       FT_HIP_CHECK(hipStreamWaitEvent(s, p->ev_call_done, 0));
@@ -1055,14 +1071,18 @@ int ft_moe_layer_forward(ft_moe_pool* p, int32_t layer, int32_t num_tokens, cons
       prof_push(p, FT_STAGE_TOPK, e0, double(T) * E * 8, 0.0);
     }
     if (mode == FT_FWD_DECODE) {
-      const bool dev = p->dev_decode && p->share == 0.0 && int64_t(T) * k <= p->C;
-      rc = dev ? forward_decode_dev(p, layer, T, x_bf16, out_bf16, s) : forward_decode(p, layer, T, x_bf16, out_bf16, s);
+      rc = dev_path ? forward_decode_dev(p, layer, T, x_bf16, out_bf16, s)
+                    : forward_decode(p, layer, T, x_bf16, out_bf16, s);
     } else {
       rc = forward_prefill(p, layer, T, x_bf16, out_bf16, s, act);
     }
     if (rc) return rc;
-    p->last_stream = s;
-    p->any_call = true;
+    if (!capturing) {
+      p->last_stream = s;
+      p->any_call = true;
+    } else {
+      p->last_pending = false;  // the lists belong to a replay, not to this call
+    }
     if (trace) {
       const size_t n = size_t(T) * k;
       if (trace->sel) FT_HIP_CHECK(hipMemcpyAsync(trace->sel, p->sel, n * 4, hipMemcpyDeviceToDevice, s));
@@ -1150,6 +1170,15 @@ int ft_moe_pool_table(ft_moe_pool* p, int32_t* slot_key, uint64_t* slot_last, ui
   if (clock) FT_HIP_CHECK(hipMemcpy(clock, p->tab.clock, 8, hipMemcpyDeviceToHost));
   if (slots) *slots = p->C;
   return FT_OK;
+}
+
+int ft_moe_reserve(ft_moe_pool* p, int32_t max_tokens) {
+  if (!p || max_tokens < 0) {
+    set_error("bad pool or token count");
+    return FT_E_INVALID;
+  }
+  DeviceGuard dg(p->device);
+  return ensure_capacity(p, max_tokens);
 }
 
 int ft_moe_set_hybrid_share(ft_moe_pool* p, double share) {
