@@ -32,7 +32,8 @@ Runtime").  Finer points are this build's readings:
 
 Pins (tests/test_oracle_lru.py): an independent brute-force list LRU,
 hand-worked traces, the compulsory-miss, inclusion and cyclic-thrash
-properties of LRU, hits + misses = T*k.
+properties of LRU, hits + misses = T*k; for resize, the list LRU's own resize
+and a textbook recency-list LRU whose capacity changes (T = k = 1).
 """
 
 from __future__ import annotations
@@ -170,6 +171,39 @@ class LRUPool:
         return dict(flag=flag, slot=slot, stream=[(e, base + e) for e in range(E)], cpu=[], D=D,
                     pair_hits=0, expert_hits=0, expert_misses=E, cpu_misses=0,
                     evictions=evictions)
+
+    def resize(self, new_capacity: int):
+        """Elastic resize of the pool at runtime (the pages: VRAM is
+        re-allocated between the expert cache and other memory while the
+        engine runs -- dev.to article "FreeToken uses bandwidth-adaptive CPU-GPU
+        co-execution on your desktop", section "Memory that moves while the
+        engine runs").  Readings: the new_capacity most recently used residents
+        survive (a shrink evicts the LRU tail); a survivor keeps its slot when
+        that slot still exists, the others -- in ascending old slot -- take the
+        lowest free slots below new_capacity; last-use values and the clock are
+        unchanged.  Returns the evicted keys and the (old slot, new slot) moves.
+        """
+        new_C = int(new_capacity)
+        assert new_C >= 1
+        res = [s for s in range(self.C) if self.key_of[s] is not None]
+        res.sort(key=lambda s: self.last_use[s])
+        n_ev = max(0, len(res) - new_C)
+        evicted, survivors = res[:n_ev], res[n_ev:]
+        keep = sorted(s for s in survivors if s < new_C)
+        move = sorted(s for s in survivors if s >= new_C)
+        kept = set(keep)
+        free_low = [s for s in range(new_C) if s not in kept]
+        key_of, last_use = [None] * new_C, [None] * new_C
+        moves = []
+        for s in keep:
+            key_of[s], last_use[s] = self.key_of[s], self.last_use[s]
+        for s, t in zip(move, free_low):
+            key_of[t], last_use[t] = self.key_of[s], self.last_use[s]
+            moves.append((s, t))
+        evicted_keys = [self.key_of[s] for s in evicted]
+        self.C, self.key_of, self.last_use = new_C, key_of, last_use
+        self.slot_of = {key: s for s, key in enumerate(key_of) if key is not None}
+        return dict(evicted=evicted_keys, moves=moves)
 
     def snapshot(self):
         """(key_of, last_use) copies, for comparisons with the device table."""

@@ -99,6 +99,26 @@ class ListLRU:
         return out, ev
 
 
+    def resize(self, new_C):
+        # the new_C most recent keys survive; a surviving slot index below
+        # new_C stays, the others move (ascending old slot) to the lowest free
+        # indices below new_C
+        n_ev = max(0, len(self.order) - new_C)
+        for key in self.order[:n_ev]:
+            del self.slot[key]
+        self.order = self.order[n_ev:]
+        stay = {key: s for key, s in self.slot.items() if s < new_C}
+        movers = sorted((s, key) for key, s in self.slot.items() if s >= new_C)
+        taken = set(stay.values())
+        holes = [s for s in range(new_C) if s not in taken]
+        for (s, key), t in zip(movers, holes):
+            stay[key] = t
+        self.slot = stay
+        used = set(stay.values())
+        self.free = [s for s in range(new_C) if s not in used]
+        self.C = new_C
+
+
 def _random_calls(rng, L, E, k, ncalls, maxT):
     calls = []
     for _ in range(ncalls):
@@ -231,3 +251,73 @@ def test_prefill_staging_slots_and_evictions():
     assert list(r["slot"]) == [7, 5, 4, 7] and r["evictions"] == 0
     # a decode access afterwards takes the lowest free slot
     assert pool.resolve_wave(1, np.array([[9]]))["stream"] == [(9, 0)]
+
+
+@settings(max_examples=60, deadline=None)
+@given(seed=st.integers(0, 10_000), C=st.integers(3, 12), share=st.sampled_from([0.0, 0.3]))
+def test_resize_matches_independent_list_lru(seed, C, share):
+    """Random traces interleaved with random grows and shrinks: decisions,
+    slots and evictions equal the list model's, and after every resize the
+    residents are the most recently used keys that fit."""
+    rng = np.random.default_rng(seed)
+    k = int(rng.integers(1, 3))
+    calls = _random_calls(rng, L=3, E=9, k=k, ncalls=30, maxT=3)
+    pool, ref = LRUPool(C), ListLRU(C)
+    for i, (layer, sel) in enumerate(calls):
+        if i % 5 == 4:
+            newC = int(rng.integers(max(k, 2), 14))
+            recent = list(ref.order)[-newC:]
+            r = pool.resize(newC)
+            ref.resize(newC)
+            assert sorted(pool.slot_of.items()) == sorted(ref.slot.items())
+            assert set(pool.slot_of) == set(recent)
+            assert all(s < newC for s in pool.slot_of.values())
+            assert all(key not in pool.slot_of for key in r["evicted"])
+        for t0, t1 in split_waves(sel, pool.C):
+            got = pool.resolve_wave(layer, sel[t0:t1], share)
+            exp, ev = ref.wave(layer, [int(v) for v in sel[t0:t1].reshape(-1)], share)
+            assert list(zip(got["flag"], got["slot"])) == exp
+            assert got["evictions"] == ev
+
+
+def test_resize_is_textbook_lru_with_a_changing_capacity():
+    """T = k = 1 calls make the pool textbook LRU; a capacity change keeps the
+    most recently used keys (an OrderedDict-based recency list, no slots)."""
+    from collections import OrderedDict
+
+    rng = np.random.default_rng(7)
+    pool = LRUPool(4)
+    lru, cap = OrderedDict(), 4
+    for i in range(400):
+        if i % 37 == 36:
+            cap = int(rng.integers(1, 8))
+            pool.resize(cap)
+            while len(lru) > cap:
+                lru.popitem(last=False)
+        e = int(rng.zipf(1.4) % 10)
+        r = pool.resolve_wave(0, np.array([[e]]))
+        hit = e in lru
+        assert (r["flag"][0] == HIT) == hit, i
+        if hit:
+            lru.move_to_end(e)
+        else:
+            if len(lru) >= cap:
+                lru.popitem(last=False)
+            lru[e] = True
+        assert set(k[1] for k in pool.slot_of) == set(lru), i
+
+
+def test_resize_hand_worked():
+    """Five residents with last uses 10..14 in slots 0..4 of 6 slots:
+    shrinking to 3 keeps the keys used at 12, 13, 14; the one in slot 2 stays,
+    the ones in slots 3 and 4 move to slots 0 and 1; growing to 8 moves nothing."""
+    pool = LRUPool(6)
+    for s, (e, last) in enumerate([(5, 10), (6, 11), (7, 12), (8, 13), (9, 14)]):
+        pool.key_of[s], pool.last_use[s] = (0, e), last
+        pool.slot_of[(0, e)] = s
+    r = pool.resize(3)
+    assert r["evicted"] == [(0, 5), (0, 6)]
+    assert r["moves"] == [(3, 0), (4, 1)]
+    assert pool.key_of == [(0, 8), (0, 9), (0, 7)] and pool.last_use == [13, 14, 12]
+    r = pool.resize(8)
+    assert r == dict(evicted=[], moves=[]) and pool.key_of[3:] == [None] * 5
