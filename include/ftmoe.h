@@ -165,6 +165,23 @@ int ft_moe_last_misses(const ft_moe_pool *p, int32_t *stream_expert, int32_t *st
 int ft_moe_pool_table(ft_moe_pool *p, int32_t *slot_key, uint64_t *slot_last, uint64_t *clock,
                       int64_t *slots);
 
+/* Change the number of pool slots at runtime, without reloading weights (the
+ * pages: VRAM is re-allocated between the expert cache and other memory while
+ * the engine runs -- dev.to "FreeToken uses bandwidth-adaptive CPU-GPU
+ * co-execution on your desktop", section "Memory that moves while the engine
+ * runs").  The new_slots most recently used residents survive (a shrink evicts
+ * the least recently used); a survivor keeps its slot when the slot still
+ * exists, the others, in ascending old slot, move to the lowest free slots
+ * below new_slots (device-to-device copies).  Last uses and the clock are
+ * unchanged; counters are not changed.  Synchronises the device.  A new slot
+ * arena is allocated before the old one is freed (both exist for a moment);
+ * if an allocation fails the pool is unchanged and FT_E_OOM_DEVICE is
+ * returned.  Requires top_k <= new_slots <= 65536 (FT_E_INVALID) and no
+ * prefill chunk in progress (FT_E_STATE).  Returns FT_WARN_STAGING_SMALL when
+ * the new pool cannot hold two staged layers.  ft_moe_last_misses still
+ * reports the call before the resize (its slot numbers may have moved). */
+int ft_moe_resize_pool(ft_moe_pool *p, int64_t new_slots);
+
 /* Grow the per-call work buffers for calls of up to max_tokens tokens now
  * (synchronises the device when it grows them; a call that needs no growth
  * allocates nothing; the buffers hold at least 64 tokens).  Needed before

@@ -34,7 +34,7 @@ FT_STAGES = ["router", "topk", "resolve", "ffn_gateup", "ffn_down", "combine", "
 EXPORTED = ["ft_moe_init_pool", "ft_moe_layer_forward", "ft_moe_pool_stats", "ft_moe_last_misses",
             "ft_moe_pool_table", "ft_moe_set_hybrid_share", "ft_moe_host_expert_rate",
             "ft_moe_set_profiling", "ft_moe_profile_read", "ft_moe_destroy_pool", "ft_moe_last_error",
-            "ft_moe_reserve"]
+            "ft_moe_reserve", "ft_moe_resize_pool"]
 
 
 class ft_moe_config(ctypes.Structure):
@@ -102,6 +102,8 @@ def lib() -> ctypes.CDLL:
     L.ft_moe_pool_table.argtypes = [P, I32P, ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint64),
                                     ctypes.POINTER(ctypes.c_int64)]
     L.ft_moe_pool_table.restype = ctypes.c_int
+    L.ft_moe_resize_pool.argtypes = [P, ctypes.c_int64]
+    L.ft_moe_resize_pool.restype = ctypes.c_int
     L.ft_moe_reserve.argtypes = [P, ctypes.c_int32]
     L.ft_moe_reserve.restype = ctypes.c_int
     L.ft_moe_set_hybrid_share.argtypes = [P, ctypes.c_double]
@@ -218,6 +220,11 @@ def ft_moe_pool_table(pool, slots: int):
                                    last.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), ctypes.byref(clock),
                                    ctypes.byref(n)))
     return key, last, clock.value
+
+
+def ft_moe_resize_pool(pool, new_slots: int) -> int:
+    """Returns FT_OK or FT_WARN_STAGING_SMALL."""
+    return _check(lib().ft_moe_resize_pool(pool, int(new_slots)), allow_warn=True)
 
 
 def ft_moe_reserve(pool, max_tokens: int):

@@ -1172,6 +1172,112 @@ int ft_moe_pool_table(ft_moe_pool* p, int32_t* slot_key, uint64_t* slot_last, ui
   return FT_OK;
 }
 
+// Elastic resize (the pages: VRAM moves between the expert cache and other
+// memory while the engine runs -- dev.to article "FreeToken uses
+// bandwidth-adaptive CPU-GPU co-execution on your desktop", section "Memory
+// that moves while the engine runs").  The new_slots most recently used
+// residents survive; a survivor keeps its slot if it still exists, the others
+// (ascending old slot) move to the lowest free slots below new_slots.  Last
+// uses and the clock are unchanged.  Everything new is allocated before the
+// pool changes, so a failed allocation leaves the pool as it was.
+int ft_moe_resize_pool(ft_moe_pool* p, int64_t new_slots) {
+  if (!p) {
+    set_error("NULL pool");
+    return FT_E_INVALID;
+  }
+  if (new_slots < p->k || new_slots > kMaxSlots) {
+    set_error("pool of %lld slots: need top_k = %d <= slots <= %d", (long long)new_slots, p->k, kMaxSlots);
+    return FT_E_INVALID;
+  }
+  if (p->prefill_next != 0) {
+    set_error("resize while a prefill chunk is at layer %d", p->prefill_next);
+    return FT_E_STATE;
+  }
+  DeviceGuard dg(p->device);
+  FT_HIP_CHECK(hipDeviceSynchronize());
+  const int64_t C = p->C, NC = new_slots, LE = int64_t(p->L) * p->E;
+  std::vector<int32_t> key(C), k2s(LE);
+  std::vector<uint64_t> last(C);
+  FT_HIP_CHECK(hipMemcpy(key.data(), p->tab.slot_key, size_t(C) * 4, hipMemcpyDeviceToHost));
+  FT_HIP_CHECK(hipMemcpy(last.data(), p->tab.slot_last, size_t(C) * 8, hipMemcpyDeviceToHost));
+  FT_HIP_CHECK(hipMemcpy(k2s.data(), p->tab.key2slot, size_t(LE) * 4, hipMemcpyDeviceToHost));
+
+  std::vector<int64_t> res;
+  for (int64_t sl = 0; sl < C; ++sl)
+    if (key[sl] >= 0) res.push_back(sl);
+  // ties in last use go to the lower slot, as in the victim order of a call
+  std::sort(res.begin(), res.end(),
+            [&](int64_t a, int64_t b) { return last[a] != last[b] ? last[a] < last[b] : a < b; });
+  const size_t n_ev = res.size() > size_t(NC) ? res.size() - size_t(NC) : 0;
+  std::vector<int64_t> keep, move;
+  for (size_t i = n_ev; i < res.size(); ++i) (res[i] < NC ? keep : move).push_back(res[i]);
+  std::sort(keep.begin(), keep.end());
+  std::sort(move.begin(), move.end());
+  std::vector<int32_t> nkey(NC, -1);
+  std::vector<uint64_t> nlast(NC, 0);
+  for (int64_t sl : keep) {
+    nkey[sl] = key[sl];
+    nlast[sl] = last[sl];
+  }
+  std::vector<std::pair<int64_t, int64_t>> moves;  // old slot -> new slot
+  {
+    int64_t hole = 0;
+    for (int64_t sl : move) {
+      while (nkey[hole] >= 0) ++hole;
+      nkey[hole] = key[sl];
+      nlast[hole] = last[sl];
+      moves.emplace_back(sl, hole);
+      ++hole;
+    }
+  }
+  for (size_t i = 0; i < n_ev; ++i) k2s[key[res[i]]] = -1;
+  for (auto& mv : moves) k2s[key[mv.first]] = int32_t(mv.second);
+  // recency order: free slots ascending, then residents by last use
+  std::vector<int32_t> order;
+  for (int64_t sl = 0; sl < NC; ++sl)
+    if (nkey[sl] < 0) order.push_back(int32_t(sl));
+  {
+    std::vector<int32_t> r;
+    for (int64_t sl = 0; sl < NC; ++sl)
+      if (nkey[sl] >= 0) r.push_back(int32_t(sl));
+    std::sort(r.begin(), r.end(),
+              [&](int32_t a, int32_t b) { return nlast[a] != nlast[b] ? nlast[a] < nlast[b] : a < b; });
+    order.insert(order.end(), r.begin(), r.end());
+  }
+
+  // new device memory first
+  uint8_t* arena = nullptr;
+  int32_t *sk = nullptr, *l0 = nullptr, *l1 = nullptr;
+  uint64_t* sla = nullptr;
+  int rc;
+  if ((rc = dev_alloc(&arena, NC * p->slot_bytes)) || (rc = dev_alloc(&sk, NC)) || (rc = dev_alloc(&sla, NC)) ||
+      (rc = dev_alloc(&l0, NC)) || (rc = dev_alloc(&l1, NC))) {
+    hipFree(arena); hipFree(sk); hipFree(sla); hipFree(l0); hipFree(l1);
+    return rc;
+  }
+  for (int64_t sl : keep)
+    FT_HIP_CHECK(hipMemcpyAsync(arena + sl * p->slot_bytes, p->arena + sl * p->slot_bytes, size_t(p->slot_bytes),
+                                hipMemcpyDeviceToDevice, nullptr));
+  for (auto& mv : moves)
+    FT_HIP_CHECK(hipMemcpyAsync(arena + mv.second * p->slot_bytes, p->arena + mv.first * p->slot_bytes,
+                                size_t(p->slot_bytes), hipMemcpyDeviceToDevice, nullptr));
+  FT_HIP_CHECK(hipMemcpy(sk, nkey.data(), size_t(NC) * 4, hipMemcpyHostToDevice));
+  FT_HIP_CHECK(hipMemcpy(sla, nlast.data(), size_t(NC) * 8, hipMemcpyHostToDevice));
+  FT_HIP_CHECK(hipMemcpy(l0, order.data(), size_t(NC) * 4, hipMemcpyHostToDevice));
+  FT_HIP_CHECK(hipMemcpy(p->tab.key2slot, k2s.data(), size_t(LE) * 4, hipMemcpyHostToDevice));
+  FT_HIP_CHECK(hipMemset(p->tab.lru_cur, 0, 4));
+  FT_HIP_CHECK(hipDeviceSynchronize());
+  hipFree(p->arena); hipFree(p->tab.slot_key); hipFree(p->tab.slot_last); hipFree(p->tab.lru[0]);
+  hipFree(p->tab.lru[1]);
+  p->arena = arena;
+  p->tab.slot_key = sk;
+  p->tab.slot_last = sla;
+  p->tab.lru[0] = l0;
+  p->tab.lru[1] = l1;
+  p->C = NC;
+  return NC < 2 * int64_t(p->E) ? FT_WARN_STAGING_SMALL : FT_OK;
+}
+
 int ft_moe_reserve(ft_moe_pool* p, int32_t max_tokens) {
   if (!p || max_tokens < 0) {
     set_error("bad pool or token count");

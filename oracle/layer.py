@@ -100,7 +100,7 @@ class OracleLayerStack:
                       evictions=r["evictions"], bytes_h2d=E * eb)
         else:
             st = dict(pair_hits=0, expert_hits=0, expert_misses=0, cpu_misses=0, evictions=0, bytes_h2d=0)
-            for (t0, t1) in split_waves(sel, self.C):
+            for (t0, t1) in split_waves(sel, self.pool.C):
                 r = self.pool.resolve_wave(layer, sel[t0:t1], self.share)
                 flag[t0 * k:t1 * k] = r["flag"]
                 slot[t0 * k:t1 * k] = r["slot"]
