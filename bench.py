@@ -367,6 +367,14 @@ def main():
             if b == 1:
                 extras["graph_tokens_per_s_batch1"] = measure_graph(ft, torch, pool, xb, bias_of, L, 1, 0, 16, dev)
         extras["graph_tokens_per_s_batch16"] = measure_graph(ft, torch, pool, x_all, bias_of, L, B, 0, 16, dev)
+        # the one-time strategy choice at this batch (measured, not applied)
+        rep = ft.ft_moe_measure_mode(pool, B, apply=False)
+        fm = sorted({f for f in w.layer_fmt})
+        extras["mode_choice"] = {
+            "mode": ["offload", "hybrid", "fused"][rep["mode"]], "share": rep["share"],
+            "t_stream_ms": rep["t_stream"] * 1e3, "t_cpu_ms": rep["t_cpu"] * 1e3, "tokens": rep["tokens"],
+            **{f"{k}_GBps_fmt{f}": rep[f"{k}_bytes_per_s"][f] / 1e9 for k in ("h2d", "gpu", "cpu") for f in fm}}
+        log(f"mode choice: {extras['mode_choice']}")
     ft.ft_moe_destroy_pool(pool)
     if prefill_pool is not None:
         extras["prefill"] = measure_prefill(ft, torch, ms, prefill_pool, dev)

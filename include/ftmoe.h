@@ -200,8 +200,55 @@ int ft_moe_resize_pool(ft_moe_pool *p, int64_t new_slots);
  * capturing, and ft_moe_last_misses reports the most recent eager call. */
 int ft_moe_reserve(ft_moe_pool *p, int32_t max_tokens);
 
-/* Set the hybrid share used by later calls (0..1). */
+/* Set the hybrid share used by later calls (0..1).  0 is the offload
+ * strategy (every miss streams); 1 is the cpu strategy (every miss is computed
+ * on host cores and the pool never changes) -- devpik "FreeToken: Run
+ * Frontier MoE Models on Your Own GPU, and the RAM It Takes", section "Why a
+ * Huge MoE Model Fits on One Consumer GPU". */
 int ft_moe_set_hybrid_share(ft_moe_pool *p, double share);
+
+/* One-time strategy choice from measured rates (mindstudio "FreeToken
+ * Explained: Run 290B+ MoE Models on One Gaming GPU", section "How does the
+ * benchmark decide between hybrid and offload mode?"; the fused case: devpik,
+ * section "Why a Huge MoE Model Fits on One Consumer GPU").  Arrays are
+ * indexed by format FT_FMT_* (index 0 unused); rates are expert-weight bytes
+ * per second, 0 for a format the model does not use. */
+enum { FT_MODE_OFFLOAD = 0, FT_MODE_HYBRID = 1, FT_MODE_FUSED = 2 };
+typedef struct {
+  int32_t tokens;             /* rows per expert the rates were measured at */
+  int32_t layers[4];          /* number of layers in each format */
+  double expert_bytes[4];     /* canonical expert bytes of each format */
+  double h2d_bytes_per_s[4];  /* pinned host -> device copies of experts */
+  double gpu_bytes_per_s[4];  /* the device's grouped expert FFN at `tokens` rows per expert */
+  double cpu_bytes_per_s[4];  /* the host expert path at `tokens` rows */
+  int64_t pool_slots;         /* C */
+  int64_t all_experts;        /* L * E */
+  /* filled by the decision: */
+  double t_stream;            /* s: one miss in every layer, copied and run on the device */
+  double t_cpu;               /* s: the same misses on host cores */
+  int32_t mode;               /* FT_MODE_* */
+  double share;               /* the hybrid share the mode implies (0 unless hybrid) */
+} ft_moe_mode_report;
+
+/* The decision alone (host code, no device work): t_stream = sum over layers
+ * of b/h2d + b/gpu, t_cpu = sum of b/cpu (b = the layer's expert bytes, rates
+ * of the layer's format, layers in format order 1..3); FUSED when pool_slots
+ * >= all_experts; else HYBRID when t_cpu < t_stream, with share =
+ * t_stream / (t_stream + t_cpu), the split at which both paths finish a step's
+ * misses together; else OFFLOAD.  The pages' cpu strategy (share 1) is never
+ * chosen by this rule.  FT_E_INVALID if a used format has a rate <= 0 or
+ * not finite. */
+int ft_moe_decide_mode(ft_moe_mode_report *r);
+
+/* Measure the rates on this machine, then decide (ft_moe_decide_mode).  For
+ * each format the model uses, the first layer of that format supplies up to 8
+ * experts: their blobs are copied from the pinned store into a temporary
+ * device buffer (h2d), the grouped expert FFN runs on them with `tokens` rows
+ * each (gpu), and the host expert path runs on one of them (cpu).  Takes
+ * about a second; synchronises the device; allocates and frees the temporary
+ * buffer; does not touch the slot table or the counters.  apply != 0 sets the
+ * pool's hybrid share to the chosen share.  1 <= tokens <= 64. */
+int ft_moe_measure_mode(ft_moe_pool *p, int32_t tokens, int32_t apply, ft_moe_mode_report *out);
 
 /* Time the host expert path on `tokens` rows of one expert of `layer`
  * (the one-time bandwidth measurement behind the hybrid share); returns

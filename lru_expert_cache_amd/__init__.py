@@ -34,7 +34,9 @@ FT_STAGES = ["router", "topk", "resolve", "ffn_gateup", "ffn_down", "combine", "
 EXPORTED = ["ft_moe_init_pool", "ft_moe_layer_forward", "ft_moe_pool_stats", "ft_moe_last_misses",
             "ft_moe_pool_table", "ft_moe_set_hybrid_share", "ft_moe_host_expert_rate",
             "ft_moe_set_profiling", "ft_moe_profile_read", "ft_moe_destroy_pool", "ft_moe_last_error",
-            "ft_moe_reserve", "ft_moe_resize_pool"]
+            "ft_moe_reserve", "ft_moe_resize_pool", "ft_moe_decide_mode", "ft_moe_measure_mode"]
+
+FT_MODE_OFFLOAD, FT_MODE_HYBRID, FT_MODE_FUSED = 0, 1, 2
 
 
 class ft_moe_config(ctypes.Structure):
@@ -66,6 +68,21 @@ class ft_moe_stats(ctypes.Structure):
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+class ft_moe_mode_report(ctypes.Structure):
+    _fields_ = [("tokens", ctypes.c_int32), ("layers", ctypes.c_int32 * 4), ("expert_bytes", ctypes.c_double * 4),
+                ("h2d_bytes_per_s", ctypes.c_double * 4), ("gpu_bytes_per_s", ctypes.c_double * 4),
+                ("cpu_bytes_per_s", ctypes.c_double * 4), ("pool_slots", ctypes.c_int64),
+                ("all_experts", ctypes.c_int64), ("t_stream", ctypes.c_double), ("t_cpu", ctypes.c_double),
+                ("mode", ctypes.c_int32), ("share", ctypes.c_double)]
+
+    def as_dict(self):
+        d = {}
+        for n, _ in self._fields_:
+            v = getattr(self, n)
+            d[n] = list(v) if isinstance(v, ctypes.Array) else v
+        return d
 
 
 class ft_moe_profile(ctypes.Structure):
@@ -102,6 +119,10 @@ def lib() -> ctypes.CDLL:
     L.ft_moe_pool_table.argtypes = [P, I32P, ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint64),
                                     ctypes.POINTER(ctypes.c_int64)]
     L.ft_moe_pool_table.restype = ctypes.c_int
+    L.ft_moe_decide_mode.argtypes = [ctypes.POINTER(ft_moe_mode_report)]
+    L.ft_moe_decide_mode.restype = ctypes.c_int
+    L.ft_moe_measure_mode.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ft_moe_mode_report)]
+    L.ft_moe_measure_mode.restype = ctypes.c_int
     L.ft_moe_resize_pool.argtypes = [P, ctypes.c_int64]
     L.ft_moe_resize_pool.restype = ctypes.c_int
     L.ft_moe_reserve.argtypes = [P, ctypes.c_int32]
@@ -225,6 +246,29 @@ def ft_moe_pool_table(pool, slots: int):
 def ft_moe_resize_pool(pool, new_slots: int) -> int:
     """Returns FT_OK or FT_WARN_STAGING_SMALL."""
     return _check(lib().ft_moe_resize_pool(pool, int(new_slots)), allow_warn=True)
+
+
+def ft_moe_decide_mode(report: dict) -> dict:
+    """The decision alone (host code): report holds the rates as returned by
+    ft_moe_measure_mode; returns it with t_stream, t_cpu, mode and share."""
+    r = ft_moe_mode_report()
+    for n, _ in r._fields_:
+        if n in report:
+            v = report[n]
+            if isinstance(getattr(r, n), ctypes.Array):
+                arr = getattr(r, n)
+                for i, x in enumerate(v):
+                    arr[i] = x
+            else:
+                setattr(r, n, v)
+    _check(lib().ft_moe_decide_mode(ctypes.byref(r)))
+    return r.as_dict()
+
+
+def ft_moe_measure_mode(pool, tokens: int, apply: bool = False) -> dict:
+    r = ft_moe_mode_report()
+    _check(lib().ft_moe_measure_mode(pool, int(tokens), int(bool(apply)), ctypes.byref(r)))
+    return r.as_dict()
 
 
 def ft_moe_reserve(pool, max_tokens: int):

@@ -1312,6 +1312,183 @@ int ft_moe_host_expert_rate(ft_moe_pool* p, int32_t layer, int32_t tokens, int32
   return FT_OK;
 }
 
+int ft_moe_decide_mode(ft_moe_mode_report* r) {
+  if (!r) {
+    set_error("NULL report");
+    return FT_E_INVALID;
+  }
+  double ts = 0.0, tc = 0.0;
+  for (int f = 1; f <= 3; ++f) {
+    if (r->layers[f] < 0) {
+      set_error("negative layer count for format %d", f);
+      return FT_E_INVALID;
+    }
+    if (r->layers[f] == 0) continue;
+    const double b = r->expert_bytes[f], h = r->h2d_bytes_per_s[f], g = r->gpu_bytes_per_s[f],
+                 c = r->cpu_bytes_per_s[f];
+    if (!(b > 0.0) || !(h > 0.0) || !(g > 0.0) || !(c > 0.0) || !std::isfinite(b) || std::isnan(h) ||
+        std::isnan(g) || std::isnan(c)) {
+      set_error("format %d: expert bytes and rates must be positive", f);
+      return FT_E_INVALID;
+    }
+    for (int l = 0; l < r->layers[f]; ++l) {
+      ts += b / h + b / g;
+      tc += b / c;
+    }
+  }
+  r->t_stream = ts;
+  r->t_cpu = tc;
+  if (r->pool_slots >= r->all_experts) {
+    r->mode = FT_MODE_FUSED;
+    r->share = 0.0;
+  } else if (tc < ts) {
+    r->mode = FT_MODE_HYBRID;
+    r->share = ts / (ts + tc);
+  } else {
+    r->mode = FT_MODE_OFFLOAD;
+    r->share = 0.0;
+  }
+  return FT_OK;
+}
+
+int ft_moe_measure_mode(ft_moe_pool* p, int32_t tokens, int32_t apply, ft_moe_mode_report* out) {
+  if (!p || !out || tokens < 1 || tokens > 64) {
+    set_error("bad arguments (need a pool, a report and 1 <= tokens <= 64)");
+    return FT_E_INVALID;
+  }
+  if (p->prefill_next != 0) {
+    set_error("mode measurement while a prefill chunk is at layer %d", p->prefill_next);
+    return FT_E_STATE;
+  }
+  DeviceGuard dg(p->device);
+  ft_moe_mode_report r{};
+  r.tokens = tokens;
+  r.pool_slots = p->C;
+  r.all_experts = int64_t(p->L) * p->E;
+  const int n = std::min(p->E, 8), T = tokens, H = p->H;
+  int rc = read_pending_misses(p);
+  if (rc) return rc;
+  if ((rc = ensure_capacity(p, (n * T + p->k - 1) / p->k))) return rc;
+  FT_HIP_CHECK(hipDeviceSynchronize());
+  uint8_t* tmp = nullptr;
+  uint16_t* xd = nullptr;
+  if ((rc = dev_alloc(&tmp, int64_t(n) * p->slot_bytes)) || (rc = dev_alloc(&xd, int64_t(T) * H))) {
+    hipFree(tmp);
+    return rc;
+  }
+  hipStream_t s = p->copy[0];
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  struct Cleanup {
+    hipEvent_t& e0;
+    hipEvent_t& e1;
+    uint8_t* tmp;
+    uint16_t* xd;
+    ~Cleanup() {
+      if (e0) hipEventDestroy(e0);
+      if (e1) hipEventDestroy(e1);
+      hipFree(tmp);
+      hipFree(xd);
+    }
+  } guard{e0, e1, tmp, xd};
+  FT_HIP_CHECK(hipEventCreate(&e0));
+  FT_HIP_CHECK(hipEventCreate(&e1));
+  {
+    std::vector<uint16_t> ones(size_t(T) * H, 0x3F80);  // bf16 1.0
+    FT_HIP_CHECK(hipMemcpy(xd, ones.data(), ones.size() * 2, hipMemcpyHostToDevice));
+  }
+  const int32_t prof_saved = p->prof_mask;
+  p->prof_mask = 0;
+  struct Restore {
+    ft_moe_pool* p;
+    int32_t m;
+    ~Restore() { p->prof_mask = m; }
+  } restore{p, prof_saved};
+  constexpr int kReps = 3;
+  double sec = 0.0;
+  auto timed = [&](auto&& body) -> int {  // sec = seconds per repetition, after one warm-up
+    body();
+    FT_HIP_CHECK(hipEventRecord(e0, s));
+    for (int i = 0; i < kReps; ++i) body();
+    FT_HIP_CHECK(hipEventRecord(e1, s));
+    FT_HIP_CHECK(hipEventSynchronize(e1));
+    float ms = 0.0f;
+    FT_HIP_CHECK(hipEventElapsedTime(&ms, e0, e1));
+    sec = std::max(double(ms), 1e-6) * 1e-3 / kReps;
+    return FT_OK;
+  };
+  for (int f = 1; f <= 3; ++f) {
+    int layer = -1;
+    for (int l = 0; l < p->L; ++l)
+      if (p->fmt[l] == f) {
+        if (layer < 0) layer = l;
+        ++r.layers[f];
+      }
+    if (layer < 0) continue;
+    const int64_t b = p->canon_bytes[f];
+    r.expert_bytes[f] = double(b);
+    // pinned host -> device
+    hipError_t cerr = hipSuccess;
+    if ((rc = timed([&]() {
+           for (int e = 0; e < n; ++e) {
+             const hipError_t ce =
+                 hipMemcpyAsync(tmp + e * p->slot_bytes, p->host_store + p->key_off[int64_t(layer) * p->E + e],
+                                size_t(b), hipMemcpyHostToDevice, s);
+             if (cerr == hipSuccess) cerr = ce;
+           }
+         })))
+      return rc;
+    FT_HIP_CHECK(cerr);
+    r.h2d_bytes_per_s[f] = double(n) * double(b) / sec;
+    // the device's grouped FFN on the n experts, T rows each
+    {
+      std::vector<GroupDesc> g(n);
+      std::vector<int32_t> gl(n), rt(size_t(n) * T);
+      std::vector<float> rw(size_t(n) * T, 1.0f);
+      for (int e = 0; e < n; ++e) {
+        g[e].wptr = reinterpret_cast<uint64_t>(tmp + e * p->slot_bytes);
+        g[e].row_begin = e * T;
+        g[e].row_count = T;
+        g[e].expert = e;
+        g[e].slot = -1;
+        gl[e] = e;
+        for (int t = 0; t < T; ++t) rt[size_t(e) * T + t] = t;
+      }
+      FT_HIP_CHECK(hipMemcpy(p->groups, g.data(), g.size() * sizeof(GroupDesc), hipMemcpyHostToDevice));
+      FT_HIP_CHECK(hipMemcpy(p->glist, gl.data(), gl.size() * 4, hipMemcpyHostToDevice));
+      FT_HIP_CHECK(hipMemcpy(p->row_tok, rt.data(), rt.size() * 4, hipMemcpyHostToDevice));
+      FT_HIP_CHECK(hipMemcpy(p->row_w, rw.data(), rw.size() * 4, hipMemcpyHostToDevice));
+    }
+    int frc = FT_OK;
+    if ((rc = timed([&]() {
+           if (frc == FT_OK) frc = run_ffn(p, layer, xd, 0, n, nullptr, s, n, double(n) * T, nullptr, T);
+         })))
+      return rc;
+    if (frc) return frc;
+    r.gpu_bytes_per_s[f] = double(n) * double(b) / sec;
+    // the host expert path on one of them
+    {
+      std::vector<uint16_t> x(size_t(T) * H, 0x3F80), o(size_t(T) * H);
+      std::vector<float> w(T, 1.0f);
+      const uint8_t* blob = p->host_store + p->key_off[int64_t(layer) * p->E];
+      host_expert(p->lay[f], blob, x.data(), w.data(), T, o.data(), p->cpu_threads);  // warm-up
+      const auto t0 = std::chrono::steady_clock::now();
+      int it = 0;
+      double el = 0.0;
+      do {
+        host_expert(p->lay[f], blob, x.data(), w.data(), T, o.data(), p->cpu_threads);
+        ++it;
+        el = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
+      } while (it < kReps && el < 0.25);
+      r.cpu_bytes_per_s[f] = double(b) * it / std::max(el, 1e-9);
+    }
+  }
+  FT_HIP_CHECK(hipDeviceSynchronize());
+  if ((rc = ft_moe_decide_mode(&r))) return rc;
+  if (apply) p->share = r.share;
+  *out = r;
+  return FT_OK;
+}
+
 int ft_moe_set_profiling(ft_moe_pool* p, int32_t stage_mask) {
   if (!p) {
     set_error("NULL pool");
