@@ -77,7 +77,7 @@ class OracleLayerStack:
         return self.deq.get(("s", layer), f, lambda: ms.shared_blob(w, layer), w.hidden, w.inter)
 
     def forward(self, layer: int, x_bits: np.ndarray, bias: Optional[np.ndarray],
-                prefill: bool = False, outputs: bool = True, out_tokens=None):
+                prefill: bool = False, outputs: bool = True, out_tokens=None, hit_d2d: bool = False):
         """Run one layer call; x_bits uint16 [T,H] bf16 bit patterns.
 
         out_tokens: compute the output only for these token indices (each
@@ -93,11 +93,11 @@ class OracleLayerStack:
         slot = np.empty(T * k, np.int32)
         waves = []
         if prefill:
-            r = self.pool.stage_layer(layer, E, sel, w.num_layers)
+            r = self.pool.stage_layer(layer, E, sel, w.num_layers, hit_d2d=hit_d2d)
             flag[:], slot[:] = r["flag"], r["slot"]
             waves.append(dict(t0=0, t1=T, **r))
-            st = dict(pair_hits=0, expert_hits=0, expert_misses=E, cpu_misses=0,
-                      evictions=r["evictions"], bytes_h2d=E * eb)
+            st = dict(pair_hits=r["pair_hits"], expert_hits=r["expert_hits"], expert_misses=r["expert_misses"],
+                      cpu_misses=0, evictions=r["evictions"], bytes_h2d=len(r["stream"]) * eb)
         else:
             st = dict(pair_hits=0, expert_hits=0, expert_misses=0, cpu_misses=0, evictions=0, bytes_h2d=0)
             for (t0, t1) in split_waves(sel, self.pool.C):

@@ -139,12 +139,21 @@ class LRUPool:
                     pair_hits=int((flag == HIT).sum()), expert_hits=len(hits),
                     expert_misses=len(misses), cpu_misses=len(cpu), evictions=evictions)
 
-    def stage_layer(self, layer: int, num_experts: int, sel: np.ndarray, num_layers: int):
+    def stage_layer(self, layer: int, num_experts: int, sel: np.ndarray, num_layers: int,
+                    hit_d2d: bool = False):
         """Prefill staging of one layer into half (layer mod 2) of slots [0, 2E).
 
         The call for layer l also starts the copy of layer l+1 into the other
         half (layer N+1 copies while layer N computes), so both halves lose
         their LRU residents here (the second one only if l+1 < L).
+
+        hit_d2d: experts of the layer already resident in the pool are not
+        copied again; only the others cross PCIe (devpik article, "Long
+        Prompts Are the Bottleneck": the prefill option that skips experts
+        already in the GPU cache).  Reading: a resident expert is used from
+        its pool slot (its pairs are HIT with that slot), residency is taken
+        after the staging halves are cleared (so it lies outside them), and
+        the LRU state is untouched as in plain staging.
         """
         E = num_experts
         assert self.C >= 2 * E
@@ -159,18 +168,23 @@ class LRUPool:
                     self.key_of[s] = None
                     self.last_use[s] = None
                     evictions += 1
+        resident = {}
+        if hit_d2d:
+            for e in range(E):
+                if (layer, e) in self.slot_of:
+                    resident[e] = self.slot_of[(layer, e)]
         pairs = np.asarray(sel).reshape(-1)
-        flag = np.full(pairs.size, MISS_STREAM, np.uint8)
-        slot = (base + pairs).astype(np.int32)
+        flag = np.array([HIT if int(e) in resident else MISS_STREAM for e in pairs], np.uint8)
+        slot = np.array([resident.get(int(e), base + int(e)) for e in pairs], np.int32)
         D = []
         seen = set()
         for e in pairs:
             if int(e) not in seen:
                 seen.add(int(e))
                 D.append(int(e))
-        return dict(flag=flag, slot=slot, stream=[(e, base + e) for e in range(E)], cpu=[], D=D,
-                    pair_hits=0, expert_hits=0, expert_misses=E, cpu_misses=0,
-                    evictions=evictions)
+        return dict(flag=flag, slot=slot, stream=[(e, base + e) for e in range(E) if e not in resident], cpu=[],
+                    D=D, pair_hits=int((flag == HIT).sum()), expert_hits=len(resident),
+                    expert_misses=E - len(resident), cpu_misses=0, evictions=evictions)
 
     def resize(self, new_capacity: int):
         """Elastic resize of the pool at runtime (the pages: VRAM is

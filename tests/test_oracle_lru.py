@@ -253,6 +253,68 @@ def test_prefill_staging_slots_and_evictions():
     assert pool.resolve_wave(1, np.array([[9]]))["stream"] == [(9, 0)]
 
 
+def test_prefill_hit_d2d_hand_worked():
+    # C = 12, E = 4: the staging region is [0, 8)
+    pool = LRUPool(12)
+    pool.resolve_wave(0, np.array([[0]]))          # (0,0) -> slot 0 (inside staging)
+    pool.resolve_wave(0, np.array([[1]]))          # (0,1) -> slot 1 (inside staging)
+    for e in range(6):
+        pool.resolve_wave(2, np.array([[e]]))      # (2,0..5) -> slots 2..7
+    pool.resolve_wave(0, np.array([[2]]))          # (0,2) -> slot 8 (beyond staging)
+    sel = np.array([[2, 0], [3, 2]])
+    r = pool.stage_layer(0, 4, sel, num_layers=2, hit_d2d=True)
+    # residents inside the staging region are evicted before residency is taken
+    assert r["evictions"] == 8
+    assert list(r["slot"]) == [8, 0, 3, 8]
+    assert list(r["flag"]) == [HIT, MISS_STREAM, MISS_STREAM, HIT]
+    assert r["stream"] == [(0, 0), (1, 1), (3, 3)]
+    assert (r["pair_hits"], r["expert_hits"], r["expert_misses"]) == (2, 1, 3)
+    assert pool.resident(0, 2) and not pool.resident(0, 0)
+
+
+def test_prefill_hit_d2d_uses_resident_slots():
+    # E = 4, C = 12: staging [0, 8); keys (1,2) and (1,0) resident at slots 8 and 9
+    pool = LRUPool(12)
+    for e in range(8):
+        pool.resolve_wave(0, np.array([[e]]))      # keys (0,0..7) fill slots 0..7
+    pool.resolve_wave(1, np.array([[2]]))          # -> slot 8
+    pool.resolve_wave(1, np.array([[0]]))          # -> slot 9
+    table_before = pool.snapshot()
+    plain = LRUPool(12)
+    plain.key_of, plain.last_use, plain.clock = list(table_before[0]), list(table_before[1]), table_before[2]
+    plain.slot_of = {k: s for s, k in enumerate(table_before[0]) if k is not None}
+    sel = np.array([[0, 3], [2, 0], [1, 2]])
+    r0 = pool.stage_layer(0, 4, sel, num_layers=2, hit_d2d=True)
+    assert r0["evictions"] == 8 and r0["expert_hits"] == 0
+    p0 = plain.stage_layer(0, 4, sel, num_layers=2)
+    r1 = pool.stage_layer(1, 4, sel, num_layers=2, hit_d2d=True)
+    # layer 1 half is [4, 8): experts 0 and 2 are used from slots 9 and 8
+    assert list(r1["slot"]) == [9, 7, 8, 9, 5, 8]
+    assert list(r1["flag"]) == [HIT, MISS_STREAM, HIT, HIT, MISS_STREAM, HIT]
+    assert r1["stream"] == [(1, 5), (3, 7)]
+    assert r1["pair_hits"] == 4 and r1["expert_hits"] == 2 and r1["expert_misses"] == 2
+    # the table evolves exactly as under plain staging
+    p1 = plain.stage_layer(1, 4, sel, num_layers=2)
+    assert pool.snapshot() == plain.snapshot()
+    assert p0["evictions"] == r0["evictions"] and p1["evictions"] == r1["evictions"]
+
+
+@given(seed=st.integers(0, 10_000))
+@settings(max_examples=60, deadline=None)
+def test_prefill_hit_d2d_without_residents_is_plain_staging(seed):
+    rng = np.random.default_rng(seed)
+    E, L = 6, 3
+    a, b = LRUPool(2 * E + 3), LRUPool(2 * E + 3)
+    for l in range(L):
+        sel = np.stack([rng.choice(E, 2, replace=False) for _ in range(5)])
+        ra = a.stage_layer(l, E, sel, L, hit_d2d=True)
+        rb = b.stage_layer(l, E, sel, L)
+        for key in ("slot", "flag"):
+            assert np.array_equal(ra[key], rb[key])
+        assert ra["stream"] == rb["stream"] and ra["expert_misses"] == E
+    assert a.snapshot() == b.snapshot()
+
+
 @settings(max_examples=60, deadline=None)
 @given(seed=st.integers(0, 10_000), C=st.integers(3, 12), share=st.sampled_from([0.0, 0.3]))
 def test_resize_matches_independent_list_lru(seed, C, share):
