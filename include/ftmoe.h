@@ -70,7 +70,20 @@ enum {
    * nearest-even, saturating) and both products run on the block-scaled MFMA. */
   FT_ACT_MXFP8 = 1 << 4,     /* x and h as MXFP8 (E4M3) */
   FT_ACT_MXFP4 = 2 << 4,     /* x and h as MXFP4 (E2M1) */
-  FT_ACT_MASK = 0xF << 4
+  FT_ACT_MASK = 0xF << 4,
+  /* Prefill option (devpik "FreeToken: Run Frontier MoE Models on Your Own
+   * GPU, and the RAM It Takes", section "Long Prompts Are the Bottleneck":
+   * skip experts already in the GPU cache so only misses cross PCIe).  An
+   * expert of the layer resident in the pool outside the staging region
+   * [0, 2E) is not copied: its pairs are FT_PAIR_HIT and read the weights
+   * in its pool slot; the others stream into the staging half as usual.
+   * Residency is read once, at layer 0 of the chunk (the device is
+   * synchronised then), and the pool outside the staging region does not
+   * change during a chunk.  Every call of a chunk must carry the same
+   * option (else FT_E_STATE).  Counters: pair hits count the pairs of
+   * resident experts, expert hits the resident experts of the layer, and
+   * bytes H2D the experts copied. */
+  FT_FWD_PREFILL_HIT_D2D = 1 << 8
 };
 
 enum { FT_PAIR_HIT = 0, FT_PAIR_MISS_STREAM = 1, FT_PAIR_MISS_CPU = 2 };

@@ -26,6 +26,7 @@ FT_E_STATE = -5
 
 FT_FMT_MXFP4, FT_FMT_NVFP4, FT_FMT_FP8_B128 = 1, 2, 3
 FT_FWD_DECODE, FT_FWD_PREFILL_STAGED = 0, 1
+FT_FWD_PREFILL_HIT_D2D = 1 << 8
 FT_ACT_BF16, FT_ACT_MXFP8, FT_ACT_MXFP4 = 0 << 4, 1 << 4, 2 << 4
 FT_PAIR_HIT, FT_PAIR_MISS_STREAM, FT_PAIR_MISS_CPU = 0, 1, 2
 

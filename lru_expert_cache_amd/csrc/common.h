@@ -144,6 +144,7 @@ struct ResolveArgs {
   int32_t prof_stages;     // bit i: stage i above is timed in this call
   int32_t fmt;             // weight format of the layer
   int32_t host_wait;       // 1: the host spins on the readback stamp (publish it system-wide)
+  int32_t stage_hits;      // staged calls: 1 = experts resident in the pool run from their slots
 };
 
 // ------------------------------------------------------------ launchers

@@ -120,6 +120,8 @@ struct ft_moe_pool {
 
   int32_t stamp = 0;
   int prefill_next = 0;
+  bool prefill_hit = false;          // the current chunk skips resident experts
+  std::vector<int32_t> prefill_res;  // [L*E] slot of each resident key at chunk start (outside staging), else -1
   uint64_t copy_counter = 0;
   int64_t fault_copy = -1;
 
@@ -497,15 +499,41 @@ int copy_layer_staging(ft_moe_pool* p, int layer) {
   uint8_t* dst = p->arena + int64_t(half) * E * p->slot_bytes;
   const ExpertLayout& L = p->lay[p->fmt[layer]];
   hipEvent_t e0 = prof_begin(p, p->copy_stream);
-  if (p->layer_contig[layer]) {
+  int copied = 0;
+  if (p->prefill_hit) {
+    // runs of consecutive experts that are not resident in the pool
+    const int32_t* res = p->prefill_res.data() + int64_t(layer) * E;
+    for (int e = 0; e < E;) {
+      if (res[e] >= 0) {
+        ++e;
+        continue;
+      }
+      int e1 = e + 1;
+      while (e1 < E && res[e1] < 0) ++e1;
+      if (p->layer_contig[layer]) {
+        FT_HIP_CHECK(hipMemcpyAsync(dst + int64_t(e) * p->slot_bytes, p->host_store + p->key_off[int64_t(layer) * E + e],
+                                    size_t(e1 - e - 1) * p->slot_bytes + size_t(L.bytes), hipMemcpyHostToDevice,
+                                    p->copy_stream));
+      } else {
+        for (int j = e; j < e1; ++j)
+          FT_HIP_CHECK(hipMemcpyAsync(dst + int64_t(j) * p->slot_bytes,
+                                      p->host_store + p->key_off[int64_t(layer) * E + j], size_t(L.bytes),
+                                      hipMemcpyHostToDevice, p->copy_stream));
+      }
+      copied += e1 - e;
+      e = e1;
+    }
+  } else if (p->layer_contig[layer]) {
     FT_HIP_CHECK(hipMemcpyAsync(dst, p->host_store + p->key_off[int64_t(layer) * E], size_t(E) * p->slot_bytes,
                                 hipMemcpyHostToDevice, p->copy_stream));
+    copied = E;
   } else {
     for (int e = 0; e < E; ++e)
       FT_HIP_CHECK(hipMemcpyAsync(dst + int64_t(e) * p->slot_bytes, p->host_store + p->key_off[int64_t(layer) * E + e],
                                   size_t(L.bytes), hipMemcpyHostToDevice, p->copy_stream));
+    copied = E;
   }
-  prof_end(p, FT_STAGE_COPY, e0, p->copy_stream, double(E) * double(p->canon_bytes[p->fmt[layer]]), 0.0);
+  prof_end(p, FT_STAGE_COPY, e0, p->copy_stream, double(copied) * double(p->canon_bytes[p->fmt[layer]]), 0.0);
   FT_HIP_CHECK(hipEventRecord(p->ev_staged[half], p->copy_stream));
   return FT_OK;
 }
@@ -542,7 +570,8 @@ int run_mx_ffn(ft_moe_pool* p, int layer, const void* x, int T, bool fp4, hipStr
   return FT_OK;
 }
 
-int forward_prefill(ft_moe_pool* p, int layer, int T, const void* x, void* out, hipStream_t s, int act) {
+int forward_prefill(ft_moe_pool* p, int layer, int T, const void* x, void* out, hipStream_t s, int act,
+                    bool hit_d2d) {
   const int L = p->L, E = p->E;
   if (act != 0 && p->fmt[layer] != FT_FMT_MXFP4) {
     set_error("MX activation modes need MXFP4 expert weights (layer %d)", layer);
@@ -556,14 +585,33 @@ int forward_prefill(ft_moe_pool* p, int layer, int T, const void* x, void* out, 
     set_error("prefill layer %d out of order (expected 0 or %d)", layer, p->prefill_next);
     return FT_E_STATE;
   }
-  // the whole layer is streamed into its staging half
+  if (layer > 0 && hit_d2d != p->prefill_hit) {
+    set_error("prefill layer %d: the hit-D2D option must match the chunk's layer 0", layer);
+    return FT_E_STATE;
+  }
+  if (layer == 0) {
+    p->prefill_hit = hit_d2d;
+    if (hit_d2d) {
+      // residency outside the staging region, fixed for the whole chunk
+      // (layer 0 clears the staging region; decode calls wait for the chunk)
+      const int64_t LE = int64_t(L) * E;
+      p->prefill_res.resize(size_t(LE));
+      FT_HIP_CHECK(hipStreamSynchronize(s));
+      FT_HIP_CHECK(hipMemcpy(p->prefill_res.data(), p->tab.key2slot, size_t(LE) * 4, hipMemcpyDeviceToHost));
+      for (auto& v : p->prefill_res)
+        if (v < 2 * E) v = -1;
+    }
+  }
+  // the layer's experts are streamed into its staging half (resident ones
+  // are skipped with the hit-D2D option)
   p->last_pending = false;
-  p->last_se.resize(E);
-  p->last_ss.resize(E);
+  p->last_se.clear();
+  p->last_ss.clear();
   p->last_ce.clear();
   for (int e = 0; e < E; ++e) {
-    p->last_se[e] = e;
-    p->last_ss[e] = (layer & 1) * E + e;
+    if (p->prefill_hit && p->prefill_res[int64_t(layer) * E + e] >= 0) continue;
+    p->last_se.push_back(e);
+    p->last_ss.push_back((layer & 1) * E + e);
   }
   // table: the staging halves lose their LRU residents
   FT_HIP_CHECK(launch_stage_table(p->tab, E, int(p->C), layer, L, T * p->k, 0, s));
@@ -584,6 +632,7 @@ int forward_prefill(ft_moe_pool* p, int layer, int T, const void* x, void* out, 
   }
   FT_HIP_CHECK(hipStreamWaitEvent(s, p->ev_staged[layer & 1], 0));
   ResolveArgs ra = resolve_args(p, layer, T, 0, 1);
+  ra.stage_hits = p->prefill_hit ? 1 : 0;
   Ev er = prof_pair(p, s, FT_STAGE_RESOLVE);
   FT_HIP_CHECK(launch_resolve(ra, s, er));
   prof_push(p, FT_STAGE_RESOLVE, er, 0.0, 0.0);
@@ -1021,7 +1070,10 @@ int ft_moe_layer_forward(ft_moe_pool* p, int32_t layer, int32_t num_tokens, cons
     }
     const int mode = flags & FT_FWD_MODE_MASK;
     const int act = (flags & FT_ACT_MASK) >> 4;
-    if (mode > FT_FWD_PREFILL_STAGED || act > 2 || (flags & ~(FT_FWD_MODE_MASK | FT_ACT_MASK))) {
+    const bool hit_d2d = (flags & FT_FWD_PREFILL_HIT_D2D) != 0;
+    if (mode > FT_FWD_PREFILL_STAGED || act > 2 ||
+        (flags & ~(FT_FWD_MODE_MASK | FT_ACT_MASK | FT_FWD_PREFILL_HIT_D2D)) ||
+        (hit_d2d && mode != FT_FWD_PREFILL_STAGED)) {
       set_error("bad flags 0x%x", flags);
       return FT_E_INVALID;
     }
@@ -1074,7 +1126,7 @@ int ft_moe_layer_forward(ft_moe_pool* p, int32_t layer, int32_t num_tokens, cons
       rc = dev_path ? forward_decode_dev(p, layer, T, x_bf16, out_bf16, s)
                     : forward_decode(p, layer, T, x_bf16, out_bf16, s);
     } else {
-      rc = forward_prefill(p, layer, T, x_bf16, out_bf16, s, act);
+      rc = forward_prefill(p, layer, T, x_bf16, out_bf16, s, act, hit_d2d);
     }
     if (rc) return rc;
     if (!capturing) {

@@ -225,8 +225,9 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
   if (decode) {
     cur = *a.tab.lru_cur;
     clk = *a.tab.clock;
-    if (tid < E) k2s = a.tab.key2slot[key0 + tid];
   }
+  const bool use_k2s = decode || a.stage_hits != 0;
+  if (use_k2s && tid < E) k2s = a.tab.key2slot[key0 + tid];
   uint64_t* st = a.tab.stats + int64_t(a.layer) * ST_COUNT;
   uint64_t st0[ST_COUNT];
   double gap0 = 0.0;
@@ -273,7 +274,7 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
     const int i = j * NT + tid;
     pf_key[j] = (decode && i < C) ? a.tab.slot_key[pf_s[j]] : -1;
   }
-  if (decode && tid < E) sm.k2s[tid] = k2s;
+  if (use_k2s && tid < E) sm.k2s[tid] = k2s;
   for (int e = tid; e < E; e += NT) {
     sm.first[e] = 0x7fffffff;
     sm.last[e] = -1;
@@ -363,7 +364,11 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
         atomicOr(&sm.prot[s >> 5], 1u << (s & 31));
       }
     } else {
-      sm.dslot[tid] = (a.layer & 1) * E + e;
+      // staged: a resident expert (outside the staging region, which was
+      // cleared before this kernel) is read from its slot
+      const int s = a.stage_hits ? sm.k2s[e] : -1;
+      hit = s >= 0;
+      sm.dslot[tid] = hit ? s : (a.layer & 1) * E + e;
     }
   }
   int nM;
@@ -568,6 +573,9 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
   const int cnt_d = live_d ? sm.cnt[tid] : 0;
   const Closing cl = block_closing(cls_d == FT_PAIR_MISS_CPU ? cnt_d : 0, cls_d == FT_PAIR_HIT ? cnt_d : 0,
                                    cls_d == FT_PAIR_MISS_STREAM ? cnt_d : 0, cnt_d, g, sm.ired, sm.dred);
+  // staged calls: experts of the layer resident in the pool (not copied)
+  int n_res = 0;
+  if (!decode && a.stage_hits) (void)block_excount(tid < E && sm.k2s[tid] >= 0, sm.wbuf, par, &n_res);
   const int max_rows = shared ? max(cl.max_rows, ntok) : cl.max_rows;
   const int cpu_rows = cl.cpu_rows, hit_pairs = cl.hit_pairs, stream_rows = cl.stream_rows;
   const double min_gap = cl.min_gap;
@@ -618,9 +626,11 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
       d[ST_EVICTIONS] = uint64_t(sm.scal[1]);
       d[ST_BYTES_H2D] = uint64_t(m_str) * uint64_t(a.expert_bytes) + uint64_t(cpu_rows) * uint64_t(a.hidden) * 2ull;
     } else {
-      d[ST_PAIR_MISSES] = uint64_t(P);
-      d[ST_EXPERT_MISSES] = uint64_t(E);
-      d[ST_BYTES_H2D] = uint64_t(E) * uint64_t(a.expert_bytes);
+      d[ST_PAIR_HITS] = uint64_t(hit_pairs);
+      d[ST_PAIR_MISSES] = uint64_t(P - hit_pairs);
+      d[ST_EXPERT_HITS] = uint64_t(n_res);
+      d[ST_EXPERT_MISSES] = uint64_t(E - n_res);
+      d[ST_BYTES_H2D] = uint64_t(E - n_res) * uint64_t(a.expert_bytes);
     }
     d[ST_CALLS] = t0 == 0 ? 1ull : 0ull;
 #pragma unroll

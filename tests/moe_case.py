@@ -39,7 +39,7 @@ class GpuLayerStack:
         b = ms.popularity_bias(self.w, layer, self.w.phase(step))
         return None if b is None else self.torch.from_numpy(b).to(self.dev)
 
-    def forward(self, layer, x_bits, bias_t, prefill=False, act=0):
+    def forward(self, layer, x_bits, bias_t, prefill=False, act=0, hit_d2d=False):
         torch = self.torch
         T, k = x_bits.shape[0], self.w.top_k
         x = torch.from_numpy(x_bits.view(np.int16)).to(self.dev)
@@ -50,6 +50,8 @@ class GpuLayerStack:
                   flag=torch.empty(T * k, dtype=torch.uint8, device=self.dev),
                   row=torch.empty(T * k, dtype=torch.int32, device=self.dev))
         flags = (ft.FT_FWD_PREFILL_STAGED if prefill else ft.FT_FWD_DECODE) | act
+        if hit_d2d:
+            flags |= ft.FT_FWD_PREFILL_HIT_D2D
         ft.ft_moe_layer_forward(self.pool, layer, T, x, bias_t, out, flags, None, tr)
         torch.cuda.synchronize()
         res = {n: t.cpu().numpy() for n, t in tr.items()}
