@@ -157,6 +157,41 @@ def measure_prefill(ft, torch, ms, pool, dev):
     return res
 
 
+def measure_prefill_hits(ft, torch, ms, w, pool, bias_of, dev):
+    """A 4096-token prefill chunk on the decode pool after its decode steps,
+    with FT_FWD_PREFILL_HIT_D2D (experts resident in the pool are read in
+    place, only the others are copied) and without it, on the same residents
+    (a chunk leaves the pool beyond the staging region unchanged)."""
+    T, L = 4096, w.num_layers
+    xs = torch.from_numpy(np.stack([ms.activations(w, l, 5000, T) for l in range(L)]).view(np.int16)).to(dev)
+    out = torch.empty((T, w.hidden), dtype=torch.int16, device=dev)
+    res = {"chunk_tokens": T}
+
+    def chunk(flags):
+        st0 = ft.ft_moe_pool_stats(pool)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for l in range(L):
+            ft.ft_moe_layer_forward(pool, l, T, xs[l], bias_of(0, l), out, flags, None, None)
+        torch.cuda.synchronize()
+        sec = time.perf_counter() - t0
+        st1 = ft.ft_moe_pool_stats(pool)
+        d = {k: st1[k] - st0[k] for k in ("pair_hits", "pair_misses", "expert_hits", "expert_misses", "bytes_h2d")}
+        return sec, d
+
+    plain = ft.FT_FWD_PREFILL_STAGED
+    hit = plain | ft.FT_FWD_PREFILL_HIT_D2D
+    chunk(hit)
+    chunk(plain)
+    for name, flags in (("hit_d2d", hit), ("plain", plain)):
+        sec, d = chunk(flags)
+        res[name] = {"tokens_per_s": T / sec, "chunk_s": sec, "h2d_GB": d["bytes_h2d"] / 1e9,
+                     "pair_hit_rate": d["pair_hits"] / max(d["pair_hits"] + d["pair_misses"], 1),
+                     "experts_copied": d["expert_misses"], "experts_resident": d["expert_hits"]}
+        log(f"[bench] prefill on the decode pool, {name}: {T / sec:.0f} tokens/s, {d['bytes_h2d'] / 1e9:.2f} GB copied")
+    return res
+
+
 def measure_graph(ft, torch, pool, x_all, bias_of, L, B, first, nrep, dev):
     """Tokens/s of a whole decode step (L layer calls) captured once into a
     HIP graph and replayed; each replay's inputs are copied into the captured
@@ -375,6 +410,8 @@ def main():
             "t_stream_ms": rep["t_stream"] * 1e3, "t_cpu_ms": rep["t_cpu"] * 1e3, "tokens": rep["tokens"],
             **{f"{k}_GBps_fmt{f}": rep[f"{k}_bytes_per_s"][f] / 1e9 for k in ("h2d", "gpu", "cpu") for f in fm}}
         log(f"mode choice: {extras['mode_choice']}")
+        if w.pool_slots >= 2 * w.num_experts:
+            extras["prefill_on_decode_pool"] = measure_prefill_hits(ft, torch, ms, w, pool, bias_of, dev)
     ft.ft_moe_destroy_pool(pool)
     if prefill_pool is not None:
         extras["prefill"] = measure_prefill(ft, torch, ms, prefill_pool, dev)
