@@ -283,6 +283,12 @@ typedef struct {
   uint64_t launches[FT_STAGE_COUNT];
 } ft_moe_profile;
 
+/* Name of the kernel (with its compile-time shape) behind the most recent
+ * FT_STAGE_FFN_GATEUP or FT_STAGE_FFN_DOWN launch enqueued by this process,
+ * for reports ("" before the first launch or for other stages).  The string
+ * belongs to the library and changes with the next launch. */
+const char *ft_moe_ffn_kernel_name(int32_t stage);
+
 /* stage_mask: bit FT_STAGE_x set = record events around that stage in later
  * calls (0 = off, (1 << FT_STAGE_COUNT) - 1 = all). */
 int ft_moe_set_profiling(ft_moe_pool *p, int32_t stage_mask);

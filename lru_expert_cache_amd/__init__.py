@@ -35,7 +35,8 @@ FT_STAGES = ["router", "topk", "resolve", "ffn_gateup", "ffn_down", "combine", "
 EXPORTED = ["ft_moe_init_pool", "ft_moe_layer_forward", "ft_moe_pool_stats", "ft_moe_last_misses",
             "ft_moe_pool_table", "ft_moe_set_hybrid_share", "ft_moe_host_expert_rate",
             "ft_moe_set_profiling", "ft_moe_profile_read", "ft_moe_destroy_pool", "ft_moe_last_error",
-            "ft_moe_reserve", "ft_moe_resize_pool", "ft_moe_decide_mode", "ft_moe_measure_mode"]
+            "ft_moe_reserve", "ft_moe_resize_pool", "ft_moe_decide_mode", "ft_moe_measure_mode",
+            "ft_moe_ffn_kernel_name"]
 
 FT_MODE_OFFLOAD, FT_MODE_HYBRID, FT_MODE_FUSED = 0, 1, 2
 
@@ -120,6 +121,8 @@ def lib() -> ctypes.CDLL:
     L.ft_moe_pool_table.argtypes = [P, I32P, ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint64),
                                     ctypes.POINTER(ctypes.c_int64)]
     L.ft_moe_pool_table.restype = ctypes.c_int
+    L.ft_moe_ffn_kernel_name.argtypes = [ctypes.c_int32]
+    L.ft_moe_ffn_kernel_name.restype = ctypes.c_char_p
     L.ft_moe_decide_mode.argtypes = [ctypes.POINTER(ft_moe_mode_report)]
     L.ft_moe_decide_mode.restype = ctypes.c_int
     L.ft_moe_measure_mode.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ft_moe_mode_report)]
@@ -284,6 +287,11 @@ def ft_moe_host_expert_rate(pool, layer: int, tokens: int, iters: int = 1) -> fl
     r = ctypes.c_double()
     _check(lib().ft_moe_host_expert_rate(pool, int(layer), int(tokens), int(iters), ctypes.byref(r)))
     return r.value
+
+
+def ft_moe_ffn_kernel_name(stage: str) -> str:
+    """Kernel behind the latest launch of stage "ffn_gateup" or "ffn_down"."""
+    return lib().ft_moe_ffn_kernel_name(FT_STAGES.index(stage)).decode()
 
 
 def ft_moe_set_profiling(pool, stages=None):

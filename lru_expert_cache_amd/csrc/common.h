@@ -162,6 +162,14 @@ inline void ft_launch(K kernel, dim3 grid, dim3 block, hipStream_t s, Ev ev, Arg
   else
     hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
 }
+// the same with dynamic LDS bytes
+template <typename K, typename... Args>
+inline void ft_launch_lds(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, Ev ev, Args... args) {
+  if (ev.a)
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, s, ev.a, ev.b, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+}
 
 // router.hip
 hipError_t launch_router_logits(const uint16_t* x, const float* wr, const float* bias, double* z,
@@ -196,6 +204,7 @@ hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t s, Ev ev = {});
 hipError_t launch_combine(const uint16_t* pbuf, const int32_t* pair_row, int t0, int T, int k, int H,
                           int shared_row0, uint16_t* out, hipStream_t s, Ev ev = {});
 bool ffn_shape_ok(int fmt, int hidden, int inter);
+const char* ffn_last_kernel(bool gateup);  // kernel of the latest gate/up or down launch
 
 // copy.hip: streamed misses copied by the GPU from the pinned host store.
 // The list is the one the resolve kernel left in device memory: entries

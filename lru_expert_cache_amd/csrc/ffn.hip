@@ -21,10 +21,12 @@
 // scale and their fp32 block scale is applied to each 128-K partial sum.
 // Split-K slices of one row tile are summed through LDS in a fixed order.
 #include <algorithm>
+#include <cstdio>
 #include <cstring>
 #include <utility>
 
 #include "common.h"
+#include "gmem.h"
 
 namespace ftmoe {
 
@@ -35,6 +37,15 @@ typedef short bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxWaves = 8;  // 512 threads: up to 256 VGPRs per wave
+
+// name of the kernel behind the latest gate/up [0] and down [1] launch (for
+// reports; the host thread that enqueues is the one that reads it back)
+char g_ffn_kernel[2][96] = {"", ""};
+const char* const kFmtName[4] = {"?", "mxfp4", "nvfp4", "fp8"};
+void note_kernel(bool gateup, const char* kern, int fmt, const char* params) {
+  std::snprintf(g_ffn_kernel[gateup ? 0 : 1], sizeof(g_ffn_kernel[0]), "%s<%s, %s, %s>", kern,
+                kFmtName[fmt & 3], gateup ? "gate/up" : "down", params);
+}
 constexpr int64_t kFfnMaxGrid = 2048;  // 8 workgroups on each of the 256 CUs
 
 __device__ inline uint16_t f32_to_bf16_rne(float f) {
@@ -42,9 +53,11 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
   return uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-__device__ inline float e8m0_to_f32(uint32_t b) {
-  return b == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(b << 23);
-}
+// An E8M0 scale as the scale operand of the scaled converts, which read only
+// its exponent field: the byte itself in bits 23..30 (byte 0 leaves the field
+// 0, which those instructions take as 2^-127, the value E8M0 byte 0 encodes).
+// No compare, so the conversion of a tile never waits on other tiles' scales.
+__device__ inline float e8m0_scale_operand(uint32_t b) { return __uint_as_float(b << 23); }
 
 __device__ inline float e4m3_to_f32(uint32_t b) {
   const uint32_t e = (b >> 3) & 15u, m = b & 7u;
@@ -118,8 +131,15 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // 16-byte streaming load (weights are read once per call: do not keep them in cache)
 __device__ inline uint4 ld_stream16(const void* p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  const u32x4 v = gload_nt<u32x4>(p);
   return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+typedef float f32x4g __attribute__((ext_vector_type(4)));
+// four fp32 values through a global pointer
+__device__ inline float4 ld_f4(const void* p) {
+  const f32x4g v = gload<f32x4g>(p);
+  return make_float4(v[0], v[1], v[2], v[3]);
 }
 
 template <int FMT>
@@ -149,9 +169,9 @@ __device__ inline void load_tile(TileRegs<FMT>& r, const uint8_t* __restrict__ W
   } else {
     r.c = ld_stream16(W + m.codes_off + (tile * 64 + lane) * 16);
     if constexpr (FMT == FT_FMT_MXFP4)
-      r.s = W[m.scales_off + tile * 64 + lane];
+      r.s = gload<uint8_t>(W + m.scales_off + tile * 64 + lane);
     else
-      r.s = *reinterpret_cast<const uint16_t*>(W + m.scales_off + (tile * 64 + lane) * 2);
+      r.s = gload<uint16_t>(W + m.scales_off + (tile * 64 + lane) * 2);
   }
 }
 
@@ -168,7 +188,7 @@ __device__ inline void tile_mma(const TileRegs<FMT>& r, const uint4 xv[4], float
     for (int j = 0; j < 4; ++j)
       t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(w[2 * j], w[2 * j + 1]), as_bf16x8(xv[j]), t, 0, 0,
                                                   0);
-    const float4 sc = *reinterpret_cast<const float4*>(fp8_scales);
+    const float4 sc = ld_f4(fp8_scales);
     acc[0] += sc.x * t[0];
     acc[1] += sc.y * t[1];
     acc[2] += sc.z * t[2];
@@ -177,7 +197,7 @@ __device__ inline void tile_mma(const TileRegs<FMT>& r, const uint4 xv[4], float
     const uint32_t w[4] = {r.c.x, r.c.y, r.c.z, r.c.w};
     float s0, s1;
     if constexpr (FMT == FT_FMT_MXFP4) {
-      s0 = s1 = e8m0_to_f32(r.s);
+      s0 = s1 = e8m0_scale_operand(r.s);
     } else {
       s0 = e4m3_to_f32(r.s & 0xFFu);
       s1 = e4m3_to_f32(r.s >> 8);
@@ -250,9 +270,9 @@ __device__ inline void load_tile_sel(TileRegs<FMT>& r, const uint8_t* __restrict
   } else {
     r.c = ld_stream16(live ? W + m.codes_off + (tile * 64 + lane) * 16 : dummy);
     if constexpr (FMT == FT_FMT_MXFP4)
-      r.s = *(live ? W + m.scales_off + tile * 64 + lane : dummy);
+      r.s = gload<uint8_t>(live ? W + m.scales_off + tile * 64 + lane : dummy);
     else
-      r.s = *reinterpret_cast<const uint16_t*>(live ? W + m.scales_off + (tile * 64 + lane) * 2 : dummy);
+      r.s = gload<uint16_t>(live ? W + m.scales_off + (tile * 64 + lane) * 2 : dummy);
   }
 }
 
@@ -302,7 +322,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_ffn_stream(FfnArgs a) {
     float tsc[NM];
 #pragma unroll
     for (int mi = 0; mi < NM; ++mi)
-      tsc[mi] = FMT == FT_FMT_NVFP4 ? reinterpret_cast<const float*>(W + a.lay.tscale_off)[GATEUP ? mi : 2] : 1.0f;
+      tsc[mi] = FMT == FT_FMT_NVFP4 ? gload<float>(W + a.lay.tscale_off + 4 * (GATEUP ? mi : 2)) : 1.0f;
 
     // the ring: weights and the activation piece of steps s .. s+D-1
     TileRegs<FMT> wring[D][NM];
@@ -319,8 +339,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_ffn_stream(FfnArgs a) {
         const MatLayout& m = a.lay.m[GATEUP ? mi : 2];
         load_tile_sel<FMT>(wring[u][mi], W, m, tile, lane, live, dummy);
         if constexpr (F8)
-          sring[u][mi] = *reinterpret_cast<const float4*>(
-              live ? W + m.scales_off + (tile * 16 + 4 * q) * 4 : dummy);
+          sring[u][mi] = ld_f4(live ? W + m.scales_off + (tile * 16 + 4 * q) * 4 : dummy);
       }
       const uint16_t* xp = a.x + xoff[c];
       xring[u] = *reinterpret_cast<const u32x4*>(live ? xp + t * kTileK + xc * 8 : a.x);
@@ -430,9 +449,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_ffn(FfnArgs a, int SK, int R
     }
     float tsc[NM];
     {
-      const float* ts = reinterpret_cast<const float*>(W + a.lay.tscale_off);
 #pragma unroll
-      for (int mi = 0; mi < NM; ++mi) tsc[mi] = FMT == FT_FMT_NVFP4 ? ts[GATEUP ? mi : 2] : 1.0f;
+      for (int mi = 0; mi < NM; ++mi)
+        tsc[mi] = FMT == FT_FMT_NVFP4 ? gload<float>(W + a.lay.tscale_off + 4 * (GATEUP ? mi : 2)) : 1.0f;
     }
 
     const int q = lane >> 4, n = lane & 15;
@@ -548,6 +567,7 @@ hipError_t launch_fmt(const FfnArgs& a, const Split& s, dim3 grid, dim3 block, h
 #define FT_KPW_CASE(N)                                                                   \
   case N:                                                                                \
     if constexpr (N <= kpw_max(FMT, GATEUP)) {                                           \
+      note_kernel(GATEUP, "k_ffn", FMT, "split-K");                                     \
       ft_launch(k_ffn<FMT, GATEUP, N>, grid, block, st, ev, a, s.SK, s.RB);              \
       return hipGetLastError();                                                          \
     }                                                                                    \
@@ -576,6 +596,7 @@ hipError_t launch_stream_d(const FfnArgs& a, hipStream_t st, Ev ev) {
   static const int64_t cap = resident_grid(k_ffn_stream<FMT, GATEUP, D>, 64 * kStreamWaves);
   const MatLayout& m = a.lay.m[GATEUP ? 0 : 2];
   const int64_t items = int64_t(a.n_list) * (m.rows / (kTileRows * kStreamWaves));
+  note_kernel(GATEUP, "k_ffn_stream", FMT, D == 4 ? "depth 4" : D == 3 ? "depth 3" : D == 2 ? "depth 2" : "depth 1");
   ft_launch(k_ffn_stream<FMT, GATEUP, D>, dim3(unsigned(std::min(items, cap))), dim3(64 * kStreamWaves), st, ev, a);
   return hipGetLastError();
 }
@@ -651,7 +672,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_ffn_ring(FfnArgs a, int SK) 
       const MatLayout& m = a.lay.m[GATEUP ? mi : 2];
       load_tile_sel<FMT>(wring[t][mi], W, m, tile, lane, live, dummy);
       if constexpr (F8)
-        sring[t][mi] = *reinterpret_cast<const float4*>(live ? W + m.scales_off + (tile * 16 + 4 * q) * 4 : dummy);
+        sring[t][mi] = ld_f4(live ? W + m.scales_off + (tile * 16 + 4 * q) * 4 : dummy);
     }
     // a missing row reads one shared line (its output column is not written)
     const u32x4* xp = reinterpret_cast<const u32x4*>(xsrc ? xsrc + (kb0 + t) * kTileK + 32 * q : a.x);
@@ -736,7 +757,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_ffn_ring(FfnArgs a, int SK) 
 #pragma unroll
     for (int mi = 0; mi < NM; ++mi)
       tsc[mi] = FMT == FT_FMT_NVFP4 && cur.row_count > 0
-                    ? reinterpret_cast<const float*>(cur.wptr + a.lay.tscale_off)[GATEUP ? mi : 2]
+                    ? gload<float>(reinterpret_cast<const uint8_t*>(cur.wptr) + a.lay.tscale_off + 4 * (GATEUP ? mi : 2))
                     : 1.0f;
     floatx4 acc[NM];
 #pragma unroll
@@ -757,6 +778,206 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_ffn_ring(FfnArgs a, int SK) 
     xs_nxt = xs_nn;
     wr_nxt = wr_nn;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Decode calls of at most 16 rows per group, one pass: a workgroup of SK waves
+// owns F 16-row weight tiles (both gate and up for gate/up) of one expert over
+// the full K, split into SK slices of KPW K tiles.  Every weight tile of a
+// wave's slice is requested at once, so that a single round of loads covers
+// the launch: at decode sizes the items fit the resident workgroups, and the
+// bytes in flight, not the issue rate, set the bandwidth.  The activation tile
+// of each K tile (16 rows x 128 K, one row per lane column) is loaded once
+// per wave and serves all F weight tiles.  Loads complete in issue order, so
+// the weights of the first K tile go out before the activations (whose row
+// addresses wait for the group's token list) and the rest after them; the
+// multiplies of K tile t then wait only for what precedes it.  Partial sums of
+// the SK slices meet in LDS and are added in slice order; wave v finishes
+// weight tiles v, v + SK, ...  Missing rows (beyond the group's count) use
+// zero activations and are not written.
+constexpr int kWideMaxWaves = 8;
+
+template <int FMT, bool GATEUP, int KPW, int F>
+__global__ __launch_bounds__(64 * kWideMaxWaves) void k_ffn_wide(FfnArgs a, int SK) {
+  constexpr int NM = GATEUP ? 2 : 1;
+  constexpr bool F8 = FMT == FT_FMT_FP8_B128;
+  extern __shared__ floatx4 wide_red[];  // [SK][F][NM][64]
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int q = lane >> 4, n = lane & 15;
+  const MatLayout& m0 = a.lay.m[GATEUP ? 0 : 2];
+  const int nkb = m0.cols / kTileK;
+  const int nfb = m0.rows / (kTileRows * F);
+  const int n_list = a.n_list_dev != nullptr ? *a.n_list_dev : a.n_list;
+  const int list_off = a.list_off_dev != nullptr ? *a.list_off_dev : 0;
+  const int item = blockIdx.x;
+  if (item >= n_list * nfb) return;
+  const int gi = item / nfb;
+  const int rb0 = (item - gi * nfb) * F;
+  const GroupDesc g = a.groups[a.glist[list_off + gi]];
+  if (g.wptr == 0 || g.row_count <= 0) return;  // whole workgroup: one group
+  const uint8_t* W = reinterpret_cast<const uint8_t*>(g.wptr);
+  const int kb0 = w * KPW;
+  const bool rv = n < g.row_count;
+  const int row = g.row_begin + (rv ? n : 0);
+  int tok = 0;
+  if constexpr (GATEUP) tok = a.row_tok[row];
+
+  TileRegs<FMT> wt[F][NM][KPW];
+  float4 ws[F][NM][KPW];
+  uint4 xv[KPW][4];
+  auto load_w = [&](auto tc) {
+    constexpr int t = decltype(tc)::value;
+#pragma unroll
+    for (int f = 0; f < F; ++f)
+#pragma unroll
+      for (int mi = 0; mi < NM; ++mi) {
+        const MatLayout& m = a.lay.m[GATEUP ? mi : 2];
+        const int64_t tile = int64_t(rb0 + f) * nkb + kb0 + t;
+        load_tile<FMT>(wt[f][mi][t], W, m, tile, lane);
+        if constexpr (F8) ws[f][mi][t] = ld_f4(W + m.scales_off + (tile * 16 + 4 * q) * 4);
+      }
+  };
+  // K tile 0 first, then the activations of every K tile, then the rest; the
+  // scheduling barriers keep the compiler from sinking loads towards their
+  // uses (which would leave only a few in flight)
+  load_w(std::integral_constant<int, 0>{});
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    const uint16_t* xs = GATEUP ? a.x + int64_t(tok) * a.hidden : a.x + int64_t(row) * a.inter;
+#pragma unroll
+    for (int t = 0; t < KPW; ++t) {
+      const uint4* xp = reinterpret_cast<const uint4*>(xs + (kb0 + t) * kTileK + 32 * q);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xv[t][j] = rv ? xp[j] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  static_for<KPW>([&](auto tc) {
+    if constexpr (decltype(tc)::value > 0) {
+      load_w(tc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  });
+  float tsc[NM];
+#pragma unroll
+  for (int mi = 0; mi < NM; ++mi)
+    tsc[mi] = FMT == FT_FMT_NVFP4 ? gload<float>(W + a.lay.tscale_off + 4 * (GATEUP ? mi : 2)) : 1.0f;
+
+  floatx4 acc[F][NM];
+#pragma unroll
+  for (int f = 0; f < F; ++f)
+#pragma unroll
+    for (int mi = 0; mi < NM; ++mi) acc[f][mi] = {0.f, 0.f, 0.f, 0.f};
+  // one K tile at a time, so that each waits only for its own loads
+  static_for<KPW>([&](auto tc) {
+    constexpr int t = decltype(tc)::value;
+#pragma unroll
+    for (int f = 0; f < F; ++f)
+#pragma unroll
+      for (int mi = 0; mi < NM; ++mi) {
+        if constexpr (F8)
+          tile_mma_sc<FMT>(wt[f][mi][t], xv[t], acc[f][mi], ws[f][mi][t]);
+        else
+          tile_mma<FMT>(wt[f][mi][t], xv[t], acc[f][mi], nullptr);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+  });
+
+  // slice sums in LDS, added in slice order
+  if (SK > 1) {
+#pragma unroll
+    for (int f = 0; f < F; ++f)
+#pragma unroll
+      for (int mi = 0; mi < NM; ++mi) wide_red[((w * F + f) * NM + mi) * 64 + lane] = acc[f][mi];
+    __syncthreads();
+  }
+  const float wr = GATEUP ? 0.0f : a.row_w[row];
+#pragma unroll
+  for (int f = 0; f < F; ++f) {
+    if (f % SK != w) continue;
+    floatx4 s[NM];
+#pragma unroll
+    for (int mi = 0; mi < NM; ++mi) {
+      if (SK > 1) {
+        s[mi] = wide_red[(f * NM + mi) * 64 + lane];
+        for (int k2 = 1; k2 < SK; ++k2) {
+          const floatx4 v = wide_red[((k2 * F + f) * NM + mi) * 64 + lane];
+          s[mi][0] += v[0]; s[mi][1] += v[1]; s[mi][2] += v[2]; s[mi][3] += v[3];
+        }
+      } else {
+        s[mi] = acc[f][mi];
+      }
+    }
+    if (!rv) continue;
+    // lane holds output features (rb0 + f) * 16 + 4q + i of row n
+    const int o0 = (rb0 + f) * kTileRows + 4 * q;
+    uint16_t hv[4];
+    if constexpr (GATEUP) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float gv = s[0][i] * tsc[0];
+        const float uv = s[1][i] * tsc[1];
+        hv[i] = f32_to_bf16_rne(gv / (1.0f + expf(-gv)) * uv);
+      }
+      *reinterpret_cast<uint2*>(a.out + int64_t(row) * a.inter + o0) =
+          make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16), uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hv[i] = f32_to_bf16_rne(wr * (s[0][i] * tsc[0]));
+      *reinterpret_cast<uint2*>(a.out + int64_t(row) * a.hidden + o0) =
+          make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16), uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
+    }
+  }
+}
+
+// The wide kernel's (K tiles per wave, weight tiles per item) for a format and
+// matrix, chosen so that a wave's registers stay within 256 (two waves per
+// SIMD): per K tile the activations take 16 registers and each weight tile 5
+// (FP4) or 12 (FP8, with its scales).
+struct WideCfg {
+  int kpw, f;
+};
+constexpr int wide_regs(int fmt, bool gateup, int kpw, int f) {
+  return (gateup ? 2 : 1) * f * kpw * (fmt == FT_FMT_FP8_B128 ? 12 : 5) + 16 * kpw + (gateup ? 8 : 4) * f + 28;
+}
+
+// Launches the wide kernel unless its items would take more than kWideMaxRounds
+// rounds of resident workgroups (large K: one pass per item then loses to the
+// item rings, which overlap one item's loads with the previous one's work);
+// *done tells which.
+constexpr int kWideMaxRounds = 6;
+
+template <int FMT, bool GATEUP, int KPW, int F>
+hipError_t launch_wide_k(const FfnArgs& a, hipStream_t st, Ev ev, bool* done) {
+  const MatLayout& m = a.lay.m[GATEUP ? 0 : 2];
+  const int SK = m.cols / kTileK / KPW;
+  constexpr int NM = GATEUP ? 2 : 1;
+  const int64_t items = int64_t(a.n_list) * (m.rows / (kTileRows * F));
+  const size_t lds = SK > 1 ? size_t(SK) * F * NM * 64 * sizeof(floatx4) : 0;
+  static int64_t resident[kWideMaxWaves + 1] = {};
+  if (!resident[SK]) {
+    int dev = 0, cus = 0, per_cu = 0;
+    (void)hipGetDevice(&dev);
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_ffn_wide<FMT, GATEUP, KPW, F>, 64 * SK, lds) !=
+            hipSuccess ||
+        per_cu < 1)
+      per_cu = 1;
+    resident[SK] = int64_t(per_cu) * std::max(cus, 1);
+  }
+  if (items > kWideMaxRounds * resident[SK]) {
+    *done = false;
+    return hipSuccess;
+  }
+  *done = true;
+  {
+    char prm[48];
+    std::snprintf(prm, sizeof(prm), "%d K tiles x %d waves, %d weight tiles", KPW, SK, F);
+    note_kernel(GATEUP, "k_ffn_wide", FMT, prm);
+  }
+  ft_launch_lds(k_ffn_wide<FMT, GATEUP, KPW, F>, dim3(unsigned(items)), dim3(64 * SK), lds, st, ev, a, SK);
+  return hipGetLastError();
 }
 
 #ifndef FT_STREAM_MAXD
@@ -793,13 +1014,55 @@ hipError_t launch_ring_k(const FfnArgs& a, int SK, hipStream_t st, Ev ev) {
   static int64_t cap[kMaxWaves + 1] = {};
   if (!cap[SK]) cap[SK] = resident_grid(k_ffn_ring<FMT, GATEUP, KPW>, 64 * SK);
   const int64_t items = int64_t(a.n_list) * (a.lay.m[GATEUP ? 0 : 2].rows / kTileRows);
+  {
+    char prm[48];
+    std::snprintf(prm, sizeof(prm), "%d K tiles x %d waves", KPW, SK);
+    note_kernel(GATEUP, "k_ffn_ring", FMT, prm);
+  }
   ft_launch(k_ffn_ring<FMT, GATEUP, KPW>, dim3(unsigned(std::min(items, cap[SK]))), dim3(64 * SK), st, ev, a, SK);
   return hipGetLastError();
+}
+
+// Wide kernel configurations compiled for each format and matrix, in order of
+// preference; a configuration applies when its K tiles per wave divide K into
+// at most 8 slices and its weight tiles per item divide the rows.
+template <int FMT, bool GATEUP>
+hipError_t launch_wide(const FfnArgs& a, hipStream_t st, Ev ev, bool* done) {
+  const MatLayout& m = a.lay.m[GATEUP ? 0 : 2];
+  const int nkb = m.cols / kTileK, nrb = m.rows / kTileRows;
+  *done = false;
+  // prefer few weight tiles per item when the call has few groups, so that
+  // the items still spread over the chip
+  const bool few = int64_t(a.n_list) * nrb < 1024;
+#define FT_WIDE_TRY(KPW, F)                                                                        \
+  if constexpr (wide_regs(FMT, GATEUP, KPW, F) <= 256) {                                          \
+    if (nkb % KPW == 0 && nkb / KPW <= kWideMaxWaves && nrb % F == 0)                             \
+      return launch_wide_k<FMT, GATEUP, KPW, F>(a, st, ev, done);                                  \
+  }
+  if (GATEUP) {
+    if (!few) { FT_WIDE_TRY(4, 3) }
+    FT_WIDE_TRY(4, 1) FT_WIDE_TRY(7, 1) FT_WIDE_TRY(6, 1) FT_WIDE_TRY(2, 2) FT_WIDE_TRY(3, 1) FT_WIDE_TRY(1, 2)
+  } else {
+    if (!few) { FT_WIDE_TRY(3, 8) FT_WIDE_TRY(4, 4) FT_WIDE_TRY(2, 8) FT_WIDE_TRY(4, 2) }
+    FT_WIDE_TRY(3, 2) FT_WIDE_TRY(4, 1) FT_WIDE_TRY(2, 2) FT_WIDE_TRY(1, 4) FT_WIDE_TRY(7, 1) FT_WIDE_TRY(6, 1)
+  }
+#undef FT_WIDE_TRY
+  return hipSuccess;
 }
 
 template <int FMT, bool GATEUP>
 hipError_t launch_small(const FfnArgs& a, hipStream_t st, Ev ev) {
   const int nkb = a.lay.m[GATEUP ? 0 : 2].cols / kTileK;
+  bool wide = a.max_rows > 0 && a.max_rows <= kTileRows;
+#ifdef FT_FFN_KERNEL_ENV
+  if (const char* e = getenv("FFN_KERNEL"))
+    if (!strcmp(e, "ring") || !strcmp(e, "stream")) wide = false;
+#endif
+  if (wide) {
+    bool done = false;
+    const hipError_t r = launch_wide<FMT, GATEUP>(a, st, ev, &done);
+    if (done) return r;
+  }
   // gate/up: the item ring; down (short K, tiny items): the K-streaming kernel
   int kpw = GATEUP && a.max_rows > 0 && a.max_rows <= kTileRows ? ring_kpw<FMT, GATEUP>(nkb) : 0;
 #ifdef FT_FFN_KERNEL_ENV
@@ -897,6 +1160,8 @@ bool ffn_shape_ok(int fmt, int hidden, int inter) {
   return choose_split(hidden, inter, kpw_max(fmt, true)).SK > 0 &&
          choose_split(inter, hidden, kpw_max(fmt, false)).SK > 0;
 }
+
+const char* ffn_last_kernel(bool gateup) { return g_ffn_kernel[gateup ? 0 : 1]; }
 
 hipError_t launch_ffn_gateup(const FfnArgs& a, hipStream_t s, Ev ev) { return launch_ffn<true>(a, s, ev); }
 hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t s, Ev ev) { return launch_ffn<false>(a, s, ev); }

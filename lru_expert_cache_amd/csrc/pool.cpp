@@ -1541,6 +1541,12 @@ int ft_moe_measure_mode(ft_moe_pool* p, int32_t tokens, int32_t apply, ft_moe_mo
   return FT_OK;
 }
 
+const char* ft_moe_ffn_kernel_name(int32_t stage) {
+  if (stage == FT_STAGE_FFN_GATEUP) return ffn_last_kernel(true);
+  if (stage == FT_STAGE_FFN_DOWN) return ffn_last_kernel(false);
+  return "";
+}
+
 int ft_moe_set_profiling(ft_moe_pool* p, int32_t stage_mask) {
   if (!p) {
     set_error("NULL pool");
