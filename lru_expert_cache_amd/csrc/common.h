@@ -131,6 +131,7 @@ struct ResolveArgs {
   float* row_w;            // [rows]
   GroupDesc* groups;       // [max groups + 1]
   int32_t* glist;          // [max groups + 1]: hit list, then streamed, then host
+  GroupDesc* gdesc;        // [max groups + 1]: the descriptors in glist order
   int32_t* dev_header;     // device copy of the header counts (for early-exit kernels)
   int32_t* tiles;          // prefill: (group, 64-row tile) pairs for the MX GEMM, or null
   int32_t tile_rows;       // rows per tile
@@ -184,11 +185,10 @@ hipError_t launch_uncommit(DevTable tab, const int32_t* keys, const int32_t* slo
                            hipStream_t s);
 // ffn.hip
 struct FfnArgs {
-  const GroupDesc* groups;
-  const int32_t* glist;   // group indices to run
-  int32_t n_list;         // entries of glist to run, or (with n_list_dev) an upper bound for the grid
-  const int32_t* n_list_dev;    // if non-null: the number of entries, read on the device
-  const int32_t* list_off_dev;  // if non-null: glist entries start at glist[*list_off_dev]
+  const GroupDesc* gdesc; // the groups to run, in run order (one load per group)
+  int32_t n_list;         // groups to run: the smaller of this (also the grid's bound) and
+  const int32_t* n_list_dev;    // the count read on the device (a constant INT32_MAX when
+                                // the host knows the count)
   const uint16_t* x;      // gate/up: activations [T][H] indexed by token; down: hbuf [rows][I]
   const int32_t* row_tok; // gate/up: token of each row
   const float* row_w;     // down: routing weight of each row
@@ -214,8 +214,7 @@ struct MissCopyArgs {
   const uint8_t* host;        // device-visible address of the pinned host store
   const int64_t* key_off;     // [L*E] offset of each key's blob in the store
   const int32_t* dev_header;  // resolve's counts
-  const int32_t* glist;
-  const GroupDesc* groups;
+  const GroupDesc* gdesc;     // groups in run order: the streamed misses from dev_header[2]
   int32_t layer, E;
   int64_t bytes;              // bytes per expert of this layer (multiple of 16)
 };

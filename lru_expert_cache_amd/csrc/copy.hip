@@ -15,6 +15,7 @@
 // are treated as one concatenated byte range that is split evenly over the
 // workgroups, so every miss count keeps all of them busy.
 #include "common.h"
+#include "gmem.h"
 
 namespace ftmoe {
 
@@ -33,22 +34,23 @@ __global__ __launch_bounds__(256) void k_miss_copy(MissCopyArgs a) {
     const int i = int(lo / n16);
     const int64_t off = lo - int64_t(i) * n16;
     const int64_t seg = (int64_t(i) + 1) * n16 < hi ? (int64_t(i) + 1) * n16 - lo : hi - lo;
-    const GroupDesc g = a.groups[a.glist[nh + i]];
+    const GroupDesc g = a.gdesc[nh + i];
+    // the slot address comes from an integer: store through a global pointer
     const u32x4* __restrict__ src =
         reinterpret_cast<const u32x4*>(a.host + a.key_off[int64_t(a.layer) * a.E + g.expert]) + off;
     u32x4* __restrict__ dst = reinterpret_cast<u32x4*>(g.wptr) + off;
     int64_t j = threadIdx.x;
     for (; j + 768 < seg; j += 1024) {
-      const u32x4 v0 = __builtin_nontemporal_load(src + j);
-      const u32x4 v1 = __builtin_nontemporal_load(src + j + 256);
-      const u32x4 v2 = __builtin_nontemporal_load(src + j + 512);
-      const u32x4 v3 = __builtin_nontemporal_load(src + j + 768);
-      dst[j] = v0;
-      dst[j + 256] = v1;
-      dst[j + 512] = v2;
-      dst[j + 768] = v3;
+      const u32x4 v0 = gload_nt<u32x4>(src + j);
+      const u32x4 v1 = gload_nt<u32x4>(src + j + 256);
+      const u32x4 v2 = gload_nt<u32x4>(src + j + 512);
+      const u32x4 v3 = gload_nt<u32x4>(src + j + 768);
+      gstore<u32x4>(dst + j, v0);
+      gstore<u32x4>(dst + j + 256, v1);
+      gstore<u32x4>(dst + j + 512, v2);
+      gstore<u32x4>(dst + j + 768, v3);
     }
-    for (; j < seg; j += 256) dst[j] = __builtin_nontemporal_load(src + j);
+    for (; j < seg; j += 256) gstore<u32x4>(dst + j, gload_nt<u32x4>(src + j));
     lo += seg;
   }
 }

@@ -287,10 +287,9 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_ffn_stream(FfnArgs a) {
   const MatLayout& m0 = a.lay.m[GATEUP ? 0 : 2];
   const int nkb = m0.cols / kTileK;
   const int nfb = m0.rows / (kTileRows * kStreamWaves);  // feature blocks of one group
-  const int n_list = a.n_list_dev != nullptr ? *a.n_list_dev : a.n_list;
-  const int list_off = a.list_off_dev != nullptr ? *a.list_off_dev : 0;
+  const int n_list = min(a.n_list, *a.n_list_dev);
   const int n_items = n_list * nfb;
-  const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.groups);
+  const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.gdesc);
   // this thread's piece of the activation tile: row xr, 8 K values at chunk xc
   const int xr = tid >> 4, xc = tid & 15;
   const int xslot = xr * 16 + (xc ^ xr);
@@ -298,7 +297,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_ffn_stream(FfnArgs a) {
 
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int gi = item / nfb;
-    const GroupDesc g = a.groups[a.glist[list_off + gi]];
+    const GroupDesc g = a.gdesc[gi];
     if (g.row_count <= 0 || g.wptr == 0) continue;  // uniform over the workgroup
     const int rb = (item - gi * nfb) * kStreamWaves + w;  // this wave's 16-row weight tile
     const uint8_t* W = reinterpret_cast<const uint8_t*>(g.wptr);
@@ -426,14 +425,13 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_ffn(FfnArgs a, int SK, int R
   const int nkb = K / kTileK;
   const int kb0 = sk * kpw;
   const int nrbb = m0.rows / kTileRows / RB;  // row blocks of one group
-  const int n_list = a.n_list_dev != nullptr ? *a.n_list_dev : a.n_list;
-  const int list_off = a.list_off_dev != nullptr ? *a.list_off_dev : 0;
+  const int n_list = min(a.n_list, *a.n_list_dev);
   const int n_items = n_list * nrbb;
 
   // items (group, row block), group-major, strided over the grid
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int gi = item / nrbb;
-    const GroupDesc g = a.groups[a.glist[list_off + gi]];
+    const GroupDesc g = a.gdesc[gi];
     if (g.row_count <= 0) continue;  // uniform over the workgroup
     const int rb = (item - gi * nrbb) * RB + rbl;
     const uint8_t* W = reinterpret_cast<const uint8_t*>(g.wptr);
@@ -627,12 +625,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_ffn_ring(FfnArgs a, int SK) 
   const int nkb = m0.cols / kTileK;
   const int kb0 = sk * KPW;
   const int nrb = m0.rows / kTileRows;
-  const int n_list = a.n_list_dev != nullptr ? *a.n_list_dev : a.n_list;
-  const int list_off = a.list_off_dev != nullptr ? *a.list_off_dev : 0;
+  const int n_list = min(a.n_list, *a.n_list_dev);
   const int n_items = n_list * nrb;
   if (int(blockIdx.x) >= n_items) return;
   const int G = int(gridDim.x);
-  const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.groups);
+  const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.gdesc);
 
   struct Item {
     uint64_t wptr;
@@ -642,7 +639,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_ffn_ring(FfnArgs a, int SK) 
     const bool ok = item < n_items;
     const int it = ok ? item : n_items - 1;
     const int gi = it / nrb;
-    const GroupDesc g = a.groups[a.glist[list_off + gi]];
+    const GroupDesc g = a.gdesc[gi];
     Item r;
     r.wptr = g.wptr;
     r.row_begin = g.row_begin;
@@ -808,14 +805,15 @@ __global__ __launch_bounds__(64 * kWideMaxWaves) void k_ffn_wide(FfnArgs a, int 
   const MatLayout& m0 = a.lay.m[GATEUP ? 0 : 2];
   const int nkb = m0.cols / kTileK;
   const int nfb = m0.rows / (kTileRows * F);
-  const int n_list = a.n_list_dev != nullptr ? *a.n_list_dev : a.n_list;
-  const int list_off = a.list_off_dev != nullptr ? *a.list_off_dev : 0;
+  // the group is read together with the count (the grid never exceeds the
+  // descriptor array), so that one load latency precedes the weight loads
   const int item = blockIdx.x;
-  if (item >= n_list * nfb) return;
   const int gi = item / nfb;
   const int rb0 = (item - gi * nfb) * F;
-  const GroupDesc g = a.groups[a.glist[list_off + gi]];
-  if (g.wptr == 0 || g.row_count <= 0) return;  // whole workgroup: one group
+  const GroupDesc g = a.gdesc[gi];
+  const int n_list = min(a.n_list, *a.n_list_dev);
+  // whole workgroup: one group
+  if (item >= n_list * nfb || g.wptr == 0 || g.row_count <= 0) return;
   const uint8_t* W = reinterpret_cast<const uint8_t*>(g.wptr);
   const int kb0 = w * KPW;
   const bool rv = n < g.row_count;

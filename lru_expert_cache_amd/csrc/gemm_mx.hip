@@ -25,6 +25,7 @@
 // feed output columns that are not written.  Epilogues as the decode FFN:
 // gate/up -> h = bf16(silu(g) * u); down -> p = bf16(w * y).
 #include "common.h"
+#include "gmem.h"
 
 namespace ftmoe {
 
@@ -113,11 +114,11 @@ __global__ __launch_bounds__(256, 2) void k_mx_gemm(MxGemmArgs a) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int ci = r * 4 + (tid >> 6);
-      ga[r] = *reinterpret_cast<const u32x4*>(W + chunk_mat(ci).codes_off + chunk_tile(ci, kb) * 1024 + lane * 16);
+      ga[r] = gload<u32x4>(W + chunk_mat(ci).codes_off + chunk_tile(ci, kb) * 1024 + lane * 16);
     }
     if (tid < 32) {
       const int ci = tid >> 2, part = tid & 3;
-      gas = *reinterpret_cast<const u32x4*>(W + chunk_mat(ci).scales_off + chunk_tile(ci, kb) * 64 + part * 16);
+      gas = gload<u32x4>(W + chunk_mat(ci).scales_off + chunk_tile(ci, kb) * 64 + part * 16);
     }
 #pragma unroll
     for (int r = 0; r < BR; ++r) {

@@ -89,6 +89,8 @@ struct ft_moe_pool {
   float* row_w = nullptr;
   GroupDesc* groups = nullptr;
   int32_t* glist = nullptr;
+  GroupDesc* gdesc = nullptr;  // descriptors in run order (what the FFN and copy kernels read)
+  int32_t* count_max = nullptr;  // device INT32_MAX: the device count of a launch whose count the host knows
   int32_t* dev_header = nullptr;
   uint16_t* hbuf = nullptr;
   uint16_t* pbuf = nullptr;
@@ -332,13 +334,11 @@ int issue_copy(ft_moe_pool* p, void* dst, const void* src, size_t bytes, hipStre
   return FT_OK;
 }
 
-FfnArgs ffn_args(ft_moe_pool* p, int layer, int list_off, int n, const int32_t* n_dev, const int32_t* off_dev) {
+FfnArgs ffn_args(ft_moe_pool* p, int layer, int list_off, int n, const int32_t* n_dev) {
   FfnArgs a{};
-  a.groups = p->groups;
-  a.glist = p->glist + list_off;
+  a.gdesc = p->gdesc + list_off;
   a.n_list = n;
-  a.n_list_dev = n_dev;
-  a.list_off_dev = off_dev;
+  a.n_list_dev = n_dev != nullptr ? n_dev : p->count_max;
   a.row_tok = p->row_tok;
   a.row_w = p->row_w;
   a.hidden = p->H;
@@ -356,13 +356,13 @@ void prof_push(ft_moe_pool* p, int stage, Ev ev, double bytes, double flops);
 
 // groups / rows: how many expert groups and rows this launch runs (for the
 // algorithmic byte and flop counts of the stage timers; 0 when the device
-// counts them).  off_dev: glist offset read on the device, or null.
+// counts them).
 int run_ffn(ft_moe_pool* p, int layer, const void* x, int list_off, int n, const int32_t* n_dev, hipStream_t s,
-            double groups, double rows, const int32_t* off_dev = nullptr, int max_group_rows = 1 << 30) {
+            double groups, double rows, int max_group_rows = 1 << 30) {
   // nothing to run (a count known on the host): no launch, and no timing record
   // (its recycled events would still hold an earlier launch's timestamps)
   if (n_dev == nullptr && n <= 0) return FT_OK;
-  FfnArgs a = ffn_args(p, layer, list_off, n, n_dev, off_dev);
+  FfnArgs a = ffn_args(p, layer, list_off, n, n_dev);
   a.max_rows = p->ffn_stream && max_group_rows <= 64 ? max_group_rows : 0;
   const int f = p->fmt[layer];
   const double H = p->H, I = p->I;
@@ -408,6 +408,7 @@ ResolveArgs resolve_args(ft_moe_pool* p, int layer, int T, int t0, int mode) {
   a.row_w = p->row_w;
   a.groups = p->groups;
   a.glist = p->glist;
+  a.gdesc = p->gdesc;
   a.dev_header = p->dev_header;
   a.host_rb = mode == 0 ? p->rb_dev : nullptr;
   a.host_rb_cap = p->rb_cap;
@@ -676,8 +677,7 @@ int forward_decode_dev(ft_moe_pool* p, int layer, int T, const void* x, void* ou
   ca.host = p->host_store_dev;
   ca.key_off = p->key_off_dev;
   ca.dev_header = p->dev_header;
-  ca.glist = p->glist;
-  ca.groups = p->groups;
+  ca.gdesc = p->gdesc;
   ca.layer = layer;
   ca.E = E;
   ca.bytes = p->lay[f].bytes;
@@ -689,7 +689,7 @@ int forward_decode_dev(ft_moe_pool* p, int layer, int T, const void* x, void* ou
   const int pairs = T * k;
   const int bound = std::min(pairs, E) + p->shared;
   // a group has at most one row per token
-  int rc = run_ffn(p, layer, x, 0, bound, p->dev_header + 9, s, 0.0, 0.0, nullptr, T);
+  int rc = run_ffn(p, layer, x, 0, bound, p->dev_header + 9, s, 0.0, 0.0, T);
   if (rc) return rc;
   const int rows = pairs + (p->shared ? T : 0);
   Ev eb = prof_pair(p, s, FT_STAGE_COMBINE);
@@ -825,10 +825,10 @@ int forward_decode(ft_moe_pool* p, int layer, int T, const void* x, void* out, h
       });
     }
 
-    int rc = run_ffn(p, layer, x, 0, h.n_hit_list, nullptr, s, h.n_hit_list, h.rows_hit_list, nullptr, T);
+    int rc = run_ffn(p, layer, x, 0, h.n_hit_list, nullptr, s, h.n_hit_list, h.rows_hit_list, T);
     if (rc == FT_OK && h.n_stream > 0) {
       FT_HIP_CHECK(hipStreamWaitEvent(s, p->ev_copied, 0));
-      rc = run_ffn(p, layer, x, h.n_hit_list, h.n_stream, nullptr, s, h.n_stream, h.rows_stream, nullptr, T);
+      rc = run_ffn(p, layer, x, h.n_hit_list, h.n_stream, nullptr, s, h.n_stream, h.rows_stream, T);
     }
     if (cpu_thread.joinable()) cpu_thread.join();
     if (rc) return rc;
@@ -1006,7 +1006,7 @@ int ft_moe_init_pool(const ft_moe_config* cfg, const ft_moe_weights* wts, ft_moe
         (rc = dev_alloc(&p->tab.lru[1], C)) || (rc = dev_alloc(&p->tab.lru_cur, 1)) ||
         (rc = dev_alloc(&p->tab.clock, 1)) || (rc = dev_alloc(&p->tab.stats, int64_t(L) * ST_COUNT)) ||
         (rc = dev_alloc(&p->tab.min_gap, L)) || (rc = dev_alloc(&p->groups, E + 2)) ||
-        (rc = dev_alloc(&p->glist, E + 2)) || (rc = dev_alloc(&p->dev_header, 16)) ||
+        (rc = dev_alloc(&p->glist, E + 2)) || (rc = dev_alloc(&p->gdesc, E + 2)) || (rc = dev_alloc(&p->count_max, 1)) || (rc = dev_alloc(&p->dev_header, 16)) ||
         (rc = dev_alloc(&p->fail_dev, 2 * E + 2)) || (rc = dev_alloc(&p->key_off_dev, int64_t(L) * E)) ||
         (rc = dev_alloc(&p->prof_cnt_dev, 24))) {
       ft_moe_destroy_pool(p.release());
@@ -1019,6 +1019,10 @@ int ft_moe_init_pool(const ft_moe_config* cfg, const ft_moe_weights* wts, ft_moe
     FT_HIP_CHECK(hipMemset(p->tab.clock, 0, 8));
     FT_HIP_CHECK(hipMemset(p->tab.stats, 0, size_t(L) * ST_COUNT * 8));
     FT_HIP_CHECK(hipMemset(p->prof_cnt_dev, 0, 24 * 8));
+    {
+      const int32_t big = INT32_MAX;
+      FT_HIP_CHECK(hipMemcpy(p->count_max, &big, 4, hipMemcpyHostToDevice));
+    }
     FT_HIP_CHECK(hipMemcpy(p->key_off_dev, p->key_off.data(), p->key_off.size() * 8, hipMemcpyHostToDevice));
     for (int f = 1; f <= 3; ++f)
       if (p->lay[f].bytes % 16) p->dev_decode = false;
@@ -1494,7 +1498,7 @@ int ft_moe_measure_mode(ft_moe_pool* p, int32_t tokens, int32_t apply, ft_moe_mo
     // the device's grouped FFN on the n experts, T rows each
     {
       std::vector<GroupDesc> g(n);
-      std::vector<int32_t> gl(n), rt(size_t(n) * T);
+      std::vector<int32_t> rt(size_t(n) * T);
       std::vector<float> rw(size_t(n) * T, 1.0f);
       for (int e = 0; e < n; ++e) {
         g[e].wptr = reinterpret_cast<uint64_t>(tmp + e * p->slot_bytes);
@@ -1502,17 +1506,15 @@ int ft_moe_measure_mode(ft_moe_pool* p, int32_t tokens, int32_t apply, ft_moe_mo
         g[e].row_count = T;
         g[e].expert = e;
         g[e].slot = -1;
-        gl[e] = e;
         for (int t = 0; t < T; ++t) rt[size_t(e) * T + t] = t;
       }
-      FT_HIP_CHECK(hipMemcpy(p->groups, g.data(), g.size() * sizeof(GroupDesc), hipMemcpyHostToDevice));
-      FT_HIP_CHECK(hipMemcpy(p->glist, gl.data(), gl.size() * 4, hipMemcpyHostToDevice));
+      FT_HIP_CHECK(hipMemcpy(p->gdesc, g.data(), g.size() * sizeof(GroupDesc), hipMemcpyHostToDevice));
       FT_HIP_CHECK(hipMemcpy(p->row_tok, rt.data(), rt.size() * 4, hipMemcpyHostToDevice));
       FT_HIP_CHECK(hipMemcpy(p->row_w, rw.data(), rw.size() * 4, hipMemcpyHostToDevice));
     }
     int frc = FT_OK;
     if ((rc = timed([&]() {
-           if (frc == FT_OK) frc = run_ffn(p, layer, xd, 0, n, nullptr, s, n, double(n) * T, nullptr, T);
+           if (frc == FT_OK) frc = run_ffn(p, layer, xd, 0, n, nullptr, s, n, double(n) * T, T);
          })))
       return rc;
     if (frc) return frc;
@@ -1600,7 +1602,7 @@ void ft_moe_destroy_pool(ft_moe_pool* p) {
   hipFree(p->tab.lru[1]); hipFree(p->tab.lru_cur); hipFree(p->tab.clock); hipFree(p->tab.stats);
   hipFree(p->tab.min_gap);
   hipFree(p->z); hipFree(p->sel); hipFree(p->w); hipFree(p->gap); hipFree(p->pair_flag); hipFree(p->pair_slot);
-  hipFree(p->pair_row); hipFree(p->row_tok); hipFree(p->row_w); hipFree(p->groups); hipFree(p->glist);
+  hipFree(p->pair_row); hipFree(p->row_tok); hipFree(p->row_w); hipFree(p->groups); hipFree(p->glist); hipFree(p->gdesc); hipFree(p->count_max);
   hipFree(p->dev_header); hipFree(p->hbuf); hipFree(p->pbuf); hipFree(p->fail_dev);
   hipFree(p->key_off_dev); hipFree(p->prof_cnt_dev);
   if (p->rb_host) hipHostFree(p->rb_host);

@@ -551,10 +551,9 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
     g.expert = sm.D[tid];
     g.slot = c == FT_PAIR_MISS_CPU ? -1 : sm.dslot[tid];
     a.groups[tid] = g;
-    if (c == FT_PAIR_HIT)
-      a.glist[hp] = tid;
-    else
-      a.glist[n_hit_list + sm.mpos[tid]] = tid;
+    const int pos = c == FT_PAIR_HIT ? hp : n_hit_list + sm.mpos[tid];
+    a.glist[pos] = tid;
+    a.gdesc[pos] = g;
   }
   if (tid == 0 && shared) {
     GroupDesc g;
@@ -565,6 +564,7 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
     g.slot = -2;
     a.groups[nD] = g;
     a.glist[nHit] = nD;
+    a.gdesc[nHit] = g;
   }
   double g = __builtin_inf();
   for (int tt = tid; tt < ntok; tt += NT) g = fmin(g, lp ? sm.pgap[tt] : a.gap[t0 + tt]);
