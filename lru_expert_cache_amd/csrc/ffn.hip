@@ -794,26 +794,18 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_ffn_ring(FfnArgs a, int SK) 
 // zero activations and are not written.
 constexpr int kWideMaxWaves = 8;
 
+// One wide item: weight tiles rb0 .. rb0 + F - 1 of group g over the full K,
+// the calling wave being K slice w of SK; red is the item's LDS area
+// ([SK][F][NM][64]).  Every thread of the workgroup calls it at the same time
+// (one barrier when SK > 1).
 template <int FMT, bool GATEUP, int KPW, int F>
-__global__ __launch_bounds__(64 * kWideMaxWaves) void k_ffn_wide(FfnArgs a, int SK) {
+__device__ __attribute__((always_inline)) inline void wide_item(const FfnArgs& a, const GroupDesc& g, int rb0, int w,
+                                                                int SK, floatx4* red) {
   constexpr int NM = GATEUP ? 2 : 1;
   constexpr bool F8 = FMT == FT_FMT_FP8_B128;
-  extern __shared__ floatx4 wide_red[];  // [SK][F][NM][64]
-
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lane = threadIdx.x & 63;
   const int q = lane >> 4, n = lane & 15;
-  const MatLayout& m0 = a.lay.m[GATEUP ? 0 : 2];
-  const int nkb = m0.cols / kTileK;
-  const int nfb = m0.rows / (kTileRows * F);
-  // the group is read together with the count (the grid never exceeds the
-  // descriptor array), so that one load latency precedes the weight loads
-  const int item = blockIdx.x;
-  const int gi = item / nfb;
-  const int rb0 = (item - gi * nfb) * F;
-  const GroupDesc g = a.gdesc[gi];
-  const int n_list = min(a.n_list, *a.n_list_dev);
-  // whole workgroup: one group
-  if (item >= n_list * nfb || g.wptr == 0 || g.row_count <= 0) return;
+  const int nkb = a.lay.m[GATEUP ? 0 : 2].cols / kTileK;
   const uint8_t* W = reinterpret_cast<const uint8_t*>(g.wptr);
   const int kb0 = w * KPW;
   const bool rv = n < g.row_count;
@@ -887,7 +879,7 @@ __global__ __launch_bounds__(64 * kWideMaxWaves) void k_ffn_wide(FfnArgs a, int 
 #pragma unroll
     for (int f = 0; f < F; ++f)
 #pragma unroll
-      for (int mi = 0; mi < NM; ++mi) wide_red[((w * F + f) * NM + mi) * 64 + lane] = acc[f][mi];
+      for (int mi = 0; mi < NM; ++mi) red[((w * F + f) * NM + mi) * 64 + lane] = acc[f][mi];
     __syncthreads();
   }
   const float wr = GATEUP ? 0.0f : a.row_w[row];
@@ -898,9 +890,9 @@ __global__ __launch_bounds__(64 * kWideMaxWaves) void k_ffn_wide(FfnArgs a, int 
 #pragma unroll
     for (int mi = 0; mi < NM; ++mi) {
       if (SK > 1) {
-        s[mi] = wide_red[(f * NM + mi) * 64 + lane];
+        s[mi] = red[(f * NM + mi) * 64 + lane];
         for (int k2 = 1; k2 < SK; ++k2) {
-          const floatx4 v = wide_red[((k2 * F + f) * NM + mi) * 64 + lane];
+          const floatx4 v = red[((k2 * F + f) * NM + mi) * 64 + lane];
           s[mi][0] += v[0]; s[mi][1] += v[1]; s[mi][2] += v[2]; s[mi][3] += v[3];
         }
       } else {
@@ -927,6 +919,23 @@ __global__ __launch_bounds__(64 * kWideMaxWaves) void k_ffn_wide(FfnArgs a, int 
           make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16), uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
     }
   }
+}
+
+template <int FMT, bool GATEUP, int KPW, int F>
+__global__ __launch_bounds__(64 * kWideMaxWaves) void k_ffn_wide(FfnArgs a, int SK) {
+  extern __shared__ floatx4 wide_red[];  // [SK][F][NM][64]
+  const MatLayout& m0 = a.lay.m[GATEUP ? 0 : 2];
+  const int nfb = m0.rows / (kTileRows * F);
+  // the group is read together with the count (the grid never exceeds the
+  // descriptor array), so that one load latency precedes the weight loads
+  const int item = blockIdx.x;
+  const int gi = item / nfb;
+  const int rb0 = (item - gi * nfb) * F;
+  const GroupDesc g = a.gdesc[gi];
+  const int n_list = min(a.n_list, *a.n_list_dev);
+  // whole workgroup: one group
+  if (item >= n_list * nfb || g.wptr == 0 || g.row_count <= 0) return;
+  wide_item<FMT, GATEUP, KPW, F>(a, g, rb0, threadIdx.x >> 6, SK, wide_red);
 }
 
 // The wide kernel's (K tiles per wave, weight tiles per item) for a format and
