@@ -206,13 +206,14 @@ def measure_graph(ft, torch, pool, x_all, bias_of, L, B, first, nrep, dev):
     with torch.cuda.graph(g, stream=side):
         for l in range(L):
             ft.ft_moe_layer_forward(pool, l, B, xin[l], bias_of(first, l), outs[l], ft.FT_FWD_DECODE, side, None)
+    ns = x_all.shape[0]
     for s in range(first, first + 2):  # warm replays
-        xin.copy_(x_all[s])
+        xin.copy_(x_all[s % ns])
         g.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(first + 2, first + 2 + nrep):
-        xin.copy_(x_all[s])
+        xin.copy_(x_all[s % ns])
         g.replay()
     torch.cuda.synchronize()
     return B * nrep / (time.perf_counter() - t0)

@@ -17,13 +17,20 @@
 // 128 features (down) or 128 rows x 64 features of both matrices (gate/up);
 // each of its 4 waves owns 64 rows x 64 accumulator columns, i.e. 16 MFMA per
 // 128-K step, and eight 16x128 weight tiles are staged per step either way.
-// Per K step the workgroup stages
-// the weight tiles (in the A-operand layout, 1 KB per 16-row tile) and the
-// activation rows (scattered into the B-operand lane layout) in LDS; the next
-// step's global loads are in flight in registers while the MFMAs run.
-// Activation rows past the group's end read a valid dummy line: they only
-// feed output columns that are not written.  Epilogues as the decode FFN:
-// gate/up -> h = bf16(silu(g) * u); down -> p = bf16(w * y).
+//
+// K steps stream through a ring of LDS stages filled by global-to-LDS loads
+// (global_load_lds_dwordx4: lane i of a wave writes 16 bytes at the stage
+// address + 16 i, so a 1 KB weight tile lands in the A-operand lane order as it
+// is stored, and 16 activation rows land in the B-operand lane order when
+// each lane reads its row's piece; the 4-byte form writes lane i at + 4 i and
+// carries the rows' scale bytes).  Every wave issues the same number of loads
+// per stage, so one immediate vmcnt wait plus a barrier makes a stage ready
+// while the later stages stay in flight: a step waits for its own data, not a
+// whole memory latency.  Steps past the end re-load the last step (never
+// used), which keeps the counts exact; the ring is drained before the
+// epilogue.  Activation rows past the group's end read a valid dummy line:
+// they only feed output columns that are not written.  Epilogues as the
+// decode FFN: gate/up -> h = bf16(silu(g) * u); down -> p = bf16(w * y).
 #include "common.h"
 #include "gmem.h"
 
@@ -46,21 +53,36 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
   return uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-template <bool GATEUP, bool ACT_FP4>
-struct MxSmem {
-  static constexpr int BB = ACT_FP4 ? 16 : 32;  // B bytes per lane
-  u32x4 a[2][8][64];                             // 8 weight tiles, A-operand layout
-  uint8_t as[2][8][64];                          // their scale bytes
-  u32x4 b[2][8][64 * (BB / 16)];                 // 8 sub-tiles of 16 rows, B-operand layout
-  uint8_t bs[2][8][64];                          // row scales: [sub-tile][16q + n]
+// One K step's operands in LDS, in the order the MFMAs read them.
+template <bool ACT_FP4>
+struct MxStage {
+  u32x4 a[8][64];                    // 8 weight tiles, A-operand lane order
+  u32x4 b[8][ACT_FP4 ? 64 : 128];    // 16-row sub-tiles: FP4 [lane]; FP8 [half * 64 + lane]
+  uint8_t as[8][64];                 // weight scale bytes [tile][lane]
+  uint32_t bs[kRowsPerTile];         // activation scales of the step: row -> bytes of blocks 0..3
 };
+constexpr int mx_stages(bool act_fp4) { return act_fp4 ? 4 : 3; }  // two workgroups per CU fit
+constexpr int mx_loads_per_stage(bool act_fp4) { return act_fp4 ? 6 : 8; }  // per wave
+
+// s_waitcnt immediate for vmcnt(n) (6-bit count: bits 3:0 and 15:14), no other waits
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+#define FT_L3 __attribute__((address_space(3)))
+// global -> LDS: lane i writes 16 (or 4) bytes at dst + 16 i (+ 4 i); dst uniform over the wave
+__device__ __attribute__((always_inline)) inline void lds_load16(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds((const FT_GLOBAL void*)src, (FT_L3 void*)dst, 16, 0, 0);
+}
+__device__ __attribute__((always_inline)) inline void lds_load4(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds((const FT_GLOBAL void*)src, (FT_L3 void*)dst, 4, 0, 0);
+}
 
 template <bool GATEUP, bool ACT_FP4>
 __global__ __launch_bounds__(256, 2) void k_mx_gemm(MxGemmArgs a) {
   constexpr int NM = GATEUP ? 2 : 1;
   constexpr int FT = feat_tiles(GATEUP);
-  constexpr int BQ = ACT_FP4 ? 1 : 2;  // u32x4 per lane of a B operand
-  __shared__ MxSmem<GATEUP, ACT_FP4> sm;
+  constexpr int S = mx_stages(ACT_FP4);
+  constexpr int LPS = mx_loads_per_stage(ACT_FP4);
+  __shared__ MxStage<ACT_FP4> sm[S];
 
   const int tile = blockIdx.x;
   if (tile >= *a.n_tiles_dev) return;
@@ -69,7 +91,8 @@ __global__ __launch_bounds__(256, 2) void k_mx_gemm(MxGemmArgs a) {
   const int r0 = tt0 * kRowsPerTile;
   if (r0 >= g.row_count) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: layout reads stay scalar
   const int q = lane >> 4, n = lane & 15;
   const int th = w & 1, fh = w >> 1;  // this wave: rows th*64.., features fh*64..
   const MatLayout& m0 = a.lay.m[GATEUP ? 0 : 2];
@@ -80,23 +103,22 @@ __global__ __launch_bounds__(256, 2) void k_mx_gemm(MxGemmArgs a) {
   const int64_t act_pitch = ACT_FP4 ? K / 2 : K;
   const int64_t sc_pitch = K / 32;
 
-  // rows this thread loads: FP4 rounds of 64 rows x 4 chunks, FP8 rounds of 32 rows x 8 chunks
-  constexpr int BR = ACT_FP4 ? 2 : 4;  // load rounds for the B codes
-  int64_t brow[BR];
+  // this lane's activation rows: row n of sub-tiles 2w and 2w+1 (codes), row
+  // 32w + lane for lanes < 32 (scales); -1 past the group's end
+  int64_t boff[2];
 #pragma unroll
-  for (int r = 0; r < BR; ++r) {
-    const int tok = ACT_FP4 ? r * 64 + (tid >> 2) : r * 32 + (tid >> 3);
-    const int rr = r0 + tok;
+  for (int j = 0; j < 2; ++j) {
+    const int rr = r0 + (2 * w + j) * 16 + n;
     const bool ok = rr < g.row_count;
     const int row = g.row_begin + (ok ? rr : 0);
-    brow[r] = ok ? (GATEUP ? int64_t(a.row_tok[row]) : int64_t(row)) : -1;
+    boff[j] = ok ? (GATEUP ? int64_t(a.row_tok[row]) : int64_t(row)) * act_pitch : -1;
   }
-  int64_t srow = -1;  // scale row of threads 0..127
-  if (tid < kRowsPerTile) {
-    const int rr = r0 + tid;
+  int64_t soff = -1;
+  {
+    const int rr = r0 + 32 * w + (lane & 31);
     if (rr < g.row_count) {
       const int row = g.row_begin + rr;
-      srow = GATEUP ? int64_t(a.row_tok[row]) : int64_t(row);
+      soff = (GATEUP ? int64_t(a.row_tok[row]) : int64_t(row)) * sc_pitch;
     }
   }
 
@@ -105,50 +127,27 @@ __global__ __launch_bounds__(256, 2) void k_mx_gemm(MxGemmArgs a) {
   auto chunk_tile = [&](int ci, int kb) -> int64_t {
     return int64_t(fb * 2 * FT + ci % (2 * FT)) * nkb + kb;
   };
-  // one K step's global reads, held in registers until they go to LDS
-  u32x4 ga[2];
-  u32x4 gas = {0u, 0u, 0u, 0u};
-  u32x4 gb[BR];
-  uint32_t gbs = 0;
-  auto load = [&](int kb) {
+  // one K step's loads into a stage: LPS per wave, whatever the wave
+  auto issue = [&](int kb, MxStage<ACT_FP4>& st) {
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int ci = r * 4 + (tid >> 6);
-      ga[r] = gload<u32x4>(W + chunk_mat(ci).codes_off + chunk_tile(ci, kb) * 1024 + lane * 16);
+    for (int j = 0; j < 2; ++j) {
+      const int ci = 2 * w + j;
+      lds_load16(W + chunk_mat(ci).codes_off + chunk_tile(ci, kb) * 1024 + lane * 16, &st.a[ci][0]);
     }
-    if (tid < 32) {
-      const int ci = tid >> 2, part = tid & 3;
-      gas = gload<u32x4>(W + chunk_mat(ci).scales_off + chunk_tile(ci, kb) * 64 + part * 16);
+    if (lane < 8) {
+      // both tiles of this wave belong to one matrix: its layout is uniform
+      const int ci = 2 * w + (lane >> 2), part = lane & 3;
+      lds_load16(W + chunk_mat(2 * w).scales_off + chunk_tile(ci, kb) * 64 + part * 16, &st.as[2 * w][0]);
     }
 #pragma unroll
-    for (int r = 0; r < BR; ++r) {
-      const int c = ACT_FP4 ? (tid & 3) : (tid & 7);
-      const uint8_t* p = brow[r] >= 0
-                             ? a.act_codes + brow[r] * act_pitch + int64_t(kb) * (ACT_FP4 ? 64 : 128) + c * 16
-                             : a.act_codes;
-      gb[r] = *reinterpret_cast<const u32x4*>(p);
+    for (int j = 0; j < 2; ++j) {
+      const uint8_t* src = boff[j] >= 0 ? a.act_codes + boff[j] + int64_t(kb) * (ACT_FP4 ? 64 : 128) + 16 * q
+                                        : a.act_codes;
+      lds_load16(src, &st.b[2 * w + j][0]);
+      if constexpr (!ACT_FP4) lds_load16(boff[j] >= 0 ? src + 64 : src, &st.b[2 * w + j][64]);
     }
-    if (tid < kRowsPerTile)
-      gbs = *reinterpret_cast<const uint32_t*>(srow >= 0 ? a.act_scales + srow * sc_pitch + kb * 4 : a.act_scales);
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int r = 0; r < 2; ++r) sm.a[buf][r * 4 + (tid >> 6)][lane] = ga[r];
-    if (tid < 32) *reinterpret_cast<u32x4*>(&sm.as[buf][tid >> 2][(tid & 3) * 16]) = gas;
-#pragma unroll
-    for (int r = 0; r < BR; ++r) {
-      if constexpr (ACT_FP4) {
-        const int tok = r * 64 + (tid >> 2), c = tid & 3;
-        sm.b[buf][tok >> 4][16 * c + (tok & 15)] = gb[r];
-      } else {
-        const int tok = r * 32 + (tid >> 3), c = tid & 7;
-        sm.b[buf][tok >> 4][2 * (16 * (c & 3) + (tok & 15)) + (c >> 2)] = gb[r];
-      }
-    }
-    if (tid < kRowsPerTile) {
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) sm.bs[buf][tid >> 4][16 * qq + (tid & 15)] = uint8_t(gbs >> (8 * qq));
-    }
+    if (lane < 32)
+      lds_load4(soff >= 0 ? a.act_scales + soff + kb * 4 : a.act_scales, &st.bs[32 * w]);
   };
 
   floatx4 acc[NM][FT][4];
@@ -159,43 +158,47 @@ __global__ __launch_bounds__(256, 2) void k_mx_gemm(MxGemmArgs a) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) acc[mi][ft][t] = {0.f, 0.f, 0.f, 0.f};
 
-  load(0);
-  store(0);
-  __syncthreads();
+#pragma unroll
+  for (int s0 = 0; s0 < S - 1; ++s0) issue(min(s0, nkb - 1), sm[s0]);
   for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < nkb) load(kb + 1);
+    // this step's stage is complete for this wave once the S - 2 later stages
+    // alone are outstanding; the barrier makes it complete for every wave and
+    // ends every wave's reads of the stage the next loads overwrite
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * LPS));
+    __builtin_amdgcn_s_barrier();
+    issue(min(kb + S - 1, nkb - 1), sm[(kb + S - 1) % S]);
+    const MxStage<ACT_FP4>& st = sm[kb % S];
     intx8 B[4];
     int sb[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int st = th * 4 + t;
-      const u32x4 lo = sm.b[buf][st][BQ * lane];
+      const int sti = th * 4 + t;
+      const u32x4 lo = st.b[sti][lane];
       if constexpr (ACT_FP4) {
         B[t] = intx8{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), 0, 0, 0, 0};
       } else {
-        const u32x4 hi = sm.b[buf][st][BQ * lane + 1];
+        const u32x4 hi = st.b[sti][64 + lane];
         B[t] = intx8{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
       }
-      sb[t] = sm.bs[buf][st][lane];
+      sb[t] = reinterpret_cast<const uint8_t*>(st.bs)[(sti * 16 + n) * 4 + q];
     }
 #pragma unroll
     for (int mi = 0; mi < NM; ++mi)
 #pragma unroll
       for (int ft = 0; ft < FT; ++ft) {
         const int ci = mi * 2 * FT + fh * FT + ft;
-        const u32x4 c = sm.a[buf][ci][lane];
+        const u32x4 c = st.a[ci][lane];
         const intx8 A = intx8{int(c[0]), int(c[1]), int(c[2]), int(c[3]), 0, 0, 0, 0};
-        const int sa = sm.as[buf][ci][lane];
+        const int sa = st.as[ci][lane];
 #pragma unroll
         for (int t = 0; t < 4; ++t)
           acc[mi][ft][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               A, B[t], acc[mi][ft][t], 4 /* A: fp4 e2m1 */, ACT_FP4 ? 4 : 0 /* B: fp4 or fp8 e4m3 */, 0, sa, 0,
               sb[t]);
       }
-    if (kb + 1 < nkb) store(buf ^ 1);
-    __syncthreads();
   }
+  // the loads of steps past the end may still be writing LDS
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   // epilogue: lane holds features (fb*2*FT*16 + fh*FT*16 + ft*16 + 4q + i) of row (r0 + th*64 + t*16 + n)
 #pragma unroll
