@@ -12,8 +12,8 @@
 //       in-bounds probe of the instruction).
 // One instruction multiplies a 16x128 weight tile by 128 K of 16 rows.
 //
-// Work: a list of (group, 128-row tile) built by the resolve kernel; grid =
-// (list bound, blocks of output features).  A workgroup computes 128 rows x
+// Work: a list of (group, 128-row tile) built by the resolve kernel, times the
+// blocks of output features; one workgroup per item, in an XCD-aware order.  A workgroup computes 128 rows x
 // 128 features (down) or 128 rows x 64 features of both matrices (gate/up);
 // each of its 4 waves owns 64 rows x 64 accumulator columns, i.e. 16 MFMA per
 // 128-K step, and eight 16x128 weight tiles are staged per step either way.
@@ -40,6 +40,7 @@ namespace {
 
 typedef int intx8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRowsPerTile = 128;  // activation rows per workgroup tile
@@ -84,8 +85,19 @@ __global__ __launch_bounds__(256, 2) void k_mx_gemm(MxGemmArgs a) {
   constexpr int LPS = mx_loads_per_stage(ACT_FP4);
   __shared__ MxStage<ACT_FP4> sm[S];
 
-  const int tile = blockIdx.x;
-  if (tile >= *a.n_tiles_dev) return;
+  // XCD-aware order: items (row tile, feature block) run row-tile-major, and
+  // the item list is cut into 8 contiguous ranges, one per XCD (workgroups
+  // are dispatched to the XCDs round-robin by linear id): an XCD runs all
+  // feature blocks of a row tile (its activations stay in that XCD's L2), then
+  // the next row tile of the same expert (whose weight tiles are still there).
+  // Any dispatch order gives every item exactly once (the grid holds at least
+  // 8 * ceil(items / 8) workgroups).
+  const int nfb = (GATEUP ? a.inter : a.hidden) / feat_per_wg(GATEUP);  // feature blocks
+  const int items = min(*a.n_tiles_dev, a.max_tiles) * nfb;
+  const int lin = int(blockIdx.x), xcd = lin & 7, k = lin >> 3;
+  const int p = int(int64_t(items) * xcd / 8) + k;
+  if (p >= int(int64_t(items) * (xcd + 1) / 8)) return;
+  const int tile = p / nfb;
   const int d = a.tiles[2 * tile], tt0 = a.tiles[2 * tile + 1];
   const GroupDesc g = a.groups[d];
   const int r0 = tt0 * kRowsPerTile;
@@ -98,7 +110,7 @@ __global__ __launch_bounds__(256, 2) void k_mx_gemm(MxGemmArgs a) {
   const MatLayout& m0 = a.lay.m[GATEUP ? 0 : 2];
   const int K = m0.cols;
   const int nkb = K / kTileK;
-  const int fb = blockIdx.y;  // feature block: weight tiles fb*2*FT .. of each matrix
+  const int fb = p - tile * nfb;  // feature block: weight tiles fb*2*FT .. of each matrix
   const uint8_t* W = reinterpret_cast<const uint8_t*>(g.wptr);
   const int64_t act_pitch = ACT_FP4 ? K / 2 : K;
   const int64_t sc_pitch = K / 32;
@@ -150,13 +162,19 @@ __global__ __launch_bounds__(256, 2) void k_mx_gemm(MxGemmArgs a) {
       lds_load4(soff >= 0 ? a.act_scales + soff + kb * 4 : a.act_scales, &st.bs[32 * w]);
   };
 
-  floatx4 acc[NM][FT][4];
+  // FP8 activations: 16x16x128 MFMAs, acc[matrix][16-feature tile][16-row tile];
+  // FP4 x FP4: 32x32x64 MFMAs (measured 1.6x the 16x16x128 FP4 rate on gfx950),
+  // acc32[matrix][32-feature block][32-row block]
+  constexpr int NA = ACT_FP4 ? 1 : NM * FT * 4;
+  constexpr int NB32 = ACT_FP4 ? NM * (FT / 2) * 2 : 1;
+  floatx4 acc[NA];
+  floatx16 acc32[NB32];
 #pragma unroll
-  for (int mi = 0; mi < NM; ++mi)
+  for (int i = 0; i < NA; ++i) acc[i] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ft = 0; ft < FT; ++ft)
+  for (int i = 0; i < NB32; ++i)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) acc[mi][ft][t] = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 16; ++j) acc32[i][j] = 0.f;
 
 #pragma unroll
   for (int s0 = 0; s0 < S - 1; ++s0) issue(min(s0, nkb - 1), sm[s0]);
@@ -168,64 +186,120 @@ __global__ __launch_bounds__(256, 2) void k_mx_gemm(MxGemmArgs a) {
     __builtin_amdgcn_s_barrier();
     issue(min(kb + S - 1, nkb - 1), sm[(kb + S - 1) % S]);
     const MxStage<ACT_FP4>& st = sm[kb % S];
-    intx8 B[4];
-    int sb[4];
+    if constexpr (ACT_FP4) {
+      // 32x32x64 operands gathered from the 16x16x128-ordered stage: lane l
+      // takes row (or token) l % 32 -- tile (l % 32) / 16, row l % 16 -- and
+      // the 32-K block 2h + l / 32 of the 128-K step (h = 0, 1)
+      const int r16 = lane & 15, hi16 = (lane >> 4) & 1, kq = lane >> 5;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int sti = th * 4 + t;
-      const u32x4 lo = st.b[sti][lane];
-      if constexpr (ACT_FP4) {
-        B[t] = intx8{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), 0, 0, 0, 0};
-      } else {
+      for (int h = 0; h < 2; ++h) {
+        const int qq = 2 * h + kq;
+        intx8 B[2];
+        int sb[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const int sti = th * 4 + rb * 2 + hi16;
+          const u32x4 v = st.b[sti][16 * qq + r16];
+          B[rb] = intx8{int(v[0]), int(v[1]), int(v[2]), int(v[3]), 0, 0, 0, 0};
+          sb[rb] = reinterpret_cast<const uint8_t*>(st.bs)[(sti * 16 + r16) * 4 + qq];
+        }
+#pragma unroll
+        for (int mi = 0; mi < NM; ++mi)
+#pragma unroll
+          for (int f2 = 0; f2 < FT / 2; ++f2) {
+            const int ci = mi * 2 * FT + fh * FT + 2 * f2 + hi16;
+            const u32x4 c = st.a[ci][16 * qq + r16];
+            const intx8 A = intx8{int(c[0]), int(c[1]), int(c[2]), int(c[3]), 0, 0, 0, 0};
+            const int sa = st.as[ci][16 * qq + r16];
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+              floatx16& ac = acc32[(mi * (FT / 2) + f2) * 2 + rb];
+              ac = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B[rb], ac, 4, 4, 0, sa, 0, sb[rb]);
+            }
+          }
+      }
+    } else {
+      intx8 B[4];
+      int sb[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int sti = th * 4 + t;
+        const u32x4 lo = st.b[sti][lane];
         const u32x4 hi = st.b[sti][64 + lane];
         B[t] = intx8{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+        sb[t] = reinterpret_cast<const uint8_t*>(st.bs)[(sti * 16 + n) * 4 + q];
       }
-      sb[t] = reinterpret_cast<const uint8_t*>(st.bs)[(sti * 16 + n) * 4 + q];
+#pragma unroll
+      for (int mi = 0; mi < NM; ++mi)
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft) {
+          const int ci = mi * 2 * FT + fh * FT + ft;
+          const u32x4 c = st.a[ci][lane];
+          const intx8 A = intx8{int(c[0]), int(c[1]), int(c[2]), int(c[3]), 0, 0, 0, 0};
+          const int sa = st.as[ci][lane];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            floatx4& ac = acc[(mi * FT + ft) * 4 + t];
+            ac = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[t], ac, 4 /* A: fp4 e2m1 */,
+                                                                 0 /* B: fp8 e4m3 */, 0, sa, 0, sb[t]);
+          }
+        }
     }
-#pragma unroll
-    for (int mi = 0; mi < NM; ++mi)
-#pragma unroll
-      for (int ft = 0; ft < FT; ++ft) {
-        const int ci = mi * 2 * FT + fh * FT + ft;
-        const u32x4 c = st.a[ci][lane];
-        const intx8 A = intx8{int(c[0]), int(c[1]), int(c[2]), int(c[3]), 0, 0, 0, 0};
-        const int sa = st.as[ci][lane];
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          acc[mi][ft][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              A, B[t], acc[mi][ft][t], 4 /* A: fp4 e2m1 */, ACT_FP4 ? 4 : 0 /* B: fp4 or fp8 e4m3 */, 0, sa, 0,
-              sb[t]);
-      }
   }
   // the loads of steps past the end may still be writing LDS
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
-  // epilogue: lane holds features (fb*2*FT*16 + fh*FT*16 + ft*16 + 4q + i) of row (r0 + th*64 + t*16 + n)
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int r = r0 + th * 64 + t * 16 + n;
-    if (r >= g.row_count) continue;
+  // epilogue: 4 consecutive features of one row per store; gate/up ->
+  // h = bf16(silu(g) * u), down -> p = bf16(w * y)
+  auto emit = [&](int rloc, int o0, const float (&gv)[4], const float (&uv)[4]) {
+    const int r = r0 + rloc;
+    if (r >= g.row_count) return;
     const int row = g.row_begin + r;
+    uint16_t hv[4];
+    if constexpr (GATEUP) {
 #pragma unroll
-    for (int ft = 0; ft < FT; ++ft) {
-      const int o0 = fb * feat_per_wg(GATEUP) + fh * FT * 16 + ft * 16 + 4 * q;
-      uint16_t hv[4];
-      if constexpr (GATEUP) {
+      for (int i = 0; i < 4; ++i) hv[i] = f32_to_bf16_rne(gv[i] / (1.0f + expf(-gv[i])) * uv[i]);
+      *reinterpret_cast<uint2*>(a.out + int64_t(row) * a.inter + o0) =
+          make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16), uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
+    } else {
+      const float wr = a.row_w[row];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hv[i] = f32_to_bf16_rne(wr * gv[i]);
+      *reinterpret_cast<uint2*>(a.out + int64_t(row) * a.hidden + o0) =
+          make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16), uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
+    }
+  };
+  const int fbase = fb * feat_per_wg(GATEUP) + fh * FT * 16;
+  if constexpr (ACT_FP4) {
+    // 32x32 result: value j of lane l is feature 8*(j/4) + 4*(l/32) + j%4, token l%32
+#pragma unroll
+    for (int f2 = 0; f2 < FT / 2; ++f2)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) {
+          float gv[4], uv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            gv[i] = acc32[(0 * (FT / 2) + f2) * 2 + rb][4 * jg + i];
+            uv[i] = GATEUP ? acc32[((NM - 1) * (FT / 2) + f2) * 2 + rb][4 * jg + i] : 0.0f;
+          }
+          emit(th * 64 + rb * 32 + (lane & 31), fbase + f2 * 32 + 8 * jg + 4 * (lane >> 5), gv, uv);
+        }
+  } else {
+    // 16x16 result: value i of lane l is feature 4*(l/16) + i, row l%16
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft) {
+        float gv[4], uv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float gv = acc[0][ft][t][i], uv = acc[1][ft][t][i];
-          hv[i] = f32_to_bf16_rne(gv / (1.0f + expf(-gv)) * uv);
+          gv[i] = acc[(0 * FT + ft) * 4 + t][i];
+          uv[i] = GATEUP ? acc[((NM - 1) * FT + ft) * 4 + t][i] : 0.0f;
         }
-        *reinterpret_cast<uint2*>(a.out + int64_t(row) * a.inter + o0) =
-            make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16), uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
-      } else {
-        const float wr = a.row_w[row];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) hv[i] = f32_to_bf16_rne(wr * acc[0][ft][t][i]);
-        *reinterpret_cast<uint2*>(a.out + int64_t(row) * a.hidden + o0) =
-            make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16), uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
+        emit(th * 64 + t * 16 + n, fbase + ft * 16 + 4 * q, gv, uv);
       }
-    }
   }
 }
 
@@ -236,7 +310,10 @@ int mx_gemm_rows_per_tile() { return kRowsPerTile; }
 hipError_t launch_mx_gemm(const MxGemmArgs& a, bool gateup, bool act_fp4, hipStream_t s, Ev ev) {
   const int outs = gateup ? a.inter : a.hidden;
   if (outs % feat_per_wg(gateup)) return hipErrorInvalidValue;
-  const dim3 grid(a.max_tiles, outs / feat_per_wg(gateup));
+  // one workgroup per (row tile, feature block) item, at least 8 * ceil(items / 8)
+  const int nfb = outs / feat_per_wg(gateup);
+  const int64_t bound = int64_t(a.max_tiles) * nfb;
+  const dim3 grid(unsigned((bound + 7) / 8 * 8));
   if (gateup) {
     if (act_fp4)
       ft_launch(k_mx_gemm<true, true>, grid, dim3(256), s, ev, a);
