@@ -22,6 +22,7 @@ constexpr int kMaxTopK = 16;
 constexpr int kTileRows = 16;     // rows of one weight tile (MFMA M)
 constexpr int kTileK = 128;       // K extent of one weight tile
 constexpr int kResolveThreads = 1024;
+constexpr int kGroupTok = 16;    // tokens of a group's first rows kept beside its descriptor
 constexpr int kMaxSlots = 65536;  // pool slots (LDS bitmap of protected slots in resolve)
 
 // ------------------------------------------------------------ device expert layout
@@ -62,13 +63,18 @@ void unpack_row_f64(const ExpertLayout& L, const uint8_t* dev_blob, int m, int r
 void unpack_matrix_f32(const ExpertLayout& L, const uint8_t* dev_blob, int m, float* out);
 
 // ------------------------------------------------------------ per-call device records
-struct GroupDesc {
+struct alignas(64) GroupDesc {
   uint64_t wptr;       // device address of the expert (device layout)
   int32_t row_begin;   // first row of the group in the grouped order
   int32_t row_count;   // rows (pairs) of the group
   int32_t expert;      // expert index (E for the shared expert)
   int32_t slot;        // pool slot, -1 for host-computed, -2 for the shared expert
+  // run-list entries: the tokens of the group's first kGroupTok rows (low 16
+  // bits), so that a decode FFN gets its activation rows from the same load
+  // as the descriptor; read only when every group has at most kGroupTok rows
+  uint16_t tok[kGroupTok];
 };
+static_assert(sizeof(GroupDesc) == 64, "one 64-byte load per descriptor");
 
 // Header the resolve kernel writes into mapped pinned memory for the host.
 struct ResolveHeader {

@@ -793,14 +793,17 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_ffn_ring(FfnArgs a, int SK) 
 // weight tiles v, v + SK, ...  Missing rows (beyond the group's count) use
 // zero activations and are not written.
 constexpr int kWideMaxWaves = 8;
+static_assert(kGroupTok >= kTileRows, "the wide kernel reads its rows' tokens from the run-list entry");
+static_assert(offsetof(GroupDesc, tok) == 24 && sizeof(GroupDesc) == 64, "descriptor dwords as the wide kernel reads them");
+typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 
 // One wide item: weight tiles rb0 .. rb0 + F - 1 of group g over the full K,
 // the calling wave being K slice w of SK; red is the item's LDS area
-// ([SK][F][NM][64]).  Every thread of the workgroup calls it at the same time
-// (one barrier when SK > 1).
+// ([SK][F][NM][64]); tok (gate/up) is the token of the lane's row.  Every
+// thread of the workgroup calls it at the same time (one barrier when SK > 1).
 template <int FMT, bool GATEUP, int KPW, int F>
 __device__ __attribute__((always_inline)) inline void wide_item(const FfnArgs& a, const GroupDesc& g, int rb0, int w,
-                                                                int SK, floatx4* red) {
+                                                                int SK, floatx4* red, int tok) {
   constexpr int NM = GATEUP ? 2 : 1;
   constexpr bool F8 = FMT == FT_FMT_FP8_B128;
   const int lane = threadIdx.x & 63;
@@ -810,8 +813,6 @@ __device__ __attribute__((always_inline)) inline void wide_item(const FfnArgs& a
   const int kb0 = w * KPW;
   const bool rv = n < g.row_count;
   const int row = g.row_begin + (rv ? n : 0);
-  int tok = 0;
-  if constexpr (GATEUP) tok = a.row_tok[row];
 
   TileRegs<FMT> wt[F][NM][KPW];
   float4 ws[F][NM][KPW];
@@ -924,18 +925,33 @@ __device__ __attribute__((always_inline)) inline void wide_item(const FfnArgs& a
 template <int FMT, bool GATEUP, int KPW, int F>
 __global__ __launch_bounds__(64 * kWideMaxWaves) void k_ffn_wide(FfnArgs a, int SK) {
   extern __shared__ floatx4 wide_red[];  // [SK][F][NM][64]
-  const MatLayout& m0 = a.lay.m[GATEUP ? 0 : 2];
-  const int nfb = m0.rows / (kTileRows * F);
-  // the group is read together with the count (the grid never exceeds the
-  // descriptor array), so that one load latency precedes the weight loads
-  const int item = blockIdx.x;
-  const int gi = item / nfb;
-  const int rb0 = (item - gi * nfb) * F;
-  const GroupDesc g = a.gdesc[gi];
+  // grid: x = block of F weight tiles, y = run-list entry (consecutive
+  // workgroups share a group).  The group is read together with the count
+  // (the grid never exceeds the descriptor array), so that one load latency
+  // precedes the weight loads.
+  const int gi = blockIdx.y;
+  const int rb0 = int(blockIdx.x) * F;
+  // the descriptor and the tokens of its rows in one 64-byte load, so that
+  // the activation addresses are known as soon as the weight addresses (no
+  // second load that the descriptor's row offset would feed)
+  const i32x16 dv = gload<i32x16>(a.gdesc + gi);
+  GroupDesc g{};
+  g.wptr = uint64_t(uint32_t(dv[0])) | (uint64_t(uint32_t(dv[1])) << 32);
+  g.row_begin = dv[2];
+  g.row_count = dv[3];
   const int n_list = min(a.n_list, *a.n_list_dev);
   // whole workgroup: one group
-  if (item >= n_list * nfb || g.wptr == 0 || g.row_count <= 0) return;
-  wide_item<FMT, GATEUP, KPW, F>(a, g, rb0, threadIdx.x >> 6, SK, wide_red);
+  if (gi >= n_list || g.wptr == 0 || g.row_count <= 0) return;
+  int tok = 0;
+  if constexpr (GATEUP) {
+    // token of row (lane & 15): 16-bit entry of dword 6 + (lane & 15) / 2
+    const int n = threadIdx.x & 15;
+    uint32_t wd = 0;
+#pragma unroll
+    for (int j = 0; j < kGroupTok / 2; ++j) wd = (n >> 1) == j ? uint32_t(dv[6 + j]) : wd;
+    tok = int((n & 1) ? wd >> 16 : wd & 0xFFFFu);
+  }
+  wide_item<FMT, GATEUP, KPW, F>(a, g, rb0, threadIdx.x >> 6, SK, wide_red, tok);
 }
 
 // The wide kernel's (K tiles per wave, weight tiles per item) for a format and
@@ -983,7 +999,8 @@ hipError_t launch_wide_k(const FfnArgs& a, hipStream_t st, Ev ev, bool* done) {
     std::snprintf(prm, sizeof(prm), "%d K tiles x %d waves, %d weight tiles", KPW, SK, F);
     note_kernel(GATEUP, "k_ffn_wide", FMT, prm);
   }
-  ft_launch_lds(k_ffn_wide<FMT, GATEUP, KPW, F>, dim3(unsigned(items)), dim3(64 * SK), lds, st, ev, a, SK);
+  ft_launch_lds(k_ffn_wide<FMT, GATEUP, KPW, F>, dim3(unsigned(m.rows / (kTileRows * F)), unsigned(a.n_list)),
+                dim3(64 * SK), lds, st, ev, a, SK);
   return hipGetLastError();
 }
 
@@ -1046,11 +1063,14 @@ hipError_t launch_wide(const FfnArgs& a, hipStream_t st, Ev ev, bool* done) {
     if (nkb % KPW == 0 && nkb / KPW <= kWideMaxWaves && nrb % F == 0)                             \
       return launch_wide_k<FMT, GATEUP, KPW, F>(a, st, ev, done);                                  \
   }
+  // (measured on the Qwen-A3B decode shape: with 8 and 17 groups gate/up
+  // 4 x 2 beat 4 x 1 by 10-13%, with 31 and 64 it tied 4 x 3; down 2 x 4 beat
+  // 3 x 8 by 7-20% from 8 to 64 groups)
   if (GATEUP) {
     if (!few) { FT_WIDE_TRY(4, 3) }
-    FT_WIDE_TRY(4, 1) FT_WIDE_TRY(7, 1) FT_WIDE_TRY(6, 1) FT_WIDE_TRY(2, 2) FT_WIDE_TRY(3, 1) FT_WIDE_TRY(1, 2)
+    FT_WIDE_TRY(4, 2) FT_WIDE_TRY(4, 1) FT_WIDE_TRY(7, 1) FT_WIDE_TRY(6, 1) FT_WIDE_TRY(2, 2) FT_WIDE_TRY(3, 1) FT_WIDE_TRY(1, 2)
   } else {
-    if (!few) { FT_WIDE_TRY(3, 8) FT_WIDE_TRY(4, 4) FT_WIDE_TRY(2, 8) FT_WIDE_TRY(4, 2) }
+    if (!few) { FT_WIDE_TRY(2, 4) FT_WIDE_TRY(3, 8) FT_WIDE_TRY(4, 4) FT_WIDE_TRY(2, 8) FT_WIDE_TRY(4, 2) }
     FT_WIDE_TRY(3, 2) FT_WIDE_TRY(4, 1) FT_WIDE_TRY(2, 2) FT_WIDE_TRY(1, 4) FT_WIDE_TRY(7, 1) FT_WIDE_TRY(6, 1)
   }
 #undef FT_WIDE_TRY

@@ -1006,13 +1006,15 @@ int ft_moe_init_pool(const ft_moe_config* cfg, const ft_moe_weights* wts, ft_moe
         (rc = dev_alloc(&p->tab.lru[1], C)) || (rc = dev_alloc(&p->tab.lru_cur, 1)) ||
         (rc = dev_alloc(&p->tab.clock, 1)) || (rc = dev_alloc(&p->tab.stats, int64_t(L) * ST_COUNT)) ||
         (rc = dev_alloc(&p->tab.min_gap, L)) || (rc = dev_alloc(&p->groups, E + 2)) ||
-        (rc = dev_alloc(&p->glist, E + 2)) || (rc = dev_alloc(&p->gdesc, E + 2)) || (rc = dev_alloc(&p->count_max, 1)) || (rc = dev_alloc(&p->dev_header, 16)) ||
+        (rc = dev_alloc(&p->glist, E + 2)) || (rc = dev_alloc(&p->gdesc, E + 2)) ||
+        (rc = dev_alloc(&p->count_max, 1)) || (rc = dev_alloc(&p->dev_header, 16)) ||
         (rc = dev_alloc(&p->fail_dev, 2 * E + 2)) || (rc = dev_alloc(&p->key_off_dev, int64_t(L) * E)) ||
         (rc = dev_alloc(&p->prof_cnt_dev, 24))) {
       ft_moe_destroy_pool(p.release());
       return rc;
     }
     FT_HIP_CHECK(hipMemset(p->tab.key2slot, 0xFF, size_t(L) * E * 4));
+    FT_HIP_CHECK(hipMemset(p->gdesc, 0, size_t(E + 2) * sizeof(GroupDesc)));
     FT_HIP_CHECK(hipMemset(p->tab.slot_key, 0xFF, size_t(C) * 4));
     FT_HIP_CHECK(hipMemset(p->tab.lru_cur, 0, 4));
     FT_HIP_CHECK(hipMemset(p->tab.slot_last, 0, size_t(C) * 8));
@@ -1507,6 +1509,7 @@ int ft_moe_measure_mode(ft_moe_pool* p, int32_t tokens, int32_t apply, ft_moe_mo
         g[e].expert = e;
         g[e].slot = -1;
         for (int t = 0; t < T; ++t) rt[size_t(e) * T + t] = t;
+        for (int t = 0; t < kGroupTok; ++t) g[e].tok[t] = uint16_t(t < T ? t : 0);
       }
       FT_HIP_CHECK(hipMemcpy(p->gdesc, g.data(), g.size() * sizeof(GroupDesc), hipMemcpyHostToDevice));
       FT_HIP_CHECK(hipMemcpy(p->row_tok, rt.data(), rt.size() * 4, hipMemcpyHostToDevice));

@@ -32,6 +32,15 @@ constexpr int NW = NT / 64;
 constexpr int kLdsPairs = 2048;  // pairs of a wave kept in LDS (decode calls with T*k up to this)
 constexpr int kPf = 4;           // recency-order entries per thread read at kernel start (C <= 4096)
 
+// A descriptor's fields other than its tokens (which other threads write)
+__device__ inline void put_desc_head(GroupDesc& d, uint64_t wptr, int row_begin, int row_count, int expert, int slot) {
+  d.wptr = wptr;
+  d.row_begin = row_begin;
+  d.row_count = row_count;
+  d.expert = expert;
+  d.slot = slot;
+}
+
 struct ResolveSmem {
   int first[kMaxExperts];
   int last[kMaxExperts];
@@ -41,6 +50,7 @@ struct ResolveSmem {
   int cls[kMaxExperts];
   int dslot[kMaxExperts];
   int mpos[kMaxExperts];
+  int gpos[kMaxExperts];  // position of each group in the run list
   int off[kMaxExperts];
   int sm[kMaxExperts];
   int wcnt[NW][kMaxExperts];
@@ -521,50 +531,49 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
     const int o = block_exscan(tid < nD ? sm.cnt[tid] : 0, sm.wbuf, par, &tot);
     if (tid < nD) sm.off[tid] = o;
   }
+  // run-list positions: hits [+ the shared expert], streamed, host
+  int nHit;
+  const bool ishit = tid < nD && sm.cls[tid] == FT_PAIR_HIT;
+  const int hp = block_excount(ishit, sm.wbuf, par, &nHit);
+  const bool shared = a.shared_ptr != 0;
+  const int n_hit_list = nHit + (shared ? 1 : 0);
+  if (tid < nD) sm.gpos[tid] = ishit ? hp : n_hit_list + sm.mpos[tid];
   __syncthreads();
+  // rows; the tokens of a group's first kGroupTok rows also go into its
+  // run-list entry, where a decode FFN reads them with the descriptor (the
+  // descriptor's other fields are written below, field by field, so the two
+  // writes never overlap)
   for (int i = tid; i < P; i += NT) {
     const int d = sm.dix[SEL(i)];
-    const int row = sm.off[d] + (lp ? sm.prow[i] : a.pair_row[pb + i]);
+    const int r = lp ? sm.prow[i] : a.pair_row[pb + i];
+    const int row = sm.off[d] + r;
     a.pair_row[pb + i] = row;
     a.row_tok[row] = t0 + i / k;
     a.row_w[row] = lp ? sm.pw[i] : a.w[pb + i];
+    if (r < kGroupTok) a.gdesc[sm.gpos[d]].tok[r] = uint16_t(t0 + i / k);
   }
-  const bool shared = a.shared_ptr != 0;
   if (shared) {
     for (int tt = tid; tt < ntok; tt += NT) {
       a.row_tok[P + tt] = t0 + tt;
       a.row_w[P + tt] = 1.0f;
+      if (tt < kGroupTok) a.gdesc[nHit].tok[tt] = uint16_t(t0 + tt);
     }
   }
 
-  // ---- 10. group descriptors and run lists (hits [+ shared], streamed, host)
-  int nHit;
-  const bool ishit = tid < nD && sm.cls[tid] == FT_PAIR_HIT;
-  const int hp = block_excount(ishit, sm.wbuf, par, &nHit);
-  const int n_hit_list = nHit + (shared ? 1 : 0);
+  // ---- 10. group descriptors and run lists
   if (tid < nD) {
     const int c = sm.cls[tid];
-    GroupDesc g;
-    g.wptr = c == FT_PAIR_MISS_CPU ? 0ull : a.arena + uint64_t(sm.dslot[tid]) * uint64_t(a.slot_bytes);
-    g.row_begin = sm.off[tid];
-    g.row_count = sm.cnt[tid];
-    g.expert = sm.D[tid];
-    g.slot = c == FT_PAIR_MISS_CPU ? -1 : sm.dslot[tid];
-    a.groups[tid] = g;
-    const int pos = c == FT_PAIR_HIT ? hp : n_hit_list + sm.mpos[tid];
+    const uint64_t wptr = c == FT_PAIR_MISS_CPU ? 0ull : a.arena + uint64_t(sm.dslot[tid]) * uint64_t(a.slot_bytes);
+    const int slot = c == FT_PAIR_MISS_CPU ? -1 : sm.dslot[tid];
+    put_desc_head(a.groups[tid], wptr, sm.off[tid], sm.cnt[tid], sm.D[tid], slot);
+    const int pos = sm.gpos[tid];
     a.glist[pos] = tid;
-    a.gdesc[pos] = g;
+    put_desc_head(a.gdesc[pos], wptr, sm.off[tid], sm.cnt[tid], sm.D[tid], slot);
   }
   if (tid == 0 && shared) {
-    GroupDesc g;
-    g.wptr = a.shared_ptr;
-    g.row_begin = P;
-    g.row_count = ntok;
-    g.expert = E;
-    g.slot = -2;
-    a.groups[nD] = g;
+    put_desc_head(a.groups[nD], a.shared_ptr, P, ntok, E, -2);
     a.glist[nHit] = nD;
-    a.gdesc[nHit] = g;
+    put_desc_head(a.gdesc[nHit], a.shared_ptr, P, ntok, E, -2);
   }
   double g = __builtin_inf();
   for (int tt = tid; tt < ntok; tt += NT) g = fmin(g, lp ? sm.pgap[tt] : a.gap[t0 + tt]);
