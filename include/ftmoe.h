@@ -275,7 +275,9 @@ int ft_moe_host_expert_rate(ft_moe_pool *p, int32_t layer, int32_t tokens, int32
  * FFN stages count the weights of the groups they run plus their activation
  * rows read and written; the copy stage counts the expert bytes streamed. */
 enum { FT_STAGE_ROUTER = 0, FT_STAGE_TOPK, FT_STAGE_RESOLVE, FT_STAGE_FFN_GATEUP, FT_STAGE_FFN_DOWN,
-       FT_STAGE_COMBINE, FT_STAGE_COPY, FT_STAGE_COUNT };
+       FT_STAGE_COMBINE, FT_STAGE_COPY,
+       FT_STAGE_ACT_QUANT, /* MX activation modes: quantising x or h and laying the rows out as GEMM tiles */
+       FT_STAGE_COUNT };
 typedef struct {
   double ms[FT_STAGE_COUNT];        /* summed event-measured durations */
   double bytes[FT_STAGE_COUNT];     /* summed algorithmic bytes */

@@ -139,7 +139,8 @@ struct ResolveArgs {
   int32_t* glist;          // [max groups + 1]: hit list, then streamed, then host
   GroupDesc* gdesc;        // [max groups + 1]: the descriptors in glist order
   int32_t* dev_header;     // device copy of the header counts (for early-exit kernels)
-  int32_t* tiles;          // prefill: (group, 64-row tile) pairs for the MX GEMM, or null
+  int32_t* tiles;          // prefill: (group, 128-row tile) pairs for the MX GEMM, or null
+  int32_t* row_slot;       // prefill (with tiles): each row's slot in the MX GEMM activation tiles
   int32_t tile_rows;       // rows per tile
   // mapped pinned memory for the host (decode only), may be 0
   uint8_t* host_rb;
@@ -227,17 +228,43 @@ struct MissCopyArgs {
 hipError_t launch_miss_copy(const MissCopyArgs& a, int workgroups, hipStream_t s, Ev ev = {});
 
 // mxq.hip: bf16 rows [rows][K] -> MX codes (FP4 [rows][K/2] or FP8 [rows][K]) + E8M0 scales [rows][K/32]
-hipError_t launch_mx_quant(const uint16_t* in, int rows, int K, bool fp4, uint8_t* codes, uint8_t* scales,
-                           hipStream_t s);
+// Activation tiles of the MX GEMM: for each (row tile, 128-K step) of the
+// work list, the tile's 128 rows of quantised codes in the GEMM's B-operand
+// lane order, one contiguous block per 16-row sub-tile, and their scales.
+//   FP4: block (tile, kb) = 8 sub-tiles x 1 KB; lane 16q + n of sub-tile s
+//        holds row 16s + n, K 128kb + 32q .. + 31 (even element in the low nibble).
+//   FP8: block (tile, kb) = 8 sub-tiles x 2 KB; half h (1 KB each), lane
+//        16q + n: row 16s + n, K 128kb + 64h + 16q .. + 15.
+//   scales: block (tile, kb) = 128 rows x 4 bytes (the rows' scales of the
+//        step's four 32-blocks), 512 bytes.
+// A row's slot is tile * 128 + (row in tile) (resolve writes it per row).
+// Slots past a group's end are not written: their stale values only reach
+// output rows that the GEMM does not store.
+constexpr int kMxTileRows = 128;
+constexpr int64_t mx_tile_code_bytes(bool fp4) { return fp4 ? 8192 : 16384; }  // per (tile, K step)
+constexpr int64_t kMxTileScaleBytes = 512;                                     // per (tile, K step)
+// mxq.hip: MX quantisation of bf16 rows straight into the activation tiles.
+// Source row r goes to the slots of grouped rows pair_row[r*k + j] (j < k)
+// and, if shared_row0 >= 0, of grouped row shared_row0 + r (gate/up input x
+// by token); with pair_row null, to the slot of grouped row r (down input h).
+struct MxQuantArgs {
+  const uint16_t* in;         // [rows][K] bf16
+  int32_t rows, K;
+  const int32_t* pair_row;    // [rows * k] or null
+  int32_t k, shared_row0;
+  const int32_t* row_slot;    // grouped row -> slot
+  uint8_t* out_codes;         // [tiles][K/128] blocks
+  uint8_t* out_scales;
+};
+hipError_t launch_mx_quant_tiles(const MxQuantArgs& a, bool fp4, hipStream_t s);
 // gemm_mx.hip: grouped prefill GEMM on the block-scaled MFMA (MXFP4 weights, MX activations)
 struct MxGemmArgs {
   const GroupDesc* groups;
   const int32_t* tiles;       // (group, tile) pairs
   const int32_t* n_tiles_dev; // number of valid pairs
   int32_t max_tiles;          // grid bound
-  const uint8_t* act_codes;   // gate/up: quantised x [T][.] by token; down: quantised h [rows][.]
+  const uint8_t* act_codes;   // activation tiles (launch_mx_quant_tiles layout)
   const uint8_t* act_scales;
-  const int32_t* row_tok;     // gate/up: token of each row
   const float* row_w;         // down: routing weight of each row
   uint16_t* out;              // gate/up: h [rows][I]; down: p [rows][H]
   int32_t hidden, inter;

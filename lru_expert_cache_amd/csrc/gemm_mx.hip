@@ -21,15 +21,18 @@
 // K steps stream through a ring of LDS stages filled by global-to-LDS loads
 // (global_load_lds_dwordx4: lane i of a wave writes 16 bytes at the stage
 // address + 16 i, so a 1 KB weight tile lands in the A-operand lane order as it
-// is stored, and 16 activation rows land in the B-operand lane order when
-// each lane reads its row's piece; the 4-byte form writes lane i at + 4 i and
-// carries the rows' scale bytes).  Every wave issues the same number of loads
+// is stored, and so does a 1 KB activation sub-tile of the tile layout that
+// launch_mx_tile_gather writes; the 4-byte form writes lane i at + 4 i and
+// carries the rows' scale bytes).  Every load reads contiguous bytes: the
+// gathered rows of the activations (64 bytes of a row per step, and 4 scale
+// bytes) spread a step over ~3x the cache lines, which the L1's outstanding
+// misses then limit.  Every wave issues the same number of loads
 // per stage, so one immediate vmcnt wait plus a barrier makes a stage ready
 // while the later stages stay in flight: a step waits for its own data, not a
 // whole memory latency.  Steps past the end re-load the last step (never
 // used), which keeps the counts exact; the ring is drained before the
-// epilogue.  Activation rows past the group's end read a valid dummy line:
-// they only feed output columns that are not written.  Epilogues as the
+// epilogue.  Activation rows past the group's end are zeros in the tile
+// layout and feed output columns that are not written.  Epilogues as the
 // decode FFN: gate/up -> h = bf16(silu(g) * u); down -> p = bf16(w * y).
 #include "common.h"
 #include "gmem.h"
@@ -43,27 +46,44 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kRowsPerTile = 128;  // activation rows per workgroup tile
+constexpr int kRowsPerTile = kMxTileRows;  // activation rows per workgroup tile
 // weight tiles of 16 features per wave and per matrix (64 accumulator columns a wave)
 constexpr int feat_tiles(bool gateup) { return gateup ? 2 : 4; }
-// output features per workgroup (per matrix)
-constexpr int feat_per_wg(bool gateup) { return 2 * feat_tiles(gateup) * 16; }
+// output features per workgroup (per matrix) with WF wave columns of 64
+// accumulator columns each (and two wave rows of 64 rows)
+constexpr int feat_per_wg(bool gateup, int wf) { return wf * feat_tiles(gateup) * 16; }
 
 __device__ inline uint16_t f32_to_bf16_rne(float f) {
   const uint32_t u = __float_as_uint(f);
   return uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+// silu(g) = g / (1 + e^-g) from the hardware exp2 and reciprocal (each about
+// 1 ulp in fp32), far inside the bf16 rounding of h that follows.  For
+// g -> -inf, e^-g overflows to inf and the reciprocal gives 0 (silu -> -0).
+__device__ inline float silu_fast(float g) {
+  const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+  return g * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
 // One K step's operands in LDS, in the order the MFMAs read them.
-template <bool ACT_FP4>
+template <bool ACT_FP4, int WF>
 struct MxStage {
-  u32x4 a[8][64];                    // 8 weight tiles, A-operand lane order
+  u32x4 a[4 * WF][64];               // 4 WF weight tiles, A-operand lane order
   u32x4 b[8][ACT_FP4 ? 64 : 128];    // 16-row sub-tiles: FP4 [lane]; FP8 [half * 64 + lane]
-  uint8_t as[8][64];                 // weight scale bytes [tile][lane]
+  uint8_t as[4 * WF][64];            // weight scale bytes [tile][lane]
   uint32_t bs[kRowsPerTile];         // activation scales of the step: row -> bytes of blocks 0..3
 };
-constexpr int mx_stages(bool act_fp4) { return act_fp4 ? 4 : 3; }  // two workgroups per CU fit
-constexpr int mx_loads_per_stage(bool act_fp4) { return act_fp4 ? 6 : 8; }  // per wave
+// 1 KB activation pieces of a step (FP4: the 8 sub-tiles; FP8: their halves)
+constexpr int mx_pieces(bool act_fp4) { return act_fp4 ? 8 : 16; }
+// ring depth: two workgroups per CU fit with WF 2 (and WF 4 FP4), one otherwise
+constexpr int mx_stages(bool act_fp4, int wf) { return wf == 2 && act_fp4 ? 4 : 3; }
+// loads per wave and stage: 2 weight tiles, their scales, the wave's share of
+// the activation pieces (half a piece when there are more waves than pieces),
+// and its share of the activation scales
+constexpr int mx_loads_per_stage(bool act_fp4, int wf) {
+  return 2 + 1 + (mx_pieces(act_fp4) >= 2 * wf ? mx_pieces(act_fp4) / (2 * wf) : 1) + 1;
+}
 
 // s_waitcnt immediate for vmcnt(n) (6-bit count: bits 3:0 and 15:14), no other waits
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
@@ -77,13 +97,15 @@ __device__ __attribute__((always_inline)) inline void lds_load4(const void* src,
   __builtin_amdgcn_global_load_lds((const FT_GLOBAL void*)src, (FT_L3 void*)dst, 4, 0, 0);
 }
 
-template <bool GATEUP, bool ACT_FP4>
-__global__ __launch_bounds__(256, 2) void k_mx_gemm(MxGemmArgs a) {
+template <bool GATEUP, bool ACT_FP4, int WF>
+__global__ __launch_bounds__(128 * WF) void k_mx_gemm(MxGemmArgs a) {
   constexpr int NM = GATEUP ? 2 : 1;
   constexpr int FT = feat_tiles(GATEUP);
-  constexpr int S = mx_stages(ACT_FP4);
-  constexpr int LPS = mx_loads_per_stage(ACT_FP4);
-  __shared__ MxStage<ACT_FP4> sm[S];
+  constexpr int NW = 2 * WF;        // waves
+  constexpr int TPM = WF * FT;      // weight tiles per matrix and workgroup
+  constexpr int S = mx_stages(ACT_FP4, WF);
+  constexpr int LPS = mx_loads_per_stage(ACT_FP4, WF);
+  __shared__ MxStage<ACT_FP4, WF> sm[S];
 
   // XCD-aware order: items (row tile, feature block) run row-tile-major, and
   // the item list is cut into 8 contiguous ranges, one per XCD (workgroups
@@ -92,7 +114,7 @@ __global__ __launch_bounds__(256, 2) void k_mx_gemm(MxGemmArgs a) {
   // the next row tile of the same expert (whose weight tiles are still there).
   // Any dispatch order gives every item exactly once (the grid holds at least
   // 8 * ceil(items / 8) workgroups).
-  const int nfb = (GATEUP ? a.inter : a.hidden) / feat_per_wg(GATEUP);  // feature blocks
+  const int nfb = (GATEUP ? a.inter : a.hidden) / feat_per_wg(GATEUP, WF);  // feature blocks
   const int items = min(*a.n_tiles_dev, a.max_tiles) * nfb;
   const int lin = int(blockIdx.x), xcd = lin & 7, k = lin >> 3;
   const int p = int(int64_t(items) * xcd / 8) + k;
@@ -110,37 +132,18 @@ __global__ __launch_bounds__(256, 2) void k_mx_gemm(MxGemmArgs a) {
   const MatLayout& m0 = a.lay.m[GATEUP ? 0 : 2];
   const int K = m0.cols;
   const int nkb = K / kTileK;
-  const int fb = p - tile * nfb;  // feature block: weight tiles fb*2*FT .. of each matrix
+  const int fb = p - tile * nfb;  // feature block: weight tiles fb*TPM .. of each matrix
   const uint8_t* W = reinterpret_cast<const uint8_t*>(g.wptr);
-  const int64_t act_pitch = ACT_FP4 ? K / 2 : K;
-  const int64_t sc_pitch = K / 32;
+  // this row tile's activation blocks, one per K step (contiguous sub-tiles
+  // in B-operand lane order, then the rows' scales)
+  const uint8_t* TB = a.act_codes + int64_t(tile) * nkb * mx_tile_code_bytes(ACT_FP4);
+  const uint8_t* TS = a.act_scales + int64_t(tile) * nkb * kMxTileScaleBytes;
 
-  // this lane's activation rows: row n of sub-tiles 2w and 2w+1 (codes), row
-  // 32w + lane for lanes < 32 (scales); -1 past the group's end
-  int64_t boff[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int rr = r0 + (2 * w + j) * 16 + n;
-    const bool ok = rr < g.row_count;
-    const int row = g.row_begin + (ok ? rr : 0);
-    boff[j] = ok ? (GATEUP ? int64_t(a.row_tok[row]) : int64_t(row)) * act_pitch : -1;
-  }
-  int64_t soff = -1;
-  {
-    const int rr = r0 + 32 * w + (lane & 31);
-    if (rr < g.row_count) {
-      const int row = g.row_begin + rr;
-      soff = (GATEUP ? int64_t(a.row_tok[row]) : int64_t(row)) * sc_pitch;
-    }
-  }
-
-  // the 8 staged weight tiles: chunk ci = matrix (ci / (2 FT)), tile fb*2*FT + ci % (2 FT)
-  auto chunk_mat = [&](int ci) -> const MatLayout& { return a.lay.m[GATEUP ? ci / (2 * FT) : 2]; };
-  auto chunk_tile = [&](int ci, int kb) -> int64_t {
-    return int64_t(fb * 2 * FT + ci % (2 * FT)) * nkb + kb;
-  };
+  // the 4 WF staged weight tiles: chunk ci = matrix (ci / TPM), tile fb*TPM + ci % TPM
+  auto chunk_mat = [&](int ci) -> const MatLayout& { return a.lay.m[GATEUP ? ci / TPM : 2]; };
+  auto chunk_tile = [&](int ci, int kb) -> int64_t { return int64_t(fb * TPM + ci % TPM) * nkb + kb; };
   // one K step's loads into a stage: LPS per wave, whatever the wave
-  auto issue = [&](int kb, MxStage<ACT_FP4>& st) {
+  auto issue = [&](int kb, MxStage<ACT_FP4, WF>& st) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int ci = 2 * w + j;
@@ -151,15 +154,19 @@ __global__ __launch_bounds__(256, 2) void k_mx_gemm(MxGemmArgs a) {
       const int ci = 2 * w + (lane >> 2), part = lane & 3;
       lds_load16(W + chunk_mat(2 * w).scales_off + chunk_tile(ci, kb) * 64 + part * 16, &st.as[2 * w][0]);
     }
+    // activation piece pc (1 KB) of the tile layout lands at piece pc of st.b
+    const uint8_t* tb = TB + int64_t(kb) * mx_tile_code_bytes(ACT_FP4) + lane * 16;
+    u32x4* bb = &st.b[0][0];
+    constexpr int PC = mx_pieces(ACT_FP4);
+    if constexpr (PC >= NW) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint8_t* src = boff[j] >= 0 ? a.act_codes + boff[j] + int64_t(kb) * (ACT_FP4 ? 64 : 128) + 16 * q
-                                        : a.act_codes;
-      lds_load16(src, &st.b[2 * w + j][0]);
-      if constexpr (!ACT_FP4) lds_load16(boff[j] >= 0 ? src + 64 : src, &st.b[2 * w + j][64]);
+      for (int j = 0; j < PC / NW; ++j) lds_load16(tb + (w * (PC / NW) + j) * 1024, bb + (w * (PC / NW) + j) * 64);
+    } else {
+      // two waves per piece, half the lanes each (lane i still writes at + 16 i)
+      if ((lane >> 5) == (w & 1)) lds_load16(tb + (w >> 1) * 1024, bb + (w >> 1) * 64);
     }
-    if (lane < 32)
-      lds_load4(soff >= 0 ? a.act_scales + soff + kb * 4 : a.act_scales, &st.bs[32 * w]);
+    constexpr int SL = kRowsPerTile / NW;  // rows of activation scales per wave
+    if (lane < SL) lds_load4(TS + int64_t(kb) * kMxTileScaleBytes + (w * SL + lane) * 4, &st.bs[w * SL]);
   };
 
   // FP8 activations: 16x16x128 MFMAs, acc[matrix][16-feature tile][16-row tile];
@@ -185,7 +192,7 @@ __global__ __launch_bounds__(256, 2) void k_mx_gemm(MxGemmArgs a) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * LPS));
     __builtin_amdgcn_s_barrier();
     issue(min(kb + S - 1, nkb - 1), sm[(kb + S - 1) % S]);
-    const MxStage<ACT_FP4>& st = sm[kb % S];
+    const MxStage<ACT_FP4, WF>& st = sm[kb % S];
     if constexpr (ACT_FP4) {
       // 32x32x64 operands gathered from the 16x16x128-ordered stage: lane l
       // takes row (or token) l % 32 -- tile (l % 32) / 16, row l % 16 -- and
@@ -207,7 +214,7 @@ __global__ __launch_bounds__(256, 2) void k_mx_gemm(MxGemmArgs a) {
         for (int mi = 0; mi < NM; ++mi)
 #pragma unroll
           for (int f2 = 0; f2 < FT / 2; ++f2) {
-            const int ci = mi * 2 * FT + fh * FT + 2 * f2 + hi16;
+            const int ci = mi * TPM + fh * FT + 2 * f2 + hi16;
             const u32x4 c = st.a[ci][16 * qq + r16];
             const intx8 A = intx8{int(c[0]), int(c[1]), int(c[2]), int(c[3]), 0, 0, 0, 0};
             const int sa = st.as[ci][16 * qq + r16];
@@ -233,7 +240,7 @@ __global__ __launch_bounds__(256, 2) void k_mx_gemm(MxGemmArgs a) {
       for (int mi = 0; mi < NM; ++mi)
 #pragma unroll
         for (int ft = 0; ft < FT; ++ft) {
-          const int ci = mi * 2 * FT + fh * FT + ft;
+          const int ci = mi * TPM + fh * FT + ft;
           const u32x4 c = st.a[ci][lane];
           const intx8 A = intx8{int(c[0]), int(c[1]), int(c[2]), int(c[3]), 0, 0, 0, 0};
           const int sa = st.as[ci][lane];
@@ -250,28 +257,36 @@ __global__ __launch_bounds__(256, 2) void k_mx_gemm(MxGemmArgs a) {
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   // epilogue: 4 consecutive features of one row per store; gate/up ->
-  // h = bf16(silu(g) * u), down -> p = bf16(w * y)
-  auto emit = [&](int rloc, int o0, const float (&gv)[4], const float (&uv)[4]) {
+  // h = bf16(silu(g) * u), down -> p = bf16(w * y).  The routing weights of
+  // the lane's rows are read once, before any store (the compiler would
+  // otherwise reload them after every store it cannot prove disjoint).
+  auto row_weight = [&](int rloc) -> float {
+    const int r = r0 + rloc;
+    return !GATEUP && r < g.row_count ? a.row_w[g.row_begin + r] : 0.0f;
+  };
+  auto emit = [&](int rloc, int o0, const float (&gv)[4], const float (&uv)[4], float wr) {
     const int r = r0 + rloc;
     if (r >= g.row_count) return;
     const int row = g.row_begin + r;
     uint16_t hv[4];
     if constexpr (GATEUP) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) hv[i] = f32_to_bf16_rne(gv[i] / (1.0f + expf(-gv[i])) * uv[i]);
+      for (int i = 0; i < 4; ++i) hv[i] = f32_to_bf16_rne(silu_fast(gv[i]) * uv[i]);
       *reinterpret_cast<uint2*>(a.out + int64_t(row) * a.inter + o0) =
           make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16), uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
     } else {
-      const float wr = a.row_w[row];
 #pragma unroll
       for (int i = 0; i < 4; ++i) hv[i] = f32_to_bf16_rne(wr * gv[i]);
       *reinterpret_cast<uint2*>(a.out + int64_t(row) * a.hidden + o0) =
           make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16), uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
     }
   };
-  const int fbase = fb * feat_per_wg(GATEUP) + fh * FT * 16;
+  const int fbase = fb * feat_per_wg(GATEUP, WF) + fh * FT * 16;
   if constexpr (ACT_FP4) {
     // 32x32 result: value j of lane l is feature 8*(j/4) + 4*(l/32) + j%4, token l%32
+    float wr[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) wr[rb] = row_weight(th * 64 + rb * 32 + (lane & 31));
 #pragma unroll
     for (int f2 = 0; f2 < FT / 2; ++f2)
 #pragma unroll
@@ -284,10 +299,13 @@ __global__ __launch_bounds__(256, 2) void k_mx_gemm(MxGemmArgs a) {
             gv[i] = acc32[(0 * (FT / 2) + f2) * 2 + rb][4 * jg + i];
             uv[i] = GATEUP ? acc32[((NM - 1) * (FT / 2) + f2) * 2 + rb][4 * jg + i] : 0.0f;
           }
-          emit(th * 64 + rb * 32 + (lane & 31), fbase + f2 * 32 + 8 * jg + 4 * (lane >> 5), gv, uv);
+          emit(th * 64 + rb * 32 + (lane & 31), fbase + f2 * 32 + 8 * jg + 4 * (lane >> 5), gv, uv, wr[rb]);
         }
   } else {
     // 16x16 result: value i of lane l is feature 4*(l/16) + i, row l%16
+    float wr[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) wr[t] = row_weight(th * 64 + t * 16 + n);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -298,7 +316,7 @@ __global__ __launch_bounds__(256, 2) void k_mx_gemm(MxGemmArgs a) {
           gv[i] = acc[(0 * FT + ft) * 4 + t][i];
           uv[i] = GATEUP ? acc[((NM - 1) * FT + ft) * 4 + t][i] : 0.0f;
         }
-        emit(th * 64 + t * 16 + n, fbase + ft * 16 + 4 * q, gv, uv);
+        emit(th * 64 + t * 16 + n, fbase + ft * 16 + 4 * q, gv, uv, wr[t]);
       }
   }
 }
@@ -307,25 +325,39 @@ __global__ __launch_bounds__(256, 2) void k_mx_gemm(MxGemmArgs a) {
 
 int mx_gemm_rows_per_tile() { return kRowsPerTile; }
 
-hipError_t launch_mx_gemm(const MxGemmArgs& a, bool gateup, bool act_fp4, hipStream_t s, Ev ev) {
-  const int outs = gateup ? a.inter : a.hidden;
-  if (outs % feat_per_wg(gateup)) return hipErrorInvalidValue;
+// Widest workgroup tile tried, in wave columns of 64 features (measured on the
+// Qwen-A3B prefill layer: FP4 activations 4 -> gate/up 106 us against 122 us
+// with 2 and 112 us with 8; FP8 activations 8 -> 125 us against 144 us with 4,
+// whose 103 KB of LDS leave one 8-wave workgroup per CU).
+constexpr int mx_max_wf(bool act_fp4) { return act_fp4 ? 4 : 8; }
+
+namespace {
+template <bool GATEUP, bool ACT_FP4, int WF>
+hipError_t launch_wf(const MxGemmArgs& a, hipStream_t s, Ev ev) {
   // one workgroup per (row tile, feature block) item, at least 8 * ceil(items / 8)
-  const int nfb = outs / feat_per_wg(gateup);
+  const int nfb = (GATEUP ? a.inter : a.hidden) / feat_per_wg(GATEUP, WF);
   const int64_t bound = int64_t(a.max_tiles) * nfb;
-  const dim3 grid(unsigned((bound + 7) / 8 * 8));
-  if (gateup) {
-    if (act_fp4)
-      ft_launch(k_mx_gemm<true, true>, grid, dim3(256), s, ev, a);
-    else
-      ft_launch(k_mx_gemm<true, false>, grid, dim3(256), s, ev, a);
-  } else {
-    if (act_fp4)
-      ft_launch(k_mx_gemm<false, true>, grid, dim3(256), s, ev, a);
-    else
-      ft_launch(k_mx_gemm<false, false>, grid, dim3(256), s, ev, a);
-  }
+  ft_launch(k_mx_gemm<GATEUP, ACT_FP4, WF>, dim3(unsigned((bound + 7) / 8 * 8)), dim3(128 * WF), s, ev, a);
   return hipGetLastError();
+}
+// the widest workgroup tile (up to mx_max_wf) whose feature block divides the outputs
+template <bool GATEUP, bool ACT_FP4>
+hipError_t launch_gf(const MxGemmArgs& a, hipStream_t s, Ev ev) {
+  const int outs = GATEUP ? a.inter : a.hidden;
+  constexpr int wf = mx_max_wf(ACT_FP4);
+  if constexpr (wf >= 8) {
+    if (outs % feat_per_wg(GATEUP, 8) == 0) return launch_wf<GATEUP, ACT_FP4, 8>(a, s, ev);
+  }
+  if (outs % feat_per_wg(GATEUP, 4) == 0) return launch_wf<GATEUP, ACT_FP4, 4>(a, s, ev);
+  if (outs % feat_per_wg(GATEUP, 2) == 0) return launch_wf<GATEUP, ACT_FP4, 2>(a, s, ev);
+  return hipErrorInvalidValue;
+}
+}  // namespace
+
+hipError_t launch_mx_gemm(const MxGemmArgs& a, bool gateup, bool act_fp4, hipStream_t s, Ev ev) {
+  if (gateup)
+    return act_fp4 ? launch_gf<true, true>(a, s, ev) : launch_gf<true, false>(a, s, ev);
+  return act_fp4 ? launch_gf<false, true>(a, s, ev) : launch_gf<false, false>(a, s, ev);
 }
 
 }  // namespace ftmoe

@@ -8,14 +8,17 @@
 // emax 8, max 448).  Every step is exact in fp32: the inputs are bf16, the
 // scale is a power of two and the grid rounding uses rintf.
 //
-// Output layout (row-major, the B operand of v_mfma_scale_f32_16x16x128_f8f6f4
-// as stored): FP4 codes [R][K/2] (even element in the low nibble), FP8 codes
-// [R][K]; scales [R][K/32].
+// Output: the MX GEMM's activation tiles (see MxQuantArgs): each source row
+// is quantised once and written to the tile slot of every grouped row that
+// reads it (the k expert rows of a token, and its shared-expert row).
 #include "common.h"
+#include "gmem.h"
 
 namespace ftmoe {
 
 namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ inline float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
@@ -73,16 +76,16 @@ __device__ inline uint32_t to_e4m3(float v) {
   return (v < 0.0f ? 0x80u : 0u) | code;
 }
 
-// One thread per 32-element block.
+// One thread per 32-element block of a source row: quantise it, then store
+// its codes and scale byte at each destination slot.
 template <bool FP4>
-__global__ __launch_bounds__(256) void k_mx_quant(const uint16_t* __restrict__ in, int rows, int K,
-                                                  uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
-  const int nblk = K / 32;
+__global__ __launch_bounds__(256) void k_mx_quant_tiles(MxQuantArgs a) {
+  const int nblk = a.K / 32, nkb = a.K / 128;
   const int64_t b = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (b >= int64_t(rows) * nblk) return;
+  if (b >= int64_t(a.rows) * nblk) return;
   const int64_t row = b / nblk;
-  const int kb = int(b % nblk);
-  const uint4* src = reinterpret_cast<const uint4*>(in + row * K + int64_t(kb) * 32);
+  const int kb32 = int(b % nblk);
+  const uint4* src = reinterpret_cast<const uint4*>(a.in + row * a.K + int64_t(kb32) * 32);
   uint32_t w[16];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -101,41 +104,60 @@ __global__ __launch_bounds__(256) void k_mx_quant(const uint16_t* __restrict__ i
   const int emax = FP4 ? 2 : 8;
   int sexp = amax > 0.0f ? ilog2f(amax) - emax : -127;
   sexp = max(-127, min(127, sexp));
-  scales[row * nblk + kb] = uint8_t(sexp + 127);
-  if (FP4) {
-    uint32_t out[4] = {0, 0, 0, 0};
+  const uint8_t sbyte = uint8_t(sexp + 127);
+  // codes: FP4 16 bytes (K 32 kb32 .. + 31), FP8 32 bytes
+  uint32_t out[FP4 ? 4 : 8] = {};
+  if constexpr (FP4) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const uint32_t c0 = to_e2m1(ldexpf(bf16_to_f32(w[i] & 0xFFFFu), -sexp));
       const uint32_t c1 = to_e2m1(ldexpf(bf16_to_f32(w[i] >> 16), -sexp));
       out[i / 4] |= (c0 | (c1 << 4)) << (8 * (i % 4));
     }
-    *reinterpret_cast<uint4*>(codes + row * (K / 2) + int64_t(kb) * 16) = make_uint4(out[0], out[1], out[2], out[3]);
   } else {
-    uint32_t out[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const uint32_t c0 = to_e4m3(ldexpf(bf16_to_f32(w[i] & 0xFFFFu), -sexp));
       const uint32_t c1 = to_e4m3(ldexpf(bf16_to_f32(w[i] >> 16), -sexp));
       out[i / 2] |= (c0 | (c1 << 8)) << (16 * (i % 2));
     }
-    uint4* dst = reinterpret_cast<uint4*>(codes + row * K + int64_t(kb) * 32);
-    dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
-    dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+  }
+  // block kb32 = step kb, 32-block q4 of the step
+  const int kb = kb32 >> 2, q4 = kb32 & 3;
+  auto put = [&](int slot) {
+    const int tile = slot / kMxTileRows, i = slot - tile * kMxTileRows;
+    const int64_t blk = int64_t(tile) * nkb + kb;
+    a.out_scales[blk * kMxTileScaleBytes + i * 4 + q4] = sbyte;
+    uint8_t* sub = a.out_codes + blk * mx_tile_code_bytes(FP4) + (i >> 4) * (FP4 ? 1024 : 2048);
+    const int n = i & 15;
+    if constexpr (FP4) {
+      gstore<u32x4>(sub + (16 * q4 + n) * 16, u32x4{out[0], out[1], out[2], out[3]});
+    } else {
+      // K 32 q4 .. + 31 of the step: half q4 / 2, lanes q = 2 q4 - 4 h and q + 1
+      const int h = q4 >> 1, q = 2 * q4 - 4 * h;
+      gstore<u32x4>(sub + h * 1024 + (16 * q + n) * 16, u32x4{out[0], out[1], out[2], out[3]});
+      gstore<u32x4>(sub + h * 1024 + (16 * (q + 1) + n) * 16, u32x4{out[4], out[5], out[6], out[7]});
+    }
+  };
+  if (a.pair_row) {
+    for (int j = 0; j < a.k; ++j) put(a.row_slot[a.pair_row[row * a.k + j]]);
+    if (a.shared_row0 >= 0) put(a.row_slot[a.shared_row0 + row]);
+  } else {
+    put(a.row_slot[row]);
   }
 }
 
 }  // namespace
 
-hipError_t launch_mx_quant(const uint16_t* in, int rows, int K, bool fp4, uint8_t* codes, uint8_t* scales,
-                           hipStream_t s) {
-  if (rows <= 0) return hipSuccess;
-  const int64_t blocks = int64_t(rows) * (K / 32);
+hipError_t launch_mx_quant_tiles(const MxQuantArgs& a, bool fp4, hipStream_t s) {
+  if (a.rows <= 0) return hipSuccess;
+  if (a.K % 128) return hipErrorInvalidValue;
+  const int64_t blocks = int64_t(a.rows) * (a.K / 32);
   const dim3 grid(unsigned((blocks + 255) / 256));
   if (fp4)
-    hipLaunchKernelGGL(k_mx_quant<true>, grid, dim3(256), 0, s, in, rows, K, codes, scales);
+    hipLaunchKernelGGL(k_mx_quant_tiles<true>, grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(k_mx_quant<false>, grid, dim3(256), 0, s, in, rows, K, codes, scales);
+    hipLaunchKernelGGL(k_mx_quant_tiles<false>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -101,10 +101,9 @@ struct ft_moe_pool {
   uint16_t* cpu_out = nullptr;      // pinned result rows of host-computed experts
   int32_t* fail_dev = nullptr;      // [2*E] keys and slots whose copy failed
   // prefill MX activation modes
-  uint8_t* xq_codes = nullptr;      // [cap][H] (FP8) or [cap][H/2] (FP4)
-  uint8_t* xq_scales = nullptr;     // [cap][H/32]
-  uint8_t* hq_codes = nullptr;      // [rows][I] or [rows][I/2]
-  uint8_t* hq_scales = nullptr;     // [rows][I/32]
+  int32_t* row_slot = nullptr;     // [rows] prefill: each row's slot in the MX GEMM activation tiles
+  uint8_t* tq_codes = nullptr;      // MX GEMM activation tiles (allocated at the first MX call)
+  uint8_t* tq_scales = nullptr;
   int32_t* tiles = nullptr;         // [2 * max_tiles]
   int32_t max_tiles = 0;
 
@@ -261,7 +260,9 @@ int ensure_capacity(ft_moe_pool* p, int T) {
   hipFree(p->z); hipFree(p->sel); hipFree(p->w); hipFree(p->gap); hipFree(p->pair_flag);
   hipFree(p->pair_slot); hipFree(p->pair_row); hipFree(p->row_tok); hipFree(p->row_w);
   hipFree(p->hbuf); hipFree(p->pbuf);
-  hipFree(p->xq_codes); hipFree(p->xq_scales); hipFree(p->hq_codes); hipFree(p->hq_scales); hipFree(p->tiles);
+  hipFree(p->row_slot); hipFree(p->tiles);
+  hipFree(p->tq_codes); hipFree(p->tq_scales);
+  p->tq_codes = p->tq_scales = nullptr;
   if (p->rb_host) hipHostFree(p->rb_host);
   if (p->x_host) hipHostFree(p->x_host);
   if (p->cpu_out) hipHostFree(p->cpu_out);
@@ -285,10 +286,7 @@ int ensure_capacity(ft_moe_pool* p, int T) {
   if ((rc = dev_alloc(&p->pbuf, rows * p->H))) return rc;
   const int tr = mx_gemm_rows_per_tile();
   p->max_tiles = int32_t((pairs + tr - 1) / tr + p->E + (cap + tr - 1) / tr + 2);
-  if ((rc = dev_alloc(&p->xq_codes, int64_t(cap) * p->H))) return rc;
-  if ((rc = dev_alloc(&p->xq_scales, int64_t(cap) * p->H / 32))) return rc;
-  if ((rc = dev_alloc(&p->hq_codes, rows * p->I))) return rc;
-  if ((rc = dev_alloc(&p->hq_scales, rows * p->I / 32))) return rc;
+  if ((rc = dev_alloc(&p->row_slot, rows))) return rc;
   if ((rc = dev_alloc(&p->tiles, 2 * int64_t(p->max_tiles)))) return rc;
   p->rb_cap = int64_t(sizeof(ResolveHeader)) + 5 * 4 * int64_t(p->E) + 8 * pairs + 64;
   if (hipHostMalloc(reinterpret_cast<void**>(&p->rb_host), p->rb_cap, hipHostMallocMapped | hipHostMallocCoherent) !=
@@ -349,7 +347,7 @@ FfnArgs ffn_args(ft_moe_pool* p, int layer, int list_off, int n, const int32_t* 
 }
 
 double mat_bytes(int fmt, double rows, double cols);
-hipEvent_t prof_begin(ft_moe_pool* p, hipStream_t s);
+hipEvent_t prof_begin(ft_moe_pool* p, hipStream_t s, int stage);
 void prof_end(ft_moe_pool* p, int stage, hipEvent_t a, hipStream_t s, double bytes, double flops);
 Ev prof_pair(ft_moe_pool* p, hipStream_t s, int stage);
 void prof_push(ft_moe_pool* p, int stage, Ev ev, double bytes, double flops);
@@ -414,6 +412,7 @@ ResolveArgs resolve_args(ft_moe_pool* p, int layer, int T, int t0, int mode) {
   a.host_rb_cap = p->rb_cap;
   a.host_wait = mode == 0 ? 1 : 0;
   a.tiles = mode == 1 ? p->tiles : nullptr;
+  a.row_slot = mode == 1 ? p->row_slot : nullptr;
   a.tile_rows = mx_gemm_rows_per_tile();
   return a;
 }
@@ -430,8 +429,8 @@ hipEvent_t prof_event(ft_moe_pool* p) {
   return e;
 }
 
-hipEvent_t prof_begin(ft_moe_pool* p, hipStream_t s) {
-  if (!(p->prof_mask & (1 << FT_STAGE_COPY))) return nullptr;
+hipEvent_t prof_begin(ft_moe_pool* p, hipStream_t s, int stage) {
+  if (!(p->prof_mask & (1 << stage))) return nullptr;
   hipEvent_t e = prof_event(p);
   if (e) (void)hipEventRecord(e, s);
   return e;
@@ -499,7 +498,7 @@ int copy_layer_staging(ft_moe_pool* p, int layer) {
   const int half = layer & 1;
   uint8_t* dst = p->arena + int64_t(half) * E * p->slot_bytes;
   const ExpertLayout& L = p->lay[p->fmt[layer]];
-  hipEvent_t e0 = prof_begin(p, p->copy_stream);
+  hipEvent_t e0 = prof_begin(p, p->copy_stream, FT_STAGE_COPY);
   int copied = 0;
   if (p->prefill_hit) {
     // runs of consecutive experts that are not resident in the pool
@@ -539,18 +538,49 @@ int copy_layer_staging(ft_moe_pool* p, int layer) {
   return FT_OK;
 }
 
+// Quantises rows straight into the GEMM's activation tiles (x by token, to
+// the slots of its k expert rows and its shared-expert row; h row by row);
+// timed as one stage.
+int mx_act_tiles(ft_moe_pool* p, const uint16_t* src, int nrows, int K, const int32_t* pair_row, int shared_row0,
+                 bool fp4, hipStream_t s) {
+  hipEvent_t e0 = prof_begin(p, s, FT_STAGE_ACT_QUANT);
+  MxQuantArgs q{};
+  q.in = src;
+  q.rows = nrows;
+  q.K = K;
+  q.pair_row = pair_row;
+  q.k = p->k;
+  q.shared_row0 = shared_row0;
+  q.row_slot = p->row_slot;
+  q.out_codes = p->tq_codes;
+  q.out_scales = p->tq_scales;
+  FT_HIP_CHECK(launch_mx_quant_tiles(q, fp4, s));
+  const double per = fp4 ? 0.5 + 1.0 / 32 : 1.0 + 1.0 / 32;
+  const double outs = pair_row ? double(nrows) * (p->k + (shared_row0 >= 0 ? 1 : 0)) : double(nrows);
+  prof_end(p, FT_STAGE_ACT_QUANT, e0, s, double(nrows) * K * 2.0 + outs * K * per, 0.0);
+  return FT_OK;
+}
+
 int run_mx_ffn(ft_moe_pool* p, int layer, const void* x, int T, bool fp4, hipStream_t s) {
   const int rows = T * p->k + (p->shared ? T : 0);
   const double H = p->H, I = p->I;
-  FT_HIP_CHECK(launch_mx_quant(static_cast<const uint16_t*>(x), T, p->H, fp4, p->xq_codes, p->xq_scales, s));
+  if (!p->tq_codes) {
+    // sized for FP8 codes of the wider matrix; freed with the per-call buffers
+    const int64_t blocks = int64_t(p->max_tiles) * (std::max(p->H, p->I) / kTileK);
+    int rc;
+    if ((rc = dev_alloc(&p->tq_codes, blocks * mx_tile_code_bytes(false))) ||
+        (rc = dev_alloc(&p->tq_scales, blocks * kMxTileScaleBytes)))
+      return rc;
+  }
+  int rc = mx_act_tiles(p, static_cast<const uint16_t*>(x), T, p->H, p->pair_row, p->shared ? T * p->k : -1, fp4, s);
+  if (rc) return rc;
   MxGemmArgs a{};
   a.groups = p->groups;
   a.tiles = p->tiles;
   a.n_tiles_dev = p->dev_header + 10;
   a.max_tiles = p->max_tiles;
-  a.act_codes = p->xq_codes;
-  a.act_scales = p->xq_scales;
-  a.row_tok = p->row_tok;
+  a.act_codes = p->tq_codes;
+  a.act_scales = p->tq_scales;
   a.row_w = p->row_w;
   a.out = p->hbuf;
   a.hidden = p->H;
@@ -560,9 +590,7 @@ int run_mx_ffn(ft_moe_pool* p, int layer, const void* x, int T, bool fp4, hipStr
   FT_HIP_CHECK(launch_mx_gemm(a, true, fp4, s, ev));
   prof_push(p, FT_STAGE_FFN_GATEUP, ev, (p->E + p->shared) * 2 * mat_bytes(FT_FMT_MXFP4, I, H) + rows * I * 2.0 +
             T * H * (fp4 ? 0.5 + 1.0 / 32 : 1.0 + 1.0 / 32), rows * 4 * H * I);
-  FT_HIP_CHECK(launch_mx_quant(p->hbuf, rows, p->I, fp4, p->hq_codes, p->hq_scales, s));
-  a.act_codes = p->hq_codes;
-  a.act_scales = p->hq_scales;
+  if ((rc = mx_act_tiles(p, p->hbuf, rows, p->I, nullptr, -1, fp4, s))) return rc;
   a.out = p->pbuf;
   ev = prof_pair(p, s, FT_STAGE_FFN_DOWN);
   FT_HIP_CHECK(launch_mx_gemm(a, false, fp4, s, ev));
@@ -778,7 +806,7 @@ int forward_decode(ft_moe_pool* p, int layer, int T, const void* x, void* out, h
     // streams.  Everything earlier on s (the readers of the victim slots) has
     // finished: the resolve kernel that published this list ran after it.
     const int ncs = std::min(p->n_copy, std::max(h.n_stream, 1));
-    hipEvent_t ec = h.n_stream > 0 ? prof_begin(p, p->copy[0]) : nullptr;
+    hipEvent_t ec = h.n_stream > 0 ? prof_begin(p, p->copy[0], FT_STAGE_COPY) : nullptr;
     if (ec)
       for (int c = 1; c < ncs; ++c) FT_HIP_CHECK(hipStreamWaitEvent(p->copy[c], ec, 0));
     for (int i = 0; i < h.n_stream; ++i) {
@@ -1608,6 +1636,8 @@ void ft_moe_destroy_pool(ft_moe_pool* p) {
   hipFree(p->pair_row); hipFree(p->row_tok); hipFree(p->row_w); hipFree(p->groups); hipFree(p->glist); hipFree(p->gdesc); hipFree(p->count_max);
   hipFree(p->dev_header); hipFree(p->hbuf); hipFree(p->pbuf); hipFree(p->fail_dev);
   hipFree(p->key_off_dev); hipFree(p->prof_cnt_dev);
+  hipFree(p->row_slot); hipFree(p->tiles);
+  hipFree(p->tq_codes); hipFree(p->tq_scales);
   if (p->rb_host) hipHostFree(p->rb_host);
   if (p->x_host) hipHostFree(p->x_host);
   if (p->cpu_out) hipHostFree(p->cpu_out);

@@ -51,6 +51,7 @@ struct ResolveSmem {
   int dslot[kMaxExperts];
   int mpos[kMaxExperts];
   int gpos[kMaxExperts];  // position of each group in the run list
+  int tbase[kMaxExperts]; // prefill: each group's first row tile in the MX GEMM work list
   int off[kMaxExperts];
   int sm[kMaxExperts];
   int wcnt[NW][kMaxExperts];
@@ -538,6 +539,14 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
   const bool shared = a.shared_ptr != 0;
   const int n_hit_list = nHit + (shared ? 1 : 0);
   if (tid < nD) sm.gpos[tid] = ishit ? hp : n_hit_list + sm.mpos[tid];
+  // prefill: row tiles of the MX GEMM work list, groups in D order, then the
+  // shared expert's; a row's slot there is (its tile) * tile_rows + (row in tile)
+  int ntiles_d = 0;
+  if (a.tiles != nullptr) {
+    const int tr = a.tile_rows;
+    const int base = block_exscan(tid < nD ? (sm.cnt[tid] + tr - 1) / tr : 0, sm.wbuf, par, &ntiles_d);
+    if (tid < nD) sm.tbase[tid] = base;
+  }
   __syncthreads();
   // rows; the tokens of a group's first kGroupTok rows also go into its
   // run-list entry, where a decode FFN reads them with the descriptor (the
@@ -551,12 +560,14 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
     a.row_tok[row] = t0 + i / k;
     a.row_w[row] = lp ? sm.pw[i] : a.w[pb + i];
     if (r < kGroupTok) a.gdesc[sm.gpos[d]].tok[r] = uint16_t(t0 + i / k);
+    if (a.tiles != nullptr) a.row_slot[row] = (sm.tbase[d] + r / a.tile_rows) * a.tile_rows + r % a.tile_rows;
   }
   if (shared) {
     for (int tt = tid; tt < ntok; tt += NT) {
       a.row_tok[P + tt] = t0 + tt;
       a.row_w[P + tt] = 1.0f;
       if (tt < kGroupTok) a.gdesc[nHit].tok[tt] = uint16_t(t0 + tt);
+      if (a.tiles != nullptr) a.row_slot[P + tt] = (ntiles_d + tt / a.tile_rows) * a.tile_rows + tt % a.tile_rows;
     }
   }
 
@@ -594,8 +605,8 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
   if (a.tiles != nullptr) {
     const int tr = a.tile_rows;
     const int nt = live_d ? (cnt_d + tr - 1) / tr : 0;
-    int ntot;
-    const int base = block_exscan(nt, sm.wbuf, par, &ntot);
+    const int ntot = ntiles_d;
+    const int base = live_d ? sm.tbase[tid] : 0;
     for (int j = 0; j < nt; ++j) {
       a.tiles[2 * (base + j)] = tid;
       a.tiles[2 * (base + j) + 1] = j;

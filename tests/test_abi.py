@@ -35,6 +35,17 @@ def test_struct_sizes_match_header_layout():
     assert ctypes.sizeof(ft.ft_moe_trace) == 5 * 8
 
 
+def test_profile_stages_match_header():
+    # the binding's stage names follow the header's FT_STAGE_* order up to FT_STAGE_COUNT
+    src = open(os.path.join(ROOT, "include", "ftmoe.h")).read()
+    body = re.search(r"enum\s*\{\s*(FT_STAGE_ROUTER[^}]*)\}", src).group(1)
+    names = [n.strip().split("=")[0].strip() for n in re.sub(r"/\*.*?\*/", "", body, flags=re.S).split(",")]
+    names = [n for n in names if n]
+    assert names[-1] == "FT_STAGE_COUNT"
+    assert [n[len("FT_STAGE_"):].lower() for n in names[:-1]] == ft.FT_STAGES
+    assert ctypes.sizeof(ft.ft_moe_profile) == 4 * 8 * (len(names) - 1)
+
+
 def _cfg(**kw):
     d = dict(num_layers=1, hidden=256, inter=128, num_experts=16, top_k=2, layer_fmt=[1], pool_slots=8)
     d.update(kw)
