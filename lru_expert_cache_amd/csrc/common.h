@@ -238,32 +238,46 @@ hipError_t launch_miss_copy(const MissCopyArgs& a, int workgroups, hipStream_t s
 //   scales: block (tile, kb) = 128 rows x 4 bytes (the rows' scales of the
 //        step's four 32-blocks), 512 bytes.
 // A row's slot is tile * 128 + (row in tile) (resolve writes it per row).
-// Slots past a group's end are not written: their stale values only reach
-// output rows that the GEMM does not store.
+// Slots past a group's end hold zeros (tile gather) or stale codes (the
+// quantiser writes only real rows): either way they only reach output rows
+// that the GEMM does not store.
 constexpr int kMxTileRows = 128;
 constexpr int64_t mx_tile_code_bytes(bool fp4) { return fp4 ? 8192 : 16384; }  // per (tile, K step)
 constexpr int64_t kMxTileScaleBytes = 512;                                     // per (tile, K step)
-// mxq.hip: MX quantisation of bf16 rows straight into the activation tiles.
-// Source row r goes to the slots of grouped rows pair_row[r*k + j] (j < k)
-// and, if shared_row0 >= 0, of grouped row shared_row0 + r (gate/up input x
-// by token); with pair_row null, to the slot of grouped row r (down input h).
+// mxq.hip: MX quantisation of bf16 rows, row-major (codes [rows][K/2] for
+// FP4, [rows][K] for FP8, even element in the low nibble; scales
+// [rows][K/32]) when row_slot is null, else into the activation tiles at
+// the slot of each row (the down input h, rows in grouped order).
 struct MxQuantArgs {
   const uint16_t* in;         // [rows][K] bf16
   int32_t rows, K;
-  const int32_t* pair_row;    // [rows * k] or null
-  int32_t k, shared_row0;
-  const int32_t* row_slot;    // grouped row -> slot
-  uint8_t* out_codes;         // [tiles][K/128] blocks
+  const int32_t* row_slot;    // row -> tile slot, or null
+  uint8_t* out_codes;
   uint8_t* out_scales;
 };
-hipError_t launch_mx_quant_tiles(const MxQuantArgs& a, bool fp4, hipStream_t s);
+hipError_t launch_mx_quant(const MxQuantArgs& a, bool fp4, hipStream_t s);
+// Copies row-major quantised rows into the activation tiles: grouped row r of
+// a work-list tile reads source row row_map[r] (the gate/up input x by token).
+struct MxTileArgs {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  int32_t K;
+  const int32_t* row_map;     // grouped row -> source row
+  const GroupDesc* groups;
+  const int32_t* tiles;       // (group, tile) pairs
+  const int32_t* n_tiles_dev;
+  int32_t max_tiles;
+  uint8_t* out_codes;
+  uint8_t* out_scales;
+};
+hipError_t launch_mx_tile_gather(const MxTileArgs& a, bool fp4, hipStream_t s);
 // gemm_mx.hip: grouped prefill GEMM on the block-scaled MFMA (MXFP4 weights, MX activations)
 struct MxGemmArgs {
   const GroupDesc* groups;
   const int32_t* tiles;       // (group, tile) pairs
   const int32_t* n_tiles_dev; // number of valid pairs
   int32_t max_tiles;          // grid bound
-  const uint8_t* act_codes;   // activation tiles (launch_mx_quant_tiles layout)
+  const uint8_t* act_codes;   // activation tiles (the layout above)
   const uint8_t* act_scales;
   const float* row_w;         // down: routing weight of each row
   uint16_t* out;              // gate/up: h [rows][I]; down: p [rows][H]

@@ -1,16 +1,16 @@
 // MX activation quantiser: bf16 rows -> element codes + one E8M0 scale per 32
-// elements along the row (OCP Microscaling Formats v1.0, "conversion from a
-// vector of scalars": X = 2^(floor(log2 amax) - emax_elem); each element is
-// v / X rounded to nearest-even on the element grid and clamped to +-max;
-// an all-zero block gets scale 2^-127).  Used by the prefill activation
-// modes, where both the expert inputs x and the SwiGLU outputs h are fed to
-// the block-scaled MFMA as MXFP4 (E2M1, emax 2, max 6) or MXFP8 (E4M3,
-// emax 8, max 448).  Every step is exact in fp32: the inputs are bf16, the
-// scale is a power of two and the grid rounding uses rintf.
+// elements along the row, by the OCP Microscaling Formats v1.0 rule for a
+// block of scalars: X = 2^(floor(log2 amax) - emax_elem), each element is
+// v / X rounded to nearest-even on the element grid and clamped to +-max, and
+// an all-zero block gets scale 2^-127.  Used by the prefill activation modes,
+// where both the expert inputs x and the SwiGLU outputs h are fed to the
+// block-scaled MFMA as MXFP4 (E2M1, emax 2, max 6) or MXFP8 (E4M3, emax 8,
+// max 448).  The inputs are bf16 and X a power of two, so v / X is exact; the
+// rounding onto the grid is the hardware convert's (see fp4x8 / fp8x4).
 //
-// Output: the MX GEMM's activation tiles (see MxQuantArgs): each source row
-// is quantised once and written to the tile slot of every grouped row that
-// reads it (the k expert rows of a token, and its shared-expert row).
+// Output: row-major codes and scales, or straight into the MX GEMM's
+// activation tiles at each row's slot (see MxQuantArgs); the tile gather
+// copies row-major rows into the tiles (the gate/up input, by token).
 #include "common.h"
 #include "gmem.h"
 
@@ -29,57 +29,45 @@ __device__ inline int ilog2f(float a) {
   return e - 1;
 }
 
-// E2M1 code of a (already scaled) value: nearest-even on {0,.5,1,1.5,2,3,4,6}, clamped.
-__device__ inline uint32_t to_e2m1(float v) {
-  const float a = fabsf(v);
-  uint32_t code;
-  if (!(a > 0.0f)) {
-    code = 0;
-  } else {
-    const int e = max(ilog2f(a), 0);
-    const float q = ldexpf(1.0f, e - 1);
-    float r = rintf(a / q) * q;
-    r = fminf(r, 6.0f);
-    // magnitude -> 3-bit code
-    if (r < 1.0f)
-      code = r > 0.0f ? 1u : 0u;  // 0.5 -> 1
-    else {
-      const int er = ilog2f(r);             // 0, 1 or 2
-      const uint32_t m = (r > ldexpf(1.0f, er)) ? 1u : 0u;  // 1.5 * 2^er
-      code = uint32_t(er + 1) * 2u + m;
-    }
-    if (v < 0.0f && code) code |= 8u;
-  }
-  return code;
+typedef short short2v __attribute__((ext_vector_type(2)));
+
+// Element codes from gfx950's scaled down-converts: v_cvt_scalef32_pk_fp4_f32
+// and _pk_fp8_f32 compute v / X with round-to-nearest-even on the element grid
+// (X a power of two, read from the exponent of the scale operand).  Measured
+// against a plain software rounding for every finite bf16 input at X = 2^-127
+// .. 2^127: identical codes once (a) FP8 inputs are clamped to +-448 X (the
+// convert turns values past 448 into the NaN code, where the MX rule
+// saturates; FP4 saturates at 6 by itself) and (b) a negative value that
+// rounds to zero is given code +0 rather than -0 (the same number).
+// 8 E2M1 codes (element 2i in the low nibble of byte i) with -0 made +0
+__device__ inline uint32_t fp4x8(const float* v, float X) {
+  uint32_t o = 0;
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, v[0], v[1], X, 0);
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, v[2], v[3], X, 1);
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, v[4], v[5], X, 2);
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, v[6], v[7], X, 3);
+  // a nibble keeps its sign bit only if its magnitude bits are not all zero
+  const uint32_t nz = ((o & 0x77777777u) + 0x77777777u) & 0x88888888u;
+  return o & (nz | 0x77777777u);
+}
+// 4 E4M3 codes (element i in byte i), saturated at +-448, -0 made +0
+__device__ inline uint32_t fp8x4(const float* v, float X) {
+  const float lim = 448.0f * X;
+  float c[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c[i] = fminf(fmaxf(v[i], -lim), lim);
+  short2v lo = {0, 0};
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, c[0], c[1], X, false);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, c[2], c[3], X, true);
+  const uint32_t o = uint32_t(uint16_t(lo[0])) | (uint32_t(uint16_t(lo[1])) << 16);
+  const uint32_t nz = ((o & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) & 0x80808080u;
+  return o & (nz | 0x7F7F7F7Fu);
 }
 
-// E4M3 ("FN") code of a scaled value: nearest-even, clamped to +-448.
-__device__ inline uint32_t to_e4m3(float v) {
-  const float a = fabsf(v);
-  if (!(a > 0.0f)) return 0;
-  const int e = max(ilog2f(a), -6);
-  const float q = ldexpf(1.0f, e - 3);
-  float r = rintf(a / q) * q;
-  r = fminf(r, 448.0f);
-  uint32_t code;
-  if (r == 0.0f) {
-    code = 0;
-  } else {
-    const int er = ilog2f(r);
-    if (er < -6) {
-      code = uint32_t(r * 512.0f);  // subnormal: m * 2^-9
-    } else {
-      const uint32_t m = uint32_t((r / ldexpf(1.0f, er) - 1.0f) * 8.0f);
-      code = (uint32_t(er + 7) << 3) | m;
-    }
-  }
-  return (v < 0.0f ? 0x80u : 0u) | code;
-}
-
-// One thread per 32-element block of a source row: quantise it, then store
-// its codes and scale byte at each destination slot.
+// One thread per 32-element block of a row: quantise it, then store its
+// codes and scale byte row-major (row_slot null) or at the row's tile slot.
 template <bool FP4>
-__global__ __launch_bounds__(256) void k_mx_quant_tiles(MxQuantArgs a) {
+__global__ __launch_bounds__(256) void k_mx_quant(MxQuantArgs a) {
   const int nblk = a.K / 32, nkb = a.K / 128;
   const int64_t b = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (b >= int64_t(a.rows) * nblk) return;
@@ -106,58 +94,103 @@ __global__ __launch_bounds__(256) void k_mx_quant_tiles(MxQuantArgs a) {
   sexp = max(-127, min(127, sexp));
   const uint8_t sbyte = uint8_t(sexp + 127);
   // codes: FP4 16 bytes (K 32 kb32 .. + 31), FP8 32 bytes
-  uint32_t out[FP4 ? 4 : 8] = {};
-  if constexpr (FP4) {
+  const float X = ldexpf(1.0f, sexp);
+  float v[32];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t c0 = to_e2m1(ldexpf(bf16_to_f32(w[i] & 0xFFFFu), -sexp));
-      const uint32_t c1 = to_e2m1(ldexpf(bf16_to_f32(w[i] >> 16), -sexp));
-      out[i / 4] |= (c0 | (c1 << 4)) << (8 * (i % 4));
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t c0 = to_e4m3(ldexpf(bf16_to_f32(w[i] & 0xFFFFu), -sexp));
-      const uint32_t c1 = to_e4m3(ldexpf(bf16_to_f32(w[i] >> 16), -sexp));
-      out[i / 2] |= (c0 | (c1 << 8)) << (16 * (i % 2));
-    }
+  for (int i = 0; i < 16; ++i) {
+    v[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+    v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
   }
-  // block kb32 = step kb, 32-block q4 of the step
+  uint32_t out[FP4 ? 4 : 8];
+#pragma unroll
+  for (int i = 0; i < (FP4 ? 4 : 8); ++i) out[i] = FP4 ? fp4x8(v + 8 * i, X) : fp8x4(v + 4 * i, X);
+  if (!a.row_slot) {
+    a.out_scales[row * nblk + kb32] = sbyte;
+    uint8_t* dst = a.out_codes + row * (FP4 ? a.K / 2 : a.K) + int64_t(kb32) * (FP4 ? 16 : 32);
+    gstore<u32x4>(dst, u32x4{out[0], out[1], out[2], out[3]});
+    if constexpr (!FP4) gstore<u32x4>(dst + 16, u32x4{out[4], out[5], out[6], out[7]});
+    return;
+  }
+  // tile slot: block kb32 = step kb, 32-block q4 of the step
+  const int slot = a.row_slot[row];
   const int kb = kb32 >> 2, q4 = kb32 & 3;
-  auto put = [&](int slot) {
-    const int tile = slot / kMxTileRows, i = slot - tile * kMxTileRows;
-    const int64_t blk = int64_t(tile) * nkb + kb;
-    a.out_scales[blk * kMxTileScaleBytes + i * 4 + q4] = sbyte;
-    uint8_t* sub = a.out_codes + blk * mx_tile_code_bytes(FP4) + (i >> 4) * (FP4 ? 1024 : 2048);
-    const int n = i & 15;
-    if constexpr (FP4) {
-      gstore<u32x4>(sub + (16 * q4 + n) * 16, u32x4{out[0], out[1], out[2], out[3]});
-    } else {
-      // K 32 q4 .. + 31 of the step: half q4 / 2, lanes q = 2 q4 - 4 h and q + 1
-      const int h = q4 >> 1, q = 2 * q4 - 4 * h;
-      gstore<u32x4>(sub + h * 1024 + (16 * q + n) * 16, u32x4{out[0], out[1], out[2], out[3]});
-      gstore<u32x4>(sub + h * 1024 + (16 * (q + 1) + n) * 16, u32x4{out[4], out[5], out[6], out[7]});
-    }
-  };
-  if (a.pair_row) {
-    for (int j = 0; j < a.k; ++j) put(a.row_slot[a.pair_row[row * a.k + j]]);
-    if (a.shared_row0 >= 0) put(a.row_slot[a.shared_row0 + row]);
+  const int tile = slot / kMxTileRows, i = slot - tile * kMxTileRows;
+  const int64_t blk = int64_t(tile) * nkb + kb;
+  a.out_scales[blk * kMxTileScaleBytes + i * 4 + q4] = sbyte;
+  uint8_t* sub = a.out_codes + blk * mx_tile_code_bytes(FP4) + (i >> 4) * (FP4 ? 1024 : 2048);
+  const int n = i & 15;
+  if constexpr (FP4) {
+    gstore<u32x4>(sub + (16 * q4 + n) * 16, u32x4{out[0], out[1], out[2], out[3]});
   } else {
-    put(a.row_slot[row]);
+    // K 32 q4 .. + 31 of the step: half q4 / 2, lanes q = 2 q4 - 4 h and q + 1
+    const int h = q4 >> 1, q = 2 * q4 - 4 * h;
+    gstore<u32x4>(sub + h * 1024 + (16 * q + n) * 16, u32x4{out[0], out[1], out[2], out[3]});
+    gstore<u32x4>(sub + h * 1024 + (16 * (q + 1) + n) * 16, u32x4{out[4], out[5], out[6], out[7]});
+  }
+}
+
+// One workgroup per (row tile, 128-K step) of the work list: copies the
+// tile's 128 rows of that step from row-major quantised rows into the tile
+// layout, 16 bytes per thread and piece, and the rows' four scale bytes.
+// Pieces are numbered in destination order, so a workgroup's writes are one
+// contiguous block (the gate/up input: a token's row feeds k tiles, and
+// writing those copies from the quantiser directly scatters 16-byte pieces).
+template <bool FP4>
+__global__ __launch_bounds__(256) void k_mx_tile_gather(MxTileArgs a) {
+  const int nkb = a.K / 128;
+  const int tile = int(blockIdx.x) / nkb, kb = int(blockIdx.x) - tile * nkb;
+  if (tile >= min(*a.n_tiles_dev, a.max_tiles)) return;
+  const int d = a.tiles[2 * tile], tt = a.tiles[2 * tile + 1];
+  const GroupDesc g = a.groups[d];
+  const int r0 = tt * kMxTileRows;
+  const int64_t pitch = FP4 ? a.K / 2 : a.K, spitch = a.K / 32;
+  const int64_t blk = int64_t(tile) * nkb + kb;
+  uint8_t* dst = a.out_codes + blk * mx_tile_code_bytes(FP4);
+  constexpr int kPieces = FP4 ? 512 : 1024;  // 16-byte pieces of a block
+  for (int pi = threadIdx.x; pi < kPieces; pi += 256) {
+    // FP4: pi = 64 s + 16 q + n; FP8: pi = 128 s + 64 h + 16 q + n
+    const int n = pi & 15, q = (pi >> 4) & 3;
+    const int h = FP4 ? 0 : (pi >> 6) & 1;
+    const int s = FP4 ? pi >> 6 : pi >> 7;
+    const int r = r0 + 16 * s + n;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < g.row_count) {
+      const int64_t src = a.row_map[g.row_begin + r];
+      const int64_t k = FP4 ? int64_t(kb) * 64 + 16 * q : int64_t(kb) * 128 + 64 * h + 16 * q;
+      v = gload<u32x4>(a.codes + src * pitch + k);
+    }
+    gstore<u32x4>(dst + int64_t(pi) * 16, v);
+  }
+  if (threadIdx.x < kMxTileRows) {
+    const int r = r0 + int(threadIdx.x);
+    uint32_t sv = 0;
+    if (r < g.row_count) sv = gload<uint32_t>(a.scales + int64_t(a.row_map[g.row_begin + r]) * spitch + int64_t(kb) * 4);
+    gstore<uint32_t>(a.out_scales + blk * kMxTileScaleBytes + int64_t(threadIdx.x) * 4, sv);
   }
 }
 
 }  // namespace
 
-hipError_t launch_mx_quant_tiles(const MxQuantArgs& a, bool fp4, hipStream_t s) {
+hipError_t launch_mx_quant(const MxQuantArgs& a, bool fp4, hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;
   if (a.K % 128) return hipErrorInvalidValue;
   const int64_t blocks = int64_t(a.rows) * (a.K / 32);
   const dim3 grid(unsigned((blocks + 255) / 256));
   if (fp4)
-    hipLaunchKernelGGL(k_mx_quant_tiles<true>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_mx_quant<true>, grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(k_mx_quant_tiles<false>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_mx_quant<false>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_tile_gather(const MxTileArgs& a, bool fp4, hipStream_t s) {
+  if (a.max_tiles <= 0) return hipSuccess;
+  if (a.K % 128) return hipErrorInvalidValue;
+  const dim3 grid(unsigned(int64_t(a.max_tiles) * (a.K / 128)));
+  if (fp4)
+    hipLaunchKernelGGL(k_mx_tile_gather<true>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_mx_tile_gather<false>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

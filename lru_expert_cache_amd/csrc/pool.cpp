@@ -101,7 +101,9 @@ struct ft_moe_pool {
   uint16_t* cpu_out = nullptr;      // pinned result rows of host-computed experts
   int32_t* fail_dev = nullptr;      // [2*E] keys and slots whose copy failed
   // prefill MX activation modes
-  int32_t* row_slot = nullptr;     // [rows] prefill: each row's slot in the MX GEMM activation tiles
+  int32_t* row_slot = nullptr;      // [rows] prefill: each row's slot in the MX GEMM activation tiles
+  uint8_t* xq_codes = nullptr;      // [cap][H] (FP8) or [cap][H/2] (FP4): quantised x, row-major
+  uint8_t* xq_scales = nullptr;     // [cap][H/32]
   uint8_t* tq_codes = nullptr;      // MX GEMM activation tiles (allocated at the first MX call)
   uint8_t* tq_scales = nullptr;
   int32_t* tiles = nullptr;         // [2 * max_tiles]
@@ -260,7 +262,7 @@ int ensure_capacity(ft_moe_pool* p, int T) {
   hipFree(p->z); hipFree(p->sel); hipFree(p->w); hipFree(p->gap); hipFree(p->pair_flag);
   hipFree(p->pair_slot); hipFree(p->pair_row); hipFree(p->row_tok); hipFree(p->row_w);
   hipFree(p->hbuf); hipFree(p->pbuf);
-  hipFree(p->row_slot); hipFree(p->tiles);
+  hipFree(p->row_slot); hipFree(p->tiles); hipFree(p->xq_codes); hipFree(p->xq_scales);
   hipFree(p->tq_codes); hipFree(p->tq_scales);
   p->tq_codes = p->tq_scales = nullptr;
   if (p->rb_host) hipHostFree(p->rb_host);
@@ -287,6 +289,8 @@ int ensure_capacity(ft_moe_pool* p, int T) {
   const int tr = mx_gemm_rows_per_tile();
   p->max_tiles = int32_t((pairs + tr - 1) / tr + p->E + (cap + tr - 1) / tr + 2);
   if ((rc = dev_alloc(&p->row_slot, rows))) return rc;
+  if ((rc = dev_alloc(&p->xq_codes, int64_t(cap) * p->H))) return rc;
+  if ((rc = dev_alloc(&p->xq_scales, int64_t(cap) * p->H / 32))) return rc;
   if ((rc = dev_alloc(&p->tiles, 2 * int64_t(p->max_tiles)))) return rc;
   p->rb_cap = int64_t(sizeof(ResolveHeader)) + 5 * 4 * int64_t(p->E) + 8 * pairs + 64;
   if (hipHostMalloc(reinterpret_cast<void**>(&p->rb_host), p->rb_cap, hipHostMallocMapped | hipHostMallocCoherent) !=
@@ -538,26 +542,37 @@ int copy_layer_staging(ft_moe_pool* p, int layer) {
   return FT_OK;
 }
 
-// Quantises rows straight into the GEMM's activation tiles (x by token, to
-// the slots of its k expert rows and its shared-expert row; h row by row);
-// timed as one stage.
-int mx_act_tiles(ft_moe_pool* p, const uint16_t* src, int nrows, int K, const int32_t* pair_row, int shared_row0,
-                 bool fp4, hipStream_t s) {
+// The GEMM's activation tiles: x is quantised row-major (one row per token)
+// and copied into the tiles of every expert row that reads it; h (rows in
+// grouped order) is quantised straight into its tile slots.  Timed as one stage.
+int mx_act_tiles(ft_moe_pool* p, const uint16_t* src, int nrows, int K, bool by_token, bool fp4, hipStream_t s) {
   hipEvent_t e0 = prof_begin(p, s, FT_STAGE_ACT_QUANT);
   MxQuantArgs q{};
   q.in = src;
   q.rows = nrows;
   q.K = K;
-  q.pair_row = pair_row;
-  q.k = p->k;
-  q.shared_row0 = shared_row0;
-  q.row_slot = p->row_slot;
-  q.out_codes = p->tq_codes;
-  q.out_scales = p->tq_scales;
-  FT_HIP_CHECK(launch_mx_quant_tiles(q, fp4, s));
+  q.row_slot = by_token ? nullptr : p->row_slot;
+  q.out_codes = by_token ? p->xq_codes : p->tq_codes;
+  q.out_scales = by_token ? p->xq_scales : p->tq_scales;
+  FT_HIP_CHECK(launch_mx_quant(q, fp4, s));
   const double per = fp4 ? 0.5 + 1.0 / 32 : 1.0 + 1.0 / 32;
-  const double outs = pair_row ? double(nrows) * (p->k + (shared_row0 >= 0 ? 1 : 0)) : double(nrows);
-  prof_end(p, FT_STAGE_ACT_QUANT, e0, s, double(nrows) * K * 2.0 + outs * K * per, 0.0);
+  double bytes = double(nrows) * K * (2.0 + per);
+  if (by_token) {
+    MxTileArgs t{};
+    t.codes = p->xq_codes;
+    t.scales = p->xq_scales;
+    t.K = K;
+    t.row_map = p->row_tok;
+    t.groups = p->groups;
+    t.tiles = p->tiles;
+    t.n_tiles_dev = p->dev_header + 10;
+    t.max_tiles = p->max_tiles;
+    t.out_codes = p->tq_codes;
+    t.out_scales = p->tq_scales;
+    FT_HIP_CHECK(launch_mx_tile_gather(t, fp4, s));
+    bytes += 2.0 * double(nrows) * p->k * K * per;
+  }
+  prof_end(p, FT_STAGE_ACT_QUANT, e0, s, bytes, 0.0);
   return FT_OK;
 }
 
@@ -572,7 +587,7 @@ int run_mx_ffn(ft_moe_pool* p, int layer, const void* x, int T, bool fp4, hipStr
         (rc = dev_alloc(&p->tq_scales, blocks * kMxTileScaleBytes)))
       return rc;
   }
-  int rc = mx_act_tiles(p, static_cast<const uint16_t*>(x), T, p->H, p->pair_row, p->shared ? T * p->k : -1, fp4, s);
+  int rc = mx_act_tiles(p, static_cast<const uint16_t*>(x), T, p->H, true, fp4, s);
   if (rc) return rc;
   MxGemmArgs a{};
   a.groups = p->groups;
@@ -590,7 +605,7 @@ int run_mx_ffn(ft_moe_pool* p, int layer, const void* x, int T, bool fp4, hipStr
   FT_HIP_CHECK(launch_mx_gemm(a, true, fp4, s, ev));
   prof_push(p, FT_STAGE_FFN_GATEUP, ev, (p->E + p->shared) * 2 * mat_bytes(FT_FMT_MXFP4, I, H) + rows * I * 2.0 +
             T * H * (fp4 ? 0.5 + 1.0 / 32 : 1.0 + 1.0 / 32), rows * 4 * H * I);
-  if ((rc = mx_act_tiles(p, p->hbuf, rows, p->I, nullptr, -1, fp4, s))) return rc;
+  if ((rc = mx_act_tiles(p, p->hbuf, rows, p->I, false, fp4, s))) return rc;
   a.out = p->pbuf;
   ev = prof_pair(p, s, FT_STAGE_FFN_DOWN);
   FT_HIP_CHECK(launch_mx_gemm(a, false, fp4, s, ev));
@@ -1636,7 +1651,7 @@ void ft_moe_destroy_pool(ft_moe_pool* p) {
   hipFree(p->pair_row); hipFree(p->row_tok); hipFree(p->row_w); hipFree(p->groups); hipFree(p->glist); hipFree(p->gdesc); hipFree(p->count_max);
   hipFree(p->dev_header); hipFree(p->hbuf); hipFree(p->pbuf); hipFree(p->fail_dev);
   hipFree(p->key_off_dev); hipFree(p->prof_cnt_dev);
-  hipFree(p->row_slot); hipFree(p->tiles);
+  hipFree(p->row_slot); hipFree(p->tiles); hipFree(p->xq_codes); hipFree(p->xq_scales);
   hipFree(p->tq_codes); hipFree(p->tq_scales);
   if (p->rb_host) hipHostFree(p->rb_host);
   if (p->x_host) hipHostFree(p->x_host);
