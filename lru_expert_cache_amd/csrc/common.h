@@ -262,7 +262,7 @@ struct MxTileArgs {
   const uint8_t* codes;
   const uint8_t* scales;
   int32_t K;
-  const int32_t* row_map;     // grouped row -> source row
+  const int32_t* row_map;     // grouped row -> source row, or null: the row itself
   const GroupDesc* groups;
   const int32_t* tiles;       // (group, tile) pairs
   const int32_t* n_tiles_dev;

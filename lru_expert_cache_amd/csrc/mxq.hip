@@ -155,7 +155,7 @@ __global__ __launch_bounds__(256) void k_mx_tile_gather(MxTileArgs a) {
     const int r = r0 + 16 * s + n;
     u32x4 v = {0u, 0u, 0u, 0u};
     if (r < g.row_count) {
-      const int64_t src = a.row_map[g.row_begin + r];
+      const int64_t src = a.row_map ? int64_t(a.row_map[g.row_begin + r]) : int64_t(g.row_begin + r);
       const int64_t k = FP4 ? int64_t(kb) * 64 + 16 * q : int64_t(kb) * 128 + 64 * h + 16 * q;
       v = gload<u32x4>(a.codes + src * pitch + k);
     }
@@ -164,7 +164,10 @@ __global__ __launch_bounds__(256) void k_mx_tile_gather(MxTileArgs a) {
   if (threadIdx.x < kMxTileRows) {
     const int r = r0 + int(threadIdx.x);
     uint32_t sv = 0;
-    if (r < g.row_count) sv = gload<uint32_t>(a.scales + int64_t(a.row_map[g.row_begin + r]) * spitch + int64_t(kb) * 4);
+    if (r < g.row_count) {
+      const int64_t src = a.row_map ? int64_t(a.row_map[g.row_begin + r]) : int64_t(g.row_begin + r);
+      sv = gload<uint32_t>(a.scales + src * spitch + int64_t(kb) * 4);
+    }
     gstore<uint32_t>(a.out_scales + blk * kMxTileScaleBytes + int64_t(threadIdx.x) * 4, sv);
   }
 }
