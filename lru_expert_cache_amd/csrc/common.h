@@ -61,6 +61,10 @@ void repack_expert(const ExpertLayout& L, const uint8_t* canonical, uint8_t* dst
 void unpack_row_f64(const ExpertLayout& L, const uint8_t* dev_blob, int m, int row, double* out);
 // device layout -> fp32 row-major matrix m (rows*cols)
 void unpack_matrix_f32(const ExpertLayout& L, const uint8_t* dev_blob, int m, float* out);
+// host_ffn.cpp: one expert's SwiGLU FFN on CPU threads, weights in the device
+// layout (the pinned host store), x bf16 [rows][H] -> p = bf16(w * y) [rows][H]
+void host_expert(const ExpertLayout& L, const uint8_t* blob, const uint16_t* x, const float* wts, int rows,
+                 uint16_t* out, int threads);
 
 // ------------------------------------------------------------ per-call device records
 struct alignas(64) GroupDesc {

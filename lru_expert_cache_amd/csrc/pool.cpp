@@ -194,67 +194,6 @@ void parallel_for(int n, int threads, const std::function<void(int, int)>& fn) {
   for (auto& x : th) x.join();
 }
 
-inline uint16_t bf16_from_double(double x) {
-  float f;
-  if (x == 0.0 || !std::isfinite(x)) {
-    f = float(x);
-  } else {
-    int e;
-    std::frexp(x, &e);
-    e = std::max(e, -125);
-    const double q = std::ldexp(1.0, e - 8);
-    f = float(std::nearbyint(x / q) * q);
-  }
-  uint32_t u;
-  std::memcpy(&u, &f, 4);
-  return uint16_t(u >> 16);
-}
-
-inline double bf16_to_double(uint16_t b) {
-  const uint32_t u = uint32_t(b) << 16;
-  float f;
-  std::memcpy(&f, &u, 4);
-  return f;
-}
-
-// Host SwiGLU expert on `rows` rows of x (bf16, [rows][H]), weights in the
-// device layout; writes p = bf16(w * y) rows.  fp64 accumulation; the same
-// rounding points as the GPU path.
-void host_expert(const ExpertLayout& L, const uint8_t* blob, const uint16_t* x, const float* wts, int rows,
-                 uint16_t* out, int threads) {
-  const int H = L.hidden, I = L.inter;
-  std::vector<double> xd(size_t(rows) * H), hd(size_t(rows) * I);
-  for (size_t i = 0; i < xd.size(); ++i) xd[i] = bf16_to_double(x[i]);
-  parallel_for(I, threads, [&](int b, int e) {
-    std::vector<double> rg(H), ru(H);
-    for (int i = b; i < e; ++i) {
-      unpack_row_f64(L, blob, 0, i, rg.data());
-      unpack_row_f64(L, blob, 1, i, ru.data());
-      for (int r = 0; r < rows; ++r) {
-        const double* xr = &xd[size_t(r) * H];
-        double g = 0.0, u = 0.0;
-        for (int h = 0; h < H; ++h) {
-          g += rg[h] * xr[h];
-          u += ru[h] * xr[h];
-        }
-        hd[size_t(r) * I + i] = bf16_to_double(bf16_from_double(g / (1.0 + std::exp(-g)) * u));
-      }
-    }
-  });
-  parallel_for(H, threads, [&](int b, int e) {
-    std::vector<double> rd(I);
-    for (int o = b; o < e; ++o) {
-      unpack_row_f64(L, blob, 2, o, rd.data());
-      for (int r = 0; r < rows; ++r) {
-        const double* hr = &hd[size_t(r) * I];
-        double y = 0.0;
-        for (int i = 0; i < I; ++i) y += rd[i] * hr[i];
-        out[size_t(r) * H + o] = bf16_from_double(double(wts[r]) * y);
-      }
-    }
-  });
-}
-
 int ensure_capacity(ft_moe_pool* p, int T) {
   if (T <= p->cap_T) return FT_OK;
   const int cap = std::max(T, 64);
