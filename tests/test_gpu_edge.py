@@ -154,19 +154,19 @@ def test_failed_copy_leaves_key_non_resident(monkeypatch):
         g.close()
 
 
-def _act_case(shared, act_mode):
+def _act_case(shared, act_mode, H=256, T=300, cfg_id=120):
     from tests.moe_case import GpuLayerStack, rel_l2
     from oracle import ffn as OFFN, formats as OF
     import lru_expert_cache_amd as ft
 
-    w = _small(120 + int(shared), 3, 256, 256, 8, 2, [MX, MX, MX], 16, shared=shared)
+    w = _small(cfg_id + int(shared), 3, H, 256, 8, 2, [MX, MX, MX], 16, shared=shared)
     g = GpuLayerStack(w)
     o = OracleLayerStack(w, pool_slots=g.C, act_mode=act_mode)
     flag = ft.FT_ACT_MXFP4 if act_mode == OFFN.ACT_MXFP4 else ft.FT_ACT_MXFP8
     rels = []
     try:
         for l in range(3):
-            x = ms.activations(w, l, 7, 300)  # ~75 rows per expert: two 64-row tiles, ragged tail
+            x = ms.activations(w, l, 7, T)  # T=300: ~75 rows per expert, one ragged 128-row tile
             gr = g.forward(l, x, g.bias(l, 0), prefill=True, act=flag)
             orr = o.forward(l, x, ms.popularity_bias(w, l, 0), prefill=True)
             from tests.moe_case import compare_call
@@ -191,6 +191,19 @@ def test_prefill_mx_activation_modes_small(shared, act):
     # accumulation vs fp64; with 8-bit operands the block-scaled MFMA also sums
     # each block with fewer bits than fp32), which moves single elements by one
     # grid step
+    assert max(rels) <= (2e-3 if act == "mxfp8" else 6e-3)
+
+
+@pytest.mark.parametrize("act", ["mxfp8", "mxfp4"])
+def test_prefill_mx_narrow_workgroup_tiles(act):
+    # hidden 384: the down GEMM's 384 output features take the 2-wave-column
+    # workgroup tile (128 features), the gate/up's 256 the wider ones; 600
+    # tokens give ~150 rows per expert, two 128-row tiles with a ragged tail
+    from oracle import ffn as OFFN
+
+    mode = OFFN.ACT_MXFP4 if act == "mxfp4" else OFFN.ACT_MXFP8
+    rels = _act_case(True, mode, H=384, T=600, cfg_id=124)
+    print(act, "rel-L2", rels)
     assert max(rels) <= (2e-3 if act == "mxfp8" else 6e-3)
 
 
