@@ -281,15 +281,18 @@ struct MxGemmArgs {
   const int32_t* tiles;       // (group, tile) pairs
   const int32_t* n_tiles_dev; // number of valid pairs
   int32_t max_tiles;          // grid bound
-  const uint8_t* act_codes;   // activation tiles (the layout above)
+  const uint8_t* act_codes;   // MX activations: the activation tiles (the layout above)
   const uint8_t* act_scales;
+  const uint16_t* act_rows;   // bf16 activations: gate/up x [T][H] (by token), down h [rows][I]
+  const int32_t* row_tok;     // bf16 gate/up: token of each row; null for down
   const float* row_w;         // down: routing weight of each row
   uint16_t* out;              // gate/up: h [rows][I]; down: p [rows][H]
   int32_t hidden, inter;
   ExpertLayout lay;
 };
 int mx_gemm_rows_per_tile();
-hipError_t launch_mx_gemm(const MxGemmArgs& a, bool gateup, bool act_fp4, hipStream_t s, Ev ev = {});
+// act: FT_ACT_* >> 4 (0 bf16, 1 MXFP8, 2 MXFP4); weights MXFP4
+hipError_t launch_mx_gemm(const MxGemmArgs& a, bool gateup, int act, hipStream_t s, Ev ev = {});
 
 // ------------------------------------------------------------ errors
 void set_error(const char* fmt, ...);

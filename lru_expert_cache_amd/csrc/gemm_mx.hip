@@ -45,6 +45,11 @@ typedef int intx8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short bf16x8 __attribute__((ext_vector_type(8)));
+typedef short bf16x2 __attribute__((ext_vector_type(2)));
+
+// activation operand (the prefill activation modes, FT_ACT_* >> 4)
+constexpr int kActBf16 = 0, kActFp8 = 1, kActFp4 = 2;
 
 constexpr int kRowsPerTile = kMxTileRows;  // activation rows per workgroup tile
 // weight tiles of 16 features per wave and per matrix (64 accumulator columns a wave)
@@ -66,23 +71,39 @@ __device__ inline float silu_fast(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// 1 KB activation pieces of a step: FP4 the 8 sub-tiles of 16 rows, FP8 their
+// halves, bf16 the 4 K quarters of each (one 16x16x32 B operand each)
+constexpr int mx_pieces(int act) { return act == kActFp4 ? 8 : act == kActFp8 ? 16 : 32; }
 // One K step's operands in LDS, in the order the MFMAs read them.
-template <bool ACT_FP4, int WF>
+template <int ACT, int WF>
 struct MxStage {
-  u32x4 a[4 * WF][64];               // 4 WF weight tiles, A-operand lane order
-  u32x4 b[8][ACT_FP4 ? 64 : 128];    // 16-row sub-tiles: FP4 [lane]; FP8 [half * 64 + lane]
-  uint8_t as[4 * WF][64];            // weight scale bytes [tile][lane]
-  uint32_t bs[kRowsPerTile];         // activation scales of the step: row -> bytes of blocks 0..3
+  u32x4 a[4 * WF][64];                        // 4 WF weight tiles, A-operand lane order
+  u32x4 b[8][mx_pieces(ACT) / 8 * 64];        // 16-row sub-tiles: FP4 [lane]; FP8 [half * 64 + lane];
+                                              // bf16 [quarter * 64 + lane]
+  uint8_t as[4 * WF][64];                     // weight scale bytes [tile][lane]
+  uint32_t bs[ACT == kActBf16 ? 1 : kRowsPerTile];  // activation scales: row -> bytes of blocks 0..3
 };
-// 1 KB activation pieces of a step (FP4: the 8 sub-tiles; FP8: their halves)
-constexpr int mx_pieces(bool act_fp4) { return act_fp4 ? 8 : 16; }
-// ring depth: two workgroups per CU fit with WF 2 (and WF 4 FP4), one otherwise
-constexpr int mx_stages(bool act_fp4, int wf) { return wf == 2 && act_fp4 ? 4 : 3; }
+// ring depth: two workgroups per CU fit with WF 2 FP4 (and WF 4 FP4), one otherwise
+constexpr int mx_stages(int act, int wf) { return wf == 2 && act == kActFp4 ? 4 : 3; }
 // loads per wave and stage: 2 weight tiles, their scales, the wave's share of
 // the activation pieces (half a piece when there are more waves than pieces),
-// and its share of the activation scales
-constexpr int mx_loads_per_stage(bool act_fp4, int wf) {
-  return 2 + 1 + (mx_pieces(act_fp4) >= 2 * wf ? mx_pieces(act_fp4) / (2 * wf) : 1) + 1;
+// and its share of the activation scales (none for bf16)
+constexpr int mx_loads_per_stage(int act, int wf) {
+  return 2 + 1 + (mx_pieces(act) >= 2 * wf ? mx_pieces(act) / (2 * wf) : 1) + (act == kActBf16 ? 0 : 1);
+}
+
+// 8 FP4 codes (element 2i in the low nibble of byte i) x E8M0 scale -> 8 bf16,
+// exact (the scaled convert applies the exponent of its scale operand)
+__device__ inline bf16x8 fp4x8_to_bf16(uint32_t w, float s) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+__device__ inline bf16x8 as_bf16x8(u32x4 v) {
+  return bf16x8{short(v[0] & 0xFFFF), short(v[0] >> 16), short(v[1] & 0xFFFF), short(v[1] >> 16),
+                short(v[2] & 0xFFFF), short(v[2] >> 16), short(v[3] & 0xFFFF), short(v[3] >> 16)};
 }
 
 // s_waitcnt immediate for vmcnt(n) (6-bit count: bits 3:0 and 15:14), no other waits
@@ -97,15 +118,17 @@ __device__ __attribute__((always_inline)) inline void lds_load4(const void* src,
   __builtin_amdgcn_global_load_lds((const FT_GLOBAL void*)src, (FT_L3 void*)dst, 4, 0, 0);
 }
 
-template <bool GATEUP, bool ACT_FP4, int WF>
+template <bool GATEUP, int ACT, int WF>
 __global__ __launch_bounds__(128 * WF) void k_mx_gemm(MxGemmArgs a) {
+  constexpr bool ACT_FP4 = ACT == kActFp4;
   constexpr int NM = GATEUP ? 2 : 1;
   constexpr int FT = feat_tiles(GATEUP);
   constexpr int NW = 2 * WF;        // waves
   constexpr int TPM = WF * FT;      // weight tiles per matrix and workgroup
-  constexpr int S = mx_stages(ACT_FP4, WF);
-  constexpr int LPS = mx_loads_per_stage(ACT_FP4, WF);
-  __shared__ MxStage<ACT_FP4, WF> sm[S];
+  constexpr int S = mx_stages(ACT, WF);
+  constexpr int LPS = mx_loads_per_stage(ACT, WF);
+  static_assert(ACT != kActBf16 || mx_pieces(ACT) % (4 * NW) == 0, "bf16: whole 16-row sub-tiles per wave");
+  __shared__ MxStage<ACT, WF> sm[S];
 
   // XCD-aware order: items (row tile, feature block) run row-tile-major, and
   // the item list is cut into 8 contiguous ranges, one per XCD (workgroups
@@ -138,12 +161,26 @@ __global__ __launch_bounds__(128 * WF) void k_mx_gemm(MxGemmArgs a) {
   // in B-operand lane order, then the rows' scales)
   const uint8_t* TB = a.act_codes + int64_t(tile) * nkb * mx_tile_code_bytes(ACT_FP4);
   const uint8_t* TS = a.act_scales + int64_t(tile) * nkb * kMxTileScaleBytes;
+  // bf16 activations come straight from their rows (x by token, h by row):
+  // this wave loads the 16-row sub-tiles w * SPW .. ; a lane's row start, the
+  // group's first row standing in past its end (those outputs are not stored)
+  constexpr int SPW = ACT == kActBf16 ? mx_pieces(ACT) / (4 * NW) : 1;
+  const uint8_t* brow[SPW];
+  if constexpr (ACT == kActBf16) {
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+      const int r = r0 + 16 * (w * SPW + i) + n;
+      const int row = g.row_begin + (r < g.row_count ? r : 0);
+      const int64_t src = a.row_tok ? int64_t(a.row_tok[row]) : int64_t(row);
+      brow[i] = reinterpret_cast<const uint8_t*>(a.act_rows + src * K);
+    }
+  }
 
   // the 4 WF staged weight tiles: chunk ci = matrix (ci / TPM), tile fb*TPM + ci % TPM
   auto chunk_mat = [&](int ci) -> const MatLayout& { return a.lay.m[GATEUP ? ci / TPM : 2]; };
   auto chunk_tile = [&](int ci, int kb) -> int64_t { return int64_t(fb * TPM + ci % TPM) * nkb + kb; };
   // one K step's loads into a stage: LPS per wave, whatever the wave
-  auto issue = [&](int kb, MxStage<ACT_FP4, WF>& st) {
+  auto issue = [&](int kb, MxStage<ACT, WF>& st) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int ci = 2 * w + j;
@@ -154,22 +191,31 @@ __global__ __launch_bounds__(128 * WF) void k_mx_gemm(MxGemmArgs a) {
       const int ci = 2 * w + (lane >> 2), part = lane & 3;
       lds_load16(W + chunk_mat(2 * w).scales_off + chunk_tile(ci, kb) * 64 + part * 16, &st.as[2 * w][0]);
     }
-    // activation piece pc (1 KB) of the tile layout lands at piece pc of st.b
-    const uint8_t* tb = TB + int64_t(kb) * mx_tile_code_bytes(ACT_FP4) + lane * 16;
-    u32x4* bb = &st.b[0][0];
-    constexpr int PC = mx_pieces(ACT_FP4);
-    if constexpr (PC >= NW) {
+    if constexpr (ACT == kActBf16) {
+      // quarter j of a sub-tile: lane 16 q + n reads its row's K 128 kb + 32 q + 8 j .. + 7
 #pragma unroll
-      for (int j = 0; j < PC / NW; ++j) lds_load16(tb + (w * (PC / NW) + j) * 1024, bb + (w * (PC / NW) + j) * 64);
+      for (int i = 0; i < SPW; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          lds_load16(brow[i] + (int64_t(kb) * kTileK + 32 * q + 8 * j) * 2, &st.b[w * SPW + i][j * 64]);
     } else {
-      // two waves per piece, half the lanes each (lane i still writes at + 16 i)
-      if ((lane >> 5) == (w & 1)) lds_load16(tb + (w >> 1) * 1024, bb + (w >> 1) * 64);
+      // activation piece pc (1 KB) of the tile layout lands at piece pc of st.b
+      const uint8_t* tb = TB + int64_t(kb) * mx_tile_code_bytes(ACT_FP4) + lane * 16;
+      u32x4* bb = &st.b[0][0];
+      constexpr int PC = mx_pieces(ACT);
+      if constexpr (PC >= NW) {
+#pragma unroll
+        for (int j = 0; j < PC / NW; ++j) lds_load16(tb + (w * (PC / NW) + j) * 1024, bb + (w * (PC / NW) + j) * 64);
+      } else {
+        // two waves per piece, half the lanes each (lane i still writes at + 16 i)
+        if ((lane >> 5) == (w & 1)) lds_load16(tb + (w >> 1) * 1024, bb + (w >> 1) * 64);
+      }
+      constexpr int SL = kRowsPerTile / NW;  // rows of activation scales per wave
+      if (lane < SL) lds_load4(TS + int64_t(kb) * kMxTileScaleBytes + (w * SL + lane) * 4, &st.bs[w * SL]);
     }
-    constexpr int SL = kRowsPerTile / NW;  // rows of activation scales per wave
-    if (lane < SL) lds_load4(TS + int64_t(kb) * kMxTileScaleBytes + (w * SL + lane) * 4, &st.bs[w * SL]);
   };
 
-  // FP8 activations: 16x16x128 MFMAs, acc[matrix][16-feature tile][16-row tile];
+  // FP8 activations: 16x16x128 MFMAs, bf16: 16x16x32 MFMAs, acc[matrix][16-feature tile][16-row tile];
   // FP4 x FP4: 32x32x64 MFMAs (measured 1.6x the 16x16x128 FP4 rate on gfx950),
   // acc32[matrix][32-feature block][32-row block]
   constexpr int NA = ACT_FP4 ? 1 : NM * FT * 4;
@@ -192,8 +238,8 @@ __global__ __launch_bounds__(128 * WF) void k_mx_gemm(MxGemmArgs a) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * LPS));
     __builtin_amdgcn_s_barrier();
     issue(min(kb + S - 1, nkb - 1), sm[(kb + S - 1) % S]);
-    const MxStage<ACT_FP4, WF>& st = sm[kb % S];
-    if constexpr (ACT_FP4) {
+    const MxStage<ACT, WF>& st = sm[kb % S];
+    if constexpr (ACT == kActFp4) {
       // 32x32x64 operands gathered from the 16x16x128-ordered stage: lane l
       // takes row (or token) l % 32 -- tile (l % 32) / 16, row l % 16 -- and
       // the 32-K block 2h + l / 32 of the 128-K step (h = 0, 1)
@@ -225,7 +271,7 @@ __global__ __launch_bounds__(128 * WF) void k_mx_gemm(MxGemmArgs a) {
             }
           }
       }
-    } else {
+    } else if constexpr (ACT == kActFp8) {
       intx8 B[4];
       int sb[4];
 #pragma unroll
@@ -251,6 +297,32 @@ __global__ __launch_bounds__(128 * WF) void k_mx_gemm(MxGemmArgs a) {
                                                                  0 /* B: fp8 e4m3 */, 0, sa, 0, sb[t]);
           }
         }
+    } else {
+      // bf16 activations: 16x16x32 MFMAs.  A = dword j of a weight tile's lane
+      // (row r, K 32 q + 8 j .. + 7 for lane 16 q + r) as bf16 with its scale;
+      // B = quarter j of a row sub-tile (the same K, token n)
+      u32x4 c[NM * FT];
+      float sa[NM * FT];
+#pragma unroll
+      for (int mi = 0; mi < NM; ++mi)
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft) {
+          const int ci = mi * TPM + fh * FT + ft;
+          c[mi * FT + ft] = st.a[ci][lane];
+          sa[mi * FT + ft] = __uint_as_float(uint32_t(st.as[ci][lane]) << 23);  // E8M0: the exponent is used
+        }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x8 B[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) B[t] = as_bf16x8(st.b[th * 4 + t][j * 64 + lane]);
+#pragma unroll
+        for (int i = 0; i < NM * FT; ++i) {
+          const bf16x8 A = fp4x8_to_bf16(c[i][j], sa[i]);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc[i * 4 + t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B[t], acc[i * 4 + t], 0, 0, 0);
+        }
+      }
     }
   }
   // the loads of steps past the end may still be writing LDS
@@ -328,36 +400,44 @@ int mx_gemm_rows_per_tile() { return kRowsPerTile; }
 // Widest workgroup tile tried, in wave columns of 64 features (measured on the
 // Qwen-A3B prefill layer: FP4 activations 4 -> gate/up 106 us against 122 us
 // with 2 and 112 us with 8; FP8 activations 8 -> 125 us against 144 us with 4,
-// whose 103 KB of LDS leave one 8-wave workgroup per CU).
-constexpr int mx_max_wf(bool act_fp4) { return act_fp4 ? 4 : 8; }
+// whose 103 KB of LDS leave one 8-wave workgroup per CU; bf16 activations 4,
+// whose 32 KB of activations per stage rule out 8).
+constexpr int mx_max_wf(int act) { return act == kActFp8 ? 8 : 4; }
 
 namespace {
-template <bool GATEUP, bool ACT_FP4, int WF>
+template <bool GATEUP, int ACT, int WF>
 hipError_t launch_wf(const MxGemmArgs& a, hipStream_t s, Ev ev) {
   // one workgroup per (row tile, feature block) item, at least 8 * ceil(items / 8)
   const int nfb = (GATEUP ? a.inter : a.hidden) / feat_per_wg(GATEUP, WF);
   const int64_t bound = int64_t(a.max_tiles) * nfb;
-  ft_launch(k_mx_gemm<GATEUP, ACT_FP4, WF>, dim3(unsigned((bound + 7) / 8 * 8)), dim3(128 * WF), s, ev, a);
+  ft_launch(k_mx_gemm<GATEUP, ACT, WF>, dim3(unsigned((bound + 7) / 8 * 8)), dim3(128 * WF), s, ev, a);
   return hipGetLastError();
 }
 // the widest workgroup tile (up to mx_max_wf) whose feature block divides the outputs
-template <bool GATEUP, bool ACT_FP4>
+template <bool GATEUP, int ACT>
 hipError_t launch_gf(const MxGemmArgs& a, hipStream_t s, Ev ev) {
   const int outs = GATEUP ? a.inter : a.hidden;
-  constexpr int wf = mx_max_wf(ACT_FP4);
+  constexpr int wf = mx_max_wf(ACT);
   if constexpr (wf >= 8) {
-    if (outs % feat_per_wg(GATEUP, 8) == 0) return launch_wf<GATEUP, ACT_FP4, 8>(a, s, ev);
+    if (outs % feat_per_wg(GATEUP, 8) == 0) return launch_wf<GATEUP, ACT, 8>(a, s, ev);
   }
-  if (outs % feat_per_wg(GATEUP, 4) == 0) return launch_wf<GATEUP, ACT_FP4, 4>(a, s, ev);
-  if (outs % feat_per_wg(GATEUP, 2) == 0) return launch_wf<GATEUP, ACT_FP4, 2>(a, s, ev);
+  if (outs % feat_per_wg(GATEUP, 4) == 0) return launch_wf<GATEUP, ACT, 4>(a, s, ev);
+  if (outs % feat_per_wg(GATEUP, 2) == 0) return launch_wf<GATEUP, ACT, 2>(a, s, ev);
   return hipErrorInvalidValue;
+}
+template <bool GATEUP>
+hipError_t launch_g(const MxGemmArgs& a, int act, hipStream_t s, Ev ev) {
+  switch (act) {
+    case kActBf16: return launch_gf<GATEUP, kActBf16>(a, s, ev);
+    case kActFp8: return launch_gf<GATEUP, kActFp8>(a, s, ev);
+    case kActFp4: return launch_gf<GATEUP, kActFp4>(a, s, ev);
+    default: return hipErrorInvalidValue;
+  }
 }
 }  // namespace
 
-hipError_t launch_mx_gemm(const MxGemmArgs& a, bool gateup, bool act_fp4, hipStream_t s, Ev ev) {
-  if (gateup)
-    return act_fp4 ? launch_gf<true, true>(a, s, ev) : launch_gf<true, false>(a, s, ev);
-  return act_fp4 ? launch_gf<false, true>(a, s, ev) : launch_gf<false, false>(a, s, ev);
+hipError_t launch_mx_gemm(const MxGemmArgs& a, bool gateup, int act, hipStream_t s, Ev ev) {
+  return gateup ? launch_g<true>(a, act, s, ev) : launch_g<false>(a, act, s, ev);
 }
 
 }  // namespace ftmoe

@@ -515,10 +515,16 @@ int mx_act_tiles(ft_moe_pool* p, const uint16_t* src, int nrows, int K, bool by_
   return FT_OK;
 }
 
-int run_mx_ffn(ft_moe_pool* p, int layer, const void* x, int T, bool fp4, hipStream_t s) {
+// The prefill expert FFN of an MXFP4 layer on the grouped GEMM: act is
+// FT_ACT_* >> 4.  MX modes quantise x and h into the GEMM's activation tiles;
+// bf16 reads them from their rows (x by token, h by row).
+int run_mx_ffn(ft_moe_pool* p, int layer, const void* x, int T, int act, hipStream_t s) {
   const int rows = T * p->k + (p->shared ? T : 0);
   const double H = p->H, I = p->I;
-  if (!p->tq_codes) {
+  const bool mx = act != 0, fp4 = act == (FT_ACT_MXFP4 >> 4);
+  // activation bytes per element as the GEMM reads them
+  const double per = !mx ? 2.0 : fp4 ? 0.5 + 1.0 / 32 : 1.0 + 1.0 / 32;
+  if (mx && !p->tq_codes) {
     // sized for FP8 codes of the wider matrix; freed with the per-call buffers
     const int64_t blocks = int64_t(p->max_tiles) * (std::max(p->H, p->I) / kTileK);
     int rc;
@@ -526,8 +532,8 @@ int run_mx_ffn(ft_moe_pool* p, int layer, const void* x, int T, bool fp4, hipStr
         (rc = dev_alloc(&p->tq_scales, blocks * kMxTileScaleBytes)))
       return rc;
   }
-  int rc = mx_act_tiles(p, static_cast<const uint16_t*>(x), T, p->H, true, fp4, s);
-  if (rc) return rc;
+  int rc;
+  if (mx && (rc = mx_act_tiles(p, static_cast<const uint16_t*>(x), T, p->H, true, fp4, s))) return rc;
   MxGemmArgs a{};
   a.groups = p->groups;
   a.tiles = p->tiles;
@@ -535,21 +541,25 @@ int run_mx_ffn(ft_moe_pool* p, int layer, const void* x, int T, bool fp4, hipStr
   a.max_tiles = p->max_tiles;
   a.act_codes = p->tq_codes;
   a.act_scales = p->tq_scales;
+  a.act_rows = static_cast<const uint16_t*>(x);
+  a.row_tok = p->row_tok;
   a.row_w = p->row_w;
   a.out = p->hbuf;
   a.hidden = p->H;
   a.inter = p->I;
   a.lay = p->lay[p->fmt[layer]];
   Ev ev = prof_pair(p, s, FT_STAGE_FFN_GATEUP);
-  FT_HIP_CHECK(launch_mx_gemm(a, true, fp4, s, ev));
+  FT_HIP_CHECK(launch_mx_gemm(a, true, act, s, ev));
   prof_push(p, FT_STAGE_FFN_GATEUP, ev, (p->E + p->shared) * 2 * mat_bytes(FT_FMT_MXFP4, I, H) + rows * I * 2.0 +
-            T * H * (fp4 ? 0.5 + 1.0 / 32 : 1.0 + 1.0 / 32), rows * 4 * H * I);
-  if ((rc = mx_act_tiles(p, p->hbuf, rows, p->I, false, fp4, s))) return rc;
+            T * H * per, rows * 4 * H * I);
+  if (mx && (rc = mx_act_tiles(p, p->hbuf, rows, p->I, false, fp4, s))) return rc;
+  a.act_rows = p->hbuf;
+  a.row_tok = nullptr;
   a.out = p->pbuf;
   ev = prof_pair(p, s, FT_STAGE_FFN_DOWN);
-  FT_HIP_CHECK(launch_mx_gemm(a, false, fp4, s, ev));
+  FT_HIP_CHECK(launch_mx_gemm(a, false, act, s, ev));
   prof_push(p, FT_STAGE_FFN_DOWN, ev, (p->E + p->shared) * mat_bytes(FT_FMT_MXFP4, H, I) + rows * H * 2.0 +
-            rows * I * (fp4 ? 0.5 + 1.0 / 32 : 1.0 + 1.0 / 32), rows * 2 * H * I);
+            rows * I * per, rows * 2 * H * I);
   return FT_OK;
 }
 
@@ -620,8 +630,9 @@ int forward_prefill(ft_moe_pool* p, int layer, int T, const void* x, void* out, 
   FT_HIP_CHECK(launch_resolve(ra, s, er));
   prof_push(p, FT_STAGE_RESOLVE, er, 0.0, 0.0);
   const double rows = double(T) * p->k + (p->shared ? T : 0);
-  int rc = act != 0 ? run_mx_ffn(p, layer, x, T, act == (FT_ACT_MXFP4 >> 4), s)
-                    : run_ffn(p, layer, x, 0, E + 1, p->dev_header + 9, s, E + p->shared, rows);
+  // MXFP4 layers run the grouped GEMM (bf16 or MX activations); others the FFN kernels
+  int rc = p->fmt[layer] == FT_FMT_MXFP4 ? run_mx_ffn(p, layer, x, T, act, s)
+                                         : run_ffn(p, layer, x, 0, E + 1, p->dev_header + 9, s, E + p->shared, rows);
   if (rc) return rc;
   Ev ev = prof_pair(p, s, FT_STAGE_COMBINE);
   FT_HIP_CHECK(launch_combine(p->pbuf, p->pair_row, 0, T, p->k, p->H, p->shared ? T * p->k : -1,
