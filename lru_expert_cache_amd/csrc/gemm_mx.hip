@@ -1,39 +1,44 @@
-// Grouped expert GEMM of a prefill chunk on gfx950's block-scaled MFMA,
-// v_mfma_scale_f32_16x16x128_f8f6f4, with MXFP4 weights and MX-quantised
-// activations (MXFP4 or MXFP8, the prefill activation modes).
+// Grouped expert GEMM of a prefill chunk with MXFP4 weights, on gfx950's
+// MFMA: bf16 activations (the default prefill mode) or MX-quantised ones
+// (MXFP8 / MXFP4, the prefill activation modes).
 //
-// Both operands reach the instruction in the form it takes, with no conversion:
+// Operands, per 16-row sub-tile and 128-K step:
 //   A = a 16x128 weight tile of the device layout: lane 16q+r holds row r,
-//       K 32q..32q+31 as 16 bytes of E2M1 codes, and its E8M0 scale byte;
-//   B = 16 activation rows: lane 16q+n holds row n and the row's E8M0 scale of
+//       K 32q..32q+31 as 16 bytes of E2M1 codes, and its E8M0 scale byte.
+//   MX activations reach v_mfma_scale_f32_*_f8f6f4 as stored, with no
+//       conversion: lane 16q+n holds activation row n and its E8M0 scale of
 //       32-block q.  FP4: K 32q..32q+31 as 16 bytes (dwords 0-3).  FP8: the
 //       8-bit operand splits K in two halves, K 16q..16q+15 in dwords 0-3 and
 //       K 64+16q..64+16q+15 in dwords 4-7 (measured on gfx950 with an
-//       in-bounds probe of the instruction).
-// One instruction multiplies a 16x128 weight tile by 128 K of 16 rows.
+//       in-bounds probe of the instruction).  FP4 x FP4 runs the 32x32x64 form
+//       (operands regathered from the same stage), FP8 the 16x16x128 one.
+//   bf16 activations run v_mfma_f32_16x16x32_bf16 four times per step: dword
+//       j of a weight lane becomes the A operand after one scaled convert
+//       (exact), and the B operand is K 32q+8j..+7 of row n, 16 bytes.
 //
 // Work: a list of (group, 128-row tile) built by the resolve kernel, times the
-// blocks of output features; one workgroup per item, in an XCD-aware order.  A workgroup computes 128 rows x
-// 128 features (down) or 128 rows x 64 features of both matrices (gate/up);
-// each of its 4 waves owns 64 rows x 64 accumulator columns, i.e. 16 MFMA per
-// 128-K step, and eight 16x128 weight tiles are staged per step either way.
+// blocks of output features; one workgroup per item, in an XCD-aware order.
+// A workgroup of 2 WF waves computes 128 rows x 64 WF accumulator columns:
+// each wave owns 64 rows x 64 columns (gate/up: 32 features of each matrix),
+// and 4 WF weight tiles are staged per step.
 //
 // K steps stream through a ring of LDS stages filled by global-to-LDS loads
 // (global_load_lds_dwordx4: lane i of a wave writes 16 bytes at the stage
 // address + 16 i, so a 1 KB weight tile lands in the A-operand lane order as it
-// is stored, and so does a 1 KB activation sub-tile of the tile layout that
-// launch_mx_tile_gather writes; the 4-byte form writes lane i at + 4 i and
-// carries the rows' scale bytes).  Every load reads contiguous bytes: the
-// gathered rows of the activations (64 bytes of a row per step, and 4 scale
-// bytes) spread a step over ~3x the cache lines, which the L1's outstanding
+// is stored; so does a 1 KB activation piece of the MX tile layout that
+// the quantiser and launch_mx_tile_gather write, and a quarter sub-tile of bf16
+// rows when each lane reads its row's 16 bytes; the 4-byte form writes lane i
+// at + 4 i and carries the rows' scale bytes).  Every load reads whole cache
+// lines: the MX rows gathered by token (64 bytes of a row per step, and 4
+// scale bytes) spread a step over ~3x the lines, which the L1's outstanding
 // misses then limit.  Every wave issues the same number of loads
 // per stage, so one immediate vmcnt wait plus a barrier makes a stage ready
 // while the later stages stay in flight: a step waits for its own data, not a
 // whole memory latency.  Steps past the end re-load the last step (never
 // used), which keeps the counts exact; the ring is drained before the
-// epilogue.  Activation rows past the group's end are zeros in the tile
-// layout and feed output columns that are not written.  Epilogues as the
-// decode FFN: gate/up -> h = bf16(silu(g) * u); down -> p = bf16(w * y).
+// epilogue.  Activation rows past the group's end (zeros, stale codes or the
+// group's first row) feed output columns that are not written.  Epilogues as
+// the decode FFN: gate/up -> h = bf16(silu(g) * u); down -> p = bf16(w * y).
 #include "common.h"
 #include "gmem.h"
 
