@@ -38,7 +38,9 @@
 // used), which keeps the counts exact; the ring is drained before the
 // epilogue.  Activation rows past the group's end (zeros, stale codes or the
 // group's first row) feed output columns that are not written.  Epilogues as
-// the decode FFN: gate/up -> h = bf16(silu(g) * u); down -> p = bf16(w * y).
+// the decode FFN: gate/up -> h = bf16(silu(g) * u); down -> p = bf16(w * y);
+// the down output and the FP4 gate/up one are put together as a 128-row tile
+// in the freed stage ring and written as whole 128-byte lines of their rows.
 #include "common.h"
 #include "gmem.h"
 
@@ -333,32 +335,41 @@ __global__ __launch_bounds__(128 * WF) void k_mx_gemm(MxGemmArgs a) {
   // the loads of steps past the end may still be writing LDS
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
-  // epilogue: 4 consecutive features of one row per store; gate/up ->
-  // h = bf16(silu(g) * u), down -> p = bf16(w * y).  The routing weights of
-  // the lane's rows are read once, before any store (the compiler would
-  // otherwise reload them after every store it cannot prove disjoint).
+  // epilogue: a lane holds 4 consecutive features of one row (gate/up ->
+  // h = bf16(silu(g) * u), down -> p = bf16(w * y)).  Stored from there, a
+  // store writes 16 (32x32 layout) or 32 bytes (16x16) in each of 32 or 16
+  // rows.  The down output (a 4096-byte row of p) and the FP4 gate/up one go
+  // through LDS instead: the workgroup's 128-row output tile is put together
+  // in the free stage ring and leaves in 16-byte pieces, 8 lanes per 128-byte
+  // line of a row.  (The 16x16 gate/up stores measured no slower than the
+  // extra barriers.)  The routing weights of the lane's rows are read once,
+  // before any output is written.
+  constexpr bool TILE_EPI = !GATEUP || ACT_FP4;
+  constexpr int NF = feat_per_wg(GATEUP, WF);  // output features of the workgroup
+  constexpr int PITCH = NF * 2 + 16;           // tile row pitch (bytes): row r starts 4 r banks on
+  static_assert(!TILE_EPI || kRowsPerTile * PITCH <= int(sizeof(sm)), "the output tile fits in the stage ring");
+  uint8_t* tile_out = reinterpret_cast<uint8_t*>(&sm[0]);
+  const int ld = GATEUP ? a.inter : a.hidden;
+  uint16_t* ob = a.out + int64_t(g.row_begin + r0) * ld + int64_t(fb) * NF;
+  // every wave is past its wait and its last reads of the stage ring
+  if constexpr (TILE_EPI) __syncthreads();
   auto row_weight = [&](int rloc) -> float {
     const int r = r0 + rloc;
     return !GATEUP && r < g.row_count ? a.row_w[g.row_begin + r] : 0.0f;
   };
-  auto emit = [&](int rloc, int o0, const float (&gv)[4], const float (&uv)[4], float wr) {
-    const int r = r0 + rloc;
-    if (r >= g.row_count) return;
-    const int row = g.row_begin + r;
+  // rloc: row in the tile, o: feature in the workgroup's block (rows past the
+  // group's end are computed from stand-in operands and not stored)
+  auto emit = [&](int rloc, int o, const float (&gv)[4], const float (&uv)[4], float wr) {
     uint16_t hv[4];
-    if constexpr (GATEUP) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) hv[i] = f32_to_bf16_rne(silu_fast(gv[i]) * uv[i]);
-      *reinterpret_cast<uint2*>(a.out + int64_t(row) * a.inter + o0) =
-          make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16), uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) hv[i] = f32_to_bf16_rne(wr * gv[i]);
-      *reinterpret_cast<uint2*>(a.out + int64_t(row) * a.hidden + o0) =
-          make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16), uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
-    }
+    for (int i = 0; i < 4; ++i) hv[i] = f32_to_bf16_rne(GATEUP ? silu_fast(gv[i]) * uv[i] : wr * gv[i]);
+    const uint2 v = make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16), uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
+    if constexpr (TILE_EPI)
+      *reinterpret_cast<uint2*>(tile_out + rloc * PITCH + o * 2) = v;
+    else if (r0 + rloc < g.row_count)
+      *reinterpret_cast<uint2*>(ob + int64_t(rloc) * ld + o) = v;
   };
-  const int fbase = fb * feat_per_wg(GATEUP, WF) + fh * FT * 16;
+  const int fbase = fh * FT * 16;
   if constexpr (ACT_FP4) {
     // 32x32 result: value j of lane l is feature 8*(j/4) + 4*(l/32) + j%4, token l%32
     float wr[2];
@@ -395,6 +406,16 @@ __global__ __launch_bounds__(128 * WF) void k_mx_gemm(MxGemmArgs a) {
         }
         emit(th * 64 + t * 16 + n, fbase + ft * 16 + 4 * q, gv, uv, wr[t]);
       }
+  }
+  if constexpr (TILE_EPI) {
+    __syncthreads();
+    constexpr int CH = NF * 2 / 16;    // 16-byte pieces of a tile row
+    constexpr int RPP = 64 * NW / CH;  // rows per pass of the workgroup
+    static_assert((64 * NW) % CH == 0, "whole rows per pass");
+    const int nrows = min(kRowsPerTile, g.row_count - r0);
+    const int c = tid % CH;
+    for (int r = tid / CH; r < nrows; r += RPP)
+      gstore<u32x4>(ob + int64_t(r) * ld + c * 8, *reinterpret_cast<const u32x4*>(tile_out + r * PITCH + c * 16));
   }
 }
 
