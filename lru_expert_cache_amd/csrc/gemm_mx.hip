@@ -59,11 +59,12 @@ typedef short bf16x2 __attribute__((ext_vector_type(2)));
 constexpr int kActBf16 = 0, kActFp8 = 1, kActFp4 = 2;
 
 constexpr int kRowsPerTile = kMxTileRows;  // activation rows per workgroup tile
-// weight tiles of 16 features per wave and per matrix (64 accumulator columns a wave)
-constexpr int feat_tiles(bool gateup) { return gateup ? 2 : 4; }
-// output features per workgroup (per matrix) with WF wave columns of 64
+// weight tiles of 16 features per wave and per matrix: 64 accumulator columns
+// a wave, 64 FX with the feature multiplier FX (2 for bf16 activations)
+constexpr int feat_tiles(bool gateup, int fx = 1) { return (gateup ? 2 : 4) * fx; }
+// output features per workgroup (per matrix) with WF wave columns of 64 FX
 // accumulator columns each (and two wave rows of 64 rows)
-constexpr int feat_per_wg(bool gateup, int wf) { return wf * feat_tiles(gateup) * 16; }
+constexpr int feat_per_wg(bool gateup, int wf, int fx = 1) { return wf * feat_tiles(gateup, fx) * 16; }
 
 __device__ inline uint16_t f32_to_bf16_rne(float f) {
   const uint32_t u = __float_as_uint(f);
@@ -82,21 +83,22 @@ __device__ inline float silu_fast(float g) {
 // halves, bf16 the 4 K quarters of each (one 16x16x32 B operand each)
 constexpr int mx_pieces(int act) { return act == kActFp4 ? 8 : act == kActFp8 ? 16 : 32; }
 // One K step's operands in LDS, in the order the MFMAs read them.
-template <int ACT, int WF>
+template <int ACT, int WF, int FX>
 struct MxStage {
-  u32x4 a[4 * WF][64];                        // 4 WF weight tiles, A-operand lane order
+  u32x4 a[4 * WF * FX][64];                   // 4 WF FX weight tiles, A-operand lane order
   u32x4 b[8][mx_pieces(ACT) / 8 * 64];        // 16-row sub-tiles: FP4 [lane]; FP8 [half * 64 + lane];
                                               // bf16 [quarter * 64 + lane]
-  uint8_t as[4 * WF][64];                     // weight scale bytes [tile][lane]
+  uint8_t as[4 * WF * FX][64];                // weight scale bytes [tile][lane]
   uint32_t bs[ACT == kActBf16 ? 1 : kRowsPerTile];  // activation scales: row -> bytes of blocks 0..3
 };
-// ring depth: two workgroups per CU fit with WF 2 FP4 (and WF 4 FP4), one otherwise
-constexpr int mx_stages(int act, int wf) { return wf == 2 && act == kActFp4 ? 4 : 3; }
-// loads per wave and stage: 2 weight tiles, their scales, the wave's share of
-// the activation pieces (half a piece when there are more waves than pieces),
-// and its share of the activation scales (none for bf16)
-constexpr int mx_loads_per_stage(int act, int wf) {
-  return 2 + 1 + (mx_pieces(act) >= 2 * wf ? mx_pieces(act) / (2 * wf) : 1) + (act == kActBf16 ? 0 : 1);
+// ring depth: two workgroups per CU fit with WF 2 FP4 (and WF 4 FP4), one
+// otherwise; with FX 2 (bf16, 66 KB a stage) two stages
+constexpr int mx_stages(int act, int wf, int fx) { return fx == 2 ? 2 : wf == 2 && act == kActFp4 ? 4 : 3; }
+// loads per wave and stage: 2 FX weight tiles, their scales, the wave's share
+// of the activation pieces (half a piece when there are more waves than
+// pieces), and its share of the activation scales (none for bf16)
+constexpr int mx_loads_per_stage(int act, int wf, int fx) {
+  return 2 * fx + 1 + (mx_pieces(act) >= 2 * wf ? mx_pieces(act) / (2 * wf) : 1) + (act == kActBf16 ? 0 : 1);
 }
 
 // 8 FP4 codes (element 2i in the low nibble of byte i) x E8M0 scale -> 8 bf16,
@@ -125,17 +127,20 @@ __device__ __attribute__((always_inline)) inline void lds_load4(const void* src,
   __builtin_amdgcn_global_load_lds((const FT_GLOBAL void*)src, (FT_L3 void*)dst, 4, 0, 0);
 }
 
-template <bool GATEUP, int ACT, int WF>
+template <bool GATEUP, int ACT, int WF, int FX>
 __global__ __launch_bounds__(128 * WF) void k_mx_gemm(MxGemmArgs a) {
   constexpr bool ACT_FP4 = ACT == kActFp4;
   constexpr int NM = GATEUP ? 2 : 1;
-  constexpr int FT = feat_tiles(GATEUP);
+  constexpr int FT = feat_tiles(GATEUP, FX);
   constexpr int NW = 2 * WF;        // waves
   constexpr int TPM = WF * FT;      // weight tiles per matrix and workgroup
-  constexpr int S = mx_stages(ACT, WF);
-  constexpr int LPS = mx_loads_per_stage(ACT, WF);
+  constexpr int S = mx_stages(ACT, WF, FX);
+  constexpr int LPS = mx_loads_per_stage(ACT, WF, FX);
+  constexpr int TW = 2 * FX;        // weight tiles a wave loads per stage (one matrix)
+  static_assert(FX == 1 || ACT == kActBf16, "wider wave tiles with bf16 activations only");
+  static_assert(TPM % TW == 0, "a wave's weight tiles belong to one matrix");
   static_assert(ACT != kActBf16 || mx_pieces(ACT) % (4 * NW) == 0, "bf16: whole 16-row sub-tiles per wave");
-  __shared__ MxStage<ACT, WF> sm[S];
+  __shared__ MxStage<ACT, WF, FX> sm[S];
 
   // XCD-aware order: items (row tile, feature block) run row-tile-major, and
   // the item list is cut into 8 contiguous ranges, one per XCD (workgroups
@@ -144,7 +149,7 @@ __global__ __launch_bounds__(128 * WF) void k_mx_gemm(MxGemmArgs a) {
   // the next row tile of the same expert (whose weight tiles are still there).
   // Any dispatch order gives every item exactly once (the grid holds at least
   // 8 * ceil(items / 8) workgroups).
-  const int nfb = (GATEUP ? a.inter : a.hidden) / feat_per_wg(GATEUP, WF);  // feature blocks
+  const int nfb = (GATEUP ? a.inter : a.hidden) / feat_per_wg(GATEUP, WF, FX);  // feature blocks
   const int items = min(*a.n_tiles_dev, a.max_tiles) * nfb;
   const int lin = int(blockIdx.x), xcd = lin & 7, k = lin >> 3;
   const int p = int(int64_t(items) * xcd / 8) + k;
@@ -183,20 +188,24 @@ __global__ __launch_bounds__(128 * WF) void k_mx_gemm(MxGemmArgs a) {
     }
   }
 
-  // the 4 WF staged weight tiles: chunk ci = matrix (ci / TPM), tile fb*TPM + ci % TPM
+  // the 4 WF FX staged weight tiles: chunk ci = matrix (ci / TPM), tile fb*TPM + ci % TPM
   auto chunk_mat = [&](int ci) -> const MatLayout& { return a.lay.m[GATEUP ? ci / TPM : 2]; };
   auto chunk_tile = [&](int ci, int kb) -> int64_t { return int64_t(fb * TPM + ci % TPM) * nkb + kb; };
+  // scale bytes of this wave's TW tiles (one matrix), held before the K loop:
+  // indexed by the wave, the layout would be re-read from the kernel
+  // arguments at every step
+  const uint8_t* const WS = W + chunk_mat(TW * w).scales_off;
   // one K step's loads into a stage: LPS per wave, whatever the wave
-  auto issue = [&](int kb, MxStage<ACT, WF>& st) {
+  auto issue = [&](int kb, MxStage<ACT, WF, FX>& st) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int ci = 2 * w + j;
+    for (int j = 0; j < TW; ++j) {
+      const int ci = TW * w + j;
       lds_load16(W + chunk_mat(ci).codes_off + chunk_tile(ci, kb) * 1024 + lane * 16, &st.a[ci][0]);
     }
-    if (lane < 8) {
-      // both tiles of this wave belong to one matrix: its layout is uniform
-      const int ci = 2 * w + (lane >> 2), part = lane & 3;
-      lds_load16(W + chunk_mat(2 * w).scales_off + chunk_tile(ci, kb) * 64 + part * 16, &st.as[2 * w][0]);
+    if (lane < 4 * TW) {
+      // all tiles of this wave belong to one matrix: its layout is uniform
+      const int ci = TW * w + (lane >> 2), part = lane & 3;
+      lds_load16(WS + chunk_tile(ci, kb) * 64 + part * 16, &st.as[TW * w][0]);
     }
     if constexpr (ACT == kActBf16) {
       // quarter j of a sub-tile: lane 16 q + n reads its row's K 128 kb + 32 q + 8 j .. + 7
@@ -245,7 +254,7 @@ __global__ __launch_bounds__(128 * WF) void k_mx_gemm(MxGemmArgs a) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * LPS));
     __builtin_amdgcn_s_barrier();
     issue(min(kb + S - 1, nkb - 1), sm[(kb + S - 1) % S]);
-    const MxStage<ACT, WF>& st = sm[kb % S];
+    const MxStage<ACT, WF, FX>& st = sm[kb % S];
     if constexpr (ACT == kActFp4) {
       // 32x32x64 operands gathered from the 16x16x128-ordered stage: lane l
       // takes row (or token) l % 32 -- tile (l % 32) / 16, row l % 16 -- and
@@ -345,7 +354,7 @@ __global__ __launch_bounds__(128 * WF) void k_mx_gemm(MxGemmArgs a) {
   // extra barriers.)  The routing weights of the lane's rows are read once,
   // before any output is written.
   constexpr bool TILE_EPI = !GATEUP || ACT_FP4;
-  constexpr int NF = feat_per_wg(GATEUP, WF);  // output features of the workgroup
+  constexpr int NF = feat_per_wg(GATEUP, WF, FX);  // output features of the workgroup
   constexpr int PITCH = NF * 2 + 16;           // tile row pitch (bytes): row r starts 4 r banks on
   static_assert(!TILE_EPI || kRowsPerTile * PITCH <= int(sizeof(sm)), "the output tile fits in the stage ring");
   uint8_t* tile_out = reinterpret_cast<uint8_t*>(&sm[0]);
@@ -431,19 +440,23 @@ int mx_gemm_rows_per_tile() { return kRowsPerTile; }
 constexpr int mx_max_wf(int act) { return act == kActFp8 ? 8 : 4; }
 
 namespace {
-template <bool GATEUP, int ACT, int WF>
+template <bool GATEUP, int ACT, int WF, int FX = 1>
 hipError_t launch_wf(const MxGemmArgs& a, hipStream_t s, Ev ev) {
   // one workgroup per (row tile, feature block) item, at least 8 * ceil(items / 8)
-  const int nfb = (GATEUP ? a.inter : a.hidden) / feat_per_wg(GATEUP, WF);
+  const int nfb = (GATEUP ? a.inter : a.hidden) / feat_per_wg(GATEUP, WF, FX);
   const int64_t bound = int64_t(a.max_tiles) * nfb;
-  ft_launch(k_mx_gemm<GATEUP, ACT, WF>, dim3(unsigned((bound + 7) / 8 * 8)), dim3(128 * WF), s, ev, a);
+  ft_launch(k_mx_gemm<GATEUP, ACT, WF, FX>, dim3(unsigned((bound + 7) / 8 * 8)), dim3(128 * WF), s, ev, a);
   return hipGetLastError();
 }
-// the widest workgroup tile (up to mx_max_wf) whose feature block divides the outputs
+// the widest workgroup tile (up to mx_max_wf, with bf16 the 128-column wave
+// tiles first) whose feature block divides the outputs
 template <bool GATEUP, int ACT>
 hipError_t launch_gf(const MxGemmArgs& a, hipStream_t s, Ev ev) {
   const int outs = GATEUP ? a.inter : a.hidden;
   constexpr int wf = mx_max_wf(ACT);
+  if constexpr (ACT == kActBf16) {
+    if (outs % feat_per_wg(GATEUP, 4, 2) == 0) return launch_wf<GATEUP, ACT, 4, 2>(a, s, ev);
+  }
   if constexpr (wf >= 8) {
     if (outs % feat_per_wg(GATEUP, 8) == 0) return launch_wf<GATEUP, ACT, 8>(a, s, ev);
   }

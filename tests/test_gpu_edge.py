@@ -162,7 +162,7 @@ def _act_case(shared, act_mode, H=256, T=300, cfg_id=120):
     w = _small(cfg_id + int(shared), 3, H, 256, 8, 2, [MX, MX, MX], 16, shared=shared)
     g = GpuLayerStack(w)
     o = OracleLayerStack(w, pool_slots=g.C, act_mode=act_mode)
-    flag = ft.FT_ACT_MXFP4 if act_mode == OFFN.ACT_MXFP4 else ft.FT_ACT_MXFP8
+    flag = {OFFN.ACT_MXFP4: ft.FT_ACT_MXFP4, OFFN.ACT_MXFP8: ft.FT_ACT_MXFP8, OFFN.ACT_BF16: ft.FT_ACT_BF16}[act_mode]
     rels = []
     try:
         for l in range(3):
@@ -205,6 +205,18 @@ def test_prefill_mx_narrow_workgroup_tiles(act):
     rels = _act_case(True, mode, H=384, T=600, cfg_id=124)
     print(act, "rel-L2", rels)
     assert max(rels) <= (2e-3 if act == "mxfp8" else 6e-3)
+
+
+def test_prefill_bf16_wide_wave_tiles():
+    # hidden 512, intermediate 256: with bf16 activations both GEMMs take the
+    # 64-row x 128-column wave tiles (feature blocks of 256 and 512), two
+    # workgroup stages; 600 tokens give two row tiles per expert with a ragged
+    # tail
+    from oracle import ffn as OFFN
+
+    rels = _act_case(True, OFFN.ACT_BF16, H=512, T=600, cfg_id=126)
+    print("bf16 rel-L2", rels)
+    assert max(rels) <= 2e-3
 
 
 def test_device_driven_and_host_driven_decode_agree():
