@@ -87,8 +87,10 @@ def measured_traffic():
         return None
 
 
-def cpu_baseline(w, batch, ncalls):
-    """The oracle as it stands, on the first `ncalls` (step 0, layer l) calls."""
+def cpu_baseline(w, batch, ncalls, one_thread_calls=2):
+    """The oracle as it stands, on the first `ncalls` (step 0, layer l) calls,
+    with every host thread; then on `one_thread_calls` of them with one BLAS
+    thread (returned separately)."""
     import moe_synth as ms
     from oracle.layer import OracleLayerStack
 
@@ -107,10 +109,28 @@ def cpu_baseline(w, batch, ncalls):
     for l in range(ncalls):
         st.forward(l, xs[l], bs[l], outputs=True)
     sec = (time.perf_counter() - t0) / ncalls
-    return {"value": batch / (sec * w.num_layers), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    full = {"value": batch / (sec * w.num_layers), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{ncalls} layer calls (step 0, layers 0..{ncalls - 1}) at batch {batch}, routing + LRU + "
                       f"fp64 expert FFN + combine; {sec:.2f} s per layer call, scaled to the {w.num_layers}-layer "
                       f"stack"}
+    one = None
+    n1 = min(one_thread_calls, ncalls)
+    if n1 > 0:
+        try:
+            from threadpoolctl import threadpool_limits
+        except ImportError:
+            threadpool_limits = None
+        if threadpool_limits is not None:
+            st1 = OracleLayerStack(w)
+            with threadpool_limits(limits=1):
+                t0 = time.perf_counter()
+                for l in range(n1):
+                    st1.forward(l, xs[l], bs[l], outputs=True)
+                sec1 = (time.perf_counter() - t0) / n1
+            one = {"value": batch / (sec1 * w.num_layers), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                   "sample": f"{n1} layer calls (step 0, layers 0..{n1 - 1}) at batch {batch} with one BLAS "
+                             f"thread; {sec1:.2f} s per layer call"}
+    return full, one
 
 
 def measure_prefill(ft, torch, ms, pool, dev):
@@ -244,7 +264,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 16; 2 for the other workloads)")
     ap.add_argument("--batch", type=int, default=None, help="tokens per call (default: the workload's largest)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-calls", type=int, default=6)
+    ap.add_argument("--cpu-calls", type=int, default=24)
     ap.add_argument("--no-extras", action="store_true", help="skip the batch 1/4 and link measurements")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
@@ -407,7 +427,9 @@ def main():
     cpu = None
     if not args.no_cpu_baseline and headline:
         t = time.perf_counter()
-        cpu = cpu_baseline(w, B, args.cpu_calls)
+        cpu, cpu1 = cpu_baseline(w, B, args.cpu_calls)
+        if cpu1 is not None:
+            extras["cpu_baseline_one_thread"] = cpu1
         log(f"[bench] cpu baseline {time.perf_counter() - t:.1f} s")
 
     value = B * args.steps / elapsed
