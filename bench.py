@@ -416,6 +416,17 @@ def main():
     if prefill_pool is not None:
         extras["prefill"] = measure_prefill(ft, torch, ms, prefill_pool, dev)
         ft.ft_moe_destroy_pool(prefill_pool)
+        # measured matrix-core rates (register-only MFMA loops), beside the data-sheet peaks
+        rates = {name: ft.ft_moe_mfma_rate(kind) / 1e12
+                 for name, kind in (("fp4_32x32x64", ft.FT_MFMA_FP4_32X32X64),
+                                    ("fp8_16x16x128", ft.FT_MFMA_FP8_16X16X128),
+                                    ("bf16_16x16x32", ft.FT_MFMA_BF16_16X16X32))}
+        extras["mfma_measured_TFLOPs"] = rates
+        log(f"[bench] measured MFMA rates (TFLOP/s): {rates}")
+        for mode, key in (("bf16", "bf16_16x16x32"), ("mxfp8", "fp8_16x16x128"), ("mxfp4", "fp4_32x32x64")):
+            r = extras["prefill"].get(mode)
+            if r and r.get("ffn_TFLOPs"):
+                r["ffn_frac_of_measured_mfma"] = r["ffn_TFLOPs"] / rates[key]
     if args.calibrate_copy:
         a = torch.empty(128 << 20, dtype=torch.int16, device=dev).fill_(1)
         b = torch.empty_like(a)

@@ -36,7 +36,7 @@ EXPORTED = ["ft_moe_init_pool", "ft_moe_layer_forward", "ft_moe_pool_stats", "ft
             "ft_moe_pool_table", "ft_moe_set_hybrid_share", "ft_moe_host_expert_rate",
             "ft_moe_set_profiling", "ft_moe_profile_read", "ft_moe_destroy_pool", "ft_moe_last_error",
             "ft_moe_reserve", "ft_moe_resize_pool", "ft_moe_decide_mode", "ft_moe_measure_mode",
-            "ft_moe_ffn_kernel_name"]
+            "ft_moe_ffn_kernel_name", "ft_moe_mfma_rate"]
 
 FT_MODE_OFFLOAD, FT_MODE_HYBRID, FT_MODE_FUSED = 0, 1, 2
 
@@ -136,6 +136,8 @@ def lib() -> ctypes.CDLL:
     L.ft_moe_host_expert_rate.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                           ctypes.POINTER(ctypes.c_double)]
     L.ft_moe_host_expert_rate.restype = ctypes.c_int
+    L.ft_moe_mfma_rate.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double)]
+    L.ft_moe_mfma_rate.restype = ctypes.c_int
     L.ft_moe_set_profiling.argtypes = [P, ctypes.c_int32]
     L.ft_moe_set_profiling.restype = ctypes.c_int
     L.ft_moe_profile_read.argtypes = [P, ctypes.POINTER(ft_moe_profile), ctypes.c_int32]
@@ -286,6 +288,16 @@ def ft_moe_set_hybrid_share(pool, share: float):
 def ft_moe_host_expert_rate(pool, layer: int, tokens: int, iters: int = 1) -> float:
     r = ctypes.c_double()
     _check(lib().ft_moe_host_expert_rate(pool, int(layer), int(tokens), int(iters), ctypes.byref(r)))
+    return r.value
+
+
+FT_MFMA_FP4_32X32X64, FT_MFMA_FP8_16X16X128, FT_MFMA_BF16_16X16X32 = 0, 1, 2
+
+
+def ft_moe_mfma_rate(kind: int, iters: int = 2000, stream: int = 0) -> float:
+    """Measured dense flops per second of one matrix-core instruction kind."""
+    r = ctypes.c_double(0.0)
+    _check(lib().ft_moe_mfma_rate(int(kind), int(iters), ctypes.c_void_p(stream or None), ctypes.byref(r)))
     return r.value
 
 

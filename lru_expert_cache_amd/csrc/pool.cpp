@@ -1363,6 +1363,41 @@ int ft_moe_host_expert_rate(ft_moe_pool* p, int32_t layer, int32_t tokens, int32
   return FT_OK;
 }
 
+int ft_moe_mfma_rate(int32_t kind, int32_t iters, void* hip_stream, double* flops_per_s) {
+  if (kind < 0 || kind > 2 || iters < 1 || iters > (1 << 20) || !flops_per_s) {
+    set_error("bad arguments");
+    return FT_E_INVALID;
+  }
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  float* out = nullptr;
+  if (hipMalloc(&out, mfma_peak_out_bytes()) != hipSuccess) {
+    (void)hipGetLastError();
+    set_error("device allocation of %zu bytes failed", mfma_peak_out_bytes());
+    return FT_E_OOM_DEVICE;
+  }
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  int rc = FT_OK;
+  float ms = 0.f;
+  auto run = [&]() -> int {
+    FT_HIP_CHECK(hipEventCreate(&e0));
+    FT_HIP_CHECK(hipEventCreate(&e1));
+    FT_HIP_CHECK(launch_mfma_peak(kind, iters, 0, out, s));  // warm-up (clocks, code load)
+    FT_HIP_CHECK(hipEventRecord(e0, s));
+    FT_HIP_CHECK(launch_mfma_peak(kind, iters, 1, out, s));
+    FT_HIP_CHECK(hipEventRecord(e1, s));
+    FT_HIP_CHECK(hipEventSynchronize(e1));
+    FT_HIP_CHECK(hipEventElapsedTime(&ms, e0, e1));
+    return FT_OK;
+  };
+  rc = run();
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  (void)hipFree(out);
+  if (rc != FT_OK) return rc;
+  *flops_per_s = mfma_peak_flops(kind, iters) / (double(std::max(ms, 1e-6f)) * 1e-3);
+  return FT_OK;
+}
+
 int ft_moe_decide_mode(ft_moe_mode_report* r) {
   if (!r) {
     set_error("NULL report");

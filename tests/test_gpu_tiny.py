@@ -61,3 +61,14 @@ def test_tiny_64_calls_of_one_token():
         assert st["slots_used"] == 8 and st["slots_total"] == 8
     finally:
         g.close()
+
+
+@pytest.mark.parametrize("kind,sheet_tflops", [(0, 10100.0), (1, 5000.0), (2, 2500.0)])
+def test_mfma_rate_is_below_the_data_sheet_peak(kind, sheet_tflops):
+    # register-only MFMA loops: a positive rate that no instruction mix can push
+    # past the data-sheet dense peak of its operand type
+    import lru_expert_cache_amd as ft
+
+    tf = ft.ft_moe_mfma_rate(kind, iters=500) / 1e12
+    print("kind", kind, "TFLOP/s", tf)
+    assert 0.05 * sheet_tflops < tf <= 1.02 * sheet_tflops
