@@ -420,7 +420,8 @@ def main():
         rates = {name: ft.ft_moe_mfma_rate(kind) / 1e12
                  for name, kind in (("fp4_32x32x64", ft.FT_MFMA_FP4_32X32X64),
                                     ("fp8_16x16x128", ft.FT_MFMA_FP8_16X16X128),
-                                    ("bf16_16x16x32", ft.FT_MFMA_BF16_16X16X32))}
+                                    ("bf16_16x16x32", ft.FT_MFMA_BF16_16X16X32),
+                                    ("bf16_32x32x16", ft.FT_MFMA_BF16_32X32X16))}
         extras["mfma_measured_TFLOPs"] = rates
         log(f"[bench] measured MFMA rates (TFLOP/s): {rates}")
         for mode, key in (("bf16", "bf16_16x16x32"), ("mxfp8", "fp8_16x16x128"), ("mxfp4", "fp4_32x32x64")):

@@ -272,9 +272,10 @@ int ft_moe_host_expert_rate(ft_moe_pool *p, int32_t layer, int32_t tokens, int32
 /* Measured issue rate of the matrix-core instructions the prefill GEMM uses,
  * reported beside the data-sheet peaks.  kind 0: v_mfma_scale_f32_32x32x64_f8f6f4
  * with FP4 operands; 1: v_mfma_scale_f32_16x16x128_f8f6f4 with FP8 operands;
- * 2: v_mfma_f32_16x16x32_bf16.  Runs 1024 workgroups of 4 waves, each wave
- * issuing `iters` rounds of independent MFMAs on register operands, once to
- * warm up and once timed with HIP events on `hip_stream` (a hipStream_t; null
+ * 2: v_mfma_f32_16x16x32_bf16; 3: v_mfma_f32_32x32x16_bf16.  Runs 1024
+ * workgroups of 4 waves, each wave issuing `iters` rounds of independent
+ * MFMAs on register operands, once to warm up and once timed with HIP
+ * events on `hip_stream` (a hipStream_t; null
  * = the null stream), and returns dense flops per second in *flops_per_s
  * (2 per multiply-add).  Allocates and frees a 1 MiB device buffer; blocks
  * until the timed run ends.  1 <= iters <= 2^20, else FT_E_INVALID. */

@@ -295,7 +295,8 @@ int mx_gemm_rows_per_tile();
 hipError_t launch_mx_gemm(const MxGemmArgs& a, bool gateup, int act, hipStream_t s, Ev ev = {});
 
 // mfma_peak.hip: register-only MFMA loops (kind 0: scaled 32x32x64 FP4, 1:
-// scaled 16x16x128 FP8, 2: 16x16x32 bf16); out holds mfma_peak_out_bytes()
+// scaled 16x16x128 FP8, 2: 16x16x32 bf16, 3: 32x32x16 bf16); out holds
+// mfma_peak_out_bytes()
 double mfma_peak_flops(int kind, int iters);
 hipError_t launch_mfma_peak(int kind, int iters, int seed, float* out, hipStream_t s);
 size_t mfma_peak_out_bytes();

@@ -17,8 +17,9 @@ typedef short bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kPeakBlocks = 1024, kPeakThreads = 256;
 
-// KIND 0: scaled 32x32x64, FP4 x FP4 (4 accumulators of 16 values);
-// KIND 1: scaled 16x16x128, FP8 x FP8; KIND 2: 16x16x32 bf16 (8 of 4 each).
+// KIND 0: scaled 32x32x64, FP4 x FP4; KIND 3: 32x32x16 bf16 (4 accumulators
+// of 16 values each); KIND 1: scaled 16x16x128, FP8 x FP8; KIND 2: 16x16x32
+// bf16 (8 of 4 each).
 // Operands depend on the lane and the seed, so nothing folds; the sums are
 // written out so that nothing is dead.
 template <int KIND>
@@ -27,7 +28,8 @@ __global__ __launch_bounds__(kPeakThreads) void k_mfma_peak(float* out, int iter
   const intx8 A = {v, v + 1, v + 2, v + 3, v + 4, v + 5, v + 6, v + 7};
   const intx8 B = {v * 3, v * 5, v * 7, v * 9, v, v, v, v};
   float s = 0.f;
-  if constexpr (KIND == 0) {
+  if constexpr (KIND == 0 || KIND == 3) {
+    const bf16x8 a16 = {short(v), 1, 2, 3, 4, 5, 6, 7}, b16 = {short(v), 7, 6, 5, 4, 3, 2, 1};
     floatx16 acc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -35,8 +37,12 @@ __global__ __launch_bounds__(kPeakThreads) void k_mfma_peak(float* out, int iter
       for (int j = 0; j < 16; ++j) acc[i][j] = 0.f;
     for (int it = 0; it < iters; ++it)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc[i], 4, 4, 0, 127, 0, 127);
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (KIND == 0)
+          acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc[i], 4, 4, 0, 127, 0, 127);
+        else
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a16, b16, acc[i], 0, 0, 0);
+      }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -66,6 +72,7 @@ __global__ __launch_bounds__(kPeakThreads) void k_mfma_peak(float* out, int iter
 double mfma_peak_flops(int kind, int iters) {
   const double waves = double(kPeakBlocks) * (kPeakThreads / 64);
   if (kind == 0) return waves * iters * 4 * (32.0 * 32 * 64 * 2);
+  if (kind == 3) return waves * iters * 4 * (32.0 * 32 * 16 * 2);
   if (kind == 1) return waves * iters * 8 * (16.0 * 16 * 128 * 2);
   return waves * iters * 8 * (16.0 * 16 * 32 * 2);
 }
@@ -76,6 +83,7 @@ hipError_t launch_mfma_peak(int kind, int iters, int seed, float* out, hipStream
     case 0: hipLaunchKernelGGL(k_mfma_peak<0>, g, b, 0, s, out, iters, seed); break;
     case 1: hipLaunchKernelGGL(k_mfma_peak<1>, g, b, 0, s, out, iters, seed); break;
     case 2: hipLaunchKernelGGL(k_mfma_peak<2>, g, b, 0, s, out, iters, seed); break;
+    case 3: hipLaunchKernelGGL(k_mfma_peak<3>, g, b, 0, s, out, iters, seed); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -1364,7 +1364,7 @@ int ft_moe_host_expert_rate(ft_moe_pool* p, int32_t layer, int32_t tokens, int32
 }
 
 int ft_moe_mfma_rate(int32_t kind, int32_t iters, void* hip_stream, double* flops_per_s) {
-  if (kind < 0 || kind > 2 || iters < 1 || iters > (1 << 20) || !flops_per_s) {
+  if (kind < 0 || kind > 3 || iters < 1 || iters > (1 << 20) || !flops_per_s) {
     set_error("bad arguments");
     return FT_E_INVALID;
   }

@@ -78,7 +78,7 @@ def test_null_arguments_rejected():
 def test_mfma_rate_rejects_bad_arguments_before_gpu():
     L = ft.lib()
     r = ctypes.c_double(0.0)
-    assert L.ft_moe_mfma_rate(3, 10, None, ctypes.byref(r)) == ft.FT_E_INVALID
+    assert L.ft_moe_mfma_rate(4, 10, None, ctypes.byref(r)) == ft.FT_E_INVALID
     assert L.ft_moe_mfma_rate(-1, 10, None, ctypes.byref(r)) == ft.FT_E_INVALID
     assert L.ft_moe_mfma_rate(0, 0, None, ctypes.byref(r)) == ft.FT_E_INVALID
     assert L.ft_moe_mfma_rate(0, 10, None, None) == ft.FT_E_INVALID
