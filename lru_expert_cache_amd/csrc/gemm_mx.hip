@@ -12,11 +12,9 @@
 //       K 64+16q..64+16q+15 in dwords 4-7 (measured on gfx950 with an
 //       in-bounds probe of the instruction).  FP4 x FP4 runs the 32x32x64 form
 //       (operands regathered from the same stage), FP8 the 16x16x128 one.
-//   bf16 activations run v_mfma_f32_32x32x16_bf16 (measured 1.4x the rate of
-//       the 16x16x32 form): dword j of a weight lane becomes 8 bf16 of the A
-//       operand after one scaled convert (exact), and the B operand is the
-//       same 8 K of the token's row, 16 bytes; operands of 32 rows are
-//       regathered from the 16-row tiles as in the FP4 x FP4 case.
+//   bf16 activations run v_mfma_f32_16x16x32_bf16 four times per step: dword
+//       j of a weight lane becomes the A operand after one scaled convert
+//       (exact), and the B operand is K 32q+8j..+7 of row n, 16 bytes.
 //
 // Work: a list of (group, 128-row tile) built by the resolve kernel, times the
 // blocks of output features; one workgroup per item, in an XCD-aware order.
@@ -41,7 +39,7 @@
 // epilogue.  Activation rows past the group's end (zeros, stale codes or the
 // group's first row) feed output columns that are not written.  Epilogues as
 // the decode FFN: gate/up -> h = bf16(silu(g) * u); down -> p = bf16(w * y);
-// the down output and the 32x32-layout gate/up one are put together as a 128-row tile
+// the down output and the FP4 gate/up one are put together as a 128-row tile
 // in the freed stage ring and written as whole 128-byte lines of their rows.
 #include "common.h"
 #include "gmem.h"
@@ -233,13 +231,11 @@ __global__ __launch_bounds__(128 * WF) void k_mx_gemm(MxGemmArgs a) {
     }
   };
 
-  // FP8 activations: 16x16x128 MFMAs, acc[matrix][16-feature tile][16-row tile];
+  // FP8 activations: 16x16x128 MFMAs, bf16: 16x16x32 MFMAs, acc[matrix][16-feature tile][16-row tile];
   // FP4 x FP4: 32x32x64 MFMAs (measured 1.6x the 16x16x128 FP4 rate on gfx950),
-  // bf16: 32x32x16 MFMAs (measured 1.4x the 16x16x32 rate),
   // acc32[matrix][32-feature block][32-row block]
-  constexpr bool USE32 = ACT != kActFp8;  // 32x32 output layout
-  constexpr int NA = USE32 ? 1 : NM * FT * 4;
-  constexpr int NB32 = USE32 ? NM * (FT / 2) * 2 : 1;
+  constexpr int NA = ACT_FP4 ? 1 : NM * FT * 4;
+  constexpr int NB32 = ACT_FP4 ? NM * (FT / 2) * 2 : 1;
   floatx4 acc[NA];
   floatx16 acc32[NB32];
 #pragma unroll
@@ -318,37 +314,31 @@ __global__ __launch_bounds__(128 * WF) void k_mx_gemm(MxGemmArgs a) {
           }
         }
     } else {
-      // bf16 activations: 32x32x16 MFMAs, operands regathered as in the FP4
-      // case (lane l: row or token l % 32 -- tile (l % 32) / 16, row l % 16).
-      // Per half step h and dword j, lane l covers K 64 h + 32 (l / 32) + 8 j
-      // .. + 7: A = dword j of weight-tile lane 16 qq + l % 16 as bf16 with its
-      // scale, B = quarter j of the token's row sub-tile at the same K.
-      const int r16 = lane & 15, hi16 = (lane >> 4) & 1, kq = lane >> 5;
+      // bf16 activations: 16x16x32 MFMAs.  A = dword j of a weight tile's lane
+      // (row r, K 32 q + 8 j .. + 7 for lane 16 q + r) as bf16 with its scale;
+      // B = quarter j of a row sub-tile (the same K, token n).  (The 32x32x16
+      // form issues 1.4x as fast in a register-only loop, but this kernel ran
+      // 3-5% slower with it on N(0,1) activations.)
+      u32x4 c[NM * FT];
+      float sa[NM * FT];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int qq = 2 * h + kq;
-        u32x4 c[NM * (FT / 2)];
-        float sa[NM * (FT / 2)];
+      for (int mi = 0; mi < NM; ++mi)
 #pragma unroll
-        for (int mi = 0; mi < NM; ++mi)
+        for (int ft = 0; ft < FT; ++ft) {
+          const int ci = mi * TPM + fh * FT + ft;
+          c[mi * FT + ft] = st.a[ci][lane];
+          sa[mi * FT + ft] = __uint_as_float(uint32_t(st.as[ci][lane]) << 23);  // E8M0: the exponent is used
+        }
 #pragma unroll
-          for (int f2 = 0; f2 < FT / 2; ++f2) {
-            const int ci = mi * TPM + fh * FT + 2 * f2 + hi16;
-            c[mi * (FT / 2) + f2] = st.a[ci][16 * qq + r16];
-            sa[mi * (FT / 2) + f2] = __uint_as_float(uint32_t(st.as[ci][16 * qq + r16]) << 23);  // E8M0 exponent
-          }
+      for (int j = 0; j < 4; ++j) {
+        bf16x8 B[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          bf16x8 B[2];
+        for (int t = 0; t < 4; ++t) B[t] = as_bf16x8(st.b[th * 4 + t][j * 64 + lane]);
 #pragma unroll
-          for (int rb = 0; rb < 2; ++rb) B[rb] = as_bf16x8(st.b[th * 4 + rb * 2 + hi16][j * 64 + 16 * qq + r16]);
+        for (int i = 0; i < NM * FT; ++i) {
+          const bf16x8 A = fp4x8_to_bf16(c[i][j], sa[i]);
 #pragma unroll
-          for (int i = 0; i < NM * (FT / 2); ++i) {
-            const bf16x8 A = fp4x8_to_bf16(c[i][j], sa[i]);
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-              acc32[i * 2 + rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B[rb], acc32[i * 2 + rb], 0, 0, 0);
-          }
+          for (int t = 0; t < 4; ++t) acc[i * 4 + t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B[t], acc[i * 4 + t], 0, 0, 0);
         }
       }
     }
@@ -359,13 +349,13 @@ __global__ __launch_bounds__(128 * WF) void k_mx_gemm(MxGemmArgs a) {
   // epilogue: a lane holds 4 consecutive features of one row (gate/up ->
   // h = bf16(silu(g) * u), down -> p = bf16(w * y)).  Stored from there, a
   // store writes 16 (32x32 layout) or 32 bytes (16x16) in each of 32 or 16
-  // rows.  The down output (a 4096-byte row of p) and the 32x32 gate/up one go
+  // rows.  The down output (a 4096-byte row of p) and the FP4 gate/up one go
   // through LDS instead: the workgroup's 128-row output tile is put together
   // in the free stage ring and leaves in 16-byte pieces, 8 lanes per 128-byte
-  // line of a row.  (The 16x16 (FP8) gate/up stores measured no slower than the
+  // line of a row.  (The 16x16 gate/up stores measured no slower than the
   // extra barriers.)  The routing weights of the lane's rows are read once,
   // before any output is written.
-  constexpr bool TILE_EPI = !GATEUP || USE32;
+  constexpr bool TILE_EPI = !GATEUP || ACT_FP4;
   constexpr int NF = feat_per_wg(GATEUP, WF, FX);  // output features of the workgroup
   constexpr int PITCH = NF * 2 + 16;           // tile row pitch (bytes): row r starts 4 r banks on
   static_assert(!TILE_EPI || kRowsPerTile * PITCH <= int(sizeof(sm)), "the output tile fits in the stage ring");
@@ -391,7 +381,7 @@ __global__ __launch_bounds__(128 * WF) void k_mx_gemm(MxGemmArgs a) {
       *reinterpret_cast<uint2*>(ob + int64_t(rloc) * ld + o) = v;
   };
   const int fbase = fh * FT * 16;
-  if constexpr (USE32) {
+  if constexpr (ACT_FP4) {
     // 32x32 result: value j of lane l is feature 8*(j/4) + 4*(l/32) + j%4, token l%32
     float wr[2];
 #pragma unroll
