@@ -91,9 +91,16 @@ struct MxStage {
   uint8_t as[4 * WF * FX][64];                // weight scale bytes [tile][lane]
   uint32_t bs[ACT == kActBf16 ? 1 : kRowsPerTile];  // activation scales: row -> bytes of blocks 0..3
 };
-// ring depth: two workgroups per CU fit with WF 2 FP4 (and WF 4 FP4), one
-// otherwise; with FX 2 (bf16, 66 KB a stage) two stages
-constexpr int mx_stages(int act, int wf, int fx) { return fx == 2 ? 2 : wf == 2 && act == kActFp4 ? 4 : 3; }
+// ring depth: 4 with WF 2 FP4, 3 with WF 4 FP4 (two workgroups per CU either
+// way); 2 with FP8 at WF 4 (34 KB stages: two workgroups per CU, measured
+// 6-8% faster than one 16-wave workgroup with 3 stages) and with FX 2 (bf16,
+// 66 KB stages); 3 otherwise
+constexpr int mx_stages(int act, int wf, int fx) {
+  return fx == 2 || (act == kActFp8 && wf == 4) ? 2 : wf == 2 && act == kActFp4 ? 4 : 3;
+}
+// waves per SIMD the register allocation must allow: 4 for the two 8-wave
+// FP8 workgroups per CU (at most 128 registers a wave)
+constexpr int mx_min_waves(int act, int wf) { return act == kActFp8 && wf == 4 ? 4 : 1; }
 // loads per wave and stage: 2 FX weight tiles, their scales, the wave's share
 // of the activation pieces (half a piece when there are more waves than
 // pieces), and its share of the activation scales (none for bf16)
@@ -128,7 +135,7 @@ __device__ __attribute__((always_inline)) inline void lds_load4(const void* src,
 }
 
 template <bool GATEUP, int ACT, int WF, int FX>
-__global__ __launch_bounds__(128 * WF) void k_mx_gemm(MxGemmArgs a) {
+__global__ __launch_bounds__(128 * WF, mx_min_waves(ACT, WF)) void k_mx_gemm(MxGemmArgs a) {
   constexpr bool ACT_FP4 = ACT == kActFp4;
   constexpr int NM = GATEUP ? 2 : 1;
   constexpr int FT = feat_tiles(GATEUP, FX);
@@ -439,7 +446,7 @@ int mx_gemm_rows_per_tile() { return kRowsPerTile; }
 // with 2 and 112 us with 8; FP8 activations 8 -> 125 us against 144 us with 4,
 // whose 103 KB of LDS leave one 8-wave workgroup per CU; bf16 activations 4,
 // whose 32 KB of activations per stage rule out 8).
-constexpr int mx_max_wf(int act) { return act == kActFp8 ? 8 : 4; }
+constexpr int mx_max_wf(int) { return 4; }
 
 namespace {
 template <bool GATEUP, int ACT, int WF, int FX = 1>
