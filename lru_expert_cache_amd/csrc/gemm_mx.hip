@@ -469,7 +469,7 @@ hipError_t launch_gf(const MxGemmArgs& a, hipStream_t s, Ev ev) {
   if constexpr (wf >= 8) {
     if (outs % feat_per_wg(GATEUP, 8) == 0) return launch_wf<GATEUP, ACT, 8>(a, s, ev);
   }
-  if (outs % feat_per_wg(GATEUP, 4) == 0) return launch_wf<GATEUP, ACT, 4>(a, s, ev);
+  if (wf >= 4 && outs % feat_per_wg(GATEUP, 4) == 0) return launch_wf<GATEUP, ACT, 4>(a, s, ev);
   if (outs % feat_per_wg(GATEUP, 2) == 0) return launch_wf<GATEUP, ACT, 2>(a, s, ev);
   return hipErrorInvalidValue;
 }
