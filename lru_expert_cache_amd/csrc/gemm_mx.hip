@@ -18,9 +18,10 @@
 //
 // Work: a list of (group, 128-row tile) built by the resolve kernel, times the
 // blocks of output features; one workgroup per item, in an XCD-aware order.
-// A workgroup of 2 WF waves computes 128 rows x 64 WF accumulator columns:
-// each wave owns 64 rows x 64 columns (gate/up: 32 features of each matrix),
-// and 4 WF weight tiles are staged per step.
+// A workgroup of 2 WF waves computes 128 rows x 64 WF FX accumulator columns:
+// each wave owns 64 rows x 64 FX columns (gate/up: 32 FX features of each
+// matrix; FX = 2 with bf16 activations, else 1), and 4 WF FX weight tiles are
+// staged per step.
 //
 // K steps stream through a ring of LDS stages filled by global-to-LDS loads
 // (global_load_lds_dwordx4: lane i of a wave writes 16 bytes at the stage
