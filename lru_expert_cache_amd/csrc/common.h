@@ -287,6 +287,12 @@ struct MxGemmArgs {
   const int32_t* row_tok;     // bf16 gate/up: token of each row; null for down
   const float* row_w;         // down: routing weight of each row
   uint16_t* out;              // gate/up: h [rows][I]; down: p [rows][H]
+  // MX gate/up: when set, h is written quantised, straight into the down
+  // GEMM's activation tiles (row i of the grouped order at tile slot
+  // row_slot[i]; these tiles must not alias act_codes), and out is not written
+  uint8_t* h_codes;
+  uint8_t* h_scales;
+  const int32_t* row_slot;
   int32_t hidden, inter;
   ExpertLayout lay;
 };

@@ -40,10 +40,13 @@
 // epilogue.  Activation rows past the group's end (zeros, stale codes or the
 // group's first row) feed output columns that are not written.  Epilogues as
 // the decode FFN: gate/up -> h = bf16(silu(g) * u); down -> p = bf16(w * y);
-// the down output and the FP4 gate/up one are put together as a 128-row tile
-// in the freed stage ring and written as whole 128-byte lines of their rows.
+// the down output and the MX gate/up one are put together as a 128-row tile
+// in the freed stage ring and written as whole 128-byte lines of their rows;
+// with h tiles given, the MX gate/up output is quantised from that tile into
+// the down GEMM's activation tiles instead (no bf16 h).
 #include "common.h"
 #include "gmem.h"
+#include "mxq.h"
 
 namespace ftmoe {
 
@@ -363,7 +366,9 @@ __global__ __launch_bounds__(128 * WF, mx_min_waves(ACT, WF)) void k_mx_gemm(MxG
   // line of a row.  (The 16x16 gate/up stores measured no slower than the
   // extra barriers.)  The routing weights of the lane's rows are read once,
   // before any output is written.
-  constexpr bool TILE_EPI = !GATEUP || ACT_FP4;
+  // (the MX gate/up output always goes through the tile: h may be quantised
+  // from there, 32-element blocks along the row)
+  constexpr bool TILE_EPI = !GATEUP || ACT != kActBf16;
   constexpr int NF = feat_per_wg(GATEUP, WF, FX);  // output features of the workgroup
   constexpr int PITCH = NF * 2 + 16;           // tile row pitch (bytes): row r starts 4 r banks on
   static_assert(!TILE_EPI || kRowsPerTile * PITCH <= int(sizeof(sm)), "the output tile fits in the stage ring");
@@ -428,10 +433,38 @@ __global__ __launch_bounds__(128 * WF, mx_min_waves(ACT, WF)) void k_mx_gemm(MxG
   }
   if constexpr (TILE_EPI) {
     __syncthreads();
+    const int nrows = min(kRowsPerTile, g.row_count - r0);
+    if constexpr (GATEUP && ACT != kActBf16) {
+      if (a.h_codes) {
+        // h quantised into the down GEMM's activation tiles: one thread per
+        // (row, 32-element block) of the tile (128 rows x NF / 32 blocks =
+        // the workgroup's threads), at the row's slot and the block's place in
+        // the down GEMM's K steps
+        constexpr bool QFP4 = ACT == kActFp4;
+        constexpr int NB = NF / 32;
+        static_assert(kRowsPerTile * NB == 64 * NW, "one block per thread");
+        const int r = tid / NB, b = tid - (tid / NB) * NB;
+        if (r < nrows) {
+          uint32_t w[16];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(tile_out + r * PITCH + b * 64 + i * 16);
+            w[4 * i] = v[0]; w[4 * i + 1] = v[1]; w[4 * i + 2] = v[2]; w[4 * i + 3] = v[3];
+          }
+          uint32_t q[QFP4 ? 4 : 8];
+          const uint8_t sb = mxq::quant_block<QFP4>(w, q);
+          const int slot = a.row_slot[g.row_begin + r0 + r];
+          const int f0 = fb * NF + 32 * b;  // first feature of the block
+          const int tl = slot / kMxTileRows;
+          mxq::store_tile_block<QFP4>(a.h_codes, a.h_scales, int64_t(tl) * (a.inter / kTileK) + f0 / kTileK,
+                                      slot - tl * kMxTileRows, (f0 % kTileK) / 32, q, sb);
+        }
+        return;
+      }
+    }
     constexpr int CH = NF * 2 / 16;    // 16-byte pieces of a tile row
     constexpr int RPP = 64 * NW / CH;  // rows per pass of the workgroup
     static_assert((64 * NW) % CH == 0, "whole rows per pass");
-    const int nrows = min(kRowsPerTile, g.row_count - r0);
     const int c = tid % CH;
     for (int r = tid / CH; r < nrows; r += RPP)
       gstore<u32x4>(ob + int64_t(r) * ld + c * 8, *reinterpret_cast<const u32x4*>(tile_out + r * PITCH + c * 16));

@@ -13,56 +13,13 @@
 // copies row-major rows into the tiles (the gate/up input, by token).
 #include "common.h"
 #include "gmem.h"
+#include "mxq.h"
 
 namespace ftmoe {
 
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ inline float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
-
-// floor(log2(a)) for a > 0 (normal or subnormal fp32)
-__device__ inline int ilog2f(float a) {
-  int e;
-  (void)frexpf(a, &e);
-  return e - 1;
-}
-
-typedef short short2v __attribute__((ext_vector_type(2)));
-
-// Element codes from gfx950's scaled down-converts: v_cvt_scalef32_pk_fp4_f32
-// and _pk_fp8_f32 compute v / X with round-to-nearest-even on the element grid
-// (X a power of two, read from the exponent of the scale operand).  Measured
-// against a plain software rounding for every finite bf16 input at X = 2^-127
-// .. 2^127: identical codes once (a) FP8 inputs are clamped to +-448 X (the
-// convert turns values past 448 into the NaN code, where the MX rule
-// saturates; FP4 saturates at 6 by itself) and (b) a negative value that
-// rounds to zero is given code +0 rather than -0 (the same number).
-// 8 E2M1 codes (element 2i in the low nibble of byte i) with -0 made +0
-__device__ inline uint32_t fp4x8(const float* v, float X) {
-  uint32_t o = 0;
-  o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, v[0], v[1], X, 0);
-  o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, v[2], v[3], X, 1);
-  o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, v[4], v[5], X, 2);
-  o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, v[6], v[7], X, 3);
-  // a nibble keeps its sign bit only if its magnitude bits are not all zero
-  const uint32_t nz = ((o & 0x77777777u) + 0x77777777u) & 0x88888888u;
-  return o & (nz | 0x77777777u);
-}
-// 4 E4M3 codes (element i in byte i), saturated at +-448, -0 made +0
-__device__ inline uint32_t fp8x4(const float* v, float X) {
-  const float lim = 448.0f * X;
-  float c[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) c[i] = fminf(fmaxf(v[i], -lim), lim);
-  short2v lo = {0, 0};
-  lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, c[0], c[1], X, false);
-  lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, c[2], c[3], X, true);
-  const uint32_t o = uint32_t(uint16_t(lo[0])) | (uint32_t(uint16_t(lo[1])) << 16);
-  const uint32_t nz = ((o & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) & 0x80808080u;
-  return o & (nz | 0x7F7F7F7Fu);
-}
+using mxq::u32x4;
 
 // One thread per 32-element block of a row: quantise it, then store its
 // codes and scale byte row-major (row_slot null) or at the row's tile slot.
@@ -83,27 +40,8 @@ __global__ __launch_bounds__(256) void k_mx_quant(MxQuantArgs a) {
     w[4 * i + 2] = v.z;
     w[4 * i + 3] = v.w;
   }
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    amax = fmaxf(amax, fabsf(bf16_to_f32(w[i] & 0xFFFFu)));
-    amax = fmaxf(amax, fabsf(bf16_to_f32(w[i] >> 16)));
-  }
-  const int emax = FP4 ? 2 : 8;
-  int sexp = amax > 0.0f ? ilog2f(amax) - emax : -127;
-  sexp = max(-127, min(127, sexp));
-  const uint8_t sbyte = uint8_t(sexp + 127);
-  // codes: FP4 16 bytes (K 32 kb32 .. + 31), FP8 32 bytes
-  const float X = ldexpf(1.0f, sexp);
-  float v[32];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    v[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
-    v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
-  }
   uint32_t out[FP4 ? 4 : 8];
-#pragma unroll
-  for (int i = 0; i < (FP4 ? 4 : 8); ++i) out[i] = FP4 ? fp4x8(v + 8 * i, X) : fp8x4(v + 4 * i, X);
+  const uint8_t sbyte = mxq::quant_block<FP4>(w, out);
   if (!a.row_slot) {
     a.out_scales[row * nblk + kb32] = sbyte;
     uint8_t* dst = a.out_codes + row * (FP4 ? a.K / 2 : a.K) + int64_t(kb32) * (FP4 ? 16 : 32);
@@ -115,18 +53,7 @@ __global__ __launch_bounds__(256) void k_mx_quant(MxQuantArgs a) {
   const int slot = a.row_slot[row];
   const int kb = kb32 >> 2, q4 = kb32 & 3;
   const int tile = slot / kMxTileRows, i = slot - tile * kMxTileRows;
-  const int64_t blk = int64_t(tile) * nkb + kb;
-  a.out_scales[blk * kMxTileScaleBytes + i * 4 + q4] = sbyte;
-  uint8_t* sub = a.out_codes + blk * mx_tile_code_bytes(FP4) + (i >> 4) * (FP4 ? 1024 : 2048);
-  const int n = i & 15;
-  if constexpr (FP4) {
-    gstore<u32x4>(sub + (16 * q4 + n) * 16, u32x4{out[0], out[1], out[2], out[3]});
-  } else {
-    // K 32 q4 .. + 31 of the step: half q4 / 2, lanes q = 2 q4 - 4 h and q + 1
-    const int h = q4 >> 1, q = 2 * q4 - 4 * h;
-    gstore<u32x4>(sub + h * 1024 + (16 * q + n) * 16, u32x4{out[0], out[1], out[2], out[3]});
-    gstore<u32x4>(sub + h * 1024 + (16 * (q + 1) + n) * 16, u32x4{out[4], out[5], out[6], out[7]});
-  }
+  mxq::store_tile_block<FP4>(a.out_codes, a.out_scales, int64_t(tile) * nkb + kb, i, q4, out, sbyte);
 }
 
 // One workgroup per (row tile, 128-K step) of the work list: copies the

@@ -104,8 +104,10 @@ struct ft_moe_pool {
   int32_t* row_slot = nullptr;      // [rows] prefill: each row's slot in the MX GEMM activation tiles
   uint8_t* xq_codes = nullptr;      // [cap][H] (FP8) or [cap][H/2] (FP4): quantised x, row-major
   uint8_t* xq_scales = nullptr;     // [cap][H/32]
-  uint8_t* tq_codes = nullptr;      // MX GEMM activation tiles (allocated at the first MX call)
+  uint8_t* tq_codes = nullptr;      // MX GEMM activation tiles (allocated at the first MX call): x
   uint8_t* tq_scales = nullptr;
+  uint8_t* hq_codes = nullptr;      // and h, written by the gate/up GEMM while x tiles are read
+  uint8_t* hq_scales = nullptr;
   int32_t* tiles = nullptr;         // [2 * max_tiles]
   int32_t max_tiles = 0;
 
@@ -204,6 +206,8 @@ int ensure_capacity(ft_moe_pool* p, int T) {
   hipFree(p->row_slot); hipFree(p->tiles); hipFree(p->xq_codes); hipFree(p->xq_scales);
   hipFree(p->tq_codes); hipFree(p->tq_scales);
   p->tq_codes = p->tq_scales = nullptr;
+  hipFree(p->hq_codes); hipFree(p->hq_scales);
+  p->hq_codes = p->hq_scales = nullptr;
   if (p->rb_host) hipHostFree(p->rb_host);
   if (p->x_host) hipHostFree(p->x_host);
   if (p->cpu_out) hipHostFree(p->cpu_out);
@@ -516,8 +520,9 @@ int mx_act_tiles(ft_moe_pool* p, const uint16_t* src, int nrows, int K, bool by_
 }
 
 // The prefill expert FFN of an MXFP4 layer on the grouped GEMM: act is
-// FT_ACT_* >> 4.  MX modes quantise x and h into the GEMM's activation tiles;
-// bf16 reads them from their rows (x by token, h by row).
+// FT_ACT_* >> 4.  MX modes quantise x into the GEMM's activation tiles, and
+// the gate/up GEMM writes h quantised into the down GEMM's tiles; bf16 reads
+// the activations from their rows (x by token, h by row).
 int run_mx_ffn(ft_moe_pool* p, int layer, const void* x, int T, int act, hipStream_t s) {
   const int rows = T * p->k + (p->shared ? T : 0);
   const double H = p->H, I = p->I;
@@ -525,11 +530,13 @@ int run_mx_ffn(ft_moe_pool* p, int layer, const void* x, int T, int act, hipStre
   // activation bytes per element as the GEMM reads them
   const double per = !mx ? 2.0 : fp4 ? 0.5 + 1.0 / 32 : 1.0 + 1.0 / 32;
   if (mx && !p->tq_codes) {
-    // sized for FP8 codes of the wider matrix; freed with the per-call buffers
-    const int64_t blocks = int64_t(p->max_tiles) * (std::max(p->H, p->I) / kTileK);
+    // sized for FP8 codes (x: K = H, h: K = I); freed with the per-call buffers
+    const int64_t xb = int64_t(p->max_tiles) * (p->H / kTileK), hb = int64_t(p->max_tiles) * (p->I / kTileK);
     int rc;
-    if ((rc = dev_alloc(&p->tq_codes, blocks * mx_tile_code_bytes(false))) ||
-        (rc = dev_alloc(&p->tq_scales, blocks * kMxTileScaleBytes)))
+    if ((rc = dev_alloc(&p->tq_codes, xb * mx_tile_code_bytes(false))) ||
+        (rc = dev_alloc(&p->tq_scales, xb * kMxTileScaleBytes)) ||
+        (rc = dev_alloc(&p->hq_codes, hb * mx_tile_code_bytes(false))) ||
+        (rc = dev_alloc(&p->hq_scales, hb * kMxTileScaleBytes)))
       return rc;
   }
   int rc;
@@ -548,11 +555,19 @@ int run_mx_ffn(ft_moe_pool* p, int layer, const void* x, int T, int act, hipStre
   a.hidden = p->H;
   a.inter = p->I;
   a.lay = p->lay[p->fmt[layer]];
+  if (mx) {
+    // h leaves the gate/up GEMM quantised, in the down GEMM's activation tiles
+    a.h_codes = p->hq_codes;
+    a.h_scales = p->hq_scales;
+    a.row_slot = p->row_slot;
+  }
   Ev ev = prof_pair(p, s, FT_STAGE_FFN_GATEUP);
   FT_HIP_CHECK(launch_mx_gemm(a, true, act, s, ev));
-  prof_push(p, FT_STAGE_FFN_GATEUP, ev, (p->E + p->shared) * 2 * mat_bytes(FT_FMT_MXFP4, I, H) + rows * I * 2.0 +
+  prof_push(p, FT_STAGE_FFN_GATEUP, ev, (p->E + p->shared) * 2 * mat_bytes(FT_FMT_MXFP4, I, H) + rows * I * per +
             T * H * per, rows * 4 * H * I);
-  if (mx && (rc = mx_act_tiles(p, p->hbuf, rows, p->I, false, fp4, s))) return rc;
+  a.act_codes = p->hq_codes;
+  a.act_scales = p->hq_scales;
+  a.h_codes = a.h_scales = nullptr;
   a.act_rows = p->hbuf;
   a.row_tok = nullptr;
   a.out = p->pbuf;
@@ -1638,6 +1653,7 @@ void ft_moe_destroy_pool(ft_moe_pool* p) {
   hipFree(p->key_off_dev); hipFree(p->prof_cnt_dev);
   hipFree(p->row_slot); hipFree(p->tiles); hipFree(p->xq_codes); hipFree(p->xq_scales);
   hipFree(p->tq_codes); hipFree(p->tq_scales);
+  hipFree(p->hq_codes); hipFree(p->hq_scales);
   if (p->rb_host) hipHostFree(p->rb_host);
   if (p->x_host) hipHostFree(p->x_host);
   if (p->cpu_out) hipHostFree(p->cpu_out);
