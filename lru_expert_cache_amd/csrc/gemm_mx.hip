@@ -360,14 +360,13 @@ __global__ __launch_bounds__(128 * WF, mx_min_waves(ACT, WF)) void k_mx_gemm(MxG
   // epilogue: a lane holds 4 consecutive features of one row (gate/up ->
   // h = bf16(silu(g) * u), down -> p = bf16(w * y)).  Stored from there, a
   // store writes 16 (32x32 layout) or 32 bytes (16x16) in each of 32 or 16
-  // rows.  The down output (a 4096-byte row of p) and the FP4 gate/up one go
+  // rows.  The down output (a 4096-byte row of p) and the MX gate/up one go
   // through LDS instead: the workgroup's 128-row output tile is put together
   // in the free stage ring and leaves in 16-byte pieces, 8 lanes per 128-byte
-  // line of a row.  (The 16x16 gate/up stores measured no slower than the
-  // extra barriers.)  The routing weights of the lane's rows are read once,
-  // before any output is written.
-  // (the MX gate/up output always goes through the tile: h may be quantised
-  // from there, 32-element blocks along the row)
+  // line of a row, or, for MX gate/up with h tiles given, as quantised 32-
+  // element blocks.  (The bf16-mode gate/up stores, 16x16 layout, measured no
+  // slower than the extra barriers.)  The routing weights of the lane's rows
+  // are read once, before any output is written.
   constexpr bool TILE_EPI = !GATEUP || ACT != kActBf16;
   constexpr int NF = feat_per_wg(GATEUP, WF, FX);  // output features of the workgroup
   constexpr int PITCH = NF * 2 + 16;           // tile row pitch (bytes): row r starts 4 r banks on
