@@ -243,19 +243,17 @@ hipError_t launch_miss_copy(const MissCopyArgs& a, int workgroups, hipStream_t s
 //        step's four 32-blocks), 512 bytes.
 // A row's slot is tile * 128 + (row in tile) (resolve writes it per row).
 // Slots past a group's end hold zeros (tile gather) or stale codes (the
-// quantiser writes only real rows): either way they only reach output rows
-// that the GEMM does not store.
+// gate/up GEMM's h output covers only real rows): either way they only reach
+// output rows that the GEMM does not store.
 constexpr int kMxTileRows = 128;
 constexpr int64_t mx_tile_code_bytes(bool fp4) { return fp4 ? 8192 : 16384; }  // per (tile, K step)
 constexpr int64_t kMxTileScaleBytes = 512;                                     // per (tile, K step)
 // mxq.hip: MX quantisation of bf16 rows, row-major (codes [rows][K/2] for
 // FP4, [rows][K] for FP8, even element in the low nibble; scales
-// [rows][K/32]) when row_slot is null, else into the activation tiles at
-// the slot of each row (the down input h, rows in grouped order).
+// [rows][K/32]); the tile gather then lays them out as activation tiles.
 struct MxQuantArgs {
   const uint16_t* in;         // [rows][K] bf16
   int32_t rows, K;
-  const int32_t* row_slot;    // row -> tile slot, or null
   uint8_t* out_codes;
   uint8_t* out_scales;
 };

@@ -8,9 +8,10 @@
 // max 448).  The inputs are bf16 and X a power of two, so v / X is exact; the
 // rounding onto the grid is the hardware convert's (see fp4x8 / fp8x4).
 //
-// Output: row-major codes and scales, or straight into the MX GEMM's
-// activation tiles at each row's slot (see MxQuantArgs); the tile gather
-// copies row-major rows into the tiles (the gate/up input, by token).
+// Output: row-major codes and scales; the tile gather copies those rows into
+// the MX GEMM's activation tiles (the gate/up input, by token).  The down
+// input h is quantised by the gate/up GEMM itself, with the same block code
+// (mxq.h).
 #include "common.h"
 #include "gmem.h"
 #include "mxq.h"
@@ -22,10 +23,10 @@ namespace {
 using mxq::u32x4;
 
 // One thread per 32-element block of a row: quantise it, then store its
-// codes and scale byte row-major (row_slot null) or at the row's tile slot.
+// codes and scale byte row-major.
 template <bool FP4>
 __global__ __launch_bounds__(256) void k_mx_quant(MxQuantArgs a) {
-  const int nblk = a.K / 32, nkb = a.K / 128;
+  const int nblk = a.K / 32;
   const int64_t b = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (b >= int64_t(a.rows) * nblk) return;
   const int64_t row = b / nblk;
@@ -42,18 +43,10 @@ __global__ __launch_bounds__(256) void k_mx_quant(MxQuantArgs a) {
   }
   uint32_t out[FP4 ? 4 : 8];
   const uint8_t sbyte = mxq::quant_block<FP4>(w, out);
-  if (!a.row_slot) {
-    a.out_scales[row * nblk + kb32] = sbyte;
-    uint8_t* dst = a.out_codes + row * (FP4 ? a.K / 2 : a.K) + int64_t(kb32) * (FP4 ? 16 : 32);
-    gstore<u32x4>(dst, u32x4{out[0], out[1], out[2], out[3]});
-    if constexpr (!FP4) gstore<u32x4>(dst + 16, u32x4{out[4], out[5], out[6], out[7]});
-    return;
-  }
-  // tile slot: block kb32 = step kb, 32-block q4 of the step
-  const int slot = a.row_slot[row];
-  const int kb = kb32 >> 2, q4 = kb32 & 3;
-  const int tile = slot / kMxTileRows, i = slot - tile * kMxTileRows;
-  mxq::store_tile_block<FP4>(a.out_codes, a.out_scales, int64_t(tile) * nkb + kb, i, q4, out, sbyte);
+  a.out_scales[row * nblk + kb32] = sbyte;
+  uint8_t* dst = a.out_codes + row * (FP4 ? a.K / 2 : a.K) + int64_t(kb32) * (FP4 ? 16 : 32);
+  gstore<u32x4>(dst, u32x4{out[0], out[1], out[2], out[3]});
+  if constexpr (!FP4) gstore<u32x4>(dst + 16, u32x4{out[4], out[5], out[6], out[7]});
 }
 
 // One workgroup per (row tile, 128-K step) of the work list: copies the

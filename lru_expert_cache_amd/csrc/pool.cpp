@@ -485,36 +485,34 @@ int copy_layer_staging(ft_moe_pool* p, int layer) {
   return FT_OK;
 }
 
-// The GEMM's activation tiles: x is quantised row-major (one row per token)
-// and copied into the tiles of every expert row that reads it; h (rows in
-// grouped order) is quantised straight into its tile slots.  Timed as one stage.
-int mx_act_tiles(ft_moe_pool* p, const uint16_t* src, int nrows, int K, bool by_token, bool fp4, hipStream_t s) {
+// The gate/up GEMM's activation tiles: x of a prefill chunk (T rows, K = H)
+// is quantised row-major (one row per token) and copied into the tiles of
+// every expert row that reads it.  Timed as one stage.  (h is quantised by
+// the gate/up GEMM into the down GEMM's tiles.)
+int mx_act_tiles(ft_moe_pool* p, const uint16_t* src, int nrows, int K, bool fp4, hipStream_t s) {
   hipEvent_t e0 = prof_begin(p, s, FT_STAGE_ACT_QUANT);
   MxQuantArgs q{};
   q.in = src;
   q.rows = nrows;
   q.K = K;
-  q.row_slot = by_token ? nullptr : p->row_slot;
-  q.out_codes = by_token ? p->xq_codes : p->tq_codes;
-  q.out_scales = by_token ? p->xq_scales : p->tq_scales;
+  q.out_codes = p->xq_codes;
+  q.out_scales = p->xq_scales;
   FT_HIP_CHECK(launch_mx_quant(q, fp4, s));
   const double per = fp4 ? 0.5 + 1.0 / 32 : 1.0 + 1.0 / 32;
   double bytes = double(nrows) * K * (2.0 + per);
-  if (by_token) {
-    MxTileArgs t{};
-    t.codes = p->xq_codes;
-    t.scales = p->xq_scales;
-    t.K = K;
-    t.row_map = p->row_tok;
-    t.groups = p->groups;
-    t.tiles = p->tiles;
-    t.n_tiles_dev = p->dev_header + 10;
-    t.max_tiles = p->max_tiles;
-    t.out_codes = p->tq_codes;
-    t.out_scales = p->tq_scales;
-    FT_HIP_CHECK(launch_mx_tile_gather(t, fp4, s));
-    bytes += 2.0 * double(nrows) * p->k * K * per;
-  }
+  MxTileArgs t{};
+  t.codes = p->xq_codes;
+  t.scales = p->xq_scales;
+  t.K = K;
+  t.row_map = p->row_tok;
+  t.groups = p->groups;
+  t.tiles = p->tiles;
+  t.n_tiles_dev = p->dev_header + 10;
+  t.max_tiles = p->max_tiles;
+  t.out_codes = p->tq_codes;
+  t.out_scales = p->tq_scales;
+  FT_HIP_CHECK(launch_mx_tile_gather(t, fp4, s));
+  bytes += 2.0 * double(nrows) * p->k * K * per;
   prof_end(p, FT_STAGE_ACT_QUANT, e0, s, bytes, 0.0);
   return FT_OK;
 }
@@ -540,7 +538,7 @@ int run_mx_ffn(ft_moe_pool* p, int layer, const void* x, int T, int act, hipStre
       return rc;
   }
   int rc;
-  if (mx && (rc = mx_act_tiles(p, static_cast<const uint16_t*>(x), T, p->H, true, fp4, s))) return rc;
+  if (mx && (rc = mx_act_tiles(p, static_cast<const uint16_t*>(x), T, p->H, fp4, s))) return rc;
   MxGemmArgs a{};
   a.groups = p->groups;
   a.tiles = p->tiles;
