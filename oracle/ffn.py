@@ -18,8 +18,11 @@ modes x' and h' are the OCP MX quantisation of x and h (blocks of 32 along
 K) with E4M3 (mxfp8) or E2M1 (mxfp4) elements.
 
 Pins (tests/test_oracle_ffn.py): a dense per-token fp64 reference without
-rounding points, and a one-hot case whose output is a closed-form expression
-of three known weights.
+rounding points; a one-hot case whose output is a closed-form expression of
+three known weights; the same kind of closed form in all three activation
+modes (tests/golden/mx_act_closed_form.txt: where Q applies to x and h, and
+its saturation); the combine with a shared expert worked by hand
+(tests/golden/combine_shared.txt: order and rounding point).
 """
 
 from __future__ import annotations
@@ -59,15 +62,18 @@ def weighted_rows(y: np.ndarray, w: np.ndarray) -> np.ndarray:
     return round_bf16(np.asarray(w, np.float32).astype(np.float64)[:, None] * y)
 
 
-def combine(p: np.ndarray, shared=None) -> np.ndarray:
-    """p: [T,k,H] bf16 values; shared: [T,H] bf16 values or None -> out [T,H] bf16 values.
+def combine(p: np.ndarray, shared_y=None) -> np.ndarray:
+    """p: [T,k,H] bf16 values; shared_y: [T,H] output of the shared expert
+    (before any rounding) or None -> out [T,H] bf16 values.
 
-    Sequential fp32 accumulation in rank order, shared expert last.
+    Sequential fp32 accumulation in rank order; the shared expert (weight 1)
+    is rounded to bf16 on its own and added last.
     """
     p32 = np.asarray(p, np.float64).astype(np.float32)
     acc = p32[:, 0, :].copy()
     for j in range(1, p32.shape[1]):
         acc = (acc + p32[:, j, :]).astype(np.float32)
-    if shared is not None:
-        acc = (acc + np.asarray(shared, np.float64).astype(np.float32)).astype(np.float32)
+    if shared_y is not None:
+        ps = round_bf16(np.asarray(shared_y, np.float64))
+        acc = (acc + ps.astype(np.float32)).astype(np.float32)
     return round_bf16(acc.astype(np.float64))

@@ -136,5 +136,5 @@ class OracleLayerStack:
         shared = None
         if w.shared_expert:
             sg, su, sd = self.shared_mats(layer)
-            shared = formats.round_bf16(ffn.expert_forward(x, sg, su, sd, self.act_mode))
+            shared = ffn.expert_forward(x, sg, su, sd, self.act_mode)
         return ffn.combine(p, shared)

@@ -3,6 +3,7 @@
 import math
 
 import numpy as np
+import pytest
 
 import moe_synth as ms
 from oracle import ffn, formats as F, router
@@ -105,17 +106,53 @@ def test_combine_is_sequential_fp32():
     assert ffn.combine(p2)[0, 0] == F.round_bf16(np.array([1.0 + 2.0 ** -23]))[0]
 
 
-def test_act_quant_modes_change_little():
-    w = ms.workload(0)
-    x_bits = ms.activations(w, 0, 0, 8)
-    outs = {}
-    for mode in (ffn.ACT_BF16, ffn.ACT_MXFP8, ffn.ACT_MXFP4):
-        st = OracleLayerStack(w, act_mode=mode)
-        outs[mode] = st.forward(0, x_bits, None)["out"]
-    base = outs[ffn.ACT_BF16]
-    r8 = np.linalg.norm(outs[ffn.ACT_MXFP8] - base) / np.linalg.norm(base)
-    r4 = np.linalg.norm(outs[ffn.ACT_MXFP4] - base) / np.linalg.norm(base)
-    assert 0 < r8 < 0.08 and r8 < r4 < 0.4
+def _golden(name):
+    import os
+
+    path = os.path.join(os.path.dirname(__file__), "golden", name)
+    return [l.strip() for l in open(path) if l.strip() and not l.startswith("#")]
+
+
+def _num(tok):
+    if "2^" in tok:
+        return sum(2.0 ** float(t.split("^")[1]) for t in tok.split("+"))
+    return float(tok)
+
+
+@pytest.mark.parametrize("mode", ["bf16", "mxfp4", "mxfp8"])
+def test_act_modes_closed_form(mode):
+    """tests/golden/mx_act_closed_form.txt: x and h quantised (OCP MX v1.0) in
+    blocks of 32 along K, h after its bf16 rounding; worked by hand."""
+    H, I = 64, 32
+    entries = [
+        (0, 3, 5, 3, 127), (1, 3, 5, 3, 127),      # a = b = 1.5
+        (0, 10, 37, 5, 127), (1, 10, 37, 3, 123),  # a = 3.0, b = 0.09375
+        (0, 17, 5, 1, 126), (1, 17, 5, 5, 127),    # a = 0.25, b = 3.0
+        (0, 20, 40, 4, 127), (1, 20, 40, 2, 127),  # a = 2.0, b = 1.0
+        (2, 0, 3, 2, 127), (2, 1, 10, 1, 128), (2, 2, 17, 10, 127), (2, 3, 20, 5, 127),
+    ]
+    blob = _blob_with(ms.FMT_MXFP4, H, I, entries)
+    wg, wu, wd = F.dequant_expert(ms.FMT_MXFP4, blob, H, I)
+    x = np.zeros((1, H))
+    x[0, 5], x[0, 37], x[0, 40] = 1.0, 1.5, F.round_bf16(np.array([0.3]))[0]
+    assert x[0, 40] == 0.30078125
+    act = {"bf16": ffn.ACT_BF16, "mxfp4": ffn.ACT_MXFP4, "mxfp8": ffn.ACT_MXFP8}[mode]
+    y = ffn.expert_forward(x, wg, wu, wd, act)
+    out = ffn.combine(ffn.weighted_rows(y, np.array([1.0], np.float32))[:, None, :])
+    rows = {l.split(";")[0].strip(): [float(v) for v in l.split(";")[1].split()] for l in _golden("mx_act_closed_form.txt")}
+    expect = np.zeros(H)
+    expect[:4] = rows[mode]
+    assert np.array_equal(out[0], expect), (out[0, :4], expect[:4])
+
+
+def test_combine_shared_by_hand():
+    """tests/golden/combine_shared.txt: the shared expert is rounded to bf16 on
+    its own and added after the routed rows, in the same fp32 accumulator."""
+    lines = [[_num(t.strip()) for t in l.split(";")] for l in _golden("combine_shared.txt")]
+    p = np.array([[[l[0] for l in lines], [l[1] for l in lines]]]).transpose(0, 1, 2)  # [T=1, k=2, H]
+    ys = np.array([[l[2] for l in lines]])
+    out = ffn.combine(p, ys)
+    assert np.array_equal(out[0], np.array([l[3] for l in lines])), out
 
 
 def test_shared_expert_added_last():
@@ -127,6 +164,7 @@ def test_shared_expert_added_last():
     x = F.bf16_from_bits(x_bits)
     sg, su, sd = F.dequant_expert(ms.FMT_NVFP4, ms.shared_blob(w, 0), 256, 128)
     ys = F.round_bf16(ffn.expert_forward(x, sg, su, sd))
+    assert np.count_nonzero(ys) > 0
     w_no = w.with_(shared_expert=False)
     st2 = OracleLayerStack(w_no)
     res2 = st2.forward(0, x_bits, ms.popularity_bias(w, 0, 0))
