@@ -140,23 +140,38 @@ typedef struct {
   uint64_t calls;                      /* forward calls */
   int64_t slots_used, slots_total;     /* cache fullness (whole pool) */
   double min_topk_gap;                 /* smallest logit gap between rank k and k+1 seen */
+  /* milliseconds spent copying experts from host RAM (misses and prefill
+   * staging): a device-driven miss copy is timed on the device's
+   * constant-rate wall clock from its first workgroup's start to its last
+   * workgroup's end; host-issued copies are bracketed by events on the copy
+   * stream.  Copies that overlap other work count in full. */
+  double copy_ms;
 } ft_moe_stats;
 
 /* Create a pool on cfg->device: validates the shapes, copies the expert
  * blobs into pinned host RAM (repacked for the GPU), allocates the slot arena,
  * the resident router weights and shared experts, and the device slot table.
  * Returns FT_OK, FT_WARN_STAGING_SMALL (pool usable for decode only), or an
- * error (then *out is NULL).  Env FT_MOE_FAULT=pinned_alloc forces
- * FT_E_OOM_PINNED (for tests). */
+ * error (then *out is NULL).  Env FT_MOE_FAULT (for tests): pinned_alloc
+ * forces FT_E_OOM_PINNED here; work_alloc:<n> / mx_alloc:<n> make the pool's
+ * n-th device allocation of per-call work buffers / of MX activation tiles
+ * fail once (the call returns FT_E_OOM_DEVICE and leaves those buffers
+ * unallocated; the next call allocates them again). */
 int ft_moe_init_pool(const ft_moe_config *cfg, const ft_moe_weights *w, ft_moe_pool **out);
 
 /* One MoE layer call on `hip_stream` (a hipStream_t, NULL = default stream).
  * x_bf16: dev [T][H] bf16; router_bias: dev [E] fp32 added to the logits, or
  * NULL; out_bf16: dev [T][H] bf16 (may not alias x).  flags: FT_FWD_* |
- * FT_ACT_*.  Decode blocks the host once per wave to read the miss list and
- * returns after the work is enqueued.  On error no slot stays assigned to an
- * expert whose copy failed.  Env FT_MOE_FAULT=copy:<n> fails the n-th miss
- * copy of the pool (for tests). */
+ * FT_ACT_*.  A decode call whose pairs fit one wave (T*top_k <= pool slots)
+ * with no hybrid share runs device-driven: router, resolve, miss copy (a
+ * kernel reading the pinned store), FFN and combine are enqueued on the
+ * stream with no host wait.  Other decode calls (hybrid share, several
+ * waves, or env FT_MOE_DECODE_PATH=host) block the host once per wave to
+ * read the miss list, issue the copies on the pool's copy streams and run
+ * host-computed experts on host threads.  The call returns once the work is
+ * enqueued.  On error no slot stays assigned to an expert whose copy failed.
+ * Env FT_MOE_FAULT=copy:<n> fails the n-th miss copy of the pool (host-driven
+ * path; for tests). */
 int ft_moe_layer_forward(ft_moe_pool *p, int32_t layer, int32_t num_tokens, const void *x_bf16,
                          const float *router_bias, void *out_bf16, int32_t flags, void *hip_stream,
                          ft_moe_trace *trace);
@@ -241,6 +256,9 @@ typedef struct {
   double t_cpu;               /* s: the same misses on host cores */
   int32_t mode;               /* FT_MODE_* */
   double share;               /* the hybrid share the mode implies (0 unless hybrid) */
+  double balanced_share;      /* t_stream / (t_stream + t_cpu) whatever the mode: the share at
+                                 which streamed and host-computed misses finish together, for a
+                                 caller that picks the hybrid strategy itself */
 } ft_moe_mode_report;
 
 /* The decision alone (host code, no device work): t_stream = sum over layers
@@ -249,7 +267,7 @@ typedef struct {
  * >= all_experts; else HYBRID when t_cpu < t_stream, with share =
  * t_stream / (t_stream + t_cpu), the split at which both paths finish a step's
  * misses together; else OFFLOAD.  The pages' cpu strategy (share 1) is never
- * chosen by this rule.  FT_E_INVALID if a used format has a rate <= 0 or
+ * chosen by this rule.  balanced_share is that split for every mode.  FT_E_INVALID if a used format has a rate <= 0 or
  * not finite. */
 int ft_moe_decide_mode(ft_moe_mode_report *r);
 

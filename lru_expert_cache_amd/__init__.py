@@ -66,7 +66,7 @@ class ft_moe_stats(ctypes.Structure):
                 ("cpu_misses", ctypes.c_uint64), ("evictions", ctypes.c_uint64),
                 ("bytes_h2d", ctypes.c_uint64), ("calls", ctypes.c_uint64),
                 ("slots_used", ctypes.c_int64), ("slots_total", ctypes.c_int64),
-                ("min_topk_gap", ctypes.c_double)]
+                ("min_topk_gap", ctypes.c_double), ("copy_ms", ctypes.c_double)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -77,7 +77,7 @@ class ft_moe_mode_report(ctypes.Structure):
                 ("h2d_bytes_per_s", ctypes.c_double * 4), ("gpu_bytes_per_s", ctypes.c_double * 4),
                 ("cpu_bytes_per_s", ctypes.c_double * 4), ("pool_slots", ctypes.c_int64),
                 ("all_experts", ctypes.c_int64), ("t_stream", ctypes.c_double), ("t_cpu", ctypes.c_double),
-                ("mode", ctypes.c_int32), ("share", ctypes.c_double)]
+                ("mode", ctypes.c_int32), ("share", ctypes.c_double), ("balanced_share", ctypes.c_double)]
 
     def as_dict(self):
         d = {}

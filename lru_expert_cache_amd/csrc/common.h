@@ -228,6 +228,12 @@ struct MissCopyArgs {
   const GroupDesc* gdesc;     // groups in run order: the streamed misses from dev_header[2]
   int32_t layer, E;
   int64_t bytes;              // bytes per expert of this layer (multiple of 16)
+  // copy time on the device's constant-rate wall clock: clk[0] (earliest
+  // workgroup start, reset to ~0), clk[1] (latest end), clk[2] (workgroups
+  // done); the last workgroup adds clk[1] - clk[0] to *ticks and resets clk.
+  // Null = not measured.
+  uint64_t* clk;
+  uint64_t* ticks;
 };
 hipError_t launch_miss_copy(const MissCopyArgs& a, int workgroups, hipStream_t s, Ev ev = {});
 

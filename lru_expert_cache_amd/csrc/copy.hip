@@ -28,6 +28,8 @@ __global__ __launch_bounds__(256) void k_miss_copy(MissCopyArgs a) {
   const int64_t n16 = a.bytes / 16;
   const int64_t total = int64_t(n) * n16;
   const int64_t per = (total + gridDim.x - 1) / gridDim.x;
+  const bool timed = a.clk != nullptr && total > 0;
+  if (timed && threadIdx.x == 0) atomicMin(reinterpret_cast<unsigned long long*>(a.clk), wall_clock64());
   int64_t lo = int64_t(blockIdx.x) * per;
   const int64_t hi = lo + per < total ? lo + per : total;
   while (lo < hi) {
@@ -52,6 +54,26 @@ __global__ __launch_bounds__(256) void k_miss_copy(MissCopyArgs a) {
     }
     for (; j < seg; j += 256) gstore<u32x4>(dst + j, gload_nt<u32x4>(src + j));
     lo += seg;
+  }
+  if (timed) {
+    // the end time is taken once every store of the workgroup has completed
+    // (`timed` is the same for the whole grid, so the barrier is uniform)
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      unsigned long long* c = reinterpret_cast<unsigned long long*>(a.clk);
+      atomicMax(c + 1, (unsigned long long)wall_clock64());
+      __threadfence();
+      if (atomicAdd(c + 2, 1ull) == gridDim.x - 1) {
+        // last workgroup: every other one has published its end
+        __threadfence();
+        const unsigned long long t0 = atomicAdd(c, 0ull), t1 = atomicAdd(c + 1, 0ull);
+        atomicAdd(reinterpret_cast<unsigned long long*>(a.ticks), t1 > t0 ? t1 - t0 : 0ull);
+        atomicExch(c, ~0ull);
+        atomicExch(c + 1, 0ull);
+        atomicExch(c + 2, 0ull);
+      }
+    }
   }
 }
 

@@ -1081,10 +1081,6 @@ template <int FMT, bool GATEUP>
 hipError_t launch_small(const FfnArgs& a, hipStream_t st, Ev ev) {
   const int nkb = a.lay.m[GATEUP ? 0 : 2].cols / kTileK;
   bool wide = a.max_rows > 0 && a.max_rows <= kTileRows;
-#ifdef FT_FFN_KERNEL_ENV
-  if (const char* e = getenv("FFN_KERNEL"))
-    if (!strcmp(e, "ring") || !strcmp(e, "stream")) wide = false;
-#endif
   if (wide) {
     bool done = false;
     const hipError_t r = launch_wide<FMT, GATEUP>(a, st, ev, &done);
@@ -1092,10 +1088,6 @@ hipError_t launch_small(const FfnArgs& a, hipStream_t st, Ev ev) {
   }
   // gate/up: the item ring; down (short K, tiny items): the K-streaming kernel
   int kpw = GATEUP && a.max_rows > 0 && a.max_rows <= kTileRows ? ring_kpw<FMT, GATEUP>(nkb) : 0;
-#ifdef FT_FFN_KERNEL_ENV
-  if (const char* e = getenv("FFN_KERNEL"))
-    if (!strcmp(e, "stream")) kpw = 0;
-#endif
   switch (kpw) {
     case 4: return launch_ring_k<FMT, GATEUP, 4>(a, nkb / 4, st, ev);
     case 3: return launch_ring_k<FMT, GATEUP, 3>(a, nkb / 3, st, ev);
@@ -1111,10 +1103,6 @@ template <bool GATEUP>
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t st, Ev ev) {
   if (a.n_list <= 0) return hipSuccess;
   bool small = a.max_rows > 0 && a.max_rows <= kStreamMaxChunks * kTileRows;
-#ifdef FT_FFN_KERNEL_ENV
-  if (const char* e = getenv("FFN_KERNEL"))
-    if (!strcmp(e, "grid")) small = false;
-#endif
   if (small) {
     switch (a.lay.fmt) {
       case FT_FMT_MXFP4: return launch_small<FT_FMT_MXFP4, GATEUP>(a, st, ev);

@@ -129,6 +129,23 @@ struct ft_moe_pool {
   std::vector<int32_t> prefill_res;  // [L*E] slot of each resident key at chunk start (outside staging), else -1
   uint64_t copy_counter = 0;
   int64_t fault_copy = -1;
+  // fault injection (FT_MOE_FAULT): fail the n-th device allocation of the
+  // per-call work buffers / of the MX activation tiles, once (1-based)
+  int fault_work_alloc = -1, fault_mx_alloc = -1;
+  int work_allocs = 0, mx_allocs = 0;
+
+  // copy time (ft_moe_stats::copy_ms): device-driven copies measure
+  // themselves on the device wall clock (copy_clk scratch, copy_ticks per
+  // layer); host-issued copies are bracketed by events, folded in per layer
+  uint64_t* copy_clk = nullptr;    // [3]
+  uint64_t* copy_ticks = nullptr;  // [L]
+  double wall_khz = 0.0;
+  std::vector<double> copy_ms_host;  // [L]
+  struct CopyRec {
+    int layer;
+    hipEvent_t a, b;
+  };
+  std::vector<CopyRec> copy_pending;
 
   // miss lists of the latest call; after a device-driven call they are read
   // from the resolve kernel's mapped readback when first asked for
@@ -196,56 +213,87 @@ void parallel_for(int n, int threads, const std::function<void(int, int)>& fn) {
   for (auto& x : th) x.join();
 }
 
+template <typename T>
+void dev_free(T*& q) {
+  if (q) (void)hipFree(q);
+  q = nullptr;
+}
+
+// A device allocation of the work buffers; fails when it is the pool's
+// injected fault (FT_MOE_FAULT=work_alloc:<n>, once).
+template <typename T>
+int work_alloc(ft_moe_pool* p, T** q, int64_t n) {
+  if (++p->work_allocs == p->fault_work_alloc) {
+    p->fault_work_alloc = -1;
+    *q = nullptr;
+    set_error("injected failure of work-buffer allocation %d", p->work_allocs);
+    return FT_E_OOM_DEVICE;
+  }
+  return dev_alloc(q, n);
+}
+
+void free_work_buffers(ft_moe_pool* p) {
+  dev_free(p->z); dev_free(p->sel); dev_free(p->w); dev_free(p->gap); dev_free(p->pair_flag);
+  dev_free(p->pair_slot); dev_free(p->pair_row); dev_free(p->row_tok); dev_free(p->row_w);
+  dev_free(p->hbuf); dev_free(p->pbuf);
+  dev_free(p->row_slot); dev_free(p->tiles); dev_free(p->xq_codes); dev_free(p->xq_scales);
+  dev_free(p->tq_codes); dev_free(p->tq_scales); dev_free(p->hq_codes); dev_free(p->hq_scales);
+  if (p->rb_host) (void)hipHostFree(p->rb_host);
+  if (p->x_host) (void)hipHostFree(p->x_host);
+  if (p->cpu_out) (void)hipHostFree(p->cpu_out);
+  p->rb_host = nullptr;
+  p->rb_dev = nullptr;
+  p->x_host = nullptr;
+  p->cpu_out = nullptr;
+  p->cap_T = 0;
+}
+
+// Grows the per-call buffers to T tokens.  Every buffer is freed and nulled
+// first, and cap_T stays 0 until all of them exist, so a failed allocation
+// leaves no dangling pointer and the next call simply tries again.
 int ensure_capacity(ft_moe_pool* p, int T) {
   if (T <= p->cap_T) return FT_OK;
   const int cap = std::max(T, 64);
   FT_HIP_CHECK(hipDeviceSynchronize());  // earlier calls may still use the old buffers
-  hipFree(p->z); hipFree(p->sel); hipFree(p->w); hipFree(p->gap); hipFree(p->pair_flag);
-  hipFree(p->pair_slot); hipFree(p->pair_row); hipFree(p->row_tok); hipFree(p->row_w);
-  hipFree(p->hbuf); hipFree(p->pbuf);
-  hipFree(p->row_slot); hipFree(p->tiles); hipFree(p->xq_codes); hipFree(p->xq_scales);
-  hipFree(p->tq_codes); hipFree(p->tq_scales);
-  p->tq_codes = p->tq_scales = nullptr;
-  hipFree(p->hq_codes); hipFree(p->hq_scales);
-  p->hq_codes = p->hq_scales = nullptr;
-  if (p->rb_host) hipHostFree(p->rb_host);
-  if (p->x_host) hipHostFree(p->x_host);
-  if (p->cpu_out) hipHostFree(p->cpu_out);
-  p->rb_host = nullptr;
-  p->x_host = nullptr;
-  p->cpu_out = nullptr;
-  p->cap_T = 0;
+  free_work_buffers(p);
   const int64_t pairs = int64_t(cap) * p->k;
   const int64_t rows = pairs + (p->shared ? cap : 0);
-  int rc;
-  if ((rc = dev_alloc(&p->z, int64_t(cap) * p->E))) return rc;
-  if ((rc = dev_alloc(&p->sel, pairs))) return rc;
-  if ((rc = dev_alloc(&p->w, pairs))) return rc;
-  if ((rc = dev_alloc(&p->gap, cap))) return rc;
-  if ((rc = dev_alloc(&p->pair_flag, pairs))) return rc;
-  if ((rc = dev_alloc(&p->pair_slot, pairs))) return rc;
-  if ((rc = dev_alloc(&p->pair_row, pairs))) return rc;
-  if ((rc = dev_alloc(&p->row_tok, rows))) return rc;
-  if ((rc = dev_alloc(&p->row_w, rows))) return rc;
-  if ((rc = dev_alloc(&p->hbuf, rows * p->I))) return rc;
-  if ((rc = dev_alloc(&p->pbuf, rows * p->H))) return rc;
   const int tr = mx_gemm_rows_per_tile();
   p->max_tiles = int32_t((pairs + tr - 1) / tr + p->E + (cap + tr - 1) / tr + 2);
-  if ((rc = dev_alloc(&p->row_slot, rows))) return rc;
-  if ((rc = dev_alloc(&p->xq_codes, int64_t(cap) * p->H))) return rc;
-  if ((rc = dev_alloc(&p->xq_scales, int64_t(cap) * p->H / 32))) return rc;
-  if ((rc = dev_alloc(&p->tiles, 2 * int64_t(p->max_tiles)))) return rc;
+  int rc;
+  if ((rc = work_alloc(p, &p->z, int64_t(cap) * p->E)) || (rc = work_alloc(p, &p->sel, pairs)) ||
+      (rc = work_alloc(p, &p->w, pairs)) || (rc = work_alloc(p, &p->gap, cap)) ||
+      (rc = work_alloc(p, &p->pair_flag, pairs)) || (rc = work_alloc(p, &p->pair_slot, pairs)) ||
+      (rc = work_alloc(p, &p->pair_row, pairs)) || (rc = work_alloc(p, &p->row_tok, rows)) ||
+      (rc = work_alloc(p, &p->row_w, rows)) || (rc = work_alloc(p, &p->hbuf, rows * p->I)) ||
+      (rc = work_alloc(p, &p->pbuf, rows * p->H)) || (rc = work_alloc(p, &p->row_slot, rows)) ||
+      (rc = work_alloc(p, &p->xq_codes, int64_t(cap) * p->H)) ||
+      (rc = work_alloc(p, &p->xq_scales, int64_t(cap) * p->H / 32)) ||
+      (rc = work_alloc(p, &p->tiles, 2 * int64_t(p->max_tiles)))) {
+    free_work_buffers(p);
+    return rc;
+  }
   p->rb_cap = int64_t(sizeof(ResolveHeader)) + 5 * 4 * int64_t(p->E) + 8 * pairs + 64;
   if (hipHostMalloc(reinterpret_cast<void**>(&p->rb_host), p->rb_cap, hipHostMallocMapped | hipHostMallocCoherent) !=
       hipSuccess) {
+    (void)hipGetLastError();
+    p->rb_host = nullptr;
+    free_work_buffers(p);
     set_error("pinned readback allocation failed");
     return FT_E_OOM_PINNED;
   }
-  FT_HIP_CHECK(hipHostGetDevicePointer(reinterpret_cast<void**>(&p->rb_dev), p->rb_host, 0));
+  if (hipHostGetDevicePointer(reinterpret_cast<void**>(&p->rb_dev), p->rb_host, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    free_work_buffers(p);
+    set_error("pinned readback buffer is not mapped for the device");
+    return FT_E_HIP;
+  }
   if (hipHostMalloc(reinterpret_cast<void**>(&p->x_host), size_t(cap) * p->H * 2, hipHostMallocDefault) !=
           hipSuccess ||
       hipHostMalloc(reinterpret_cast<void**>(&p->cpu_out), size_t(pairs) * p->H * 2, hipHostMallocDefault) !=
           hipSuccess) {
+    (void)hipGetLastError();
+    free_work_buffers(p);
     set_error("pinned staging allocation failed");
     return FT_E_OOM_PINNED;
   }
@@ -406,6 +454,47 @@ void prof_push(ft_moe_pool* p, int stage, Ev ev, double bytes, double flops) {
   if (ev.a) p->prof_pending.push_back({stage, ev.a, ev.b, bytes, flops});
 }
 
+// Copy-time events of host-issued copies (always on; ft_moe_stats::copy_ms).
+hipEvent_t copy_timer_begin(ft_moe_pool* p, hipStream_t s) {
+  hipEvent_t e = prof_event(p);
+  if (e && hipEventRecord(e, s) != hipSuccess) {
+    (void)hipGetLastError();
+    p->prof_free.push_back(e);
+    return nullptr;
+  }
+  return e;
+}
+
+void copy_timer_end(ft_moe_pool* p, int layer, hipEvent_t a, hipStream_t s) {
+  if (!a) return;
+  hipEvent_t b = prof_event(p);
+  if (!b || hipEventRecord(b, s) != hipSuccess) {
+    (void)hipGetLastError();
+    p->prof_free.push_back(a);
+    if (b) p->prof_free.push_back(b);
+    return;
+  }
+  p->copy_pending.push_back({layer, a, b});
+}
+
+void copy_drain(ft_moe_pool* p, bool wait) {
+  std::vector<ft_moe_pool::CopyRec> keep;
+  for (auto& r : p->copy_pending) {
+    if (wait)
+      (void)hipEventSynchronize(r.b);
+    else if (hipEventQuery(r.b) != hipSuccess) {
+      keep.push_back(r);
+      continue;
+    }
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) p->copy_ms_host[r.layer] += ms;
+    p->prof_free.push_back(r.a);
+    p->prof_free.push_back(r.b);
+  }
+  (void)hipGetLastError();
+  p->copy_pending.swap(keep);
+}
+
 // Fold finished records into the sums (all of them if wait).
 void prof_drain(ft_moe_pool* p, bool wait) {
   std::vector<ft_moe_pool::ProfRec> keep;
@@ -446,6 +535,7 @@ int copy_layer_staging(ft_moe_pool* p, int layer) {
   uint8_t* dst = p->arena + int64_t(half) * E * p->slot_bytes;
   const ExpertLayout& L = p->lay[p->fmt[layer]];
   hipEvent_t e0 = prof_begin(p, p->copy_stream, FT_STAGE_COPY);
+  hipEvent_t ct = copy_timer_begin(p, p->copy_stream);
   int copied = 0;
   if (p->prefill_hit) {
     // runs of consecutive experts that are not resident in the pool
@@ -481,6 +571,7 @@ int copy_layer_staging(ft_moe_pool* p, int layer) {
     copied = E;
   }
   prof_end(p, FT_STAGE_COPY, e0, p->copy_stream, double(copied) * double(p->canon_bytes[p->fmt[layer]]), 0.0);
+  copy_timer_end(p, layer, ct, p->copy_stream);
   FT_HIP_CHECK(hipEventRecord(p->ev_staged[half], p->copy_stream));
   return FT_OK;
 }
@@ -527,15 +618,29 @@ int run_mx_ffn(ft_moe_pool* p, int layer, const void* x, int T, int act, hipStre
   const bool mx = act != 0, fp4 = act == (FT_ACT_MXFP4 >> 4);
   // activation bytes per element as the GEMM reads them
   const double per = !mx ? 2.0 : fp4 ? 0.5 + 1.0 / 32 : 1.0 + 1.0 / 32;
-  if (mx && !p->tq_codes) {
-    // sized for FP8 codes (x: K = H, h: K = I); freed with the per-call buffers
+  if (mx && !(p->tq_codes && p->tq_scales && p->hq_codes && p->hq_scales)) {
+    // sized for FP8 codes (x: K = H, h: K = I); freed with the per-call
+    // buffers.  All four exist or none does: a failed allocation frees the
+    // others, so a later call never runs with part of them.
     const int64_t xb = int64_t(p->max_tiles) * (p->H / kTileK), hb = int64_t(p->max_tiles) * (p->I / kTileK);
+    auto mx_alloc = [p](uint8_t** q, int64_t n) -> int {
+      if (++p->mx_allocs == p->fault_mx_alloc) {
+        p->fault_mx_alloc = -1;
+        *q = nullptr;
+        set_error("injected failure of MX tile allocation %d", p->mx_allocs);
+        return FT_E_OOM_DEVICE;
+      }
+      return dev_alloc(q, n);
+    };
+    dev_free(p->tq_codes); dev_free(p->tq_scales); dev_free(p->hq_codes); dev_free(p->hq_scales);
     int rc;
-    if ((rc = dev_alloc(&p->tq_codes, xb * mx_tile_code_bytes(false))) ||
-        (rc = dev_alloc(&p->tq_scales, xb * kMxTileScaleBytes)) ||
-        (rc = dev_alloc(&p->hq_codes, hb * mx_tile_code_bytes(false))) ||
-        (rc = dev_alloc(&p->hq_scales, hb * kMxTileScaleBytes)))
+    if ((rc = mx_alloc(&p->tq_codes, xb * mx_tile_code_bytes(false))) ||
+        (rc = mx_alloc(&p->tq_scales, xb * kMxTileScaleBytes)) ||
+        (rc = mx_alloc(&p->hq_codes, hb * mx_tile_code_bytes(false))) ||
+        (rc = mx_alloc(&p->hq_scales, hb * kMxTileScaleBytes))) {
+      dev_free(p->tq_codes); dev_free(p->tq_scales); dev_free(p->hq_codes); dev_free(p->hq_scales);
       return rc;
+    }
   }
   int rc;
   if (mx && (rc = mx_act_tiles(p, static_cast<const uint16_t*>(x), T, p->H, fp4, s))) return rc;
@@ -687,6 +792,8 @@ int forward_decode_dev(ft_moe_pool* p, int layer, int T, const void* x, void* ou
   ca.layer = layer;
   ca.E = E;
   ca.bytes = p->lay[f].bytes;
+  ca.clk = p->copy_clk;
+  ca.ticks = p->copy_ticks + layer;
   Ev ec = prof_pair(p, s, FT_STAGE_COPY);
   FT_HIP_CHECK(launch_miss_copy(ca, p->copy_wgs, s, ec));
   prof_push(p, FT_STAGE_COPY, ec, 0.0, 0.0);
@@ -723,6 +830,7 @@ int read_pending_misses(const ft_moe_pool* p) {
 
 int forward_decode(ft_moe_pool* p, int layer, int T, const void* x, void* out, hipStream_t s) {
   const int E = p->E, k = p->k;
+  if (!p->copy_pending.empty()) copy_drain(p, false);
   const ExpertLayout& L = p->lay[p->fmt[layer]];
   p->last_se.clear();
   p->last_ss.clear();
@@ -785,8 +893,9 @@ int forward_decode(ft_moe_pool* p, int layer, int T, const void* x, void* out, h
     // finished: the resolve kernel that published this list ran after it.
     const int ncs = std::min(p->n_copy, std::max(h.n_stream, 1));
     hipEvent_t ec = h.n_stream > 0 ? prof_begin(p, p->copy[0], FT_STAGE_COPY) : nullptr;
-    if (ec)
-      for (int c = 1; c < ncs; ++c) FT_HIP_CHECK(hipStreamWaitEvent(p->copy[c], ec, 0));
+    hipEvent_t et = h.n_stream > 0 ? copy_timer_begin(p, p->copy[0]) : nullptr;
+    if (et)
+      for (int c = 1; c < ncs; ++c) FT_HIP_CHECK(hipStreamWaitEvent(p->copy[c], et, 0));
     for (int i = 0; i < h.n_stream; ++i) {
       const int64_t key = int64_t(layer) * E + se[i];
       int rc = issue_copy(p, p->arena + int64_t(ss[i]) * p->slot_bytes, p->host_store + p->key_off[key],
@@ -802,6 +911,7 @@ int forward_decode(ft_moe_pool* p, int layer, int T, const void* x, void* out, h
         FT_HIP_CHECK(hipStreamWaitEvent(p->copy[0], p->ev_copy_done[c], 0));
       }
       prof_end(p, FT_STAGE_COPY, ec, p->copy[0], double(h.n_stream) * double(p->canon_bytes[p->fmt[layer]]), 0.0);
+      copy_timer_end(p, layer, et, p->copy[0]);
       FT_HIP_CHECK(hipEventRecord(p->ev_copied, p->copy[0]));
     }
 
@@ -923,6 +1033,8 @@ int ft_moe_init_pool(const ft_moe_config* cfg, const ft_moe_weights* wts, ft_moe
     }
     const char* fault = std::getenv("FT_MOE_FAULT");
     if (fault && std::strncmp(fault, "copy:", 5) == 0) p->fault_copy = std::atoll(fault + 5);
+    if (fault && std::strncmp(fault, "work_alloc:", 11) == 0) p->fault_work_alloc = std::atoi(fault + 11);
+    if (fault && std::strncmp(fault, "mx_alloc:", 9) == 0) p->fault_mx_alloc = std::atoi(fault + 9);
 
     // ---- pinned host store: one entry per distinct (blob pointer, format)
     std::map<std::pair<const void*, int>, int64_t> seen;
@@ -1015,7 +1127,8 @@ int ft_moe_init_pool(const ft_moe_config* cfg, const ft_moe_weights* wts, ft_moe
         (rc = dev_alloc(&p->glist, E + 2)) || (rc = dev_alloc(&p->gdesc, E + 2)) ||
         (rc = dev_alloc(&p->count_max, 1)) || (rc = dev_alloc(&p->dev_header, 16)) ||
         (rc = dev_alloc(&p->fail_dev, 2 * E + 2)) || (rc = dev_alloc(&p->key_off_dev, int64_t(L) * E)) ||
-        (rc = dev_alloc(&p->prof_cnt_dev, 24))) {
+        (rc = dev_alloc(&p->prof_cnt_dev, 24)) || (rc = dev_alloc(&p->copy_clk, 3)) ||
+        (rc = dev_alloc(&p->copy_ticks, L))) {
       ft_moe_destroy_pool(p.release());
       return rc;
     }
@@ -1027,6 +1140,15 @@ int ft_moe_init_pool(const ft_moe_config* cfg, const ft_moe_weights* wts, ft_moe
     FT_HIP_CHECK(hipMemset(p->tab.clock, 0, 8));
     FT_HIP_CHECK(hipMemset(p->tab.stats, 0, size_t(L) * ST_COUNT * 8));
     FT_HIP_CHECK(hipMemset(p->prof_cnt_dev, 0, 24 * 8));
+    FT_HIP_CHECK(hipMemset(p->copy_ticks, 0, size_t(L) * 8));
+    {
+      const uint64_t clk0[3] = {~0ull, 0ull, 0ull};
+      FT_HIP_CHECK(hipMemcpy(p->copy_clk, clk0, sizeof(clk0), hipMemcpyHostToDevice));
+      int khz = 0;
+      FT_HIP_CHECK(hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, p->device));
+      p->wall_khz = double(khz);
+      p->copy_ms_host.assign(L, 0.0);
+    }
     {
       const int32_t big = INT32_MAX;
       FT_HIP_CHECK(hipMemcpy(p->count_max, &big, 4, hipMemcpyHostToDevice));
@@ -1172,7 +1294,10 @@ int ft_moe_pool_stats(ft_moe_pool* p, int32_t layer, ft_moe_stats* out, int32_t 
   std::vector<uint64_t> st(size_t(p->L) * ST_COUNT);
   std::vector<double> g(p->L);
   std::vector<int32_t> sk(p->C);
+  std::vector<uint64_t> ticks(p->L);
+  copy_drain(p, true);
   FT_HIP_CHECK(hipMemcpy(st.data(), p->tab.stats, st.size() * 8, hipMemcpyDeviceToHost));
+  FT_HIP_CHECK(hipMemcpy(ticks.data(), p->copy_ticks, ticks.size() * 8, hipMemcpyDeviceToHost));
   FT_HIP_CHECK(hipMemcpy(g.data(), p->tab.min_gap, g.size() * 8, hipMemcpyDeviceToHost));
   FT_HIP_CHECK(hipMemcpy(sk.data(), p->tab.slot_key, sk.size() * 4, hipMemcpyDeviceToHost));
   std::memset(out, 0, sizeof(*out));
@@ -1189,11 +1314,14 @@ int ft_moe_pool_stats(ft_moe_pool* p, int32_t layer, ft_moe_stats* out, int32_t 
     out->bytes_h2d += s[ST_BYTES_H2D];
     out->calls += s[ST_CALLS];
     out->min_topk_gap = std::min(out->min_topk_gap, g[l]);
+    out->copy_ms += (p->wall_khz > 0 ? double(ticks[l]) / p->wall_khz : 0.0) + p->copy_ms_host[l];
   }
   out->slots_total = p->C;
   for (int32_t v : sk) out->slots_used += v >= 0;
   if (reset) {
     FT_HIP_CHECK(hipMemset(p->tab.stats, 0, st.size() * 8));
+    FT_HIP_CHECK(hipMemset(p->copy_ticks, 0, ticks.size() * 8));
+    std::fill(p->copy_ms_host.begin(), p->copy_ms_host.end(), 0.0);
     std::vector<double> inf(p->L, INFINITY);
     FT_HIP_CHECK(hipMemcpy(p->tab.min_gap, inf.data(), inf.size() * 8, hipMemcpyHostToDevice));
   }
@@ -1437,6 +1565,7 @@ int ft_moe_decide_mode(ft_moe_mode_report* r) {
   }
   r->t_stream = ts;
   r->t_cpu = tc;
+  r->balanced_share = ts / (ts + tc);
   if (r->pool_slots >= r->all_experts) {
     r->mode = FT_MODE_FUSED;
     r->share = 0.0;
@@ -1640,6 +1769,7 @@ void ft_moe_destroy_pool(ft_moe_pool* p) {
   DeviceGuard dg(p->device);
   (void)hipDeviceSynchronize();
   prof_drain(p, true);
+  copy_drain(p, true);
   for (hipEvent_t e : p->prof_free) hipEventDestroy(e);
   hipFree(p->arena); hipFree(p->shared_dev); hipFree(p->router_dev);
   hipFree(p->tab.key2slot); hipFree(p->tab.slot_key); hipFree(p->tab.slot_last); hipFree(p->tab.lru[0]);
@@ -1648,7 +1778,7 @@ void ft_moe_destroy_pool(ft_moe_pool* p) {
   hipFree(p->z); hipFree(p->sel); hipFree(p->w); hipFree(p->gap); hipFree(p->pair_flag); hipFree(p->pair_slot);
   hipFree(p->pair_row); hipFree(p->row_tok); hipFree(p->row_w); hipFree(p->groups); hipFree(p->glist); hipFree(p->gdesc); hipFree(p->count_max);
   hipFree(p->dev_header); hipFree(p->hbuf); hipFree(p->pbuf); hipFree(p->fail_dev);
-  hipFree(p->key_off_dev); hipFree(p->prof_cnt_dev);
+  hipFree(p->key_off_dev); hipFree(p->prof_cnt_dev); hipFree(p->copy_clk); hipFree(p->copy_ticks);
   hipFree(p->row_slot); hipFree(p->tiles); hipFree(p->xq_codes); hipFree(p->xq_scales);
   hipFree(p->tq_codes); hipFree(p->tq_scales);
   hipFree(p->hq_codes); hipFree(p->hq_scales);

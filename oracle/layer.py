@@ -48,7 +48,7 @@ class OracleLayerStack:
 
     def __init__(self, w: ms.Workload, pool_slots: Optional[int] = None, share: float = 0.0,
                  act_mode: int = ffn.ACT_BF16, blob_fn: Optional[Callable] = None,
-                 dequant_items: int = 64):
+                 dequant_items: int = 64, threads: int = 1):
         self.w = w
         self.C = w.pool_slots if pool_slots is None else pool_slots
         self.pool = LRUPool(self.C)
@@ -57,6 +57,10 @@ class OracleLayerStack:
         self._router = {}
         self._blob_fn = blob_fn or (lambda l, e: ms.expert_blob(w, l, e))
         self.deq = DequantCache(dequant_items)
+        # threads > 1: the distinct experts of a call are dequantised
+        # concurrently, `threads` at a time (independent work; the arithmetic
+        # and the order of every sum are unchanged)
+        self.threads = max(1, int(threads))
         self.stats = dict(pair_hits=0, pair_misses=0, expert_hits=0, expert_misses=0,
                           cpu_misses=0, evictions=0, bytes_h2d=0, calls=0)
 
@@ -124,15 +128,30 @@ class OracleLayerStack:
                 res["out_tokens"] = tk
         return res
 
+    def _mats_of(self, layer, experts):
+        """Dequantised matrices of several experts of one layer."""
+        if self.threads == 1 or len(experts) == 1:
+            return [self.expert_mats(layer, int(e)) for e in experts]
+        from concurrent.futures import ThreadPoolExecutor
+
+        with ThreadPoolExecutor(self.threads) as ex:
+            return list(ex.map(lambda e: self.expert_mats_uncached(layer, int(e)), experts))
+
+    def expert_mats_uncached(self, layer, e):
+        w = self.w
+        return formats.dequant_expert(w.fmt(layer), self._blob_fn(layer, e), w.hidden, w.inter)
+
     def outputs(self, layer, x, sel, wts):
         w = self.w
         T, k = sel.shape
         p = np.zeros((T, k, w.hidden), np.float64)
-        for e in np.unique(sel):
-            rows = np.argwhere(sel == e)  # (t, j) pairs
-            wg, wu, wd = self.expert_mats(layer, int(e))
-            y = ffn.expert_forward(x[rows[:, 0]], wg, wu, wd, self.act_mode)
-            p[rows[:, 0], rows[:, 1]] = ffn.weighted_rows(y, wts[rows[:, 0], rows[:, 1]])
+        experts = np.unique(sel)
+        for c0 in range(0, len(experts), self.threads):
+            chunk = experts[c0:c0 + self.threads]
+            for e, (wg, wu, wd) in zip(chunk, self._mats_of(layer, chunk)):
+                rows = np.argwhere(sel == e)  # (t, j) pairs
+                y = ffn.expert_forward(x[rows[:, 0]], wg, wu, wd, self.act_mode)
+                p[rows[:, 0], rows[:, 1]] = ffn.weighted_rows(y, wts[rows[:, 0], rows[:, 1]])
         shared = None
         if w.shared_expert:
             sg, su, sd = self.shared_mats(layer)

@@ -30,6 +30,9 @@ Readings where the pages stop short:
   both paths finish together, m*share*t_cpu = m*(1 - share)*t_stream, i.e.
   share = t_stream / (t_stream + t_cpu).  offload and fused use share 0.  The
   pages' "cpu" strategy is share 1, chosen by the user, never by this rule.
+  The same split (balanced_share) is reported for every mode, for a caller
+  that picks the hybrid strategy itself (a workload whose configuration names
+  a host/PCIe split uses it).
 
 Pins: tests/test_oracle_mode.py (hand-worked cases in exact fractions, the
 balance property, the fused bound, the measured-machine case).
@@ -52,10 +55,11 @@ def choose_mode(layer_fmt: Sequence[int], expert_bytes: Dict[int, float], h2d: D
         b = expert_bytes[f]
         t_stream += b / h2d[f] + b / gpu[f]
         t_cpu += b / cpu[f]
+    balanced = t_stream / (t_stream + t_cpu)
     if pool_slots >= len(layer_fmt) * num_experts:
         mode, share = FUSED, 0.0
     elif t_cpu < t_stream:
         mode, share = HYBRID, t_stream / (t_stream + t_cpu)
     else:
         mode, share = OFFLOAD, 0.0
-    return dict(mode=mode, share=share, t_stream=t_stream, t_cpu=t_cpu)
+    return dict(mode=mode, share=share, t_stream=t_stream, t_cpu=t_cpu, balanced_share=balanced)

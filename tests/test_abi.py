@@ -28,11 +28,39 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, name), name
 
 
-def test_struct_sizes_match_header_layout():
-    # int32 x6, pointer, int64 x2, double, int32 x2
-    assert ctypes.sizeof(ft.ft_moe_config) == 6 * 4 + 8 + 8 + 8 + 8 + 4 + 4
-    assert ctypes.sizeof(ft.ft_moe_stats) == 8 * 8 + 8 + 8 + 8
-    assert ctypes.sizeof(ft.ft_moe_trace) == 5 * 8
+def _c_layout(structs):
+    """Sizes and field offsets of header structs, as gcc lays them out."""
+    import shutil
+    import subprocess
+    import tempfile
+
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "ftmoe.h"', "int main(void) {"]
+    for st, fields in structs.items():
+        lines.append(f'  printf("{st} size %zu\\n", sizeof({st}));')
+        for f in fields:
+            lines.append(f'  printf("{st} {f} %zu\\n", offsetof({st}, {f}));')
+    lines += ["  return 0;", "}"]
+    with tempfile.TemporaryDirectory() as d:
+        src, exe = os.path.join(d, "l.c"), os.path.join(d, "l")
+        open(src, "w").write("\n".join(lines) + "\n")
+        subprocess.run([cc, "-I", os.path.join(ROOT, "include"), src, "-o", exe], check=True)
+        out = subprocess.run([exe], check=True, capture_output=True, text=True).stdout
+    return {tuple(l.split()[:2]): int(l.split()[2]) for l in out.splitlines()}
+
+
+def test_struct_layouts_match_header():
+    # every struct the binding declares, field by field, against the C compiler
+    structs = {"ft_moe_config": ft.ft_moe_config, "ft_moe_weights": ft.ft_moe_weights,
+               "ft_moe_trace": ft.ft_moe_trace, "ft_moe_stats": ft.ft_moe_stats,
+               "ft_moe_mode_report": ft.ft_moe_mode_report, "ft_moe_profile": ft.ft_moe_profile}
+    c = _c_layout({n: [f for f, _ in t._fields_] for n, t in structs.items()})
+    for n, t in structs.items():
+        assert c[(n, "size")] == ctypes.sizeof(t), n
+        for f, _ in t._fields_:
+            assert c[(n, f)] == getattr(t, f).offset, (n, f)
 
 
 def test_profile_stages_match_header():

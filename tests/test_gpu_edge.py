@@ -186,12 +186,7 @@ def test_prefill_mx_activation_modes_small(shared, act):
     mode = OFFN.ACT_MXFP4 if act == "mxfp4" else OFFN.ACT_MXFP8
     rels = _act_case(shared, mode)
     print(act, "shared" if shared else "", "rel-L2", rels)
-    # x is quantised identically on both sides; h may land on the other side of
-    # an element rounding boundary when its bf16 value differs by a bit (fp32
-    # accumulation vs fp64; with 8-bit operands the block-scaled MFMA also sums
-    # each block with fewer bits than fp32), which moves single elements by one
-    # grid step
-    assert max(rels) <= (2e-3 if act == "mxfp8" else 6e-3)
+    assert max(rels) <= 2e-3
 
 
 @pytest.mark.parametrize("act", ["mxfp8", "mxfp4"])
@@ -204,7 +199,7 @@ def test_prefill_mx_narrow_workgroup_tiles(act):
     mode = OFFN.ACT_MXFP4 if act == "mxfp4" else OFFN.ACT_MXFP8
     rels = _act_case(True, mode, H=384, T=600, cfg_id=124)
     print(act, "rel-L2", rels)
-    assert max(rels) <= (2e-3 if act == "mxfp8" else 6e-3)
+    assert max(rels) <= 2e-3
 
 
 def test_prefill_bf16_wide_wave_tiles():
@@ -265,8 +260,73 @@ def test_device_driven_and_host_driven_decode_agree():
         assert ft.ft_moe_last_misses(gd.pool) == ft.ft_moe_last_misses(gh.pool)
         compare_table(gd, o)
         sh, sd = ft.ft_moe_pool_stats(gh.pool), ft.ft_moe_pool_stats(gd.pool)
+        # copy time is measured, not computed: both paths report some
+        assert sh.pop("copy_ms") > 0 and sd.pop("copy_ms") > 0
         assert sh == sd, (sh, sd)
         assert sd["evictions"] > 0 and sd["pair_hits"] > 0
     finally:
         gh.close()
         gd.close()
+
+
+def test_failed_work_buffer_allocation_recovers(monkeypatch):
+    """A device allocation of the per-call buffers fails (injected): the call
+    returns FT_E_OOM_DEVICE before any work is enqueued, and the next call
+    allocates the buffers again and matches the oracle."""
+    import torch
+    from tests.moe_case import GpuLayerStack, compare_call, compare_table
+    import lru_expert_cache_amd as ft
+
+    w = _small(114, 2, 256, 128, 8, 2, [MX, NV], 16)
+    monkeypatch.setenv("FT_MOE_FAULT", "work_alloc:5")
+    g = GpuLayerStack(w)
+    monkeypatch.delenv("FT_MOE_FAULT")
+    o = OracleLayerStack(w, pool_slots=g.C)
+    try:
+        x_bits = ms.activations(w, 0, 0, 100)  # more than the 64 tokens buffers start with
+        x = torch.from_numpy(x_bits.view(np.int16)).cuda()
+        with pytest.raises(ft.FtError) as ei:
+            ft.ft_moe_layer_forward(g.pool, 0, 100, x, None, torch.empty_like(x), ft.FT_FWD_DECODE)
+        assert ei.value.code == ft.FT_E_OOM_DEVICE and "injected" in str(ei.value)
+        for l in range(2):
+            xb = ms.activations(w, l, 0, 100)
+            compare_call(g.forward(l, xb, g.bias(l, 0)), o.forward(l, xb, ms.popularity_bias(w, l, 0)), 2)
+        compare_table(g, o)
+        st = ft.ft_moe_pool_stats(g.pool)
+        assert st["calls"] == o.stats["calls"] and st["bytes_h2d"] == o.stats["bytes_h2d"]
+    finally:
+        g.close()
+
+
+@pytest.mark.parametrize("which", [1, 3, 4])
+def test_failed_mx_tile_allocation_recovers(monkeypatch, which):
+    """One of the four MX activation-tile buffers fails to allocate
+    (injected): the prefill call returns FT_E_OOM_DEVICE with none of them
+    left allocated, and the retried chunk allocates all four and matches the
+    oracle."""
+    import torch
+    from tests.moe_case import GpuLayerStack, compare_call, rel_l2
+    from oracle import ffn as OFFN, formats as OF
+    import lru_expert_cache_amd as ft
+
+    w = _small(115, 2, 256, 256, 8, 2, [MX, MX], 16)
+    monkeypatch.setenv("FT_MOE_FAULT", f"mx_alloc:{which}")
+    g = GpuLayerStack(w)
+    monkeypatch.delenv("FT_MOE_FAULT")
+    o = OracleLayerStack(w, pool_slots=g.C, act_mode=OFFN.ACT_MXFP4)
+    try:
+        x_bits = ms.activations(w, 0, 3, 200)
+        x = torch.from_numpy(x_bits.view(np.int16)).cuda()
+        with pytest.raises(ft.FtError) as ei:
+            ft.ft_moe_layer_forward(g.pool, 0, 200, x, None, torch.empty_like(x),
+                                    ft.FT_FWD_PREFILL_STAGED | ft.FT_ACT_MXFP4)
+        assert ei.value.code == ft.FT_E_OOM_DEVICE and "injected" in str(ei.value)
+        torch.cuda.synchronize()
+        for l in range(2):
+            xb = ms.activations(w, l, 3, 200)
+            gr = g.forward(l, xb, g.bias(l, 0), prefill=True, act=ft.FT_ACT_MXFP4)
+            orr = o.forward(l, xb, ms.popularity_bias(w, l, 0), prefill=True)
+            compare_call(gr, orr, 2, check_out=False)
+            assert rel_l2(OF.bf16_from_bits(gr["out_bits"]), orr["out"]) <= 2e-3
+    finally:
+        g.close()

@@ -73,6 +73,8 @@ def test_captured_decode_step_replays_like_eager_calls():
         assert np.array_equal(ka, ke) and np.array_equal(la, le) and ca == ce
         compare_table(ga, o)
         sa, se = ft.ft_moe_pool_stats(ga.pool), ft.ft_moe_pool_stats(ge.pool)
+        # copy time is measured (also inside replays, on the device clock), not computed
+        assert sa.pop("copy_ms") > 0 and se.pop("copy_ms") > 0
         assert sa == se, (sa, se)
         for key in ("pair_hits", "pair_misses", "expert_hits", "expert_misses", "evictions", "bytes_h2d", "calls"):
             assert sa[key] == o.stats[key], (key, sa[key], o.stats[key])

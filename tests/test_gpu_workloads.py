@@ -3,8 +3,11 @@ the benchmark uses (whole layer stacks, the pool sizes of each workload).
 
 Decisions (experts, weights, hit/miss flags, slots, miss lists, grouped row
 order) are compared exactly on every call; outputs (rel-L2 <= 2e-3, bf16) on
-sampled calls the oracle computes one by one.
+every row of sampled calls the oracle computes one by one (the prefill chunk:
+on sampled rows).
 """
+
+import os
 
 import numpy as np
 import pytest
@@ -15,6 +18,8 @@ from oracle.layer import OracleLayerStack
 pytestmark = pytest.mark.gpu
 
 _STORES = {}
+# the oracle dequantises the distinct experts of a sampled call this many at a time
+THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 
 
 def _decode_run(w, T, steps, sample, share=0.0, store=None, layers_out=None):
@@ -43,6 +48,11 @@ def _decode_run(w, T, steps, sample, share=0.0, store=None, layers_out=None):
                     "bytes_h2d", "calls"):
             assert st[key] == o.stats[key], (key, st[key], o.stats[key])
         assert st["min_topk_gap"] > 1e-9
+        # copy time: the streamed bytes over it is a plausible host-to-device rate
+        if st["bytes_h2d"] > 0:
+            rate = st["bytes_h2d"] / (st["copy_ms"] * 1e-3)
+            print(f"copy {st['copy_ms']:.1f} ms, {rate / 1e9:.1f} GB/s")
+            assert 1e9 < rate < 200e9, rate
         return rels, st
     finally:
         g.close()
@@ -65,7 +75,7 @@ def test_qwen_a3b_decode(qwen_store, T):
 
 
 @pytest.mark.timeout(1200)
-@pytest.mark.parametrize("T,steps", [(1, 2), (8, 2), (64, 1)])
+@pytest.mark.parametrize("T,steps", [(1, 2), (8, 2), (32, 1), (64, 1)])
 def test_deepseek_decode_nvfp4_shared(T, steps):
     w = ms.workload("deepseek-v4-flash-decode")
     from tests.moe_case import GpuLayerStack, compare_call, compare_table
@@ -75,7 +85,8 @@ def test_deepseek_decode_nvfp4_shared(T, steps):
         _STORES[w.name] = ms.BlobStore(w)
     store = _STORES[w.name]
     g = GpuLayerStack(w, store=store)
-    o = OracleLayerStack(w, pool_slots=g.C, blob_fn=lambda l, e: store.expert(l, e), dequant_items=24)
+    o = OracleLayerStack(w, pool_slots=g.C, blob_fn=lambda l, e: store.expert(l, e), dequant_items=24,
+                         threads=THREADS)
     try:
         rels = []
         for s in range(steps):
@@ -84,7 +95,7 @@ def test_deepseek_decode_nvfp4_shared(T, steps):
                 b = ms.popularity_bias(w, l, 0)
                 want = (s, l) in {(0, 0), (steps - 1, 60)}
                 gr = g.forward(l, x, g.bias(l, s))
-                orr = o.forward(l, x, b, outputs=want, out_tokens=[0, T - 1] if want else None)
+                orr = o.forward(l, x, b, outputs=want)
                 r = compare_call(gr, orr, w.top_k, check_out=want)
                 if r is not None:
                     rels.append(r)
@@ -93,23 +104,31 @@ def test_deepseek_decode_nvfp4_shared(T, steps):
         st = ft.ft_moe_pool_stats(g.pool)
         for key in ("pair_hits", "pair_misses", "expert_misses", "evictions", "bytes_h2d", "calls"):
             assert st[key] == o.stats[key], key
+        assert len(rels) == 2
         print("rel-L2", rels, st)
     finally:
         g.close()
 
 
-
 @pytest.mark.timeout(1200)
 def test_glm_mixed_formats_hybrid():
+    """The GLM-shaped stack at the hybrid share the library measures on this
+    machine (ft_moe_measure_mode's balanced share: streamed and host-computed
+    misses finish together)."""
     w = ms.workload("glm-5.2-mixed-decode")
     from tests.moe_case import GpuLayerStack, compare_call, compare_table
     import lru_expert_cache_amd as ft
 
     store = ms.BlobStore(w)
-    share = 0.02
-    g = GpuLayerStack(w, store=store, share=share)
-    o = OracleLayerStack(w, pool_slots=g.C, share=share, blob_fn=lambda l, e: store.expert(l, e), dequant_items=24)
     T = 32
+    g = GpuLayerStack(w, store=store)
+    rep = ft.ft_moe_measure_mode(g.pool, max(1, T * w.top_k // 64))
+    share = rep["balanced_share"]
+    print("measured mode", ["offload", "hybrid", "fused"][rep["mode"]], "balanced share", share)
+    assert 0.0 < share < 1.0
+    ft.ft_moe_set_hybrid_share(g.pool, share)
+    o = OracleLayerStack(w, pool_slots=g.C, share=share, blob_fn=lambda l, e: store.expert(l, e), dequant_items=24,
+                         threads=THREADS)
     try:
         rels = []
         for s in (0, 33):  # two popularity phases
@@ -118,7 +137,7 @@ def test_glm_mixed_formats_hybrid():
                 b = ms.popularity_bias(w, l, w.phase(s))
                 want = (s, l) in {(0, 0), (0, 1), (33, 90), (33, 91)}
                 gr = g.forward(l, x, g.bias(l, s))
-                orr = o.forward(l, x, b, outputs=want, out_tokens=[3, 17] if want else None)
+                orr = o.forward(l, x, b, outputs=want)
                 r = compare_call(gr, orr, w.top_k, check_out=want)
                 if r is not None:
                     rels.append(r)
@@ -127,7 +146,7 @@ def test_glm_mixed_formats_hybrid():
         st = ft.ft_moe_pool_stats(g.pool)
         for key in ("pair_hits", "pair_misses", "expert_misses", "cpu_misses", "evictions", "bytes_h2d", "calls"):
             assert st[key] == o.stats[key], key
-        assert st["cpu_misses"] > 0
+        assert st["cpu_misses"] > 0 and len(rels) == 4
         print("rel-L2", rels, st)
     finally:
         g.close()
@@ -191,7 +210,7 @@ def test_qwen_a3b_prefill_4096_mx_activations(qwen_store, act):
             toks = np.sort(rng.choice(T, 16, replace=False)) if want else None
             gr = g.forward(l, x, g.bias(l, 0), prefill=True, act=flag)
             orr = o.forward(l, x, b, prefill=True, outputs=want, out_tokens=toks)
-            r = compare_call(gr, orr, w.top_k, check_out=want, tol=2e-3 if act == "mxfp8" else 6e-3)
+            r = compare_call(gr, orr, w.top_k, check_out=want)
             if r is not None:
                 rels.append(r)
         print(act, "rel-L2", rels)

@@ -49,6 +49,7 @@ def test_library_rule_matches_oracle():
                            C, E)
         assert math.isclose(got["t_stream"], want["t_stream"], rel_tol=1e-12)
         assert math.isclose(got["t_cpu"], want["t_cpu"], rel_tol=1e-12)
+        assert math.isclose(got["balanced_share"], want["balanced_share"], rel_tol=1e-12)
         # the decision is taken on the same totals unless they tie within rounding
         if abs(want["t_cpu"] - want["t_stream"]) > 1e-9 * want["t_stream"]:
             assert got["mode"] == want["mode"], case

@@ -84,3 +84,17 @@ def test_hybrid_share_balances_the_two_paths(h, g, c, b):
         assert cpu_time < m * float(min(tc, ts))
     else:
         assert r["mode"] == OFFLOAD and r["share"] == 0.0
+
+
+def test_balanced_share_is_reported_for_every_mode():
+    # one layer, b = 1 byte: streamed 1/3 + 1/6 = 1/2 s, host 1 s -> offload,
+    # and the split at which both paths finish together is (1/2) / (3/2) = 1/3
+    r = choose_mode([MX], {MX: 1.0}, {MX: 3.0}, {MX: 6.0}, {MX: 1.0}, 1, 2)
+    assert r["mode"] == OFFLOAD and r["share"] == 0.0
+    assert abs(r["balanced_share"] - 1 / 3) < 1e-15
+    # m misses split at that share: m/3 on the host take m/3 s, 2m/3 streamed take m/3 s
+    m = 9.0
+    assert abs(m * r["balanced_share"] * r["t_cpu"] - m * (1 - r["balanced_share"]) * r["t_stream"]) < 1e-12
+    # a hybrid decision reports the same split as its share
+    r2 = choose_mode([MX], {MX: 1.0}, {MX: 3.0}, {MX: 6.0}, {MX: 4.0}, 1, 2)
+    assert r2["mode"] == HYBRID and r2["share"] == r2["balanced_share"] == 0.5 / 0.75
