@@ -176,6 +176,30 @@ int ft_moe_layer_forward(ft_moe_pool *p, int32_t layer, int32_t num_tokens, cons
                          const float *router_bias, void *out_bf16, int32_t flags, void *hip_stream,
                          ft_moe_trace *trace);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * ft_moe_layer_forward for a device-driven decode call -- flags ==
+ * FT_FWD_DECODE, no hybrid share, T * top_k <= pool slots, the device path
+ * not switched off by FT_MOE_DECODE_PATH=host -- whose per-call work buffers
+ * (logits, routing, pair and row records, h and p rows) are carved from one
+ * static device array of 16 MiB per GPU instead of the pool's own buffers.
+ * It calls no hipMalloc, hipFree or other allocating routine and creates no
+ * events (stage timing is off for these calls); the pool, the caller's x,
+ * out, router_bias and trace are used as in ft_moe_layer_forward, and the
+ * slot table, counters and outputs are the same.  Limits: the call must fit
+ * the array (about 170 KB per token at H 7168, I 2048, top-8 with a shared
+ * expert: 64 tokens fit), else FT_E_INVALID with the bytes it needs; any
+ * other kind of call is FT_E_INVALID.  The array's device address is looked
+ * up once per GPU at pool creation (FT_E_HIP if that failed).
+ * ft_moe_last_misses does not report these calls (it keeps the previous
+ * call's lists).  Every call of this entry point on one GPU -- any pool, any
+ * stream, any host thread -- uses the same array and leaves its contents
+ * behind: calls that overlap in time on one GPU race and must be ordered by
+ * the caller (one stream, or events). */
+int ft_moe_layer_forward_noalloc(ft_moe_pool *p, int32_t layer, int32_t num_tokens, const void *x_bf16,
+                                 const float *router_bias, void *out_bf16, int32_t flags, void *hip_stream,
+                                 ft_moe_trace *trace);
+
 /* Counters of one layer (or all layers for layer = -1); synchronises the
  * pool's device.  reset != 0 zeroes the counters afterwards. */
 int ft_moe_pool_stats(ft_moe_pool *p, int32_t layer, ft_moe_stats *out, int32_t reset);

@@ -36,7 +36,7 @@ EXPORTED = ["ft_moe_init_pool", "ft_moe_layer_forward", "ft_moe_pool_stats", "ft
             "ft_moe_pool_table", "ft_moe_set_hybrid_share", "ft_moe_host_expert_rate",
             "ft_moe_set_profiling", "ft_moe_profile_read", "ft_moe_destroy_pool", "ft_moe_last_error",
             "ft_moe_reserve", "ft_moe_resize_pool", "ft_moe_decide_mode", "ft_moe_measure_mode",
-            "ft_moe_ffn_kernel_name", "ft_moe_mfma_rate"]
+            "ft_moe_ffn_kernel_name", "ft_moe_mfma_rate", "ft_moe_layer_forward_noalloc"]
 
 FT_MODE_OFFLOAD, FT_MODE_HYBRID, FT_MODE_FUSED = 0, 1, 2
 
@@ -113,6 +113,8 @@ def lib() -> ctypes.CDLL:
     L.ft_moe_layer_forward.argtypes = [P, ctypes.c_int32, ctypes.c_int32, P, P, P, ctypes.c_int32, P,
                                        ctypes.POINTER(ft_moe_trace)]
     L.ft_moe_layer_forward.restype = ctypes.c_int
+    L.ft_moe_layer_forward_noalloc.argtypes = L.ft_moe_layer_forward.argtypes
+    L.ft_moe_layer_forward_noalloc.restype = ctypes.c_int
     L.ft_moe_pool_stats.argtypes = [P, ctypes.c_int32, ctypes.POINTER(ft_moe_stats), ctypes.c_int32]
     L.ft_moe_pool_stats.restype = ctypes.c_int
     I32P = ctypes.POINTER(ctypes.c_int32)
@@ -216,6 +218,22 @@ def ft_moe_layer_forward(pool, layer: int, num_tokens: int, x, router_bias, out,
         s = stream if isinstance(stream, int) else int(stream.cuda_stream)
     rc = lib().ft_moe_layer_forward(pool, int(layer), int(num_tokens), _ptr(x), _ptr(router_bias), _ptr(out),
                                     int(flags), s, ctypes.byref(tr) if tr is not None else None)
+    return _check(rc)
+
+
+def ft_moe_layer_forward_noalloc(pool, layer: int, num_tokens: int, x, router_bias, out, flags: int = 0,
+                                 stream=None, trace: Optional[dict] = None) -> int:
+    """ft_moe_layer_forward for a device-driven decode call, with its work
+    buffers in the library's static per-GPU scratch (no allocation)."""
+    tr = None
+    if trace is not None:
+        tr = ft_moe_trace(_ptr(trace.get("sel")), _ptr(trace.get("w")), _ptr(trace.get("slot")),
+                          _ptr(trace.get("flag")), _ptr(trace.get("row")))
+    s = 0
+    if stream is not None:
+        s = stream if isinstance(stream, int) else int(stream.cuda_stream)
+    rc = lib().ft_moe_layer_forward_noalloc(pool, int(layer), int(num_tokens), _ptr(x), _ptr(router_bias), _ptr(out),
+                                            int(flags), s, ctypes.byref(tr) if tr is not None else None)
     return _check(rc)
 
 

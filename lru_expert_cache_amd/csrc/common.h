@@ -311,6 +311,14 @@ double mfma_peak_flops(int kind, int iters);
 hipError_t launch_mfma_peak(int kind, int iters, int seed, float* out, hipStream_t s);
 size_t mfma_peak_out_bytes();
 
+// noalloc.hip: the static scratch array of ft_moe_layer_forward_noalloc (one
+// per GPU).  scratch_register_device looks up its device address on `device`
+// (which must be current) once; scratch_device_ptr returns the kept address
+// (null before registration or after a failed one).
+constexpr int64_t kScratchBytes = int64_t(16) << 20;
+int scratch_register_device(int device);
+uint8_t* scratch_device_ptr(int device);
+
 // ------------------------------------------------------------ errors
 void set_error(const char* fmt, ...);
 const char* get_error();

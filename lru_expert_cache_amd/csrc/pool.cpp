@@ -1063,6 +1063,12 @@ int ft_moe_init_pool(const ft_moe_config* cfg, const ft_moe_weights* wts, ft_moe
     }
     p->host_bytes = off;
     DeviceGuard dg(p->device);
+    // the static scratch of ft_moe_layer_forward_noalloc: its device address
+    // on this device, looked up once (a failure is reported by that call)
+    {
+      const std::string keep = get_error();
+      if (scratch_register_device(p->device) != FT_OK) set_error("%s", keep.c_str());
+    }
     if (fault && std::strcmp(fault, "pinned_alloc") == 0) {
       set_error("injected pinned allocation failure (%lld bytes)", (long long)off);
       return FT_E_OOM_PINNED;
@@ -1186,10 +1192,76 @@ int ft_moe_init_pool(const ft_moe_config* cfg, const ft_moe_weights* wts, ft_moe
   }
 }
 
-int ft_moe_layer_forward(ft_moe_pool* p, int32_t layer, int32_t num_tokens, const void* x_bf16,
-                         const float* router_bias, void* out_bf16, int32_t flags, void* hip_stream,
-                         ft_moe_trace* trace) {
-  try {
+}  // extern "C"
+
+namespace {
+
+// Per-call buffers of a device-driven decode call carved from `base` (256-byte
+// aligned regions, in this order); with base null only the size is computed.
+struct ScratchCarve {
+  double* z;
+  int32_t *sel, *pair_slot, *pair_row, *row_tok;
+  float *w, *row_w;
+  double* gap;
+  uint8_t* pair_flag;
+  uint16_t *hbuf, *pbuf;
+  int64_t bytes;
+};
+
+ScratchCarve carve_scratch(const ft_moe_pool* p, int T, uint8_t* base) {
+  ScratchCarve c{};
+  int64_t off = 0;
+  auto take = [&](int64_t n) -> uint8_t* {
+    uint8_t* q = base ? base + off : nullptr;
+    off += (n + 255) & ~int64_t(255);
+    return q;
+  };
+  const int64_t pairs = int64_t(T) * p->k, rows = pairs + (p->shared ? T : 0);
+  c.z = reinterpret_cast<double*>(take(int64_t(T) * p->E * 8));
+  c.sel = reinterpret_cast<int32_t*>(take(pairs * 4));
+  c.w = reinterpret_cast<float*>(take(pairs * 4));
+  c.gap = reinterpret_cast<double*>(take(int64_t(T) * 8));
+  c.pair_flag = take(pairs);
+  c.pair_slot = reinterpret_cast<int32_t*>(take(pairs * 4));
+  c.pair_row = reinterpret_cast<int32_t*>(take(pairs * 4));
+  c.row_tok = reinterpret_cast<int32_t*>(take(rows * 4));
+  c.row_w = reinterpret_cast<float*>(take(rows * 4));
+  c.hbuf = reinterpret_cast<uint16_t*>(take(rows * p->I * 2));
+  c.pbuf = reinterpret_cast<uint16_t*>(take(rows * p->H * 2));
+  c.bytes = off;
+  return c;
+}
+
+// Points the pool's per-call buffers at a carve of the scratch for one call
+// (no mapped readback: the resolve kernel then publishes no miss lists) and
+// puts them back afterwards.
+struct ScratchView {
+  ft_moe_pool* p;
+  double *z, *gap;
+  int32_t *sel, *pair_slot, *pair_row, *row_tok;
+  float *w, *row_w;
+  uint8_t *pair_flag, *rb_dev;
+  uint16_t *hbuf, *pbuf;
+  bool last_pending;
+  ScratchView(ft_moe_pool* pp, const ScratchCarve& c)
+      : p(pp), z(pp->z), gap(pp->gap), sel(pp->sel), pair_slot(pp->pair_slot), pair_row(pp->pair_row),
+        row_tok(pp->row_tok), w(pp->w), row_w(pp->row_w), pair_flag(pp->pair_flag), rb_dev(pp->rb_dev),
+        hbuf(pp->hbuf), pbuf(pp->pbuf), last_pending(pp->last_pending) {
+    p->z = c.z; p->gap = c.gap; p->sel = c.sel; p->pair_slot = c.pair_slot; p->pair_row = c.pair_row;
+    p->row_tok = c.row_tok; p->w = c.w; p->row_w = c.row_w; p->pair_flag = c.pair_flag; p->rb_dev = nullptr;
+    p->hbuf = c.hbuf; p->pbuf = c.pbuf;
+  }
+  ~ScratchView() {
+    p->z = z; p->gap = gap; p->sel = sel; p->pair_slot = pair_slot; p->pair_row = pair_row; p->row_tok = row_tok;
+    p->w = w; p->row_w = row_w; p->pair_flag = pair_flag; p->rb_dev = rb_dev; p->hbuf = hbuf; p->pbuf = pbuf;
+    // the mapped readback still holds the lists of the call before this one
+    p->last_pending = last_pending;
+  }
+};
+
+int forward_impl(ft_moe_pool* p, int32_t layer, int32_t num_tokens, const void* x_bf16, const float* router_bias,
+                 void* out_bf16, int32_t flags, void* hip_stream, ft_moe_trace* trace, bool noalloc) {
+  {
     if (!p || !x_bf16 || !out_bf16) {
       set_error("NULL pool, x or out");
       return FT_E_INVALID;
@@ -1220,22 +1292,47 @@ int ft_moe_layer_forward(ft_moe_pool* p, int32_t layer, int32_t num_tokens, cons
       return FT_E_STATE;
     }
     if (num_tokens == 0) return FT_OK;
+    const int T = num_tokens, E = p->E, k = p->k;
+    const bool dev_path = mode == FT_FWD_DECODE && p->dev_decode && p->share == 0.0 && int64_t(T) * k <= p->C;
+    ScratchCarve carve{};
+    if (noalloc) {
+      if (!dev_path || flags != FT_FWD_DECODE) {
+        set_error("ft_moe_layer_forward_noalloc runs device-driven decode calls only: flags FT_FWD_DECODE, no "
+                  "hybrid share, T*top_k <= pool slots (T=%d, flags 0x%x, share %g)", T, flags, p->share);
+        return FT_E_INVALID;
+      }
+      carve = carve_scratch(p, T, nullptr);
+      if (carve.bytes > kScratchBytes) {
+        set_error("ft_moe_layer_forward_noalloc: %d tokens need %lld bytes of scratch, the maximum is %lld", T,
+                  (long long)carve.bytes, (long long)kScratchBytes);
+        return FT_E_INVALID;
+      }
+    }
     DeviceGuard dg(p->device);
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    const int T = num_tokens, E = p->E, k = p->k;
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     FT_HIP_CHECK(hipStreamIsCapturing(s, &cap));
     const bool capturing = cap != hipStreamCaptureStatusNone;
-    const bool dev_path = mode == FT_FWD_DECODE && p->dev_decode && p->share == 0.0 && int64_t(T) * k <= p->C;
-    if (capturing && (!dev_path || T > p->cap_T)) {
+    if (capturing && !noalloc && (!dev_path || T > p->cap_T)) {
       set_error("a captured call must be a device-driven decode call of at most the reserved %d tokens "
                 "(T=%d, mode %d)", p->cap_T, T, mode);
       return FT_E_INVALID;
     }
-    int rc = ensure_capacity(p, num_tokens);
-    if (rc) return rc;
+    int rc;
+    std::unique_ptr<ScratchView> view;
+    if (noalloc) {
+      uint8_t* base = scratch_device_ptr(p->device);
+      if (base == nullptr) {
+        if ((rc = scratch_register_device(p->device))) return rc;
+        base = scratch_device_ptr(p->device);
+      }
+      view = std::make_unique<ScratchView>(p, carve_scratch(p, T, base));
+    } else if ((rc = ensure_capacity(p, num_tokens))) {
+      return rc;
+    }
     const int32_t prof_saved = p->prof_mask;
-    if (capturing) p->prof_mask = 0;  // no event records inside a graph
+    // no event records inside a graph; the no-alloc call creates no events
+    if (capturing || noalloc) p->prof_mask = 0;
     struct Restore {
       ft_moe_pool* p;
       int32_t m;
@@ -1278,6 +1375,29 @@ int ft_moe_layer_forward(ft_moe_pool* p, int32_t layer, int32_t num_tokens, cons
       if (trace->row) FT_HIP_CHECK(hipMemcpyAsync(trace->row, p->pair_row, n * 4, hipMemcpyDeviceToDevice, s));
     }
     return FT_OK;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int ft_moe_layer_forward(ft_moe_pool* p, int32_t layer, int32_t num_tokens, const void* x_bf16,
+                         const float* router_bias, void* out_bf16, int32_t flags, void* hip_stream,
+                         ft_moe_trace* trace) {
+  try {
+    return forward_impl(p, layer, num_tokens, x_bf16, router_bias, out_bf16, flags, hip_stream, trace, false);
+  } catch (const std::exception& ex) {
+    set_error("forward failed: %s", ex.what());
+    return FT_E_INVALID;
+  }
+}
+
+int ft_moe_layer_forward_noalloc(ft_moe_pool* p, int32_t layer, int32_t num_tokens, const void* x_bf16,
+                                 const float* router_bias, void* out_bf16, int32_t flags, void* hip_stream,
+                                 ft_moe_trace* trace) {
+  try {
+    return forward_impl(p, layer, num_tokens, x_bf16, router_bias, out_bf16, flags, hip_stream, trace, true);
   } catch (const std::exception& ex) {
     set_error("forward failed: %s", ex.what());
     return FT_E_INVALID;
