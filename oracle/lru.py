@@ -28,7 +28,9 @@ Runtime").  Finer points are this build's readings:
   starts the copy of layer l+1 into the other half, residents of both halves
   are evicted (the second only if l+1 < L); the LRU order of other slots is
   untouched and the clock does not move (devpik article, "Long Prompts Are
-  the Bottleneck").
+  the Bottleneck").  With the hit-D2D option, resident experts are read in
+  place and the copied ones become residents of their staging slots (see
+  stage_layer).
 
 Pins (tests/test_oracle_lru.py): an independent brute-force list LRU,
 hand-worked traces, the compulsory-miss, inclusion and cyclic-thrash
@@ -150,10 +152,16 @@ class LRUPool:
         hit_d2d: experts of the layer already resident in the pool are not
         copied again; only the others cross PCIe (devpik article, "Long
         Prompts Are the Bottleneck": the prefill option that skips experts
-        already in the GPU cache).  Reading: a resident expert is used from
-        its pool slot (its pairs are HIT with that slot), residency is taken
-        after the staging halves are cleared (so it lies outside them), and
-        the LRU state is untouched as in plain staging.
+        already in the GPU cache).  Readings: a resident expert is used from
+        its pool slot (its pairs are HIT with that slot), and residency is
+        taken after the staging halves are cleared (so it lies outside them).
+        The copied experts become LRU residents of their staging slots (until
+        a later call clears that half), and the call updates the LRU order
+        like one decode wave over its pairs: the copied experts that no token
+        selects take the first clock ticks, in expert order; then every expert
+        the tokens select -- read in place or copied -- takes the clock at its
+        last pair; the clock advances by both counts.  Without hit_d2d the
+        LRU order, the clock and the staging slots' residency are untouched.
         """
         E = num_experts
         assert self.C >= 2 * E
@@ -177,11 +185,22 @@ class LRUPool:
         flag = np.array([HIT if int(e) in resident else MISS_STREAM for e in pairs], np.uint8)
         slot = np.array([resident.get(int(e), base + int(e)) for e in pairs], np.int32)
         D = []
-        seen = set()
-        for e in pairs:
-            if int(e) not in seen:
-                seen.add(int(e))
+        last_pos = {}
+        for p, e in enumerate(pairs):
+            if int(e) not in last_pos:
                 D.append(int(e))
+            last_pos[int(e)] = p
+        if hit_d2d:
+            copied = [e for e in range(E) if e not in resident]
+            for e in copied:
+                self.key_of[base + e] = (layer, e)
+                self.slot_of[(layer, e)] = base + e
+            unselected = [e for e in copied if e not in last_pos]
+            for i, e in enumerate(unselected):
+                self.last_use[base + e] = self.clock + i
+            for e in D:
+                self.last_use[self.slot_of[(layer, e)]] = self.clock + len(unselected) + last_pos[e]
+            self.clock += len(unselected) + len(pairs)
         return dict(flag=flag, slot=slot, stream=[(e, base + e) for e in range(E) if e not in resident], cpu=[],
                     D=D, pair_hits=int((flag == HIT).sum()), expert_hits=len(resident),
                     expert_misses=E - len(resident), cpu_misses=0, evictions=evictions)

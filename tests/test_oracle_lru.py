@@ -269,7 +269,13 @@ def test_prefill_hit_d2d_hand_worked():
     assert list(r["flag"]) == [HIT, MISS_STREAM, MISS_STREAM, HIT]
     assert r["stream"] == [(0, 0), (1, 1), (3, 3)]
     assert (r["pair_hits"], r["expert_hits"], r["expert_misses"]) == (2, 1, 3)
-    assert pool.resident(0, 2) and not pool.resident(0, 0)
+    # the copied experts 0, 1, 3 are residents of slots 0, 1, 3.  Clock 9 before
+    # the call: the unselected copied expert 1 takes tick 9; then the pairs
+    # [2, 0, 3, 2] (last positions 2->3, 0->1, 3->2) take 9 + 1 + position
+    key, last, clock = pool.snapshot()
+    assert key[:4] == [(0, 0), (0, 1), None, (0, 3)] and key[8] == (0, 2)
+    assert (last[0], last[1], last[3], last[8], clock) == (11, 9, 12, 13, 14)
+    assert all(k is None for k in key[4:8] + key[9:])
 
 
 def test_prefill_hit_d2d_uses_resident_slots():
@@ -293,10 +299,19 @@ def test_prefill_hit_d2d_uses_resident_slots():
     assert list(r1["flag"]) == [HIT, MISS_STREAM, HIT, HIT, MISS_STREAM, HIT]
     assert r1["stream"] == [(1, 5), (3, 7)]
     assert r1["pair_hits"] == 4 and r1["expert_hits"] == 2 and r1["expert_misses"] == 2
-    # the table evolves exactly as under plain staging
+    # evictions are those of plain staging (the clears); the table differs by
+    # the registered copies and the clock
     p1 = plain.stage_layer(1, 4, sel, num_layers=2)
-    assert pool.snapshot() == plain.snapshot()
-    assert p0["evictions"] == r0["evictions"] and p1["evictions"] == r1["evictions"]
+    assert (r0["evictions"], r1["evictions"]) == (p0["evictions"], p1["evictions"]) == (8, 0)
+    key, last, clock = pool.snapshot()
+    pkey, plast, pclock = plain.snapshot()
+    # layer 0 (clock 10 -> 16, pairs [0,3,2,0,1,2]) and layer 1 (16 -> 22,
+    # experts 1 and 3 copied into slots 5 and 7, 0 and 2 read from 9 and 8)
+    assert key[:8] == [(0, 0), (0, 1), (0, 2), (0, 3), None, (1, 1), None, (1, 3)]
+    assert pkey[:8] == [None] * 8 and key[8:] == pkey[8:]
+    assert (clock, pclock) == (22, 10)
+    assert (last[0], last[1], last[2], last[3]) == (13, 14, 15, 11)
+    assert (last[5], last[7], last[8], last[9]) == (20, 17, 21, 19)
 
 
 @given(seed=st.integers(0, 10_000))
@@ -312,7 +327,45 @@ def test_prefill_hit_d2d_without_residents_is_plain_staging(seed):
         for key in ("slot", "flag"):
             assert np.array_equal(ra[key], rb[key])
         assert ra["stream"] == rb["stream"] and ra["expert_misses"] == E
-    assert a.snapshot() == b.snapshot()
+    # the last two staged layers stay resident in their halves under hit-D2D
+    ka, kb = a.snapshot()[0], b.snapshot()[0]
+    assert all(k is None for k in kb[:2 * E])
+    assert sorted(k for k in ka[:2 * E]) == sorted((l, e) for l in (L - 2, L - 1) for e in range(E))
+    assert all(ka[(l % 2) * E + e] == (l, e) for l in (L - 2, L - 1) for e in range(E))
+
+
+def test_prefill_hit_d2d_registers_staged_experts_hand_worked():
+    """L = 3 layers of E = 2 experts, k = 1, C = 6: staging [0, 4), slots 4, 5
+    beyond it.  Six one-token decode calls fill the pool: (0,0)..(2,1) in
+    slots 0..5 with last uses 0..5, clock 6.  A hit-D2D chunk of 2 tokens:
+      layer 0, sel [1, 1]: clears [0,2) and [2,4) (4 evictions); copies 0, 1
+        into slots 0, 1; unselected copy 0 -> tick 6; expert 1's last pair is
+        position 1 -> 6 + 1 + 1 = 8; clock 9.
+      layer 1, sel [0, 1]: clears [2,4) and [0,2) (2 evictions: layer 0's
+        copies); copies into slots 2, 3; last uses 9 + 0 and 9 + 1; clock 11.
+      layer 2, sel [1, 1]: clears [0,2) only (no layer 3); (2,0) and (2,1)
+        are resident in slots 4, 5 and read in place; expert 1's last pair is
+        position 1 -> 12; expert 0 keeps 4; clock 13.
+    Afterwards a decode call of layer 1 hits the staged copy in slot 2, and a
+    miss takes the lowest free slot, 0."""
+    pool = LRUPool(6)
+    for key in range(6):
+        pool.resolve_wave(key // 2, np.array([[key % 2]]))
+    assert pool.clock == 6
+    r0 = pool.stage_layer(0, 2, np.array([[1], [1]]), 3, hit_d2d=True)
+    r1 = pool.stage_layer(1, 2, np.array([[0], [1]]), 3, hit_d2d=True)
+    r2 = pool.stage_layer(2, 2, np.array([[1], [1]]), 3, hit_d2d=True)
+    assert [r["evictions"] for r in (r0, r1, r2)] == [4, 2, 0]
+    assert [r["expert_hits"] for r in (r0, r1, r2)] == [0, 0, 2]
+    assert [len(r["stream"]) for r in (r0, r1, r2)] == [2, 2, 0]
+    assert list(r2["flag"]) == [HIT, HIT] and list(r2["slot"]) == [5, 5]
+    key, last, clock = pool.snapshot()
+    assert key == [None, None, (1, 0), (1, 1), (2, 0), (2, 1)]
+    assert last[2:] == [9, 10, 4, 12] and clock == 13
+    d = pool.resolve_wave(1, np.array([[0]]))
+    assert list(d["flag"]) == [HIT] and list(d["slot"]) == [2]
+    m = pool.resolve_wave(0, np.array([[0]]))
+    assert m["stream"] == [(0, 0)] and m["evictions"] == 0
 
 
 @settings(max_examples=60, deadline=None)
