@@ -80,7 +80,12 @@ enum {
    * Residency is read once, at layer 0 of the chunk (the device is
    * synchronised then), and the pool outside the staging region does not
    * change during a chunk.  Every call of a chunk must carry the same
-   * option (else FT_E_STATE).  Counters: pair hits count the pairs of
+   * option (else FT_E_STATE).  The copied experts become residents of
+   * their staging slots (until a later call clears that half, so after a
+   * chunk the last two layers stay cached), and each call updates the LRU
+   * order like one decode wave over its pairs: copies that no token selects
+   * take the first clock ticks (expert order), then every selected expert
+   * the clock of its last pair.  Counters: pair hits count the pairs of
    * resident experts, expert hits the resident experts of the layer, and
    * bytes H2D the experts copied. */
   FT_FWD_PREFILL_HIT_D2D = 1 << 8

@@ -233,11 +233,11 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
   int cur = 0;
   uint64_t clk = 0;
   int k2s = -1;
-  if (decode) {
+  const bool use_k2s = decode || a.stage_hits != 0;
+  if (use_k2s) {
     cur = *a.tab.lru_cur;
     clk = *a.tab.clock;
   }
-  const bool use_k2s = decode || a.stage_hits != 0;
   if (use_k2s && tid < E) k2s = a.tab.key2slot[key0 + tid];
   uint64_t* st = a.tab.stats + int64_t(a.layer) * ST_COUNT;
   uint64_t st0[ST_COUNT];
@@ -395,6 +395,77 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
   }
   if (tid == 0) sm.scal[1] = 0;  // evictions
   __syncthreads();
+
+  // ---- 5b. hit-D2D staging: the copied experts (not resident elsewhere)
+  // become residents of their staging slots, and the call updates the
+  // recency order like one wave over its pairs -- copies no token selects
+  // first (one clock tick each, in expert order), then every selected expert
+  // (read in place or copied) at the clock of its last pair.  The staging
+  // halves were cleared before this kernel, so a copy's slot is free here.
+  // New order: free slots ascending, residents this call does not touch in
+  // their old order, unselected copies, selected experts by last pair.
+  if (!decode && a.stage_hits) {
+    const int base = (a.layer & 1) * E;
+    for (int i = tid; i < (C + 31) / 32; i += NT) sm.prot[i] = 0u;
+    __syncthreads();
+    if (tid < nD && sm.cls[tid] == FT_PAIR_HIT) {
+      const int s = sm.dslot[tid];
+      atomicOr(&sm.prot[s >> 5], 1u << (s & 31));
+    }
+    const bool copied = tid < E && sm.k2s[tid] < 0;
+    const bool unsel = copied && sm.last[tid] < 0;
+    int u;
+    const int ur = block_excount(unsel, sm.wbuf, par, &u);  // its barrier publishes the marks above
+    int32_t* lru_out = a.tab.lru[cur ^ 1];
+    int nfree = 0;
+    for (int c0 = 0; c0 < C; c0 += NT) {
+      const int s = c0 + tid;
+      bool f = false;
+      if (s < C) {
+        const bool reg = s >= base && s < base + E && sm.k2s[s - base] < 0;
+        f = !reg && a.tab.slot_key[s] < 0;
+      }
+      int tot;
+      const int p = block_excount(f, sm.wbuf, par, &tot);
+      if (f) lru_out[nfree + p] = s;
+      nfree += tot;
+    }
+    int nold = 0;
+    for (int c0 = 0; c0 < C; c0 += NT) {
+      const int i = c0 + tid;
+      int s = 0;
+      bool r = false;
+      if (i < C) {
+        s = lru_in[i];
+        r = a.tab.slot_key[s] >= 0 && !((sm.prot[s >> 5] >> (s & 31)) & 1u);
+      }
+      int tot;
+      const int p = block_excount(r, sm.wbuf, par, &tot);
+      if (r) lru_out[nfree + nold + p] = s;
+      nold += tot;
+    }
+    if (unsel) {
+      lru_out[nfree + nold + ur] = base + tid;
+      a.tab.slot_last[base + tid] = clk + uint64_t(ur);
+    }
+    for (int d = tid; d < nD; d += NT) {
+      const int mylast = sm.last[sm.D[d]];
+      int rank = 0;
+      for (int d2 = 0; d2 < nD; ++d2) rank += sm.last[sm.D[d2]] < mylast ? 1 : 0;
+      lru_out[nfree + nold + u + rank] = sm.dslot[d];
+      a.tab.slot_last[sm.dslot[d]] = clk + uint64_t(u) + uint64_t(mylast);
+    }
+    __syncthreads();  // every read of slot_key above precedes the registrations
+    if (copied) {
+      a.tab.slot_key[base + tid] = key0 + tid;
+      a.tab.key2slot[key0 + tid] = base + tid;
+    }
+    if (tid == 0) {
+      *a.tab.clock = clk + uint64_t(u) + uint64_t(P);
+      *a.tab.lru_cur = cur ^ 1;
+    }
+    __syncthreads();
+  }
 
   // ---- 5. victims and recency update in one pass over the recency order.
   // An entry is eligible unless it holds a hit of this wave; the first m_str

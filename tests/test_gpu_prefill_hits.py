@@ -4,7 +4,8 @@ Own GPU, and the RAM It Takes", section "Long Prompts Are the Bottleneck"):
 decisions, outputs, tables and counters against the oracle's staging with the
 same option, chunks interleaved with decode calls, an MX activation chunk, a
 chunk whose pool has no residents beyond the staging region, and the
-same-option rule inside a chunk."""
+same-option rule inside a chunk.  With the option the copied experts become
+residents of their staging slots, so later decode calls can hit them."""
 
 import numpy as np
 import pytest
@@ -34,12 +35,15 @@ def test_hit_d2d_chunks_between_decode_calls(shared):
     g = GpuLayerStack(w)
     o = OracleLayerStack(w, pool_slots=g.C)
     hits = 0
+    staged_hits = 0  # decode pairs served by a previous chunk's staged copies
     try:
         for rnd in range(3):
             for s in range(3):
                 for l in range(3):
                     x = ms.activations(w, l, 10 * rnd + s, 8)
-                    compare_call(g.forward(l, x, g.bias(l, 0)), o.forward(l, x, ms.popularity_bias(w, l, 0)), 2)
+                    orr = o.forward(l, x, ms.popularity_bias(w, l, 0))
+                    compare_call(g.forward(l, x, g.bias(l, 0)), orr, 2)
+                    staged_hits += int(((orr["flag"] == ft.FT_PAIR_HIT) & (orr["slot"] < 2 * w.num_experts)).sum())
             for l in range(3):
                 x = ms.activations(w, l, 200 + rnd, 45)
                 gr = g.forward(l, x, g.bias(l, 0), prefill=True, hit_d2d=True)
@@ -51,6 +55,7 @@ def test_hit_d2d_chunks_between_decode_calls(shared):
         for key in ("pair_hits", "pair_misses", "expert_hits", "expert_misses", "evictions", "bytes_h2d", "calls"):
             assert st[key] == o.stats[key], (key, st[key], o.stats[key])
         assert hits > 0, "no resident expert was reused: the case does not exercise the option"
+        assert staged_hits > 0, "no decode call hit a staged copy"
     finally:
         g.close()
 
