@@ -13,58 +13,16 @@
 #include <vector>
 
 #include "../../include/ftmoe.h"
+#include "layout.h"
 
 namespace ftmoe {
 
 // ------------------------------------------------------------ limits
 constexpr int kMaxExperts = 512;  // per layer (LDS tables in the resolve kernel)
 constexpr int kMaxTopK = 16;
-constexpr int kTileRows = 16;     // rows of one weight tile (MFMA M)
-constexpr int kTileK = 128;       // K extent of one weight tile
 constexpr int kResolveThreads = 1024;
 constexpr int kGroupTok = 16;    // tokens of a group's first rows kept beside its descriptor
 constexpr int kMaxSlots = 65536;  // pool slots (LDS bitmap of protected slots in resolve)
-
-// ------------------------------------------------------------ device expert layout
-// One expert in GPU memory (and in the pinned host store, which holds the same
-// bytes so a miss is one contiguous copy):
-//   [gate codes][up codes][down codes][gate scales][up scales][down scales][tensor scales]
-// each section 256-byte aligned.  A matrix W[R][K] is cut into tiles of
-// 16 rows x 128 K, stored tile-major ([R/16][K/128]).  Inside a tile, lane
-// l = 16*q + r of a 64-wide wavefront owns row r and K range [32q, 32q+32):
-//   FP4 codes: 16 bytes per lane, 1024 per tile (nibble order unchanged)
-//   FP8 codes: 32 bytes per lane, 2048 per tile
-//   MXFP4 scales: 1 byte per lane per tile ([R/16][K/128][64])
-//   NVFP4 scales: 2 bytes per lane per tile ([R/16][K/128][64][2])
-//   FP8 scales: 16 fp32 per tile, one per row ([R/16][K/128][16])
-// so that one 16-byte load per lane fetches a whole tile of FP4 codes, and
-// the lane's 8-element sub-blocks are exactly the A operand of
-// v_mfma_f32_16x16x32_bf16 (lane 16q+r holds row r, K 8j..8j+7 of sub-step j).
-struct MatLayout {
-  int64_t codes_off;
-  int64_t scales_off;
-  int32_t rows, cols;
-};
-
-struct ExpertLayout {
-  int32_t fmt = 0, hidden = 0, inter = 0;
-  MatLayout m[3];  // 0 gate [I][H], 1 up [I][H], 2 down [H][I]
-  int64_t tscale_off = 0;  // 4 fp32 (NVFP4 per-matrix scales; others 1.0)
-  int64_t bytes = 0;
-};
-
-ExpertLayout make_layout(int fmt, int hidden, int inter);
-int64_t canonical_bytes(int fmt, int hidden, int inter);
-// canonical blob -> device layout (dst has layout.bytes bytes)
-void repack_expert(const ExpertLayout& L, const uint8_t* canonical, uint8_t* dst);
-// device layout -> one row of matrix m as exact fp64 values (tensor scale applied)
-void unpack_row_f64(const ExpertLayout& L, const uint8_t* dev_blob, int m, int row, double* out);
-// device layout -> fp32 row-major matrix m (rows*cols)
-void unpack_matrix_f32(const ExpertLayout& L, const uint8_t* dev_blob, int m, float* out);
-// host_ffn.cpp: one expert's SwiGLU FFN on CPU threads, weights in the device
-// layout (the pinned host store), x bf16 [rows][H] -> p = bf16(w * y) [rows][H]
-void host_expert(const ExpertLayout& L, const uint8_t* blob, const uint16_t* x, const float* wts, int rows,
-                 uint16_t* out, int threads);
 
 // ------------------------------------------------------------ per-call device records
 struct alignas(64) GroupDesc {
@@ -236,6 +194,8 @@ struct MissCopyArgs {
   uint64_t* ticks;
 };
 hipError_t launch_miss_copy(const MissCopyArgs& a, int workgroups, hipStream_t s, Ev ev = {});
+// debug: fill the slots of the streamed misses with 0xFF bytes (FT_MOE_POISON)
+hipError_t launch_poison_slots(const MissCopyArgs& a, int workgroups, hipStream_t s);
 
 // mxq.hip: bf16 rows [rows][K] -> MX codes (FP4 [rows][K/2] or FP8 [rows][K]) + E8M0 scales [rows][K/32]
 // Activation tiles of the MX GEMM: for each (row tile, 128-K step) of the

@@ -77,7 +77,29 @@ __global__ __launch_bounds__(256) void k_miss_copy(MissCopyArgs a) {
   }
 }
 
+// Debug mode (pool created with FT_MOE_POISON set): fill every slot about to
+// receive a streamed miss with 0xFF bytes before the copy, so that a reader
+// racing the copy sees NaN block scales (E8M0 / E4M3 0xFF, fp32 all ones)
+// instead of plausible stale weights.
+__global__ __launch_bounds__(256) void k_poison_slots(MissCopyArgs a) {
+  const int nh = a.dev_header[2], n = a.dev_header[3];
+  const int64_t n16 = a.bytes / 16;
+  const int64_t total = int64_t(n) * n16;
+  const u32x4 ones = {~0u, ~0u, ~0u, ~0u};
+  for (int64_t j = int64_t(blockIdx.x) * 256 + threadIdx.x; j < total; j += int64_t(gridDim.x) * 256) {
+    const int i = int(j / n16);
+    const GroupDesc g = a.gdesc[nh + i];
+    gstore<u32x4>(reinterpret_cast<u32x4*>(g.wptr) + (j - int64_t(i) * n16), ones);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_poison_slots(const MissCopyArgs& a, int workgroups, hipStream_t s) {
+  if (a.bytes <= 0 || a.bytes % 16 || workgroups < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_poison_slots, dim3(workgroups), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_miss_copy(const MissCopyArgs& a, int workgroups, hipStream_t s, Ev ev) {
   if (a.bytes <= 0 || a.bytes % 16 || workgroups < 1) return hipErrorInvalidValue;

@@ -17,13 +17,14 @@
 // time) an explicitly vectorised build decodes and multiplies 8 weights at a
 // time.
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <functional>
 #include <immintrin.h>
 #include <thread>
 #include <vector>
 
-#include "common.h"
+#include "layout.h"
 
 namespace ftmoe {
 
@@ -218,8 +219,11 @@ struct RowBlocks<true> {
 };
 #undef FT_HOST_BODY
 
+// The AVX2 build where the CPU has AVX2 and FMA, unless the environment
+// variable FT_MOE_HOST_PORTABLE is set (the portable build, for tests).
 bool cpu_has_avx2_fma() {
-  static const bool ok = __builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma");
+  static const bool ok = __builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma") &&
+                         std::getenv("FT_MOE_HOST_PORTABLE") == nullptr;
   return ok;
 }
 

@@ -1,8 +1,10 @@
 // Expert blob layouts: the canonical host format accepted at init, and the
 // tiled device format used by the GPU kernels and the pinned host store.
 #include <cmath>
+#include <cstring>
+#include <vector>
 
-#include "common.h"
+#include "layout.h"
 
 namespace ftmoe {
 

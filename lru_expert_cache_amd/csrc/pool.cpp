@@ -65,6 +65,10 @@ struct ft_moe_pool {
   // FT_MOE_DECODE_PATH=host / injected copy failures.
   bool dev_decode = true;
   int copy_wgs = 64;                // workgroups of the miss-copy kernel
+  // debug (env FT_MOE_POISON at creation): every slot is filled with 0xFF
+  // bytes (NaN block scales) just before a copy into it, so a reader that
+  // races a copy produces NaN instead of stale values
+  bool poison = false;
   // decode calls of up to 32 tokens use the K-streaming FFN kernel unless
   // FT_MOE_FFN=grid (the split-K kernel every other call uses)
   bool ffn_stream = true;
@@ -323,6 +327,7 @@ int issue_copy(ft_moe_pool* p, void* dst, const void* src, size_t bytes, hipStre
     set_error("injected failure of miss copy %llu", (unsigned long long)p->copy_counter);
     return FT_E_HIP;
   }
+  if (p->poison) FT_HIP_CHECK(hipMemsetAsync(dst, 0xFF, bytes, cs));
   FT_HIP_CHECK(hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, cs));
   return FT_OK;
 }
@@ -537,6 +542,12 @@ int copy_layer_staging(ft_moe_pool* p, int layer) {
   hipEvent_t e0 = prof_begin(p, p->copy_stream, FT_STAGE_COPY);
   hipEvent_t ct = copy_timer_begin(p, p->copy_stream);
   int copied = 0;
+  if (p->poison) {
+    // every slot of the half that this call copies into
+    for (int e = 0; e < E; ++e)
+      if (!(p->prefill_hit && p->prefill_res[int64_t(layer) * E + e] >= 0))
+        FT_HIP_CHECK(hipMemsetAsync(dst + int64_t(e) * p->slot_bytes, 0xFF, size_t(L.bytes), p->copy_stream));
+  }
   if (p->prefill_hit) {
     // runs of consecutive experts that are not resident in the pool
     const int32_t* res = p->prefill_res.data() + int64_t(layer) * E;
@@ -794,6 +805,7 @@ int forward_decode_dev(ft_moe_pool* p, int layer, int T, const void* x, void* ou
   ca.bytes = p->lay[f].bytes;
   ca.clk = p->copy_clk;
   ca.ticks = p->copy_ticks + layer;
+  if (p->poison) FT_HIP_CHECK(launch_poison_slots(ca, p->copy_wgs, s));
   Ev ec = prof_pair(p, s, FT_STAGE_COPY);
   FT_HIP_CHECK(launch_miss_copy(ca, p->copy_wgs, s, ec));
   prof_push(p, FT_STAGE_COPY, ec, 0.0, 0.0);
@@ -1166,6 +1178,7 @@ int ft_moe_init_pool(const ft_moe_config* cfg, const ft_moe_weights* wts, ft_moe
     if (p->fault_copy >= 0) p->dev_decode = false;  // injected copy failures exist on the host path only
     if (const char* fk = std::getenv("FT_MOE_FFN")) p->ffn_stream = std::strcmp(fk, "grid") != 0;
     if (const char* cw = std::getenv("FT_MOE_COPY_WGS")) p->copy_wgs = std::max(1, std::min(1024, std::atoi(cw)));
+    if (const char* pz = std::getenv("FT_MOE_POISON")) p->poison = pz[0] != '\0' && std::strcmp(pz, "0") != 0;
     {
       std::vector<int32_t> lru(C);
       for (int64_t i = 0; i < C; ++i) lru[i] = int32_t(i);
