@@ -161,7 +161,15 @@ typedef struct {
  * forces FT_E_OOM_PINNED here; work_alloc:<n> / mx_alloc:<n> make the pool's
  * n-th device allocation of per-call work buffers / of MX activation tiles
  * fail once (the call returns FT_E_OOM_DEVICE and leaves those buffers
- * unallocated; the next call allocates them again). */
+ * unallocated; the next call allocates them again); corrupt:<n> damages the
+ * n-th miss copy (256 bytes overwritten; host-driven path).
+ * Debug environment, read here: FT_MOE_POISON fills every slot with 0xFF
+ * bytes (NaN block scales) just before a copy into it, so a read racing the
+ * copy shows up as NaN; FT_MOE_DEBUG_CHECKSUM checks, before each FFN, that
+ * every slot it reads holds its key's weights (a checksum of the slot against
+ * the host store's blob) and makes each call wait and return FT_E_HIP naming
+ * the key and slot of a mismatch (no graph capture in this mode);
+ * FT_MOE_LOG=<n> prints the counters on stderr every n forward calls. */
 int ft_moe_init_pool(const ft_moe_config *cfg, const ft_moe_weights *w, ft_moe_pool **out);
 
 /* One MoE layer call on `hip_stream` (a hipStream_t, NULL = default stream).

@@ -196,6 +196,13 @@ struct MissCopyArgs {
 hipError_t launch_miss_copy(const MissCopyArgs& a, int workgroups, hipStream_t s, Ev ev = {});
 // debug: fill the slots of the streamed misses with 0xFF bytes (FT_MOE_POISON)
 hipError_t launch_poison_slots(const MissCopyArgs& a, int workgroups, hipStream_t s);
+// debug (FT_MOE_DEBUG_CHECKSUM): checksum of an expert in the device layout
+// (host side, the store), and a kernel that recomputes it for the groups
+// g0 .. min(g1, *n_dev) - 1 of a run list before their FFN reads them and
+// records the first mismatch in bad[0] = 1 + key, bad[1] = slot
+uint64_t slot_checksum(const uint8_t* blob, int64_t bytes);
+hipError_t launch_verify_slots(const GroupDesc* gdesc, int g0, int g1, const int32_t* n_dev, const uint64_t* key_sum,
+                               int key0, int64_t bytes, uint64_t* bad, hipStream_t s);
 
 // mxq.hip: bf16 rows [rows][K] -> MX codes (FP4 [rows][K/2] or FP8 [rows][K]) + E8M0 scales [rows][K/32]
 // Activation tiles of the MX GEMM: for each (row tile, 128-K step) of the

@@ -14,6 +14,8 @@
 // the FFN of the hit experts on the rest of the chip.  The streamed experts
 // are treated as one concatenated byte range that is split evenly over the
 // workgroups, so every miss count keeps all of them busy.
+#include <cstring>
+
 #include "common.h"
 #include "gmem.h"
 
@@ -93,7 +95,58 @@ __global__ __launch_bounds__(256) void k_poison_slots(MissCopyArgs a) {
   }
 }
 
+// Debug mode (pool created with FT_MOE_DEBUG_CHECKSUM set): one workgroup
+// per group recomputes the checksum of the weights its FFN is about to read
+// (slot_checksum: the sum of the expert's 32-bit words, each XOR-ed with its
+// index times 0x9E3779B1, modulo 2^64) and compares it with the checksum of
+// the key's blob in the host store.  The first mismatch is recorded in
+// bad[0] = 1 + key, bad[1] = slot.  Groups g0 .. min(g1, *n_dev) - 1 of the
+// run list; host-computed groups (slot -1) and the shared expert (-2) are
+// skipped.
+__global__ __launch_bounds__(256) void k_verify_slots(const GroupDesc* __restrict__ gdesc, int g0, int g1,
+                                                      const int32_t* __restrict__ n_dev,
+                                                      const uint64_t* __restrict__ key_sum, int key0, int64_t bytes,
+                                                      unsigned long long* bad) {
+  __shared__ unsigned long long part[4];
+  const int n = n_dev != nullptr ? min(g1, *n_dev) : g1;
+  const int gi = g0 + int(blockIdx.x);
+  if (gi >= n) return;
+  const GroupDesc g = gdesc[gi];
+  if (g.slot < 0 || g.wptr == 0) return;  // uniform over the workgroup
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(g.wptr);
+  const int64_t nw = bytes / 4;
+  unsigned long long acc = 0;
+  for (int64_t i = threadIdx.x; i < nw; i += 256) acc += gload<uint32_t>(w + i) ^ (uint32_t(i) * 0x9E3779B1u);
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_down(acc, off, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned long long sum = part[0] + part[1] + part[2] + part[3];
+    if (sum != key_sum[key0 + g.expert] &&
+        atomicCAS(bad, 0ull, (unsigned long long)(key0 + g.expert) + 1ull) == 0ull)
+      atomicExch(bad + 1, (unsigned long long)g.slot);
+  }
+}
+
 }  // namespace
+
+uint64_t slot_checksum(const uint8_t* blob, int64_t bytes) {
+  uint64_t acc = 0;
+  for (int64_t i = 0; i < bytes / 4; ++i) {
+    uint32_t v;
+    std::memcpy(&v, blob + 4 * i, 4);
+    acc += uint64_t(v ^ (uint32_t(i) * 0x9E3779B1u));
+  }
+  return acc;
+}
+
+hipError_t launch_verify_slots(const GroupDesc* gdesc, int g0, int g1, const int32_t* n_dev, const uint64_t* key_sum,
+                               int key0, int64_t bytes, uint64_t* bad, hipStream_t s) {
+  if (g1 <= g0) return hipSuccess;
+  hipLaunchKernelGGL(k_verify_slots, dim3(g1 - g0), dim3(256), 0, s, gdesc, g0, g1, n_dev, key_sum, key0, bytes,
+                     reinterpret_cast<unsigned long long*>(bad));
+  return hipGetLastError();
+}
 
 hipError_t launch_poison_slots(const MissCopyArgs& a, int workgroups, hipStream_t s) {
   if (a.bytes <= 0 || a.bytes % 16 || workgroups < 1) return hipErrorInvalidValue;

@@ -69,6 +69,16 @@ struct ft_moe_pool {
   // bytes (NaN block scales) just before a copy into it, so a reader that
   // races a copy produces NaN instead of stale values
   bool poison = false;
+  // debug (env FT_MOE_DEBUG_CHECKSUM at creation): before an FFN reads a slot,
+  // a kernel recomputes the slot's checksum and compares it with the key's
+  // blob in the host store; each call then waits and reports a mismatch
+  bool checksum = false;
+  uint64_t* key_sum_dev = nullptr;  // [L*E] checksum of each key's blob (device layout)
+  uint64_t* bad_dev = nullptr;      // [2] first mismatch: 1 + key, slot
+  int64_t corrupt_copy = -1;        // FT_MOE_FAULT=corrupt:<n>: the n-th miss copy lands damaged (tests)
+  // env FT_MOE_LOG=<n>: a counters line on stderr every n forward calls
+  int log_every = 0;
+  uint64_t log_calls = 0;
   // decode calls of up to 32 tokens use the K-streaming FFN kernel unless
   // FT_MOE_FFN=grid (the split-K kernel every other call uses)
   bool ffn_stream = true;
@@ -329,6 +339,17 @@ int issue_copy(ft_moe_pool* p, void* dst, const void* src, size_t bytes, hipStre
   }
   if (p->poison) FT_HIP_CHECK(hipMemsetAsync(dst, 0xFF, bytes, cs));
   FT_HIP_CHECK(hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, cs));
+  if (int64_t(p->copy_counter) == p->corrupt_copy)  // damaged copy (tests): 256 bytes of 0xA5
+    FT_HIP_CHECK(hipMemsetAsync(dst, 0xA5, std::min<size_t>(bytes, 256), cs));
+  return FT_OK;
+}
+
+// Debug checksums: groups g0 .. min(g1, *n_dev) - 1 of the run list must
+// hold their key's weights (FT_MOE_DEBUG_CHECKSUM).
+int verify_groups(ft_moe_pool* p, int layer, int g0, int g1, const int32_t* n_dev, hipStream_t s) {
+  if (!p->checksum) return FT_OK;
+  FT_HIP_CHECK(launch_verify_slots(p->gdesc, g0, g1, n_dev, p->key_sum_dev, layer * p->E,
+                                   p->lay[p->fmt[layer]].bytes, p->bad_dev, s));
   return FT_OK;
 }
 
@@ -758,6 +779,7 @@ int forward_prefill(ft_moe_pool* p, int layer, int T, const void* x, void* out, 
   Ev er = prof_pair(p, s, FT_STAGE_RESOLVE);
   FT_HIP_CHECK(launch_resolve(ra, s, er));
   prof_push(p, FT_STAGE_RESOLVE, er, 0.0, 0.0);
+  if (int rc = verify_groups(p, layer, 0, E + 1, p->dev_header + 9, s)) return rc;
   const double rows = double(T) * p->k + (p->shared ? T : 0);
   // MXFP4 layers run the grouped GEMM (bf16 or MX activations); others the FFN kernels
   int rc = p->fmt[layer] == FT_FMT_MXFP4 ? run_mx_ffn(p, layer, x, T, act, s)
@@ -813,6 +835,7 @@ int forward_decode_dev(ft_moe_pool* p, int layer, int T, const void* x, void* ou
   // all groups (hit list, then streamed misses; no host-computed ones here)
   const int pairs = T * k;
   const int bound = std::min(pairs, E) + p->shared;
+  if (int rc = verify_groups(p, layer, 0, bound, p->dev_header + 9, s)) return rc;
   // a group has at most one row per token
   int rc = run_ffn(p, layer, x, 0, bound, p->dev_header + 9, s, 0.0, 0.0, T);
   if (rc) return rc;
@@ -953,10 +976,13 @@ int forward_decode(ft_moe_pool* p, int layer, int T, const void* x, void* out, h
       });
     }
 
-    int rc = run_ffn(p, layer, x, 0, h.n_hit_list, nullptr, s, h.n_hit_list, h.rows_hit_list, T);
+    int rc = verify_groups(p, layer, 0, h.n_hit_list, nullptr, s);
+    if (rc == FT_OK) rc = run_ffn(p, layer, x, 0, h.n_hit_list, nullptr, s, h.n_hit_list, h.rows_hit_list, T);
     if (rc == FT_OK && h.n_stream > 0) {
       FT_HIP_CHECK(hipStreamWaitEvent(s, p->ev_copied, 0));
-      rc = run_ffn(p, layer, x, h.n_hit_list, h.n_stream, nullptr, s, h.n_stream, h.rows_stream, T);
+      rc = verify_groups(p, layer, h.n_hit_list, h.n_hit_list + h.n_stream, nullptr, s);
+      if (rc == FT_OK)
+        rc = run_ffn(p, layer, x, h.n_hit_list, h.n_stream, nullptr, s, h.n_stream, h.rows_stream, T);
     }
     if (cpu_thread.joinable()) cpu_thread.join();
     if (rc) return rc;
@@ -1047,6 +1073,9 @@ int ft_moe_init_pool(const ft_moe_config* cfg, const ft_moe_weights* wts, ft_moe
     if (fault && std::strncmp(fault, "copy:", 5) == 0) p->fault_copy = std::atoll(fault + 5);
     if (fault && std::strncmp(fault, "work_alloc:", 11) == 0) p->fault_work_alloc = std::atoi(fault + 11);
     if (fault && std::strncmp(fault, "mx_alloc:", 9) == 0) p->fault_mx_alloc = std::atoi(fault + 9);
+    if (fault && std::strncmp(fault, "corrupt:", 8) == 0) p->corrupt_copy = std::atoll(fault + 8);
+    if (const char* cs = std::getenv("FT_MOE_DEBUG_CHECKSUM")) p->checksum = cs[0] != '\0' && std::strcmp(cs, "0");
+    if (const char* lg = std::getenv("FT_MOE_LOG")) p->log_every = std::max(0, std::atoi(lg));
 
     // ---- pinned host store: one entry per distinct (blob pointer, format)
     std::map<std::pair<const void*, int>, int64_t> seen;
@@ -1175,7 +1204,22 @@ int ft_moe_init_pool(const ft_moe_config* cfg, const ft_moe_weights* wts, ft_moe
     for (int f = 1; f <= 3; ++f)
       if (p->lay[f].bytes % 16) p->dev_decode = false;
     if (const char* dp = std::getenv("FT_MOE_DECODE_PATH")) p->dev_decode = p->dev_decode && std::strcmp(dp, "host");
-    if (p->fault_copy >= 0) p->dev_decode = false;  // injected copy failures exist on the host path only
+    if (p->fault_copy >= 0 || p->corrupt_copy >= 0) p->dev_decode = false;  // injected copy faults: host path only
+    if (p->checksum) {
+      // checksum of every key's blob as the pinned store holds it
+      std::vector<uint64_t> sums(size_t(L) * E);
+      const int nthr = std::max(1, std::min(16, int(std::thread::hardware_concurrency())));
+      parallel_for(L * E, nthr, [&](int b, int e) {
+        for (int i = b; i < e; ++i)
+          sums[i] = slot_checksum(p->host_store + p->key_off[i], p->lay[p->fmt[i / E]].bytes);
+      });
+      if ((rc = dev_alloc(&p->key_sum_dev, int64_t(L) * E)) || (rc = dev_alloc(&p->bad_dev, 2))) {
+        ft_moe_destroy_pool(p.release());
+        return rc;
+      }
+      FT_HIP_CHECK(hipMemcpy(p->key_sum_dev, sums.data(), sums.size() * 8, hipMemcpyHostToDevice));
+      FT_HIP_CHECK(hipMemset(p->bad_dev, 0, 16));
+    }
     if (const char* fk = std::getenv("FT_MOE_FFN")) p->ffn_stream = std::strcmp(fk, "grid") != 0;
     if (const char* cw = std::getenv("FT_MOE_COPY_WGS")) p->copy_wgs = std::max(1, std::min(1024, std::atoi(cw)));
     if (const char* pz = std::getenv("FT_MOE_POISON")) p->poison = pz[0] != '\0' && std::strcmp(pz, "0") != 0;
@@ -1326,6 +1370,10 @@ int forward_impl(ft_moe_pool* p, int32_t layer, int32_t num_tokens, const void* 
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     FT_HIP_CHECK(hipStreamIsCapturing(s, &cap));
     const bool capturing = cap != hipStreamCaptureStatusNone;
+    if (capturing && p->checksum) {
+      set_error("the debug checksum mode (FT_MOE_DEBUG_CHECKSUM) waits after each call: no graph capture");
+      return FT_E_INVALID;
+    }
     if (capturing && !noalloc && (!dev_path || T > p->cap_T)) {
       set_error("a captured call must be a device-driven decode call of at most the reserved %d tokens "
                 "(T=%d, mode %d)", p->cap_T, T, mode);
@@ -1386,6 +1434,30 @@ int forward_impl(ft_moe_pool* p, int32_t layer, int32_t num_tokens, const void* 
       if (trace->slot) FT_HIP_CHECK(hipMemcpyAsync(trace->slot, p->pair_slot, n * 4, hipMemcpyDeviceToDevice, s));
       if (trace->flag) FT_HIP_CHECK(hipMemcpyAsync(trace->flag, p->pair_flag, n, hipMemcpyDeviceToDevice, s));
       if (trace->row) FT_HIP_CHECK(hipMemcpyAsync(trace->row, p->pair_row, n * 4, hipMemcpyDeviceToDevice, s));
+    }
+    if (p->checksum && !capturing) {
+      uint64_t bad[2] = {0, 0};
+      FT_HIP_CHECK(hipStreamSynchronize(s));
+      FT_HIP_CHECK(hipMemcpy(bad, p->bad_dev, 16, hipMemcpyDeviceToHost));
+      if (bad[0] != 0) {
+        FT_HIP_CHECK(hipMemset(p->bad_dev, 0, 16));
+        const int64_t key = int64_t(bad[0]) - 1;
+        set_error("slot checksum mismatch: key %lld (layer %lld, expert %lld) in slot %lld does not hold its weights",
+                  (long long)key, (long long)(key / E), (long long)(key % E), (long long)bad[1]);
+        return FT_E_HIP;
+      }
+    }
+    if (p->log_every > 0 && !capturing && ++p->log_calls % uint64_t(p->log_every) == 0) {
+      ft_moe_stats st;
+      if (ft_moe_pool_stats(p, -1, &st, 0) == FT_OK)
+        std::fprintf(stderr,
+                     "ftmoe: %llu calls, pair hit rate %.4f, experts %llu hit / %llu missed (%llu on host), "
+                     "%llu evictions, %.3f GB copied in %.1f ms, slots %lld / %lld\n",
+                     (unsigned long long)st.calls,
+                     double(st.pair_hits) / double(std::max<uint64_t>(st.pair_hits + st.pair_misses, 1)),
+                     (unsigned long long)st.expert_hits, (unsigned long long)st.expert_misses,
+                     (unsigned long long)st.cpu_misses, (unsigned long long)st.evictions, double(st.bytes_h2d) * 1e-9,
+                     st.copy_ms, (long long)st.slots_used, (long long)st.slots_total);
     }
     return FT_OK;
   }
@@ -1912,6 +1984,7 @@ void ft_moe_destroy_pool(ft_moe_pool* p) {
   hipFree(p->pair_row); hipFree(p->row_tok); hipFree(p->row_w); hipFree(p->groups); hipFree(p->glist); hipFree(p->gdesc); hipFree(p->count_max);
   hipFree(p->dev_header); hipFree(p->hbuf); hipFree(p->pbuf); hipFree(p->fail_dev);
   hipFree(p->key_off_dev); hipFree(p->prof_cnt_dev); hipFree(p->copy_clk); hipFree(p->copy_ticks);
+  hipFree(p->key_sum_dev); hipFree(p->bad_dev);
   hipFree(p->row_slot); hipFree(p->tiles); hipFree(p->xq_codes); hipFree(p->xq_scales);
   hipFree(p->tq_codes); hipFree(p->tq_scales);
   hipFree(p->hq_codes); hipFree(p->hq_scales);
