@@ -51,6 +51,14 @@ def host_threads():
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
+# Host worker threads of the hybrid split (--host-threads; default every core)
+HYBRID_THREADS = None
+
+
+def hybrid_threads():
+    return HYBRID_THREADS or host_threads()
+
+
 def measure_h2d(torch, dev, sizes=(52_224, 2_506_752, 20_054_016, 38_928_384, 320_864_256), reps=6):
     """Pinned host -> device copy bandwidth (GB/s) per size."""
     out = {}
@@ -140,7 +148,7 @@ class DecodeRun:
         router = np.stack([ms.router_weight(w, l) for l in range(L)])
         shared = [self.store.shared(l) for l in range(L)] if w.shared_expert else None
         cfg = ft.make_config(L, H, w.inter, E, w.top_k, w.layer_fmt, pool_slots=w.pool_slots, shared=w.shared_expert,
-                             cpu_threads=host_threads())
+                             cpu_threads=hybrid_threads())
         self.pool, _ = ft.ft_moe_init_pool(cfg, blobs, router, shared)
         del blobs
         log(f"[bench] {w.name}: pool of {w.pool_slots} slots ready in {time.perf_counter() - t:.1f} s")
@@ -449,7 +457,14 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="skip the Qwen-A3B, link, HBM and MFMA measurements")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--host-threads", type=int, default=None,
+                    help="host worker threads of the hybrid split (default: every core)")
+    ap.add_argument("--only", choices=["prefill"], default=None,
+                    help="prefill: time only the staged Qwen-A3B prefill chunk (one JSON line of its figures; for "
+                         "profiling the prefill kernels)")
     args = ap.parse_args()
+    global HYBRID_THREADS
+    HYBRID_THREADS = args.host_threads
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
               file=sys.stderr)
@@ -462,6 +477,13 @@ def main():
 
     ft.lib()
     dev = torch.device("cuda", 0)
+    if args.only == "prefill":
+        wq = ms.workload("qwen-a3b-prefill-4096")
+        store = ms.BlobStore(wq)
+        blobs = [store.expert(l, e) for l in range(wq.num_layers) for e in range(wq.num_experts)]
+        router = np.stack([ms.router_weight(wq, l) for l in range(wq.num_layers)])
+        print(json.dumps({"prefill": measure_prefill(ft, torch, ms, blobs, router, dev)}))
+        return
     w = ms.workload(args.workload)
     if w.mode != "decode":
         print(f"bench.py times decode workloads; {w.name} is a {w.mode} workload (its chunk is timed as an extra)",
@@ -547,6 +569,7 @@ def main():
                    "format": "|".join({1: "mxfp4", 2: "nvfp4", 3: "fp8-b128"}[f] for f in fmts),
                    "zipf_alpha": w.zipf_alpha, "popularity_shift_steps": w.phase_steps,
                    "shared_expert": w.shared_expert, "hybrid_share": share_used,
+                   "host_threads": hybrid_threads() if w.hybrid else 0,
                    "host_blob_aliasing": w.n_blobs},
         "roofline": {"kernel": kernel, "bound": "hbm", "achieved": gu_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": gu_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(traffic_profile),

@@ -309,10 +309,11 @@ typedef struct {
 int ft_moe_decide_mode(ft_moe_mode_report *r);
 
 /* Measure the rates on this machine, then decide (ft_moe_decide_mode).  For
- * each format the model uses, the first layer of that format supplies up to 8
+ * each format the model uses, the first layer of that format supplies up to 16
  * experts: their blobs are copied from the pinned store into a temporary
  * device buffer (h2d), the grouped expert FFN runs on them with `tokens` rows
- * each (gpu), and the host expert path runs on one of them (cpu).  Takes
+ * each (gpu), and the host expert path runs on all of them in one batched
+ * call, as a step's host-computed misses do (cpu).  Takes
  * about a second; synchronises the device; allocates and frees the temporary
  * buffer; does not touch the slot table or the counters.  apply != 0 sets the
  * pool's hybrid share to the chosen share.  1 <= tokens <= 64. */
@@ -344,6 +345,8 @@ int ft_moe_mfma_rate(int32_t kind, int32_t iters, void *hip_stream, double *flop
 enum { FT_STAGE_ROUTER = 0, FT_STAGE_TOPK, FT_STAGE_RESOLVE, FT_STAGE_FFN_GATEUP, FT_STAGE_FFN_DOWN,
        FT_STAGE_COMBINE, FT_STAGE_COPY,
        FT_STAGE_ACT_QUANT, /* MX activation modes: quantising x or h and laying the rows out as GEMM tiles */
+       FT_STAGE_HOST_FFN,  /* hybrid split: the host-computed experts of a call, host wall time (overlaps the
+                              GPU work); bytes = their expert bytes, flops = 6 x rows x H x I */
        FT_STAGE_COUNT };
 typedef struct {
   double ms[FT_STAGE_COUNT];        /* summed event-measured durations */

@@ -30,7 +30,7 @@ FT_FWD_PREFILL_HIT_D2D = 1 << 8
 FT_ACT_BF16, FT_ACT_MXFP8, FT_ACT_MXFP4 = 0 << 4, 1 << 4, 2 << 4
 FT_PAIR_HIT, FT_PAIR_MISS_STREAM, FT_PAIR_MISS_CPU = 0, 1, 2
 
-FT_STAGES = ["router", "topk", "resolve", "ffn_gateup", "ffn_down", "combine", "copy", "act_quant"]
+FT_STAGES = ["router", "topk", "resolve", "ffn_gateup", "ffn_down", "combine", "copy", "act_quant", "host_ffn"]
 
 EXPORTED = ["ft_moe_init_pool", "ft_moe_layer_forward", "ft_moe_pool_stats", "ft_moe_last_misses",
             "ft_moe_pool_table", "ft_moe_set_hybrid_share", "ft_moe_host_expert_rate",

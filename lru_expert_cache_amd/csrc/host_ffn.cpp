@@ -19,8 +19,12 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <algorithm>
+#include <atomic>
+#include <condition_variable>
 #include <functional>
 #include <immintrin.h>
+#include <mutex>
 #include <thread>
 #include <vector>
 
@@ -108,7 +112,8 @@ struct RowBlocks;
 #define FT_HOST_BODY                                                                                   \
   const Tables& tb = tables();                                                                         \
   const int K = L.m[m0].cols, nkb = K / kTileK;                                                        \
-  std::vector<float> acc(size_t(nm) * rows * 16);                                                      \
+  thread_local std::vector<float> acc;                                                                 \
+  acc.resize(size_t(nm) * rows * 16);                                                                  \
   float w[32];                                                                                         \
   for (int rb = rb_begin; rb < rb_end; ++rb) {                                                         \
     std::fill(acc.begin(), acc.end(), 0.0f);                                                           \
@@ -151,8 +156,10 @@ struct RowBlocks<true> {
     const Tables& tb = tables();
     const int K = L.m[m0].cols, nkb = K / kTileK;
     const int fmt = L.fmt;
-    std::vector<float> acc(size_t(nm) * rows * 16);
-    std::vector<__m256> part(size_t(64) * rows);
+    thread_local std::vector<float> acc;
+    thread_local std::vector<__m256> part;
+    acc.resize(size_t(nm) * rows * 16);
+    part.resize(size_t(64) * rows);
     const __m128i lut2 = _mm_setr_epi8(0, 1, 2, 3, 4, 6, 8, 12, 0, -1, -2, -3, -4, -6, -8, -12);
     const __m128i lo4 = _mm_set1_epi8(0x0F);
     for (int rb = rb_begin; rb < rb_end; ++rb) {
@@ -227,60 +234,153 @@ bool cpu_has_avx2_fma() {
   return ok;
 }
 
-void parallel_blocks(int n, int threads, const std::function<void(int, int)>& fn) {
-  threads = std::max(1, std::min(threads, n));
-  if (threads == 1) {
-    fn(0, n);
-    return;
+}  // namespace
+
+// ---- worker pool: threads - 1 background threads plus the calling thread
+// take work items from a shared counter; run() returns when every item of
+// its task is done.
+struct WorkerPool::Impl {
+  std::mutex mu;
+  std::condition_variable start_cv, done_cv;
+  std::vector<std::thread> threads;
+  const std::function<void(int64_t)>* fn = nullptr;
+  int64_t items = 0;
+  std::atomic<int64_t> next{0};
+  uint64_t generation = 0;
+  int busy = 0;  // background threads still working on the current task
+  bool stop = false;
+
+  void work() {
+    for (;;) {
+      const int64_t i = next.fetch_add(1, std::memory_order_relaxed);
+      if (i >= items) return;
+      (*fn)(i);
+    }
   }
-  std::vector<std::thread> th;
-  const int chunk = (n + threads - 1) / threads;
-  for (int t = 0; t < threads; ++t) {
-    const int b = t * chunk, e = std::min(n, b + chunk);
-    if (b >= e) break;
-    th.emplace_back(fn, b, e);
+  void loop() {
+    uint64_t seen = 0;
+    for (;;) {
+      {
+        std::unique_lock<std::mutex> lk(mu);
+        start_cv.wait(lk, [&] { return stop || generation != seen; });
+        if (stop) return;
+        seen = generation;
+      }
+      work();
+      std::lock_guard<std::mutex> lk(mu);
+      if (--busy == 0) done_cv.notify_one();
+    }
   }
-  for (auto& x : th) x.join();
+};
+
+WorkerPool::WorkerPool(int threads) : impl_(new Impl) {
+  for (int t = 1; t < std::max(1, threads); ++t) impl_->threads.emplace_back([this] { impl_->loop(); });
 }
 
-void row_blocks(const ExpertLayout& L, const uint8_t* blob, int m0, int nm, const float* gsc, const float* xf, int rows,
-                int threads, const std::function<void(int, const float*)>& finish) {
-  const int nrb = L.m[m0].rows / kTileRows;
-  const bool avx2 = cpu_has_avx2_fma();
-  parallel_blocks(nrb, threads, [&](int b, int e) {
-    if (avx2)
-      RowBlocks<true>::run(L, blob, m0, nm, gsc, xf, rows, b, e, finish);
-    else
-      RowBlocks<false>::run(L, blob, m0, nm, gsc, xf, rows, b, e, finish);
-  });
+WorkerPool::~WorkerPool() {
+  {
+    std::lock_guard<std::mutex> lk(impl_->mu);
+    impl_->stop = true;
+  }
+  impl_->start_cv.notify_all();
+  for (auto& t : impl_->threads) t.join();
+  delete impl_;
+}
+
+int WorkerPool::size() const { return int(impl_->threads.size()) + 1; }
+
+void WorkerPool::run(int64_t items, const std::function<void(int64_t)>& fn) {
+  if (items <= 0) return;
+  Impl& m = *impl_;
+  if (m.threads.empty() || items == 1) {
+    for (int64_t i = 0; i < items; ++i) fn(i);
+    return;
+  }
+  {
+    std::lock_guard<std::mutex> lk(m.mu);
+    m.fn = &fn;
+    m.items = items;
+    m.next.store(0, std::memory_order_relaxed);
+    m.busy = int(m.threads.size());
+    ++m.generation;
+  }
+  m.start_cv.notify_all();
+  m.work();
+  std::unique_lock<std::mutex> lk(m.mu);
+  m.done_cv.wait(lk, [&] { return m.busy == 0; });
+  m.fn = nullptr;
+}
+
+namespace {
+
+// Row blocks per work item: enough tiles per item to amortise its setup,
+// few enough that a layer's host experts spread over every thread.
+constexpr int kBlocksPerItem = 4;
+
+void run_blocks(const ExpertLayout& L, const uint8_t* blob, int m0, int nm, const float* gsc, const float* xf,
+                int rows, int rb_begin, int rb_end, const std::function<void(int, const float*)>& finish) {
+  if (cpu_has_avx2_fma())
+    RowBlocks<true>::run(L, blob, m0, nm, gsc, xf, rows, rb_begin, rb_end, finish);
+  else
+    RowBlocks<false>::run(L, blob, m0, nm, gsc, xf, rows, rb_begin, rb_end, finish);
 }
 
 }  // namespace
 
+void host_experts(const ExpertLayout& L, const HostExpertJob* jobs, int n, WorkerPool& pool) {
+  if (n <= 0) return;
+  const int H = L.hidden, I = L.inter;
+  const bool nv = L.fmt == FT_FMT_NVFP4;
+  struct JobState {
+    std::vector<float> xf, hf;
+    float ts[4];
+  };
+  std::vector<JobState> js(static_cast<size_t>(n));
+  for (int j = 0; j < n; ++j) {
+    const HostExpertJob& jb = jobs[j];
+    js[j].xf.resize(size_t(std::max(jb.rows, 0)) * H);
+    js[j].hf.resize(size_t(std::max(jb.rows, 0)) * I);
+    for (size_t i = 0; i < js[j].xf.size(); ++i) js[j].xf[i] = bf16_to_f32(jb.x[i]);
+    std::memcpy(js[j].ts, jb.blob + L.tscale_off, 16);
+  }
+  const float one[2] = {1.0f, 1.0f};
+  // phase 1, gate and up: h = bf16(silu(g) * u); items = (expert, group of row blocks)
+  const int ngu = (I / kTileRows + kBlocksPerItem - 1) / kBlocksPerItem;
+  pool.run(int64_t(n) * ngu, [&](int64_t it) {
+    const int j = int(it / ngu), b0 = int(it % ngu) * kBlocksPerItem;
+    const int rows = jobs[j].rows;
+    if (rows <= 0) return;
+    float* hf = js[j].hf.data();
+    run_blocks(L, jobs[j].blob, 0, 2, nv ? js[j].ts : one, js[j].xf.data(), rows, b0,
+               std::min(b0 + kBlocksPerItem, I / kTileRows), [&](int rb, const float* acc) {
+                 for (int t = 0; t < rows; ++t)
+                   for (int r = 0; r < kTileRows; ++r) {
+                     const float g = acc[(0 * size_t(rows) + t) * 16 + r], u = acc[(1 * size_t(rows) + t) * 16 + r];
+                     hf[size_t(t) * I + rb * kTileRows + r] = bf16_to_f32(f32_to_bf16(g / (1.0f + std::exp(-g)) * u));
+                   }
+               });
+  });
+  // phase 2, down: p = bf16(w * y)
+  const int ndn = (H / kTileRows + kBlocksPerItem - 1) / kBlocksPerItem;
+  pool.run(int64_t(n) * ndn, [&](int64_t it) {
+    const int j = int(it / ndn), b0 = int(it % ndn) * kBlocksPerItem;
+    const HostExpertJob& jb = jobs[j];
+    if (jb.rows <= 0) return;
+    run_blocks(L, jb.blob, 2, 1, nv ? js[j].ts + 2 : one, js[j].hf.data(), jb.rows, b0,
+               std::min(b0 + kBlocksPerItem, H / kTileRows), [&](int rb, const float* acc) {
+                 for (int t = 0; t < jb.rows; ++t)
+                   for (int r = 0; r < kTileRows; ++r)
+                     jb.out[size_t(t) * H + rb * kTileRows + r] = f32_to_bf16(jb.w[t] * acc[size_t(t) * 16 + r]);
+               });
+  });
+}
+
 void host_expert(const ExpertLayout& L, const uint8_t* blob, const uint16_t* x, const float* wts, int rows,
                  uint16_t* out, int threads) {
   if (rows <= 0) return;
-  const int H = L.hidden, I = L.inter;
-  float ts[4];
-  std::memcpy(ts, blob + L.tscale_off, 16);
-  const float one[2] = {1.0f, 1.0f};
-  const bool nv = L.fmt == FT_FMT_NVFP4;
-  std::vector<float> xf(size_t(rows) * H), hf(size_t(rows) * I);
-  for (size_t i = 0; i < xf.size(); ++i) xf[i] = bf16_to_f32(x[i]);
-  // gate and up: h = bf16(silu(g) * u)
-  row_blocks(L, blob, 0, 2, nv ? ts : one, xf.data(), rows, threads, [&](int rb, const float* acc) {
-    for (int t = 0; t < rows; ++t)
-      for (int r = 0; r < kTileRows; ++r) {
-        const float g = acc[(0 * size_t(rows) + t) * 16 + r], u = acc[(1 * size_t(rows) + t) * 16 + r];
-        hf[size_t(t) * I + rb * kTileRows + r] = bf16_to_f32(f32_to_bf16(g / (1.0f + std::exp(-g)) * u));
-      }
-  });
-  // down: p = bf16(w * y)
-  row_blocks(L, blob, 2, 1, nv ? ts + 2 : one, hf.data(), rows, threads, [&](int rb, const float* acc) {
-    for (int t = 0; t < rows; ++t)
-      for (int r = 0; r < kTileRows; ++r)
-        out[size_t(t) * H + rb * kTileRows + r] = f32_to_bf16(wts[t] * acc[size_t(t) * 16 + r]);
-  });
+  WorkerPool pool(threads);
+  const HostExpertJob job{blob, x, wts, rows, out};
+  host_experts(L, &job, 1, pool);
 }
 
 }  // namespace ftmoe

@@ -6,6 +6,7 @@
 #pragma once
 
 #include <cstdint>
+#include <functional>
 
 #include "../../include/ftmoe.h"
 
@@ -50,8 +51,37 @@ void repack_expert(const ExpertLayout& L, const uint8_t* canonical, uint8_t* dst
 void unpack_row_f64(const ExpertLayout& L, const uint8_t* dev_blob, int m, int row, double* out);
 // device layout -> fp32 row-major matrix m (rows*cols)
 void unpack_matrix_f32(const ExpertLayout& L, const uint8_t* dev_blob, int m, float* out);
-// host_ffn.cpp: one expert's SwiGLU FFN on CPU threads, weights in the device
-// layout (the pinned host store), x bf16 [rows][H] -> p = bf16(w * y) [rows][H]
+// host_ffn.cpp: persistent host worker threads.  run() hands items 0 ..
+// items - 1 to the threads - 1 background threads and the calling thread
+// (each item once) and returns when all are done.  One caller at a time.
+class WorkerPool {
+ public:
+  explicit WorkerPool(int threads);
+  ~WorkerPool();
+  WorkerPool(const WorkerPool&) = delete;
+  WorkerPool& operator=(const WorkerPool&) = delete;
+  void run(int64_t items, const std::function<void(int64_t)>& fn);
+  int size() const;
+
+ private:
+  struct Impl;
+  Impl* impl_;
+};
+
+// One host-computed expert: weights in the device layout (the pinned host
+// store), x bf16 [rows][H] in, p = bf16(w * y) [rows][H] out.
+struct HostExpertJob {
+  const uint8_t* blob;
+  const uint16_t* x;
+  const float* w;
+  int rows;
+  uint16_t* out;
+};
+// The SwiGLU FFN of n experts of one format on the pool's threads: first the
+// gate/up row blocks of every expert, then the down row blocks (one work item
+// per few row blocks of one expert).
+void host_experts(const ExpertLayout& L, const HostExpertJob* jobs, int n, WorkerPool& pool);
+// One expert on a temporary pool of `threads` threads.
 void host_expert(const ExpertLayout& L, const uint8_t* blob, const uint16_t* x, const float* wts, int rows,
                  uint16_t* out, int threads);
 

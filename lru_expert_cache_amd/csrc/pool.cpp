@@ -45,6 +45,7 @@ using namespace ftmoe;
 
 struct ft_moe_pool {
   int L = 0, H = 0, I = 0, E = 0, k = 0, shared = 0, device = 0, cpu_threads = 8;
+  std::unique_ptr<WorkerPool> workers;  // host threads of the hybrid split (created on first use)
   int64_t C = 0;
   std::vector<int32_t> fmt;
   ExpertLayout lay[4];
@@ -923,6 +924,14 @@ int forward_decode(ft_moe_pool* p, int layer, int T, const void* x, void* out, h
     }
     for (int i = 0; i < h.n_cpu; ++i) p->last_ce.push_back(ce[i]);
 
+    // the activation rows the host-computed experts need, fetched before the
+    // streamed copies are queued: behind them the small device-to-host copy
+    // would wait for the whole transfer, and the host work would start only
+    // when the copies end instead of overlapping them
+    if (h.n_cpu > 0) {
+      if (p->cpu_copy_pending) FT_HIP_CHECK(hipEventSynchronize(p->ev_cpu_copied));
+      FT_HIP_CHECK(hipMemcpy(p->x_host, x, size_t(T) * p->H * 2, hipMemcpyDeviceToHost));
+    }
     // streamed misses: one contiguous copy per expert, rotating over the copy
     // streams.  Everything earlier on s (the readers of the victim slots) has
     // finished: the resolve kernel that published this list ran after it.
@@ -950,29 +959,34 @@ int forward_decode(ft_moe_pool* p, int layer, int T, const void* x, void* out, h
       FT_HIP_CHECK(hipEventRecord(p->ev_copied, p->copy[0]));
     }
 
-    // host-computed misses run on CPU threads while the GPU works
+    // host-computed misses run on the host worker threads while the GPU works
+    // (one batched call for all of them: gate/up row blocks of every expert,
+    // then their down row blocks)
     std::thread cpu_thread;
     std::vector<int64_t> cpu_base;
+    double host_sec = 0.0;
     if (h.n_cpu > 0) {
-      if (p->cpu_copy_pending) FT_HIP_CHECK(hipEventSynchronize(p->ev_cpu_copied));
-      FT_HIP_CHECK(hipMemcpy(p->x_host, x, size_t(T) * p->H * 2, hipMemcpyDeviceToHost));
       int64_t base = 0;
       for (int j = 0; j < h.n_cpu; ++j) {
         cpu_base.push_back(base);
         base += cc[j];
       }
+      if (!p->workers) p->workers = std::make_unique<WorkerPool>(p->cpu_threads);
       std::vector<int32_t> toks(ct, ct + h.cpu_rows);
       std::vector<float> wts(cw, cw + h.cpu_rows);
       std::vector<int32_t> experts(ce, ce + h.n_cpu), counts(cc, cc + h.n_cpu);
-      cpu_thread = std::thread([p, layer, toks, wts, experts, counts, cpu_base, &L]() {
-        for (size_t j = 0; j < experts.size(); ++j) {
-          const int rows = counts[j];
-          std::vector<uint16_t> xr(size_t(rows) * p->H);
-          for (int r = 0; r < rows; ++r)
-            std::memcpy(&xr[size_t(r) * p->H], p->x_host + int64_t(toks[cpu_base[j] + r]) * p->H, size_t(p->H) * 2);
-          const uint8_t* blob = p->host_store + p->key_off[int64_t(layer) * p->E + experts[j]];
-          host_expert(L, blob, xr.data(), &wts[cpu_base[j]], rows, p->cpu_out + cpu_base[j] * p->H, p->cpu_threads);
-        }
+      cpu_thread = std::thread([p, layer, toks, wts, experts, counts, cpu_base, &L, &host_sec]() {
+        const auto t0 = std::chrono::steady_clock::now();
+        std::vector<uint16_t> xr(toks.size() * size_t(p->H));
+        for (size_t r = 0; r < toks.size(); ++r)
+          std::memcpy(&xr[r * p->H], p->x_host + int64_t(toks[r]) * p->H, size_t(p->H) * 2);
+        std::vector<HostExpertJob> jobs(experts.size());
+        for (size_t j = 0; j < experts.size(); ++j)
+          jobs[j] = HostExpertJob{p->host_store + p->key_off[int64_t(layer) * p->E + experts[j]],
+                                  xr.data() + cpu_base[j] * p->H, wts.data() + cpu_base[j], counts[j],
+                                  p->cpu_out + cpu_base[j] * p->H};
+        host_experts(L, jobs.data(), int(jobs.size()), *p->workers);
+        host_sec = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
       });
     }
 
@@ -984,7 +998,15 @@ int forward_decode(ft_moe_pool* p, int layer, int T, const void* x, void* out, h
       if (rc == FT_OK)
         rc = run_ffn(p, layer, x, h.n_hit_list, h.n_stream, nullptr, s, h.n_stream, h.rows_stream, T);
     }
-    if (cpu_thread.joinable()) cpu_thread.join();
+    if (cpu_thread.joinable()) {
+      cpu_thread.join();
+      if (p->prof_mask & (1 << FT_STAGE_HOST_FFN)) {
+        p->prof.ms[FT_STAGE_HOST_FFN] += host_sec * 1e3;
+        p->prof.bytes[FT_STAGE_HOST_FFN] += double(h.n_cpu) * double(p->canon_bytes[p->fmt[layer]]);
+        p->prof.flops[FT_STAGE_HOST_FFN] += double(h.cpu_rows) * 6.0 * p->H * p->I;
+        p->prof.launches[FT_STAGE_HOST_FFN] += 1;
+      }
+    }
     if (rc) return rc;
     if (h.n_cpu > 0) {
       for (int j = 0; j < h.n_cpu; ++j)
@@ -1702,8 +1724,10 @@ int ft_moe_host_expert_rate(ft_moe_pool* p, int32_t layer, int32_t tokens, int32
   std::vector<uint16_t> x(size_t(tokens) * p->H, 0x3F80), out(size_t(tokens) * p->H);
   std::vector<float> w(tokens, 1.0f);
   const uint8_t* blob = p->host_store + p->key_off[int64_t(layer) * p->E];
+  if (!p->workers) p->workers = std::make_unique<WorkerPool>(p->cpu_threads);
+  const HostExpertJob job{blob, x.data(), w.data(), tokens, out.data()};
   const auto t0 = std::chrono::steady_clock::now();
-  for (int i = 0; i < iters; ++i) host_expert(L, blob, x.data(), w.data(), tokens, out.data(), p->cpu_threads);
+  for (int i = 0; i < iters; ++i) host_experts(L, &job, 1, *p->workers);
   const double sec = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
   *bytes_per_s = double(p->canon_bytes[p->fmt[layer]]) * iters / std::max(sec, 1e-9);
   return FT_OK;
@@ -1798,7 +1822,7 @@ int ft_moe_measure_mode(ft_moe_pool* p, int32_t tokens, int32_t apply, ft_moe_mo
   r.tokens = tokens;
   r.pool_slots = p->C;
   r.all_experts = int64_t(p->L) * p->E;
-  const int n = std::min(p->E, 8), T = tokens, H = p->H;
+  const int n = std::min(p->E, 16), T = tokens, H = p->H;
   int rc = read_pending_misses(p);
   if (rc) return rc;
   if ((rc = ensure_capacity(p, (n * T + p->k - 1) / p->k))) return rc;
@@ -1897,21 +1921,26 @@ int ft_moe_measure_mode(ft_moe_pool* p, int32_t tokens, int32_t apply, ft_moe_mo
       return rc;
     if (frc) return frc;
     r.gpu_bytes_per_s[f] = double(n) * double(b) / sec;
-    // the host expert path on one of them
+    // the host expert path on the same n experts, in one batched call as a
+    // step's host-computed misses run
     {
-      std::vector<uint16_t> x(size_t(T) * H, 0x3F80), o(size_t(T) * H);
+      std::vector<uint16_t> x(size_t(T) * H, 0x3F80), o(size_t(n) * T * H);
       std::vector<float> w(T, 1.0f);
-      const uint8_t* blob = p->host_store + p->key_off[int64_t(layer) * p->E];
-      host_expert(p->lay[f], blob, x.data(), w.data(), T, o.data(), p->cpu_threads);  // warm-up
+      if (!p->workers) p->workers = std::make_unique<WorkerPool>(p->cpu_threads);
+      std::vector<HostExpertJob> jobs(n);
+      for (int e = 0; e < n; ++e)
+        jobs[e] = HostExpertJob{p->host_store + p->key_off[int64_t(layer) * p->E + e], x.data(), w.data(), T,
+                                o.data() + size_t(e) * T * H};
+      host_experts(p->lay[f], jobs.data(), n, *p->workers);  // warm-up
       const auto t0 = std::chrono::steady_clock::now();
       int it = 0;
       double el = 0.0;
       do {
-        host_expert(p->lay[f], blob, x.data(), w.data(), T, o.data(), p->cpu_threads);
+        host_experts(p->lay[f], jobs.data(), n, *p->workers);
         ++it;
         el = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
       } while (it < kReps && el < 0.25);
-      r.cpu_bytes_per_s[f] = double(b) * it / std::max(el, 1e-9);
+      r.cpu_bytes_per_s[f] = double(n) * double(b) * it / std::max(el, 1e-9);
     }
   }
   FT_HIP_CHECK(hipDeviceSynchronize());

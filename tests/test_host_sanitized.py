@@ -1,10 +1,11 @@
 """The host runtime pieces that need no GPU -- repacking canonical blobs into
 the device layout (layout.cpp) and the host expert path of the hybrid split
-(host_ffn.cpp) -- built with g++ under the address and undefined-behaviour
-sanitizers and run on seeded blobs of every format, in the AVX2 and the
-portable build.  The decoded matrices must equal the oracle's exactly; the
-host expert's rows must match the oracle's expert FFN (same rounding points,
-fp32 sums) within the parity bar; no sanitizer may report."""
+(host_ffn.cpp, with its worker threads) -- built with g++ under the address
+and undefined-behaviour sanitizers (and the thread sanitizer) and run on
+seeded blobs of every format, in the AVX2 and the portable build.  The decoded
+matrices must equal the oracle's exactly; the host expert's rows must match the
+oracle's expert FFN (same rounding points, fp32 sums) within the parity bar; no
+sanitizer may report."""
 
 import os
 import shutil
@@ -20,19 +21,27 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "lru_expert_cache_amd", "csrc")
 
 
-@pytest.fixture(scope="module")
-def host_check(tmp_path_factory):
+def _build(tmp_path_factory, name, sanitize):
     gxx = shutil.which("g++")
     if gxx is None:
         pytest.skip("no g++")
-    exe = str(tmp_path_factory.mktemp("asan") / "host_check")
-    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
-           "-fno-sanitize-recover=all", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           os.path.join(ROOT, "tests", "native", "host_check.cpp"), os.path.join(CSRC, "layout.cpp"),
-           os.path.join(CSRC, "host_ffn.cpp"), "-lpthread", "-o", exe]
+    exe = str(tmp_path_factory.mktemp(name) / "host_check")
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", sanitize, "-fno-sanitize-recover=all",
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC, os.path.join(ROOT, "tests", "native", "host_check.cpp"),
+           os.path.join(CSRC, "layout.cpp"), os.path.join(CSRC, "host_ffn.cpp"), "-lpthread", "-o", exe]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
     return exe
+
+
+@pytest.fixture(scope="module")
+def host_check(tmp_path_factory):
+    return _build(tmp_path_factory, "asan", "-fsanitize=address,undefined")
+
+
+@pytest.fixture(scope="module")
+def host_check_tsan(tmp_path_factory):
+    return _build(tmp_path_factory, "tsan", "-fsanitize=thread")
 
 
 CASES = [(ms.FMT_MXFP4, 256, 128, 1), (ms.FMT_MXFP4, 384, 256, 5), (ms.FMT_NVFP4, 256, 384, 3),
@@ -67,3 +76,19 @@ def test_repack_and_host_expert_under_sanitizers(host_check, tmp_path, case, por
     want = ffn.weighted_rows(ffn.expert_forward(F.bf16_from_bits(x_bits), wg, wu, wd), w)
     rel = np.linalg.norm(p - want) / np.linalg.norm(want)
     assert rel <= 2e-3, rel
+
+
+@pytest.mark.parametrize("case", CASES[:3], ids=lambda c: f"{ms.FMT_NAMES[c[0]]}-H{c[1]}-I{c[2]}-rows{c[3]}")
+def test_host_worker_pool_under_thread_sanitizer(host_check_tsan, tmp_path, case):
+    """The host worker pool (persistent threads taking work items) runs the
+    expert without a data race that ThreadSanitizer can see."""
+    fmt, H, I, rows = case
+    blob = ms.gen_blob(92, ms.KIND_EXPERT, fmt, H, I, 7)
+    x_bits = ms.f32_to_bf16_bits(np.random.default_rng(3).standard_normal((rows, H)).astype(np.float32))
+    blob.tofile(tmp_path / "blob.bin")
+    x_bits.astype(np.uint16).tofile(tmp_path / "x.bin")
+    np.full(rows, 0.5, np.float32).tofile(tmp_path / "w.bin")
+    env = dict(os.environ, TSAN_OPTIONS="halt_on_error=1")
+    r = subprocess.run([host_check_tsan, str(fmt), str(H), str(I), str(rows), "4", str(tmp_path)],
+                       capture_output=True, text=True, env=env, timeout=600)
+    assert r.returncode == 0 and "ThreadSanitizer" not in r.stderr, r.stderr[-4000:]
