@@ -243,8 +243,8 @@ __device__ inline void tile_mma_sc(const TileRegs<FMT>& r, const uint4 xv[4], fl
 // a step that are not streamed (tokens, routing weights, tensor scales) are
 // made when an item starts, before its first prefetch; a prefetch past the end
 // reads one shared line instead of branching.  Groups with more than 16 rows
-// (at most 64) stream their weights once per 16 rows (decode calls have few
-// such rows).
+// (at most 64) multiply each weight tile by every 16-row chunk of their
+// activations, so the weights are read once whatever the row count.
 // f(integral_constant<0>) ... f(integral_constant<N-1>): ring slots indexed at compile time
 template <typename F, int... I>
 __device__ __attribute__((always_inline)) inline void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
@@ -276,11 +276,12 @@ __device__ inline void load_tile_sel(TileRegs<FMT>& r, const uint8_t* __restrict
   }
 }
 
-template <int FMT, bool GATEUP, int D>
+template <int FMT, bool GATEUP, int D, int NC>
 __global__ __launch_bounds__(64 * kStreamWaves) void k_ffn_stream(FfnArgs a) {
   constexpr int NM = GATEUP ? 2 : 1;
   constexpr bool F8 = FMT == FT_FMT_FP8_B128;
-  __shared__ uint4 xs[2][256];  // activation tile: 16 rows x 128 K bf16, swizzled
+  // per K step, the activation tile of each row chunk: 16 rows x 128 K bf16, swizzled
+  __shared__ uint4 xs[2][NC][256];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int q = lane >> 4, n = lane & 15;
@@ -290,7 +291,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_ffn_stream(FfnArgs a) {
   const int n_list = min(a.n_list, *a.n_list_dev);
   const int n_items = n_list * nfb;
   const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.gdesc);
-  // this thread's piece of the activation tile: row xr, 8 K values at chunk xc
+  // this thread's piece of an activation tile: row xr, 8 K values at chunk xc
   const int xr = tid >> 4, xc = tid & 15;
   const int xslot = xr * 16 + (xc ^ xr);
   int par = 0;  // LDS buffer parity, kept across items
@@ -301,16 +302,17 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_ffn_stream(FfnArgs a) {
     if (g.row_count <= 0 || g.wptr == 0) continue;  // uniform over the workgroup
     const int rb = (item - gi * nfb) * kStreamWaves + w;  // this wave's 16-row weight tile
     const uint8_t* W = reinterpret_cast<const uint8_t*>(g.wptr);
-    const int nrc = min((g.row_count + 15) >> 4, kStreamMaxChunks);
-    const int nsteps = nrc * nkb;
+    // row chunks of this group (uniform over the workgroup; the launch takes
+    // NC = the call's bound on the rows of any group, in chunks of 16)
+    const int nrc = min((g.row_count + 15) >> 4, NC);
 
     // per-item reads, made before the stream starts: per row chunk, this
     // thread's activation row (element offset from x) and, for down, the
-    // routing weight of the lane's epilogue row (vectors: indexed in registers)
-    i64x4 xoff;
-    f32x4 wr;
+    // routing weight of the lane's epilogue row
+    int64_t xoff[NC];
+    float wr[NC];
 #pragma unroll
-    for (int c = 0; c < kStreamMaxChunks; ++c) {
+    for (int c = 0; c < NC; ++c) {
       const int r = c * 16 + xr;
       const bool ok = c < nrc && r < g.row_count;
       const int row = g.row_begin + (ok ? r : 0);
@@ -323,15 +325,16 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_ffn_stream(FfnArgs a) {
     for (int mi = 0; mi < NM; ++mi)
       tsc[mi] = FMT == FT_FMT_NVFP4 ? gload<float>(W + a.lay.tscale_off + 4 * (GATEUP ? mi : 2)) : 1.0f;
 
-    // the ring: weights and the activation piece of steps s .. s+D-1
+    // the ring: weights and the activation pieces (one per row chunk) of
+    // K steps s .. s+D-1; each weight tile is read once and multiplied by
+    // every row chunk
     TileRegs<FMT> wring[D][NM];
     float4 sring[D][NM];
-    u32x4 xring[D];
-    auto fetch = [&](int slot_s, auto uc) {
+    u32x4 xring[D][NC];
+    auto fetch = [&](int t_s, auto uc) {
       constexpr int u = decltype(uc)::value;
-      const bool live = slot_s < nsteps;
-      const int c = live ? slot_s / nkb : 0;
-      const int t = live ? slot_s - c * nkb : 0;
+      const bool live = t_s < nkb;
+      const int t = live ? t_s : 0;
       const int64_t tile = int64_t(rb) * nkb + t;
 #pragma unroll
       for (int mi = 0; mi < NM; ++mi) {
@@ -340,25 +343,27 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_ffn_stream(FfnArgs a) {
         if constexpr (F8)
           sring[u][mi] = ld_f4(live ? W + m.scales_off + (tile * 16 + 4 * q) * 4 : dummy);
       }
-      const uint16_t* xp = a.x + xoff[c];
-      xring[u] = *reinterpret_cast<const u32x4*>(live ? xp + t * kTileK + xc * 8 : a.x);
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        if (c < nrc)
+          xring[u][c] = *reinterpret_cast<const u32x4*>(live ? a.x + xoff[c] + t * kTileK + xc * 8 : a.x);
     };
     static_for<D>([&](auto uc) { fetch(decltype(uc)::value, uc); });
 
-    floatx4 acc[NM];
+    floatx4 acc[NC][NM];
 #pragma unroll
-    for (int mi = 0; mi < NM; ++mi) acc[mi] = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < nsteps; s0 += D) {
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int mi = 0; mi < NM; ++mi) acc[c][mi] = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < nkb; s0 += D) {
       static_for<D>([&](auto uc) {
         constexpr int u = decltype(uc)::value;
         const int s = s0 + u;
-        // activation tile of step s -> LDS, then the operands of this wave
-        xs[par][xslot] = make_uint4(xring[u][0], xring[u][1], xring[u][2], xring[u][3]);
-        __syncthreads();
-        uint4 bx[4];
+        // activation tiles of step s -> LDS, then the operands of this wave
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bx[j] = xs[par][n * 16 + ((4 * q + j) ^ n)];
-        par ^= 1;
+        for (int c = 0; c < NC; ++c)
+          if (c < nrc) xs[par][c][xslot] = make_uint4(xring[u][c][0], xring[u][c][1], xring[u][c][2], xring[u][c][3]);
+        __syncthreads();
         TileRegs<FMT> wt[NM];
         float4 st[NM];
 #pragma unroll
@@ -368,41 +373,47 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_ffn_stream(FfnArgs a) {
         }
         fetch(s + D, uc);  // refill the slot just consumed
 #pragma unroll
-        for (int mi = 0; mi < NM; ++mi) {
-          if constexpr (F8)
-            tile_mma_sc<FMT>(wt[mi], bx, acc[mi], st[mi]);
-          else
-            tile_mma<FMT>(wt[mi], bx, acc[mi], nullptr);
-        }
-        const int t = s % nkb;
-        if (t == nkb - 1) {  // end of a row chunk: epilogue, lane holds features rb*16+4q+i of row c*16+n
-          const int c = s / nkb;
-          const int r = c * 16 + n;
-          if (r < g.row_count) {
-            const int row = g.row_begin + r;
-            const int o0 = rb * 16 + 4 * q;
-            uint16_t hv[4];
-            if constexpr (GATEUP) {
+        for (int c = 0; c < NC; ++c) {
+          if (c < nrc) {
+            uint4 bx[4];
 #pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const float gv = acc[0][i] * tsc[0];
-                const float uv = acc[1][i] * tsc[1];
-                hv[i] = f32_to_bf16_rne(gv / (1.0f + expf(-gv)) * uv);
-              }
-              *reinterpret_cast<uint2*>(a.out + int64_t(row) * a.inter + o0) =
-                  make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16), uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
-            } else {
-              const float wrow = wr[c];
+            for (int j = 0; j < 4; ++j) bx[j] = xs[par][c][n * 16 + ((4 * q + j) ^ n)];
 #pragma unroll
-              for (int i = 0; i < 4; ++i) hv[i] = f32_to_bf16_rne(wrow * (acc[0][i] * tsc[0]));
-              *reinterpret_cast<uint2*>(a.out + int64_t(row) * a.hidden + o0) =
-                  make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16), uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
+            for (int mi = 0; mi < NM; ++mi) {
+              if constexpr (F8)
+                tile_mma_sc<FMT>(wt[mi], bx, acc[c][mi], st[mi]);
+              else
+                tile_mma<FMT>(wt[mi], bx, acc[c][mi], nullptr);
             }
           }
-#pragma unroll
-          for (int mi = 0; mi < NM; ++mi) acc[mi] = {0.f, 0.f, 0.f, 0.f};
         }
+        par ^= 1;
       });
+    }
+    // epilogue: lane holds features rb*16+4q+i of row c*16+n of each chunk
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int r = c * 16 + n;
+      if (c < nrc && r < g.row_count) {
+        const int row = g.row_begin + r;
+        const int o0 = rb * 16 + 4 * q;
+        uint16_t hv[4];
+        if constexpr (GATEUP) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float gv = acc[c][0][i] * tsc[0];
+            const float uv = acc[c][1][i] * tsc[1];
+            hv[i] = f32_to_bf16_rne(gv / (1.0f + expf(-gv)) * uv);
+          }
+          *reinterpret_cast<uint2*>(a.out + int64_t(row) * a.inter + o0) =
+              make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16), uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) hv[i] = f32_to_bf16_rne(wr[c] * (acc[c][0][i] * tsc[0]));
+          *reinterpret_cast<uint2*>(a.out + int64_t(row) * a.hidden + o0) =
+              make_uint2(uint32_t(hv[0]) | (uint32_t(hv[1]) << 16), uint32_t(hv[2]) | (uint32_t(hv[3]) << 16));
+        }
+      }
     }
   }
 }
@@ -589,13 +600,16 @@ int64_t resident_grid(Kern k, int block) {
   return int64_t(per_cu) * std::max(cus, 1);
 }
 
-template <int FMT, bool GATEUP, int D>
+template <int FMT, bool GATEUP, int D, int NC>
 hipError_t launch_stream_d(const FfnArgs& a, hipStream_t st, Ev ev) {
-  static const int64_t cap = resident_grid(k_ffn_stream<FMT, GATEUP, D>, 64 * kStreamWaves);
+  static const int64_t cap = resident_grid(k_ffn_stream<FMT, GATEUP, D, NC>, 64 * kStreamWaves);
   const MatLayout& m = a.lay.m[GATEUP ? 0 : 2];
   const int64_t items = int64_t(a.n_list) * (m.rows / (kTileRows * kStreamWaves));
-  note_kernel(GATEUP, "k_ffn_stream", FMT, D == 4 ? "depth 4" : D == 3 ? "depth 3" : D == 2 ? "depth 2" : "depth 1");
-  ft_launch(k_ffn_stream<FMT, GATEUP, D>, dim3(unsigned(std::min(items, cap))), dim3(64 * kStreamWaves), st, ev, a);
+  char prm[48];
+  std::snprintf(prm, sizeof(prm), "depth %d, %d row chunk%s", D, NC, NC > 1 ? "s" : "");
+  note_kernel(GATEUP, "k_ffn_stream", FMT, prm);
+  ft_launch(k_ffn_stream<FMT, GATEUP, D, NC>, dim3(unsigned(std::min(items, cap))), dim3(64 * kStreamWaves), st, ev,
+            a);
   return hipGetLastError();
 }
 
@@ -1010,17 +1024,29 @@ hipError_t launch_wide_k(const FfnArgs& a, hipStream_t st, Ev ev, bool* done) {
 // Ring depth: the deepest (up to 4: deeper rings cost occupancy and measured
 // slower) that divides the K steps and keeps the weight ring within 80
 // registers.
+// Ring depth for NC row chunks: the registers of a ring slot (weights of
+// one K tile of each matrix, plus one activation piece per chunk beyond the
+// first) within a fixed budget; the depth must divide the K tiles.
+template <int FMT, bool GATEUP, int NC>
+hipError_t launch_stream_nc(const FfnArgs& a, hipStream_t st, Ev ev) {
+  const int nkb = a.lay.m[GATEUP ? 0 : 2].cols / kTileK;
+  constexpr int regs = (GATEUP ? 2 : 1) * (FMT == FT_FMT_FP8_B128 ? 12 : 5) + 4 * (NC - 1);  // per ring slot
+  constexpr int dmax = std::min(FT_STREAM_MAXD, (NC > 1 ? 96 : 80) / regs);
+  if (dmax >= 4 && nkb % 4 == 0) return launch_stream_d<FMT, GATEUP, (dmax >= 4 ? 4 : 1), NC>(a, st, ev);
+  if (dmax >= 3 && nkb % 3 == 0) return launch_stream_d<FMT, GATEUP, (dmax >= 3 ? 3 : 1), NC>(a, st, ev);
+  if (dmax >= 2 && nkb % 2 == 0) return launch_stream_d<FMT, GATEUP, (dmax >= 2 ? 2 : 1), NC>(a, st, ev);
+  return launch_stream_d<FMT, GATEUP, 1, NC>(a, st, ev);
+}
+
+// Row chunks of 16 the launch carries: enough for the call's bound on the
+// rows of any group (at most kStreamMaxChunks), so every group's weights
+// are read once whatever its row count.
 template <int FMT, bool GATEUP>
 hipError_t launch_stream(const FfnArgs& a, hipStream_t st, Ev ev) {
-  const int nkb = a.lay.m[GATEUP ? 0 : 2].cols / kTileK;
-  constexpr int regs = (GATEUP ? 2 : 1) * (FMT == FT_FMT_FP8_B128 ? 12 : 5);  // per ring slot
-  constexpr int dmax = std::min(FT_STREAM_MAXD, 80 / regs);
-  if (dmax >= 8 && nkb % 8 == 0) return launch_stream_d<FMT, GATEUP, (dmax >= 8 ? 8 : 1)>(a, st, ev);
-  if (dmax >= 6 && nkb % 6 == 0) return launch_stream_d<FMT, GATEUP, (dmax >= 6 ? 6 : 1)>(a, st, ev);
-  if (dmax >= 4 && nkb % 4 == 0) return launch_stream_d<FMT, GATEUP, (dmax >= 4 ? 4 : 1)>(a, st, ev);
-  if (dmax >= 3 && nkb % 3 == 0) return launch_stream_d<FMT, GATEUP, (dmax >= 3 ? 3 : 1)>(a, st, ev);
-  if (dmax >= 2 && nkb % 2 == 0) return launch_stream_d<FMT, GATEUP, 2>(a, st, ev);
-  return launch_stream_d<FMT, GATEUP, 1>(a, st, ev);
+  const int chunks = a.max_rows > 0 ? (a.max_rows + kTileRows - 1) / kTileRows : kStreamMaxChunks;
+  if (chunks <= 1) return launch_stream_nc<FMT, GATEUP, 1>(a, st, ev);
+  if (chunks <= 2) return launch_stream_nc<FMT, GATEUP, 2>(a, st, ev);
+  return launch_stream_nc<FMT, GATEUP, 4>(a, st, ev);
 }
 
 // Ring kernel split: the most K tiles per wave (at most 4) that divide K with
