@@ -7,7 +7,9 @@ layers MXFP4 and odd layers FP8 with a fp32 scale per 128 weights, Zipf(1.2)
 popularity redrawn every 32 steps, one global LRU pool of 1027 slots (40 GB
 of the largest expert size), batch 32, with the hybrid strategy: each step's
 misses are split between host-core compute and PCIe streaming at the share
-the library measures on this machine (ft_moe_measure_mode's balanced share).
+the library measures on this machine (ft_moe_measure_mode's balanced share),
+refined per weight format after each warm-up step from the copy and host
+rates the library observed in it (ft_moe_rebalance).
 The store uses host-blob aliasing (key (l, e) reads blob (l*E + e) mod 256
 per format) so that it fits the host; keys, cache decisions and the bytes
 moved are those of the full model.
@@ -200,7 +202,16 @@ class DecodeRun:
 
     def timed(self, warmup, steps, timed_layers):
         ft, torch = self.ft, self.torch
-        self.steps(0, warmup)
+        self.rebalances = []
+        for s in range(warmup):
+            self.steps(s, 1)
+            if self.w.hybrid:
+                # bandwidth-adaptive refinement: each format's share from the
+                # copy and host rates the library observed in this step
+                rep = ft.ft_moe_rebalance(self.pool, apply=True)
+                self.rebalances.append(rep)
+                log("[bench] warm-up step %d: shares %s" % (s, {FMT_NAME[f]: round(rep["share"][f], 4)
+                                                                for f in range(1, 4) if rep["changed"][f]}))
         torch.cuda.synchronize()
         ft.ft_moe_pool_stats(self.pool, reset=True)
         ft.ft_moe_set_profiling(self.pool, [])
@@ -497,8 +508,9 @@ def main():
         # so the events cost nothing measurable)
         big = max(set(w.layer_fmt), key=lambda f: ms.expert_bytes(f, w.hidden, w.inter))
         big_layers = tuple(l for l in range(L) if w.fmt(l) == big)
-        share_used = run.share
         elapsed, kernel, prof, st = run.timed(args.warmup, args.steps, lambda s: big_layers)
+        shares = {f: ft.ft_moe_get_hybrid_share(run.pool, f) for f in sorted(set(w.layer_fmt))}
+        share_used = {FMT_NAME[f]: v for f, v in shares.items()} if w.hybrid else 0.0
         log(f"[bench] timed {args.steps} steps in {elapsed:.3f} s")
         nb = min(2, args.steps)
         stages = run.breakdown(args.warmup, nb)
@@ -515,10 +527,18 @@ def main():
                 "t_cpu_ms": rep["t_cpu"] * 1e3, "rows_per_expert": rep["tokens"],
                 **{f"{k}_GBps_{FMT_NAME[f]}": rep[f"{k}_bytes_per_s"][f] / 1e9 for k in ("h2d", "gpu", "cpu")
                    for f in fm}}
+            # the in-situ refinement after each warm-up step (ft_moe_rebalance)
+            extras["hybrid_measurement"]["rebalance"] = [
+                {FMT_NAME[f]: {"share": r["share"][f],
+                               "host_GBps": r["host_bytes"][f] / r["host_seconds"][f] / 1e9
+                               if r["host_seconds"][f] > 0 else None,
+                               "copy_GBps": r["copy_bytes"][f] / r["copy_seconds"][f] / 1e9
+                               if r["copy_seconds"][f] > 0 else None} for f in fm}
+                for r in run.rebalances]
         cpu = None
         if not args.no_cpu_baseline:
             t = time.perf_counter()
-            cpu = cpu_baseline(w, B, args.cpu_calls, run.share, run.store.expert)
+            cpu = cpu_baseline(w, B, args.cpu_calls, shares if w.hybrid else 0.0, run.store.expert)
             log(f"[bench] cpu baseline {time.perf_counter() - t:.1f} s")
     finally:
         run.close()

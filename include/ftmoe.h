@@ -265,12 +265,19 @@ int ft_moe_resize_pool(ft_moe_pool *p, int64_t new_slots);
  * capturing, and ft_moe_last_misses reports the most recent eager call. */
 int ft_moe_reserve(ft_moe_pool *p, int32_t max_tokens);
 
-/* Set the hybrid share used by later calls (0..1).  0 is the offload
- * strategy (every miss streams); 1 is the cpu strategy (every miss is computed
- * on host cores and the pool never changes) -- devpik "FreeToken: Run
- * Frontier MoE Models on Your Own GPU, and the RAM It Takes", section "Why a
- * Huge MoE Model Fits on One Consumer GPU". */
+/* Set the hybrid share used by later calls (0..1), for layers of every
+ * weight format.  0 is the offload strategy (every miss streams); 1 is the cpu
+ * strategy (every miss is computed on host cores and the pool never changes)
+ * -- devpik "FreeToken: Run Frontier MoE Models on Your Own GPU, and the RAM
+ * It Takes", section "Why a Huge MoE Model Fits on One Consumer GPU".  A call
+ * on a layer uses the share of that layer's format (the split rule itself is
+ * unchanged: m_cpu = floor(m * share + 1/2)).  Clears the in-situ
+ * observations of ft_moe_rebalance. */
 int ft_moe_set_hybrid_share(ft_moe_pool *p, double share);
+/* The same for the layers of one format fmt (FT_FMT_*) only. */
+int ft_moe_set_hybrid_share_format(ft_moe_pool *p, int32_t fmt, double share);
+/* The share in use for layers of format fmt. */
+int ft_moe_get_hybrid_share(const ft_moe_pool *p, int32_t fmt, double *share);
 
 /* One-time strategy choice from measured rates (mindstudio "FreeToken
  * Explained: Run 290B+ MoE Models on One Gaming GPU", section "How does the
@@ -315,9 +322,35 @@ int ft_moe_decide_mode(ft_moe_mode_report *r);
  * each (gpu), and the host expert path runs on all of them in one batched
  * call, as a step's host-computed misses do (cpu).  Takes
  * about a second; synchronises the device; allocates and frees the temporary
- * buffer; does not touch the slot table or the counters.  apply != 0 sets the
- * pool's hybrid share to the chosen share.  1 <= tokens <= 64. */
+ * buffer; does not touch the slot table or the counters.  Keeps the device FFN
+ * rates for ft_moe_rebalance.  apply != 0 sets the pool's hybrid share, for
+ * every format, to the chosen share.  1 <= tokens <= 64. */
 int ft_moe_measure_mode(ft_moe_pool *p, int32_t tokens, int32_t apply, ft_moe_mode_report *out);
+
+/* Bandwidth-adaptive refinement of the hybrid split from the running
+ * workload (dev.to "FreeToken uses bandwidth-adaptive CPU-GPU co-execution on
+ * your desktop", section "What the project says it does").  Since the last
+ * share change (or rebalance) every host-driven decode call has recorded, per
+ * weight format, the expert bytes its host worker threads computed and their
+ * wall time, and the expert bytes it streamed and their copy time (HIP events
+ * around the copies).  For each format with both, the new share is the
+ * balanced split of ft_moe_decide_mode with these in-situ costs per byte:
+ * t_stream = copy seconds / copy bytes + 1 / (device FFN rate of the last
+ * ft_moe_measure_mode, the term left out if none), t_cpu = host seconds /
+ * host bytes, share = t_stream / (t_stream + t_cpu).  Formats without both
+ * observations keep their share (changed[f] = 0).  Waits for the pool's
+ * outstanding copies; apply != 0 sets the new shares; the observations are
+ * cleared either way.  Arrays are indexed by FT_FMT_* (index 0 unused). */
+typedef struct {
+  double host_bytes[4];       /* expert bytes computed on host cores */
+  double host_seconds[4];     /* their wall time (the host worker phase of each call) */
+  double copy_bytes[4];       /* expert bytes streamed host -> device */
+  double copy_seconds[4];     /* their copy time */
+  double gpu_bytes_per_s[4];  /* device FFN rate from the last mode measurement, 0 if none */
+  double share[4];            /* the refined share (the current one where changed[f] = 0) */
+  int32_t changed[4];
+} ft_moe_rebalance_report;
+int ft_moe_rebalance(ft_moe_pool *p, int32_t apply, ft_moe_rebalance_report *out);
 
 /* Time the host expert path on `tokens` rows of one expert of `layer`
  * (the one-time bandwidth measurement behind the hybrid share); returns

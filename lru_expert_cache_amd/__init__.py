@@ -36,7 +36,8 @@ EXPORTED = ["ft_moe_init_pool", "ft_moe_layer_forward", "ft_moe_pool_stats", "ft
             "ft_moe_pool_table", "ft_moe_set_hybrid_share", "ft_moe_host_expert_rate",
             "ft_moe_set_profiling", "ft_moe_profile_read", "ft_moe_destroy_pool", "ft_moe_last_error",
             "ft_moe_reserve", "ft_moe_resize_pool", "ft_moe_decide_mode", "ft_moe_measure_mode",
-            "ft_moe_ffn_kernel_name", "ft_moe_mfma_rate", "ft_moe_layer_forward_noalloc"]
+            "ft_moe_ffn_kernel_name", "ft_moe_mfma_rate", "ft_moe_layer_forward_noalloc",
+            "ft_moe_set_hybrid_share_format", "ft_moe_get_hybrid_share", "ft_moe_rebalance"]
 
 FT_MODE_OFFLOAD, FT_MODE_HYBRID, FT_MODE_FUSED = 0, 1, 2
 
@@ -87,6 +88,15 @@ class ft_moe_mode_report(ctypes.Structure):
         return d
 
 
+class ft_moe_rebalance_report(ctypes.Structure):
+    _fields_ = [("host_bytes", ctypes.c_double * 4), ("host_seconds", ctypes.c_double * 4),
+                ("copy_bytes", ctypes.c_double * 4), ("copy_seconds", ctypes.c_double * 4),
+                ("gpu_bytes_per_s", ctypes.c_double * 4), ("share", ctypes.c_double * 4),
+                ("changed", ctypes.c_int32 * 4)]
+
+    as_dict = ft_moe_mode_report.as_dict
+
+
 class ft_moe_profile(ctypes.Structure):
     _fields_ = [("ms", ctypes.c_double * len(FT_STAGES)), ("bytes", ctypes.c_double * len(FT_STAGES)),
                 ("flops", ctypes.c_double * len(FT_STAGES)), ("launches", ctypes.c_uint64 * len(FT_STAGES))]
@@ -135,6 +145,12 @@ def lib() -> ctypes.CDLL:
     L.ft_moe_reserve.restype = ctypes.c_int
     L.ft_moe_set_hybrid_share.argtypes = [P, ctypes.c_double]
     L.ft_moe_set_hybrid_share.restype = ctypes.c_int
+    L.ft_moe_set_hybrid_share_format.argtypes = [P, ctypes.c_int32, ctypes.c_double]
+    L.ft_moe_set_hybrid_share_format.restype = ctypes.c_int
+    L.ft_moe_get_hybrid_share.argtypes = [P, ctypes.c_int32, ctypes.POINTER(ctypes.c_double)]
+    L.ft_moe_get_hybrid_share.restype = ctypes.c_int
+    L.ft_moe_rebalance.argtypes = [P, ctypes.c_int32, ctypes.POINTER(ft_moe_rebalance_report)]
+    L.ft_moe_rebalance.restype = ctypes.c_int
     L.ft_moe_host_expert_rate.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                           ctypes.POINTER(ctypes.c_double)]
     L.ft_moe_host_expert_rate.restype = ctypes.c_int
@@ -301,6 +317,22 @@ def ft_moe_reserve(pool, max_tokens: int):
 
 def ft_moe_set_hybrid_share(pool, share: float):
     _check(lib().ft_moe_set_hybrid_share(pool, float(share)))
+
+
+def ft_moe_set_hybrid_share_format(pool, fmt: int, share: float):
+    _check(lib().ft_moe_set_hybrid_share_format(pool, int(fmt), float(share)))
+
+
+def ft_moe_get_hybrid_share(pool, fmt: int) -> float:
+    v = ctypes.c_double()
+    _check(lib().ft_moe_get_hybrid_share(pool, int(fmt), ctypes.byref(v)))
+    return v.value
+
+
+def ft_moe_rebalance(pool, apply: bool = True) -> dict:
+    r = ft_moe_rebalance_report()
+    _check(lib().ft_moe_rebalance(pool, int(bool(apply)), ctypes.byref(r)))
+    return r.as_dict()
 
 
 def ft_moe_host_expert_rate(pool, layer: int, tokens: int, iters: int = 1) -> float:

@@ -103,6 +103,71 @@ inline void decode_lane(const Tables& tb, const ExpertLayout& L, const uint8_t* 
   }
 }
 
+// AVX2: the 32 weights of lane `lane` of tile `tile` of matrix M as four
+// 8-float vectors, the same values as decode_lane.  E2M1: pshufb on the
+// nibbles with a table of 2 x the element values, widened and scaled by half
+// the block scale.  E4M3: the code's bits moved into an fp32 and rescaled by a
+// power of two; the value table only where a lane holds a NaN code.
+__attribute__((target("avx2,fma"))) inline void decode_lane_avx2(const MatLayout& M, int fmt, const uint8_t* blob,
+                                                                  int64_t tile, int lane, float g, __m256 w[4]) {
+  const Tables& tb = tables();
+  if (fmt == FT_FMT_FP8_B128) {
+    const uint8_t* c = blob + M.codes_off + (tile * 64 + lane) * 32;
+    float sc;
+    std::memcpy(&sc, blob + M.scales_off + (tile * 16 + (lane & 15)) * 4, 4);
+    const __m256 vs = _mm256_set1_ps(sc);
+    const __m256i abs7 = _mm256_set1_epi8(0x7F);
+    const __m256i cb = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(c));
+    if (!_mm256_testz_si256(_mm256_cmpeq_epi8(_mm256_and_si256(cb, abs7), abs7), abs7)) {
+      // a NaN code (S.1111.111) among the 32: the table keeps it NaN
+      for (int v = 0; v < 4; ++v) {
+        const __m256i idx = _mm256_cvtepu8_epi32(_mm_loadl_epi64(reinterpret_cast<const __m128i*>(c + 8 * v)));
+        w[v] = _mm256_mul_ps(_mm256_i32gather_ps(tb.e4m3, idx, 4), vs);
+      }
+      return;
+    }
+    // S.EEEE.MMM placed as the fp32 bits S.0000EEEE.MMM0..0 reads as 2^-120
+    // times the E4M3 value, subnormals included (an fp32 subnormal then):
+    // times 2^120 is exact, times the block scale rounds once.
+    const __m256i keep = _mm256_set1_epi32(int32_t(0x87F00000u));
+    const __m256 two120 = _mm256_set1_ps(0x1p120f);
+    for (int v = 0; v < 4; ++v) {
+      const __m256i s32 = _mm256_cvtepi8_epi32(_mm_loadl_epi64(reinterpret_cast<const __m128i*>(c + 8 * v)));
+      const __m256 f = _mm256_castsi256_ps(_mm256_and_si256(_mm256_slli_epi32(s32, 20), keep));
+      w[v] = _mm256_mul_ps(_mm256_mul_ps(f, two120), vs);
+    }
+    return;
+  }
+  const uint8_t* c = blob + M.codes_off + (tile * 64 + lane) * 16;
+  float s0, s1;
+  if (fmt == FT_FMT_MXFP4) {
+    s0 = s1 = e8m0_value(blob[M.scales_off + tile * 64 + lane]);
+  } else {
+    const uint8_t* sp = blob + M.scales_off + (tile * 64 + lane) * 2;
+    s0 = tb.e4m3[sp[0]] * g;
+    s1 = tb.e4m3[sp[1]] * g;
+  }
+  const __m128i lut2 = _mm_setr_epi8(0, 1, 2, 3, 4, 6, 8, 12, 0, -1, -2, -3, -4, -6, -8, -12);
+  const __m128i lo4 = _mm_set1_epi8(0x0F);
+  const __m128i b = _mm_loadu_si128(reinterpret_cast<const __m128i*>(c));
+  const __m128i lo = _mm_and_si128(b, lo4), hi = _mm_and_si128(_mm_srli_epi16(b, 4), lo4);
+  // elements 0..15 and 16..31 (element 2i = low nibble of byte i), as 2 x value
+  const __m128i e0 = _mm_shuffle_epi8(lut2, _mm_unpacklo_epi8(lo, hi));
+  const __m128i e1 = _mm_shuffle_epi8(lut2, _mm_unpackhi_epi8(lo, hi));
+  const __m256 h0 = _mm256_set1_ps(0.5f * s0), h1 = _mm256_set1_ps(0.5f * s1);
+  w[0] = _mm256_mul_ps(_mm256_cvtepi32_ps(_mm256_cvtepi8_epi32(e0)), h0);
+  w[1] = _mm256_mul_ps(_mm256_cvtepi32_ps(_mm256_cvtepi8_epi32(_mm_srli_si128(e0, 8))), h0);
+  w[2] = _mm256_mul_ps(_mm256_cvtepi32_ps(_mm256_cvtepi8_epi32(e1)), h1);
+  w[3] = _mm256_mul_ps(_mm256_cvtepi32_ps(_mm256_cvtepi8_epi32(_mm_srli_si128(e1, 8))), h1);
+}
+
+__attribute__((target("avx2,fma"))) void decode_lane_avx2_store(const MatLayout& M, int fmt, const uint8_t* blob,
+                                                                 int64_t tile, int lane, float g, float* out) {
+  __m256 w[4];
+  decode_lane_avx2(M, fmt, blob, tile, lane, g, w);
+  for (int v = 0; v < 4; ++v) _mm256_storeu_ps(out + 8 * v, w[v]);
+}
+
 // Sums over K of the tiles of row blocks [rb_begin, rb_end) of matrices
 // m0 .. m0 + nm - 1 against `rows` input rows xf [rows][K]; acc receives
 // [matrix][row][16] per row block and `finish(rb, acc)` consumes it.
@@ -142,26 +207,21 @@ struct RowBlocks<false> {
     FT_HOST_BODY
   }
 };
-// AVX2 + FMA: a lane's 32 weights decode as four 8-float vectors (E2M1:
-// pshufb on the nibbles with a table of 2 x the element values, widened and
-// scaled by half the block scale; E4M3: gathers from the value table), and
-// each (lane, input row) keeps an 8-wide partial sum across the K tiles of the
-// row block, added up once at its end.
+// AVX2 + FMA: a lane's 32 weights decode as four 8-float vectors
+// (decode_lane_avx2), and each (lane, input row) keeps an 8-wide partial sum
+// across the K tiles of the row block, added up once at its end.
 template <>
 struct RowBlocks<true> {
   __attribute__((target("avx2,fma"))) static void run(const ExpertLayout& L, const uint8_t* blob, int m0, int nm,
                                                        const float* gsc, const float* xf, int rows, int rb_begin,
                                                        int rb_end,
                                                        const std::function<void(int, const float*)>& finish) {
-    const Tables& tb = tables();
     const int K = L.m[m0].cols, nkb = K / kTileK;
     const int fmt = L.fmt;
     thread_local std::vector<float> acc;
     thread_local std::vector<__m256> part;
     acc.resize(size_t(nm) * rows * 16);
     part.resize(size_t(64) * rows);
-    const __m128i lut2 = _mm_setr_epi8(0, 1, 2, 3, 4, 6, 8, 12, 0, -1, -2, -3, -4, -6, -8, -12);
-    const __m128i lo4 = _mm_set1_epi8(0x0F);
     for (int rb = rb_begin; rb < rb_end; ++rb) {
       std::fill(acc.begin(), acc.end(), 0.0f);
       for (int mi = 0; mi < nm; ++mi) {
@@ -171,36 +231,7 @@ struct RowBlocks<true> {
           const int64_t tile = int64_t(rb) * nkb + kb;
           for (int lane = 0; lane < 64; ++lane) {
             __m256 w[4];
-            if (fmt == FT_FMT_FP8_B128) {
-              const uint8_t* c = blob + M.codes_off + (tile * 64 + lane) * 32;
-              float sc;
-              std::memcpy(&sc, blob + M.scales_off + (tile * 16 + (lane & 15)) * 4, 4);
-              const __m256 vs = _mm256_set1_ps(sc);
-              for (int v = 0; v < 4; ++v) {
-                const __m256i idx = _mm256_cvtepu8_epi32(_mm_loadl_epi64(reinterpret_cast<const __m128i*>(c + 8 * v)));
-                w[v] = _mm256_mul_ps(_mm256_i32gather_ps(tb.e4m3, idx, 4), vs);
-              }
-            } else {
-              const uint8_t* c = blob + M.codes_off + (tile * 64 + lane) * 16;
-              float s0, s1;
-              if (fmt == FT_FMT_MXFP4) {
-                s0 = s1 = e8m0_value(blob[M.scales_off + tile * 64 + lane]);
-              } else {
-                const uint8_t* sp = blob + M.scales_off + (tile * 64 + lane) * 2;
-                s0 = tb.e4m3[sp[0]] * gsc[mi];
-                s1 = tb.e4m3[sp[1]] * gsc[mi];
-              }
-              const __m128i b = _mm_loadu_si128(reinterpret_cast<const __m128i*>(c));
-              const __m128i lo = _mm_and_si128(b, lo4), hi = _mm_and_si128(_mm_srli_epi16(b, 4), lo4);
-              // elements 0..15 and 16..31 (element 2i = low nibble of byte i), as 2 x value
-              const __m128i e0 = _mm_shuffle_epi8(lut2, _mm_unpacklo_epi8(lo, hi));
-              const __m128i e1 = _mm_shuffle_epi8(lut2, _mm_unpackhi_epi8(lo, hi));
-              const __m256 h0 = _mm256_set1_ps(0.5f * s0), h1 = _mm256_set1_ps(0.5f * s1);
-              w[0] = _mm256_mul_ps(_mm256_cvtepi32_ps(_mm256_cvtepi8_epi32(e0)), h0);
-              w[1] = _mm256_mul_ps(_mm256_cvtepi32_ps(_mm256_cvtepi8_epi32(_mm_srli_si128(e0, 8))), h0);
-              w[2] = _mm256_mul_ps(_mm256_cvtepi32_ps(_mm256_cvtepi8_epi32(e1)), h1);
-              w[3] = _mm256_mul_ps(_mm256_cvtepi32_ps(_mm256_cvtepi8_epi32(_mm_srli_si128(e1, 8))), h1);
-            }
+            decode_lane_avx2(M, fmt, blob, tile, lane, gsc[mi], w);
             const int k0 = kb * kTileK + 32 * (lane >> 4);
             for (int t = 0; t < rows; ++t) {
               const float* xr = xf + size_t(t) * K + k0;
@@ -373,6 +404,16 @@ void host_experts(const ExpertLayout& L, const HostExpertJob* jobs, int n, Worke
                      jb.out[size_t(t) * H + rb * kTileRows + r] = f32_to_bf16(jb.w[t] * acc[size_t(t) * 16 + r]);
                });
   });
+}
+
+void host_decode_lane(const ExpertLayout& L, const uint8_t* blob, int m, int64_t tile, int lane, float* w) {
+  float g = 1.0f;
+  if (L.fmt == FT_FMT_NVFP4) std::memcpy(&g, blob + L.tscale_off + 4 * m, 4);
+  if (cpu_has_avx2_fma()) {
+    decode_lane_avx2_store(L.m[m], L.fmt, blob, tile, lane, g, w);
+    return;
+  }
+  decode_lane(tables(), L, blob, m, tile, lane, g, w);
 }
 
 void host_expert(const ExpertLayout& L, const uint8_t* blob, const uint16_t* x, const float* wts, int rows,

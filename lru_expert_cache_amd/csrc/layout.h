@@ -81,6 +81,10 @@ struct HostExpertJob {
 // gate/up row blocks of every expert, then the down row blocks (one work item
 // per few row blocks of one expert).
 void host_experts(const ExpertLayout& L, const HostExpertJob* jobs, int n, WorkerPool& pool);
+// The 32 fp32 weights that the host FFN decodes for lane `lane` of tile `tile`
+// of matrix m (row lane % 16 of the tile, K 32 (lane / 16) .. + 31), in the
+// build the CPU runs (the AVX2 one where it can).
+void host_decode_lane(const ExpertLayout& L, const uint8_t* blob, int m, int64_t tile, int lane, float* w);
 // One expert on a temporary pool of `threads` threads.
 void host_expert(const ExpertLayout& L, const uint8_t* blob, const uint16_t* x, const float* wts, int rows,
                  uint16_t* out, int threads);

@@ -51,7 +51,13 @@ struct ft_moe_pool {
   ExpertLayout lay[4];
   int64_t canon_bytes[4] = {0, 0, 0, 0};
   int64_t slot_bytes = 0;
-  double share = 0.0;
+  double share_fmt[4] = {0.0, 0.0, 0.0, 0.0};  // hybrid share of each weight format (index FT_FMT_*)
+  double gpu_rate[4] = {0.0, 0.0, 0.0, 0.0};   // device FFN bytes/s from the last mode measurement
+  // in-situ observations of the hybrid path since the last share change
+  // (ft_moe_rebalance): host-computed and streamed expert bytes and times
+  struct Obs {
+    double host_bytes = 0.0, host_sec = 0.0, copy_bytes = 0.0, copy_ms = 0.0;
+  } obs[4];
 
   // pinned host store (device layout), one entry per distinct (blob, format)
   uint8_t* host_store = nullptr;
@@ -159,6 +165,7 @@ struct ft_moe_pool {
   struct CopyRec {
     int layer;
     hipEvent_t a, b;
+    double bytes;  // streamed expert bytes (decode calls) for the in-situ rates, else 0
   };
   std::vector<CopyRec> copy_pending;
 
@@ -414,7 +421,7 @@ ResolveArgs resolve_args(ft_moe_pool* p, int layer, int T, int t0, int mode) {
   a.C = int(p->C);
   a.mode = mode;
   a.stamp = p->stamp++;
-  a.share = p->share;
+  a.share = p->share_fmt[p->fmt[layer]];
   a.expert_bytes = p->canon_bytes[p->fmt[layer]];
   a.hidden = p->H;
   a.arena = reinterpret_cast<uint64_t>(p->arena);
@@ -492,7 +499,7 @@ hipEvent_t copy_timer_begin(ft_moe_pool* p, hipStream_t s) {
   return e;
 }
 
-void copy_timer_end(ft_moe_pool* p, int layer, hipEvent_t a, hipStream_t s) {
+void copy_timer_end(ft_moe_pool* p, int layer, hipEvent_t a, hipStream_t s, double obs_bytes = 0.0) {
   if (!a) return;
   hipEvent_t b = prof_event(p);
   if (!b || hipEventRecord(b, s) != hipSuccess) {
@@ -501,7 +508,7 @@ void copy_timer_end(ft_moe_pool* p, int layer, hipEvent_t a, hipStream_t s) {
     if (b) p->prof_free.push_back(b);
     return;
   }
-  p->copy_pending.push_back({layer, a, b});
+  p->copy_pending.push_back({layer, a, b, obs_bytes});
 }
 
 void copy_drain(ft_moe_pool* p, bool wait) {
@@ -514,7 +521,14 @@ void copy_drain(ft_moe_pool* p, bool wait) {
       continue;
     }
     float ms = 0.f;
-    if (hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) p->copy_ms_host[r.layer] += ms;
+    if (hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) {
+      p->copy_ms_host[r.layer] += ms;
+      if (r.bytes > 0.0) {
+        ft_moe_pool::Obs& o = p->obs[p->fmt[r.layer]];
+        o.copy_ms += ms;
+        o.copy_bytes += r.bytes;
+      }
+    }
     p->prof_free.push_back(r.a);
     p->prof_free.push_back(r.b);
   }
@@ -955,7 +969,7 @@ int forward_decode(ft_moe_pool* p, int layer, int T, const void* x, void* out, h
         FT_HIP_CHECK(hipStreamWaitEvent(p->copy[0], p->ev_copy_done[c], 0));
       }
       prof_end(p, FT_STAGE_COPY, ec, p->copy[0], double(h.n_stream) * double(p->canon_bytes[p->fmt[layer]]), 0.0);
-      copy_timer_end(p, layer, et, p->copy[0]);
+      copy_timer_end(p, layer, et, p->copy[0], double(h.n_stream) * double(p->canon_bytes[p->fmt[layer]]));
       FT_HIP_CHECK(hipEventRecord(p->ev_copied, p->copy[0]));
     }
 
@@ -1000,6 +1014,8 @@ int forward_decode(ft_moe_pool* p, int layer, int T, const void* x, void* out, h
     }
     if (cpu_thread.joinable()) {
       cpu_thread.join();
+      p->obs[p->fmt[layer]].host_sec += host_sec;
+      p->obs[p->fmt[layer]].host_bytes += double(h.n_cpu) * double(p->canon_bytes[p->fmt[layer]]);
       if (p->prof_mask & (1 << FT_STAGE_HOST_FFN)) {
         p->prof.ms[FT_STAGE_HOST_FFN] += host_sec * 1e3;
         p->prof.bytes[FT_STAGE_HOST_FFN] += double(h.n_cpu) * double(p->canon_bytes[p->fmt[layer]]);
@@ -1009,9 +1025,15 @@ int forward_decode(ft_moe_pool* p, int layer, int T, const void* x, void* out, h
     }
     if (rc) return rc;
     if (h.n_cpu > 0) {
-      for (int j = 0; j < h.n_cpu; ++j)
+      // one copy per run of host experts whose rows are adjacent in pbuf
+      for (int j = 0; j < h.n_cpu;) {
+        int j1 = j + 1;
+        int64_t rows = cc[j];
+        while (j1 < h.n_cpu && int64_t(cb[j1]) == int64_t(cb[j]) + rows) rows += cc[j1++];
         FT_HIP_CHECK(hipMemcpyAsync(p->pbuf + int64_t(cb[j]) * p->H, p->cpu_out + cpu_base[j] * p->H,
-                                    size_t(cc[j]) * p->H * 2, hipMemcpyHostToDevice, s));
+                                    size_t(rows) * p->H * 2, hipMemcpyHostToDevice, s));
+        j = j1;
+      }
       FT_HIP_CHECK(hipEventRecord(p->ev_cpu_copied, s));
       p->cpu_copy_pending = true;
     }
@@ -1079,7 +1101,7 @@ int ft_moe_init_pool(const ft_moe_config* cfg, const ft_moe_weights* wts, ft_moe
     p->shared = cfg->has_shared_expert ? 1 : 0;
     p->device = cfg->device;
     p->cpu_threads = cfg->cpu_threads > 0 ? cfg->cpu_threads : 8;
-    p->share = cfg->hybrid_cpu_share;
+    for (double& v : p->share_fmt) v = cfg->hybrid_cpu_share;
     p->fmt.assign(cfg->layer_fmt, cfg->layer_fmt + L);
     for (int f = 1; f <= 3; ++f) {
       p->lay[f] = make_layout(f, H, I);
@@ -1372,12 +1394,13 @@ int forward_impl(ft_moe_pool* p, int32_t layer, int32_t num_tokens, const void* 
     }
     if (num_tokens == 0) return FT_OK;
     const int T = num_tokens, E = p->E, k = p->k;
-    const bool dev_path = mode == FT_FWD_DECODE && p->dev_decode && p->share == 0.0 && int64_t(T) * k <= p->C;
+    const bool dev_path = mode == FT_FWD_DECODE && p->dev_decode && p->share_fmt[p->fmt[layer]] == 0.0 && int64_t(T) * k <= p->C;
     ScratchCarve carve{};
     if (noalloc) {
       if (!dev_path || flags != FT_FWD_DECODE) {
         set_error("ft_moe_layer_forward_noalloc runs device-driven decode calls only: flags FT_FWD_DECODE, no "
-                  "hybrid share, T*top_k <= pool slots (T=%d, flags 0x%x, share %g)", T, flags, p->share);
+                  "hybrid share, T*top_k <= pool slots (T=%d, flags 0x%x, share %g)", T, flags,
+                  p->share_fmt[p->fmt[layer]]);
         return FT_E_INVALID;
       }
       carve = carve_scratch(p, T, nullptr);
@@ -1711,7 +1734,59 @@ int ft_moe_set_hybrid_share(ft_moe_pool* p, double share) {
     set_error("share must be in [0,1]");
     return FT_E_INVALID;
   }
-  p->share = share;
+  for (double& v : p->share_fmt) v = share;
+  for (auto& o : p->obs) o = ft_moe_pool::Obs{};
+  return FT_OK;
+}
+
+int ft_moe_set_hybrid_share_format(ft_moe_pool* p, int32_t fmt, double share) {
+  if (!p || fmt < FT_FMT_MXFP4 || fmt > FT_FMT_FP8_B128 || !(share >= 0.0 && share <= 1.0)) {
+    set_error("need a pool, a format FT_FMT_* and a share in [0,1]");
+    return FT_E_INVALID;
+  }
+  p->share_fmt[fmt] = share;
+  p->obs[fmt] = ft_moe_pool::Obs{};
+  return FT_OK;
+}
+
+int ft_moe_get_hybrid_share(const ft_moe_pool* p, int32_t fmt, double* share) {
+  if (!p || fmt < FT_FMT_MXFP4 || fmt > FT_FMT_FP8_B128 || !share) {
+    set_error("need a pool, a format FT_FMT_* and an output");
+    return FT_E_INVALID;
+  }
+  *share = p->share_fmt[fmt];
+  return FT_OK;
+}
+
+int ft_moe_rebalance(ft_moe_pool* p, int32_t apply, ft_moe_rebalance_report* out) {
+  if (!p || !out) {
+    set_error("need a pool and a report");
+    return FT_E_INVALID;
+  }
+  DeviceGuard dg(p->device);
+  copy_drain(p, true);
+  ft_moe_rebalance_report r{};
+  for (int f = FT_FMT_MXFP4; f <= FT_FMT_FP8_B128; ++f) {
+    const ft_moe_pool::Obs& o = p->obs[f];
+    r.host_bytes[f] = o.host_bytes;
+    r.host_seconds[f] = o.host_sec;
+    r.copy_bytes[f] = o.copy_bytes;
+    r.copy_seconds[f] = o.copy_ms * 1e-3;
+    r.gpu_bytes_per_s[f] = p->gpu_rate[f];
+    r.share[f] = p->share_fmt[f];
+    if (o.host_bytes > 0.0 && o.host_sec > 0.0 && o.copy_bytes > 0.0 && o.copy_ms > 0.0) {
+      // seconds per expert byte on each side, as in the one-time decision
+      const double ts = o.copy_ms * 1e-3 / o.copy_bytes + (p->gpu_rate[f] > 0.0 ? 1.0 / p->gpu_rate[f] : 0.0);
+      const double tc = o.host_sec / o.host_bytes;
+      r.share[f] = ts / (ts + tc);
+      r.changed[f] = 1;
+    }
+  }
+  if (apply)
+    for (int f = FT_FMT_MXFP4; f <= FT_FMT_FP8_B128; ++f)
+      if (r.changed[f]) p->share_fmt[f] = r.share[f];
+  for (auto& o : p->obs) o = ft_moe_pool::Obs{};
+  *out = r;
   return FT_OK;
 }
 
@@ -1945,7 +2020,11 @@ int ft_moe_measure_mode(ft_moe_pool* p, int32_t tokens, int32_t apply, ft_moe_mo
   }
   FT_HIP_CHECK(hipDeviceSynchronize());
   if ((rc = ft_moe_decide_mode(&r))) return rc;
-  if (apply) p->share = r.share;
+  for (int f = 1; f <= 3; ++f) p->gpu_rate[f] = r.gpu_bytes_per_s[f];
+  if (apply) {
+    for (double& v : p->share_fmt) v = r.share;
+    for (auto& o : p->obs) o = ft_moe_pool::Obs{};
+  }
   *out = r;
   return FT_OK;
 }

@@ -46,12 +46,15 @@ class DequantCache:
 class OracleLayerStack:
     """Oracle state for one workload: the global pool plus per-layer weights."""
 
-    def __init__(self, w: ms.Workload, pool_slots: Optional[int] = None, share: float = 0.0,
+    def __init__(self, w: ms.Workload, pool_slots: Optional[int] = None, share=0.0,
                  act_mode: int = ffn.ACT_BF16, blob_fn: Optional[Callable] = None,
                  dequant_items: int = 64, threads: int = 1):
         self.w = w
         self.C = w.pool_slots if pool_slots is None else pool_slots
         self.pool = LRUPool(self.C)
+        # the hybrid share: one number for every layer, or a mapping from weight
+        # format to the share of that format's layers (the split rule is the
+        # same; only the share it is given differs by format)
         self.share = share
         self.act_mode = act_mode
         self._router = {}
@@ -63,6 +66,11 @@ class OracleLayerStack:
         self.threads = max(1, int(threads))
         self.stats = dict(pair_hits=0, pair_misses=0, expert_hits=0, expert_misses=0,
                           cpu_misses=0, evictions=0, bytes_h2d=0, calls=0)
+
+    def share_of(self, layer: int) -> float:
+        if isinstance(self.share, dict):
+            return float(self.share.get(self.w.fmt(layer), 0.0))
+        return float(self.share)
 
     def router_w(self, layer):
         if layer not in self._router:
@@ -105,7 +113,7 @@ class OracleLayerStack:
         else:
             st = dict(pair_hits=0, expert_hits=0, expert_misses=0, cpu_misses=0, evictions=0, bytes_h2d=0)
             for (t0, t1) in split_waves(sel, self.pool.C):
-                r = self.pool.resolve_wave(layer, sel[t0:t1], self.share)
+                r = self.pool.resolve_wave(layer, sel[t0:t1], self.share_of(layer))
                 flag[t0 * k:t1 * k] = r["flag"]
                 slot[t0 * k:t1 * k] = r["slot"]
                 waves.append(dict(t0=t0, t1=t1, **r))

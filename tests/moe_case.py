@@ -25,9 +25,13 @@ class GpuLayerStack:
         blobs = [self.store.expert(l, e) for l in range(L) for e in range(E)]
         router = np.stack([ms.router_weight(w, l) for l in range(L)])
         shared = [self.store.shared(l) for l in range(L)] if w.shared_expert else None
+        per_fmt = isinstance(share, dict)
         cfg = ft.make_config(L, w.hidden, w.inter, E, w.top_k, w.layer_fmt, pool_slots=self.C, shared=w.shared_expert,
-                             hybrid_cpu_share=share, device=device)
+                             hybrid_cpu_share=0.0 if per_fmt else share, device=device)
         self.pool, self.init_rc = ft.ft_moe_init_pool(cfg, blobs, router, shared)
+        if per_fmt and self.pool:
+            for f, v in share.items():
+                ft.ft_moe_set_hybrid_share_format(self.pool, f, v)
         self.dev = torch.device("cuda", device)
 
     def close(self):

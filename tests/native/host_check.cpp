@@ -9,6 +9,10 @@
 // <dir>/w.bin (fp32 [rows]); writes <dir>/mats.bin (fp64: gate [I][H], up
 // [I][H], down [H][I], decoded from the device layout) and <dir>/p.bin (bf16
 // [rows][hidden], the host expert's weighted rows).
+//
+//   host_check decode <fmt> <hidden> <inter> <dir>
+// reads <dir>/blob.bin and writes <dir>/dec.bin: fp32 gate, up, down as the
+// host FFN decodes them lane by lane, in [rows][cols] order.
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -35,7 +39,34 @@ static bool spill(const std::string& path, const void* p, size_t n) {
   return std::fclose(f) == 0 && ok;
 }
 
+static int decode_mode(int argc, char** argv) {
+  if (argc != 6) return 2;
+  const int fmt = std::atoi(argv[2]), H = std::atoi(argv[3]), I = std::atoi(argv[4]);
+  const std::string dir = argv[5];
+  const std::vector<unsigned char> blob = slurp(dir + "/blob.bin");
+  if (int64_t(blob.size()) != ftmoe::canonical_bytes(fmt, H, I)) return 2;
+  const ftmoe::ExpertLayout L = ftmoe::make_layout(fmt, H, I);
+  std::vector<uint8_t> dev(size_t(L.bytes));
+  ftmoe::repack_expert(L, blob.data(), dev.data());
+  std::vector<float> out;
+  for (int m = 0; m < 3; ++m) {
+    const int R = L.m[m].rows, K = L.m[m].cols, nkb = K / ftmoe::kTileK;
+    std::vector<float> mat(size_t(R) * K);
+    float w[32];
+    for (int rb = 0; rb < R / ftmoe::kTileRows; ++rb)
+      for (int kb = 0; kb < nkb; ++kb)
+        for (int lane = 0; lane < 64; ++lane) {
+          ftmoe::host_decode_lane(L, dev.data(), m, int64_t(rb) * nkb + kb, lane, w);
+          const int r = rb * ftmoe::kTileRows + (lane & 15), k0 = kb * ftmoe::kTileK + 32 * (lane >> 4);
+          std::memcpy(&mat[size_t(r) * K + k0], w, sizeof(w));
+        }
+    out.insert(out.end(), mat.begin(), mat.end());
+  }
+  return spill(dir + "/dec.bin", out.data(), out.size() * 4) ? 0 : 3;
+}
+
 int main(int argc, char** argv) {
+  if (argc >= 2 && std::string(argv[1]) == "decode") return decode_mode(argc, argv);
   if (argc != 7) {
     std::fprintf(stderr, "usage: host_check fmt hidden inter rows threads dir\n");
     return 2;

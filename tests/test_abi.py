@@ -55,7 +55,8 @@ def test_struct_layouts_match_header():
     # every struct the binding declares, field by field, against the C compiler
     structs = {"ft_moe_config": ft.ft_moe_config, "ft_moe_weights": ft.ft_moe_weights,
                "ft_moe_trace": ft.ft_moe_trace, "ft_moe_stats": ft.ft_moe_stats,
-               "ft_moe_mode_report": ft.ft_moe_mode_report, "ft_moe_profile": ft.ft_moe_profile}
+               "ft_moe_mode_report": ft.ft_moe_mode_report, "ft_moe_profile": ft.ft_moe_profile,
+               "ft_moe_rebalance_report": ft.ft_moe_rebalance_report}
     c = _c_layout({n: [f for f, _ in t._fields_] for n, t in structs.items()})
     for n, t in structs.items():
         assert c[(n, "size")] == ctypes.sizeof(t), n

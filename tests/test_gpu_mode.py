@@ -86,3 +86,83 @@ def test_pool_with_a_slot_for_every_expert_is_fused():
             ft.ft_moe_measure_mode(g.pool, 65)
     finally:
         g.close()
+
+
+def test_share_per_format_splits_each_layer_by_its_format():
+    """Each layer's misses split by the share of its weight format, exactly
+    as the oracle's split rule with that share."""
+    from tests.moe_case import GpuLayerStack, compare_call, compare_table
+    import lru_expert_cache_amd as ft
+
+    w = ms.Workload(133, "small-133", 3, 256, 256, 16, 4, (MX, F8, NV), 24, (4,), 4, "decode", None, None,
+                    True, False, None)
+    shares = {MX: 0.25, F8: 0.75, NV: 0.5}
+    g = GpuLayerStack(w, share=shares)
+    o = OracleLayerStack(w, pool_slots=g.C, share=shares)
+    try:
+        for f, v in shares.items():
+            assert ft.ft_moe_get_hybrid_share(g.pool, f) == v
+        for step in range(3):
+            for l in range(w.num_layers):
+                x = ms.activations(w, l, step, 5)
+                compare_call(g.forward(l, x, None), o.forward(l, x, None), w.top_k)
+        compare_table(g, o)
+        st = ft.ft_moe_pool_stats(g.pool)
+        assert st["cpu_misses"] == o.stats["cpu_misses"] > 0
+        with pytest.raises(ft.FtError):
+            ft.ft_moe_set_hybrid_share_format(g.pool, 4, 0.5)
+        with pytest.raises(ft.FtError):
+            ft.ft_moe_set_hybrid_share_format(g.pool, MX, 1.5)
+    finally:
+        g.close()
+
+
+def test_rebalance_from_in_situ_rates():
+    """ft_moe_rebalance: the bytes it observed are exactly the host-computed and
+    streamed expert bytes of the calls since the last share change (by
+    format, from the oracle's miss lists); the refined share of each format is
+    the balanced split of its observed costs per byte; later calls split by
+    the new shares exactly as the oracle does with them; the observations
+    start again from zero."""
+    from tests.moe_case import GpuLayerStack, compare_call, compare_table
+    import lru_expert_cache_amd as ft
+
+    w = ms.Workload(134, "small-134", 4, 256, 256, 16, 4, (MX, F8, MX, F8), 24, (4,), 4, "decode", None, None,
+                    False, False, None)
+    g = GpuLayerStack(w, share=0.5)
+    o = OracleLayerStack(w, pool_slots=g.C, share=0.5)
+    eb = {f: ms.expert_bytes(f, w.hidden, w.inter) for f in (MX, F8)}
+    host_b = {MX: 0, F8: 0}
+    copy_b = {MX: 0, F8: 0}
+    try:
+        rep0 = ft.ft_moe_measure_mode(g.pool, 4, apply=False)  # keeps the device FFN rates
+        for step in range(3):
+            for l in range(w.num_layers):
+                x = ms.activations(w, l, step, 6)
+                ro = o.forward(l, x, None)
+                compare_call(g.forward(l, x, None), ro, w.top_k)
+                f = w.fmt(l)
+                host_b[f] += eb[f] * sum(len(wv["cpu"]) for wv in ro["waves"])
+                copy_b[f] += eb[f] * sum(len(wv["stream"]) for wv in ro["waves"])
+        rep = ft.ft_moe_rebalance(g.pool, apply=True)
+        for f in (MX, F8):
+            assert host_b[f] > 0 and copy_b[f] > 0
+            assert rep["host_bytes"][f] == host_b[f] and rep["copy_bytes"][f] == copy_b[f]
+            assert rep["host_seconds"][f] > 0 and rep["copy_seconds"][f] > 0
+            assert rep["gpu_bytes_per_s"][f] == rep0["gpu_bytes_per_s"][f] > 0
+            ts = rep["copy_seconds"][f] / copy_b[f] + 1.0 / rep["gpu_bytes_per_s"][f]
+            tc = rep["host_seconds"][f] / host_b[f]
+            assert rep["changed"][f] == 1 and 0.0 < rep["share"][f] < 1.0
+            assert math.isclose(rep["share"][f], ts / (ts + tc), rel_tol=1e-12)
+            assert ft.ft_moe_get_hybrid_share(g.pool, f) == rep["share"][f]
+        assert rep["changed"][NV] == 0 and rep["host_bytes"][NV] == 0
+        again = ft.ft_moe_rebalance(g.pool, apply=True)
+        assert again["changed"] == [0, 0, 0, 0] and sum(again["host_bytes"]) == 0
+        o.share = {f: rep["share"][f] for f in (MX, F8)}
+        for step in range(3, 5):
+            for l in range(w.num_layers):
+                x = ms.activations(w, l, step, 6)
+                compare_call(g.forward(l, x, None), o.forward(l, x, None), w.top_k)
+        compare_table(g, o)
+    finally:
+        g.close()

@@ -92,3 +92,37 @@ def test_host_worker_pool_under_thread_sanitizer(host_check_tsan, tmp_path, case
     r = subprocess.run([host_check_tsan, str(fmt), str(H), str(I), str(rows), "4", str(tmp_path)],
                        capture_output=True, text=True, env=env, timeout=600)
     assert r.returncode == 0 and "ThreadSanitizer" not in r.stderr, r.stderr[-4000:]
+
+
+@pytest.mark.parametrize("portable", [False, True])
+@pytest.mark.parametrize("fmt", [ms.FMT_FP8_B128, ms.FMT_MXFP4, ms.FMT_NVFP4], ids=lambda f: ms.FMT_NAMES[f])
+def test_host_lane_decode_is_exact(host_check, tmp_path, fmt, portable):
+    """Every weight the host FFN decodes, lane by lane from the device layout,
+    equals the oracle's exact value rounded once to fp32 (NVFP4: the E4M3 block
+    scale times the per-matrix scale is rounded first, so two roundings).  The
+    FP8 blob gets NaN codes planted in two lanes (S.1111.111, both signs):
+    they must decode as NaN, the rest of their lanes as usual."""
+    H, I = 256, 384
+    blob = ms.gen_blob(93, ms.KIND_EXPERT, fmt, H, I, 11)
+    if fmt == ms.FMT_FP8_B128:
+        cod, _, _, _ = F.blob_offsets(fmt, H, I)
+        co, _ = cod[0]
+        blob[co + 3] = 0x7F
+        blob[co + 5 * H + 200] = 0xFF
+    blob.tofile(tmp_path / "blob.bin")
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:halt_on_error=1",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+    if portable:
+        env["FT_MOE_HOST_PORTABLE"] = "1"
+    r = subprocess.run([host_check, "decode", str(fmt), str(H), str(I), str(tmp_path)], capture_output=True,
+                       text=True, env=env, timeout=300)
+    assert r.returncode == 0, r.stderr[-4000:]
+    got = np.split(np.fromfile(tmp_path / "dec.bin", np.float32), [I * H, 2 * I * H])
+    for a, b in zip(got, F.dequant_expert(fmt, blob, H, I)):
+        b = b.reshape(-1)
+        if fmt == ms.FMT_NVFP4:
+            assert np.allclose(a, b, rtol=2.0 ** -22, atol=0.0)
+        else:
+            assert np.array_equal(a, b.astype(np.float32), equal_nan=True)
+    if fmt == ms.FMT_FP8_B128:
+        assert np.isnan(got[0][3]) and np.isnan(got[0][5 * H + 200]) and np.isnan(got[0]).sum() == 2

@@ -436,3 +436,29 @@ def test_resize_hand_worked():
     assert pool.key_of == [(0, 8), (0, 9), (0, 7)] and pool.last_use == [13, 14, 12]
     r = pool.resize(8)
     assert r == dict(evicted=[], moves=[]) and pool.key_of[3:] == [None] * 5
+
+
+def test_layer_stack_share_per_format():
+    """A share given per weight format applies to the layers of that format
+    only: with 0 for MXFP4 and 1 for FP8, MXFP4 layers stream every miss and
+    FP8 layers compute every miss on the host (and leave the pool alone)."""
+    import moe_synth as ms
+    from oracle.layer import OracleLayerStack
+
+    MX, F8 = ms.FMT_MXFP4, ms.FMT_FP8_B128
+    w = ms.Workload(135, "small-135", 2, 256, 128, 8, 2, (MX, F8), 8, (4,), 4, "decode", None, None,
+                    False, False, None)
+    o = OracleLayerStack(w, share={MX: 0.0, F8: 1.0})
+    for step in range(2):
+        for l in range(2):
+            r = o.forward(l, ms.activations(w, l, step, 3), None, outputs=False)
+            stream = [m for wv in r["waves"] for m in wv["stream"]]
+            cpu = [e for wv in r["waves"] for e in wv["cpu"]]
+            if l == 0:
+                assert cpu == [] and (step > 0 or len(stream) > 0)
+            else:
+                assert stream == [] and len(cpu) == len(set(r["sel"].reshape(-1).tolist()))
+    key, _, _ = o.pool.snapshot()
+    assert all(k is None or k[0] == 0 for k in key)
+    assert o.share_of(0) == 0.0 and o.share_of(1) == 1.0
+    assert OracleLayerStack(w, share=0.25).share_of(1) == 0.25
