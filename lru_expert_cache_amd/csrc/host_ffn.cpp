@@ -13,9 +13,9 @@
 // values, the block scale as a power of two or an E4M3 value) and adding its
 // products to the rows' sums.  The portable build's inner products have
 // eight independent partial sums, so that the compiler vectorises them without
-// reassociating a single sum; on CPUs with AVX2 and FMA (checked at run
-// time) an explicitly vectorised build decodes and multiplies 8 weights at a
-// time.
+// reassociating a single sum; on CPUs with AVX2 and FMA, or AVX-512 (checked
+// at run time), explicitly vectorised builds decode and multiply 8 or 16
+// weights at a time.
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -25,6 +25,7 @@
 #include <functional>
 #include <immintrin.h>
 #include <mutex>
+#include <string>
 #include <thread>
 #include <vector>
 
@@ -33,6 +34,8 @@
 namespace ftmoe {
 
 namespace {
+
+enum Isa { kPortable = 0, kAvx2 = 1, kAvx512 = 2 };
 
 struct Tables {
   float e2m1[16];
@@ -106,9 +109,10 @@ inline void decode_lane(const Tables& tb, const ExpertLayout& L, const uint8_t* 
 // AVX2: the 32 weights of lane `lane` of tile `tile` of matrix M as four
 // 8-float vectors, the same values as decode_lane.  E2M1: pshufb on the
 // nibbles with a table of 2 x the element values, widened and scaled by half
-// the block scale.  E4M3: the code's bits moved into an fp32 and rescaled by a
-// power of two; the value table only where a lane holds a NaN code.
-__attribute__((target("avx2,fma"))) inline void decode_lane_avx2(const MatLayout& M, int fmt, const uint8_t* blob,
+// the block scale.  E4M3: the code's bits moved into an fp16, widened to
+// fp32 and rescaled by a power of two; the value table only where a lane
+// holds a NaN code.
+__attribute__((target("avx2,fma,f16c"))) inline void decode_lane_avx2(const MatLayout& M, int fmt, const uint8_t* blob,
                                                                   int64_t tile, int lane, float g, __m256 w[4]) {
   const Tables& tb = tables();
   if (fmt == FT_FMT_FP8_B128) {
@@ -126,15 +130,16 @@ __attribute__((target("avx2,fma"))) inline void decode_lane_avx2(const MatLayout
       }
       return;
     }
-    // S.EEEE.MMM placed as the fp32 bits S.0000EEEE.MMM0..0 reads as 2^-120
-    // times the E4M3 value, subnormals included (an fp32 subnormal then):
-    // times 2^120 is exact, times the block scale rounds once.
-    const __m256i keep = _mm256_set1_epi32(int32_t(0x87F00000u));
-    const __m256 two120 = _mm256_set1_ps(0x1p120f);
+    // S.EEEE.MMM placed as the fp16 bits S.0EEEE.MMM0000000 is 2^-8 times the
+    // E4M3 value, subnormals included (fp16 subnormals then, which widen to
+    // normal fp32 exactly); times 2^8 is exact, times the block scale rounds
+    // once.  No fp32 subnormal is formed (slow on some CPUs).
+    const __m128i keep = _mm_set1_epi16(int16_t(0xBF80u));
+    const __m256 two8 = _mm256_set1_ps(256.0f);
     for (int v = 0; v < 4; ++v) {
-      const __m256i s32 = _mm256_cvtepi8_epi32(_mm_loadl_epi64(reinterpret_cast<const __m128i*>(c + 8 * v)));
-      const __m256 f = _mm256_castsi256_ps(_mm256_and_si256(_mm256_slli_epi32(s32, 20), keep));
-      w[v] = _mm256_mul_ps(_mm256_mul_ps(f, two120), vs);
+      const __m128i h = _mm_and_si128(
+          _mm_slli_epi16(_mm_cvtepi8_epi16(_mm_loadl_epi64(reinterpret_cast<const __m128i*>(c + 8 * v))), 7), keep);
+      w[v] = _mm256_mul_ps(_mm256_mul_ps(_mm256_cvtph_ps(h), two8), vs);
     }
     return;
   }
@@ -161,17 +166,77 @@ __attribute__((target("avx2,fma"))) inline void decode_lane_avx2(const MatLayout
   w[3] = _mm256_mul_ps(_mm256_cvtepi32_ps(_mm256_cvtepi8_epi32(_mm_srli_si128(e1, 8))), h1);
 }
 
-__attribute__((target("avx2,fma"))) void decode_lane_avx2_store(const MatLayout& M, int fmt, const uint8_t* blob,
+__attribute__((target("avx2,fma,f16c"))) void decode_lane_avx2_store(const MatLayout& M, int fmt, const uint8_t* blob,
                                                                  int64_t tile, int lane, float g, float* out) {
   __m256 w[4];
   decode_lane_avx2(M, fmt, blob, tile, lane, g, w);
   for (int v = 0; v < 4; ++v) _mm256_storeu_ps(out + 8 * v, w[v]);
 }
 
+// AVX-512: the same 32 weights as two 16-float vectors, by the same steps
+// (16 codes widened per step).
+__attribute__((target("avx512f,avx512bw,avx2,fma,f16c"))) inline void decode_lane_avx512(const MatLayout& M, int fmt,
+                                                                                     const uint8_t* blob,
+                                                                                     int64_t tile, int lane,
+                                                                                     float g, __m512 w[2]) {
+  const Tables& tb = tables();
+  if (fmt == FT_FMT_FP8_B128) {
+    const uint8_t* c = blob + M.codes_off + (tile * 64 + lane) * 32;
+    float sc;
+    std::memcpy(&sc, blob + M.scales_off + (tile * 16 + (lane & 15)) * 4, 4);
+    const __m512 vs = _mm512_set1_ps(sc);
+    const __m256i abs7 = _mm256_set1_epi8(0x7F);
+    const __m256i cb = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(c));
+    if (!_mm256_testz_si256(_mm256_cmpeq_epi8(_mm256_and_si256(cb, abs7), abs7), abs7)) {
+      for (int v = 0; v < 2; ++v) {
+        const __m512i idx = _mm512_cvtepu8_epi32(_mm_loadu_si128(reinterpret_cast<const __m128i*>(c + 16 * v)));
+        w[v] = _mm512_mul_ps(_mm512_i32gather_ps(idx, tb.e4m3, 4), vs);
+      }
+      return;
+    }
+    const __m256i keep = _mm256_set1_epi16(int16_t(0xBF80u));
+    const __m512 two8 = _mm512_set1_ps(256.0f);
+    for (int v = 0; v < 2; ++v) {
+      const __m256i h = _mm256_and_si256(
+          _mm256_slli_epi16(_mm256_cvtepi8_epi16(_mm_loadu_si128(reinterpret_cast<const __m128i*>(c + 16 * v))), 7),
+          keep);
+      w[v] = _mm512_mul_ps(_mm512_mul_ps(_mm512_cvtph_ps(h), two8), vs);
+    }
+    return;
+  }
+  const uint8_t* c = blob + M.codes_off + (tile * 64 + lane) * 16;
+  float s0, s1;
+  if (fmt == FT_FMT_MXFP4) {
+    s0 = s1 = e8m0_value(blob[M.scales_off + tile * 64 + lane]);
+  } else {
+    const uint8_t* sp = blob + M.scales_off + (tile * 64 + lane) * 2;
+    s0 = tb.e4m3[sp[0]] * g;
+    s1 = tb.e4m3[sp[1]] * g;
+  }
+  const __m128i lut2 = _mm_setr_epi8(0, 1, 2, 3, 4, 6, 8, 12, 0, -1, -2, -3, -4, -6, -8, -12);
+  const __m128i lo4 = _mm_set1_epi8(0x0F);
+  const __m128i b = _mm_loadu_si128(reinterpret_cast<const __m128i*>(c));
+  const __m128i lo = _mm_and_si128(b, lo4), hi = _mm_and_si128(_mm_srli_epi16(b, 4), lo4);
+  const __m128i e0 = _mm_shuffle_epi8(lut2, _mm_unpacklo_epi8(lo, hi));
+  const __m128i e1 = _mm_shuffle_epi8(lut2, _mm_unpackhi_epi8(lo, hi));
+  w[0] = _mm512_mul_ps(_mm512_cvtepi32_ps(_mm512_cvtepi8_epi32(e0)), _mm512_set1_ps(0.5f * s0));
+  w[1] = _mm512_mul_ps(_mm512_cvtepi32_ps(_mm512_cvtepi8_epi32(e1)), _mm512_set1_ps(0.5f * s1));
+}
+
+__attribute__((target("avx512f,avx512bw,avx2,fma,f16c"))) void decode_lane_avx512_store(const MatLayout& M, int fmt,
+                                                                                    const uint8_t* blob,
+                                                                                    int64_t tile, int lane, float g,
+                                                                                    float* out) {
+  __m512 w[2];
+  decode_lane_avx512(M, fmt, blob, tile, lane, g, w);
+  _mm512_storeu_ps(out, w[0]);
+  _mm512_storeu_ps(out + 16, w[1]);
+}
+
 // Sums over K of the tiles of row blocks [rb_begin, rb_end) of matrices
 // m0 .. m0 + nm - 1 against `rows` input rows xf [rows][K]; acc receives
 // [matrix][row][16] per row block and `finish(rb, acc)` consumes it.
-template <bool AVX2>
+template <int ISA>
 struct RowBlocks;
 
 #define FT_HOST_BODY                                                                                   \
@@ -201,7 +266,7 @@ struct RowBlocks;
   }
 
 template <>
-struct RowBlocks<false> {
+struct RowBlocks<kPortable> {
   static void run(const ExpertLayout& L, const uint8_t* blob, int m0, int nm, const float* gsc, const float* xf,
                   int rows, int rb_begin, int rb_end, const std::function<void(int, const float*)>& finish) {
     FT_HOST_BODY
@@ -211,22 +276,21 @@ struct RowBlocks<false> {
 // (decode_lane_avx2), and each (lane, input row) keeps an 8-wide partial sum
 // across the K tiles of the row block, added up once at its end.
 template <>
-struct RowBlocks<true> {
-  __attribute__((target("avx2,fma"))) static void run(const ExpertLayout& L, const uint8_t* blob, int m0, int nm,
+struct RowBlocks<kAvx2> {
+  __attribute__((target("avx2,fma,f16c"))) static void run(const ExpertLayout& L, const uint8_t* blob, int m0, int nm,
                                                        const float* gsc, const float* xf, int rows, int rb_begin,
                                                        int rb_end,
                                                        const std::function<void(int, const float*)>& finish) {
     const int K = L.m[m0].cols, nkb = K / kTileK;
     const int fmt = L.fmt;
-    thread_local std::vector<float> acc;
-    thread_local std::vector<__m256> part;
+    thread_local std::vector<float> acc, part;  // part: [lane][row][8] (plain floats: unaligned vector access)
     acc.resize(size_t(nm) * rows * 16);
-    part.resize(size_t(64) * rows);
+    part.resize(size_t(64) * rows * 8);
     for (int rb = rb_begin; rb < rb_end; ++rb) {
       std::fill(acc.begin(), acc.end(), 0.0f);
       for (int mi = 0; mi < nm; ++mi) {
         const MatLayout& M = L.m[m0 + mi];
-        for (auto& v : part) v = _mm256_setzero_ps();
+        std::fill(part.begin(), part.end(), 0.0f);
         for (int kb = 0; kb < nkb; ++kb) {
           const int64_t tile = int64_t(rb) * nkb + kb;
           for (int lane = 0; lane < 64; ++lane) {
@@ -235,19 +299,19 @@ struct RowBlocks<true> {
             const int k0 = kb * kTileK + 32 * (lane >> 4);
             for (int t = 0; t < rows; ++t) {
               const float* xr = xf + size_t(t) * K + k0;
-              __m256 a = part[size_t(lane) * rows + t];
+              float* pp = &part[(size_t(lane) * rows + t) * 8];
+              __m256 a = _mm256_loadu_ps(pp);
               a = _mm256_fmadd_ps(w[0], _mm256_loadu_ps(xr), a);
               a = _mm256_fmadd_ps(w[1], _mm256_loadu_ps(xr + 8), a);
               a = _mm256_fmadd_ps(w[2], _mm256_loadu_ps(xr + 16), a);
               a = _mm256_fmadd_ps(w[3], _mm256_loadu_ps(xr + 24), a);
-              part[size_t(lane) * rows + t] = a;
+              _mm256_storeu_ps(pp, a);
             }
           }
         }
         for (int lane = 0; lane < 64; ++lane)
           for (int t = 0; t < rows; ++t) {
-            alignas(32) float v[8];
-            _mm256_store_ps(v, part[size_t(lane) * rows + t]);
+            const float* v = &part[(size_t(lane) * rows + t) * 8];
             acc[(size_t(mi) * rows + t) * 16 + (lane & 15)] += ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
           }
       }
@@ -255,14 +319,83 @@ struct RowBlocks<true> {
     }
   }
 };
+// AVX-512: a lane's 32 weights as two 16-float vectors.  Lanes are taken
+// K-quarter by K-quarter (lane = 16 q + row), so the 32 inputs of each row
+// that a quarter multiplies are loaded once per tile for its 16 lanes.
+template <>
+struct RowBlocks<kAvx512> {
+  __attribute__((target("avx512f,avx512bw,avx2,fma,f16c"))) static void run(
+      const ExpertLayout& L, const uint8_t* blob, int m0, int nm, const float* gsc, const float* xf, int rows,
+      int rb_begin, int rb_end, const std::function<void(int, const float*)>& finish) {
+    const int K = L.m[m0].cols, nkb = K / kTileK;
+    const int fmt = L.fmt;
+    thread_local std::vector<float> acc, part;  // part: [lane][row][16]
+    acc.resize(size_t(nm) * rows * 16);
+    part.resize(size_t(64) * rows * 16);
+    constexpr int kRegRows = 8;  // input rows whose quarter stays in registers
+    __m512 xv[2 * kRegRows];
+    for (int rb = rb_begin; rb < rb_end; ++rb) {
+      std::fill(acc.begin(), acc.end(), 0.0f);
+      for (int mi = 0; mi < nm; ++mi) {
+        const MatLayout& M = L.m[m0 + mi];
+        std::fill(part.begin(), part.end(), 0.0f);
+        for (int kb = 0; kb < nkb; ++kb) {
+          const int64_t tile = int64_t(rb) * nkb + kb;
+          for (int q = 0; q < 4; ++q) {
+            const int k0 = kb * kTileK + 32 * q;
+            const int nreg = std::min(rows, kRegRows);
+            for (int t = 0; t < nreg; ++t) {
+              xv[2 * t] = _mm512_loadu_ps(xf + size_t(t) * K + k0);
+              xv[2 * t + 1] = _mm512_loadu_ps(xf + size_t(t) * K + k0 + 16);
+            }
+            for (int r = 0; r < 16; ++r) {
+              const int lane = 16 * q + r;
+              __m512 w[2];
+              decode_lane_avx512(M, fmt, blob, tile, lane, gsc[mi], w);
+              float* pa = &part[size_t(lane) * rows * 16];
+              for (int t = 0; t < nreg; ++t)
+                _mm512_storeu_ps(pa + 16 * t, _mm512_fmadd_ps(w[1], xv[2 * t + 1],
+                                                              _mm512_fmadd_ps(w[0], xv[2 * t],
+                                                                              _mm512_loadu_ps(pa + 16 * t))));
+              for (int t = nreg; t < rows; ++t) {
+                const float* xr = xf + size_t(t) * K + k0;
+                _mm512_storeu_ps(pa + 16 * t, _mm512_fmadd_ps(w[1], _mm512_loadu_ps(xr + 16),
+                                                              _mm512_fmadd_ps(w[0], _mm512_loadu_ps(xr),
+                                                                              _mm512_loadu_ps(pa + 16 * t))));
+              }
+            }
+          }
+        }
+        for (int lane = 0; lane < 64; ++lane)
+          for (int t = 0; t < rows; ++t)
+            acc[(size_t(mi) * rows + t) * 16 + (lane & 15)] +=
+                _mm512_reduce_add_ps(_mm512_loadu_ps(&part[(size_t(lane) * rows + t) * 16]));
+      }
+      finish(rb, acc.data());
+    }
+  }
+};
 #undef FT_HOST_BODY
 
-// The AVX2 build where the CPU has AVX2 and FMA, unless the environment
-// variable FT_MOE_HOST_PORTABLE is set (the portable build, for tests).
-bool cpu_has_avx2_fma() {
-  static const bool ok = __builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma") &&
-                         std::getenv("FT_MOE_HOST_PORTABLE") == nullptr;
-  return ok;
+// The widest build the CPU runs (AVX-512 F+BW, else AVX2 with FMA, else
+// portable), capped by the environment for tests: FT_MOE_HOST_ISA =
+// "portable" | "avx2" | "avx512" (or FT_MOE_HOST_PORTABLE set: portable).
+int host_isa() {
+  static const int isa = [] {
+    int best = kPortable;
+    if (__builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma") && __builtin_cpu_supports("f16c")) {
+      best = kAvx2;
+      if (__builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw")) best = kAvx512;
+    }
+    if (std::getenv("FT_MOE_HOST_PORTABLE") != nullptr) return int(kPortable);
+    if (const char* e = std::getenv("FT_MOE_HOST_ISA")) {
+      const std::string v(e);
+      const int cap = v == "portable" ? kPortable : v == "avx2" ? kAvx2 : kAvx512;
+      best = std::min(best, cap);
+    }
+    return best;
+  }();
+  return isa;
 }
 
 }  // namespace
@@ -350,10 +483,16 @@ constexpr int kBlocksPerItem = 4;
 
 void run_blocks(const ExpertLayout& L, const uint8_t* blob, int m0, int nm, const float* gsc, const float* xf,
                 int rows, int rb_begin, int rb_end, const std::function<void(int, const float*)>& finish) {
-  if (cpu_has_avx2_fma())
-    RowBlocks<true>::run(L, blob, m0, nm, gsc, xf, rows, rb_begin, rb_end, finish);
-  else
-    RowBlocks<false>::run(L, blob, m0, nm, gsc, xf, rows, rb_begin, rb_end, finish);
+  switch (host_isa()) {
+    case kAvx512:
+      RowBlocks<kAvx512>::run(L, blob, m0, nm, gsc, xf, rows, rb_begin, rb_end, finish);
+      break;
+    case kAvx2:
+      RowBlocks<kAvx2>::run(L, blob, m0, nm, gsc, xf, rows, rb_begin, rb_end, finish);
+      break;
+    default:
+      RowBlocks<kPortable>::run(L, blob, m0, nm, gsc, xf, rows, rb_begin, rb_end, finish);
+  }
 }
 
 }  // namespace
@@ -409,7 +548,11 @@ void host_experts(const ExpertLayout& L, const HostExpertJob* jobs, int n, Worke
 void host_decode_lane(const ExpertLayout& L, const uint8_t* blob, int m, int64_t tile, int lane, float* w) {
   float g = 1.0f;
   if (L.fmt == FT_FMT_NVFP4) std::memcpy(&g, blob + L.tscale_off + 4 * m, 4);
-  if (cpu_has_avx2_fma()) {
+  if (host_isa() == kAvx512) {
+    decode_lane_avx512_store(L.m[m], L.fmt, blob, tile, lane, g, w);
+    return;
+  }
+  if (host_isa() == kAvx2) {
     decode_lane_avx2_store(L.m[m], L.fmt, blob, tile, lane, g, w);
     return;
   }

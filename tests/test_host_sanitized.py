@@ -48,9 +48,12 @@ CASES = [(ms.FMT_MXFP4, 256, 128, 1), (ms.FMT_MXFP4, 384, 256, 5), (ms.FMT_NVFP4
          (ms.FMT_FP8_B128, 384, 256, 4), (ms.FMT_FP8_B128, 256, 128, 1)]
 
 
-@pytest.mark.parametrize("portable", [False, True])
+ISAS = ["native", "avx2", "portable"]  # the widest build the CPU runs, then capped ones
+
+
+@pytest.mark.parametrize("isa", ISAS)
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"{ms.FMT_NAMES[c[0]]}-H{c[1]}-I{c[2]}-rows{c[3]}")
-def test_repack_and_host_expert_under_sanitizers(host_check, tmp_path, case, portable):
+def test_repack_and_host_expert_under_sanitizers(host_check, tmp_path, case, isa):
     fmt, H, I, rows = case
     blob = ms.gen_blob(91, ms.KIND_EXPERT, fmt, H, I, H + I + rows)
     x_bits = ms.f32_to_bf16_bits(np.random.default_rng(H + rows).standard_normal((rows, H)).astype(np.float32))
@@ -60,8 +63,8 @@ def test_repack_and_host_expert_under_sanitizers(host_check, tmp_path, case, por
     w.tofile(tmp_path / "w.bin")
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0:halt_on_error=1",
                UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
-    if portable:
-        env["FT_MOE_HOST_PORTABLE"] = "1"
+    if isa != "native":
+        env["FT_MOE_HOST_ISA"] = isa
     r = subprocess.run([host_check, str(fmt), str(H), str(I), str(rows), "3", str(tmp_path)], capture_output=True,
                        text=True, env=env, timeout=300)
     assert r.returncode == 0, r.stderr[-4000:]
@@ -94,9 +97,9 @@ def test_host_worker_pool_under_thread_sanitizer(host_check_tsan, tmp_path, case
     assert r.returncode == 0 and "ThreadSanitizer" not in r.stderr, r.stderr[-4000:]
 
 
-@pytest.mark.parametrize("portable", [False, True])
+@pytest.mark.parametrize("isa", ISAS)
 @pytest.mark.parametrize("fmt", [ms.FMT_FP8_B128, ms.FMT_MXFP4, ms.FMT_NVFP4], ids=lambda f: ms.FMT_NAMES[f])
-def test_host_lane_decode_is_exact(host_check, tmp_path, fmt, portable):
+def test_host_lane_decode_is_exact(host_check, tmp_path, fmt, isa):
     """Every weight the host FFN decodes, lane by lane from the device layout,
     equals the oracle's exact value rounded once to fp32 (NVFP4: the E4M3 block
     scale times the per-matrix scale is rounded first, so two roundings).  The
@@ -112,8 +115,8 @@ def test_host_lane_decode_is_exact(host_check, tmp_path, fmt, portable):
     blob.tofile(tmp_path / "blob.bin")
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:halt_on_error=1",
                UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
-    if portable:
-        env["FT_MOE_HOST_PORTABLE"] = "1"
+    if isa != "native":
+        env["FT_MOE_HOST_ISA"] = isa
     r = subprocess.run([host_check, "decode", str(fmt), str(H), str(I), str(tmp_path)], capture_output=True,
                        text=True, env=env, timeout=300)
     assert r.returncode == 0, r.stderr[-4000:]
