@@ -173,8 +173,11 @@ __attribute__((target("avx2,fma,f16c"))) void decode_lane_avx2_store(const MatLa
   for (int v = 0; v < 4; ++v) _mm256_storeu_ps(out + 8 * v, w[v]);
 }
 
-// AVX-512: the same 32 weights as two 16-float vectors, by the same steps
-// (16 codes widened per step).
+// AVX-512: the same 32 weights as two 16-float vectors.  E4M3 by the same
+// steps as AVX2 (16 codes widened per step).  E2M1: each byte's two nibbles
+// index a 16-entry table of the element values times the block scale (one
+// permute per 16 weights), so w[0] holds the even elements 0, 2, .., 30 and
+// w[1] the odd ones; the caller pairs them with inputs split the same way.
 __attribute__((target("avx512f,avx512bw,avx2,fma,f16c"))) inline void decode_lane_avx512(const MatLayout& M, int fmt,
                                                                                      const uint8_t* blob,
                                                                                      int64_t tile, int lane,
@@ -205,22 +208,22 @@ __attribute__((target("avx512f,avx512bw,avx2,fma,f16c"))) inline void decode_lan
     return;
   }
   const uint8_t* c = blob + M.codes_off + (tile * 64 + lane) * 16;
-  float s0, s1;
+  const __m512 lut = _mm512_setr_ps(0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f, -0.0f, -0.5f, -1.0f, -1.5f,
+                                    -2.0f, -3.0f, -4.0f, -6.0f);
+  const __m512i v = _mm512_cvtepu8_epi32(_mm_loadu_si128(reinterpret_cast<const __m128i*>(c)));
+  const __m512i lo = _mm512_and_si512(v, _mm512_set1_epi32(15)), hi = _mm512_srli_epi32(v, 4);
   if (fmt == FT_FMT_MXFP4) {
-    s0 = s1 = e8m0_value(blob[M.scales_off + tile * 64 + lane]);
-  } else {
-    const uint8_t* sp = blob + M.scales_off + (tile * 64 + lane) * 2;
-    s0 = tb.e4m3[sp[0]] * g;
-    s1 = tb.e4m3[sp[1]] * g;
+    const __m512 ls = _mm512_mul_ps(lut, _mm512_set1_ps(e8m0_value(blob[M.scales_off + tile * 64 + lane])));
+    w[0] = _mm512_permutexvar_ps(lo, ls);
+    w[1] = _mm512_permutexvar_ps(hi, ls);
+    return;
   }
-  const __m128i lut2 = _mm_setr_epi8(0, 1, 2, 3, 4, 6, 8, 12, 0, -1, -2, -3, -4, -6, -8, -12);
-  const __m128i lo4 = _mm_set1_epi8(0x0F);
-  const __m128i b = _mm_loadu_si128(reinterpret_cast<const __m128i*>(c));
-  const __m128i lo = _mm_and_si128(b, lo4), hi = _mm_and_si128(_mm_srli_epi16(b, 4), lo4);
-  const __m128i e0 = _mm_shuffle_epi8(lut2, _mm_unpacklo_epi8(lo, hi));
-  const __m128i e1 = _mm_shuffle_epi8(lut2, _mm_unpackhi_epi8(lo, hi));
-  w[0] = _mm512_mul_ps(_mm512_cvtepi32_ps(_mm512_cvtepi8_epi32(e0)), _mm512_set1_ps(0.5f * s0));
-  w[1] = _mm512_mul_ps(_mm512_cvtepi32_ps(_mm512_cvtepi8_epi32(e1)), _mm512_set1_ps(0.5f * s1));
+  // NVFP4: bytes 0..7 (elements 0..15) take the first scale, bytes 8..15 the second
+  const uint8_t* sp = blob + M.scales_off + (tile * 64 + lane) * 2;
+  const __m512 sv = _mm512_mask_blend_ps(__mmask16(0xFF00), _mm512_set1_ps(tb.e4m3[sp[0]] * g),
+                                         _mm512_set1_ps(tb.e4m3[sp[1]] * g));
+  w[0] = _mm512_mul_ps(_mm512_permutexvar_ps(lo, lut), sv);
+  w[1] = _mm512_mul_ps(_mm512_permutexvar_ps(hi, lut), sv);
 }
 
 __attribute__((target("avx512f,avx512bw,avx2,fma,f16c"))) void decode_lane_avx512_store(const MatLayout& M, int fmt,
@@ -229,8 +232,18 @@ __attribute__((target("avx512f,avx512bw,avx2,fma,f16c"))) void decode_lane_avx51
                                                                                     float* out) {
   __m512 w[2];
   decode_lane_avx512(M, fmt, blob, tile, lane, g, w);
-  _mm512_storeu_ps(out, w[0]);
-  _mm512_storeu_ps(out + 16, w[1]);
+  if (fmt == FT_FMT_FP8_B128) {
+    _mm512_storeu_ps(out, w[0]);
+    _mm512_storeu_ps(out + 16, w[1]);
+    return;
+  }
+  alignas(64) float ev[16], od[16];
+  _mm512_store_ps(ev, w[0]);
+  _mm512_store_ps(od, w[1]);
+  for (int i = 0; i < 16; ++i) {
+    out[2 * i] = ev[i];
+    out[2 * i + 1] = od[i];
+  }
 }
 
 // Sums over K of the tiles of row blocks [rb_begin, rb_end) of matrices
@@ -319,9 +332,24 @@ struct RowBlocks<kAvx2> {
     }
   }
 };
+// 32 inputs as two 16-float vectors: in order, or (split) the even positions
+// then the odd ones.
+__attribute__((target("avx512f,avx512bw,avx2,fma,f16c"))) inline void load_x512(const float* p, bool split,
+                                                                                 __m512* o) {
+  const __m512 a = _mm512_loadu_ps(p), b = _mm512_loadu_ps(p + 16);
+  if (!split) {
+    o[0] = a;
+    o[1] = b;
+    return;
+  }
+  o[0] = _mm512_permutex2var_ps(a, _mm512_setr_epi32(0, 2, 4, 6, 8, 10, 12, 14, 16, 18, 20, 22, 24, 26, 28, 30), b);
+  o[1] = _mm512_permutex2var_ps(a, _mm512_setr_epi32(1, 3, 5, 7, 9, 11, 13, 15, 17, 19, 21, 23, 25, 27, 29, 31), b);
+}
+
 // AVX-512: a lane's 32 weights as two 16-float vectors.  Lanes are taken
 // K-quarter by K-quarter (lane = 16 q + row), so the 32 inputs of each row
-// that a quarter multiplies are loaded once per tile for its 16 lanes.
+// that a quarter multiplies are loaded once per tile for its 16 lanes (split
+// into even and odd positions for the E2M1 formats, as their weights come).
 template <>
 struct RowBlocks<kAvx512> {
   __attribute__((target("avx512f,avx512bw,avx2,fma,f16c"))) static void run(
@@ -334,6 +362,7 @@ struct RowBlocks<kAvx512> {
     part.resize(size_t(64) * rows * 16);
     constexpr int kRegRows = 8;  // input rows whose quarter stays in registers
     __m512 xv[2 * kRegRows];
+    const bool fp4 = fmt != FT_FMT_FP8_B128;
     for (int rb = rb_begin; rb < rb_end; ++rb) {
       std::fill(acc.begin(), acc.end(), 0.0f);
       for (int mi = 0; mi < nm; ++mi) {
@@ -344,10 +373,7 @@ struct RowBlocks<kAvx512> {
           for (int q = 0; q < 4; ++q) {
             const int k0 = kb * kTileK + 32 * q;
             const int nreg = std::min(rows, kRegRows);
-            for (int t = 0; t < nreg; ++t) {
-              xv[2 * t] = _mm512_loadu_ps(xf + size_t(t) * K + k0);
-              xv[2 * t + 1] = _mm512_loadu_ps(xf + size_t(t) * K + k0 + 16);
-            }
+            for (int t = 0; t < nreg; ++t) load_x512(xf + size_t(t) * K + k0, fp4, &xv[2 * t]);
             for (int r = 0; r < 16; ++r) {
               const int lane = 16 * q + r;
               __m512 w[2];
@@ -358,9 +384,10 @@ struct RowBlocks<kAvx512> {
                                                               _mm512_fmadd_ps(w[0], xv[2 * t],
                                                                               _mm512_loadu_ps(pa + 16 * t))));
               for (int t = nreg; t < rows; ++t) {
-                const float* xr = xf + size_t(t) * K + k0;
-                _mm512_storeu_ps(pa + 16 * t, _mm512_fmadd_ps(w[1], _mm512_loadu_ps(xr + 16),
-                                                              _mm512_fmadd_ps(w[0], _mm512_loadu_ps(xr),
+                __m512 xr[2];
+                load_x512(xf + size_t(t) * K + k0, fp4, xr);
+                _mm512_storeu_ps(pa + 16 * t, _mm512_fmadd_ps(w[1], xr[1],
+                                                              _mm512_fmadd_ps(w[0], xr[0],
                                                                               _mm512_loadu_ps(pa + 16 * t))));
               }
             }
