@@ -97,15 +97,20 @@ def measure_hbm_copy(torch, dev, nbytes=2 << 30, reps=5):
     return 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
-def measured_traffic(profile_name):
+def measured_traffic(profile_name, algorithmic_bytes):
     """HBM bytes per launch of a kernel from a committed rocprofv3 counter
-    summary, or None when the kernel's source has changed since it was taken."""
+    summary, or None when the kernel's source has changed since it was taken
+    or when this run's launches are not the workload the counters saw (their
+    algorithmic bytes per launch differ by more than 2%)."""
     path = os.path.join(ROOT, "profiles", profile_name)
     src = os.path.join(ROOT, "lru_expert_cache_amd", "csrc", "ffn.hip")
     try:
         kv = dict(l.strip().split("=", 1) for l in open(path) if "=" in l and not l.startswith(" "))
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
         if kv.get("ffn_source_sha256") != sha:
+            return None
+        ref = float(kv["algorithmic_bytes_per_launch"])
+        if not abs(algorithmic_bytes - ref) <= 0.02 * ref:
             return None
         return float(kv["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -409,7 +414,8 @@ def qwen_extras(ft, torch, ms, dev, steps, warmup, cpu):
         res["decode_b16"]["roofline_gateup"] = {
             "kernel": kernel, "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": gu["bytes"] / max(gu["launches"], 1),
-            "traffic": measured_traffic("ffn_gateup_qwen_a3b_decode_b16_hbm_traffic.md")}
+            "traffic": measured_traffic("ffn_gateup_qwen_a3b_decode_b16_hbm_traffic.md",
+                                        gu["bytes"] / max(gu["launches"], 1))}
         log(f"[bench] qwen-a3b decode b16: {res['decode_b16']['tokens_per_s']:.0f} tokens/s, gate/up {gbs:.0f} GB/s")
         for b in (1, 4):
             xb = torch.from_numpy(np.stack([[ms.activations(w, l, 1000 + s, b) for l in range(L)]
@@ -592,7 +598,8 @@ def main():
                    "host_threads": hybrid_threads() if w.hybrid else 0,
                    "host_blob_aliasing": w.n_blobs},
         "roofline": {"kernel": kernel, "bound": "hbm", "achieved": gu_gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": gu_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(traffic_profile),
+                     "unit": "GB/s", "frac": gu_gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(traffic_profile, gu["bytes"] / max(gu["launches"], 1)),
                      "algorithmic_bytes_per_launch": gu["bytes"] / max(gu["launches"], 1),
                      "avg_launch_us": gu["ms"] / max(gu["launches"], 1) * 1e3, "launches": gu["launches"],
                      "layers_timed": f"every {FMT_NAME[big]} layer"},
