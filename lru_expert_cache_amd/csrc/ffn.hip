@@ -277,7 +277,7 @@ __device__ inline void load_tile_sel(TileRegs<FMT>& r, const uint8_t* __restrict
 }
 
 template <int FMT, bool GATEUP, int D, int NC>
-__global__ __launch_bounds__(64 * kStreamWaves) void k_ffn_stream(FfnArgs a) {
+__global__ __launch_bounds__(64 * kStreamWaves, 2) void k_ffn_stream(FfnArgs a) {
   constexpr int NM = GATEUP ? 2 : 1;
   constexpr bool F8 = FMT == FT_FMT_FP8_B128;
   // per K step, the activation tile of each row chunk: 16 rows x 128 K bf16, swizzled
