@@ -92,70 +92,101 @@ __global__ __launch_bounds__(kSmallThreads) void k_router_logits_small(
   }
 }
 
-// Large batches (prefill): 32 tokens x 32 experts per workgroup, each thread
-// a 2x2 register tile, K staged through LDS in chunks of 64 as fp64.
-constexpr int kTT = 32, kTE = 32, kKC = 64;
+// Large batches (prefill), on the fp64 matrix cores: v_mfma_f64_16x16x4_f64
+// takes a 16 x 4 block of x (lane l: token l % 16, K index l / 16), a 4 x 16
+// block of Wr^T (lane l: K index l / 16, expert l % 16) and accumulates the
+// 16 x 16 logits in fp64 (lane l, element i: token 4 i + l / 16, expert l % 16).
+// Products of bf16 and fp32 values are exact in fp64 and every sum is fp64,
+// as in the scalar kernels; only the summation order differs.  The order of
+// K in a sum is free, so in each 64-wide K chunk the four lane groups take
+// sixteen consecutive K values each (group g: K 16g .. 16g + 15, one per MFMA
+// step): a lane's operands are then two 16-byte loads of its x row and four
+// of its router row per expert tile, straight from global memory (the router
+// rows are shared by the workgroup's waves through the L1), with the next
+// chunk's loads issued before this chunk's MFMAs.  A wave owns 16 tokens x 32
+// experts (two MFMA tiles), a workgroup 64 x 32.
+constexpr int kMfmaTokW = 16, kMfmaWaves = 4, kMfmaExp = 32, kMfmaKC = 64;
+// wave groups splitting K (two waves per SIMD: 4096 x 2048 x 128 took 69 us
+// with one group, 54 with two, 53.5 with four)
+constexpr int kMfmaKS = 2;
 
-__global__ __launch_bounds__(256) void k_router_logits_tiled(
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+// One K chunk of a lane's operands: 16 bf16 of its token, 16 fp32 of its
+// router row in each of the two expert tiles.
+struct RouterChunk {
+  uint4 xv[2];
+  float4 wv[2][4];
+};
+
+__device__ inline void router_chunk_load(RouterChunk& c, const uint16_t* xr, const float* w0, const float* w1,
+                                         int k0) {
+  c.xv[0] = *reinterpret_cast<const uint4*>(xr + k0);
+  c.xv[1] = *reinterpret_cast<const uint4*>(xr + k0 + 8);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    c.wv[0][j] = *reinterpret_cast<const float4*>(w0 + k0 + 4 * j);
+    c.wv[1][j] = *reinterpret_cast<const float4*>(w1 + k0 + 4 * j);
+  }
+}
+
+__device__ inline float f4_at(const float4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
+
+// KS wave groups of the workgroup split K: group q takes chunks q, q + KS,
+// ...; groups 1 .. KS-1 leave their sums in LDS and group 0 adds them in
+// group order (a fixed order, so the logits do not depend on timing).
+template <int KS>
+__global__ __launch_bounds__(64 * kMfmaWaves * KS) void k_router_logits_mfma(
     const uint16_t* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
     double* __restrict__ z, int T, int H, int E) {
-  __shared__ double xs[kTT][kKC + 1];
-  __shared__ double ws[kTE][kKC + 1];
-  const int tid = threadIdx.x;
-  const int tt0 = blockIdx.x * kTT, te0 = blockIdx.y * kTE;
-  const int ty = tid / 16, tx = tid % 16;  // 16 x 16 threads, 2x2 each
-  double acc[2][2] = {{0.0, 0.0}, {0.0, 0.0}};
-  for (int k0 = 0; k0 < H; k0 += kKC) {
-    // x tile: 32 x 64 bf16 = 2048 values, 8 per thread
-    {
-      const int r = tid / 8, c = (tid % 8) * 8;
-      const int t = tt0 + r;
-      if (t < T) {
-        const uint4 v = *reinterpret_cast<const uint4*>(x + int64_t(t) * H + k0 + c);
-        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+  __shared__ f64x4 part[KS > 1 ? KS - 1 : 1][kMfmaWaves][2][64];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wv = wid % kMfmaWaves, q = wid / kMfmaWaves;
+  const int g = lane >> 4, n = lane & 15;
+  const int t0 = blockIdx.x * (kMfmaTokW * kMfmaWaves) + wv * kMfmaTokW;
+  const int e0 = blockIdx.y * kMfmaExp;
+  // operand rows of this lane (clamped: rows past T or E are computed and not
+  // stored); lane group g takes K 16g .. 16g + 15 of every 64-wide chunk
+  const uint16_t* xr = x + int64_t(min(t0 + n, T - 1)) * H + 16 * g;
+  const float* w0 = wr + int64_t(min(e0 + n, E - 1)) * H + 16 * g;
+  const float* w1 = wr + int64_t(min(e0 + 16 + n, E - 1)) * H + 16 * g;
+  f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
+  RouterChunk cur, nxt;
+  const int kstep = kMfmaKC * KS;
+  if (q * kMfmaKC < H) router_chunk_load(cur, xr, w0, w1, q * kMfmaKC);
+  for (int k0 = q * kMfmaKC; k0 < H; k0 += kstep) {
+    if (k0 + kstep < H) router_chunk_load(nxt, xr, w0, w1, k0 + kstep);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          xs[r][c + 2 * i] = bf16_to_f64(uint16_t(u[i] & 0xFFFF));
-          xs[r][c + 2 * i + 1] = bf16_to_f64(uint16_t(u[i] >> 16));
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) xs[r][c + i] = 0.0;
-      }
+    for (int s = 0; s < 16; ++s) {
+      const uint32_t xu = s < 8 ? (s < 4 ? (s < 2 ? cur.xv[0].x : cur.xv[0].y) : (s < 6 ? cur.xv[0].z : cur.xv[0].w))
+                                : (s < 12 ? (s < 10 ? cur.xv[1].x : cur.xv[1].y) : (s < 14 ? cur.xv[1].z : cur.xv[1].w));
+      const double a = bf16_to_f64(uint16_t(s & 1 ? xu >> 16 : xu & 0xFFFF));
+      acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(a, double(f4_at(cur.wv[0][s >> 2], s & 3)), acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(a, double(f4_at(cur.wv[1][s >> 2], s & 3)), acc1, 0, 0, 0);
     }
-    // w tile: 32 x 64 fp32, 8 per thread
-    {
-      const int r = tid / 8, c = (tid % 8) * 8;
-      const int e = te0 + r;
-      if (e < E) {
-        const float4 a = *reinterpret_cast<const float4*>(wr + int64_t(e) * H + k0 + c);
-        const float4 b = *reinterpret_cast<const float4*>(wr + int64_t(e) * H + k0 + c + 4);
-        ws[r][c + 0] = a.x; ws[r][c + 1] = a.y; ws[r][c + 2] = a.z; ws[r][c + 3] = a.w;
-        ws[r][c + 4] = b.x; ws[r][c + 5] = b.y; ws[r][c + 6] = b.z; ws[r][c + 7] = b.w;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) ws[r][c + i] = 0.0;
-      }
+    cur = nxt;
+  }
+  if constexpr (KS > 1) {
+    if (q > 0) {
+      part[q - 1][wv][0][lane] = acc0;
+      part[q - 1][wv][1][lane] = acc1;
     }
     __syncthreads();
-#pragma unroll 8
-    for (int h = 0; h < kKC; ++h) {
-      const double a0 = xs[2 * ty][h], a1 = xs[2 * ty + 1][h];
-      const double b0 = ws[2 * tx][h], b1 = ws[2 * tx + 1][h];
-      acc[0][0] = fma(a0, b0, acc[0][0]);
-      acc[0][1] = fma(a0, b1, acc[0][1]);
-      acc[1][0] = fma(a1, b0, acc[1][0]);
-      acc[1][1] = fma(a1, b1, acc[1][1]);
+    if (q > 0) return;
+#pragma unroll
+    for (int j = 0; j < KS - 1; ++j) {
+      acc0 += part[j][wv][0][lane];
+      acc1 += part[j][wv][1][lane];
     }
-    __syncthreads();
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int t = tt0 + 2 * ty + i, e = te0 + 2 * tx + j;
-      if (t < T && e < E) z[int64_t(t) * E + e] = acc[i][j] + (bias ? double(bias[e]) : 0.0);
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + 4 * i + g;
+    if (t >= T) continue;
+    const int ea = e0 + n, eb = e0 + 16 + n;
+    if (ea < E) z[int64_t(t) * E + ea] = acc0[i] + (bias ? double(bias[ea]) : 0.0);
+    if (eb < E) z[int64_t(t) * E + eb] = acc1[i] + (bias ? double(bias[eb]) : 0.0);
+  }
 }
 
 }  // namespace
@@ -183,8 +214,8 @@ hipError_t launch_router_logits(const uint16_t* x, const float* wr, const float*
     else
       ft_launch(k_router_logits_small<16>, dim3(E), dim3(kSmallThreads), s, ev, x, wr, bias, z, T, H, E);
   } else {
-    ft_launch(k_router_logits_tiled, dim3((T + kTT - 1) / kTT, (E + kTE - 1) / kTE), dim3(256), s, ev, x, wr,
-              bias, z, T, H, E);
+    const dim3 grid((T + kMfmaTokW * kMfmaWaves - 1) / (kMfmaTokW * kMfmaWaves), (E + kMfmaExp - 1) / kMfmaExp);
+    ft_launch(k_router_logits_mfma<kMfmaKS>, grid, dim3(64 * kMfmaWaves * kMfmaKS), s, ev, x, wr, bias, z, T, H, E);
   }
   return hipGetLastError();
 }
