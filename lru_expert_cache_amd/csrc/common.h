@@ -115,19 +115,29 @@ struct ResolveArgs {
   int32_t fmt;             // weight format of the layer
   int32_t host_wait;       // 1: the host spins on the readback stamp (publish it system-wide)
   int32_t stage_hits;      // staged calls: 1 = experts resident in the pool run from their slots
+  // staged calls, spread over workgroups: per-chunk histograms and the
+  // per-expert results of the resolve, see launch_resolve (null = one workgroup)
+  int32_t* agg;
+  int32_t nchunks;         // chunks of kStageChunk pairs
 };
+constexpr int kStageChunk = 1024;  // pairs per workgroup of the staged histogram / rows kernels
+// ints of the staged-resolve scratch for `pairs` pairs of E experts
+inline int64_t stage_agg_ints(int64_t pairs, int E) {
+  return 4 * ((pairs + kStageChunk - 1) / kStageChunk) * int64_t(E) + 5 * int64_t(E);
+}
 
 // ------------------------------------------------------------ launchers
 // Every launcher takes an optional pair of events (ev0, ev1).  When given, the
 // kernel is launched with hipExtLaunchKernelGGL so that the events bracket the
-// kernel's own execution (not the gap while the host enqueues it).
+// kernel's own execution (not the gap while the host enqueues it); either may
+// be null (a stage of several kernels: the first records ev0, the last ev1).
 struct Ev {
   hipEvent_t a = nullptr, b = nullptr;
 };
 
 template <typename K, typename... Args>
 inline void ft_launch(K kernel, dim3 grid, dim3 block, hipStream_t s, Ev ev, Args... args) {
-  if (ev.a)
+  if (ev.a || ev.b)
     hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev.a, ev.b, 0, args...);
   else
     hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
@@ -135,7 +145,7 @@ inline void ft_launch(K kernel, dim3 grid, dim3 block, hipStream_t s, Ev ev, Arg
 // the same with dynamic LDS bytes
 template <typename K, typename... Args>
 inline void ft_launch_lds(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, Ev ev, Args... args) {
-  if (ev.a)
+  if (ev.a || ev.b)
     hipExtLaunchKernelGGL(kernel, grid, block, lds, s, ev.a, ev.b, 0, args...);
   else
     hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);

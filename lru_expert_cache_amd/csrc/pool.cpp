@@ -130,6 +130,7 @@ struct ft_moe_pool {
   uint8_t* hq_codes = nullptr;      // and h, written by the gate/up GEMM while x tiles are read
   uint8_t* hq_scales = nullptr;
   int32_t* tiles = nullptr;         // [2 * max_tiles]
+  int32_t* stage_agg = nullptr;     // staged resolve scratch (stage_agg_ints)
   int32_t max_tiles = 0;
 
   // Miss copies rotate over n_copy streams (several DMA queues overlap the
@@ -259,6 +260,7 @@ void free_work_buffers(ft_moe_pool* p) {
   dev_free(p->pair_slot); dev_free(p->pair_row); dev_free(p->row_tok); dev_free(p->row_w);
   dev_free(p->hbuf); dev_free(p->pbuf);
   dev_free(p->row_slot); dev_free(p->tiles); dev_free(p->xq_codes); dev_free(p->xq_scales);
+  dev_free(p->stage_agg);
   dev_free(p->tq_codes); dev_free(p->tq_scales); dev_free(p->hq_codes); dev_free(p->hq_scales);
   if (p->rb_host) (void)hipHostFree(p->rb_host);
   if (p->x_host) (void)hipHostFree(p->x_host);
@@ -291,7 +293,8 @@ int ensure_capacity(ft_moe_pool* p, int T) {
       (rc = work_alloc(p, &p->pbuf, rows * p->H)) || (rc = work_alloc(p, &p->row_slot, rows)) ||
       (rc = work_alloc(p, &p->xq_codes, int64_t(cap) * p->H)) ||
       (rc = work_alloc(p, &p->xq_scales, int64_t(cap) * p->H / 32)) ||
-      (rc = work_alloc(p, &p->tiles, 2 * int64_t(p->max_tiles)))) {
+      (rc = work_alloc(p, &p->tiles, 2 * int64_t(p->max_tiles))) ||
+      (rc = work_alloc(p, &p->stage_agg, stage_agg_ints(pairs, p->E)))) {
     free_work_buffers(p);
     return rc;
   }
@@ -443,6 +446,10 @@ ResolveArgs resolve_args(ft_moe_pool* p, int layer, int T, int t0, int mode) {
   a.tiles = mode == 1 ? p->tiles : nullptr;
   a.row_slot = mode == 1 ? p->row_slot : nullptr;
   a.tile_rows = mx_gemm_rows_per_tile();
+  if (mode == 1) {
+    a.agg = p->stage_agg;
+    a.nchunks = int32_t((int64_t(T) * p->k + kStageChunk - 1) / kStageChunk);
+  }
   return a;
 }
 

@@ -331,33 +331,101 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
   }
   auto SEL = [&](int i) -> int { return lp ? sm.psel[i] : a.sel[pb + i]; };
 
-  // ---- 2. first and last pair of each expert in the wave
-  for (int i = tid; i < P; i += NT) {
-    const int e = SEL(i);
-    atomicMin(&sm.first[e], i);
-    atomicMax(&sm.last[e], i);
-  }
-  __syncthreads();
-
-  // ---- 3. D: distinct experts in order of first appearance
   int nD = 0;
-  for (int c0 = 0; c0 < P; c0 += NT) {
-    const int i = c0 + tid;
-    int e = 0;
-    bool f = false;
-    if (i < P) {
-      e = SEL(i);
-      f = sm.first[e] == i;
+  const bool agg = a.agg != nullptr;  // staged call spread over workgroups
+  if (!agg) {
+    // ---- 2. first and last pair of each expert in the wave
+    for (int i = tid; i < P; i += NT) {
+      const int e = SEL(i);
+      atomicMin(&sm.first[e], i);
+      atomicMax(&sm.last[e], i);
     }
-    int tot;
-    const int pos = block_excount(f, sm.wbuf, par, &tot);
-    if (f) {
-      sm.D[nD + pos] = e;
-      sm.dix[e] = nD + pos;
+    __syncthreads();
+
+    // ---- 3. D: distinct experts in order of first appearance
+    for (int c0 = 0; c0 < P; c0 += NT) {
+      const int i = c0 + tid;
+      int e = 0;
+      bool f = false;
+      if (i < P) {
+        e = SEL(i);
+        f = sm.first[e] == i;
+      }
+      int tot;
+      const int pos = block_excount(f, sm.wbuf, par, &tot);
+      if (f) {
+        sm.D[nD + pos] = e;
+        sm.dix[e] = nD + pos;
+      }
+      nD += tot;
     }
-    nD += tot;
+    __syncthreads();
+  } else {
+    // ---- 2-3 from the per-chunk histograms (k_stage_hist): each expert's
+    // first and last pair and count, and the exclusive prefix of its count
+    // over the chunks (the row base of its pairs in each chunk, for
+    // k_stage_rows).  Thread (j, e) takes a contiguous run of chunks.
+    const int nc = a.nchunks;
+    const int32_t* hist = a.agg;
+    const int32_t* cfirst = hist + int64_t(nc) * E;
+    const int32_t* clast = cfirst + int64_t(nc) * E;
+    int32_t* cbase = const_cast<int32_t*>(clast) + int64_t(nc) * E;
+    const int J = max(1, NT / E);
+    const int e = tid % E, j = tid / E;
+    const int per = (nc + J - 1) / J;
+    const int c_lo = min(nc, j * per), c_hi = min(nc, c_lo + per);
+    int* tcnt = &sm.wcnt[0][0];  // [J][E] scratch (the rank tables are not used here)
+    int* tfirst = tcnt + NT;
+    int* tlast = tfirst + NT;
+    const bool mine = tid < J * E;
+    int n = 0, f = 0x7fffffff, l = -1;
+    if (mine)
+      for (int c = c_lo; c < c_hi; ++c) {
+        n += hist[int64_t(c) * E + e];
+        f = min(f, cfirst[int64_t(c) * E + e]);
+        l = max(l, clast[int64_t(c) * E + e]);
+      }
+    if (mine) {
+      tcnt[j * E + e] = n;
+      tfirst[j * E + e] = f;
+      tlast[j * E + e] = l;
+    }
+    __syncthreads();
+    if (mine) {
+      int run = 0;
+      for (int j2 = 0; j2 < j; ++j2) run += tcnt[j2 * E + e];
+      for (int c = c_lo; c < c_hi; ++c) {
+        cbase[int64_t(c) * E + e] = run;
+        run += hist[int64_t(c) * E + e];
+      }
+    }
+    if (tid < E) {
+      int tn = 0, tf = 0x7fffffff, tl = -1;
+      for (int j2 = 0; j2 < J; ++j2) {
+        tn += tcnt[j2 * E + tid];
+        tf = min(tf, tfirst[j2 * E + tid]);
+        tl = max(tl, tlast[j2 * E + tid]);
+      }
+      sm.first[tid] = tf;
+      sm.last[tid] = tl;
+      sm.off[tid] = tn;  // the expert's count until its D position is known
+    }
+    __syncthreads();
+    // D order: rank of each selected expert by its first pair
+    const bool sel_e = tid < E && sm.off[tid] > 0;
+    int rank = 0;
+    if (sel_e) {
+      const int myf = sm.first[tid];
+      for (int e2 = 0; e2 < E; ++e2) rank += (sm.off[e2] > 0 && sm.first[e2] < myf) ? 1 : 0;
+    }
+    (void)block_excount(sel_e, sm.wbuf, par, &nD);
+    if (sel_e) {
+      sm.D[rank] = tid;
+      sm.dix[tid] = rank;
+      sm.cnt[rank] = sm.off[tid];
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   // ---- 4. hits, misses, hybrid split
   if (decode) {
@@ -551,8 +619,9 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
     __syncthreads();
   }
 
-  // ---- 7. per-pair decisions
-  for (int i = tid; i < P; i += NT) {
+  // ---- 7. per-pair decisions (k_stage_rows makes them for staged calls
+  // spread over workgroups)
+  for (int i = tid; i < (agg ? 0 : P); i += NT) {
     const int d = sm.dix[SEL(i)];
     const int c = sm.cls[d];
     a.pair_flag[pb + i] = uint8_t(c);
@@ -562,7 +631,7 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
   // ---- 8. rank of each pair inside its group (pair order), via ballot match
   int nbits = 1;
   while ((1 << nbits) < nD) ++nbits;
-  for (int c0 = 0; c0 < P; c0 += NT) {
+  for (int c0 = 0; c0 < (agg ? 0 : P); c0 += NT) {
     for (int j = tid; j < NW * nD; j += NT) sm.wcnt[j / nD][j % nD] = 0;
     __syncthreads();
     const int i = c0 + tid;
@@ -623,7 +692,7 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
   // run-list entry, where a decode FFN reads them with the descriptor (the
   // descriptor's other fields are written below, field by field, so the two
   // writes never overlap)
-  for (int i = tid; i < P; i += NT) {
+  for (int i = tid; i < (agg ? 0 : P); i += NT) {
     const int d = sm.dix[SEL(i)];
     const int r = lp ? sm.prow[i] : a.pair_row[pb + i];
     const int row = sm.off[d] + r;
@@ -640,6 +709,17 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
       if (tt < kGroupTok) a.gdesc[nHit].tok[tt] = uint16_t(t0 + tt);
       if (a.tiles != nullptr) a.row_slot[P + tt] = (ntiles_d + tt / a.tile_rows) * a.tile_rows + tt % a.tile_rows;
     }
+  }
+
+  // per-expert results for k_stage_rows: row base, run-list position, class,
+  // slot, first MX tile
+  if (agg && tid < nD) {
+    int32_t* etab = a.agg + 4 * int64_t(a.nchunks) * E + 5 * int64_t(sm.D[tid]);
+    etab[0] = sm.off[tid];
+    etab[1] = sm.gpos[tid];
+    etab[2] = sm.cls[tid];
+    etab[3] = sm.cls[tid] == FT_PAIR_MISS_CPU ? -1 : sm.dslot[tid];
+    etab[4] = a.tiles != nullptr ? sm.tbase[tid] : 0;
   }
 
   // ---- 10. group descriptors and run lists
@@ -799,6 +879,84 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
   }
 }
 
+// Staged calls spread over workgroups, 1: per chunk of kStageChunk pairs, each
+// expert's pair count and first and last pair.
+__global__ __launch_bounds__(NT) void k_stage_hist(const int32_t* __restrict__ sel, int P, int E,
+                                                   int32_t* __restrict__ agg, int nchunks) {
+  __shared__ int cnt[kMaxExperts], first[kMaxExperts], last[kMaxExperts];
+  const int tid = threadIdx.x, c = blockIdx.x;
+  for (int e = tid; e < E; e += NT) {
+    cnt[e] = 0;
+    first[e] = 0x7fffffff;
+    last[e] = -1;
+  }
+  __syncthreads();
+  const int i = c * kStageChunk + tid;
+  if (i < P) {
+    const int e = sel[i];
+    atomicAdd(&cnt[e], 1);
+    atomicMin(&first[e], i);
+    atomicMax(&last[e], i);
+  }
+  __syncthreads();
+  int32_t* hist = agg + int64_t(c) * E;
+  for (int e = tid; e < E; e += NT) {
+    hist[e] = cnt[e];
+    hist[int64_t(nchunks) * E + e] = first[e];
+    hist[2 * int64_t(nchunks) * E + e] = last[e];
+  }
+}
+
+// Staged calls spread over workgroups, 3 (after the resolve kernel): the
+// pairs of one chunk -- flag, slot and row of each pair (its group's row base
+// + the pairs of its expert in earlier chunks + its rank in this chunk, by a
+// wavefront-ballot match and a per-wave prefix), the row's token and weight,
+// the group's first tokens in its run-list entry and the row's MX tile slot.
+__global__ __launch_bounds__(NT) void k_stage_rows(ResolveArgs a) {
+  __shared__ int wcnt[NW][kMaxExperts];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, c = blockIdx.x;
+  const int E = a.E, k = a.k, P = a.T * a.k;
+  const int32_t* cbase = a.agg + 3 * int64_t(a.nchunks) * E + int64_t(c) * E;
+  const int32_t* etab = a.agg + 4 * int64_t(a.nchunks) * E;
+  for (int j = tid; j < NW * E; j += NT) wcnt[j / E][j % E] = 0;
+  __syncthreads();
+  const int i = c * kStageChunk + tid;
+  const bool valid = i < P;
+  const int e = valid ? a.sel[i] : 0;
+  int nbits = 1;
+  while ((1 << nbits) < E) ++nbits;
+  uint64_t same = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t bb = __ballot(valid && bit);
+    same &= bit ? bb : ~bb;
+  }
+  const int lrank = __popcll(same & ((1ull << lane) - 1ull));
+  if (valid && lrank == 0) wcnt[wid][e] = __popcll(same);
+  __syncthreads();
+  for (int g = tid; g < E; g += NT) {
+    int run = cbase[g];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int v = wcnt[w][g];
+      wcnt[w][g] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  if (!valid) return;
+  const int r = wcnt[wid][e] + lrank;  // rank in the group
+  const int32_t* et = etab + 5 * e;
+  const int row = et[0] + r, cls = et[2];
+  a.pair_flag[i] = uint8_t(cls);
+  a.pair_slot[i] = et[3];
+  a.pair_row[i] = row;
+  a.row_tok[row] = i / k;
+  a.row_w[row] = a.w[i];
+  if (r < kGroupTok) a.gdesc[et[1]].tok[r] = uint16_t(i / k);
+  if (a.tiles != nullptr) a.row_slot[row] = (et[4] + r / a.tile_rows) * a.tile_rows + r % a.tile_rows;
+}
+
 // Free slots (prefill staging halves, or slots whose copy failed) and restore
 // the recency order invariant: free slots first by index, then residents in
 // their previous order.
@@ -865,8 +1023,19 @@ __global__ __launch_bounds__(NT) void k_free_slots(DevTable tab, int C, int lo0,
 
 }  // namespace
 
+// Staged calls (a.agg set; one wave starting at token 0) run as three
+// kernels: per-chunk histograms over many workgroups, the resolve itself on
+// per-expert totals, the per-pair rows over many workgroups.  The results
+// are the same as the one-workgroup resolve's.  The events bracket all three.
 hipError_t launch_resolve(const ResolveArgs& a, hipStream_t s, Ev ev) {
-  ft_launch(k_resolve, dim3(1), dim3(NT), s, ev, a);
+  if (a.agg == nullptr) {
+    ft_launch(k_resolve, dim3(1), dim3(NT), s, ev, a);
+    return hipGetLastError();
+  }
+  const int P = a.T * a.k;
+  ft_launch(k_stage_hist, dim3(a.nchunks), dim3(NT), s, Ev{ev.a, nullptr}, a.sel, P, a.E, a.agg, a.nchunks);
+  ft_launch(k_resolve, dim3(1), dim3(NT), s, Ev{}, a);
+  ft_launch(k_stage_rows, dim3(a.nchunks), dim3(NT), s, Ev{nullptr, ev.b}, a);
   return hipGetLastError();
 }
 
