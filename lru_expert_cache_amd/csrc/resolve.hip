@@ -845,15 +845,26 @@ __global__ __launch_bounds__(NT) void k_resolve(ResolveArgs a) {
       }
     }
     if (m_cpu > 0) {
+      // rows of host-computed groups, packed group after group: the groups'
+      // D indices and packed bases in LDS (first[] and tbase[] are free in
+      // decode calls by now; the lists above are in host memory, which the
+      // device does not read back)
+      if (tid < nD && sm.cls[tid] == FT_PAIR_MISS_CPU) sm.first[sm.mpos[tid] - m_str] = tid;
       __syncthreads();
-      // rows of host-computed groups, packed group after group
-      for (int j = 0; j < m_cpu; ++j) {
-        int base = 0;
-        for (int j2 = 0; j2 < j; ++j2) base += cc[j2];
-        for (int r = tid; r < cc[j]; r += NT) {
-          ct[base + r] = a.row_tok[cb[j] + r];
-          cw[base + r] = a.row_w[cb[j] + r];
+      int tot;
+      const int hb = block_exscan(tid < m_cpu ? sm.cnt[sm.first[tid]] : 0, sm.wbuf, par, &tot);
+      if (tid < m_cpu) sm.tbase[tid] = hb;
+      __syncthreads();
+      for (int idx = tid; idx < cpu_rows; idx += NT) {
+        int lo = 0, hi = m_cpu - 1;  // last group whose base is <= idx
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (sm.tbase[mid] <= idx) lo = mid;
+          else hi = mid - 1;
         }
+        const int row = sm.off[sm.first[lo]] + (idx - sm.tbase[lo]);
+        ct[idx] = a.row_tok[row];
+        cw[idx] = a.row_w[row];
       }
     }
     if (tid == 0) {
