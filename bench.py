@@ -101,7 +101,8 @@ def measured_traffic(profile_name, algorithmic_bytes):
     """HBM bytes per launch of a kernel from a committed rocprofv3 counter
     summary, or None when the kernel's source has changed since it was taken
     or when this run's launches are not the workload the counters saw (their
-    algorithmic bytes per launch differ by more than 2%)."""
+    algorithmic bytes per launch differ by more than 5%: the hybrid split,
+    measured per run, moves them by a few percent)."""
     path = os.path.join(ROOT, "profiles", profile_name)
     src = os.path.join(ROOT, "lru_expert_cache_amd", "csrc", "ffn.hip")
     try:
@@ -110,7 +111,7 @@ def measured_traffic(profile_name, algorithmic_bytes):
         if kv.get("ffn_source_sha256") != sha:
             return None
         ref = float(kv["algorithmic_bytes_per_launch"])
-        if not abs(algorithmic_bytes - ref) <= 0.02 * ref:
+        if not abs(algorithmic_bytes - ref) <= 0.05 * ref:
             return None
         return float(kv["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
