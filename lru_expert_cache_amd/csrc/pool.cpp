@@ -945,14 +945,47 @@ int forward_decode(ft_moe_pool* p, int layer, int T, const void* x, void* out, h
     }
     for (int i = 0; i < h.n_cpu; ++i) p->last_ce.push_back(ce[i]);
 
-    // the activation rows the host-computed experts need, fetched before the
-    // streamed copies are queued: behind them the small device-to-host copy
-    // would wait for the whole transfer, and the host work would start only
-    // when the copies end instead of overlapping them
+    // the activation rows the host-computed experts need, then the host work,
+    // both before the streamed copies are queued: behind the copies the small
+    // device-to-host copy would wait for the whole transfer, and issuing the
+    // copies (tens of microseconds of API time each) would delay the host work
+    std::thread cpu_thread;
+    struct JoinGuard {
+      std::thread& t;
+      ~JoinGuard() {
+        if (t.joinable()) t.join();
+      }
+    } join_guard{cpu_thread};  // every return below waits for the host work
+    std::vector<int64_t> cpu_base;
+    double host_sec = 0.0;
     if (h.n_cpu > 0) {
       if (p->cpu_copy_pending) FT_HIP_CHECK(hipEventSynchronize(p->ev_cpu_copied));
-      FT_HIP_CHECK(hipMemcpy(p->x_host, x, size_t(T) * p->H * 2, hipMemcpyDeviceToHost));
+      FT_HIP_CHECK(hipMemcpyAsync(p->x_host, x, size_t(T) * p->H * 2, hipMemcpyDeviceToHost, s));
+      FT_HIP_CHECK(hipStreamSynchronize(s));
+      int64_t base = 0;
+      for (int j = 0; j < h.n_cpu; ++j) {
+        cpu_base.push_back(base);
+        base += cc[j];
+      }
+      if (!p->workers) p->workers = std::make_unique<WorkerPool>(p->cpu_threads);
+      std::vector<int32_t> toks(ct, ct + h.cpu_rows);
+      std::vector<float> wts(cw, cw + h.cpu_rows);
+      std::vector<int32_t> experts(ce, ce + h.n_cpu), counts(cc, cc + h.n_cpu);
+      cpu_thread = std::thread([p, layer, toks, wts, experts, counts, cpu_base, &L, &host_sec]() {
+        const auto t0 = std::chrono::steady_clock::now();
+        std::vector<uint16_t> xr(toks.size() * size_t(p->H));
+        for (size_t r = 0; r < toks.size(); ++r)
+          std::memcpy(&xr[r * p->H], p->x_host + int64_t(toks[r]) * p->H, size_t(p->H) * 2);
+        std::vector<HostExpertJob> jobs(experts.size());
+        for (size_t j = 0; j < experts.size(); ++j)
+          jobs[j] = HostExpertJob{p->host_store + p->key_off[int64_t(layer) * p->E + experts[j]],
+                                  xr.data() + cpu_base[j] * p->H, wts.data() + cpu_base[j], counts[j],
+                                  p->cpu_out + cpu_base[j] * p->H};
+        host_experts(L, jobs.data(), int(jobs.size()), *p->workers);
+        host_sec = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
+      });
     }
+
     // streamed misses: one contiguous copy per expert, rotating over the copy
     // streams.  Everything earlier on s (the readers of the victim slots) has
     // finished: the resolve kernel that published this list ran after it.
@@ -978,37 +1011,6 @@ int forward_decode(ft_moe_pool* p, int layer, int T, const void* x, void* out, h
       prof_end(p, FT_STAGE_COPY, ec, p->copy[0], double(h.n_stream) * double(p->canon_bytes[p->fmt[layer]]), 0.0);
       copy_timer_end(p, layer, et, p->copy[0], double(h.n_stream) * double(p->canon_bytes[p->fmt[layer]]));
       FT_HIP_CHECK(hipEventRecord(p->ev_copied, p->copy[0]));
-    }
-
-    // host-computed misses run on the host worker threads while the GPU works
-    // (one batched call for all of them: gate/up row blocks of every expert,
-    // then their down row blocks)
-    std::thread cpu_thread;
-    std::vector<int64_t> cpu_base;
-    double host_sec = 0.0;
-    if (h.n_cpu > 0) {
-      int64_t base = 0;
-      for (int j = 0; j < h.n_cpu; ++j) {
-        cpu_base.push_back(base);
-        base += cc[j];
-      }
-      if (!p->workers) p->workers = std::make_unique<WorkerPool>(p->cpu_threads);
-      std::vector<int32_t> toks(ct, ct + h.cpu_rows);
-      std::vector<float> wts(cw, cw + h.cpu_rows);
-      std::vector<int32_t> experts(ce, ce + h.n_cpu), counts(cc, cc + h.n_cpu);
-      cpu_thread = std::thread([p, layer, toks, wts, experts, counts, cpu_base, &L, &host_sec]() {
-        const auto t0 = std::chrono::steady_clock::now();
-        std::vector<uint16_t> xr(toks.size() * size_t(p->H));
-        for (size_t r = 0; r < toks.size(); ++r)
-          std::memcpy(&xr[r * p->H], p->x_host + int64_t(toks[r]) * p->H, size_t(p->H) * 2);
-        std::vector<HostExpertJob> jobs(experts.size());
-        for (size_t j = 0; j < experts.size(); ++j)
-          jobs[j] = HostExpertJob{p->host_store + p->key_off[int64_t(layer) * p->E + experts[j]],
-                                  xr.data() + cpu_base[j] * p->H, wts.data() + cpu_base[j], counts[j],
-                                  p->cpu_out + cpu_base[j] * p->H};
-        host_experts(L, jobs.data(), int(jobs.size()), *p->workers);
-        host_sec = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
-      });
     }
 
     int rc = verify_groups(p, layer, 0, h.n_hit_list, nullptr, s);
