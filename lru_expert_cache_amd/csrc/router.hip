@@ -105,87 +105,91 @@ __global__ __launch_bounds__(kSmallThreads) void k_router_logits_small(
 // rows are shared by the workgroup's waves through the L1), with the next
 // chunk's loads issued before this chunk's MFMAs.  A wave owns 16 tokens x 32
 // experts (two MFMA tiles), a workgroup 64 x 32.
-constexpr int kMfmaTokW = 16, kMfmaWaves = 4, kMfmaExp = 32, kMfmaKC = 64;
-// wave groups splitting K (two waves per SIMD: 4096 x 2048 x 128 took 69 us
-// with one group, 54 with two, 53.5 with four)
-constexpr int kMfmaKS = 2;
+constexpr int kMfmaTokW = 16, kMfmaKC = 64;
 
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 // One K chunk of a lane's operands: 16 bf16 of its token, 16 fp32 of its
-// router row in each of the two expert tiles.
+// router row in each of the wave's ET expert tiles.
+template <int ET>
 struct RouterChunk {
   uint4 xv[2];
-  float4 wv[2][4];
+  float4 wv[ET][4];
 };
 
-__device__ inline void router_chunk_load(RouterChunk& c, const uint16_t* xr, const float* w0, const float* w1,
+template <int ET>
+__device__ inline void router_chunk_load(RouterChunk<ET>& c, const uint16_t* xr, const float* const (&wrow)[ET],
                                          int k0) {
   c.xv[0] = *reinterpret_cast<const uint4*>(xr + k0);
   c.xv[1] = *reinterpret_cast<const uint4*>(xr + k0 + 8);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    c.wv[0][j] = *reinterpret_cast<const float4*>(w0 + k0 + 4 * j);
-    c.wv[1][j] = *reinterpret_cast<const float4*>(w1 + k0 + 4 * j);
-  }
+  for (int e = 0; e < ET; ++e)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c.wv[e][j] = *reinterpret_cast<const float4*>(wrow[e] + k0 + 4 * j);
 }
 
 __device__ inline float f4_at(const float4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
 
-// KS wave groups of the workgroup split K: group q takes chunks q, q + KS,
-// ...; groups 1 .. KS-1 leave their sums in LDS and group 0 adds them in
-// group order (a fixed order, so the logits do not depend on timing).
-template <int KS>
-__global__ __launch_bounds__(64 * kMfmaWaves * KS) void k_router_logits_mfma(
+// A workgroup is TW x KS waves: TW waves of 16 tokens each (a wave owns ET
+// tiles of 16 experts), times KS wave groups splitting K: group q takes
+// chunks q, q + KS, ...; groups 1 .. KS-1 leave their sums in LDS and group 0
+// adds them in group order (a fixed order, so the logits do not depend on
+// timing).
+template <int TW, int ET, int KS>
+__global__ __launch_bounds__(64 * TW * KS) void k_router_logits_mfma(
     const uint16_t* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
     double* __restrict__ z, int T, int H, int E) {
-  __shared__ f64x4 part[KS > 1 ? KS - 1 : 1][kMfmaWaves][2][64];
+  __shared__ f64x4 part[KS > 1 ? KS - 1 : 1][TW][ET][64];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int wv = wid % kMfmaWaves, q = wid / kMfmaWaves;
+  const int wv = wid % TW, q = wid / TW;
   const int g = lane >> 4, n = lane & 15;
-  const int t0 = blockIdx.x * (kMfmaTokW * kMfmaWaves) + wv * kMfmaTokW;
-  const int e0 = blockIdx.y * kMfmaExp;
+  const int t0 = blockIdx.x * (kMfmaTokW * TW) + wv * kMfmaTokW;
+  const int e0 = blockIdx.y * (16 * ET);
   // operand rows of this lane (clamped: rows past T or E are computed and not
   // stored); lane group g takes K 16g .. 16g + 15 of every 64-wide chunk
   const uint16_t* xr = x + int64_t(min(t0 + n, T - 1)) * H + 16 * g;
-  const float* w0 = wr + int64_t(min(e0 + n, E - 1)) * H + 16 * g;
-  const float* w1 = wr + int64_t(min(e0 + 16 + n, E - 1)) * H + 16 * g;
-  f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
-  RouterChunk cur, nxt;
+  const float* wrow[ET];
+#pragma unroll
+  for (int e = 0; e < ET; ++e) wrow[e] = wr + int64_t(min(e0 + 16 * e + n, E - 1)) * H + 16 * g;
+  f64x4 acc[ET];
+#pragma unroll
+  for (int e = 0; e < ET; ++e) acc[e] = {0.0, 0.0, 0.0, 0.0};
+  RouterChunk<ET> cur, nxt;
   const int kstep = kMfmaKC * KS;
-  if (q * kMfmaKC < H) router_chunk_load(cur, xr, w0, w1, q * kMfmaKC);
+  if (q * kMfmaKC < H) router_chunk_load<ET>(cur, xr, wrow, q * kMfmaKC);
   for (int k0 = q * kMfmaKC; k0 < H; k0 += kstep) {
-    if (k0 + kstep < H) router_chunk_load(nxt, xr, w0, w1, k0 + kstep);
+    if (k0 + kstep < H) router_chunk_load<ET>(nxt, xr, wrow, k0 + kstep);
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
       const uint32_t xu = s < 8 ? (s < 4 ? (s < 2 ? cur.xv[0].x : cur.xv[0].y) : (s < 6 ? cur.xv[0].z : cur.xv[0].w))
                                 : (s < 12 ? (s < 10 ? cur.xv[1].x : cur.xv[1].y) : (s < 14 ? cur.xv[1].z : cur.xv[1].w));
       const double a = bf16_to_f64(uint16_t(s & 1 ? xu >> 16 : xu & 0xFFFF));
-      acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(a, double(f4_at(cur.wv[0][s >> 2], s & 3)), acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(a, double(f4_at(cur.wv[1][s >> 2], s & 3)), acc1, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < ET; ++e)
+        acc[e] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, double(f4_at(cur.wv[e][s >> 2], s & 3)), acc[e], 0, 0, 0);
     }
     cur = nxt;
   }
   if constexpr (KS > 1) {
-    if (q > 0) {
-      part[q - 1][wv][0][lane] = acc0;
-      part[q - 1][wv][1][lane] = acc1;
-    }
+    if (q > 0)
+#pragma unroll
+      for (int e = 0; e < ET; ++e) part[q - 1][wv][e][lane] = acc[e];
     __syncthreads();
     if (q > 0) return;
 #pragma unroll
-    for (int j = 0; j < KS - 1; ++j) {
-      acc0 += part[j][wv][0][lane];
-      acc1 += part[j][wv][1][lane];
-    }
+    for (int j = 0; j < KS - 1; ++j)
+#pragma unroll
+      for (int e = 0; e < ET; ++e) acc[e] += part[j][wv][e][lane];
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int t = t0 + 4 * i + g;
     if (t >= T) continue;
-    const int ea = e0 + n, eb = e0 + 16 + n;
-    if (ea < E) z[int64_t(t) * E + ea] = acc0[i] + (bias ? double(bias[ea]) : 0.0);
-    if (eb < E) z[int64_t(t) * E + eb] = acc1[i] + (bias ? double(bias[eb]) : 0.0);
+#pragma unroll
+    for (int e = 0; e < ET; ++e) {
+      const int ex = e0 + 16 * e + n;
+      if (ex < E) z[int64_t(t) * E + ex] = acc[e][i] + (bias ? double(bias[ex]) : 0.0);
+    }
   }
 }
 
@@ -206,16 +210,26 @@ __global__ __launch_bounds__(64 * kTopkWaves) void k_topk(const double* __restri
 
 }  // namespace
 
+// Up to 16 tokens: the scalar kernels (one workgroup per expert; a batch of
+// 1 takes 4.4 us on the Qwen-A3B shape, where the matrix-core kernel was
+// slower).  17 to 64 tokens: one 16-token wave per 16 experts with K split
+// over 16 wave groups, so a layer's few tokens still spread over many
+// workgroups (GLM-shaped layer at 32 tokens: 23 us against 67 us scalar).
+// More (prefill): four 16-token waves of 32 experts each and two K groups
+// (two waves per SIMD: 4096 x 2048 x 128 took 69 us with one group, 54 with
+// two, 53.5 with four).
 hipError_t launch_router_logits(const uint16_t* x, const float* wr, const float* bias, double* z, int T,
                                 int H, int E, hipStream_t s, Ev ev) {
-  if (T <= 64) {
-    if (T <= 4)
-      ft_launch(k_router_logits_small<4>, dim3(E), dim3(kSmallThreads), s, ev, x, wr, bias, z, T, H, E);
-    else
-      ft_launch(k_router_logits_small<16>, dim3(E), dim3(kSmallThreads), s, ev, x, wr, bias, z, T, H, E);
+  if (T <= 4) {
+    ft_launch(k_router_logits_small<4>, dim3(E), dim3(kSmallThreads), s, ev, x, wr, bias, z, T, H, E);
+  } else if (T <= 16) {
+    ft_launch(k_router_logits_small<16>, dim3(E), dim3(kSmallThreads), s, ev, x, wr, bias, z, T, H, E);
+  } else if (T <= 64) {
+    const dim3 grid((T + 15) / 16, (E + 15) / 16);
+    ft_launch(k_router_logits_mfma<1, 1, 16>, grid, dim3(64 * 16), s, ev, x, wr, bias, z, T, H, E);
   } else {
-    const dim3 grid((T + kMfmaTokW * kMfmaWaves - 1) / (kMfmaTokW * kMfmaWaves), (E + kMfmaExp - 1) / kMfmaExp);
-    ft_launch(k_router_logits_mfma<kMfmaKS>, grid, dim3(64 * kMfmaWaves * kMfmaKS), s, ev, x, wr, bias, z, T, H, E);
+    const dim3 grid((T + 63) / 64, (E + 31) / 32);
+    ft_launch(k_router_logits_mfma<4, 2, 2>, grid, dim3(64 * 4 * 2), s, ev, x, wr, bias, z, T, H, E);
   }
   return hipGetLastError();
 }

@@ -119,3 +119,33 @@ def test_hit_d2d_without_residents_streams_everything_and_option_is_per_chunk():
         assert ei.value.code == ft.FT_E_INVALID
     finally:
         g.close()
+
+
+@pytest.mark.parametrize("hit_d2d", [False, True])
+def test_staged_resolve_many_experts_several_chunks(hit_d2d):
+    """Staged calls resolve over many workgroups (chunks of 1024 pairs): 512
+    experts, the most a layer may have (two threads per expert in the
+    per-expert totals), and 700 tokens x top-4 = 2800 pairs (three chunks, the
+    last one partial), with and without hit-D2D, between decode calls: the
+    same decisions, tables and counters as the oracle's staging."""
+    from tests.moe_case import GpuLayerStack, compare_call, compare_table
+    import lru_expert_cache_amd as ft
+
+    w = _small(145 + int(hit_d2d), 2, 128, 128, 512, 4, [MX, NV], 2 * 512 + 200)
+    g = GpuLayerStack(w)
+    o = OracleLayerStack(w, pool_slots=g.C)
+    try:
+        for rnd in range(2):
+            for l in range(2):
+                x = ms.activations(w, l, 10 * rnd, 8)
+                compare_call(g.forward(l, x, g.bias(l, 0)), o.forward(l, x, ms.popularity_bias(w, l, 0)), 4)
+            for l in range(2):
+                x = ms.activations(w, l, 300 + rnd, 700)
+                gr = g.forward(l, x, g.bias(l, 0), prefill=True, hit_d2d=hit_d2d)
+                compare_call(gr, o.forward(l, x, ms.popularity_bias(w, l, 0), prefill=True, hit_d2d=hit_d2d), 4)
+            compare_table(g, o)
+        st = ft.ft_moe_pool_stats(g.pool)
+        for key in ("pair_hits", "pair_misses", "expert_hits", "expert_misses", "evictions", "bytes_h2d", "calls"):
+            assert st[key] == o.stats[key], (key, st[key], o.stats[key])
+    finally:
+        g.close()
