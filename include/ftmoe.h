@@ -400,6 +400,23 @@ int ft_moe_set_profiling(ft_moe_pool *p, int32_t stage_mask);
 /* Waits for recorded events, returns the sums; reset != 0 clears them. */
 int ft_moe_profile_read(ft_moe_pool *p, ft_moe_profile *out, int32_t reset);
 
+/* Diagnostics for tests: copies an internal device buffer of the pool into host
+ * memory dst (bytes from its start), after waiting for all work on the device.
+ * FT_DBG_H_CODES / FT_DBG_H_SCALES: the activation tiles of h that the latest
+ * prefill call in an MX activation mode (FT_ACT_MXFP4 / FT_ACT_MXFP8) wrote
+ * in its gate/up GEMM for its down GEMM -- per (128-row tile, 128-K step)
+ * block: codes in 16-row sub-tiles of 1 KB (FP4) or 2 KB (FP8), a row's
+ * 32-element block q at byte (16 q + row % 16) * 16 of its sub-tile (FP4: 32
+ * E2M1 codes, element 2i in the low nibble of byte i; FP8: the two 16-byte
+ * halves of the block at sub-tile bytes (q / 2) * 1024 + (16 (2 q % 4) + row
+ * % 16) * 16 and the next lane's 16 bytes), and 512 bytes of E8M0 scales
+ * (row * 4 + q); blocks of FP4 codes 8 KB apart, of FP8 codes 16 KB, of
+ * scales 512 bytes.  FT_DBG_ROW_SLOT: int32 per row of that call, the row's
+ * slot in the tiles (128 * tile + row in tile).  FT_E_INVALID when the buffer
+ * does not exist yet or is smaller than bytes. */
+enum { FT_DBG_H_CODES = 0, FT_DBG_H_SCALES = 1, FT_DBG_ROW_SLOT = 2 };
+int ft_moe_debug_read(ft_moe_pool *p, int32_t what, void *dst, int64_t bytes);
+
 void ft_moe_destroy_pool(ft_moe_pool *p);
 const char *ft_moe_last_error(void);
 

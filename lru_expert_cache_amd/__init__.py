@@ -37,7 +37,9 @@ EXPORTED = ["ft_moe_init_pool", "ft_moe_layer_forward", "ft_moe_pool_stats", "ft
             "ft_moe_set_profiling", "ft_moe_profile_read", "ft_moe_destroy_pool", "ft_moe_last_error",
             "ft_moe_reserve", "ft_moe_resize_pool", "ft_moe_decide_mode", "ft_moe_measure_mode",
             "ft_moe_ffn_kernel_name", "ft_moe_mfma_rate", "ft_moe_layer_forward_noalloc",
-            "ft_moe_set_hybrid_share_format", "ft_moe_get_hybrid_share", "ft_moe_rebalance"]
+            "ft_moe_set_hybrid_share_format", "ft_moe_get_hybrid_share", "ft_moe_rebalance",
+            "ft_moe_debug_read"]
+FT_DBG_H_CODES, FT_DBG_H_SCALES, FT_DBG_ROW_SLOT = 0, 1, 2
 
 FT_MODE_OFFLOAD, FT_MODE_HYBRID, FT_MODE_FUSED = 0, 1, 2
 
@@ -151,6 +153,8 @@ def lib() -> ctypes.CDLL:
     L.ft_moe_get_hybrid_share.restype = ctypes.c_int
     L.ft_moe_rebalance.argtypes = [P, ctypes.c_int32, ctypes.POINTER(ft_moe_rebalance_report)]
     L.ft_moe_rebalance.restype = ctypes.c_int
+    L.ft_moe_debug_read.argtypes = [P, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64]
+    L.ft_moe_debug_read.restype = ctypes.c_int
     L.ft_moe_host_expert_rate.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                           ctypes.POINTER(ctypes.c_double)]
     L.ft_moe_host_expert_rate.restype = ctypes.c_int
@@ -327,6 +331,13 @@ def ft_moe_get_hybrid_share(pool, fmt: int) -> float:
     v = ctypes.c_double()
     _check(lib().ft_moe_get_hybrid_share(pool, int(fmt), ctypes.byref(v)))
     return v.value
+
+
+def ft_moe_debug_read(pool, what: int, nbytes: int) -> bytes:
+    """A copy of the first nbytes of an internal buffer (FT_DBG_*), for tests."""
+    buf = ctypes.create_string_buffer(int(nbytes))
+    _check(lib().ft_moe_debug_read(pool, int(what), buf, int(nbytes)))
+    return buf.raw
 
 
 def ft_moe_rebalance(pool, apply: bool = True) -> dict:

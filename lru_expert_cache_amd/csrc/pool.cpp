@@ -128,6 +128,7 @@ struct ft_moe_pool {
   uint8_t* tq_codes = nullptr;      // MX GEMM activation tiles (allocated at the first MX call): x
   uint8_t* tq_scales = nullptr;
   uint8_t* hq_codes = nullptr;      // and h, written by the gate/up GEMM while x tiles are read
+  int64_t hq_blocks = 0;            // (tile, K step) blocks of the h tiles
   uint8_t* hq_scales = nullptr;
   int32_t* tiles = nullptr;         // [2 * max_tiles]
   int32_t* stage_agg = nullptr;     // staged resolve scratch (stage_agg_ints)
@@ -693,8 +694,10 @@ int run_mx_ffn(ft_moe_pool* p, int layer, const void* x, int T, int act, hipStre
         (rc = mx_alloc(&p->hq_codes, hb * mx_tile_code_bytes(false))) ||
         (rc = mx_alloc(&p->hq_scales, hb * kMxTileScaleBytes))) {
       dev_free(p->tq_codes); dev_free(p->tq_scales); dev_free(p->hq_codes); dev_free(p->hq_scales);
+      p->hq_blocks = 0;
       return rc;
     }
+    p->hq_blocks = hb;
   }
   int rc;
   if (mx && (rc = mx_act_tiles(p, static_cast<const uint16_t*>(x), T, p->H, fp4, s))) return rc;
@@ -2083,6 +2086,36 @@ int ft_moe_profile_read(ft_moe_pool* p, ft_moe_profile* out, int32_t reset) {
   }
   *out = p->prof;
   if (reset) p->prof = ft_moe_profile{};
+  return FT_OK;
+}
+
+int ft_moe_debug_read(ft_moe_pool* p, int32_t what, void* dst, int64_t bytes) {
+  if (!p || !dst || bytes < 0) {
+    set_error("need a pool, a destination and a byte count");
+    return FT_E_INVALID;
+  }
+  const void* src = nullptr;
+  int64_t cap = 0;
+  if (what == FT_DBG_H_CODES) {
+    src = p->hq_codes;
+    cap = p->hq_codes ? p->hq_blocks * mx_tile_code_bytes(false) : 0;
+  } else if (what == FT_DBG_H_SCALES) {
+    src = p->hq_scales;
+    cap = p->hq_scales ? p->hq_blocks * kMxTileScaleBytes : 0;
+  } else if (what == FT_DBG_ROW_SLOT) {
+    src = p->row_slot;
+    cap = p->row_slot ? (int64_t(p->cap_T) * p->k + (p->shared ? p->cap_T : 0)) * 4 : 0;
+  } else {
+    set_error("unknown buffer %d", what);
+    return FT_E_INVALID;
+  }
+  if (src == nullptr || bytes > cap) {
+    set_error("buffer %d holds %lld bytes, %lld asked", what, (long long)cap, (long long)bytes);
+    return FT_E_INVALID;
+  }
+  DeviceGuard dg(p->device);
+  FT_HIP_CHECK(hipDeviceSynchronize());
+  FT_HIP_CHECK(hipMemcpy(dst, src, size_t(bytes), hipMemcpyDeviceToHost));
   return FT_OK;
 }
 
