@@ -562,12 +562,20 @@ def main():
                  for name, kind in (("fp4_32x32x64", ft.FT_MFMA_FP4_32X32X64),
                                     ("fp8_16x16x128", ft.FT_MFMA_FP8_16X16X128),
                                     ("bf16_16x16x32", ft.FT_MFMA_BF16_16X16X32),
-                                    ("bf16_32x32x16", ft.FT_MFMA_BF16_32X32X16))}
+                                    ("bf16_32x32x16", ft.FT_MFMA_BF16_32X32X16),
+                                    ("f64_16x16x4", ft.FT_MFMA_F64_16X16X4))}
         extras["mfma_measured_TFLOPs"] = rates
         for mode, key in (("bf16", "bf16_16x16x32"), ("mxfp8", "fp8_16x16x128"), ("mxfp4", "fp4_32x32x64")):
             r = extras["qwen_a3b"]["prefill"].get(mode)
             if r and r.get("ffn_TFLOPs"):
                 r["ffn_frac_of_measured_mfma"] = r["ffn_TFLOPs"] / rates[key]
+        # the prefill router (fp64 logits on the matrix cores), 2 T E H flop per layer
+        pf, wq = extras["qwen_a3b"]["prefill"], ms.workload("qwen-a3b-prefill-4096")
+        rt = pf.get("mxfp4", {}).get("stage_ms_per_layer", {}).get("router")
+        if rt:
+            tf = 2.0 * pf["chunk_tokens"] * wq.num_experts * wq.hidden / (rt * 1e-3) / 1e12
+            pf["router"] = {"us_per_layer": rt * 1e3, "TFLOPs": tf, "frac_of_sheet_fp64": tf / 78.6,
+                            "frac_of_measured_fp64": tf / rates["f64_16x16x4"]}
     if args.calibrate_copy:
         a = torch.empty(128 << 20, dtype=torch.int16, device=dev).fill_(1)
         b = torch.empty_like(a)

@@ -358,10 +358,12 @@ int ft_moe_rebalance(ft_moe_pool *p, int32_t apply, ft_moe_rebalance_report *out
 int ft_moe_host_expert_rate(ft_moe_pool *p, int32_t layer, int32_t tokens, int32_t iters,
                             double *bytes_per_s);
 
-/* Measured issue rate of the matrix-core instructions the prefill GEMM uses,
- * reported beside the data-sheet peaks.  kind 0: v_mfma_scale_f32_32x32x64_f8f6f4
- * with FP4 operands; 1: v_mfma_scale_f32_16x16x128_f8f6f4 with FP8 operands;
- * 2: v_mfma_f32_16x16x32_bf16; 3: v_mfma_f32_32x32x16_bf16.  Runs 1024
+/* Measured issue rate of the matrix-core instructions the prefill GEMM and
+ * the router use, reported beside the data-sheet peaks.  kind 0:
+ * v_mfma_scale_f32_32x32x64_f8f6f4 with FP4 operands; 1:
+ * v_mfma_scale_f32_16x16x128_f8f6f4 with FP8 operands; 2:
+ * v_mfma_f32_16x16x32_bf16; 3: v_mfma_f32_32x32x16_bf16; 4:
+ * v_mfma_f64_16x16x4_f64 (the router's logits).  Runs 1024
  * workgroups of 4 waves, each wave issuing `iters` rounds of independent
  * MFMAs on register operands, once to warm up and once timed with HIP
  * events on `hip_stream` (a hipStream_t; null

@@ -352,7 +352,8 @@ def ft_moe_host_expert_rate(pool, layer: int, tokens: int, iters: int = 1) -> fl
     return r.value
 
 
-FT_MFMA_FP4_32X32X64, FT_MFMA_FP8_16X16X128, FT_MFMA_BF16_16X16X32, FT_MFMA_BF16_32X32X16 = 0, 1, 2, 3
+FT_MFMA_FP4_32X32X64, FT_MFMA_FP8_16X16X128, FT_MFMA_BF16_16X16X32, FT_MFMA_BF16_32X32X16, FT_MFMA_F64_16X16X4 = \
+    0, 1, 2, 3, 4
 
 
 def ft_moe_mfma_rate(kind: int, iters: int = 2000, stream: int = 0) -> float:

@@ -63,7 +63,7 @@ def test_tiny_64_calls_of_one_token():
         g.close()
 
 
-@pytest.mark.parametrize("kind,sheet_tflops", [(0, 10100.0), (1, 5000.0), (2, 2500.0), (3, 2500.0)])
+@pytest.mark.parametrize("kind,sheet_tflops", [(0, 10100.0), (1, 5000.0), (2, 2500.0), (3, 2500.0), (4, 78.6)])
 def test_mfma_rate_is_below_the_data_sheet_peak(kind, sheet_tflops):
     # register-only MFMA loops: a positive rate that no instruction mix can push
     # past the data-sheet dense peak of its operand type
