@@ -182,7 +182,6 @@ __attribute__((target("avx512f,avx512bw,avx2,fma,f16c"))) inline void decode_lan
                                                                                      const uint8_t* blob,
                                                                                      int64_t tile, int lane,
                                                                                      float g, __m512 w[2]) {
-  const Tables& tb = tables();
   if (fmt == FT_FMT_FP8_B128) {
     const uint8_t* c = blob + M.codes_off + (tile * 64 + lane) * 32;
     float sc;
@@ -191,6 +190,7 @@ __attribute__((target("avx512f,avx512bw,avx2,fma,f16c"))) inline void decode_lan
     const __m256i abs7 = _mm256_set1_epi8(0x7F);
     const __m256i cb = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(c));
     if (!_mm256_testz_si256(_mm256_cmpeq_epi8(_mm256_and_si256(cb, abs7), abs7), abs7)) {
+      const Tables& tb = tables();
       for (int v = 0; v < 2; ++v) {
         const __m512i idx = _mm512_cvtepu8_epi32(_mm_loadu_si128(reinterpret_cast<const __m128i*>(c + 16 * v)));
         w[v] = _mm512_mul_ps(_mm512_i32gather_ps(idx, tb.e4m3, 4), vs);
@@ -219,11 +219,32 @@ __attribute__((target("avx512f,avx512bw,avx2,fma,f16c"))) inline void decode_lan
     return;
   }
   // NVFP4: bytes 0..7 (elements 0..15) take the first scale, bytes 8..15 the second
+  const Tables& tb = tables();
   const uint8_t* sp = blob + M.scales_off + (tile * 64 + lane) * 2;
   const __m512 sv = _mm512_mask_blend_ps(__mmask16(0xFF00), _mm512_set1_ps(tb.e4m3[sp[0]] * g),
                                          _mm512_set1_ps(tb.e4m3[sp[1]] * g));
   w[0] = _mm512_mul_ps(_mm512_permutexvar_ps(lo, lut), sv);
   w[1] = _mm512_mul_ps(_mm512_permutexvar_ps(hi, lut), sv);
+}
+
+// MXFP4 on AVX-512, for callers that hold the lane's scale: the 16 lanes of a
+// K quarter have their E8M0 bytes side by side, so mx_scales16 turns them into
+// 16 floats at once (the same values as e8m0_value) and each lane's decode is
+// then the table scaling and two permutes, as in decode_lane_avx512.
+__attribute__((target("avx512f,avx512bw,avx2,fma,f16c"))) inline void mx_scales16(const uint8_t* s, float* out) {
+  const __m512i b = _mm512_cvtepu8_epi32(_mm_loadu_si128(reinterpret_cast<const __m128i*>(s)));
+  const __m512i u = _mm512_mask_blend_epi32(_mm512_cmpeq_epi32_mask(b, _mm512_setzero_si512()),
+                                            _mm512_slli_epi32(b, 23), _mm512_set1_epi32(0x00400000));
+  _mm512_storeu_ps(out, _mm512_castsi512_ps(u));
+}
+__attribute__((target("avx512f,avx512bw,avx2,fma,f16c"))) inline void decode_mxfp4_avx512(const uint8_t* c, float s,
+                                                                                          __m512 w[2]) {
+  const __m512 lut = _mm512_setr_ps(0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f, -0.0f, -0.5f, -1.0f, -1.5f,
+                                    -2.0f, -3.0f, -4.0f, -6.0f);
+  const __m512i v = _mm512_cvtepu8_epi32(_mm_loadu_si128(reinterpret_cast<const __m128i*>(c)));
+  const __m512 ls = _mm512_mul_ps(lut, _mm512_set1_ps(s));
+  w[0] = _mm512_permutexvar_ps(_mm512_and_si512(v, _mm512_set1_epi32(15)), ls);
+  w[1] = _mm512_permutexvar_ps(_mm512_srli_epi32(v, 4), ls);
 }
 
 __attribute__((target("avx512f,avx512bw,avx2,fma,f16c"))) void decode_lane_avx512_store(const MatLayout& M, int fmt,
@@ -362,7 +383,7 @@ struct RowBlocks<kAvx512> {
     part.resize(size_t(64) * rows * 16);
     constexpr int kRegRows = 8;  // input rows whose quarter stays in registers
     __m512 xv[2 * kRegRows];
-    const bool fp4 = fmt != FT_FMT_FP8_B128;
+    const bool fp4 = fmt != FT_FMT_FP8_B128, mx = fmt == FT_FMT_MXFP4;
     for (int rb = rb_begin; rb < rb_end; ++rb) {
       std::fill(acc.begin(), acc.end(), 0.0f);
       for (int mi = 0; mi < nm; ++mi) {
@@ -374,10 +395,15 @@ struct RowBlocks<kAvx512> {
             const int k0 = kb * kTileK + 32 * q;
             const int nreg = std::min(rows, kRegRows);
             for (int t = 0; t < nreg; ++t) load_x512(xf + size_t(t) * K + k0, fp4, &xv[2 * t]);
+            float msc[16];
+            if (mx) mx_scales16(blob + M.scales_off + tile * 64 + 16 * q, msc);
             for (int r = 0; r < 16; ++r) {
               const int lane = 16 * q + r;
               __m512 w[2];
-              decode_lane_avx512(M, fmt, blob, tile, lane, gsc[mi], w);
+              if (mx)
+                decode_mxfp4_avx512(blob + M.codes_off + (tile * 64 + lane) * 16, msc[r], w);
+              else
+                decode_lane_avx512(M, fmt, blob, tile, lane, gsc[mi], w);
               float* pa = &part[size_t(lane) * rows * 16];
               for (int t = 0; t < nreg; ++t)
                 _mm512_storeu_ps(pa + 16 * t, _mm512_fmadd_ps(w[1], xv[2 * t + 1],
