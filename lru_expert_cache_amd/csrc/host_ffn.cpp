@@ -247,6 +247,35 @@ __attribute__((target("avx512f,avx512bw,avx2,fma,f16c"))) inline void decode_mxf
   w[1] = _mm512_permutexvar_ps(_mm512_srli_epi32(v, 4), ls);
 }
 
+// FP8-b128 on AVX-512 for callers that hold the lane's block scale: the fp16
+// placement of decode_lane_avx512, with lanes holding a NaN code (S.1111.111)
+// decoded by table out of line.
+__attribute__((target("avx512f,avx512bw,avx2,fma,f16c"), noinline)) void decode_fp8_nan_avx512(const uint8_t* c,
+                                                                                                 float sc,
+                                                                                                 __m512 w[2]) {
+  const Tables& tb = tables();
+  for (int v = 0; v < 2; ++v) {
+    const __m512i idx = _mm512_cvtepu8_epi32(_mm_loadu_si128(reinterpret_cast<const __m128i*>(c + 16 * v)));
+    w[v] = _mm512_mul_ps(_mm512_i32gather_ps(idx, tb.e4m3, 4), _mm512_set1_ps(sc));
+  }
+}
+__attribute__((target("avx512f,avx512bw,avx2,fma,f16c"))) inline void decode_fp8_avx512(const uint8_t* c, float sc,
+                                                                                        __m512 w[2]) {
+  const __m256i abs7 = _mm256_set1_epi8(0x7F);
+  const __m256i cb = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(c));
+  if (__builtin_expect(!_mm256_testz_si256(_mm256_cmpeq_epi8(_mm256_and_si256(cb, abs7), abs7), abs7), 0)) {
+    decode_fp8_nan_avx512(c, sc, w);
+    return;
+  }
+  const __m256i keep = _mm256_set1_epi16(int16_t(0xBF80u));
+  const __m512 vs = _mm512_set1_ps(sc), two8 = _mm512_set1_ps(256.0f);
+  const __m128i half[2] = {_mm256_castsi256_si128(cb), _mm256_extracti128_si256(cb, 1)};
+  for (int v = 0; v < 2; ++v) {
+    const __m256i h = _mm256_and_si256(_mm256_slli_epi16(_mm256_cvtepi8_epi16(half[v]), 7), keep);
+    w[v] = _mm512_mul_ps(_mm512_mul_ps(_mm512_cvtph_ps(h), two8), vs);
+  }
+}
+
 __attribute__((target("avx512f,avx512bw,avx2,fma,f16c"))) void decode_lane_avx512_store(const MatLayout& M, int fmt,
                                                                                     const uint8_t* blob,
                                                                                     int64_t tile, int lane, float g,
@@ -373,6 +402,62 @@ __attribute__((target("avx512f,avx512bw,avx2,fma,f16c"))) inline void load_x512(
 // into even and odd positions for the E2M1 formats, as their weights come).
 template <>
 struct RowBlocks<kAvx512> {
+  // Up to four input rows of an MXFP4 or FP8 matrix (the experts the hybrid
+  // split sends to the host are the least used ones, mostly one or two rows):
+  // the inputs of QG K quarters of a tile stay in registers (all four for one
+  // or two rows, two for three or four), and a tile row's lanes of those
+  // quarters are summed there, so its partial sums part[r][t] are read and
+  // written 4 / QG times per tile instead of once per lane.  The decode is the
+  // format's own (no branch on the format in the loop): MXFP4 with the
+  // quarter's 16 scales converted at once, FP8 with the tile row's block
+  // scale read once and the rare NaN codes decoded out of line.
+  template <int RR, int QG, bool MX>
+  __attribute__((target("avx512f,avx512bw,avx2,fma,f16c"))) static void few_rows(
+      const MatLayout& M, const uint8_t* blob, int64_t rb, int nkb, const float* xf, int K, float* part) {
+    for (int kb = 0; kb < nkb; ++kb) {
+      const int64_t tile = rb * nkb + kb;
+      const uint8_t* codes = blob + M.codes_off + tile * (MX ? 1024 : 2048);
+      for (int q0 = 0; q0 < 4; q0 += QG) {
+        __m512 xv[RR][QG][2];
+        for (int t = 0; t < RR; ++t)
+          for (int j = 0; j < QG; ++j) load_x512(xf + size_t(t) * K + kb * kTileK + 32 * (q0 + j), MX, xv[t][j]);
+        float msc[16 * QG];
+        if constexpr (MX)
+          for (int j = 0; j < QG; ++j) mx_scales16(blob + M.scales_off + tile * 64 + 16 * (q0 + j), msc + 16 * j);
+        for (int r = 0; r < 16; ++r) {
+          __m512 a[RR];
+          for (int t = 0; t < RR; ++t) a[t] = _mm512_setzero_ps();
+          float sc = 0.0f;
+          if constexpr (!MX) std::memcpy(&sc, blob + M.scales_off + (tile * 16 + r) * 4, 4);
+          for (int j = 0; j < QG; ++j) {
+            __m512 w[2];
+            const int lane = 16 * (q0 + j) + r;
+            if constexpr (MX)
+              decode_mxfp4_avx512(codes + lane * 16, msc[16 * j + r], w);
+            else
+              decode_fp8_avx512(codes + lane * 32, sc, w);
+            for (int t = 0; t < RR; ++t)
+              a[t] = _mm512_fmadd_ps(w[1], xv[t][j][1], _mm512_fmadd_ps(w[0], xv[t][j][0], a[t]));
+          }
+          for (int t = 0; t < RR; ++t) {
+            float* pp = part + (r * RR + t) * 16;
+            _mm512_storeu_ps(pp, _mm512_add_ps(_mm512_loadu_ps(pp), a[t]));
+          }
+        }
+      }
+    }
+  }
+  template <bool MX>
+  __attribute__((target("avx512f,avx512bw,avx2,fma,f16c"))) static void few_rows_any(
+      int rows, const MatLayout& M, const uint8_t* blob, int64_t rb, int nkb, const float* xf, int K, float* part) {
+    switch (rows) {
+      case 1: few_rows<1, 4, MX>(M, blob, rb, nkb, xf, K, part); break;
+      case 2: few_rows<2, 4, MX>(M, blob, rb, nkb, xf, K, part); break;
+      case 3: few_rows<3, 2, MX>(M, blob, rb, nkb, xf, K, part); break;
+      default: few_rows<4, 2, MX>(M, blob, rb, nkb, xf, K, part); break;
+    }
+  }
+
   __attribute__((target("avx512f,avx512bw,avx2,fma,f16c"))) static void run(
       const ExpertLayout& L, const uint8_t* blob, int m0, int nm, const float* gsc, const float* xf, int rows,
       int rb_begin, int rb_end, const std::function<void(int, const float*)>& finish) {
@@ -389,6 +474,17 @@ struct RowBlocks<kAvx512> {
       for (int mi = 0; mi < nm; ++mi) {
         const MatLayout& M = L.m[m0 + mi];
         std::fill(part.begin(), part.end(), 0.0f);
+        if (rows <= 4 && fmt != FT_FMT_NVFP4) {
+          // part: [tile row][input row][16]
+          if (mx)
+            few_rows_any<true>(rows, M, blob, rb, nkb, xf, K, part.data());
+          else
+            few_rows_any<false>(rows, M, blob, rb, nkb, xf, K, part.data());
+          for (int r = 0; r < 16; ++r)
+            for (int t = 0; t < rows; ++t)
+              acc[(size_t(mi) * rows + t) * 16 + r] += _mm512_reduce_add_ps(_mm512_loadu_ps(&part[(r * rows + t) * 16]));
+          continue;
+        }
         for (int kb = 0; kb < nkb; ++kb) {
           const int64_t tile = int64_t(rb) * nkb + kb;
           for (int q = 0; q < 4; ++q) {
