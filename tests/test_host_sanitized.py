@@ -44,8 +44,12 @@ def host_check_tsan(tmp_path_factory):
     return _build(tmp_path_factory, "tsan", "-fsanitize=thread")
 
 
+# rows 1-4 of MXFP4 and FP8 take the few-rows loop of the AVX-512 build (all
+# four K quarters in registers up to 2 rows, two at a time for 3 and 4), other
+# counts the general one
 CASES = [(ms.FMT_MXFP4, 256, 128, 1), (ms.FMT_MXFP4, 384, 256, 5), (ms.FMT_NVFP4, 256, 384, 3),
-         (ms.FMT_FP8_B128, 384, 256, 4), (ms.FMT_FP8_B128, 256, 128, 1)]
+         (ms.FMT_FP8_B128, 384, 256, 4), (ms.FMT_FP8_B128, 256, 128, 1), (ms.FMT_MXFP4, 384, 256, 2),
+         (ms.FMT_MXFP4, 256, 384, 3), (ms.FMT_FP8_B128, 384, 128, 2), (ms.FMT_FP8_B128, 256, 384, 3)]
 
 
 ISAS = ["native", "avx2", "portable"]  # the widest build the CPU runs, then capped ones
@@ -129,3 +133,38 @@ def test_host_lane_decode_is_exact(host_check, tmp_path, fmt, isa):
             assert np.array_equal(a, b.astype(np.float32), equal_nan=True)
     if fmt == ms.FMT_FP8_B128:
         assert np.isnan(got[0][3]) and np.isnan(got[0][5 * H + 200]) and np.isnan(got[0]).sum() == 2
+
+
+@pytest.mark.parametrize("isa", ISAS)
+@pytest.mark.parametrize("rows", [2, 6])
+def test_host_expert_fp8_nan_code_reaches_its_output_only(host_check, tmp_path, rows, isa):
+    """An FP8 NaN code (S.1111.111) planted in W_down at (output 5, input 17)
+    makes output feature 5 NaN for every row and leaves every other output
+    finite and equal to the oracle's within the parity bar: the host decodes
+    NaN lanes by table in both the few-rows loop (2 rows) and the general one
+    (6 rows), as the oracle's E4M3 decode does."""
+    fmt, H, I = ms.FMT_FP8_B128, 256, 384
+    blob = ms.gen_blob(95, ms.KIND_EXPERT, fmt, H, I, rows)
+    cod, _, _, _ = F.blob_offsets(fmt, H, I)
+    co, _ = cod[2]
+    blob[co + 5 * I + 17] = 0x7F
+    x_bits = ms.f32_to_bf16_bits(np.random.default_rng(rows).standard_normal((rows, H)).astype(np.float32))
+    w = np.random.default_rng(I + rows).uniform(0.05, 1.0, rows).astype(np.float32)
+    blob.tofile(tmp_path / "blob.bin")
+    x_bits.astype(np.uint16).tofile(tmp_path / "x.bin")
+    w.tofile(tmp_path / "w.bin")
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:halt_on_error=1",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+    if isa != "native":
+        env["FT_MOE_HOST_ISA"] = isa
+    r = subprocess.run([host_check, str(fmt), str(H), str(I), str(rows), "2", str(tmp_path)], capture_output=True,
+                       text=True, env=env, timeout=300)
+    assert r.returncode == 0, r.stderr[-4000:]
+    p = F.bf16_from_bits(np.fromfile(tmp_path / "p.bin", np.uint16).reshape(rows, H))
+    wg, wu, wd = F.dequant_expert(fmt, blob, H, I)
+    want = ffn.weighted_rows(ffn.expert_forward(F.bf16_from_bits(x_bits), wg, wu, wd), w)
+    assert np.isnan(want[:, 5]).all() and np.isnan(p[:, 5]).all()
+    keep = np.arange(H) != 5
+    assert np.isfinite(p[:, keep]).all()
+    rel = np.linalg.norm(p[:, keep] - want[:, keep]) / np.linalg.norm(want[:, keep])
+    assert rel <= 2e-3, rel
