@@ -1,7 +1,8 @@
 """GPU parity on small synthetic layers that cover the edge cases: every
-format, ragged token counts, odd expert counts, k = 1, waves, the all-resident
-("fused") pool, the shared expert, hybrid shares 0 < s < 1 and s = 1, prefill
-staging followed by decode, and the error paths forced from the host."""
+format, ragged token counts, odd expert counts, k = 1, the largest expert
+count and top-k, waves, the all-resident ("fused") pool, the shared expert,
+hybrid shares 0 < s < 1 and s = 1, calls with no tokens, prefill staging
+followed by decode, and the error paths forced from the host."""
 
 import os
 
@@ -31,6 +32,9 @@ CASES = {
     "k1-odd-E": (_small(104, 2, 128, 128, 5, 1, [MX, MX], 3, alpha=None), [(17, 0), (1, 1), (33, 2)], 0.0),
     "wide-k": (_small(105, 1, 512, 256, 40, 16, [MX], 48), [(3, 0), (11, 1)], 0.0),
     "aliased-blobs": (_small(106, 4, 256, 128, 8, 2, [MX, NV, MX, F8], 10, n_blobs=5), [(6, 0), (6, 1)], 0.0),
+    # the largest expert count and top-k the library takes (512, 16); the second call's 640 pairs
+    # exceed the 600 slots, so it runs in waves
+    "max-experts-top16": (_small(110, 1, 128, 128, 512, 16, [MX], 600), [(12, 0), (40, 1)], 0.0),
 }
 
 
@@ -328,5 +332,43 @@ def test_failed_mx_tile_allocation_recovers(monkeypatch, which):
             orr = o.forward(l, xb, ms.popularity_bias(w, l, 0), prefill=True)
             compare_call(gr, orr, 2, check_out=False)
             assert rel_l2(OF.bf16_from_bits(gr["out_bits"]), orr["out"]) <= 2e-3
+    finally:
+        g.close()
+
+
+def test_zero_token_calls_change_nothing():
+    """Calls with no tokens (decode, a staged prefill layer, the no-alloc entry
+    point) return FT_OK and change nothing: the output buffer, the counters and
+    the slot table stay as they were, a staged prefill does not start, and the
+    next calls still match the oracle, which never saw the empty calls."""
+    import torch
+
+    import lru_expert_cache_amd as ft
+    from tests.moe_case import GpuLayerStack, compare_call, compare_table
+
+    w = _small(109, 2, 256, 128, 8, 2, [MX, F8], 6)
+    g = GpuLayerStack(w)
+    o = OracleLayerStack(w, pool_slots=g.C)
+    try:
+        def calls(step):
+            for l in range(w.num_layers):
+                x = ms.activations(w, l, step, 5)
+                compare_call(g.forward(l, x, g.bias(l, step)), o.forward(l, x, ms.popularity_bias(w, l, 0)),
+                             w.top_k)
+
+        calls(0)
+        st0 = ft.ft_moe_pool_stats(g.pool)
+        x = torch.zeros((1, w.hidden), dtype=torch.int16, device=g.dev)
+        out = torch.full((1, w.hidden), 0x1234, dtype=torch.int16, device=g.dev)
+        for l in range(w.num_layers):
+            assert ft.ft_moe_layer_forward(g.pool, l, 0, x, None, out, ft.FT_FWD_DECODE) == ft.FT_OK
+            assert ft.ft_moe_layer_forward(g.pool, l, 0, x, None, out, ft.FT_FWD_PREFILL_STAGED) == ft.FT_OK
+            assert ft.ft_moe_layer_forward_noalloc(g.pool, l, 0, x, None, out, ft.FT_FWD_DECODE) == ft.FT_OK
+        torch.cuda.synchronize()
+        assert bool((out == 0x1234).all())
+        assert ft.ft_moe_pool_stats(g.pool) == st0
+        compare_table(g, o)
+        calls(1)  # decode still allowed: no prefill chunk was started
+        compare_table(g, o)
     finally:
         g.close()
