@@ -71,7 +71,7 @@ struct ft_moe_pool {
   // waits) unless the call needs the host: hybrid split, several waves, or
   // FT_MOE_DECODE_PATH=host / injected copy failures.
   bool dev_decode = true;
-  int copy_wgs = 64;                // workgroups of the miss-copy kernel
+  int copy_wgs = 64;                // workgroups of the miss-copy kernel (a sweep measured 64 best)
   // debug (env FT_MOE_POISON at creation): every slot is filled with 0xFF
   // bytes (NaN block scales) just before a copy into it, so a reader that
   // races a copy produces NaN instead of stale values
@@ -86,9 +86,6 @@ struct ft_moe_pool {
   // env FT_MOE_LOG=<n>: a counters line on stderr every n forward calls
   int log_every = 0;
   uint64_t log_calls = 0;
-  // decode calls of up to 32 tokens use the K-streaming FFN kernel unless
-  // FT_MOE_FFN=grid (the split-K kernel every other call uses)
-  bool ffn_stream = true;
 
   // device memory
   uint8_t* arena = nullptr;
@@ -394,7 +391,7 @@ int run_ffn(ft_moe_pool* p, int layer, const void* x, int list_off, int n, const
   // (its recycled events would still hold an earlier launch's timestamps)
   if (n_dev == nullptr && n <= 0) return FT_OK;
   FfnArgs a = ffn_args(p, layer, list_off, n, n_dev);
-  a.max_rows = p->ffn_stream && max_group_rows <= 64 ? max_group_rows : 0;
+  a.max_rows = max_group_rows <= 64 ? max_group_rows : 0;
   const int f = p->fmt[layer];
   const double H = p->H, I = p->I;
   a.x = static_cast<const uint16_t*>(x);
@@ -1276,8 +1273,6 @@ int ft_moe_init_pool(const ft_moe_config* cfg, const ft_moe_weights* wts, ft_moe
       FT_HIP_CHECK(hipMemcpy(p->key_sum_dev, sums.data(), sums.size() * 8, hipMemcpyHostToDevice));
       FT_HIP_CHECK(hipMemset(p->bad_dev, 0, 16));
     }
-    if (const char* fk = std::getenv("FT_MOE_FFN")) p->ffn_stream = std::strcmp(fk, "grid") != 0;
-    if (const char* cw = std::getenv("FT_MOE_COPY_WGS")) p->copy_wgs = std::max(1, std::min(1024, std::atoi(cw)));
     if (const char* pz = std::getenv("FT_MOE_POISON")) p->poison = pz[0] != '\0' && std::strcmp(pz, "0") != 0;
     {
       std::vector<int32_t> lru(C);
@@ -1286,8 +1281,6 @@ int ft_moe_init_pool(const ft_moe_config* cfg, const ft_moe_weights* wts, ft_moe
       std::vector<double> g(L, INFINITY);
       FT_HIP_CHECK(hipMemcpy(p->tab.min_gap, g.data(), size_t(L) * 8, hipMemcpyHostToDevice));
     }
-    if (const char* cs = std::getenv("FT_MOE_COPY_STREAMS"))
-      p->n_copy = std::max(1, std::min(ft_moe_pool::kMaxCopyStreams, std::atoi(cs)));
     for (int c = 0; c < p->n_copy; ++c) {
       FT_HIP_CHECK(hipStreamCreateWithFlags(&p->copy[c], hipStreamNonBlocking));
       FT_HIP_CHECK(hipEventCreateWithFlags(&p->ev_copy_done[c], hipEventDisableTiming));
