@@ -484,7 +484,7 @@ def main():
     global HYBRID_THREADS
     HYBRID_THREADS = args.host_threads
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the library has no multi-GPU path",
               file=sys.stderr)
         sys.exit(2)
 

@@ -4,7 +4,7 @@ TEST INFRASTRUCTURE (oracle).  The pages say only that a routed token runs
 through the few experts its router picks (devpik article, "Why a Huge MoE
 Model Fits on One Consumer GPU") and that experts are stored in MXFP4, NVFP4,
 FP8 or BF16 (devpik article, "The Real Requirement Is System RAM").  The
-expert is the usual SwiGLU MLP; rounding points are this build's reading:
+expert is the usual SwiGLU MLP; the pages fix no rounding points, so these are a reading:
 
   g = W_g x', u = W_u x'            (fp64 here)
   h = bf16(silu(g) * u),  silu(g) = g / (1 + exp(-g))

@@ -6,7 +6,7 @@ place and a miss is streamed over PCIe (devpik article, "Why a Huge MoE Model
 Fits on One Consumer GPU"); one LRU pool is shared by all layers (same
 section); the hybrid strategy splits each step's misses between host compute
 and streaming (same section; byteiota article, "The Bandwidth-Adaptive
-Runtime").  Finer points are this build's readings:
+Runtime").  Finer points are readings of the pages:
 
 * Keys are (layer, expert).  A call's tokens are walked in order; a *wave* is
   the longest run of consecutive tokens whose union of selected experts has
