@@ -217,3 +217,45 @@ def test_qwen_a3b_prefill_4096_mx_activations(qwen_store, act):
         assert len(rels) == 2
     finally:
         g.close()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("T", [8192, 1])
+def test_qwen_a3b_prefill_other_chunk_sizes(T):
+    """The staged path at the pages' default chunk of 8,192 tokens (devpik,
+    "Long Prompts Are the Bottleneck": 65,536 pairs, ~640 row tiles per layer)
+    and at a one-token chunk, on the first four Qwen-A3B-shaped layers with
+    MXFP4 activations: decisions exact on every layer and the pool table after
+    the chunk; outputs on sampled rows of the first and the last layer."""
+    from tests.moe_case import GpuLayerStack, compare_call, compare_table
+    from oracle import ffn as OFFN
+    import lru_expert_cache_amd as ft
+
+    w0 = ms.workload("qwen-a3b-prefill-4096")
+    w = w0.with_(num_layers=4, layer_fmt=w0.layer_fmt[:4], batches=(T,))
+    store = ms.BlobStore(w)
+    g = GpuLayerStack(w, store=store)
+    o = OracleLayerStack(w, pool_slots=g.C, blob_fn=lambda l, e: store.expert(l, e), dequant_items=130,
+                         act_mode=OFFN.ACT_MXFP4)
+    rng = np.random.default_rng(2)
+    try:
+        rels = []
+        for l in range(w.num_layers):
+            x = ms.activations(w, l, 0, T)
+            b = ms.popularity_bias(w, l, 0)
+            want = l in (0, w.num_layers - 1)
+            toks = np.sort(rng.choice(T, min(T, 24), replace=False)) if want else None
+            gr = g.forward(l, x, g.bias(l, 0), prefill=True, act=ft.FT_ACT_MXFP4)
+            orr = o.forward(l, x, b, prefill=True, outputs=want, out_tokens=toks)
+            r = compare_call(gr, orr, w.top_k, check_out=want)
+            if r is not None:
+                rels.append(r)
+        compare_table(g, o)
+        st = ft.ft_moe_pool_stats(g.pool)
+        assert st["bytes_h2d"] == o.stats["bytes_h2d"] == w.num_layers * w.num_experts * ms.expert_bytes(
+            ms.FMT_MXFP4, w.hidden, w.inter)
+        assert st["pair_misses"] == w.num_layers * T * w.top_k
+        print(f"T={T} rel-L2", rels)
+        assert len(rels) == 2
+    finally:
+        g.close()
