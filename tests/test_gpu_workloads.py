@@ -259,3 +259,45 @@ def test_qwen_a3b_prefill_other_chunk_sizes(T):
         assert len(rels) == 2
     finally:
         g.close()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["deepseek-v4-flash-decode", "glm-5.2-mixed-decode"])
+def test_split_k_ffn_at_full_shapes(name):
+    """The split-K expert FFN (k_ffn: NVFP4 and FP8 prefill, and decode calls of
+    more than 64 tokens) at the DeepSeek- and GLM-shaped layer sizes, on their
+    first two layers: a 128-token decode call per layer (with DeepSeek's 968
+    slots its 1,024 pairs run in two waves), a 256-token staged prefill chunk,
+    then decode again.  Decisions, tables and counters exact; outputs on four
+    sampled rows of every call."""
+    from tests.moe_case import GpuLayerStack, compare_call, compare_table
+    import lru_expert_cache_amd as ft
+
+    w0 = ms.workload(name)
+    w = w0.with_(num_layers=2, layer_fmt=w0.layer_fmt[:2])
+    store = ms.BlobStore(w)
+    g = GpuLayerStack(w, store=store)
+    o = OracleLayerStack(w, pool_slots=g.C, blob_fn=lambda l, e: store.expert(l, e), dequant_items=24,
+                         threads=THREADS)
+    rng = np.random.default_rng(3)
+    try:
+        rels = []
+        for step, (prefill, T) in enumerate(((False, 128), (True, 256), (False, 128))):
+            for l in range(w.num_layers):
+                x = ms.activations(w, l, 5 + step, T)
+                b = ms.popularity_bias(w, l, 0)
+                toks = np.sort(rng.choice(T, 4, replace=False))
+                gr = g.forward(l, x, g.bias(l, 0), prefill=prefill)
+                orr = o.forward(l, x, b, prefill=prefill, outputs=True, out_tokens=toks)
+                rels.append(compare_call(gr, orr, w.top_k))
+            # the last call ran layer 1 (NVFP4, or FP8): the split-K kernel
+            kern = ft.ft_moe_ffn_kernel_name("ffn_gateup")
+            print(f"{name} {'prefill' if prefill else 'decode'} T={T} ok, {kern}", flush=True)
+            assert kern.startswith("k_ffn<"), kern
+        compare_table(g, o)
+        st = ft.ft_moe_pool_stats(g.pool)
+        for key in ("pair_hits", "pair_misses", "expert_hits", "expert_misses", "evictions", "bytes_h2d", "calls"):
+            assert st[key] == o.stats[key], (key, st[key], o.stats[key])
+        print("rel-L2", rels)
+    finally:
+        g.close()
