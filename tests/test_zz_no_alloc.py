@@ -51,22 +51,47 @@ CASES = {
 }
 
 
-@pytest.mark.parametrize("name", list(CASES))
+def _deepseek_four_layers():
+    """The DeepSeek-shaped layers (H 7168, I 2048, 256 NVFP4 experts, top-8,
+    shared expert), four of them over 520 slots: 64-token calls (512 pairs, one
+    wave) take about two thirds of the scratch array, and the layers' distinct
+    experts outnumber the slots, so calls evict."""
+    w0 = ms.workload("deepseek-v4-flash-decode")
+    return w0.with_(num_layers=4, layer_fmt=w0.layer_fmt[:4], pool_slots=520)
+
+
+# full-size case: decisions against the oracle, outputs against the regular
+# entry point bit for bit (the regular path's outputs at this shape are checked
+# against the oracle by the workload tests)
+FULL_CASES = {"deepseek-shape": (_deepseek_four_layers, [(64, 0), (16, 1)])}
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", list(CASES) + list(FULL_CASES))
 def test_noalloc_matches_forward_on_consecutive_calls(name):
     import torch
     from tests.moe_case import GpuLayerStack, compare_call, compare_table
     import lru_expert_cache_amd as ft
 
-    w, calls = CASES[name]
-    ga = GpuLayerStack(w)
-    gn = GpuLayerStack(w)
-    o = OracleLayerStack(w, pool_slots=ga.C)
+    full = name in FULL_CASES
+    if full:
+        make, calls = FULL_CASES[name]
+        w = make()
+        store = ms.BlobStore(w)
+        o = OracleLayerStack(w, pool_slots=w.pool_slots, blob_fn=lambda l, e: store.expert(l, e))
+    else:
+        w, calls = CASES[name]
+        store = None
+        o = OracleLayerStack(w, pool_slots=w.pool_slots)
+    ga = GpuLayerStack(w, store=store)
+    gn = GpuLayerStack(w, store=store)
     try:
         for T, s in calls:
             for l in range(w.num_layers):
                 x_bits = ms.activations(w, l, s, T)
                 ra = ga.forward(l, x_bits, ga.bias(l, s))
-                compare_call(ra, o.forward(l, x_bits, ms.popularity_bias(w, l, 0)), w.top_k)
+                compare_call(ra, o.forward(l, x_bits, ms.popularity_bias(w, l, 0), outputs=not full), w.top_k,
+                             check_out=not full)
                 rn, grew = _noalloc_call(ft, torch, gn, l, x_bits, gn.bias(l, s))
                 assert grew == 0, f"device memory fell by {grew} bytes during a no-alloc call"
                 assert np.array_equal(rn["out_bits"], ra["out_bits"]), (T, l)
