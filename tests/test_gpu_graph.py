@@ -22,36 +22,57 @@ def _w():
                        True, False, None)
 
 
+def _qwen_four_layers():
+    # the Qwen-A3B-shaped layers (H 2048, I 768, 128 MXFP4 experts, top-8), four of
+    # them over 154 slots (30% of their keys): a 16-token call (128 pairs) is one wave
+    w0 = ms.workload("qwen-a3b-decode")
+    return w0.with_(num_layers=4, layer_fmt=w0.layer_fmt[:4], pool_slots=154)
+
+
 def test_captured_decode_step_replays_like_eager_calls():
+    _replay_case(_w(), 4, 6, big_tokens=7)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("T", [16, 1])
+def test_captured_qwen_a3b_step_replays_like_eager_calls(T):
+    """The same at the Qwen-A3B layer size, in the launch shapes of the
+    benchmark's graph replays (batch 16 and 1)."""
+    # enough steps that the calls' distinct experts outnumber the slots (evictions)
+    _replay_case(_qwen_four_layers(), T, 4 if T > 1 else 8, big_tokens=0)
+
+
+def _replay_case(w, T, steps, big_tokens):
     import torch
 
     from tests.moe_case import GpuLayerStack, compare_table
     import lru_expert_cache_amd as ft
 
-    w = _w()
-    T, L, H = 4, w.num_layers, w.hidden
-    ga, ge = GpuLayerStack(w), GpuLayerStack(w)  # graph-driven, eager
-    o = OracleLayerStack(w, pool_slots=ga.C)
+    L, H = w.num_layers, w.hidden
+    store = ms.BlobStore(w)
+    ga, ge = GpuLayerStack(w, store=store), GpuLayerStack(w, store=store)  # graph-driven, eager
+    o = OracleLayerStack(w, pool_slots=ga.C, blob_fn=lambda l, e: store.expert(l, e))
     dev = ga.dev
     s = torch.cuda.Stream(dev)
     try:
         ft.ft_moe_reserve(ga.pool, T)
         xin = torch.zeros((L, T, H), dtype=torch.int16, device=dev)
         outs = torch.zeros((L, T, H), dtype=torch.int16, device=dev)
-        big = torch.zeros((7, H), dtype=torch.int16, device=dev)
+        big = torch.zeros((max(big_tokens, 1), H), dtype=torch.int16, device=dev)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=s):
             for l in range(L):
                 ft.ft_moe_layer_forward(ga.pool, l, T, xin[l], None, outs[l], ft.FT_FWD_DECODE, s, None)
-            # 7 tokens x top-4 > 24 slots: a call the host splits into waves cannot be
-            # captured; it is rejected and nothing is captured for it
-            with pytest.raises(ft.FtError):
-                ft.ft_moe_layer_forward(ga.pool, 0, 7, big, None, big, ft.FT_FWD_DECODE, s, None)
+            if big_tokens:
+                # 7 tokens x top-4 > 24 slots: a call the host splits into waves cannot be
+                # captured; it is rejected and nothing is captured for it
+                with pytest.raises(ft.FtError):
+                    ft.ft_moe_layer_forward(ga.pool, 0, big_tokens, big, None, big, ft.FT_FWD_DECODE, s, None)
         torch.cuda.synchronize()
         assert int(outs.abs().sum().item()) == 0, "capturing ran the calls"
 
-        for step in range(6):
+        for step in range(steps):
             xs = [ms.activations(w, l, step, T) for l in range(L)]
             xin.copy_(torch.from_numpy(np.stack(xs).view(np.int16)))
             torch.cuda.synchronize()
