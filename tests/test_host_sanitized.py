@@ -55,11 +55,34 @@ CASES = [(ms.FMT_MXFP4, 256, 128, 1), (ms.FMT_MXFP4, 384, 256, 5), (ms.FMT_NVFP4
 ISAS = ["native", "avx2", "portable"]  # the widest build the CPU runs, then capped ones
 
 
+def _plant_e8m0_edges_small(blob, H, I):
+    """E8M0 scales 0 and 1 (2^-127 and 2^-126: subnormal weights) in one block
+    of W_gate and of W_down; their weights are tiny, so the expert's output
+    stays comparable with the oracle's."""
+    _, sca, _, _ = F.blob_offsets(ms.FMT_MXFP4, H, I)
+    blob[sca[0][0] + 6] = 0
+    blob[sca[2][0] + 3] = 1
+
+
+def _plant_e8m0_edges(blob, H, I):
+    """E8M0 block scales at the small and large ends of the range (0, 1, 2:
+    2^-127 .. 2^-125, subnormal weights among them; 251, 252: up to
+    6 * 2^125) in W_gate and W_down; every weight stays finite in fp32, so
+    each must decode exactly."""
+    _, sca, _, _ = F.blob_offsets(ms.FMT_MXFP4, H, I)
+    for m, blocks in ((0, (0, 1, 2, 3, 4, 37)), (2, (5, 9))):
+        so, _ = sca[m]
+        for b, v in zip(blocks, (0, 1, 2, 251, 252, 0)):
+            blob[so + b] = v
+
+
 @pytest.mark.parametrize("isa", ISAS)
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"{ms.FMT_NAMES[c[0]]}-H{c[1]}-I{c[2]}-rows{c[3]}")
 def test_repack_and_host_expert_under_sanitizers(host_check, tmp_path, case, isa):
     fmt, H, I, rows = case
     blob = ms.gen_blob(91, ms.KIND_EXPERT, fmt, H, I, H + I + rows)
+    if fmt == ms.FMT_MXFP4:
+        _plant_e8m0_edges_small(blob, H, I)
     x_bits = ms.f32_to_bf16_bits(np.random.default_rng(H + rows).standard_normal((rows, H)).astype(np.float32))
     w = np.random.default_rng(I).uniform(0.05, 1.0, rows).astype(np.float32)
     blob.tofile(tmp_path / "blob.bin")
@@ -116,6 +139,8 @@ def test_host_lane_decode_is_exact(host_check, tmp_path, fmt, isa):
         co, _ = cod[0]
         blob[co + 3] = 0x7F
         blob[co + 5 * H + 200] = 0xFF
+    if fmt == ms.FMT_MXFP4:
+        _plant_e8m0_edges(blob, H, I)
     blob.tofile(tmp_path / "blob.bin")
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:halt_on_error=1",
                UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
