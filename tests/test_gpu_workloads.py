@@ -75,6 +75,19 @@ def test_qwen_a3b_decode(qwen_store, T):
 
 
 @pytest.mark.timeout(1200)
+def test_qwen_a3b_decode_all_256_steps(qwen_store):
+    """The whole Qwen-A3B-shaped decode run at batch 16: 256 steps x 48 layers,
+    every call's decisions exact (experts, weights, flags, slots, miss lists,
+    rows) and the table and counters after it; outputs on steps {0, 127, 255}
+    x layers {0, 23, 47}."""
+    w = ms.workload("qwen-a3b-decode")
+    sample = {(s, l) for s in (0, 127, 255) for l in (0, 23, 47)}
+    rels, st = _decode_run(w, 16, 256, sample, store=qwen_store)
+    print("rel-L2", rels, "hits", st["pair_hits"], "misses", st["pair_misses"], "evictions", st["evictions"])
+    assert len(rels) == len(sample) and max(rels) <= 2e-3
+
+
+@pytest.mark.timeout(1200)
 @pytest.mark.parametrize("T,steps", [(1, 2), (8, 2), (32, 1), (64, 1)])
 def test_deepseek_decode_nvfp4_shared(T, steps):
     w = ms.workload("deepseek-v4-flash-decode")
