@@ -144,11 +144,11 @@ def test_glm_mixed_formats_hybrid():
                          threads=THREADS)
     try:
         rels = []
-        for s in (0, 33):  # two popularity phases
+        for s in (0, 33, 65, 97, 127):  # every popularity phase (a shift every 32 steps) and the last step
             for l in range(w.num_layers):
                 x = ms.activations(w, l, s, T)
                 b = ms.popularity_bias(w, l, w.phase(s))
-                want = (s, l) in {(0, 0), (0, 1), (33, 90), (33, 91)}
+                want = (s, l) in {(0, 0), (0, 1), (33, 90), (33, 91), (127, 90), (127, 91)}
                 gr = g.forward(l, x, g.bias(l, s))
                 orr = o.forward(l, x, b, outputs=want)
                 r = compare_call(gr, orr, w.top_k, check_out=want)
@@ -159,7 +159,7 @@ def test_glm_mixed_formats_hybrid():
         st = ft.ft_moe_pool_stats(g.pool)
         for key in ("pair_hits", "pair_misses", "expert_misses", "cpu_misses", "evictions", "bytes_h2d", "calls"):
             assert st[key] == o.stats[key], key
-        assert st["cpu_misses"] > 0 and len(rels) == 4
+        assert st["cpu_misses"] > 0 and len(rels) == 6
         print("rel-L2", rels, st)
     finally:
         g.close()
